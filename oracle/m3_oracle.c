@@ -1,0 +1,449 @@
+/*
+ * m3_oracle.c -- plain, slow CPU oracle (test infrastructure only).
+ *
+ * Sources of each definition (the pages, by title and section):
+ *  [metal]  TensorFold PR #987 "MiniMax Music 3 on Metal": the precision list
+ *           (bf16 activations rounded where torch rounds, fp32 norms; int8
+ *           weight-only with a scale per row for the body and lm_head and per
+ *           group of 128 for the depth decoder), "What it adds" (decode GEMVs
+ *           with a SwiGLU variant; Philox counters in the draw), the frame
+ *           bookkeeping paragraph and "Kernel contract".
+ *  [hf]     diffusers issue #14486 "MiniMax Music 3 modular pipeline", item 3
+ *           (sliced lm_head is identical to the masked full one; Gumbel-argmax
+ *           in place of softmax + multinomial) and item 4 (lockstep rows).
+ *  [ds]     rkmt.cn "MiniMax-Music3 ... DiffSynth-Studio": model overview
+ *           (Qwen3 body 4096 x 36, 32/8 heads; RVQ depth decoder 4 layers,
+ *           16 heads, 8 codebooks) and stage 2 (vocab mask to the audio
+ *           codes, per-codebook depth draws, frame embedding fed back as the
+ *           sum of embed_tokens and the RVQ audio embeddings times 8^-1/2).
+ *
+ * Built with -ffp-contract=off and without fast-math: every fp32 operation
+ * in the sampler is one IEEE operation in the order written.
+ */
+#include "m3_oracle.h"
+
+#include <math.h>
+#include <string.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int m3o_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ */
+/* bf16: the upper 16 bits of an IEEE binary32; 8 significant bits.     */
+/* Rounding is defined on the real value: pick the nearest bf16, ties   */
+/* to the even significand; NaN -> 0x7FC0 (torch's canonical NaN).      */
+/* ------------------------------------------------------------------ */
+uint16_t m3o_f64_to_bf16(double v) {
+  if (isnan(v)) return 0x7FC0;
+  if (isinf(v)) return v > 0 ? 0x7F80 : 0xFF80;
+  if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e);                 /* a = m * 2^e, m in [0.5, 1) */
+  double r;
+  if (e - 1 < -126) {
+    /* below the normal range: bf16 subnormals are multiples of 2^-133 */
+    r = ldexp(nearbyint(ldexp(a, 133)), -133);
+  } else {
+    /* 8 significant bits: multiples of 2^(e-8) */
+    r = ldexp(nearbyint(ldexp(a, 8 - e)), e - 8);
+  }
+  /* largest finite bf16 is (2 - 2^-7) * 2^127; anything that rounds past it
+     is infinity */
+  if (r >= ldexp(1.0, 128)) return v > 0 ? 0x7F80 : 0xFF80;
+  float f = (float)r;           /* exact: r has <= 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint16_t b = (uint16_t)(u >> 16);
+  return v < 0 ? (uint16_t)(b | 0x8000) : b;
+}
+
+double m3o_bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+void m3o_f64_to_bf16_n(const double* v, uint16_t* out, size_t n) {
+  #pragma omp parallel for schedule(static)
+  for (long i = 0; i < (long)n; ++i) out[i] = m3o_f64_to_bf16(v[i]);
+}
+
+void m3o_f32_to_bf16_n(const float* v, uint16_t* out, size_t n) {
+  #pragma omp parallel for schedule(static)
+  for (long i = 0; i < (long)n; ++i) out[i] = m3o_f64_to_bf16((double)v[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* RMSNorm ([metal] precision list: fp32 norms, bf16 activations).      */
+/* The oracle evaluates r in float64; one bf16 rounding of x*r*gamma.   */
+/* ------------------------------------------------------------------ */
+void m3o_rmsnorm(const uint16_t* x, int B, int K, int ldx, const float* gamma,
+                 float eps, uint16_t* a, int lda) {
+  for (int b = 0; b < B; ++b) {
+    const uint16_t* xr = x + (size_t)b * ldx;
+    uint16_t* ar = a + (size_t)b * lda;
+    if (!gamma) {
+      for (int k = 0; k < K; ++k) ar[k] = xr[k];
+      continue;
+    }
+    double ss = 0.0;
+    for (int k = 0; k < K; ++k) {
+      double v = m3o_bf16_to_f64(xr[k]);
+      ss += v * v;
+    }
+    double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+    for (int k = 0; k < K; ++k)
+      ar[k] = m3o_f64_to_bf16(m3o_bf16_to_f64(xr[k]) * r * (double)gamma[k]);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* int8 weight-only quantisation ([metal] precision list).              */
+/* scale = absmax / 127 as one fp32 division; q = nearest integer of    */
+/* W / scale (ties to even), clamped to [-127, 127]; an all-zero row or */
+/* group gets scale 0 and q 0.                                           */
+/* ------------------------------------------------------------------ */
+static void quant_span(const uint16_t* w, int n, int8_t* q, float* s) {
+  double amax = 0.0;
+  for (int k = 0; k < n; ++k) {
+    double v = fabs(m3o_bf16_to_f64(w[k]));
+    if (v > amax) amax = v;
+  }
+  float sc = (float)amax / 127.0f;   /* amax is exact in fp32 */
+  *s = sc;
+  for (int k = 0; k < n; ++k) {
+    if (sc == 0.0f) { q[k] = 0; continue; }
+    double t = nearbyint(m3o_bf16_to_f64(w[k]) / (double)sc);
+    if (t > 127.0) t = 127.0;
+    if (t < -127.0) t = -127.0;
+    q[k] = (int8_t)t;
+  }
+}
+
+void m3o_quant_i8row(const uint16_t* W, int N, int K, int8_t* q, float* s) {
+  #pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    quant_span(W + (size_t)n * K, K, q + (size_t)n * K, s + n);
+}
+
+void m3o_quant_i8g128(const uint16_t* W, int N, int K, int8_t* q, float* s) {
+  int G = K / 128;
+  #pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int g = 0; g < G; ++g)
+      quant_span(W + (size_t)n * K + g * 128, 128, q + (size_t)n * K + g * 128,
+                 s + (size_t)n * G + g);
+}
+
+/* ------------------------------------------------------------------ */
+/* y = Wdeq . a, summed in float64.  Each bf16*bf16 product is exact in */
+/* float64, int8*bf16 too; only the running sum rounds (at 2^-53).      */
+/* ------------------------------------------------------------------ */
+static double dot_row(const m3o_mat* m, int n, const uint16_t* a) {
+  int K = m->K;
+  if (m->fmt == M3O_BF16) {
+    const uint16_t* w = m->w + (size_t)n * K;
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) acc += m3o_bf16_to_f64(w[k]) * m3o_bf16_to_f64(a[k]);
+    return acc;
+  }
+  const int8_t* q = m->q + (size_t)n * K;
+  if (m->fmt == M3O_I8ROW) {
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) acc += (double)q[k] * m3o_bf16_to_f64(a[k]);
+    return (double)m->s[n] * acc;
+  }
+  int G = K / 128;
+  double acc = 0.0;
+  for (int g = 0; g < G; ++g) {
+    double part = 0.0;
+    for (int k = g * 128; k < g * 128 + 128; ++k)
+      part += (double)q[k] * m3o_bf16_to_f64(a[k]);
+    acc += (double)m->s[(size_t)n * G + g] * part;
+  }
+  return acc;
+}
+
+void m3o_gemv_rows(const m3o_mat* m, int row0, int nrows, const uint16_t* a,
+                   int B, int lda, double* y) {
+  #pragma omp parallel for schedule(static)
+  for (int n = 0; n < nrows; ++n)
+    for (int b = 0; b < B; ++b)
+      y[(size_t)b * nrows + n] = dot_row(m, row0 + n, a + (size_t)b * lda);
+}
+
+void m3o_gemv(const m3o_mat* m, const uint16_t* a, int B, int lda, double* y) {
+  m3o_gemv_rows(m, 0, m->N, a, B, lda, y);
+}
+
+/* ------------------------------------------------------------------ */
+/* Epilogues.  SwiGLU from an interleaved gate/up pair ([metal] "What   */
+/* it adds": a gate and an up row whose SwiGLU is written together).    */
+/* g and u are the bf16-rounded products; silu(g)*u is rounded once.    */
+/* ------------------------------------------------------------------ */
+void m3o_swiglu_interleaved(const double* y, int B, int F, uint16_t* m) {
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < F; ++i) {
+      double g = m3o_bf16_to_f64(m3o_f64_to_bf16(y[(size_t)b * 2 * F + 2 * i]));
+      double u = m3o_bf16_to_f64(m3o_f64_to_bf16(y[(size_t)b * 2 * F + 2 * i + 1]));
+      m[(size_t)b * F + i] = m3o_f64_to_bf16(g * u / (1.0 + exp(-g)));
+    }
+}
+
+void m3o_residual(const double* y, const uint16_t* h, int n, uint16_t* h_out) {
+  for (int i = 0; i < n; ++i) {
+    double yb = m3o_bf16_to_f64(m3o_f64_to_bf16(y[i]));
+    h_out[i] = m3o_f64_to_bf16(m3o_bf16_to_f64(h[i]) + yb);
+  }
+}
+
+/* Identity attention: with one cached position the softmax over one key is
+   exactly 1, so each query head's output is its KV group's value head. */
+void m3o_attn_stub(const uint16_t* qkv, int B, int ldq, int voff, int n_heads,
+                   int group, int hd, uint16_t* o) {
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < n_heads; ++h)
+      for (int d = 0; d < hd; ++d)
+        o[(size_t)b * n_heads * hd + h * hd + d] =
+            qkv[(size_t)b * ldq + voff + (h / group) * hd + d];
+}
+
+/* ------------------------------------------------------------------ */
+/* Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers:*/
+/* As Easy as 1, 2, 3", SC'11): 10 rounds of two 32x32->64 multiplies   */
+/* (multipliers 0xD2511F53, 0xCD9E8D57) with a Weyl key schedule        */
+/* (0x9E3779B9, 0xBB67AE85).                                             */
+/* ------------------------------------------------------------------ */
+void m3o_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Natural log of a positive normal fp32, from the identity
+   ln x = e ln2 + 2 atanh(t), x = m 2^e, m in (1/sqrt2, sqrt2], t = (m-1)/(m+1),
+   2 atanh t = 2 (t + t^3/3 + t^5/5 + t^7/7 + t^9/9 + t^11/11 + ...).
+   |t| <= 0.1716, so the first omitted term is below 2^-36 relative.
+   Every step is one IEEE fp32 operation (fmaf is the fused one). */
+float m3o_logf(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  int e = (int)((u >> 23) & 0xFFu) - 127;
+  uint32_t mb = (u & 0x007FFFFFu) | 0x3F800000u;
+  float m;
+  memcpy(&m, &mb, 4);                       /* m in [1, 2) */
+  if (m > 1.41421354f) { m = m * 0.5f; e = e + 1; }
+  float f = m - 1.0f;                       /* exact */
+  float d = m + 1.0f;
+  float t = f / d;
+  float s = t * t;
+  float p = 0.0909090936f;                  /* 1/11 */
+  p = fmaf(p, s, 0.111111112f);             /* 1/9  */
+  p = fmaf(p, s, 0.142857149f);             /* 1/7  */
+  p = fmaf(p, s, 0.200000003f);             /* 1/5  */
+  p = fmaf(p, s, 0.333333343f);             /* 1/3  */
+  float sp = s * p;
+  float r = sp * t;
+  float lm = t + r;
+  lm = lm + lm;
+  float ef = (float)e;
+  float res = fmaf(ef, 1.42860677e-06f, lm);   /* ln2 - ln2_hi */
+  res = fmaf(ef, 0.693145752f, res);           /* ln2_hi = 0x3F317200 */
+  return res;
+}
+
+/* Uniform on (0,1): the top 23 bits k of the word give the midpoint of the
+   k-th of 2^23 equal cells, (k + 1/2) 2^-23 = (2k+1) 2^-24, exact in fp32. */
+float m3o_uniform_from_word(uint32_t w) {
+  uint32_t k = ((w >> 9) << 1) | 1u;       /* odd, < 2^24 */
+  return (float)k * 5.96046448e-08f;        /* 2^-24 */
+}
+
+/* Gumbel noise keyed by (seed, batch row, frame, draw, absolute id). */
+float m3o_gumbel(uint64_t seed, uint32_t row, uint32_t frame, uint32_t draw,
+                 uint32_t id) {
+  uint32_t ctr[4] = {id >> 2, row, frame, draw};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  m3o_philox4x32_10(ctr, key, w);
+  float uu = m3o_uniform_from_word(w[id & 3u]);
+  float l1 = m3o_logf(uu);        /* < 0 */
+  float l2 = m3o_logf(-l1);
+  return -l2;
+}
+
+/* total order used by the argmax: NaN above everything, then numeric;
+   returns 1 if (za) ranks strictly above (zb) */
+static int ranks_above(float za, float zb) {
+  if (isnan(za)) return !isnan(zb);
+  if (isnan(zb)) return 0;
+  return za > zb;
+}
+
+/* Gumbel-argmax ([hf] item 3): argmax_j (l_j/T + G_j) draws j with
+   probability softmax(l/T)_j.  Ties go to the lowest index. */
+void m3o_gumbel_argmax(const float* logits, int B, int V, int ldl,
+                       const m3o_sample_params* p, int32_t* out,
+                       float* zbest, float* zsecond) {
+  float invT = 1.0f / p->temperature;
+  for (int b = 0; b < B; ++b) {
+    int best = -1;
+    float zb = 0.0f, z2 = -INFINITY;
+    for (int j = 0; j < V; ++j) {
+      int32_t id = p->ids ? p->ids[j] : p->index_base + j;
+      float z;
+      if (p->valid_lo < p->valid_hi && (id < p->valid_lo || id >= p->valid_hi)) {
+        z = -INFINITY;
+      } else {
+        float g = p->noise_override ? p->noise_override[(size_t)b * V + j]
+                                    : m3o_gumbel(p->seed, (uint32_t)b, p->frame,
+                                                 p->draw, (uint32_t)id);
+        float lt = logits[(size_t)b * ldl + j] * invT;
+        z = lt + g;
+      }
+      if (best < 0 || ranks_above(z, zb)) {
+        if (best >= 0) z2 = zb;
+        best = j; zb = z;
+      } else if (ranks_above(z, z2)) {
+        z2 = z;
+      }
+    }
+    out[b] = p->ids ? p->ids[best] : p->index_base + best;
+    if (zbest) zbest[b] = zb;
+    if (zsecond) zsecond[b] = z2;
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* One frame ([ds] stage 2; [metal] frame bookkeeping).                 */
+/* ------------------------------------------------------------------ */
+static void run_layer(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads,
+                      int n_kv, int hd, int F, float eps, uint16_t* a, uint16_t* qkvb,
+                      uint16_t* o, uint16_t* mm, double* y) {
+  int nq = n_heads * hd, nkv = n_kv * hd;
+  int nqkv = nq + 2 * nkv;
+  /* attention block */
+  m3o_rmsnorm(h, B, Hd, Hd, L->attn_norm, eps, a, Hd);
+  m3o_gemv(&L->qkv, a, B, Hd, y);
+  m3o_f64_to_bf16_n(y, qkvb, (size_t)B * nqkv);
+  m3o_attn_stub(qkvb, B, nqkv, nq + nkv, n_heads, n_heads / n_kv, hd, o);
+  m3o_gemv(&L->o, o, B, nq, y);
+  m3o_residual(y, h, B * Hd, h);
+  /* MLP block */
+  m3o_rmsnorm(h, B, Hd, Hd, L->ffn_norm, eps, a, Hd);
+  m3o_gemv(&L->gu, a, B, Hd, y);
+  m3o_swiglu_interleaved(y, B, F, mm);
+  m3o_gemv(&L->down, mm, B, F, y);
+  m3o_residual(y, h, B * Hd, h);
+}
+
+void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
+                      uint64_t seed, uint32_t frame, float temperature,
+                      int32_t* codes, uint16_t* x_next, m3o_frame_trace* tr) {
+  int H = m->H, D = m->D;
+  int nq = m->n_heads * m->head_dim, nkv = m->n_kv_heads * m->head_dim;
+  int dq = m->d_heads * m->d_head_dim;
+  size_t big = (size_t)B * (size_t)(2 * (m->F > m->Fd ? m->F : m->Fd) + nq + 2 * nkv + 3 * dq + m->V0 + 16);
+  double* y = (double*)malloc(big * sizeof(double));
+  uint16_t* h = (uint16_t*)malloc((size_t)B * H * 2);
+  uint16_t* a = (uint16_t*)malloc((size_t)B * (H > D ? H : D) * 2);
+  uint16_t* qkvb = (uint16_t*)malloc((size_t)B * (nq + 2 * nkv + 3 * dq) * 2);
+  uint16_t* o = (uint16_t*)malloc((size_t)B * (nq > dq ? nq : dq) * 2);
+  uint16_t* mm = (uint16_t*)malloc((size_t)B * (m->F > m->Fd ? m->F : m->Fd) * 2);
+  uint16_t* u = (uint16_t*)malloc((size_t)B * D * 2);
+  uint16_t* hd = (uint16_t*)malloc((size_t)B * D * 2);
+  float* lg = (float*)malloc((size_t)B * (m->V0 > m->code_vocab ? m->V0 : m->code_vocab) * 4);
+  int32_t* draw_out = (int32_t*)malloc((size_t)B * 4);
+  float* zb = (float*)malloc((size_t)B * 4);
+  float* z2 = (float*)malloc((size_t)B * 4);
+
+  memcpy(h, x_in, (size_t)B * H * 2);
+  for (int l = 0; l < m->n_layers; ++l)
+    run_layer(&m->layers[l], h, B, H, m->n_heads, m->n_kv_heads, m->head_dim, m->F,
+              m->eps, a, qkvb, o, mm, y);
+  if (tr && tr->h_body) memcpy(tr->h_body, h, (size_t)B * H * 2);
+
+  /* final norm -> sliced lm_head -> draw 0 over the reachable rows */
+  m3o_rmsnorm(h, B, H, H, m->final_norm, m->eps, a, H);
+  m3o_gemv(&m->lm_head, a, B, H, y);
+  for (size_t i = 0; i < (size_t)B * m->V0; ++i) lg[i] = (float)y[i];
+  if (tr && tr->logits0) memcpy(tr->logits0, lg, (size_t)B * m->V0 * 4);
+  m3o_sample_params sp = {seed, frame, 0u, temperature, m->vocab_base, NULL,
+                          m->vocab_base, m->vocab_base + m->V0, NULL};
+  m3o_gumbel_argmax(lg, B, m->V0, m->V0, &sp, draw_out, zb, z2);
+  for (int b = 0; b < B; ++b) {
+    codes[b * 8 + 0] = draw_out[b];
+    if (tr && tr->zgap) tr->zgap[b * 8 + 0] = zb[b] - z2[b];
+  }
+
+  /* depth decoder input: u = bf16(P_in . normed body state) */
+  m3o_gemv(&m->p_in, a, B, H, y);
+  m3o_f64_to_bf16_n(y, u, (size_t)B * D);
+
+  for (int j = 1; j < m->n_codebooks; ++j) {
+    /* d_j = bf16(u + Emb_j[c_{j-1}]) */
+    for (int b = 0; b < B; ++b) {
+      int32_t prev;
+      const uint16_t* E;
+      if (j == 1) {
+        prev = codes[b * 8] - m->vocab_base;
+        if (prev < 0 || prev >= m->V0) prev = 0;
+        E = m->emb1;
+      } else {
+        prev = codes[b * 8 + j - 1];
+        E = m->emb[j - 2];
+      }
+      for (int k = 0; k < D; ++k)
+        hd[(size_t)b * D + k] = m3o_f64_to_bf16(m3o_bf16_to_f64(u[(size_t)b * D + k]) +
+                                                m3o_bf16_to_f64(E[(size_t)prev * D + k]));
+    }
+    for (int l = 0; l < m->d_layers; ++l)
+      run_layer(&m->d_layers_w[l], hd, B, D, m->d_heads, m->d_heads, m->d_head_dim, m->Fd,
+                m->eps, a, qkvb, o, mm, y);
+    m3o_rmsnorm(hd, B, D, D, m->d_final_norm, m->eps, a, D);
+    m3o_gemv(&m->heads[j - 1], a, B, D, y);
+    for (size_t i = 0; i < (size_t)B * m->code_vocab; ++i) lg[i] = (float)y[i];
+    m3o_sample_params dp = {seed, frame, (uint32_t)j, temperature, 0, NULL, 0, 0, NULL};
+    m3o_gumbel_argmax(lg, B, m->code_vocab, m->code_vocab, &dp, draw_out, zb, z2);
+    for (int b = 0; b < B; ++b) {
+      codes[b * 8 + j] = draw_out[b];
+      if (tr && tr->zgap) tr->zgap[b * 8 + j] = zb[b] - z2[b];
+    }
+  }
+
+  /* feedback: x' = bf16((E_tok[c0] + sum_j A_j[c_j]) * 8^-1/2) */
+  double scale = 1.0 / sqrt((double)m->n_codebooks);
+  for (int b = 0; b < B; ++b) {
+    int32_t c0 = codes[b * 8] - m->vocab_base;
+    if (c0 < 0 || c0 >= m->V0) c0 = 0;
+    for (int k = 0; k < H; ++k) {
+      double acc = m3o_bf16_to_f64(m->tok_emb_audio[(size_t)c0 * H + k]);
+      for (int j = 1; j < m->n_codebooks; ++j)
+        acc += m3o_bf16_to_f64(m->audio_emb[j - 1][(size_t)codes[b * 8 + j] * H + k]);
+      x_next[(size_t)b * H + k] = m3o_f64_to_bf16(acc * scale);
+    }
+  }
+  free(y); free(h); free(a); free(qkvb); free(o); free(mm); free(u); free(hd);
+  free(lg); free(draw_out); free(zb); free(z2);
+}

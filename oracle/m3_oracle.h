@@ -1,0 +1,140 @@
+/*
+ * m3_oracle.h -- CPU oracle for the per-frame autoregressive decode of a
+ * MiniMax-Music-3-style audio LM (Qwen3-shaped body + RVQ depth decoder).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this code; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * Every routine is plain scalar C in float64 unless a step is defined in fp32
+ * by the method itself (the sampler).  Weights and activations are bf16 bit
+ * patterns (uint16_t), fp32 scales/gammas are float.
+ *
+ * Parity pins: every function here is pinned by a CPU test that does not
+ * re-use this code (exact rational brute force, closed forms, a library
+ * routine, exhaustive sweeps).  The depth-decoder coupling inside
+ * m3o_decode_frame is the one part whose interface the pages do not give:
+ * "parity unpinned" for that coupling beyond its components.
+ */
+#ifndef M3_ORACLE_H
+#define M3_ORACLE_H
+
+#include <stdint.h>
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* weight formats (MiniMax Music 3 Metal port, precision section: bf16,
+   int8 with one scale per row, int8 with one scale per group of 128) */
+enum { M3O_BF16 = 0, M3O_I8ROW = 1, M3O_I8G128 = 2 };
+
+/* ---- bf16 ---------------------------------------------------------- */
+uint16_t m3o_f64_to_bf16(double v);      /* one round-to-nearest-even */
+double   m3o_bf16_to_f64(uint16_t b);
+void     m3o_f64_to_bf16_n(const double* v, uint16_t* out, size_t n);
+void     m3o_f32_to_bf16_n(const float* v, uint16_t* out, size_t n);
+
+/* ---- RMSNorm ------------------------------------------------------- */
+/* a[b,k] = bf16( x[b,k] * r_b * gamma[k] ),  r_b = 1/sqrt(mean_k x^2 + eps).
+   gamma == NULL: a = x (no norm). */
+void m3o_rmsnorm(const uint16_t* x, int B, int K, int ldx, const float* gamma,
+                 float eps, uint16_t* a, int lda);
+
+/* ---- int8 quantisers ------------------------------------------------ */
+/* s_n = fl32(absmax_n / 127); q = clamp(rne(W/s), -127, 127); zero row: s=q=0 */
+void m3o_quant_i8row(const uint16_t* W, int N, int K, int8_t* q, float* s);
+/* the same per (row, group of 128 along K); s is [N, K/128] */
+void m3o_quant_i8g128(const uint16_t* W, int N, int K, int8_t* q, float* s);
+
+/* ---- matrix-vector products (exact fp64 sums, unrounded) ------------ */
+typedef struct {
+  int fmt;              /* M3O_BF16 / M3O_I8ROW / M3O_I8G128 */
+  int N, K;
+  const uint16_t* w;    /* bf16 [N,K]            (fmt == M3O_BF16) */
+  const int8_t* q;      /* int8 [N,K]            (int8 formats)    */
+  const float* s;       /* [N] or [N, K/128]     (int8 formats)    */
+} m3o_mat;
+
+/* y[b*N + n] = sum_k Wdeq[n,k] * a[b,k]; Wdeq = w, s_n*q or s_{n,g}*q */
+void m3o_gemv(const m3o_mat* m, const uint16_t* a, int B, int lda, double* y);
+/* same, rows [row0, row0+nrows) only; y is [B, nrows] */
+void m3o_gemv_rows(const m3o_mat* m, int row0, int nrows, const uint16_t* a,
+                   int B, int lda, double* y);
+
+/* ---- epilogues / attention stub ------------------------------------ */
+/* g = bf16(y[b, 2i]) (gate), u = bf16(y[b, 2i+1]) (up) from interleaved rows;
+   m[b, i] = bf16( g * u / (1 + exp(-g)) ) */
+void m3o_swiglu_interleaved(const double* y, int B, int F, uint16_t* m);
+/* h_out = bf16( h + bf16(y) ) */
+void m3o_residual(const double* y, const uint16_t* h, int n, uint16_t* h_out);
+/* identity attention: o[b, h*hd + d] = qkv[b, voff + (h/group)*hd + d] */
+void m3o_attn_stub(const uint16_t* qkv, int B, int ldq, int voff, int n_heads,
+                   int group, int hd, uint16_t* o);
+
+/* ---- sampler -------------------------------------------------------- */
+void  m3o_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+float m3o_logf(float x);                       /* fixed-sequence fp32 log   */
+float m3o_uniform_from_word(uint32_t w);       /* (2*(w>>9)+1) * 2^-24      */
+float m3o_gumbel(uint64_t seed, uint32_t row, uint32_t frame, uint32_t draw,
+                 uint32_t id);
+typedef struct {
+  uint64_t seed; uint32_t frame; uint32_t draw; float temperature;
+  int32_t index_base; const int32_t* ids; int32_t valid_lo, valid_hi;
+  const float* noise_override;   /* [B, V] (row stride V) or NULL */
+} m3o_sample_params;
+/* out[b] = absolute id of argmax_j z[b,j]; z = fl32(l*fl32(1/T)) + g.
+   zbest/zsecond (optional) receive the best and second-best z of each row
+   (used by tests to judge how close a decision was). */
+void m3o_gumbel_argmax(const float* logits, int B, int V, int ldl,
+                       const m3o_sample_params* p, int32_t* out,
+                       float* zbest, float* zsecond);
+
+/* ---- one decode frame ------------------------------------------------ */
+typedef struct {
+  m3o_mat qkv, o, gu, down;      /* gu: interleaved gate/up rows [2F, H] */
+  const float* attn_norm; const float* ffn_norm;
+} m3o_layer;
+
+typedef struct {
+  /* body */
+  int H, n_layers, n_heads, n_kv_heads, head_dim, F;
+  const m3o_layer* layers;
+  const float* final_norm;
+  m3o_mat lm_head;               /* the reachable slice only [V0, H]  */
+  int32_t vocab_base;            /* absolute id of slice row 0 (151675) */
+  int V0;                        /* rows in the slice (16384)           */
+  /* depth decoder */
+  int D, d_layers, d_heads, d_head_dim, Fd, n_codebooks, code_vocab;
+  m3o_mat p_in;                  /* [D, H] */
+  const uint16_t* emb1;          /* [V0, D] semantic code embedding     */
+  const uint16_t* const* emb;    /* emb[j-2], j = 2..7: [code_vocab, D] */
+  const m3o_layer* d_layers_w;
+  const float* d_final_norm;
+  const m3o_mat* heads;          /* heads[j-1], [code_vocab, D]         */
+  /* feedback */
+  const uint16_t* tok_emb_audio; /* [V0, H]: embed_tokens rows of the audio codes */
+  const uint16_t* const* audio_emb; /* audio_emb[j-1], [code_vocab, H]  */
+  float eps;
+} m3o_model;
+
+typedef struct {
+  uint16_t* h_body;    /* [B, H]  body output before the final norm (optional) */
+  float* logits0;      /* [B, V0] semantic logits (optional)                 */
+  float* zgap;         /* [B, 8]  best - second-best z per draw (optional)    */
+} m3o_frame_trace;
+
+/* codes[b*8 + 0] = absolute semantic id; codes[b*8 + j] = code j in [0,1024).
+   x_next = bf16( (E_tok[c0] + sum_j A_j[c_j]) * 8^-1/2 ). */
+void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
+                      uint64_t seed, uint32_t frame, float temperature,
+                      int32_t* codes, uint16_t* x_next, m3o_frame_trace* tr);
+
+int m3o_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
