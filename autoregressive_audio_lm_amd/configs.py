@@ -26,7 +26,7 @@ SMALL = dict(
     H=512, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=128, F=1008,
     vocab=200000, vocab_base=151675, V0=1000, end_token=151670,
     D=256, d_layers=2, d_heads=2, d_head_dim=128, Fd=384,
-    n_codebooks=8, code_vocab=100, eps=1e-6,
+    n_codebooks=8, code_vocab=104, eps=1e-6,
 )
 
 # weight formats (mirror of the C enum)

@@ -1,0 +1,524 @@
+// capi.cpp -- the C ABI of libm3: host-side validation, then launches.
+//
+// Every entry point checks its arguments before touching the GPU and returns
+// a negative m3_status without enqueuing anything when they fall outside the
+// supported set (TensorFold PR #987, "Kernel contract": unsupported edges are
+// refused; DiffSynth-Studio's MiniMax-Music3 parameters: invalid input raises
+// instead of proceeding).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "m3_internal.h"
+
+using namespace m3;
+
+namespace {
+
+constexpr size_t kLdsMax = 160 * 1024;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int k_ok(int fmt, int K) {
+  if (K < 8) return 0;
+  switch (fmt) {
+    case M3_BF16: return K % 8 == 0;
+    case M3_I8ROW: return K % 16 == 0;
+    case M3_I8G128: return K % 128 == 0;
+    default: return 0;
+  }
+}
+
+bool fmt_ok(int fmt) { return fmt == M3_BF16 || fmt == M3_I8ROW || fmt == M3_I8G128; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? M3_OK : M3_ERR_HIP; }
+
+// [a0, a1) and [b0, b1) overlap?
+bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+int validate_gemv(int fmt, const void* w, int N, int K, const uint16_t* x, int B, int ldx,
+                  const float* gamma, float eps, int stub_group, int stub_voff, void* y,
+                  int ldy, int out_dtype, int epi, const uint16_t* res, int ldr) {
+  if (!w || !x || !y) return M3_ERR_NULL;
+  if (!fmt_ok(fmt)) return M3_ERR_FORMAT;
+  if (out_dtype != M3_OUT_BF16 && out_dtype != M3_OUT_F32) return M3_ERR_FORMAT;
+  if (epi != M3_EPI_NONE && epi != M3_EPI_SWIGLU && epi != M3_EPI_RESIDUAL) return M3_ERR_FORMAT;
+  if (epi != M3_EPI_NONE && out_dtype != M3_OUT_BF16) return M3_ERR_FORMAT;
+  if (N < 1 || !k_ok(fmt, K) || B < 1 || B > M3_MAX_B) return M3_ERR_SHAPE;
+  if (epi == M3_EPI_SWIGLU && (N % 2) != 0) return M3_ERR_SHAPE;
+  if (epi == M3_EPI_RESIDUAL && !res) return M3_ERR_NULL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return M3_ERR_SHAPE;
+  // operand columns read from x
+  long need_ldx = K;
+  if (stub_group < 0) return M3_ERR_SHAPE;
+  if (stub_group > 0) {
+    if (K % 128 != 0 || (K / 128) % stub_group != 0 || stub_voff < 0 || stub_voff % 8 != 0)
+      return M3_ERR_SHAPE;
+    need_ldx = (long)stub_voff + (long)(K / 128 / stub_group) * 128;
+  }
+  if (ldx < need_ldx) return M3_ERR_SHAPE;
+  const int ncols = epi == M3_EPI_SWIGLU ? N / 2 : N;
+  if (ldy < ncols) return M3_ERR_SHAPE;
+  if (epi == M3_EPI_RESIDUAL && ldr < N) return M3_ERR_SHAPE;
+  if (ldx % 8 != 0 || ldy % 8 != 0 || (epi == M3_EPI_RESIDUAL && ldr % 8 != 0)) return M3_ERR_ALIGN;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16)) return M3_ERR_ALIGN;
+  if (gamma && !aligned(gamma, 16)) return M3_ERR_ALIGN;
+  if (res && !aligned(res, 16)) return M3_ERR_ALIGN;
+  if (gamma && (long)B * k_pad(fmt, K) > kMaxNormElems) return M3_ERR_SHAPE;
+  if (gemv_smem_bytes(fmt, K, B, gamma != nullptr) > kLdsMax) return M3_ERR_SHAPE;
+  // x is read by every workgroup while outputs are written: no overlap
+  const size_t esz = out_dtype == M3_OUT_F32 ? 4 : 2;
+  const size_t xbytes = ((size_t)(B - 1) * ldx + need_ldx) * 2;
+  const size_t ybytes = ((size_t)(B - 1) * ldy + ncols) * esz;
+  if (overlap(x, xbytes, y, ybytes)) return M3_ERR_ALIAS;
+  if (epi == M3_EPI_RESIDUAL && res != y) {
+    const size_t rbytes = ((size_t)(B - 1) * ldr + N) * 2;
+    if (overlap(res, rbytes, y, ybytes)) return M3_ERR_ALIAS;
+  }
+  if (epi == M3_EPI_RESIDUAL && res == y && ldr != ldy) return M3_ERR_ALIAS;
+  return M3_OK;
+}
+
+int gemv_entry(int fmt, const void* w, int N, int K, const uint16_t* x, int B, int ldx,
+               const float* gamma, float eps, int stub_group, int stub_voff, void* y, int ldy,
+               int out_dtype, int epi, const uint16_t* res, int ldr, void* stream) {
+  const int st = validate_gemv(fmt, w, N, K, x, B, ldx, gamma, eps, stub_group, stub_voff, y,
+                               ldy, out_dtype, epi, res, ldr);
+  if (st != M3_OK) return st;
+  GemvDesc d{fmt, w, N, K, x, ldx, B, gamma, eps, stub_group, stub_voff, y, ldy,
+             out_dtype == M3_OUT_F32, epi, res, ldr};
+  return hip_status(launch_gemv(d, static_cast<hipStream_t>(stream)));
+}
+
+// ---- frame -------------------------------------------------------------------
+struct Dims {
+  int H, nq, nkv, nqkv, F, D, dq, dqkv, Fd, V0, CV, ncb;
+};
+
+Dims dims_of(const m3_config& c) {
+  Dims d;
+  d.H = c.hidden;
+  d.nq = c.n_heads * c.head_dim;
+  d.nkv = c.n_kv_heads * c.head_dim;
+  d.nqkv = d.nq + 2 * d.nkv;
+  d.F = c.ffn;
+  d.D = c.d_hidden;
+  d.dq = c.d_heads * c.d_head_dim;
+  d.dqkv = 3 * d.dq;
+  d.Fd = c.d_ffn;
+  d.V0 = c.n_slice;
+  d.CV = c.code_vocab;
+  d.ncb = c.n_codebooks;
+  return d;
+}
+
+uint64_t mat_bytes(int fmt, uint64_t N, uint64_t K) {
+  if (fmt == M3_BF16) return 2 * N * K;
+  if (fmt == M3_I8ROW) return N * K + 4 * N;
+  return N * K + 4 * N * (K / 128);
+}
+
+int validate_config(const m3_config* c, int B) {
+  if (!c) return M3_ERR_NULL;
+  if (!fmt_ok(c->fmt_body) || !fmt_ok(c->fmt_depth)) return M3_ERR_FORMAT;
+  if (c->fmt_lm != M3_BF16 && c->fmt_lm != M3_I8ROW) return M3_ERR_FORMAT;
+  if (B < 1 || B > M3_MAX_B_FRAME) return M3_ERR_SHAPE;
+  if (c->n_layers < 1 || c->d_layers < 1) return M3_ERR_SHAPE;
+  if (c->head_dim != 128 || c->d_head_dim != 128) return M3_ERR_SHAPE;
+  if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return M3_ERR_SHAPE;
+  if (c->d_heads < 1) return M3_ERR_SHAPE;
+  if (c->n_codebooks < 2 || c->n_codebooks > 8) return M3_ERR_SHAPE;
+  if (c->n_slice < 1 || c->code_vocab < 1 || c->vocab_base < 0) return M3_ERR_SHAPE;
+  if (!(c->temperature > 0.0f) || !std::isfinite(c->temperature)) return M3_ERR_SHAPE;
+  if (!(c->eps >= 0.0f) || !std::isfinite(c->eps)) return M3_ERR_SHAPE;
+  const Dims d = dims_of(*c);
+  const int fb = c->fmt_body, fd = c->fmt_depth;
+  // every K a GEMV of the frame contracts over
+  if (!k_ok(fb, d.H) || !k_ok(fb, d.nq) || !k_ok(fb, d.F)) return M3_ERR_SHAPE;
+  if (!k_ok(c->fmt_lm, d.H) || !k_ok(fd, d.H)) return M3_ERR_SHAPE;
+  if (!k_ok(fd, d.D) || !k_ok(fd, d.dq) || !k_ok(fd, d.Fd)) return M3_ERR_SHAPE;
+  // leading dimensions are multiples of 8 elements
+  if (d.H % 8 || d.nqkv % 8 || d.F % 8 || d.D % 8 || d.dqkv % 8 || d.Fd % 8 || d.V0 % 8 ||
+      d.CV % 8)
+    return M3_ERR_SHAPE;
+  // norm-fused GEMVs must fit LDS
+  if ((long)B * k_pad(fb, d.H) > kMaxNormElems || (long)B * k_pad(fd, d.D) > kMaxNormElems ||
+      (long)B * k_pad(c->fmt_lm, d.H) > kMaxNormElems || (long)B * k_pad(fd, d.H) > kMaxNormElems)
+    return M3_ERR_SHAPE;
+  if (gemv_smem_bytes(fb, d.H, B, true) > kLdsMax || gemv_smem_bytes(c->fmt_lm, d.H, B, true) > kLdsMax ||
+      gemv_smem_bytes(fd, d.H, B, true) > kLdsMax || gemv_smem_bytes(fd, d.D, B, true) > kLdsMax)
+    return M3_ERR_SHAPE;
+  return M3_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+m3_frame_layout layout_of(const m3_config& c, int B) {
+  const Dims d = dims_of(c);
+  m3_frame_layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.x = take((size_t)B * d.H * 2);
+  L.h = take((size_t)B * d.H * 2);
+  L.qkv = take((size_t)B * d.nqkv * 2);
+  L.mlp = take((size_t)B * d.F * 2);
+  L.logits = take((size_t)B * d.V0 * 4);
+  L.u = take((size_t)B * d.D * 2);
+  L.hd = take((size_t)B * d.D * 2);
+  L.dqkv = take((size_t)B * d.dqkv * 2);
+  L.dmlp = take((size_t)B * d.Fd * 2);
+  L.dlogits = take((size_t)B * d.CV * 4);
+  L.ring = take((size_t)16 * B * 8 * 4);
+  L.frame = take(4);
+  const size_t ws0 = sample_ws_bytes(B, d.V0), ws1 = sample_ws_bytes(B, d.CV);
+  L.sample_ws = take(ws0 > ws1 ? ws0 : ws1);
+  L.total = off;
+  return L;
+}
+
+int validate_model(const m3_model* m) {
+  if (!m || !m->layers || !m->final_norm || !m->lm_head || !m->p_in || !m->emb1 ||
+      !m->d_layers_w || !m->d_final_norm || !m->heads || !m->tok_emb_audio || !m->audio_emb)
+    return M3_ERR_NULL;
+  if (m->cfg.n_codebooks > 2 && !m->emb) return M3_ERR_NULL;
+  for (int l = 0; l < m->cfg.n_layers; ++l) {
+    const m3_layer_weights& L = m->layers[l];
+    if (!L.qkv || !L.o || !L.gate_up || !L.down || !L.attn_norm || !L.ffn_norm) return M3_ERR_NULL;
+  }
+  for (int l = 0; l < m->cfg.d_layers; ++l) {
+    const m3_layer_weights& L = m->d_layers_w[l];
+    if (!L.qkv || !L.o || !L.gate_up || !L.down || !L.attn_norm || !L.ffn_norm) return M3_ERR_NULL;
+  }
+  for (int j = 0; j < m->cfg.n_codebooks - 1; ++j)
+    if (!m->heads[j] || !m->audio_emb[j]) return M3_ERR_NULL;
+  for (int j = 0; j < m->cfg.n_codebooks - 2; ++j)
+    if (!m->emb[j]) return M3_ERR_NULL;
+  return M3_OK;
+}
+
+#define M3_TRY(expr)                         \
+  do {                                       \
+    const hipError_t e_ = (expr);            \
+    if (e_ != hipSuccess) return M3_ERR_HIP; \
+  } while (0)
+
+int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStream_t s) {
+  const m3_config& c = m->cfg;
+  const Dims d = dims_of(c);
+  const m3_frame_layout L = layout_of(c, B);
+  uint16_t* x = reinterpret_cast<uint16_t*>(S + L.x);
+  uint16_t* h = reinterpret_cast<uint16_t*>(S + L.h);
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(S + L.qkv);
+  uint16_t* mlp = reinterpret_cast<uint16_t*>(S + L.mlp);
+  float* logits = reinterpret_cast<float*>(S + L.logits);
+  uint16_t* u = reinterpret_cast<uint16_t*>(S + L.u);
+  uint16_t* hd = reinterpret_cast<uint16_t*>(S + L.hd);
+  uint16_t* dqkv = reinterpret_cast<uint16_t*>(S + L.dqkv);
+  uint16_t* dmlp = reinterpret_cast<uint16_t*>(S + L.dmlp);
+  float* dlogits = reinterpret_cast<float*>(S + L.dlogits);
+  int32_t* ring = reinterpret_cast<int32_t*>(S + L.ring);
+  uint32_t* frame = reinterpret_cast<uint32_t*>(S + L.frame);
+  void* ws = S + L.sample_ws;
+  const float eps = c.eps;
+  auto gemv = [&](int fmt, const void* w, int N, int K, const uint16_t* xin, int ldx,
+                  const float* gamma, int sg, int sv, void* y, int ldy, int f32, int epi,
+                  const uint16_t* res, int ldr) {
+    GemvDesc g{fmt, w, N, K, xin, ldx, B, gamma, eps, sg, sv, y, ldy, f32, epi, res, ldr};
+    return launch_gemv(g, s);
+  };
+  // ---- body ----
+  const int group = c.n_heads / c.n_kv_heads;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const m3_layer_weights& W = m->layers[l];
+    const uint16_t* xin = l == 0 ? x : h;
+    M3_TRY(gemv(c.fmt_body, W.qkv, d.nqkv, d.H, xin, d.H, W.attn_norm, 0, 0, qkv, d.nqkv, 0,
+                M3_EPI_NONE, nullptr, 0));
+    M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, qkv, d.nqkv, nullptr, group, d.nq + d.nkv, h, d.H, 0,
+                M3_EPI_RESIDUAL, xin, d.H));
+    M3_TRY(gemv(c.fmt_body, W.gate_up, 2 * d.F, d.H, h, d.H, W.ffn_norm, 0, 0, mlp, d.F, 0,
+                M3_EPI_SWIGLU, nullptr, 0));
+    M3_TRY(gemv(c.fmt_body, W.down, d.H, d.F, mlp, d.F, nullptr, 0, 0, h, d.H, 0,
+                M3_EPI_RESIDUAL, h, d.H));
+  }
+  // ---- sliced lm_head + semantic draw ----
+  M3_TRY(gemv(c.fmt_lm, m->lm_head, d.V0, d.H, h, d.H, m->final_norm, 0, 0, logits, d.V0, 1,
+              M3_EPI_NONE, nullptr, 0));
+  SampleDesc sd{};
+  sd.logits = logits;
+  sd.B = B;
+  sd.V = d.V0;
+  sd.ldl = d.V0;
+  sd.seed = c.seed;
+  sd.frame_dev = frame;
+  sd.draw = 0;
+  sd.temperature = c.temperature;
+  sd.index_base = c.vocab_base;
+  sd.valid_lo = c.vocab_base;
+  sd.valid_hi = c.vocab_base + c.n_slice;
+  sd.out = codes;
+  sd.out_stride = 8;
+  sd.ws = ws;
+  M3_TRY(launch_sample(sd, s));
+  // ---- depth decoder ----
+  M3_TRY(gemv(c.fmt_depth, m->p_in, d.D, d.H, h, d.H, m->final_norm, 0, 0, u, d.D, 0,
+              M3_EPI_NONE, nullptr, 0));
+  for (int j = 1; j < d.ncb; ++j) {
+    const uint16_t* E = j == 1 ? m->emb1 : m->emb[j - 2];
+    M3_TRY(launch_depth_input(u, E, codes, j - 1, j == 1 ? c.vocab_base : 0,
+                              j == 1 ? c.n_slice : c.code_vocab, B, d.D, hd, s));
+    for (int l = 0; l < c.d_layers; ++l) {
+      const m3_layer_weights& W = m->d_layers_w[l];
+      M3_TRY(gemv(c.fmt_depth, W.qkv, d.dqkv, d.D, hd, d.D, W.attn_norm, 0, 0, dqkv, d.dqkv, 0,
+                  M3_EPI_NONE, nullptr, 0));
+      M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd, d.D, 0,
+                  M3_EPI_RESIDUAL, hd, d.D));
+      M3_TRY(gemv(c.fmt_depth, W.gate_up, 2 * d.Fd, d.D, hd, d.D, W.ffn_norm, 0, 0, dmlp, d.Fd, 0,
+                  M3_EPI_SWIGLU, nullptr, 0));
+      M3_TRY(gemv(c.fmt_depth, W.down, d.D, d.Fd, dmlp, d.Fd, nullptr, 0, 0, hd, d.D, 0,
+                  M3_EPI_RESIDUAL, hd, d.D));
+    }
+    M3_TRY(gemv(c.fmt_depth, m->heads[j - 1], d.CV, d.D, hd, d.D, m->d_final_norm, 0, 0, dlogits,
+                d.CV, 1, M3_EPI_NONE, nullptr, 0));
+    SampleDesc dd = sd;
+    dd.logits = dlogits;
+    dd.V = d.CV;
+    dd.ldl = d.CV;
+    dd.draw = (uint32_t)j;
+    dd.index_base = 0;
+    dd.valid_lo = dd.valid_hi = 0;
+    dd.out = codes + j;
+    M3_TRY(launch_sample(dd, s));
+  }
+  // ---- feedback, code ring, frame counter ----
+  M3_TRY(launch_feedback(m->tok_emb_audio, m->audio_emb, codes, c.vocab_base, c.n_slice,
+                         c.code_vocab, d.ncb, B, d.H, x, ring, frame, s));
+  return M3_OK;
+}
+
+struct FrameGraph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* m3_status_str(int status) {
+  switch (status) {
+    case M3_OK: return "ok";
+    case M3_ERR_NULL: return "a required pointer is NULL";
+    case M3_ERR_SHAPE: return "a size is outside the supported set";
+    case M3_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
+    case M3_ERR_FORMAT: return "unknown weight format, epilogue or output type";
+    case M3_ERR_WORKSPACE: return "workspace too small";
+    case M3_ERR_HIP: return "a HIP call failed";
+    case M3_ERR_ALIAS: return "an input overlaps an output";
+    default: return "unknown status";
+  }
+}
+
+const char* m3_version(void) { return "m3 0.1.0 gfx950"; }
+
+size_t m3_packed_bytes(int fmt, int N, int K, int flags) {
+  if (!fmt_ok(fmt) || N < 1 || !k_ok(fmt, K)) return 0;
+  if (flags & ~M3_PACK_GLU_INTERLEAVE) return 0;
+  if ((flags & M3_PACK_GLU_INTERLEAVE) && (N % 2) != 0) return 0;
+  return (size_t)n_blocks(N) * block_bytes(fmt, K);
+}
+
+int m3_pack(int fmt, const uint16_t* W, int N, int K, int flags, void* packed, void* stream) {
+  if (!W || !packed) return M3_ERR_NULL;
+  if (!fmt_ok(fmt)) return M3_ERR_FORMAT;
+  if (m3_packed_bytes(fmt, N, K, flags) == 0) return M3_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(packed, 16)) return M3_ERR_ALIGN;
+  if (overlap(W, (size_t)N * K * 2, packed, m3_packed_bytes(fmt, N, K, flags))) return M3_ERR_ALIAS;
+  return hip_status(launch_pack(fmt, W, N, K, flags, packed, static_cast<hipStream_t>(stream)));
+}
+
+int m3_rmsnorm_gemv(const void* w, int N, int K, const uint16_t* x, int B, int ldx,
+                    const float* gamma, float eps, int stub_group, int stub_voff, void* y, int ldy,
+                    int out_dtype, int epi, const uint16_t* res, int ldr, void* stream) {
+  return gemv_entry(M3_BF16, w, N, K, x, B, ldx, gamma, eps, stub_group, stub_voff, y, ldy,
+                    out_dtype, epi, res, ldr, stream);
+}
+
+int m3_gemv_i8row(const void* w, int N, int K, const uint16_t* x, int B, int ldx,
+                  const float* gamma, float eps, int stub_group, int stub_voff, void* y, int ldy,
+                  int out_dtype, int epi, const uint16_t* res, int ldr, void* stream) {
+  return gemv_entry(M3_I8ROW, w, N, K, x, B, ldx, gamma, eps, stub_group, stub_voff, y, ldy,
+                    out_dtype, epi, res, ldr, stream);
+}
+
+int m3_gemv_i8g128(const void* w, int N, int K, const uint16_t* x, int B, int ldx,
+                   const float* gamma, float eps, int stub_group, int stub_voff, void* y, int ldy,
+                   int out_dtype, int epi, const uint16_t* res, int ldr, void* stream) {
+  return gemv_entry(M3_I8G128, w, N, K, x, B, ldx, gamma, eps, stub_group, stub_voff, y, ldy,
+                    out_dtype, epi, res, ldr, stream);
+}
+
+int m3_lmhead_sliced(int fmt, const void* packed_slice, int n_rows, int K, const uint16_t* x,
+                     int B, int ldx, const float* gamma, float eps, float* logits, int ldl,
+                     void* stream) {
+  if (fmt != M3_BF16 && fmt != M3_I8ROW) return M3_ERR_FORMAT;
+  if (ldl % 4 != 0) return M3_ERR_ALIGN;
+  const int st = validate_gemv(fmt, packed_slice, n_rows, K, x, B, ldx, gamma, eps, 0, 0, logits,
+                               ldl, M3_OUT_F32, M3_EPI_NONE, nullptr, 0);
+  if (st != M3_OK) return st;
+  GemvDesc d{fmt, packed_slice, n_rows, K, x, ldx, B, gamma, eps, 0, 0, logits, ldl, 1,
+             M3_EPI_NONE, nullptr, 0};
+  return hip_status(launch_gemv(d, static_cast<hipStream_t>(stream)));
+}
+
+size_t m3_gumbel_workspace_bytes(int B, int V) {
+  if (B < 1 || B > M3_MAX_B || V < 1 || V > (1 << 24)) return 0;
+  return sample_ws_bytes(B, V);
+}
+
+int m3_gumbel_argmax(const float* logits, int B, int V, int ldl, const m3_sample_params* p,
+                     int32_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !p || !out || !ws) return M3_ERR_NULL;
+  if (B < 1 || B > M3_MAX_B || V < 1 || V > (1 << 24) || ldl < V) return M3_ERR_SHAPE;
+  if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return M3_ERR_SHAPE;
+  if (ldl % 4 != 0 || !aligned(logits, 16) || !aligned(ws, 16) || !aligned(out, 4))
+    return M3_ERR_ALIGN;
+  if (ws_bytes < sample_ws_bytes(B, V)) return M3_ERR_WORKSPACE;
+  SampleDesc d{};
+  d.logits = logits;
+  d.B = B;
+  d.V = V;
+  d.ldl = ldl;
+  d.seed = p->seed;
+  d.frame = p->frame;
+  d.frame_dev = p->frame_dev;
+  d.draw = p->draw;
+  d.temperature = p->temperature;
+  d.index_base = p->index_base;
+  d.ids = p->ids;
+  d.valid_lo = p->valid_lo;
+  d.valid_hi = p->valid_hi;
+  d.noise = p->noise_override;
+  d.out = out;
+  d.out_stride = 1;
+  d.ws = ws;
+  return hip_status(launch_sample(d, static_cast<hipStream_t>(stream)));
+}
+
+uint64_t m3_frame_weight_bytes(const m3_config* c) {
+  if (!c) return 0;
+  const Dims d = dims_of(*c);
+  const int fb = c->fmt_body, fd = c->fmt_depth;
+  const uint64_t layer = mat_bytes(fb, d.nqkv, d.H) + mat_bytes(fb, d.H, d.nq) +
+                         mat_bytes(fb, 2ull * d.F, d.H) + mat_bytes(fb, d.H, d.F);
+  uint64_t total = (uint64_t)c->n_layers * layer + 4ull * d.H * (2ull * c->n_layers + 1);
+  total += mat_bytes(c->fmt_lm, d.V0, d.H);
+  total += mat_bytes(fd, d.D, d.H);
+  const uint64_t dlayer = mat_bytes(fd, d.dqkv, d.D) + mat_bytes(fd, d.D, d.dq) +
+                          mat_bytes(fd, 2ull * d.Fd, d.D) + mat_bytes(fd, d.D, d.Fd);
+  const uint64_t step = (uint64_t)c->d_layers * dlayer + mat_bytes(fd, d.CV, d.D) +
+                        4ull * d.D * (2ull * c->d_layers + 1);
+  total += (uint64_t)(d.ncb - 1) * step;
+  return total;
+}
+
+int m3_frame_layout_get(const m3_config* cfg, int B, m3_frame_layout* out) {
+  if (!out) return M3_ERR_NULL;
+  const int st = validate_config(cfg, B);
+  if (st != M3_OK) return st;
+  *out = layout_of(*cfg, B);
+  return M3_OK;
+}
+
+size_t m3_frame_workspace_bytes(const m3_config* cfg, int B) {
+  if (validate_config(cfg, B) != M3_OK) return 0;
+  return layout_of(*cfg, B).total;
+}
+
+int m3_frame_state_init(const m3_config* cfg, int B, void* state, const uint16_t* x0,
+                        uint32_t frame0, void* stream) {
+  if (!state || !x0) return M3_ERR_NULL;
+  const int st = validate_config(cfg, B);
+  if (st != M3_OK) return st;
+  if (!aligned(state, 256) || !aligned(x0, 16)) return M3_ERR_ALIGN;
+  const m3_frame_layout L = layout_of(*cfg, B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* S = static_cast<uint8_t*>(state);
+  M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S), 0u, L.total / 4, s));
+  M3_TRY(launch_copy_bf16(x0, reinterpret_cast<uint16_t*>(S + L.x), (size_t)B * cfg->hidden, s));
+  M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S + L.frame), frame0, 1, s));
+  return M3_OK;
+}
+
+int m3_decode_frame_weights(const m3_model* model, void* state, int B, int32_t* codes,
+                            uint64_t* bytes_read, void* stream) {
+  if (!model || !state || !codes) return M3_ERR_NULL;
+  int st = validate_config(&model->cfg, B);
+  if (st != M3_OK) return st;
+  st = validate_model(model);
+  if (st != M3_OK) return st;
+  if (!aligned(state, 256) || !aligned(codes, 16)) return M3_ERR_ALIGN;
+  if (bytes_read) *bytes_read = m3_frame_weight_bytes(&model->cfg);
+  return enqueue_frame(model, static_cast<uint8_t*>(state), B, codes,
+                       static_cast<hipStream_t>(stream));
+}
+
+int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* codes, void* stream,
+                          void** graph_out) {
+  if (!model || !state || !codes || !graph_out) return M3_ERR_NULL;
+  int st = validate_config(&model->cfg, B);
+  if (st != M3_OK) return st;
+  st = validate_model(model);
+  if (st != M3_OK) return st;
+  if (!aligned(state, 256) || !aligned(codes, 16)) return M3_ERR_ALIGN;
+  if (!stream) return M3_ERR_NULL;   // the legacy default stream cannot be captured
+  M3_TRY(gemv_prepare());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  M3_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+  const int est = enqueue_frame(model, static_cast<uint8_t*>(state), B, codes, s);
+  hipGraph_t g = nullptr;
+  const hipError_t ce = hipStreamEndCapture(s, &g);
+  if (est != M3_OK || ce != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return est != M3_OK ? est : M3_ERR_HIP;
+  }
+  hipGraphExec_t ex = nullptr;
+  if (hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return M3_ERR_HIP;
+  }
+  FrameGraph* fg = new (std::nothrow) FrameGraph{g, ex};
+  if (!fg) {
+    (void)hipGraphExecDestroy(ex);
+    (void)hipGraphDestroy(g);
+    return M3_ERR_HIP;
+  }
+  *graph_out = fg;
+  return M3_OK;
+}
+
+int m3_frame_graph_launch(void* graph, void* stream) {
+  if (!graph) return M3_ERR_NULL;
+  FrameGraph* fg = static_cast<FrameGraph*>(graph);
+  return hip_status(hipGraphLaunch(fg->exec, static_cast<hipStream_t>(stream)));
+}
+
+int m3_frame_graph_destroy(void* graph) {
+  if (!graph) return M3_ERR_NULL;
+  FrameGraph* fg = static_cast<FrameGraph*>(graph);
+  const hipError_t a = hipGraphExecDestroy(fg->exec);
+  const hipError_t b = hipGraphDestroy(fg->graph);
+  delete fg;
+  return (a == hipSuccess && b == hipSuccess) ? M3_OK : M3_ERR_HIP;
+}
+
+}  // extern "C"

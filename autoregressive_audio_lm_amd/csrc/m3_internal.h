@@ -1,0 +1,88 @@
+// m3_internal.h -- shared declarations of the HIP library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/m3.h"
+
+namespace m3 {
+
+// ---- packed weight layout (see m3.h, "Packed layout") ----------------------
+constexpr int kTileBytes = 1024;   // 16 rows x 64 bytes
+constexpr int kRowsPerBlock = 16;
+
+__host__ __device__ inline int tile_k(int fmt) { return fmt == M3_BF16 ? 32 : 64; }
+__host__ __device__ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
+__host__ __device__ inline int k_pad(int fmt, int K) { return round_up(K, tile_k(fmt)); }
+__host__ __device__ inline int n_tiles(int fmt, int K) { return k_pad(fmt, K) / tile_k(fmt); }
+__host__ __device__ inline int n_blocks(int N) { return (N + kRowsPerBlock - 1) / kRowsPerBlock; }
+__host__ __device__ inline int scale_bytes(int fmt, int K) {
+  return fmt == M3_I8ROW ? 128 : (fmt == M3_I8G128 ? round_up((K / 128) * 64, 128) : 0);
+}
+__host__ __device__ inline size_t block_bytes(int fmt, int K) {
+  return (size_t)n_tiles(fmt, K) * kTileBytes + scale_bytes(fmt, K);
+}
+
+// ---- GEMV launch description -------------------------------------------------
+struct GemvDesc {
+  int fmt;
+  const void* w;
+  int N, K;
+  const uint16_t* x;
+  int ldx, B;
+  const float* gamma;
+  float eps;
+  int stub_group, stub_voff;
+  void* y;
+  int ldy, out_f32;
+  int epi;
+  const uint16_t* res;
+  int ldr;
+};
+
+// Largest fused-norm activation block held in LDS (elements of B * K_pad).
+constexpr int kMaxNormElems = 65536;
+
+hipError_t launch_gemv(const GemvDesc& d, hipStream_t s);
+// dynamic LDS bytes launch_gemv uses for (fmt, K, B, fused norm); > 160 KiB = unsupported
+size_t gemv_smem_bytes(int fmt, int K, int B, bool has_gamma);
+// set kernel attributes of every GEMV instantiation (before graph capture)
+hipError_t gemv_prepare();
+hipError_t launch_pack(int fmt, const uint16_t* W, int N, int K, int flags, void* packed,
+                       hipStream_t s);
+
+// ---- sampler -----------------------------------------------------------------
+struct SampleDesc {
+  const float* logits;
+  int B, V, ldl;
+  uint64_t seed;
+  uint32_t frame;
+  const uint32_t* frame_dev;
+  uint32_t draw;
+  float temperature;
+  int32_t index_base;
+  const int32_t* ids;
+  int32_t valid_lo, valid_hi;
+  const float* noise;
+  int32_t* out;
+  int out_stride;       // out[b * out_stride]
+  void* ws;
+};
+size_t sample_ws_bytes(int B, int V);
+hipError_t launch_sample(const SampleDesc& d, hipStream_t s);
+
+// ---- frame helpers -------------------------------------------------------------
+hipError_t launch_depth_input(const uint16_t* u, const uint16_t* emb, const int32_t* codes,
+                              int code_col, int32_t code_base, int n_codes, int B, int D,
+                              uint16_t* out, hipStream_t s);
+// audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)
+hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const* audio_emb,
+                           const int32_t* codes, int32_t vocab_base, int n_slice,
+                           int code_vocab, int n_cb, int B, int H, uint16_t* x_out, int32_t* ring,
+                           uint32_t* frame, hipStream_t s);
+hipError_t launch_copy_bf16(const uint16_t* src, uint16_t* dst, size_t n, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, size_t n, hipStream_t s);
+
+}  // namespace m3

@@ -1,0 +1,132 @@
+"""Python binding of the libm3 C ABI, same names as the C entry points.
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every step runs in libm3's kernels.  Validation refusals
+raise ValueError (M3ValueError), HIP failures RuntimeError (M3Error).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (BF16, I8ROW, I8G128, EPI_NONE, EPI_SWIGLU, EPI_RESIDUAL, OUT_BF16, OUT_F32,
+                   PACK_GLU_INTERLEAVE, check, lib)
+
+__all__ = ["packed_bytes", "pack", "rmsnorm_gemv", "gemv_i8row", "gemv_i8g128", "gemv",
+           "lmhead_sliced", "gumbel_workspace_bytes", "gumbel_argmax", "BF16", "I8ROW", "I8G128",
+           "EPI_NONE", "EPI_SWIGLU", "EPI_RESIDUAL", "OUT_BF16", "OUT_F32", "PACK_GLU_INTERLEAVE"]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _cuda(t, name):
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def packed_bytes(fmt: int, N: int, K: int, flags: int = 0) -> int:
+    return int(lib().m3_packed_bytes(fmt, N, K, flags))
+
+
+def pack(fmt: int, W: torch.Tensor, flags: int = 0, out: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """Quantise (int8 formats) and pack a bf16 [N, K] weight on the GPU."""
+    _cuda(W, "W")
+    if W.dtype != torch.bfloat16 or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous bf16 [N, K] tensor")
+    N, K = W.shape
+    nb = packed_bytes(fmt, N, K, flags)
+    if nb == 0:
+        raise ValueError(f"unsupported pack shape fmt={fmt} N={N} K={K} flags={flags}")
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=W.device)
+    check(lib().m3_pack(fmt, _ptr(W), N, K, flags, _ptr(out), _stream(stream)))
+    return out
+
+
+_GEMV = {BF16: "m3_rmsnorm_gemv", I8ROW: "m3_gemv_i8row", I8G128: "m3_gemv_i8g128"}
+
+
+def gemv(fmt: int, packed: torch.Tensor, N: int, K: int, x: torch.Tensor,
+         gamma: torch.Tensor | None = None, eps: float = 1e-6, stub_group: int = 0,
+         stub_voff: int = 0, y: torch.Tensor | None = None, out_dtype: int = OUT_BF16,
+         epi: int = EPI_NONE, residual: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = epi(W . rmsnorm(x; gamma, eps)) through the C ABI (see m3.h)."""
+    for t, n in ((packed, "packed"), (x, "x"), (gamma, "gamma"), (y, "y"), (residual, "residual")):
+        _cuda(t, n)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a bf16 [B, ldx] tensor")
+    B = x.shape[0]
+    ncols = N // 2 if epi == EPI_SWIGLU else N
+    if y is None:
+        y = torch.empty(B, ncols, dtype=torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+                        device=x.device)
+    ldr = residual.stride(0) if residual is not None else 0
+    check(getattr(lib(), _GEMV[fmt])(
+        _ptr(packed), N, K, _ptr(x), B, x.stride(0), _ptr(gamma), float(eps), stub_group, stub_voff,
+        _ptr(y), y.stride(0), out_dtype, epi, _ptr(residual), ldr, _stream(stream)))
+    return y
+
+
+def rmsnorm_gemv(packed, N, K, x, **kw):
+    return gemv(BF16, packed, N, K, x, **kw)
+
+
+def gemv_i8row(packed, N, K, x, **kw):
+    return gemv(I8ROW, packed, N, K, x, **kw)
+
+
+def gemv_i8g128(packed, N, K, x, **kw):
+    return gemv(I8G128, packed, N, K, x, **kw)
+
+
+def lmhead_sliced(fmt: int, packed: torch.Tensor, n_rows: int, K: int, x: torch.Tensor,
+                  gamma: torch.Tensor | None, eps: float = 1e-6,
+                  logits: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _cuda(packed, "packed")
+    _cuda(x, "x")
+    _cuda(gamma, "gamma")
+    B = x.shape[0]
+    if logits is None:
+        logits = torch.empty(B, n_rows, dtype=torch.float32, device=x.device)
+    check(lib().m3_lmhead_sliced(fmt, _ptr(packed), n_rows, K, _ptr(x), B, x.stride(0),
+                                 _ptr(gamma), float(eps), _ptr(logits), logits.stride(0),
+                                 _stream(stream)))
+    return logits
+
+
+def gumbel_workspace_bytes(B: int, V: int) -> int:
+    return int(lib().m3_gumbel_workspace_bytes(B, V))
+
+
+def gumbel_argmax(logits: torch.Tensor, seed: int = 0, frame: int = 0, draw: int = 0,
+                  temperature: float = 1.0, index_base: int = 0, ids: torch.Tensor | None = None,
+                  valid=(0, 0), noise: torch.Tensor | None = None,
+                  frame_dev: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    for t, n in ((logits, "logits"), (ids, "ids"), (noise, "noise"), (frame_dev, "frame_dev"),
+                 (out, "out"), (workspace, "workspace")):
+        _cuda(t, n)
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be a float32 [B, V] tensor")
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    need = gumbel_workspace_bytes(B, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+    p = _lib.SampleParams(int(seed) & (2**64 - 1), int(frame), _ptr(frame_dev), int(draw),
+                          float(temperature), int(index_base), _ptr(ids), int(valid[0]),
+                          int(valid[1]), _ptr(noise))
+    check(lib().m3_gumbel_argmax(_ptr(logits), B, V, logits.stride(0), ctypes.byref(p), _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

@@ -1,0 +1,270 @@
+/*
+ * m3.h -- C ABI of libm3: the per-frame autoregressive decode hot path of a
+ * MiniMax-Music-3-style audio LM (Qwen3-shaped body + RVQ depth decoder) on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *    memory (packed weights, activations, outputs, workspaces); the library
+ *    never allocates device memory on these paths.
+ *  - bf16 values are passed as uint16_t bit patterns; fp32 as float.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream).  Results are valid once the stream
+ *    reaches them.
+ *  - Arguments are validated on the host BEFORE anything is launched; on a
+ *    refusal the call returns a negative m3_status and enqueues nothing.
+ *    Unsupported shapes are refused, never mis-computed (TensorFold PR #987,
+ *    "Kernel contract": shapes within the bound, unsupported edges refused).
+ *    A HIP launch error is reported as M3_ERR_HIP.
+ *  - Determinism: identical inputs give byte-identical outputs; within one
+ *    call, batch row b's result never depends on the other rows.
+ *
+ * Weight formats (TensorFold PR #987, precision list): bf16; int8 with one
+ * fp32 scale per output row (body and lm_head); int8 with one fp32 scale per
+ * group of 128 along K (depth decoder and its heads); quantised on the GPU
+ * at load by m3_pack.
+ */
+#ifndef M3_H
+#define M3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ----------------------------------------------------- */
+typedef enum {
+  M3_OK = 0,
+  M3_ERR_NULL = -1,       /* a required pointer is NULL                      */
+  M3_ERR_SHAPE = -2,      /* a size is outside the supported set             */
+  M3_ERR_ALIGN = -3,      /* a pointer or leading dimension is misaligned    */
+  M3_ERR_FORMAT = -4,     /* unknown weight format / epilogue / output type  */
+  M3_ERR_WORKSPACE = -5,  /* workspace too small                             */
+  M3_ERR_HIP = -6,        /* a HIP call failed (launch or graph error)       */
+  M3_ERR_ALIAS = -7       /* an input overlaps an output it must not overlap */
+} m3_status;
+
+/* ---- enums ------------------------------------------------------------ */
+enum { M3_BF16 = 0, M3_I8ROW = 1, M3_I8G128 = 2 };          /* weight formats */
+enum { M3_EPI_NONE = 0, M3_EPI_SWIGLU = 1, M3_EPI_RESIDUAL = 2 };
+enum { M3_OUT_BF16 = 0, M3_OUT_F32 = 1 };
+enum { M3_PACK_GLU_INTERLEAVE = 1 };
+
+#define M3_MAX_B 64          /* lockstep rows per GEMV call                 */
+#define M3_MAX_B_NORM_4K 16  /* rows when a 4096-wide norm is fused         */
+#define M3_MAX_B_FRAME 16    /* rows per frame                              */
+
+const char* m3_status_str(int status);
+/* library version string (host) */
+const char* m3_version(void);
+
+/* ---- packing (a load-time step) --------------------------------------- */
+/* Packed layout, identical for all formats: the rows are cut into blocks of
+ * 16; each block is a run of 1024-byte tiles along K, each tile holding 64
+ * bytes of each of the 16 rows (32 bf16 or 64 int8 values per row).  Byte
+ * 16*l .. 16*l+15 of a tile belongs to row (l mod 16), K-bytes 16*(l/16) ..
+ * 16*(l/16)+15 of the tile's 64-byte K-segment, so that one 16-byte load per
+ * lane of a 64-lane wave reads the whole tile contiguously.  K is zero-padded
+ * to a whole tile and N to a whole block.  int8 blocks end with their fp32
+ * scales: i8row: scale[r] for r = 0..15 (64 B, then 64 B padding);
+ * i8g128: scale[g][r] for every group g of 128 (K/128 x 64 B, rounded up to
+ * 128 B).  int8 codes are two's-complement bytes in [-127, 127].
+ *
+ * Quantisation (int8): scale = absmax / 127 as one fp32 division; q is the
+ * nearest integer of W/scale (ties to even), clamped to [-127, 127]; an
+ * all-zero row or group gets scale 0.  Weights must be finite.
+ *
+ * flags & M3_PACK_GLU_INTERLEAVE: W is a stacked [gate; up] matrix [2F, K];
+ * packed row 2i is gate row i and row 2i+1 is up row i, so one GEMV with the
+ * SwiGLU epilogue produces both halves of each pair (TensorFold PR #987, "What
+ * it adds": a gate and an up row whose SwiGLU the GEMV writes).  N = 2F.
+ *
+ * Sizes: bf16 K % 8 == 0; i8row K % 16 == 0; i8g128 K % 128 == 0; N >= 1.
+ * W_bf16 is [N, K] row-major (leading dimension K); W and packed must be
+ * 16-byte aligned.  packed must hold m3_packed_bytes(fmt, N, K, flags). */
+size_t m3_packed_bytes(int fmt, int N, int K, int flags);   /* host only; 0 = refused */
+int m3_pack(int fmt, const uint16_t* W_bf16, int N, int K, int flags, void* packed,
+            void* stream);
+
+/* ---- RMSNorm-fused skinny GEMV/GEMM ------------------------------------ */
+/* y[b, n] = epi( sum_k W[n, k] * a[b, k] ), fp32 accumulation, where
+ *   a = x                                         if gamma == NULL
+ *   a[b, k] = bf16(x[b, k] * r_b * gamma[k]),  r_b = (mean_k x[b,k]^2 + eps)^-1/2
+ * (fp32 norm, bf16 operand: TensorFold PR #987 precision list; the norm is
+ * folded into the GEMV that reads it, as that page's next steps propose).
+ *
+ * Attention stub (stub_group > 0): x is the [B, *] output row of a fused QKV
+ * GEMV and the operand is a[b, h*hd + d] = x[b, stub_voff + (h/stub_group)*hd + d]
+ * with hd = 128: identity attention over one cached position (the softmax
+ * over a single key is 1), each query head reading its KV group's value.
+ *
+ * Epilogues:
+ *   M3_EPI_NONE      y = acc (fp32) or bf16(acc)
+ *   M3_EPI_RESIDUAL  y = bf16(residual + bf16(acc)); residual may equal y
+ *                    (in-place update of the residual stream); bf16 out only
+ *   M3_EPI_SWIGLU    rows are interleaved gate/up pairs (M3_PACK_GLU_INTERLEAVE);
+ *                    y[b, i] = bf16(silu(bf16(acc_gate)) * bf16(acc_up)) rounded
+ *                    once; y has N/2 columns; bf16 out only
+ *
+ * Sizes: 1 <= B <= M3_MAX_B; with gamma, B * roundup(K, tile) <= 65536
+ * (B <= 16 at K = 4096, B <= 32 at K = 2048); ldx >= K (stub: >= voff + K/group),
+ * ldy >= N (N/2 for SwiGLU), ldr >= N; x, y, residual 16-byte aligned and ldx,
+ * ldy, ldr multiples of 8.  x must not overlap y.  eps >= 0. */
+int m3_rmsnorm_gemv(const void* packed_bf16, int N, int K,
+                    const uint16_t* x, int B, int ldx,
+                    const float* gamma, float eps, int stub_group, int stub_voff,
+                    void* y, int ldy, int out_dtype,
+                    int epi, const uint16_t* residual, int ldr, void* stream);
+int m3_gemv_i8row(const void* packed_i8row, int N, int K,
+                  const uint16_t* x, int B, int ldx,
+                  const float* gamma, float eps, int stub_group, int stub_voff,
+                  void* y, int ldy, int out_dtype,
+                  int epi, const uint16_t* residual, int ldr, void* stream);
+int m3_gemv_i8g128(const void* packed_i8g128, int N, int K,
+                   const uint16_t* x, int B, int ldx,
+                   const float* gamma, float eps, int stub_group, int stub_voff,
+                   void* y, int ldy, int out_dtype,
+                   int epi, const uint16_t* residual, int ldr, void* stream);
+
+/* ---- sliced lm_head ------------------------------------------------------ */
+/* logits[b, j] = fp32( sum_k Wslice[j, k] * a[b, k] ), a = RMSNorm(x; gamma).
+ * packed_slice holds only the reachable vocab rows (packed with m3_pack from
+ * the full matrix's rows [row0, row0 + n_rows)): reading only the sampleable
+ * rows gives the same draw as masking all other rows to -inf (diffusers issue
+ * #14486 item 3; "MiniMax Music 3, local", where the time went).  Each
+ * logit's summation order depends only on K, never on n_rows, the batch or
+ * the slice offset, so a slice reproduces the full matrix's logits bit for
+ * bit.  fmt is M3_BF16 or M3_I8ROW.  Sizes as m3_rmsnorm_gemv; ldl >= n_rows,
+ * ldl % 4 == 0. */
+int m3_lmhead_sliced(int fmt, const void* packed_slice, int n_rows, int K,
+                     const uint16_t* x, int B, int ldx, const float* gamma, float eps,
+                     float* logits, int ldl, void* stream);
+
+/* ---- Gumbel-argmax sampler ----------------------------------------------- */
+/* out[b] = id of argmax_j z[b, j],  z = fl32(l[b, j] * fl32(1/T)) + G  (two
+ * roundings, no contraction), ties to the lowest index, NaN above every number
+ * (first NaN wins), ids outside [valid_lo, valid_hi) at -inf when lo < hi
+ * (the vocab mask of DiffSynth-Studio's MiniMax-Music3 stage 2).  A draw from
+ * softmax(l/T) (diffusers issue #14486 item 3: Gumbel-argmax in place of
+ * softmax + multinomial).
+ * G = -log(-log(u)), u = (2*(w >> 9) + 1) * 2^-24, w = word (id & 3) of
+ * Philox-4x32-10 (Salmon et al., SC'11) with key (seed lo, seed hi) and
+ * counter (id >> 2, b, frame, draw); id is the ABSOLUTE vocab id
+ * (index_base + j, or ids[j]).  log is a fixed sequence of IEEE fp32
+ * operations (frexp split + atanh series), so the noise is bit-reproducible.
+ * frame_dev (optional): the frame number is read from device memory (the
+ * frame counter the frame driver advances on the GPU).
+ * noise_override (optional, device [B, V], row stride V): used in place of G. */
+typedef struct {
+  uint64_t seed;
+  uint32_t frame;
+  const uint32_t* frame_dev;     /* device, optional                         */
+  uint32_t draw;                 /* 0 = semantic, 1..7 = depth codebooks      */
+  float temperature;             /* > 0                                       */
+  int32_t index_base;            /* absolute id of column 0 when ids == NULL  */
+  const int32_t* ids;            /* device, optional [V]: absolute ids        */
+  int32_t valid_lo, valid_hi;    /* mask; lo == hi disables it                */
+  const float* noise_override;   /* device, optional [B, V]                   */
+} m3_sample_params;
+
+/* workspace bytes m3_gumbel_argmax needs for (B, V) (host) */
+size_t m3_gumbel_workspace_bytes(int B, int V);
+/* 1 <= B <= M3_MAX_B, 1 <= V <= 2^24, ldl >= V, ldl % 4 == 0, logits and
+ * workspace 16-byte aligned.  params is a HOST struct. */
+int m3_gumbel_argmax(const float* logits, int B, int V, int ldl,
+                     const m3_sample_params* params, int32_t* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- one decode frame ------------------------------------------------------ */
+typedef struct {
+  int hidden, n_layers, n_heads, n_kv_heads, head_dim, ffn;
+  int vocab_base, n_slice;        /* reachable ids [vocab_base, vocab_base+n_slice) */
+  int d_hidden, d_layers, d_heads, d_head_dim, d_ffn;
+  int n_codebooks, code_vocab;
+  int fmt_body, fmt_lm, fmt_depth;
+  float eps, temperature;
+  uint64_t seed;
+} m3_config;
+
+typedef struct {
+  const void* qkv;        /* packed [nq + 2 nkv, hidden]              */
+  const void* o;          /* packed [hidden, nq]                      */
+  const void* gate_up;    /* packed, GLU-interleaved [2 ffn, hidden]  */
+  const void* down;       /* packed [hidden, ffn]                     */
+  const float* attn_norm; /* [hidden] */
+  const float* ffn_norm;  /* [hidden] */
+} m3_layer_weights;
+
+typedef struct {
+  m3_config cfg;
+  const m3_layer_weights* layers;     /* host array [n_layers]                   */
+  const float* final_norm;            /* [hidden]                                */
+  const void* lm_head;                /* packed slice [n_slice, hidden] (fmt_lm) */
+  const void* p_in;                   /* packed [d_hidden, hidden] (fmt_depth)   */
+  const uint16_t* emb1;               /* bf16 [n_slice, d_hidden]                */
+  const uint16_t* const* emb;         /* host array [n_codebooks-2] of [code_vocab, d_hidden] */
+  const m3_layer_weights* d_layers_w; /* host array [d_layers]                   */
+  const float* d_final_norm;          /* [d_hidden]                              */
+  const void* const* heads;           /* host array [n_codebooks-1], packed [code_vocab, d_hidden] */
+  const uint16_t* tok_emb_audio;      /* bf16 [n_slice, hidden]: embed_tokens rows of the codes */
+  const uint16_t* const* audio_emb;   /* host array [n_codebooks-1] of [code_vocab, hidden] */
+} m3_model;
+
+/* Device buffers inside the frame state (byte offsets from its base). */
+typedef struct {
+  size_t x;        /* bf16 [B, hidden]   frame input; overwritten by x_next    */
+  size_t h;        /* bf16 [B, hidden]   body residual stream                  */
+  size_t qkv;      /* bf16 [B, nq+2nkv]                                        */
+  size_t mlp;      /* bf16 [B, ffn]                                            */
+  size_t logits;   /* f32  [B, n_slice]  semantic logits of the last frame     */
+  size_t u;        /* bf16 [B, d_hidden] depth-decoder input projection        */
+  size_t hd;       /* bf16 [B, d_hidden] depth residual stream                 */
+  size_t dqkv;     /* bf16 [B, 3 d_hidden]                                     */
+  size_t dmlp;     /* bf16 [B, d_ffn]                                          */
+  size_t dlogits;  /* f32  [B, code_vocab] logits of the last depth draw       */
+  size_t ring;     /* i32  [16, B, 8]    codes of the last 16 frames           */
+  size_t frame;    /* u32  frame counter (advanced on the GPU)                 */
+  size_t sample_ws;/* sampler workspace                                        */
+  size_t total;
+} m3_frame_layout;
+
+/* Algorithmic weight bytes one frame streams: every body matrix once, the
+ * lm_head slice once, the depth input projection once, the depth layers and
+ * one head per codebook step (7 steps), plus the fp32 gammas of every norm
+ * application.  bf16: 2NK; i8row: NK + 4N; i8g128: NK + 4N*K/128.
+ * (TensorFold PR #987 asks the engine for "the weight bytes a frame reads".) */
+uint64_t m3_frame_weight_bytes(const m3_config* cfg /* host */);
+/* layout of the caller-allocated frame state; 0 / M3_ERR_* on refusal */
+int m3_frame_layout_get(const m3_config* cfg /* host */, int B, m3_frame_layout* out /* host */);
+size_t m3_frame_workspace_bytes(const m3_config* cfg /* host */, int B);
+/* Zero the frame state, copy x0 (device bf16 [B, hidden]) into its input and
+ * set the frame counter to frame0. */
+int m3_frame_state_init(const m3_config* cfg, int B, void* state, const uint16_t* x0,
+                        uint32_t frame0, void* stream);
+/* Enqueue one frame: body (per layer: norm+QKV, stub+O+residual, norm+gate/up
+ * +SwiGLU, down+residual) -> final norm + sliced lm_head -> draw 0 -> depth
+ * input projection -> 7 x (embedding of the previous code, depth layers, final
+ * norm + head_j, draw j) -> feedback x' = bf16((E_tok[c0] + sum_j A_j[c_j]) *
+ * 8^-1/2) into the state's input, codes into `codes` (device [B, 8]: absolute
+ * semantic id, then codes 1..7) and into the 16-frame ring, frame counter + 1
+ * on the GPU (DiffSynth-Studio MiniMax-Music3 stage 2; TensorFold PR #987:
+ * position and count advance on the GPU, the host reads the drawn tokens
+ * every 16 frames).  1 <= B <= M3_MAX_B_FRAME.  bytes_read (host, optional)
+ * receives m3_frame_weight_bytes. */
+int m3_decode_frame_weights(const m3_model* model /* host */, void* state, int B,
+                            int32_t* codes, uint64_t* bytes_read, void* stream);
+
+/* HIP-graph form of the frame: capture the launches of one frame once and
+ * replay them; every replay is a new frame (the counter lives on the GPU).
+ * The captured graph keeps the model's and the state's device addresses. */
+int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* codes,
+                          void* stream, void** graph_out /* host */);
+int m3_frame_graph_launch(void* graph, void* stream);
+int m3_frame_graph_destroy(void* graph);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* M3_H */

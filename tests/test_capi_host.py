@@ -1,0 +1,137 @@
+"""Host-side checks of libm3 (no GPU needed): the library loads, exports every
+entry point include/m3.h declares, computes sizes, and refuses unsupported
+arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from autoregressive_audio_lm_amd import _lib, configs
+from autoregressive_audio_lm_amd.runtime import make_config, frame_weight_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from autoregressive_audio_lm_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "m3.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(m3_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert len(syms) >= 18
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(_lib.SYMBOLS)
+
+
+def test_status_strings(L):
+    for st in range(0, -8, -1):
+        assert L.m3_status_str(st)
+    assert b"gfx950" in L.m3_version()
+
+
+FAKE = ctypes.c_void_p(0x100000)      # aligned, never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x900000)
+
+
+def gemv(L, fmt=0, N=64, K=256, x=FAKE, B=1, ldx=256, gamma=None, eps=1e-6, sg=0, sv=0, y=FAKE2,
+         ldy=64, out=0, epi=0, res=None, ldr=0):
+    f = {0: L.m3_rmsnorm_gemv, 1: L.m3_gemv_i8row, 2: L.m3_gemv_i8g128}[fmt]
+    return f(FAKE, N, K, x, B, ldx, gamma, eps, sg, sv, y, ldy, out, epi, res, ldr, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.M3_ERR_NULL),
+    (dict(y=None), _lib.M3_ERR_NULL),
+    (dict(B=0), _lib.M3_ERR_SHAPE),
+    (dict(B=65), _lib.M3_ERR_SHAPE),
+    (dict(N=0), _lib.M3_ERR_SHAPE),
+    (dict(K=4, ldx=8), _lib.M3_ERR_SHAPE),
+    (dict(K=250), _lib.M3_ERR_SHAPE),
+    (dict(fmt=1, K=248, ldx=248), _lib.M3_ERR_SHAPE),       # i8row needs K % 16
+    (dict(fmt=2, K=192, ldx=192), _lib.M3_ERR_SHAPE),       # g128 needs K % 128
+    (dict(ldx=128), _lib.M3_ERR_SHAPE),
+    (dict(ldy=32), _lib.M3_ERR_SHAPE),
+    (dict(ldx=260), _lib.M3_ERR_ALIGN),
+    (dict(x=ctypes.c_void_p(0x100008)), _lib.M3_ERR_ALIGN),
+    (dict(out=7), _lib.M3_ERR_FORMAT),
+    (dict(epi=5), _lib.M3_ERR_FORMAT),
+    (dict(epi=1, out=1), _lib.M3_ERR_FORMAT),               # SwiGLU writes bf16 only
+    (dict(epi=2, res=None), _lib.M3_ERR_NULL),
+    (dict(N=63, epi=1), _lib.M3_ERR_SHAPE),                 # SwiGLU needs pairs
+    (dict(eps=-1.0), _lib.M3_ERR_SHAPE),
+    (dict(eps=float("nan")), _lib.M3_ERR_SHAPE),
+    (dict(sg=-1), _lib.M3_ERR_SHAPE),
+    (dict(sg=4, sv=0, K=256, ldx=128), _lib.M3_ERR_SHAPE),  # stub: K/128 heads not divisible by 4
+    (dict(sg=2, sv=4, K=256, ldx=256), _lib.M3_ERR_SHAPE),  # stub: voff % 8
+    (dict(y=ctypes.c_void_p(0x100000 + 64)), _lib.M3_ERR_ALIAS),
+    (dict(gamma=FAKE2, K=4096, ldx=4096, B=17, y=ctypes.c_void_p(0x4000000)), _lib.M3_ERR_SHAPE),
+])
+def test_gemv_refusals(L, kw, status):
+    assert gemv(L, **kw) == status
+
+
+def test_pack_and_sizes(L):
+    assert L.m3_packed_bytes(0, 16, 32, 0) == 1024
+    assert L.m3_packed_bytes(0, 17, 40, 0) == 2 * 2 * 1024          # 2 blocks x 2 tiles
+    assert L.m3_packed_bytes(1, 16, 64, 0) == 1024 + 128            # tile + scales
+    assert L.m3_packed_bytes(2, 16, 256, 0) == 4 * 1024 + 128       # 2 groups x 64 B -> 128
+    assert L.m3_packed_bytes(2, 16, 200, 0) == 0
+    assert L.m3_packed_bytes(0, 15, 64, 1) == 0                     # GLU needs even N
+    assert L.m3_packed_bytes(3, 16, 64, 0) == 0
+    assert L.m3_pack(0, None, 16, 32, 0, FAKE, None) == _lib.M3_ERR_NULL
+    assert L.m3_pack(0, FAKE, 16, 30, 0, FAKE2, None) == _lib.M3_ERR_SHAPE
+    assert L.m3_pack(5, FAKE, 16, 32, 0, FAKE2, None) == _lib.M3_ERR_FORMAT
+
+
+def test_sampler_refusals(L):
+    p = _lib.SampleParams(0, 0, None, 0, 1.0, 0, None, 0, 0, None)
+    ws = L.m3_gumbel_workspace_bytes(4, 5000)
+    assert ws == 4 * 5 * 8
+    arg = lambda **k: (k.get("lg", FAKE), k.get("B", 4), k.get("V", 5000), k.get("ldl", 5000),
+                       ctypes.byref(k.get("p", p)), k.get("out", FAKE2), k.get("ws", ctypes.c_void_p(0x2000000)),
+                       k.get("wsb", ws), None)
+    assert L.m3_gumbel_argmax(*arg(lg=None)) == _lib.M3_ERR_NULL
+    assert L.m3_gumbel_argmax(*arg(B=0)) == _lib.M3_ERR_SHAPE
+    assert L.m3_gumbel_argmax(*arg(ldl=4000)) == _lib.M3_ERR_SHAPE
+    assert L.m3_gumbel_argmax(*arg(wsb=ws - 1)) == _lib.M3_ERR_WORKSPACE
+    assert L.m3_gumbel_argmax(*arg(ldl=5001)) == _lib.M3_ERR_ALIGN
+    bad = _lib.SampleParams(0, 0, None, 0, 0.0, 0, None, 0, 0, None)
+    assert L.m3_gumbel_argmax(*arg(p=bad)) == _lib.M3_ERR_SHAPE
+
+
+@pytest.mark.parametrize("preset", ["A", "B"])
+@pytest.mark.parametrize("name", ["frame-full", "frame-small"])
+def test_frame_weight_bytes_matches_oracle_formula(L, oracle, preset, name):
+    cfg = configs.config(name)
+    p = configs.PRESETS[preset]
+    c = make_config(cfg, **p)
+    assert frame_weight_bytes(c) == oracle.frame_weight_bytes(cfg, **p)
+
+
+def test_frame_layout_and_refusals(L):
+    cfg = configs.config("frame-full")
+    c = make_config(cfg, **configs.PRESETS["A"])
+    lay = _lib.FrameLayout()
+    assert L.m3_frame_layout_get(ctypes.byref(c), 16, ctypes.byref(lay)) == 0
+    assert lay.total % 256 == 0 and lay.x == 0 and lay.total > lay.sample_ws
+    assert L.m3_frame_workspace_bytes(ctypes.byref(c), 17) == 0
+    assert L.m3_frame_layout_get(ctypes.byref(c), 0, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
+    c2 = make_config(cfg, 0, 2, 2)                                   # lm_head must be bf16/i8row
+    assert L.m3_frame_layout_get(ctypes.byref(c2), 1, ctypes.byref(lay)) == _lib.M3_ERR_FORMAT
+    c3 = make_config(dict(cfg, head_dim=64), **configs.PRESETS["A"])
+    assert L.m3_frame_layout_get(ctypes.byref(c3), 1, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
+    m = _lib.Model(cfg=c)
+    codes = ctypes.c_void_p(0x300000)
+    assert L.m3_decode_frame_weights(ctypes.byref(m), FAKE, 1, codes, None, None) == _lib.M3_ERR_NULL
