@@ -381,16 +381,18 @@ int m3_lmhead_sliced(int fmt, const void* packed_slice, int n_rows, int K, const
 }
 
 size_t m3_gumbel_workspace_bytes(int B, int V) {
-  if (B < 1 || B > M3_MAX_B || V < 1 || V > (1 << 24)) return 0;
+  if (B < 1 || B > M3_MAX_B_SAMPLE || V < 1 || V > (1 << 24)) return 0;
   return sample_ws_bytes(B, V);
 }
 
 int m3_gumbel_argmax(const float* logits, int B, int V, int ldl, const m3_sample_params* p,
                      int32_t* out, void* ws, size_t ws_bytes, void* stream) {
   if (!logits || !p || !out || !ws) return M3_ERR_NULL;
-  if (B < 1 || B > M3_MAX_B || V < 1 || V > (1 << 24) || ldl < V) return M3_ERR_SHAPE;
+  if (B < 1 || B > M3_MAX_B_SAMPLE || V < 1 || V > (1 << 24) || ldl < V) return M3_ERR_SHAPE;
   if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return M3_ERR_SHAPE;
-  if (ldl % 4 != 0 || !aligned(logits, 16) || !aligned(ws, 16) || !aligned(out, 4))
+  if (!aligned(logits, 4) || !aligned(ws, 16) || !aligned(out, 4)) return M3_ERR_ALIGN;
+  if ((p->ids && !aligned(p->ids, 4)) || (p->noise_override && !aligned(p->noise_override, 4)) ||
+      (p->frame_dev && !aligned(p->frame_dev, 4)))
     return M3_ERR_ALIGN;
   if (ws_bytes < sample_ws_bytes(B, V)) return M3_ERR_WORKSPACE;
   SampleDesc d{};

@@ -190,10 +190,10 @@ __device__ __forceinline__ float row_scale(const uint8_t* blk, const Params& p, 
 }
 
 // Cross-wave reduction in fixed wave order, scale, epilogue, store.
-template <int FMT, int NB>
+template <int FMT, int NB, bool GLU>
 __device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const float* red) {
   const int tid = threadIdx.x;
-  if (p.epi == M3_EPI_SWIGLU) {
+  if constexpr (GLU) {
     for (int t = tid; t < p.B * 8; t += kThreads) {
       const int b = t >> 3, pr = t & 7;
       const int n = rb * 16 + 2 * pr;
@@ -269,7 +269,7 @@ __device__ __forceinline__ void valu_tile(const Params& p, const uint16_t* act, 
   }
 }
 
-template <int FMT, int NB, bool LDS>
+template <int FMT, int NB, bool LDS, bool GLU>
 __device__ void valu_block(const Params& p, const uint16_t* act, float* red, int rb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint8_t* blk = p.w + (size_t)rb * p.bbytes;
@@ -321,7 +321,7 @@ __device__ void valu_block(const Params& p, const uint16_t* act, float* red, int
     if (lane < 16) red[(wave * NB + b) * 16 + lane] = v;
   }
   __syncthreads();
-  finish_block<FMT, NB>(p, blk, rb, red);
+  finish_block<FMT, NB, GLU>(p, blk, rb, red);
   __syncthreads();
 }
 
@@ -364,7 +364,7 @@ __device__ __forceinline__ void mfma_tile(const Params& p, const uint16_t* act, 
   }
 }
 
-template <int FMT, int NT, bool LDS>
+template <int FMT, int NT, bool LDS, bool GLU>
 __device__ void mfma_block(const Params& p, const uint16_t* act, float* red, int rb) {
   constexpr int NB = NT * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -416,11 +416,13 @@ __device__ void mfma_block(const Params& p, const uint16_t* act, float* red, int
     for (int q = 0; q < 4; ++q)
       red[(wave * NB + bt * 16 + 4 * (lane >> 4) + q) * 16 + (lane & 15)] = acc[bt][q];
   __syncthreads();
-  finish_block<FMT, NB>(p, blk, rb, red);
+  finish_block<FMT, NB, GLU>(p, blk, rb, red);
   __syncthreads();
 }
 
-template <int FMT, int NB, bool MFMA, bool LDS>
+// GLU selects the SwiGLU epilogue at compile time (its own kernel symbol, so
+// the gate/up GEMVs can be told apart in a profile).
+template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
   extern __shared__ __align__(16) uint8_t smem[];
   float* red = reinterpret_cast<float*>(smem);                       // [kWaves][NB][16]
@@ -429,25 +431,30 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
   if (LDS) stage_activations(p, act, ss_buf);
   for (int rb = blockIdx.x; rb < p.nblocks; rb += gridDim.x) {
     if constexpr (MFMA)
-      mfma_block<FMT, NB / 16, LDS>(p, act, red, rb);
+      mfma_block<FMT, NB / 16, LDS, GLU>(p, act, red, rb);
     else
-      valu_block<FMT, NB, LDS>(p, act, red, rb);
+      valu_block<FMT, NB, LDS, GLU>(p, act, red, rb);
   }
 }
 
-template <int FMT, int NB, bool MFMA, bool LDS>
+template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
 hipError_t configure_one() {
   static hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(gemv_kernel<FMT, NB, MFMA, LDS>),
+      reinterpret_cast<const void*>(gemv_kernel<FMT, NB, MFMA, LDS, GLU>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   return status;
 }
 
 template <int FMT, int NB, bool MFMA, bool LDS>
 hipError_t launch_one(const Params& p, int grid, size_t smem, hipStream_t s) {
-  const hipError_t e = configure_one<FMT, NB, MFMA, LDS>();
+  const bool glu = p.epi == M3_EPI_SWIGLU;
+  const hipError_t e = glu ? configure_one<FMT, NB, MFMA, LDS, true>()
+                           : configure_one<FMT, NB, MFMA, LDS, false>();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_kernel<FMT, NB, MFMA, LDS>), dim3(grid), dim3(kThreads), smem, s, p);
+  if (glu)
+    hipLaunchKernelGGL((gemv_kernel<FMT, NB, MFMA, LDS, true>), dim3(grid), dim3(kThreads), smem, s, p);
+  else
+    hipLaunchKernelGGL((gemv_kernel<FMT, NB, MFMA, LDS, false>), dim3(grid), dim3(kThreads), smem, s, p);
   return hipGetLastError();
 }
 
@@ -464,13 +471,21 @@ hipError_t dispatch_b(const Params& p, int grid, size_t smem, hipStream_t s) {
   return launch_one<FMT, 64, true, LDS>(p, grid, smem, s);
 }
 
+template <int FMT, bool LDS, bool GLU>
+hipError_t configure_epi() {
+  const hipError_t es[] = {
+      configure_one<FMT, 1, false, LDS, GLU>(),  configure_one<FMT, 2, false, LDS, GLU>(),
+      configure_one<FMT, 4, false, LDS, GLU>(),  configure_one<FMT, 8, false, LDS, GLU>(),
+      configure_one<FMT, 16, true, LDS, GLU>(),  configure_one<FMT, 32, true, LDS, GLU>(),
+      configure_one<FMT, 48, true, LDS, GLU>(),  configure_one<FMT, 64, true, LDS, GLU>()};
+  for (hipError_t e : es)
+    if (e != hipSuccess) return e;
+  return hipSuccess;
+}
+
 template <int FMT, bool LDS>
 hipError_t configure_fmt() {
-  const hipError_t es[] = {
-      configure_one<FMT, 1, false, LDS>(),  configure_one<FMT, 2, false, LDS>(),
-      configure_one<FMT, 4, false, LDS>(),  configure_one<FMT, 8, false, LDS>(),
-      configure_one<FMT, 16, true, LDS>(),  configure_one<FMT, 32, true, LDS>(),
-      configure_one<FMT, 48, true, LDS>(),  configure_one<FMT, 64, true, LDS>()};
+  const hipError_t es[] = {configure_epi<FMT, LDS, false>(), configure_epi<FMT, LDS, true>()};
   for (hipError_t e : es)
     if (e != hipSuccess) return e;
   return hipSuccess;

@@ -53,11 +53,16 @@ class DecodeModel:
             self._keep.append(P)
             return ctypes.c_void_p(P.data_ptr())
 
-        def layer(L, fmt):
+        self.packed_layers, self.packed_dlayers = [], []
+
+        def layer(L, fmt, dst):
             gu = torch.cat([L["gate"], L["up"]], 0)
             lw = _lib.LayerWeights(packed(L["qkv"], fmt), packed(L["o"], fmt),
                                    packed(gu, fmt, m3.PACK_GLU_INTERLEAVE), packed(L["down"], fmt),
                                    keep(L["attn_norm"]), keep(L["ffn_norm"]))
+            # the four packed tensors just appended, the two gammas after them
+            dst.append(dict(zip(("qkv", "o", "gate_up", "down", "attn_norm", "ffn_norm"),
+                                self._keep[-6:])))
             del gu
             if free_sources:
                 for k in ("qkv", "o", "gate", "up", "down"):
@@ -65,9 +70,10 @@ class DecodeModel:
             return lw
 
         nl = len(md["layers"])
-        self._layers = (_lib.LayerWeights * nl)(*[layer(L, self.fmt_body) for L in md["layers"]])
+        self._layers = (_lib.LayerWeights * nl)(
+            *[layer(L, self.fmt_body, self.packed_layers) for L in md["layers"]])
         self._dlayers = (_lib.LayerWeights * len(md["d_layers"]))(
-            *[layer(L, self.fmt_depth) for L in md["d_layers"]])
+            *[layer(L, self.fmt_depth, self.packed_dlayers) for L in md["d_layers"]])
         heads = [packed(W, self.fmt_depth) for W in md["heads"]]
         self._heads = (ctypes.c_void_p * len(heads))(*heads)
         embs = [keep(e) for e in md["emb"]]

@@ -55,6 +55,7 @@ enum { M3_PACK_GLU_INTERLEAVE = 1 };
 #define M3_MAX_B 64          /* lockstep rows per GEMV call                 */
 #define M3_MAX_B_NORM_4K 16  /* rows when a 4096-wide norm is fused         */
 #define M3_MAX_B_FRAME 16    /* rows per frame                              */
+#define M3_MAX_B_SAMPLE 65535 /* rows per sampler call                      */
 
 const char* m3_status_str(int status);
 /* library version string (host) */
@@ -171,8 +172,9 @@ typedef struct {
 
 /* workspace bytes m3_gumbel_argmax needs for (B, V) (host) */
 size_t m3_gumbel_workspace_bytes(int B, int V);
-/* 1 <= B <= M3_MAX_B, 1 <= V <= 2^24, ldl >= V, ldl % 4 == 0, logits and
- * workspace 16-byte aligned.  params is a HOST struct. */
+/* 1 <= B <= M3_MAX_B_SAMPLE, 1 <= V <= 2^24, ldl >= V; logits, out, ids,
+ * noise_override, frame_dev 4-byte aligned, workspace 16-byte aligned.
+ * params is a HOST struct. */
 int m3_gumbel_argmax(const float* logits, int B, int V, int ldl,
                      const m3_sample_params* params, int32_t* out,
                      void* workspace, size_t workspace_bytes, void* stream);

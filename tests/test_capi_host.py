@@ -106,7 +106,8 @@ def test_sampler_refusals(L):
     assert L.m3_gumbel_argmax(*arg(B=0)) == _lib.M3_ERR_SHAPE
     assert L.m3_gumbel_argmax(*arg(ldl=4000)) == _lib.M3_ERR_SHAPE
     assert L.m3_gumbel_argmax(*arg(wsb=ws - 1)) == _lib.M3_ERR_WORKSPACE
-    assert L.m3_gumbel_argmax(*arg(ldl=5001)) == _lib.M3_ERR_ALIGN
+    assert L.m3_gumbel_argmax(*arg(lg=ctypes.c_void_p(0x100002))) == _lib.M3_ERR_ALIGN
+    assert L.m3_gumbel_argmax(*arg(B=65536)) == _lib.M3_ERR_SHAPE
     bad = _lib.SampleParams(0, 0, None, 0, 0.0, 0, None, 0, 0, None)
     assert L.m3_gumbel_argmax(*arg(p=bad)) == _lib.M3_ERR_SHAPE
 
