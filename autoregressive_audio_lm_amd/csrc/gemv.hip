@@ -37,7 +37,6 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBatchTiles = 8;         // weight tiles in flight per wave and batch
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -57,6 +56,7 @@ struct Params {
   const uint16_t* res;
   int ldr;
   int lds_rows;        // activation rows staged in LDS (0: direct global reads)
+  int lds_stride;      // LDS row stride in elements: Kp + one zero tile + 8 (bank skew)
 };
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -109,8 +109,8 @@ __device__ __forceinline__ uint4 load_x8(const Params& p, int b, int k) {
 // Stage the operand rows in LDS (bf16, row stride Kp + 8), fusing the norm.
 __device__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int stride = p.Kp + 8;
-  const int nchunk = p.Kp >> 3;
+  const int stride = p.lds_stride;
+  const int nchunk = (p.lds_stride - 8) >> 3;   // K, its padding and the zero tile
   for (int b = 0; b < p.lds_rows; ++b) {
     float ss = 0.f;
     for (int i = tid; i < nchunk; i += kThreads) {
@@ -161,13 +161,16 @@ __device__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf)
   __syncthreads();
 }
 
+// 8 operand values of row b from k; k >= K reads zeros.  Branch-free, so the
+// waits for the weight stream are not made conservative by control flow.
 template <bool LDS>
 __device__ __forceinline__ uint4 act8(const Params& p, const uint16_t* act, int b, int k) {
   if constexpr (LDS) {
-    return *reinterpret_cast<const uint4*>(act + (size_t)b * (p.Kp + 8) + k);
+    return *reinterpret_cast<const uint4*>(act + (size_t)b * p.lds_stride + k);
   } else {
-    if (k >= p.K) return make_uint4(0, 0, 0, 0);
-    return load_x8(p, b, k);
+    const bool in = k < p.K;
+    const uint4 v = load_x8(p, b, in ? k : 0);
+    return in ? v : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -225,36 +228,79 @@ __device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const 
 }
 
 // ---------------------------------------------------------------------------
-// VALU path: NB activation rows (B <= NB), lane = (row l%16, K-chunk l/16).
+// Weight stream.  Tiles are read with non-temporal 16-byte loads: each weight
+// byte is used once per call, so it should not displace the activations and
+// partial sums from the caches.
 // ---------------------------------------------------------------------------
-template <int FMT, int NB, bool LDS>
-__device__ __forceinline__ void valu_tile(const Params& p, const uint16_t* act, const uint4& wv,
-                                          int k0, float* acc) {
-  const int lane = threadIdx.x & 63, c = lane >> 4;
-  if constexpr (FMT == M3_BF16) {
-    const int kk = k0 + c * 8;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource over the whole packed matrix (< 2 GiB).  A raw buffer load
+// whose VGPR offset is past num_records returns zeros without touching memory;
+// adding kOob to a lane's offset turns a load into such a no-op.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes, non-temporal (each weight byte is used once per call); the
+// uniform part of the address goes in the scalar offset.
+__device__ __forceinline__ uint4 ldw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+#ifndef M3_GEMV_KU
+#define M3_GEMV_KU 8
+#endif
+#ifndef M3_GEMV_DOUBLE_BUFFER
+#define M3_GEMV_DOUBLE_BUFFER 1
+#endif
+constexpr int kU = M3_GEMV_KU;   // tiles per batch
+constexpr bool kDoubleBuffer = M3_GEMV_DOUBLE_BUFFER;   // a second batch in flight
+static_assert(kU % 2 == 0 && kU <= 16, "batches hold whole i8g128 groups");
+
+// ---------------------------------------------------------------------------
+// VALU accumulators: NB activation rows (B <= NB); lane = (row l%16, K-chunk
+// l/16); partial sums of the 4 lanes of a row meet with two exchanges.
+// ---------------------------------------------------------------------------
+template <int FMT, int NB, bool MFMA>
+struct Accum {
+  float acc[NB], gacc[NB];
+
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b < p.B) {
-        const uint4 av = act8<LDS>(p, act, b, kk);
-        float a = acc[b];
+    for (int b = 0; b < NB; ++b) acc[b] = gacc[b] = 0.f;
+  }
+
+  template <bool LDS>
+  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0) {
+    float* dst = FMT == M3_I8G128 ? gacc : acc;
+    const int c = (threadIdx.x & 63) >> 4;
+    if constexpr (FMT == M3_BF16) {
+      const int kk = k0 + c * 8;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        // rows past B repeat row B-1 (valid memory); their sums are never stored
+        const uint4 av = act8<LDS>(p, act, min(b, p.B - 1), kk);
+        float a = dst[b];
         a = dot2(wv.x, av.x, a);
         a = dot2(wv.y, av.y, a);
         a = dot2(wv.z, av.z, a);
         a = dot2(wv.w, av.w, a);
-        acc[b] = a;
+        dst[b] = a;
       }
-    }
-  } else {
-    const int kk = k0 + c * 16;
-    uint32_t wb[8];
-    i8x16_to_bf16(wv, wb);
+    } else {
+      const int kk = k0 + c * 16;
+      uint32_t wb[8];
+      i8x16_to_bf16(wv, wb);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b < p.B) {
-        const uint4 a0 = act8<LDS>(p, act, b, kk);
-        const uint4 a1 = act8<LDS>(p, act, b, kk + 8);
-        float a = acc[b];
+      for (int b = 0; b < NB; ++b) {
+        const int bb = min(b, p.B - 1);
+        const uint4 a0 = act8<LDS>(p, act, bb, kk);
+        const uint4 a1 = act8<LDS>(p, act, bb, kk + 8);
+        float a = dst[b];
         a = dot2(wb[0], a0.x, a);
         a = dot2(wb[1], a0.y, a);
         a = dot2(wb[2], a0.z, a);
@@ -263,163 +309,104 @@ __device__ __forceinline__ void valu_tile(const Params& p, const uint16_t* act, 
         a = dot2(wb[5], a1.y, a);
         a = dot2(wb[6], a1.z, a);
         a = dot2(wb[7], a1.w, a);
-        acc[b] = a;
+        dst[b] = a;
       }
     }
   }
-}
 
-template <int FMT, int NB, bool LDS, bool GLU>
-__device__ void valu_block(const Params& p, const uint16_t* act, float* red, int rb) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint8_t* blk = p.w + (size_t)rb * p.bbytes;
-  const int TK = tile_k(FMT);
-  const int tpu = FMT == M3_I8G128 ? 2 : 1;
-  const int units = p.T / tpu;
-  const int t_lo = (units * wave / kWaves) * tpu;
-  const int t_hi = (units * (wave + 1) / kWaves) * tpu;
-  const float* gscale = reinterpret_cast<const float*>(blk + (size_t)p.T * kTileBytes);
-
-  float acc[NB];
+  // end of a group of 128 (i8g128): scale the group's partial sums
+  __device__ __forceinline__ void group_end(float s) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-  float gacc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) gacc[b] = 0.f;
-
-  for (int t0 = t_lo; t0 < t_hi; t0 += kBatchTiles) {
-    uint4 wv[kBatchTiles];
-#pragma unroll
-    for (int i = 0; i < kBatchTiles; ++i)
-      if (t0 + i < t_hi)
-        wv[i] = *reinterpret_cast<const uint4*>(blk + (size_t)(t0 + i) * kTileBytes + lane * 16);
-#pragma unroll
-    for (int i = 0; i < kBatchTiles; ++i) {
-      if (t0 + i < t_hi) {
-        const int t = t0 + i;
-        if constexpr (FMT == M3_I8G128) {
-          valu_tile<FMT, NB, LDS>(p, act, wv[i], t * TK, gacc);
-          if (t & 1) {
-            const float s = gscale[(t >> 1) * 16 + (lane & 15)];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              acc[b] = fmaf(s, gacc[b], acc[b]);
-              gacc[b] = 0.f;
-            }
-          }
-        } else {
-          valu_tile<FMT, NB, LDS>(p, act, wv[i], t * TK, acc);
-        }
-      }
+    for (int b = 0; b < NB; ++b) {
+      acc[b] = fmaf(s, gacc[b], acc[b]);
+      gacc[b] = 0.f;
     }
   }
+
+  __device__ __forceinline__ void to_red(float* red, int wave) const {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float v = acc[b];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    if (lane < 16) red[(wave * NB + b) * 16 + lane] = v;
+    for (int b = 0; b < NB; ++b) {
+      float v = acc[b];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (lane < 16) red[(wave * NB + b) * 16 + lane] = v;
+    }
   }
-  __syncthreads();
-  finish_block<FMT, NB, GLU>(p, blk, rb, red);
-  __syncthreads();
-}
+};
 
 // ---------------------------------------------------------------------------
-// MFMA path: NT tiles of 16 activation rows.  D[i][j] += sum_k A[i][k] B[k][j]
-// with A = activations (row i = lane%16 of tile), B = weight tile (column j =
-// weight row lane%16); lane l supplies k = 8*(l/16) .. +7 of each operand and
-// receives D[4*(l/16) + q][l%16], q = 0..3.
+// MFMA accumulators: NB/16 tiles of 16 activation rows.  D[i][j] += sum_k
+// A[i][k] B[k][j] with A = activations (row i = lane%16 of a tile), B = the
+// weight tile (column j = weight row lane%16); lane l supplies k = 8*(l/16)
+// .. +7 of each operand and receives D[4*(l/16) + q][l%16], q = 0..3.
 // ---------------------------------------------------------------------------
-template <int FMT, int NT, bool LDS>
-__device__ __forceinline__ void mfma_tile(const Params& p, const uint16_t* act, const uint4& wv,
-                                          int k0, f32x4_t* acc) {
-  const int lane = threadIdx.x & 63, c = lane >> 4, i = lane & 15;
-  if constexpr (FMT == M3_BF16) {
-    const int kk = k0 + c * 8;
-    const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wv);
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) {
-      const int b = min(bt * 16 + i, p.B - 1);
-      const uint4 av = act8<LDS>(p, act, b, kk);
-      acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), bw,
-                                                        acc[bt], 0, 0, 0);
-    }
-  } else {
-    const int kk = k0 + c * 16;
-    uint32_t wb[8];
-    i8x16_to_bf16(wv, wb);
-    const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, make_uint4(wb[0], wb[1], wb[2], wb[3]));
-    const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, make_uint4(wb[4], wb[5], wb[6], wb[7]));
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) {
-      const int b = min(bt * 16 + i, p.B - 1);
-      const uint4 a0 = act8<LDS>(p, act, b, kk);
-      const uint4 a1 = act8<LDS>(p, act, b, kk + 8);
-      acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), blo,
-                                                        acc[bt], 0, 0, 0);
-      acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), bhi,
-                                                        acc[bt], 0, 0, 0);
-    }
-  }
-}
-
-template <int FMT, int NT, bool LDS, bool GLU>
-__device__ void mfma_block(const Params& p, const uint16_t* act, float* red, int rb) {
-  constexpr int NB = NT * 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint8_t* blk = p.w + (size_t)rb * p.bbytes;
-  const int TK = tile_k(FMT);
-  const int tpu = FMT == M3_I8G128 ? 2 : 1;
-  const int units = p.T / tpu;
-  const int t_lo = (units * wave / kWaves) * tpu;
-  const int t_hi = (units * (wave + 1) / kWaves) * tpu;
-  const float* gscale = reinterpret_cast<const float*>(blk + (size_t)p.T * kTileBytes);
-
+template <int FMT, int NB>
+struct Accum<FMT, NB, true> {
+  static constexpr int NT = NB / 16;
   f32x4_t acc[NT], gacc[NT];
+
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-  for (int bt = 0; bt < NT; ++bt) {
-    acc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    gacc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int bt = 0; bt < NT; ++bt) acc[bt] = gacc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int t0 = t_lo; t0 < t_hi; t0 += kBatchTiles) {
-    uint4 wv[kBatchTiles];
+  template <bool LDS>
+  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0) {
+    f32x4_t* dst = FMT == M3_I8G128 ? gacc : acc;
+    const int lane = threadIdx.x & 63, c = lane >> 4, i = lane & 15;
+    if constexpr (FMT == M3_BF16) {
+      const int kk = k0 + c * 8;
+      const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wv);
 #pragma unroll
-    for (int i = 0; i < kBatchTiles; ++i)
-      if (t0 + i < t_hi)
-        wv[i] = *reinterpret_cast<const uint4*>(blk + (size_t)(t0 + i) * kTileBytes + lane * 16);
+      for (int bt = 0; bt < NT; ++bt) {
+        const int b = min(bt * 16 + i, p.B - 1);
+        const uint4 av = act8<LDS>(p, act, b, kk);
+        dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), bw,
+                                                          dst[bt], 0, 0, 0);
+      }
+    } else {
+      const int kk = k0 + c * 16;
+      uint32_t wb[8];
+      i8x16_to_bf16(wv, wb);
+      const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, make_uint4(wb[0], wb[1], wb[2], wb[3]));
+      const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, make_uint4(wb[4], wb[5], wb[6], wb[7]));
 #pragma unroll
-    for (int i = 0; i < kBatchTiles; ++i) {
-      if (t0 + i < t_hi) {
-        const int t = t0 + i;
-        if constexpr (FMT == M3_I8G128) {
-          mfma_tile<FMT, NT, LDS>(p, act, wv[i], t * TK, gacc);
-          if (t & 1) {
-            const float s = gscale[(t >> 1) * 16 + (lane & 15)];
-#pragma unroll
-            for (int bt = 0; bt < NT; ++bt) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc[bt][q] = fmaf(s, gacc[bt][q], acc[bt][q]);
-              gacc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-          }
-        } else {
-          mfma_tile<FMT, NT, LDS>(p, act, wv[i], t * TK, acc);
-        }
+      for (int bt = 0; bt < NT; ++bt) {
+        const int b = min(bt * 16 + i, p.B - 1);
+        const uint4 a0 = act8<LDS>(p, act, b, kk);
+        const uint4 a1 = act8<LDS>(p, act, b, kk + 8);
+        dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), blo,
+                                                          dst[bt], 0, 0, 0);
+        dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), bhi,
+                                                          dst[bt], 0, 0, 0);
       }
     }
   }
-#pragma unroll
-  for (int bt = 0; bt < NT; ++bt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      red[(wave * NB + bt * 16 + 4 * (lane >> 4) + q) * 16 + (lane & 15)] = acc[bt][q];
-  __syncthreads();
-  finish_block<FMT, NB, GLU>(p, blk, rb, red);
-  __syncthreads();
-}
 
+  __device__ __forceinline__ void group_end(float s) {
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[bt][q] = fmaf(s, gacc[bt][q], acc[bt][q]);
+      gacc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  __device__ __forceinline__ void to_red(float* red, int wave) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        red[(wave * NB + bt * 16 + 4 * (lane >> 4) + q) * 16 + (lane & 15)] = acc[bt][q];
+  }
+};
+
+// Every wave walks the same flat sequence of items (row block, batch of kU
+// tiles of its K-slice); item j+1's tiles are requested before item j is
+// computed, so two batches stay in flight across row-block boundaries and the
+// first batch is in flight while the activations are being staged.
 // GLU selects the SwiGLU epilogue at compile time (its own kernel symbol, so
 // the gate/up GEMVs can be told apart in a profile).
 template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
@@ -428,12 +415,90 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
   float* red = reinterpret_cast<float*>(smem);                       // [kWaves][NB][16]
   float* ss_buf = red + kWaves * NB * 16;                            // [lds_rows][kWaves]
   uint16_t* act = reinterpret_cast<uint16_t*>(ss_buf + M3_MAX_B * kWaves);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int TPU = FMT == M3_I8G128 ? 2 : 1;    // tiles per unit of the K split
+  constexpr int TK = FMT == M3_BF16 ? 32 : 64;     // K elements per tile
+  const int units = p.T / TPU;
+  const int t_lo = (units * wave / kWaves) * TPU;
+  const int ntw = (units * (wave + 1) / kWaves) * TPU - t_lo;       // tiles of this wave
+  const int nbat = ((units + kWaves - 1) / kWaves * TPU + kU - 1) / kU;   // same for all waves
+  const int my_blocks = (p.nblocks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const int nitems = my_blocks * nbat;
+
+  // Every wave walks nbat * kU tiles per row block.  Tiles past the end of its
+  // K-slice, and the prefetch past the last item, are out-of-range buffer
+  // loads (zeros, no memory traffic); their operand is the zero tile, so they
+  // add exactly nothing.  The loop has no data-dependent branches, so the
+  // compiler's waits let both batches stay in flight.
+  const __amdgpu_buffer_rsrc_t wr = weight_rsrc(p.w, (uint32_t)((size_t)p.nblocks * p.bbytes));
+  const uint32_t vlane = (uint32_t)lane * 16u, vlane_oob = vlane + kOob;
+  const int G = p.K / 128;                 // groups per row (i8g128)
+  auto load = [&](uint4* dst, float* sc, int j) {
+    const bool live = j < nitems;
+    const int rb = blockIdx.x + (j / nbat) * gridDim.x, bi = j % nbat;
+    const uint32_t base = (uint32_t)((size_t)rb * p.bbytes) + (uint32_t)t_lo * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int tt = bi * kU + i;
+      const bool real = live && tt < ntw;
+      dst[i] = ldw(wr, real ? vlane : vlane_oob, real ? base + (uint32_t)tt * kTileBytes : 0u);
+    }
+    if constexpr (FMT == M3_I8G128) {
+      // scales of this batch's kU/2 groups for row lane%16 ([row][group]
+      // layout); one dword each so a group past the slice reads a zero
+      const uint32_t g0 = (uint32_t)(t_lo + bi * kU) >> 1;
+      const uint32_t sbase = (uint32_t)((size_t)rb * p.bbytes) + (uint32_t)p.T * kTileBytes + g0 * 4u;
+      const uint32_t vrow = (uint32_t)(lane & 15) * (uint32_t)G * 4u;
+#pragma unroll
+      for (int q = 0; q < kU / 2; ++q) {
+        const bool real = live && bi * kU + 2 * q < ntw;
+        sc[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            wr, real ? vrow : vrow + kOob, real ? sbase + 4u * q : 0u, 0));
+      }
+    }
+  };
+
+  Accum<FMT, NB, MFMA> A;
+  A.reset();
+  auto compute = [&](const uint4* src, const float* scv, int j) {
+    const int rb = blockIdx.x + (j / nbat) * gridDim.x, bi = j % nbat;
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int tt = bi * kU + i;
+      const bool real = tt < ntw;
+      A.template tile<LDS>(p, act, src[i], real ? (t_lo + tt) * TK : p.Kp);
+      if (FMT == M3_I8G128 && (i & 1)) {
+        // groups are tile pairs (t_lo and kU are even): scale the finished group
+        A.group_end(real ? scv[i >> 1] : 0.f);
+      }
+    }
+    if (bi == nbat - 1) {          // row block complete: cross-wave sum and epilogue
+      A.to_red(red, wave);
+      __syncthreads();
+      finish_block<FMT, NB, GLU>(p, p.w + (size_t)rb * p.bbytes, rb, red);
+      __syncthreads();
+      A.reset();
+    }
+  };
+
+  uint4 bufA[kU], bufB[kU];
+  float scA[kU / 2], scB[kU / 2];
+  load(bufA, scA, 0);
   if (LDS) stage_activations(p, act, ss_buf);
-  for (int rb = blockIdx.x; rb < p.nblocks; rb += gridDim.x) {
-    if constexpr (MFMA)
-      mfma_block<FMT, NB / 16, LDS, GLU>(p, act, red, rb);
-    else
-      valu_block<FMT, NB, LDS, GLU>(p, act, red, rb);
+  if constexpr (kDoubleBuffer) {
+    for (int j = 0; j < nitems; j += 2) {
+      load(bufB, scB, j + 1);
+      compute(bufA, scA, j);
+      if (j + 1 >= nitems) break;
+      load(bufA, scA, j + 2);
+      compute(bufB, scB, j + 1);
+    }
+  } else {
+    for (int j = 0; j < nitems; ++j) {
+      if (j > 0) load(bufA, scA, j);
+      compute(bufA, scA, j);
+    }
   }
 }
 
@@ -505,7 +570,7 @@ size_t fixed_smem(int NB) { return (size_t)kWaves * NB * 16 * 4 + (size_t)M3_MAX
 
 size_t gemv_smem_bytes(int fmt, int K, int B, bool has_gamma) {
   const size_t fixed = fixed_smem(nb_of(B));
-  const size_t act = (size_t)B * (k_pad(fmt, K) + 8) * 2;
+  const size_t act = (size_t)B * (k_pad(fmt, K) + tile_k(fmt) + 8) * 2;
   if (has_gamma || fixed + act <= 96 * 1024) return fixed + act;
   return fixed;
 }
@@ -545,6 +610,7 @@ hipError_t launch_gemv(const GemvDesc& d, hipStream_t s) {
   const size_t smem = gemv_smem_bytes(d.fmt, d.K, d.B, d.gamma != nullptr);
   const bool lds = smem > fixed;
   p.lds_rows = lds ? d.B : 0;
+  p.lds_stride = p.Kp + tile_k(d.fmt) + 8;
   // resident workgroups per CU from LDS (8 waves each, at most 2 per CU)
   int per_cu = (int)((160 * 1024) / (smem + 1024));
   per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void scale_kernel(PackParams p) {
     const float s = __fdiv_rn(amax, 127.0f);
     const int rb = n >> 4, r = n & 15;
     float* sc = reinterpret_cast<float*>(p.out + (size_t)rb * p.bbytes + (size_t)p.T * kTileBytes);
-    sc[FMT == M3_I8G128 ? g * 16 + r : r] = s;
+    sc[FMT == M3_I8G128 ? r * G + g : r] = s;
   }
 }
 
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
     const int k = t * 64 + (l >> 4) * 16;
     if (n < p.N && k < p.K) {
       const float* sc = reinterpret_cast<const float*>(blk + (size_t)p.T * kTileBytes);
-      const float s = FMT == M3_I8G128 ? sc[(k / 128) * 16 + (l & 15)] : sc[l & 15];
+      const float s = FMT == M3_I8G128 ? sc[(l & 15) * (p.K / 128) + k / 128] : sc[l & 15];
       const uint16_t* src = p.W + (size_t)src_row(p, n) * p.K + k;
       const uint4 a = *reinterpret_cast<const uint4*>(src);
       const uint4 b = *reinterpret_cast<const uint4*>(src + 8);

@@ -70,8 +70,9 @@ const char* m3_version(void);
  * lane of a 64-lane wave reads the whole tile contiguously.  K is zero-padded
  * to a whole tile and N to a whole block.  int8 blocks end with their fp32
  * scales: i8row: scale[r] for r = 0..15 (64 B, then 64 B padding);
- * i8g128: scale[g][r] for every group g of 128 (K/128 x 64 B, rounded up to
- * 128 B).  int8 codes are two's-complement bytes in [-127, 127].
+ * i8g128: scale[r][g] for the 16 rows and every group g of 128 along K
+ * (16 x K/128 floats, rounded up to 128 B).  int8 codes are two's-complement
+ * bytes in [-127, 127].  A packed matrix must be smaller than 2 GiB.
  *
  * Quantisation (int8): scale = absmax / 127 as one fp32 division; q is the
  * nearest integer of W/scale (ties to even), clamped to [-127, 127]; an

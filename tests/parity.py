@@ -109,5 +109,5 @@ def unpack(packed: np.ndarray, fmt: int, N: int, K: int):
         s = sc[:, :64].view(np.float32).reshape(nb * 16)
     else:
         G = K // 128
-        s = sc[:, : G * 64].view(np.float32).reshape(nb, G, 16).transpose(0, 2, 1).reshape(nb * 16, G)
+        s = sc[:, : G * 64].view(np.float32).reshape(nb * 16, G)
     return q[:N, :K], s[:N]
