@@ -62,7 +62,7 @@ class Model(ctypes.Structure):
 
 class FrameLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("x", "h", "qkv", "mlp", "logits", "u", "hd", "dqkv",
-                                               "dmlp", "dlogits", "ring", "frame", "sample_ws",
+                                               "dmlp", "dlogits", "ring", "frame", "part_sem", "part_dep",
                                                "total")]
 
 

@@ -180,8 +180,8 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.dlogits = take((size_t)B * d.CV * 4);
   L.ring = take((size_t)16 * B * 8 * 4);
   L.frame = take(4);
-  const size_t ws0 = sample_ws_bytes(B, d.V0), ws1 = sample_ws_bytes(B, d.CV);
-  L.sample_ws = take(ws0 > ws1 ? ws0 : ws1);
+  L.part_sem = take((size_t)B * n_blocks(d.V0) * sizeof(Best));
+  L.part_dep = take((size_t)B * n_blocks(d.CV) * sizeof(Best));
   L.total = off;
   return L;
 }
@@ -228,12 +228,14 @@ int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStrea
   float* dlogits = reinterpret_cast<float*>(S + L.dlogits);
   int32_t* ring = reinterpret_cast<int32_t*>(S + L.ring);
   uint32_t* frame = reinterpret_cast<uint32_t*>(S + L.frame);
-  void* ws = S + L.sample_ws;
+  Best* part_sem = reinterpret_cast<Best*>(S + L.part_sem);
+  Best* part_dep = reinterpret_cast<Best*>(S + L.part_dep);
   const float eps = c.eps;
   auto gemv = [&](int fmt, const void* w, int N, int K, const uint16_t* xin, int ldx,
                   const float* gamma, int sg, int sv, void* y, int ldy, int f32, int epi,
-                  const uint16_t* res, int ldr) {
-    GemvDesc g{fmt, w, N, K, xin, ldx, B, gamma, eps, sg, sv, y, ldy, f32, epi, res, ldr};
+                  const uint16_t* res, int ldr, const SampleEpi* smp = nullptr,
+                  const GatherPro* gat = nullptr) {
+    GemvDesc g{fmt, w, N, K, xin, ldx, B, gamma, eps, sg, sv, y, ldy, f32, epi, res, ldr, smp, gat};
     return launch_gemv(g, s);
   };
   // ---- body ----
@@ -250,36 +252,33 @@ int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStrea
     M3_TRY(gemv(c.fmt_body, W.down, d.H, d.F, mlp, d.F, nullptr, 0, 0, h, d.H, 0,
                 M3_EPI_RESIDUAL, h, d.H));
   }
-  // ---- sliced lm_head + semantic draw ----
+  // ---- sliced lm_head; its epilogue adds the Gumbel noise of draw 0 and
+  // leaves each row block's winner; the draw completes in the next consumer
+  SampleEpi sem{c.seed, frame, 0u, c.temperature, c.vocab_base, c.vocab_base,
+                c.vocab_base + c.n_slice, part_sem};
   M3_TRY(gemv(c.fmt_lm, m->lm_head, d.V0, d.H, h, d.H, m->final_norm, 0, 0, logits, d.V0, 1,
-              M3_EPI_NONE, nullptr, 0));
-  SampleDesc sd{};
-  sd.logits = logits;
-  sd.B = B;
-  sd.V = d.V0;
-  sd.ldl = d.V0;
-  sd.seed = c.seed;
-  sd.frame_dev = frame;
-  sd.draw = 0;
-  sd.temperature = c.temperature;
-  sd.index_base = c.vocab_base;
-  sd.valid_lo = c.vocab_base;
-  sd.valid_hi = c.vocab_base + c.n_slice;
-  sd.out = codes;
-  sd.out_stride = 8;
-  sd.ws = ws;
-  M3_TRY(launch_sample(sd, s));
+              M3_EPI_NONE, nullptr, 0, &sem));
   // ---- depth decoder ----
   M3_TRY(gemv(c.fmt_depth, m->p_in, d.D, d.H, h, d.H, m->final_norm, 0, 0, u, d.D, 0,
               M3_EPI_NONE, nullptr, 0));
   for (int j = 1; j < d.ncb; ++j) {
-    const uint16_t* E = j == 1 ? m->emb1 : m->emb[j - 2];
-    M3_TRY(launch_depth_input(u, E, codes, j - 1, j == 1 ? c.vocab_base : 0,
-                              j == 1 ? c.n_slice : c.code_vocab, B, d.D, hd, s));
+    // step j's input: bf16(u + Emb_j[previous code]); the previous draw is
+    // finished from its row-block winners in the prologue of the first GEMV
+    GatherPro gp;
+    gp.u = u;
+    gp.emb = j == 1 ? m->emb1 : m->emb[j - 2];
+    gp.part = j == 1 ? part_sem : part_dep;
+    gp.nparts = j == 1 ? n_blocks(d.V0) : n_blocks(d.CV);
+    gp.index_base = j == 1 ? c.vocab_base : 0;
+    gp.code_base = j == 1 ? c.vocab_base : 0;
+    gp.n_codes = j == 1 ? c.n_slice : c.code_vocab;
+    gp.codes = codes;
+    gp.code_col = j - 1;
+    gp.out = hd;
     for (int l = 0; l < c.d_layers; ++l) {
       const m3_layer_weights& W = m->d_layers_w[l];
       M3_TRY(gemv(c.fmt_depth, W.qkv, d.dqkv, d.D, hd, d.D, W.attn_norm, 0, 0, dqkv, d.dqkv, 0,
-                  M3_EPI_NONE, nullptr, 0));
+                  M3_EPI_NONE, nullptr, 0, nullptr, l == 0 ? &gp : nullptr));
       M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd, d.D, 0,
                   M3_EPI_RESIDUAL, hd, d.D));
       M3_TRY(gemv(c.fmt_depth, W.gate_up, 2 * d.Fd, d.D, hd, d.D, W.ffn_norm, 0, 0, dmlp, d.Fd, 0,
@@ -287,21 +286,13 @@ int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStrea
       M3_TRY(gemv(c.fmt_depth, W.down, d.D, d.Fd, dmlp, d.Fd, nullptr, 0, 0, hd, d.D, 0,
                   M3_EPI_RESIDUAL, hd, d.D));
     }
+    SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep};
     M3_TRY(gemv(c.fmt_depth, m->heads[j - 1], d.CV, d.D, hd, d.D, m->d_final_norm, 0, 0, dlogits,
-                d.CV, 1, M3_EPI_NONE, nullptr, 0));
-    SampleDesc dd = sd;
-    dd.logits = dlogits;
-    dd.V = d.CV;
-    dd.ldl = d.CV;
-    dd.draw = (uint32_t)j;
-    dd.index_base = 0;
-    dd.valid_lo = dd.valid_hi = 0;
-    dd.out = codes + j;
-    M3_TRY(launch_sample(dd, s));
+                d.CV, 1, M3_EPI_NONE, nullptr, 0, &dep));
   }
-  // ---- feedback, code ring, frame counter ----
-  M3_TRY(launch_feedback(m->tok_emb_audio, m->audio_emb, codes, c.vocab_base, c.n_slice,
-                         c.code_vocab, d.ncb, B, d.H, x, ring, frame, s));
+  // ---- last draw, feedback, code ring, frame counter ----
+  M3_TRY(launch_feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, n_blocks(d.CV),
+                         c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame, s));
   return M3_OK;
 }
 

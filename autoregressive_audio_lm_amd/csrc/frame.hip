@@ -1,6 +1,6 @@
-// frame.hip -- the small per-frame kernels around the GEMVs: depth-decoder
-// input embedding, frame-embedding feedback with the GPU-side frame counter
-// and 16-frame code ring, and state initialisation.
+// frame.hip -- the small per-frame kernels around the GEMVs: the last draw
+// and the frame-embedding feedback with the GPU-side frame counter and the
+// 16-frame code ring, and state initialisation.
 //
 // DiffSynth-Studio MiniMax-Music3 article, stage 2: after the semantic code,
 // the RVQ depth decoder draws the remaining 7 codes one codebook at a time;
@@ -21,34 +21,12 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return u >> 16;
 }
 
-// d[b, :] = bf16(u[b, :] + E[c, :]), c = codes[b*8 + col] - base (0 if out of range)
-__global__ __launch_bounds__(256) void depth_input_kernel(const uint16_t* u, const uint16_t* E,
-                                                          const int32_t* codes, int col,
-                                                          int32_t base, int n_codes, int B,
-                                                          int D, uint16_t* out) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;   // one thread per 8 elements
-  const int per_row = D >> 3;
-  if (idx >= (long)B * per_row) return;
-  const int b = (int)(idx / per_row), k = (int)(idx % per_row) * 8;
-  int c = codes[b * 8 + col] - base;
-  if (c < 0 || c >= n_codes) c = 0;
-  const uint4 uv = *reinterpret_cast<const uint4*>(u + (size_t)b * D + k);
-  const uint4 ev = *reinterpret_cast<const uint4*>(E + (size_t)c * D + k);
-  const uint32_t a[4] = {uv.x, uv.y, uv.z, uv.w}, e[4] = {ev.x, ev.y, ev.z, ev.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = f2bf(bf2f(a[j] & 0xffffu) + bf2f(e[j] & 0xffffu));
-    const uint32_t hi = f2bf(bf2f(a[j] >> 16) + bf2f(e[j] >> 16));
-    o[j] = lo | (hi << 16);
-  }
-  *reinterpret_cast<uint4*>(out + (size_t)b * D + k) = make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 struct FeedbackArgs {
   const uint16_t* tok;           // [n_slice, H]
   const uint16_t* aemb[8];       // [code_vocab, H] for codebooks 1..n_cb-1
-  const int32_t* codes;          // [B, 8]
+  int32_t* codes;                // [B, 8]
+  const Best* last_part;         // [B, last_nparts] winners of the last head's row blocks
+  int last_nparts;
   int32_t vocab_base;
   int n_slice, code_vocab, n_cb, B, H;
   uint16_t* x;
@@ -56,11 +34,44 @@ struct FeedbackArgs {
   uint32_t* frame;
 };
 
+// the last codebook's draw for row b (same total order as the sampler)
+__device__ int last_code(const FeedbackArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  float bz = -INFINITY;
+  int bj = 0x7fffffff;
+  for (int c = lane; c < a.last_nparts; c += 64) {
+    const Best r = a.last_part[(size_t)b * a.last_nparts + c];
+    if (above(r.z, r.j, bz, bj)) {
+      bz = r.z;
+      bj = r.j;
+    }
+  }
+  best_reduce(bz, bj, 64);
+  return __shfl(bj, 0, 64);
+}
+
+// grid (H / 2048 blocks of 256 threads x 8 values, B).  Block (x, b) handles
+// row b; block (0, 0) also writes the last codes, the ring slot and bumps the
+// frame counter (it is the only reader of the counter in this kernel).
 __global__ __launch_bounds__(256) void feedback_kernel(FeedbackArgs a) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = a.H >> 3;
-  if (idx < (long)a.B * per_row) {
-    const int b = (int)(idx / per_row), k = (int)(idx % per_row) * 8;
+  __shared__ int c_last[M3_MAX_B_FRAME];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bsel = blockIdx.y;
+  const bool leader = blockIdx.x == 0 && blockIdx.y == 0;
+  // every block needs its own row's last code; the leader needs all of them
+  if (leader) {
+    for (int b = wave; b < a.B; b += 4) {
+      const int c = last_code(a, b);
+      if (lane == 0) c_last[b] = c;
+    }
+  } else if (wave == 0) {
+    const int c = last_code(a, bsel);
+    if (lane == 0) c_last[bsel] = c;
+  }
+  __syncthreads();
+  {
+    const int b = bsel, k = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (k < a.H) {
     int c0 = a.codes[b * 8] - a.vocab_base;
     if (c0 < 0 || c0 >= a.n_slice) c0 = 0;
     float acc[8];
@@ -72,7 +83,7 @@ __global__ __launch_bounds__(256) void feedback_kernel(FeedbackArgs a) {
       acc[2 * j + 1] = bf2f(tv[j] >> 16);
     }
     for (int cb = 1; cb < a.n_cb; ++cb) {
-      int c = a.codes[b * 8 + cb];
+      int c = cb == a.n_cb - 1 ? c_last[b] : a.codes[b * 8 + cb];
       if (c < 0 || c >= a.code_vocab) c = 0;
       const uint4 v = *reinterpret_cast<const uint4*>(a.aemb[cb - 1] + (size_t)c * a.H + k);
       const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
@@ -87,12 +98,16 @@ __global__ __launch_bounds__(256) void feedback_kernel(FeedbackArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = f2bf(acc[2 * j] * sc) | (f2bf(acc[2 * j + 1] * sc) << 16);
     *reinterpret_cast<uint4*>(a.x + (size_t)b * a.H + k) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
-  if (blockIdx.x == 0) {
-    // ring slot of this frame, then advance the counter (only block 0 reads it)
+  if (leader) {
     const uint32_t f = *a.frame;
-    for (int i = threadIdx.x; i < a.B * 8; i += 256)
-      a.ring[(size_t)(f & 15u) * a.B * 8 + i] = a.codes[i];
+    for (int i = threadIdx.x; i < a.B * 8; i += 256) {
+      const int b = i >> 3, cb = i & 7;
+      const int32_t v = cb == a.n_cb - 1 ? c_last[b] : a.codes[i];
+      if (cb == a.n_cb - 1) a.codes[i] = v;
+      a.ring[(size_t)(f & 15u) * a.B * 8 + i] = v;
+    }
     __syncthreads();
     if (threadIdx.x == 0) *a.frame = f + 1u;
   }
@@ -110,21 +125,14 @@ __global__ __launch_bounds__(256) void fill_kernel(uint32_t* dst, uint32_t v, si
 
 }  // namespace
 
-hipError_t launch_depth_input(const uint16_t* u, const uint16_t* emb, const int32_t* codes,
-                              int code_col, int32_t code_base, int n_codes, int B, int D,
-                              uint16_t* out, hipStream_t s) {
-  const long n = (long)B * (D / 8);
-  hipLaunchKernelGGL(depth_input_kernel, dim3((int)((n + 255) / 256)), dim3(256), 0, s, u, emb,
-                     codes, code_col, code_base, n_codes, B, D, out);
-  return hipGetLastError();
-}
-
 hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const* audio_emb,
-                           const int32_t* codes, int32_t vocab_base, int n_slice,
-                           int code_vocab, int n_cb, int B, int H, uint16_t* x_out, int32_t* ring,
-                           uint32_t* frame, hipStream_t s) {
+                           int32_t* codes, const Best* last_part, int last_nparts,
+                           int32_t vocab_base, int n_slice, int code_vocab, int n_cb, int B,
+                           int H, uint16_t* x_out, int32_t* ring, uint32_t* frame, hipStream_t s) {
   FeedbackArgs a;
   a.code_vocab = code_vocab;
+  a.last_part = last_part;
+  a.last_nparts = last_nparts;
   a.tok = tok_emb_audio;
   for (int i = 0; i < 8; ++i) a.aemb[i] = (i < n_cb - 1) ? audio_emb[i] : nullptr;
   a.codes = codes;
@@ -136,8 +144,7 @@ hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const*
   a.x = x_out;
   a.ring = ring;
   a.frame = frame;
-  const long n = (long)B * (H / 8);
-  hipLaunchKernelGGL(feedback_kernel, dim3((int)((n + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(feedback_kernel, dim3((H + 2047) / 2048, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -57,6 +57,9 @@ struct Params {
   int ldr;
   int lds_rows;        // activation rows staged in LDS (0: direct global reads)
   int lds_stride;      // LDS row stride in elements: Kp + one zero tile + 8 (bank skew)
+  int has_sample, has_gather;
+  SampleEpi smp;       // sampling epilogue (logits GEMVs)
+  GatherPro gat;       // gather prologue (first GEMV of a depth step)
 };
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -106,48 +109,170 @@ __device__ __forceinline__ uint4 load_x8(const Params& p, int b, int k) {
   return *reinterpret_cast<const uint4*>(p.x + (size_t)b * p.ldx + src_col(p, k));
 }
 
-// Stage the operand rows in LDS (bf16, row stride Kp + 8), fusing the norm.
-__device__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf) {
+// Gather prologue: the previous draw of every batch row, from the per-block
+// winners the head GEMV wrote (rows b = wave, wave + 8, ... per wave).
+__device__ void gather_codes(const Params& p, int* code_lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const GatherPro& g = p.gat;
+  for (int b = wave; b < p.lds_rows; b += kWaves) {
+    float bz = -INFINITY;
+    int bj = 0x7fffffff;
+    for (int c = lane; c < g.nparts; c += 64) {
+      const Best r = g.part[(size_t)b * g.nparts + c];
+      if (above(r.z, r.j, bz, bj)) {
+        bz = r.z;
+        bj = r.j;
+      }
+    }
+    best_reduce(bz, bj, 64);
+    if (lane == 0) {
+      const int32_t id = g.index_base + bj;
+      code_lds[b] = id;
+      if (blockIdx.x == 0) g.codes[b * 8 + g.code_col] = id;
+    }
+  }
+  __syncthreads();
+}
+
+// Stage the operand rows in LDS (bf16, row stride lds_stride), fusing the
+// norm.  Row b's source is x (with the attention-stub remap) or, in gather
+// mode, bf16(u[b] + emb[code_b]).  Three flat passes over all rows so the
+// global loads of every row are in flight together: copy (8 chunks of 8
+// values per thread per step), per-row sum of squares (one wave per row, a
+// fixed order), normalise.
+constexpr int kStageUnroll = 8;
+
+__device__ __forceinline__ uint4 bf16x8_add(const uint4& a, const uint4& b) {
+  const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = f2bf(bf2f(ua[j] & 0xffffu) + bf2f(ub[j] & 0xffffu)) |
+           (f2bf(bf2f(ua[j] >> 16) + bf2f(ub[j] >> 16)) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// One or two rows: the copy also accumulates the sum of squares, spread over
+// all threads (row by row; a row's loads are all in flight together).
+__device__ void stage_rows_few(const Params& p, uint16_t* act, float* ss_buf, const int* code_lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int stride = p.lds_stride;
-  const int nchunk = (p.lds_stride - 8) >> 3;   // K, its padding and the zero tile
+  const int nchunk = (stride - 8) >> 3;
   for (int b = 0; b < p.lds_rows; ++b) {
+    const uint16_t* erow = nullptr;
+    if (p.has_gather) {
+      int c = code_lds[b] - p.gat.code_base;
+      if (c < 0 || c >= p.gat.n_codes) c = 0;
+      erow = p.gat.emb + (size_t)c * p.K;
+    }
     float ss = 0.f;
     for (int i = tid; i < nchunk; i += kThreads) {
       const int k = i << 3;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (k < p.K) v = load_x8(p, b, k);
-      *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v;
-      if (p.gamma) {
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float a0 = bf2f(wv[j] & 0xffffu), a1 = bf2f(wv[j] >> 16);
-          ss = fmaf(a0, a0, ss);
-          ss = fmaf(a1, a1, ss);
+      if (k < p.K) {
+        if (p.has_gather) {
+          v = bf16x8_add(*reinterpret_cast<const uint4*>(p.gat.u + (size_t)b * p.K + k),
+                         *reinterpret_cast<const uint4*>(erow + k));
+          if (blockIdx.x == 0) *reinterpret_cast<uint4*>(p.gat.out + (size_t)b * p.K + k) = v;
+        } else {
+          v = load_x8(p, b, k);
         }
       }
+      *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v;
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = bf2f(wv[j] & 0xffffu), a1 = bf2f(wv[j] >> 16);
+        ss = fmaf(a0, a0, ss);
+        ss = fmaf(a1, a1, ss);
+      }
     }
-    if (p.gamma) {
-      ss = wave_sum(ss);
-      if (lane == 0) ss_buf[b * kWaves + wave] = ss;
+    ss = wave_sum(ss);
+    if (lane == 0) ss_buf[M3_MAX_B + b * kWaves + wave] = ss;
+  }
+  __syncthreads();
+  if (p.gamma && tid < p.lds_rows) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += ss_buf[M3_MAX_B + tid * kWaves + w];
+    ss_buf[tid] = 1.0f / sqrtf(tot / (float)p.K + p.eps);
+  }
+}
+
+__device__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf, int* code_lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int stride = p.lds_stride;
+  const int cpr = (stride - 8) >> 3;            // chunks per row: K, padding, zero tile
+  const int total = p.lds_rows * cpr;
+  if (p.has_gather) gather_codes(p, code_lds);
+  if (p.lds_rows <= 2) {
+    stage_rows_few(p, act, ss_buf, code_lds);
+    if (!p.gamma) return;
+  } else {
+  // pass 1: copy
+  for (int base = tid; base < total; base += kThreads * kStageUnroll) {
+    uint4 v[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int it = base + u * kThreads;
+      const int b = it / cpr, k = (it - b * cpr) * 8;
+      const bool in = it < total && k < p.K;
+      const int bs = in ? b : 0, ks = in ? k : 0;
+      uint4 x;
+      if (p.has_gather) {
+        int c = code_lds[bs] - p.gat.code_base;
+        c = (c < 0 || c >= p.gat.n_codes) ? 0 : c;
+        const uint4 uv = *reinterpret_cast<const uint4*>(p.gat.u + (size_t)bs * p.K + ks);
+        const uint4 ev = *reinterpret_cast<const uint4*>(p.gat.emb + (size_t)c * p.K + ks);
+        x = bf16x8_add(uv, ev);
+      } else {
+        x = load_x8(p, bs, ks);
+      }
+      v[u] = in ? x : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int it = base + u * kThreads;
+      if (it < total) {
+        const int b = it / cpr, k = (it - b * cpr) * 8;
+        *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v[u];
+        if (p.has_gather && blockIdx.x == 0 && k < p.K)
+          *reinterpret_cast<uint4*>(p.gat.out + (size_t)b * p.K + k) = v[u];
+      }
     }
   }
   __syncthreads();
   if (!p.gamma) return;
-  for (int b = 0; b < p.lds_rows; ++b) {
-    float tot = 0.f;
+  // pass 2: r_b from the sum of squares of row b
+  for (int b = wave; b < p.lds_rows; b += kWaves) {
+    const int kc = p.K >> 3;
+    float ss = 0.f;
+    for (int c = lane; c < kc; c += 64) {
+      const uint4 v = *reinterpret_cast<const uint4*>(act + (size_t)b * stride + c * 8);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += ss_buf[b * kWaves + w];
-    const float r = 1.0f / sqrtf(tot / (float)p.K + p.eps);
-    for (int i = tid; i < nchunk; i += kThreads) {
-      const int k = i << 3;
-      if (k >= p.K) continue;
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = bf2f(wv[j] & 0xffffu), a1 = bf2f(wv[j] >> 16);
+        ss = fmaf(a0, a0, ss);
+        ss = fmaf(a1, a1, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) ss_buf[b] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+  }
+  }
+  __syncthreads();
+  // pass 3: a = bf16(x * r_b * gamma); gamma is loaded once per chunk
+  const int kc = p.K >> 3;
+  for (int i = tid; i < kc; i += kThreads) {
+    const int k = i * 8;
+    const float4 g0 = *reinterpret_cast<const float4*>(p.gamma + k);
+    const float4 g1 = *reinterpret_cast<const float4*>(p.gamma + k + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    for (int b = 0; b < p.lds_rows; ++b) {
+      const float r = ss_buf[b];
       uint4* ptr = reinterpret_cast<uint4*>(act + (size_t)b * stride + k);
-      uint4 v = *ptr;
-      const float4 g0 = *reinterpret_cast<const float4*>(p.gamma + k);
-      const float4 g1 = *reinterpret_cast<const float4*>(p.gamma + k + 4);
-      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const uint4 v = *ptr;
       uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -215,6 +340,36 @@ __device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const 
     }
     return;
   }
+  if (p.has_sample) {
+    // logits, then each batch row's best (z, column) over this block's rows;
+    // the 16 rows of a batch row are 16 consecutive lanes of one wave
+    const SampleEpi& sm = p.smp;
+    const uint32_t frame = *sm.frame;
+    const float inv_t = inv_temperature(sm.temperature);
+    for (int t0 = 0; t0 < p.B * 16; t0 += kThreads) {
+      const int t = t0 + tid;
+      const int b = t >> 4, r = t & 15;
+      const int n = rb * 16 + r;
+      float z = -INFINITY;
+      int j = 0x7fffffff;
+      if (t < p.B * 16 && n < p.N) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += red[(w * NB + b) * 16 + r];
+        v *= row_scale<FMT>(blk, p, r);
+        reinterpret_cast<float*>(p.y)[(size_t)b * p.ldy + n] = v;
+        const int32_t id = sm.index_base + n;
+        j = n;
+        if (sm.valid_lo < sm.valid_hi && (id < sm.valid_lo || id >= sm.valid_hi))
+          z = -INFINITY;
+        else
+          z = gumbel_z(v, inv_t, gumbel_noise(sm.seed, (uint32_t)b, frame, sm.draw, (uint32_t)id));
+      }
+      best_reduce(z, j, 16);
+      if (t < p.B * 16 && r == 0) sm.part[(size_t)b * p.nblocks + rb] = Best{z, j};
+    }
+    return;
+  }
   for (int t = tid; t < p.B * 16; t += kThreads) {
     const int b = t >> 4, r = t & 15;
     const int n = rb * 16 + r;
@@ -251,15 +406,9 @@ __device__ __forceinline__ uint4 ldw(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-#ifndef M3_GEMV_KU
-#define M3_GEMV_KU 8
-#endif
-#ifndef M3_GEMV_DOUBLE_BUFFER
-#define M3_GEMV_DOUBLE_BUFFER 1
-#endif
-constexpr int kU = M3_GEMV_KU;   // tiles per batch
-constexpr bool kDoubleBuffer = M3_GEMV_DOUBLE_BUFFER;   // a second batch in flight
-static_assert(kU % 2 == 0 && kU <= 16, "batches hold whole i8g128 groups");
+// Tiles per batch (KU) is a kernel parameter: 8 for long K slices, 4 where a
+// wave's K slice is short (fewer padding tiles).  A wave keeps two batches in
+// flight.
 
 // ---------------------------------------------------------------------------
 // VALU accumulators: NB activation rows (B <= NB); lane = (row l%16, K-chunk
@@ -409,12 +558,15 @@ struct Accum<FMT, NB, true> {
 // first batch is in flight while the activations are being staged.
 // GLU selects the SwiGLU epilogue at compile time (its own kernel symbol, so
 // the gate/up GEMVs can be told apart in a profile).
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
+template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
+  constexpr int kU = KU;
+  static_assert(kU % 2 == 0 && kU <= 16, "batches hold whole i8g128 groups");
   extern __shared__ __align__(16) uint8_t smem[];
   float* red = reinterpret_cast<float*>(smem);                       // [kWaves][NB][16]
   float* ss_buf = red + kWaves * NB * 16;                            // [lds_rows][kWaves]
-  uint16_t* act = reinterpret_cast<uint16_t*>(ss_buf + M3_MAX_B * kWaves);
+  int* code_lds = reinterpret_cast<int*>(ss_buf + M3_MAX_B * kWaves);  // [M3_MAX_B]
+  uint16_t* act = reinterpret_cast<uint16_t*>(code_lds + M3_MAX_B);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int TPU = FMT == M3_I8G128 ? 2 : 1;    // tiles per unit of the K split
@@ -485,42 +637,54 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
   uint4 bufA[kU], bufB[kU];
   float scA[kU / 2], scB[kU / 2];
   load(bufA, scA, 0);
-  if (LDS) stage_activations(p, act, ss_buf);
-  if constexpr (kDoubleBuffer) {
-    for (int j = 0; j < nitems; j += 2) {
-      load(bufB, scB, j + 1);
-      compute(bufA, scA, j);
-      if (j + 1 >= nitems) break;
-      load(bufA, scA, j + 2);
-      compute(bufB, scB, j + 1);
-    }
-  } else {
-    for (int j = 0; j < nitems; ++j) {
-      if (j > 0) load(bufA, scA, j);
-      compute(bufA, scA, j);
-    }
+  if (LDS) stage_activations(p, act, ss_buf, code_lds);
+  // the scheduling barriers keep each batch's loads ahead of the previous
+  // batch's arithmetic (the scheduler would otherwise sink them into it)
+  for (int j = 0; j < nitems; j += 2) {
+    load(bufB, scB, j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bufA, scA, j);
+    if (j + 1 >= nitems) break;
+    load(bufA, scA, j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bufB, scB, j + 1);
   }
 }
 
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
+template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
 hipError_t configure_one() {
   static hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(gemv_kernel<FMT, NB, MFMA, LDS, GLU>),
+      reinterpret_cast<const void*>(gemv_kernel<FMT, NB, MFMA, LDS, GLU, KU>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   return status;
 }
 
+template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
+hipError_t launch_ku(const Params& p, int grid, size_t smem, hipStream_t s) {
+  const hipError_t e = configure_one<FMT, NB, MFMA, LDS, GLU, KU>();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemv_kernel<FMT, NB, MFMA, LDS, GLU, KU>), dim3(grid), dim3(kThreads), smem,
+                     s, p);
+  return hipGetLastError();
+}
+
+// short K slices take batches of 4 (only with staged activations)
+template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
+hipError_t launch_epi(const Params& p, int grid, size_t smem, hipStream_t s, bool ku4) {
+  if constexpr (LDS) {
+    if (ku4) return launch_ku<FMT, NB, MFMA, LDS, GLU, 4>(p, grid, smem, s);
+  }
+  return launch_ku<FMT, NB, MFMA, LDS, GLU, 8>(p, grid, smem, s);
+}
+
 template <int FMT, int NB, bool MFMA, bool LDS>
 hipError_t launch_one(const Params& p, int grid, size_t smem, hipStream_t s) {
-  const bool glu = p.epi == M3_EPI_SWIGLU;
-  const hipError_t e = glu ? configure_one<FMT, NB, MFMA, LDS, true>()
-                           : configure_one<FMT, NB, MFMA, LDS, false>();
-  if (e != hipSuccess) return e;
-  if (glu)
-    hipLaunchKernelGGL((gemv_kernel<FMT, NB, MFMA, LDS, true>), dim3(grid), dim3(kThreads), smem, s, p);
-  else
-    hipLaunchKernelGGL((gemv_kernel<FMT, NB, MFMA, LDS, false>), dim3(grid), dim3(kThreads), smem, s, p);
-  return hipGetLastError();
+  // padding tiles per wave with batches of 4 vs 8: prefer 4 when it pads less
+  const int tpu = FMT == M3_I8G128 ? 2 : 1;
+  const int tpw = (p.T / tpu + kWaves - 1) / kWaves * tpu;
+  const bool ku4 = (tpw + 3) / 4 * 4 < (tpw + 7) / 8 * 8;
+  if (p.epi == M3_EPI_SWIGLU) return launch_epi<FMT, NB, MFMA, LDS, true>(p, grid, smem, s, ku4);
+  return launch_epi<FMT, NB, MFMA, LDS, false>(p, grid, smem, s, ku4);
 }
 
 template <int FMT, bool LDS>
@@ -536,16 +700,25 @@ hipError_t dispatch_b(const Params& p, int grid, size_t smem, hipStream_t s) {
   return launch_one<FMT, 64, true, LDS>(p, grid, smem, s);
 }
 
-template <int FMT, bool LDS, bool GLU>
-hipError_t configure_epi() {
+template <int FMT, bool LDS, bool GLU, int KU>
+hipError_t configure_ku() {
   const hipError_t es[] = {
-      configure_one<FMT, 1, false, LDS, GLU>(),  configure_one<FMT, 2, false, LDS, GLU>(),
-      configure_one<FMT, 4, false, LDS, GLU>(),  configure_one<FMT, 8, false, LDS, GLU>(),
-      configure_one<FMT, 16, true, LDS, GLU>(),  configure_one<FMT, 32, true, LDS, GLU>(),
-      configure_one<FMT, 48, true, LDS, GLU>(),  configure_one<FMT, 64, true, LDS, GLU>()};
+      configure_one<FMT, 1, false, LDS, GLU, KU>(),  configure_one<FMT, 2, false, LDS, GLU, KU>(),
+      configure_one<FMT, 4, false, LDS, GLU, KU>(),  configure_one<FMT, 8, false, LDS, GLU, KU>(),
+      configure_one<FMT, 16, true, LDS, GLU, KU>(),  configure_one<FMT, 32, true, LDS, GLU, KU>(),
+      configure_one<FMT, 48, true, LDS, GLU, KU>(),  configure_one<FMT, 64, true, LDS, GLU, KU>()};
   for (hipError_t e : es)
     if (e != hipSuccess) return e;
   return hipSuccess;
+}
+
+template <int FMT, bool LDS, bool GLU>
+hipError_t configure_epi() {
+  hipError_t e = configure_ku<FMT, LDS, GLU, 8>();
+  if constexpr (LDS) {
+    if (e == hipSuccess) e = configure_ku<FMT, LDS, GLU, 4>();
+  }
+  return e;
 }
 
 template <int FMT, bool LDS>
@@ -564,14 +737,16 @@ int nb_of(int B) {
   return (B + 15) / 16 * 16;
 }
 
-size_t fixed_smem(int NB) { return (size_t)kWaves * NB * 16 * 4 + (size_t)M3_MAX_B * kWaves * 4; }
+size_t fixed_smem(int NB) {
+  return (size_t)kWaves * NB * 16 * 4 + (size_t)M3_MAX_B * kWaves * 4 + (size_t)M3_MAX_B * 4;
+}
 
 }  // namespace
 
 size_t gemv_smem_bytes(int fmt, int K, int B, bool has_gamma) {
   const size_t fixed = fixed_smem(nb_of(B));
   const size_t act = (size_t)B * (k_pad(fmt, K) + tile_k(fmt) + 8) * 2;
-  if (has_gamma || fixed + act <= 96 * 1024) return fixed + act;
+  if (has_gamma || fixed + act <= 160 * 1024) return fixed + act;
   return fixed;
 }
 
@@ -611,6 +786,11 @@ hipError_t launch_gemv(const GemvDesc& d, hipStream_t s) {
   const bool lds = smem > fixed;
   p.lds_rows = lds ? d.B : 0;
   p.lds_stride = p.Kp + tile_k(d.fmt) + 8;
+  p.has_sample = d.sample != nullptr;
+  p.has_gather = d.gather != nullptr;
+  if (d.sample) p.smp = *d.sample;
+  if (d.gather) p.gat = *d.gather;
+  if (d.gather && !lds) return hipErrorInvalidValue;   // the gather stages through LDS
   // resident workgroups per CU from LDS (8 waves each, at most 2 per CU)
   int per_cu = (int)((160 * 1024) / (smem + 1024));
   per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/m3.h"
+#include "m3_sampling.h"
 
 namespace m3 {
 
@@ -26,6 +27,35 @@ __host__ __device__ inline size_t block_bytes(int fmt, int K) {
 }
 
 // ---- GEMV launch description -------------------------------------------------
+// Gumbel sampling epilogue of a logits GEMV (fp32 out): besides the logits,
+// every row block writes the best (z, column) of its 16 rows for each batch
+// row to part[b * nblocks + block].
+struct SampleEpi {
+  uint64_t seed;
+  const uint32_t* frame;        // device frame counter
+  uint32_t draw;
+  float temperature;
+  int32_t index_base;           // absolute id of output row 0
+  int32_t valid_lo, valid_hi;   // lo == hi: no mask
+  Best* part;
+};
+
+// Gather prologue of the first GEMV of a depth-decoder step: the operand row
+// b is bf16(u[b] + emb[c_b]) with c_b = index_base + argmax of part[b][*]
+// (the previous draw) minus code_base (0 if out of range).  Workgroup 0 also
+// writes the rows to out (the step's residual stream) and the drawn absolute
+// id to codes[b * 8 + code_col].
+struct GatherPro {
+  const uint16_t* u;
+  const uint16_t* emb;
+  const Best* part;
+  int nparts;
+  int32_t index_base, code_base, n_codes;
+  int32_t* codes;
+  int code_col;
+  uint16_t* out;
+};
+
 struct GemvDesc {
   int fmt;
   const void* w;
@@ -40,6 +70,8 @@ struct GemvDesc {
   int epi;
   const uint16_t* res;
   int ldr;
+  const SampleEpi* sample = nullptr;
+  const GatherPro* gather = nullptr;
 };
 
 // Largest fused-norm activation block held in LDS (elements of B * K_pad).
@@ -74,14 +106,14 @@ size_t sample_ws_bytes(int B, int V);
 hipError_t launch_sample(const SampleDesc& d, hipStream_t s);
 
 // ---- frame helpers -------------------------------------------------------------
-hipError_t launch_depth_input(const uint16_t* u, const uint16_t* emb, const int32_t* codes,
-                              int code_col, int32_t code_base, int n_codes, int B, int D,
-                              uint16_t* out, hipStream_t s);
 // audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)
+// Final draw of the last codebook from the head's per-block winners, then the
+// frame embedding x' = bf16((E_tok[c0] + sum_j A_j[c_j]) * 8^-1/2), the code
+// ring slot of this frame and the frame counter.
 hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const* audio_emb,
-                           const int32_t* codes, int32_t vocab_base, int n_slice,
-                           int code_vocab, int n_cb, int B, int H, uint16_t* x_out, int32_t* ring,
-                           uint32_t* frame, hipStream_t s);
+                           int32_t* codes, const Best* last_part, int last_nparts,
+                           int32_t vocab_base, int n_slice, int code_vocab, int n_cb, int B,
+                           int H, uint16_t* x_out, int32_t* ring, uint32_t* frame, hipStream_t s);
 hipError_t launch_copy_bf16(const uint16_t* src, uint16_t* dst, size_t n, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, size_t n, hipStream_t s);
 

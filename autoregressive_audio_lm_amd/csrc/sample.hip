@@ -15,6 +15,7 @@
 // (z descending with NaN on top, then index ascending) is total, so the
 // result does not depend on how the reduction is arranged.
 #include "m3_internal.h"
+#include "m3_sampling.h"
 
 #pragma clang fp contract(off)
 
@@ -24,91 +25,11 @@ namespace {
 constexpr int kChunk = 1024;
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ void philox10(uint32_t c[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
-    }
-    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
-    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
-  }
-}
-
-// ln x for positive normal x: x = m 2^e with m in (1/sqrt2, sqrt2],
-// ln x = e ln2 + 2 atanh((m-1)/(m+1)), atanh t = t + t^3/3 + ... + t^11/11.
-__device__ __forceinline__ float log_fixed(float x) {
-  const uint32_t u = __float_as_uint(x);
-  int e = (int)((u >> 23) & 0xffu) - 127;
-  float m = __uint_as_float((u & 0x007fffffu) | 0x3f800000u);
-  if (m > (float)1.41421356237309504880) {
-    m = m * 0.5f;
-    e = e + 1;
-  }
-  const float f = m - 1.0f;
-  const float d = m + 1.0f;
-  const float t = f / d;
-  const float s = t * t;
-  float p = 1.0f / 11.0f;
-  p = __builtin_fmaf(p, s, 1.0f / 9.0f);
-  p = __builtin_fmaf(p, s, 1.0f / 7.0f);
-  p = __builtin_fmaf(p, s, 1.0f / 5.0f);
-  p = __builtin_fmaf(p, s, 1.0f / 3.0f);
-  const float sp = s * p;
-  const float r = sp * t;
-  float lm = t + r;
-  lm = lm + lm;
-  const float ef = (float)e;
-  constexpr float kLn2Hi = 0x1.62e4p-1f;
-  constexpr float kLn2Lo = (float)(0.69314718055994530942 - 0.693145751953125);
-  float res = __builtin_fmaf(ef, kLn2Lo, lm);
-  res = __builtin_fmaf(ef, kLn2Hi, res);
-  return res;
-}
-
-__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
-  const float uu = (float)(((w >> 9) << 1) | 1u) * 0x1p-24f;
-  const float l1 = log_fixed(uu);
-  const float l2 = log_fixed(-l1);
-  return -l2;
-}
-
-// true if (za, ia) ranks above (zb, ib)
-__device__ __forceinline__ bool above(float za, int ia, float zb, int ib) {
-  const bool an = za != za, bn = zb != zb;
-  if (an != bn) return an;
-  if (!an && za != zb) return za > zb;
-  return ia < ib;
-}
-
-__device__ __forceinline__ void wave_best(float& z, int& j) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float oz = __shfl_xor(z, o, 64);
-    const int oj = __shfl_xor(j, o, 64);
-    if (above(oz, oj, z, j)) {
-      z = oz;
-      j = oj;
-    }
-  }
-}
-
-struct Best {
-  float z;
-  int j;
-};
-
 __global__ __launch_bounds__(kThreads) void gumbel_partial(SampleDesc d) {
   const int b = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t frame = d.frame_dev ? *d.frame_dev : d.frame;
-  const float invT = 1.0f / d.temperature;
+  const float invT = inv_temperature(d.temperature);
   const uint32_t k0 = (uint32_t)d.seed, k1 = (uint32_t)(d.seed >> 32);
   float bz = -INFINITY;
   int bj = 0x7fffffff;
@@ -139,15 +60,14 @@ __global__ __launch_bounds__(kThreads) void gumbel_partial(SampleDesc d) {
         }
         g = gumbel_from_word(words[(uint32_t)id & 3u]);
       }
-      const float lt = d.logits[(size_t)b * d.ldl + j] * invT;
-      z = lt + g;
+      z = gumbel_z(d.logits[(size_t)b * d.ldl + j], invT, g);
     }
     if (above(z, j, bz, bj)) {
       bz = z;
       bj = j;
     }
   }
-  wave_best(bz, bj);
+  best_reduce(bz, bj, 64);
   __shared__ Best sb[kThreads / 64];
   if (lane == 0) sb[wave] = Best{bz, bj};
   __syncthreads();
@@ -171,7 +91,7 @@ __global__ __launch_bounds__(64) void gumbel_final(SampleDesc d, int nchunk) {
       bj = r.j;
     }
   }
-  wave_best(bz, bj);
+  best_reduce(bz, bj, 64);
   if (lane == 0) {
     // an all -inf row keeps every element tied at -inf: the lowest index wins
     const int j = bj;

@@ -229,7 +229,8 @@ typedef struct {
   size_t dlogits;  /* f32  [B, code_vocab] logits of the last depth draw       */
   size_t ring;     /* i32  [16, B, 8]    codes of the last 16 frames           */
   size_t frame;    /* u32  frame counter (advanced on the GPU)                 */
-  size_t sample_ws;/* sampler workspace                                        */
+  size_t part_sem; /* per-row-block winners of the semantic draw               */
+  size_t part_dep; /* per-row-block winners of the latest depth draw           */
   size_t total;
 } m3_frame_layout;
 

@@ -126,7 +126,7 @@ def test_frame_layout_and_refusals(L):
     c = make_config(cfg, **configs.PRESETS["A"])
     lay = _lib.FrameLayout()
     assert L.m3_frame_layout_get(ctypes.byref(c), 16, ctypes.byref(lay)) == 0
-    assert lay.total % 256 == 0 and lay.x == 0 and lay.total > lay.sample_ws
+    assert lay.total % 256 == 0 and lay.x == 0 and lay.total > lay.part_dep > lay.part_sem > lay.frame
     assert L.m3_frame_workspace_bytes(ctypes.byref(c), 17) == 0
     assert L.m3_frame_layout_get(ctypes.byref(c), 0, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
     c2 = make_config(cfg, 0, 2, 2)                                   # lm_head must be bf16/i8row

@@ -115,6 +115,25 @@ def test_graph_replay_equals_eager_and_resume(small):
     graphed.release()
 
 
+def test_fused_draws_equal_standalone_sampler(small):
+    """The draws finished inside the frame (sampling epilogue + gather
+    prologue) equal m3_gumbel_argmax run on the same frame's logits."""
+    from autoregressive_audio_lm_amd import m3
+    cfg, dm, om = small
+    B = 3
+    x0 = synth.activations(B, cfg["H"], 99).to(DEV)
+    st = runtime.FrameState(dm, B, x0, frame0=11)
+    st.decode()
+    torch.cuda.synchronize()
+    base = cfg["vocab_base"]
+    c0 = m3.gumbel_argmax(st.logits, seed=5, frame=11, draw=0, index_base=base,
+                          valid=(base, base + cfg["V0"]))
+    assert torch.equal(c0, st.codes[:, 0])
+    dl = st.view("dlogits", torch.float32, cfg["code_vocab"])
+    c7 = m3.gumbel_argmax(dl, seed=5, frame=11, draw=cfg["n_codebooks"] - 1)
+    assert torch.equal(c7, st.codes[:, cfg["n_codebooks"] - 1])
+
+
 def test_frame_repeat_byte_identical(small):
     cfg, dm, om = small
     B = 3
