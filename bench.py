@@ -29,6 +29,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode weight-stream GB/s (% of HBM peak) and frames/s at B=1/6/16"
 HBM_PEAK_GBS = 8000.0
+# Counter-derived HBM bytes of the dominant kernel; valid only for the kernel
+# sources it was measured on (their sha256 is recorded beside the figures).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_gate_up_bf16_B1.txt")
+KERNEL_SOURCES = ("gemv.hip", "m3_internal.h", "m3_sampling.h")
 
 
 def log(*a):
@@ -117,6 +121,48 @@ def time_gate_up(dm, st, stream, reps=3):
     return us, wbytes + 4 * H, n
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "autoregressive_audio_lm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the body gate/up GEMV from the committed
+    FETCH_SIZE/WRITE_SIZE passes, or None when the kernel sources changed
+    since those counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calib_copy(stream, nbytes=256 << 20, reps=3):
+    """A plain elementwise copy of known size (nbytes read, nbytes written),
+    the yardstick that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    with torch.cuda.stream(stream):
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(reps):
+            torch.neg(src, out=dst)
+        stream.synchronize()
+    del src, dst
+
+
 def cpu_baseline(cfg, L0, target_s: float):
     """The oracle (plain C, float64 sums) on one body layer of the same
     workload at B = 1, repeated to fill about target_s seconds."""
@@ -143,7 +189,7 @@ def cpu_baseline(cfg, L0, target_s: float):
     t0 = time.perf_counter()
     h = one_layer(x)
     t1 = time.perf_counter() - t0
-    reps = max(1, min(200, int(math.ceil(target_s / max(t1, 1e-3))) - 1))
+    reps = max(1, min(20000, int(math.ceil(target_s / max(t1, 1e-3))) - 1))
     t0 = time.perf_counter()
     for _ in range(reps):
         h = one_layer(h)
@@ -166,6 +212,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the B = 2/6/16 and int8 context points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 256 MiB elementwise copy (counter calibration runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -194,12 +242,15 @@ def main():
     us, kbytes, n = time_gate_up(dm, st, stream)
     k_gbs = kbytes / (us * 1e-6) / 1e9
     log(f"[bench] gate/up GEMV: {us:.2f} us per launch over {n} launches, {k_gbs:.1f} GB/s")
+    traffic = measured_traffic() if (args.preset == "A" and args.B == 1) else None
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "gemv_kernel<bf16, VALU, SwiGLU> (body gate/up, RMSNorm fused)"
                           if dm.fmt_body == 0 else "gemv_kernel<int8, SwiGLU> (body gate/up)",
                 "avg_us": round(us, 3), "bytes_per_launch": kbytes}
     st.release()
+    if args.calib_copy:
+        calib_copy(stream)
 
     sweep = []
     if not args.no_sweep:
