@@ -63,7 +63,7 @@ class Model(ctypes.Structure):
 class FrameLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("x", "h", "qkv", "mlp", "logits", "u", "hd", "dqkv",
                                                "dmlp", "dlogits", "ring", "frame", "part_sem", "part_dep",
-                                               "total")]
+                                               "flags", "err", "phases", "total")]
 
 
 _lib = None
@@ -88,6 +88,9 @@ _SIGS = {
     "m3_frame_graph_create": (_I, [ctypes.POINTER(Model), _P, _I, _P, _P, ctypes.POINTER(_P)]),
     "m3_frame_graph_launch": (_I, [_P, _P]),
     "m3_frame_graph_destroy": (_I, [_P]),
+    "m3_frame_persistent_create": (_I, [ctypes.POINTER(Model), _P, _I, _P, _P, ctypes.POINTER(_P)]),
+    "m3_frame_persistent_launch": (_I, [_P, _P]),
+    "m3_frame_persistent_destroy": (_I, [_P]),
 }
 
 SYMBOLS = tuple(_SIGS)

@@ -154,10 +154,17 @@ int validate_config(const m3_config* c, int B) {
   if (gemv_smem_bytes(fb, d.H, B, true) > kLdsMax || gemv_smem_bytes(c->fmt_lm, d.H, B, true) > kLdsMax ||
       gemv_smem_bytes(fd, d.H, B, true) > kLdsMax || gemv_smem_bytes(fd, d.D, B, true) > kLdsMax)
     return M3_ERR_SHAPE;
+  if (c->n_layers > 1000 || c->d_layers > 1000) return M3_ERR_SHAPE;
   return M3_OK;
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// phases of one frame: 4 GEMVs per body layer, lm_head, depth input, per depth
+// step 4 GEMVs per layer and the head, then the frame end
+int frame_phases(const m3_config& c) {
+  return 4 * c.n_layers + 2 + (c.n_codebooks - 1) * (4 * c.d_layers + 1) + 1;
+}
 
 m3_frame_layout layout_of(const m3_config& c, int B) {
   const Dims d = dims_of(c);
@@ -182,6 +189,9 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.frame = take(4);
   L.part_sem = take((size_t)B * n_blocks(d.V0) * sizeof(Best));
   L.part_dep = take((size_t)B * n_blocks(d.CV) * sizeof(Best));
+  L.flags = take((size_t)kPersistFlags * 4);
+  L.err = take(4);
+  L.phases = take((size_t)frame_phases(c) * persist_phase_bytes());
   L.total = off;
   return L;
 }
@@ -212,7 +222,43 @@ int validate_model(const m3_model* m) {
     if (e_ != hipSuccess) return M3_ERR_HIP; \
   } while (0)
 
-int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStream_t s) {
+// Where the frame's steps go: launched one kernel each on a stream, or recorded
+// as the phases of one persistent launch.
+struct FrameSink {
+  virtual hipError_t gemv(const GemvDesc& d) = 0;
+  virtual hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
+                              const Best* last_part, int last_nparts, int32_t vocab_base,
+                              int n_slice, int code_vocab, int n_cb, int B, int H, uint16_t* x,
+                              int32_t* ring, uint32_t* frame) = 0;
+};
+
+struct LaunchSink final : FrameSink {
+  hipStream_t s;
+  explicit LaunchSink(hipStream_t st) : s(st) {}
+  hipError_t gemv(const GemvDesc& d) override { return launch_gemv(d, s); }
+  hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
+                      const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
+                      int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
+                      uint32_t* frame) override {
+    return launch_feedback(tok, aemb, codes, last_part, last_nparts, vocab_base, n_slice,
+                           code_vocab, n_cb, B, H, x, ring, frame, s);
+  }
+};
+
+struct PlanSink final : FrameSink {
+  PersistPlan* pl;
+  explicit PlanSink(PersistPlan* p) : pl(p) {}
+  hipError_t gemv(const GemvDesc& d) override { return persist_add_gemv(pl, d); }
+  hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
+                      const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
+                      int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
+                      uint32_t* frame) override {
+    return persist_add_feedback(pl, tok, aemb, codes, last_part, last_nparts, vocab_base, n_slice,
+                                code_vocab, n_cb, B, H, x, ring, frame);
+  }
+};
+
+int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink& sink) {
   const m3_config& c = m->cfg;
   const Dims d = dims_of(c);
   const m3_frame_layout L = layout_of(c, B);
@@ -236,7 +282,7 @@ int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStrea
                   const uint16_t* res, int ldr, const SampleEpi* smp = nullptr,
                   const GatherPro* gat = nullptr) {
     GemvDesc g{fmt, w, N, K, xin, ldx, B, gamma, eps, sg, sv, y, ldy, f32, epi, res, ldr, smp, gat};
-    return launch_gemv(g, s);
+    return sink.gemv(g);
   };
   // ---- body ----
   const int group = c.n_heads / c.n_kv_heads;
@@ -291,9 +337,14 @@ int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStrea
                 d.CV, 1, M3_EPI_NONE, nullptr, 0, &dep));
   }
   // ---- last draw, feedback, code ring, frame counter ----
-  M3_TRY(launch_feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, n_blocks(d.CV),
-                         c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame, s));
+  M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, n_blocks(d.CV),
+                       c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame));
   return M3_OK;
+}
+
+int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStream_t s) {
+  LaunchSink sink(s);
+  return build_frame(m, S, B, codes, sink);
 }
 
 struct FrameGraph {
@@ -449,6 +500,8 @@ int m3_frame_state_init(const m3_config* cfg, int B, void* state, const uint16_t
   M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S), 0u, L.total / 4, s));
   M3_TRY(launch_copy_bf16(x0, reinterpret_cast<uint16_t*>(S + L.x), (size_t)B * cfg->hidden, s));
   M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S + L.frame), frame0, 1, s));
+  M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S + L.flags), frame0 * kPhaseStride,
+                         kPersistFlags, s));
   return M3_OK;
 }
 
@@ -512,6 +565,60 @@ int m3_frame_graph_destroy(void* graph) {
   const hipError_t b = hipGraphDestroy(fg->graph);
   delete fg;
   return (a == hipSuccess && b == hipSuccess) ? M3_OK : M3_ERR_HIP;
+}
+
+int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_t* codes,
+                               void* stream, void** handle_out) {
+  if (!model || !state || !codes || !handle_out) return M3_ERR_NULL;
+  int st = validate_config(&model->cfg, B);
+  if (st != M3_OK) return st;
+  st = validate_model(model);
+  if (st != M3_OK) return st;
+  if (!aligned(state, 256) || !aligned(codes, 16)) return M3_ERR_ALIGN;
+  if (frame_phases(model->cfg) > persist_max_phases()) return M3_ERR_SHAPE;
+  // one frame kernel per body format: bf16 or int8-row body and lm_head, int8-g128 depth
+  const m3_config& c = model->cfg;
+  if ((c.fmt_body != M3_BF16 && c.fmt_body != M3_I8ROW) || c.fmt_lm != c.fmt_body ||
+      c.fmt_depth != M3_I8G128)
+    return M3_ERR_FORMAT;
+  uint8_t* S = static_cast<uint8_t*>(state);
+  const m3_frame_layout L = layout_of(model->cfg, B);
+  PersistPlan* pl = persist_plan_new(B);
+  if (!pl) return M3_ERR_HIP;
+  PlanSink sink(pl);
+  st = build_frame(model, S, B, codes, sink);
+  // recording makes no HIP call: a failure is a step the frame kernel does not carry
+  if (st == M3_ERR_HIP) st = M3_ERR_SHAPE;
+  if (st == M3_OK && persist_plan_size(pl) != frame_phases(model->cfg)) st = M3_ERR_SHAPE;
+  PersistLaunch* PL = st == M3_OK ? persist_launch_new() : nullptr;
+  if (st == M3_OK && PL) {
+    const hipError_t e = persist_upload(pl, S + L.phases, reinterpret_cast<uint32_t*>(S + L.flags),
+                                        reinterpret_cast<uint32_t*>(S + L.err),
+                                        reinterpret_cast<const uint32_t*>(S + L.frame),
+                                        static_cast<hipStream_t>(stream), PL);
+    if (e != hipSuccess) st = M3_ERR_HIP;
+  } else if (st == M3_OK) {
+    st = M3_ERR_HIP;
+  }
+  persist_plan_free(pl);
+  if (st != M3_OK) {
+    if (PL) persist_launch_free(PL);
+    return st;
+  }
+  *handle_out = PL;
+  return M3_OK;
+}
+
+int m3_frame_persistent_launch(void* handle, void* stream) {
+  if (!handle) return M3_ERR_NULL;
+  return hip_status(persist_launch(*static_cast<PersistLaunch*>(handle),
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int m3_frame_persistent_destroy(void* handle) {
+  if (!handle) return M3_ERR_NULL;
+  persist_launch_free(static_cast<PersistLaunch*>(handle));
+  return M3_OK;
 }
 
 }  // extern "C"

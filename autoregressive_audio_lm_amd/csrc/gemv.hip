@@ -1,655 +1,9 @@
-// gemv.hip -- RMSNorm-fused skinny GEMV/GEMM over packed bf16 / int8-row /
-// int8-group-128 weights for gfx950 (MI355X).
-//
-// What is computed (TensorFold PR #987, precision list and "What it adds";
-// DiffSynth-Studio MiniMax-Music3 model overview):
-//   a = x                              (no norm)
-//   a[b,k] = bf16(x[b,k] * r_b * g[k]) r_b = (mean_k x^2 + eps)^-1/2, fp32
-//   y[b,n] = epi( sum_k W[n,k] a[b,k] ) with fp32 accumulation.
-//
-// Design (MI355X-first):
-//  * The weights are the only large stream (the decode is bandwidth bound:
-//    diffusers issue #14486 item 4 counts ~23 GB of weight reads per frame).
-//    They are packed in 1 KB tiles (16 rows x 64 B) so that one 16-byte load
-//    per lane of a wave64 fetches a whole tile contiguously.  Every weight
-//    byte is read exactly once per call.
-//  * A workgroup of 8 waves owns a block of 16 output rows; wave w owns a
-//    fixed slice of K (a function of K only).  The reduction order of every
-//    output therefore depends only on K -- never on N, B, the grid or where a
-//    slice of rows starts -- so a sliced lm_head reproduces the full one bit
-//    for bit, and row b never depends on the other rows.
-//  * The activation block (after the fused RMSNorm) is staged once per
-//    workgroup in LDS (row stride padded by 16 B against bank conflicts) and
-//    re-used for every tile; workgroups loop over row blocks when there are
-//    more blocks than resident workgroups.
-//  * Few rows (B < 8): VALU path, v_dot2_f32_bf16 on bf16 pairs; lane l holds
-//    row l%16 and one 16-byte K-chunk of each tile, partial sums meet with two
-//    cross-lane exchanges.  B >= 8: the product is a real dense contraction
-//    and goes to v_mfma_f32_16x16x32_bf16 (A = 16 activation rows, B = the
-//    weight tile, exactly the packed lane layout).
-//  * int8 is dequantised to bf16 exactly (|q| <= 127 has 7 significant bits)
-//    with one SDWA sign-extending convert per byte; scales are applied per row
-//    (i8row) or per group of 128 along K (i8g128).
-#include "m3_internal.h"
+// gemv.hip -- one RMSNorm-fused GEMV per launch (the C-ABI GEMV entry points
+// and the graph-replayed frame).  The device code lives in gemv_impl.h.
+#include "gemv_impl.h"
 
 namespace m3 {
 namespace {
-
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-struct Params {
-  const uint8_t* w;
-  int N, K, Kp, T, nblocks;
-  size_t bbytes;
-  const uint16_t* x;
-  int ldx, B;
-  const float* gamma;
-  float eps;
-  int stub_group, stub_voff;
-  void* y;
-  int ldy, out_f32, epi;
-  const uint16_t* res;
-  int ldr;
-  int lds_rows;        // activation rows staged in LDS (0: direct global reads)
-  int lds_stride;      // LDS row stride in elements: Kp + one zero tile + 8 (bank skew)
-  int has_sample, has_gather;
-  SampleEpi smp;       // sampling epilogue (logits GEMVs)
-  GatherPro gat;       // gather prologue (first GEMV of a depth step)
-};
-
-__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
-
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                         __builtin_bit_cast(bf16x2_t, a), acc, false);
-}
-
-// four int8 (one dword) -> two dwords of bf16 pairs (exact)
-__device__ __forceinline__ void i8x4_to_bf16x4(uint32_t v, uint32_t& lo, uint32_t& hi) {
-  float f0 = (float)(int8_t)(v & 0xffu);
-  float f1 = (float)(int8_t)((v >> 8) & 0xffu);
-  float f2 = (float)(int8_t)((v >> 16) & 0xffu);
-  float f3 = (float)((int32_t)v >> 24);
-  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
-}
-
-__device__ __forceinline__ void i8x16_to_bf16(const uint4& q, uint32_t* o) {
-  i8x4_to_bf16x4(q.x, o[0], o[1]);
-  i8x4_to_bf16x4(q.y, o[2], o[3]);
-  i8x4_to_bf16x4(q.z, o[4], o[5]);
-  i8x4_to_bf16x4(q.w, o[6], o[7]);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// source column of operand element k (8-aligned chunk) in x
-__device__ __forceinline__ int src_col(const Params& p, int k) {
-  if (p.stub_group <= 0) return k;
-  return p.stub_voff + (k / (128 * p.stub_group)) * 128 + (k & 127);
-}
-
-__device__ __forceinline__ uint4 load_x8(const Params& p, int b, int k) {
-  return *reinterpret_cast<const uint4*>(p.x + (size_t)b * p.ldx + src_col(p, k));
-}
-
-// Gather prologue: the previous draw of every batch row, from the per-block
-// winners the head GEMV wrote (rows b = wave, wave + 8, ... per wave).
-__device__ void gather_codes(const Params& p, int* code_lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const GatherPro& g = p.gat;
-  for (int b = wave; b < p.lds_rows; b += kWaves) {
-    float bz = -INFINITY;
-    int bj = 0x7fffffff;
-    for (int c = lane; c < g.nparts; c += 64) {
-      const Best r = g.part[(size_t)b * g.nparts + c];
-      if (above(r.z, r.j, bz, bj)) {
-        bz = r.z;
-        bj = r.j;
-      }
-    }
-    best_reduce(bz, bj, 64);
-    if (lane == 0) {
-      const int32_t id = g.index_base + bj;
-      code_lds[b] = id;
-      if (blockIdx.x == 0) g.codes[b * 8 + g.code_col] = id;
-    }
-  }
-  __syncthreads();
-}
-
-// Stage the operand rows in LDS (bf16, row stride lds_stride), fusing the
-// norm.  Row b's source is x (with the attention-stub remap) or, in gather
-// mode, bf16(u[b] + emb[code_b]).  Three flat passes over all rows so the
-// global loads of every row are in flight together: copy (8 chunks of 8
-// values per thread per step), per-row sum of squares (one wave per row, a
-// fixed order), normalise.
-constexpr int kStageUnroll = 8;
-
-__device__ __forceinline__ uint4 bf16x8_add(const uint4& a, const uint4& b) {
-  const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = f2bf(bf2f(ua[j] & 0xffffu) + bf2f(ub[j] & 0xffffu)) |
-           (f2bf(bf2f(ua[j] >> 16) + bf2f(ub[j] >> 16)) << 16);
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-// One or two rows: the copy also accumulates the sum of squares, spread over
-// all threads (row by row; a row's loads are all in flight together).
-__device__ void stage_rows_few(const Params& p, uint16_t* act, float* ss_buf, const int* code_lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int stride = p.lds_stride;
-  const int nchunk = (stride - 8) >> 3;
-  for (int b = 0; b < p.lds_rows; ++b) {
-    const uint16_t* erow = nullptr;
-    if (p.has_gather) {
-      int c = code_lds[b] - p.gat.code_base;
-      if (c < 0 || c >= p.gat.n_codes) c = 0;
-      erow = p.gat.emb + (size_t)c * p.K;
-    }
-    float ss = 0.f;
-    for (int i = tid; i < nchunk; i += kThreads) {
-      const int k = i << 3;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k < p.K) {
-        if (p.has_gather) {
-          v = bf16x8_add(*reinterpret_cast<const uint4*>(p.gat.u + (size_t)b * p.K + k),
-                         *reinterpret_cast<const uint4*>(erow + k));
-          if (blockIdx.x == 0) *reinterpret_cast<uint4*>(p.gat.out + (size_t)b * p.K + k) = v;
-        } else {
-          v = load_x8(p, b, k);
-        }
-      }
-      *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v;
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = bf2f(wv[j] & 0xffffu), a1 = bf2f(wv[j] >> 16);
-        ss = fmaf(a0, a0, ss);
-        ss = fmaf(a1, a1, ss);
-      }
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) ss_buf[M3_MAX_B + b * kWaves + wave] = ss;
-  }
-  __syncthreads();
-  if (p.gamma && tid < p.lds_rows) {
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += ss_buf[M3_MAX_B + tid * kWaves + w];
-    ss_buf[tid] = 1.0f / sqrtf(tot / (float)p.K + p.eps);
-  }
-}
-
-__device__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf, int* code_lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int stride = p.lds_stride;
-  const int cpr = (stride - 8) >> 3;            // chunks per row: K, padding, zero tile
-  const int total = p.lds_rows * cpr;
-  if (p.has_gather) gather_codes(p, code_lds);
-  if (p.lds_rows <= 2) {
-    stage_rows_few(p, act, ss_buf, code_lds);
-    if (!p.gamma) return;
-  } else {
-  // pass 1: copy
-  for (int base = tid; base < total; base += kThreads * kStageUnroll) {
-    uint4 v[kStageUnroll];
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int it = base + u * kThreads;
-      const int b = it / cpr, k = (it - b * cpr) * 8;
-      const bool in = it < total && k < p.K;
-      const int bs = in ? b : 0, ks = in ? k : 0;
-      uint4 x;
-      if (p.has_gather) {
-        int c = code_lds[bs] - p.gat.code_base;
-        c = (c < 0 || c >= p.gat.n_codes) ? 0 : c;
-        const uint4 uv = *reinterpret_cast<const uint4*>(p.gat.u + (size_t)bs * p.K + ks);
-        const uint4 ev = *reinterpret_cast<const uint4*>(p.gat.emb + (size_t)c * p.K + ks);
-        x = bf16x8_add(uv, ev);
-      } else {
-        x = load_x8(p, bs, ks);
-      }
-      v[u] = in ? x : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int it = base + u * kThreads;
-      if (it < total) {
-        const int b = it / cpr, k = (it - b * cpr) * 8;
-        *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v[u];
-        if (p.has_gather && blockIdx.x == 0 && k < p.K)
-          *reinterpret_cast<uint4*>(p.gat.out + (size_t)b * p.K + k) = v[u];
-      }
-    }
-  }
-  __syncthreads();
-  if (!p.gamma) return;
-  // pass 2: r_b from the sum of squares of row b
-  for (int b = wave; b < p.lds_rows; b += kWaves) {
-    const int kc = p.K >> 3;
-    float ss = 0.f;
-    for (int c = lane; c < kc; c += 64) {
-      const uint4 v = *reinterpret_cast<const uint4*>(act + (size_t)b * stride + c * 8);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = bf2f(wv[j] & 0xffffu), a1 = bf2f(wv[j] >> 16);
-        ss = fmaf(a0, a0, ss);
-        ss = fmaf(a1, a1, ss);
-      }
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) ss_buf[b] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
-  }
-  }
-  __syncthreads();
-  // pass 3: a = bf16(x * r_b * gamma); gamma is loaded once per chunk
-  const int kc = p.K >> 3;
-  for (int i = tid; i < kc; i += kThreads) {
-    const int k = i * 8;
-    const float4 g0 = *reinterpret_cast<const float4*>(p.gamma + k);
-    const float4 g1 = *reinterpret_cast<const float4*>(p.gamma + k + 4);
-    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    for (int b = 0; b < p.lds_rows; ++b) {
-      const float r = ss_buf[b];
-      uint4* ptr = reinterpret_cast<uint4*>(act + (size_t)b * stride + k);
-      const uint4 v = *ptr;
-      uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = (bf2f(wv[j] & 0xffffu) * r) * g[2 * j];
-        const float a1 = (bf2f(wv[j] >> 16) * r) * g[2 * j + 1];
-        wv[j] = f2bf(a0) | (f2bf(a1) << 16);
-      }
-      *ptr = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    }
-  }
-  __syncthreads();
-}
-
-// 8 operand values of row b from k; k >= K reads zeros.  Branch-free, so the
-// waits for the weight stream are not made conservative by control flow.
-template <bool LDS>
-__device__ __forceinline__ uint4 act8(const Params& p, const uint16_t* act, int b, int k) {
-  if constexpr (LDS) {
-    return *reinterpret_cast<const uint4*>(act + (size_t)b * p.lds_stride + k);
-  } else {
-    const bool in = k < p.K;
-    const uint4 v = load_x8(p, b, in ? k : 0);
-    return in ? v : make_uint4(0, 0, 0, 0);
-  }
-}
-
-// Epilogue for one output element (or a gate/up pair) after the cross-wave sum.
-__device__ __forceinline__ void store_out(const Params& p, int b, int n, float v) {
-  if (p.out_f32) {
-    reinterpret_cast<float*>(p.y)[(size_t)b * p.ldy + n] = v;
-    return;
-  }
-  uint32_t o = f2bf(v);
-  if (p.epi == M3_EPI_RESIDUAL) o = f2bf(bf2f(p.res[(size_t)b * p.ldr + n]) + bf2f(o));
-  reinterpret_cast<uint16_t*>(p.y)[(size_t)b * p.ldy + n] = (uint16_t)o;
-}
-
-template <int FMT>
-__device__ __forceinline__ float row_scale(const uint8_t* blk, const Params& p, int r) {
-  if constexpr (FMT == M3_I8ROW)
-    return reinterpret_cast<const float*>(blk + (size_t)p.T * kTileBytes)[r];
-  return 1.0f;
-}
-
-// Cross-wave reduction in fixed wave order, scale, epilogue, store.
-template <int FMT, int NB, bool GLU>
-__device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const float* red) {
-  const int tid = threadIdx.x;
-  if constexpr (GLU) {
-    for (int t = tid; t < p.B * 8; t += kThreads) {
-      const int b = t >> 3, pr = t & 7;
-      const int n = rb * 16 + 2 * pr;
-      if (n + 1 >= p.N) continue;
-      float vg = 0.f, vu = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        vg += red[(w * NB + b) * 16 + 2 * pr];
-        vu += red[(w * NB + b) * 16 + 2 * pr + 1];
-      }
-      vg *= row_scale<FMT>(blk, p, 2 * pr);
-      vu *= row_scale<FMT>(blk, p, 2 * pr + 1);
-      const float g = bf2f(f2bf(vg)), u = bf2f(f2bf(vu));
-      const float s = g / (1.0f + expf(-g));
-      reinterpret_cast<uint16_t*>(p.y)[(size_t)b * p.ldy + (n >> 1)] = (uint16_t)f2bf(s * u);
-    }
-    return;
-  }
-  if (p.has_sample) {
-    // logits, then each batch row's best (z, column) over this block's rows;
-    // the 16 rows of a batch row are 16 consecutive lanes of one wave
-    const SampleEpi& sm = p.smp;
-    const uint32_t frame = *sm.frame;
-    const float inv_t = inv_temperature(sm.temperature);
-    for (int t0 = 0; t0 < p.B * 16; t0 += kThreads) {
-      const int t = t0 + tid;
-      const int b = t >> 4, r = t & 15;
-      const int n = rb * 16 + r;
-      float z = -INFINITY;
-      int j = 0x7fffffff;
-      if (t < p.B * 16 && n < p.N) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += red[(w * NB + b) * 16 + r];
-        v *= row_scale<FMT>(blk, p, r);
-        reinterpret_cast<float*>(p.y)[(size_t)b * p.ldy + n] = v;
-        const int32_t id = sm.index_base + n;
-        j = n;
-        if (sm.valid_lo < sm.valid_hi && (id < sm.valid_lo || id >= sm.valid_hi))
-          z = -INFINITY;
-        else
-          z = gumbel_z(v, inv_t, gumbel_noise(sm.seed, (uint32_t)b, frame, sm.draw, (uint32_t)id));
-      }
-      best_reduce(z, j, 16);
-      if (t < p.B * 16 && r == 0) sm.part[(size_t)b * p.nblocks + rb] = Best{z, j};
-    }
-    return;
-  }
-  for (int t = tid; t < p.B * 16; t += kThreads) {
-    const int b = t >> 4, r = t & 15;
-    const int n = rb * 16 + r;
-    if (n >= p.N) continue;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[(w * NB + b) * 16 + r];
-    v *= row_scale<FMT>(blk, p, r);
-    store_out(p, b, n, v);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Weight stream.  Tiles are read with non-temporal 16-byte loads: each weight
-// byte is used once per call, so it should not displace the activations and
-// partial sums from the caches.
-// ---------------------------------------------------------------------------
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer resource over the whole packed matrix (< 2 GiB).  A raw buffer load
-// whose VGPR offset is past num_records returns zeros without touching memory;
-// adding kOob to a lane's offset turns a load into such a no-op.
-constexpr uint32_t kOob = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// 16 bytes, non-temporal (each weight byte is used once per call); the
-// uniform part of the address goes in the scalar offset.
-__device__ __forceinline__ uint4 ldw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-// Tiles per batch (KU) is a kernel parameter: 8 for long K slices, 4 where a
-// wave's K slice is short (fewer padding tiles).  A wave keeps two batches in
-// flight.
-
-// ---------------------------------------------------------------------------
-// VALU accumulators: NB activation rows (B <= NB); lane = (row l%16, K-chunk
-// l/16); partial sums of the 4 lanes of a row meet with two exchanges.
-// ---------------------------------------------------------------------------
-template <int FMT, int NB, bool MFMA>
-struct Accum {
-  float acc[NB], gacc[NB];
-
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = gacc[b] = 0.f;
-  }
-
-  template <bool LDS>
-  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0) {
-    float* dst = FMT == M3_I8G128 ? gacc : acc;
-    const int c = (threadIdx.x & 63) >> 4;
-    if constexpr (FMT == M3_BF16) {
-      const int kk = k0 + c * 8;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        // rows past B repeat row B-1 (valid memory); their sums are never stored
-        const uint4 av = act8<LDS>(p, act, min(b, p.B - 1), kk);
-        float a = dst[b];
-        a = dot2(wv.x, av.x, a);
-        a = dot2(wv.y, av.y, a);
-        a = dot2(wv.z, av.z, a);
-        a = dot2(wv.w, av.w, a);
-        dst[b] = a;
-      }
-    } else {
-      const int kk = k0 + c * 16;
-      uint32_t wb[8];
-      i8x16_to_bf16(wv, wb);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int bb = min(b, p.B - 1);
-        const uint4 a0 = act8<LDS>(p, act, bb, kk);
-        const uint4 a1 = act8<LDS>(p, act, bb, kk + 8);
-        float a = dst[b];
-        a = dot2(wb[0], a0.x, a);
-        a = dot2(wb[1], a0.y, a);
-        a = dot2(wb[2], a0.z, a);
-        a = dot2(wb[3], a0.w, a);
-        a = dot2(wb[4], a1.x, a);
-        a = dot2(wb[5], a1.y, a);
-        a = dot2(wb[6], a1.z, a);
-        a = dot2(wb[7], a1.w, a);
-        dst[b] = a;
-      }
-    }
-  }
-
-  // end of a group of 128 (i8g128): scale the group's partial sums
-  __device__ __forceinline__ void group_end(float s) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      acc[b] = fmaf(s, gacc[b], acc[b]);
-      gacc[b] = 0.f;
-    }
-  }
-
-  __device__ __forceinline__ void to_red(float* red, int wave) const {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float v = acc[b];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (lane < 16) red[(wave * NB + b) * 16 + lane] = v;
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// MFMA accumulators: NB/16 tiles of 16 activation rows.  D[i][j] += sum_k
-// A[i][k] B[k][j] with A = activations (row i = lane%16 of a tile), B = the
-// weight tile (column j = weight row lane%16); lane l supplies k = 8*(l/16)
-// .. +7 of each operand and receives D[4*(l/16) + q][l%16], q = 0..3.
-// ---------------------------------------------------------------------------
-template <int FMT, int NB>
-struct Accum<FMT, NB, true> {
-  static constexpr int NT = NB / 16;
-  f32x4_t acc[NT], gacc[NT];
-
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) acc[bt] = gacc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  template <bool LDS>
-  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0) {
-    f32x4_t* dst = FMT == M3_I8G128 ? gacc : acc;
-    const int lane = threadIdx.x & 63, c = lane >> 4, i = lane & 15;
-    if constexpr (FMT == M3_BF16) {
-      const int kk = k0 + c * 8;
-      const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wv);
-#pragma unroll
-      for (int bt = 0; bt < NT; ++bt) {
-        const int b = min(bt * 16 + i, p.B - 1);
-        const uint4 av = act8<LDS>(p, act, b, kk);
-        dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), bw,
-                                                          dst[bt], 0, 0, 0);
-      }
-    } else {
-      const int kk = k0 + c * 16;
-      uint32_t wb[8];
-      i8x16_to_bf16(wv, wb);
-      const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, make_uint4(wb[0], wb[1], wb[2], wb[3]));
-      const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, make_uint4(wb[4], wb[5], wb[6], wb[7]));
-#pragma unroll
-      for (int bt = 0; bt < NT; ++bt) {
-        const int b = min(bt * 16 + i, p.B - 1);
-        const uint4 a0 = act8<LDS>(p, act, b, kk);
-        const uint4 a1 = act8<LDS>(p, act, b, kk + 8);
-        dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), blo,
-                                                          dst[bt], 0, 0, 0);
-        dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), bhi,
-                                                          dst[bt], 0, 0, 0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void group_end(float s) {
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[bt][q] = fmaf(s, gacc[bt][q], acc[bt][q]);
-      gacc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-
-  __device__ __forceinline__ void to_red(float* red, int wave) const {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int bt = 0; bt < NT; ++bt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        red[(wave * NB + bt * 16 + 4 * (lane >> 4) + q) * 16 + (lane & 15)] = acc[bt][q];
-  }
-};
-
-// Every wave walks the same flat sequence of items (row block, batch of kU
-// tiles of its K-slice); item j+1's tiles are requested before item j is
-// computed, so two batches stay in flight across row-block boundaries and the
-// first batch is in flight while the activations are being staged.
-// GLU selects the SwiGLU epilogue at compile time (its own kernel symbol, so
-// the gate/up GEMVs can be told apart in a profile).
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
-  constexpr int kU = KU;
-  static_assert(kU % 2 == 0 && kU <= 16, "batches hold whole i8g128 groups");
-  extern __shared__ __align__(16) uint8_t smem[];
-  float* red = reinterpret_cast<float*>(smem);                       // [kWaves][NB][16]
-  float* ss_buf = red + kWaves * NB * 16;                            // [lds_rows][kWaves]
-  int* code_lds = reinterpret_cast<int*>(ss_buf + M3_MAX_B * kWaves);  // [M3_MAX_B]
-  uint16_t* act = reinterpret_cast<uint16_t*>(code_lds + M3_MAX_B);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int TPU = FMT == M3_I8G128 ? 2 : 1;    // tiles per unit of the K split
-  constexpr int TK = FMT == M3_BF16 ? 32 : 64;     // K elements per tile
-  const int units = p.T / TPU;
-  const int t_lo = (units * wave / kWaves) * TPU;
-  const int ntw = (units * (wave + 1) / kWaves) * TPU - t_lo;       // tiles of this wave
-  const int nbat = ((units + kWaves - 1) / kWaves * TPU + kU - 1) / kU;   // same for all waves
-  const int my_blocks = (p.nblocks - blockIdx.x + gridDim.x - 1) / gridDim.x;
-  const int nitems = my_blocks * nbat;
-
-  // Every wave walks nbat * kU tiles per row block.  Tiles past the end of its
-  // K-slice, and the prefetch past the last item, are out-of-range buffer
-  // loads (zeros, no memory traffic); their operand is the zero tile, so they
-  // add exactly nothing.  The loop has no data-dependent branches, so the
-  // compiler's waits let both batches stay in flight.
-  const __amdgpu_buffer_rsrc_t wr = weight_rsrc(p.w, (uint32_t)((size_t)p.nblocks * p.bbytes));
-  const uint32_t vlane = (uint32_t)lane * 16u, vlane_oob = vlane + kOob;
-  const int G = p.K / 128;                 // groups per row (i8g128)
-  auto load = [&](uint4* dst, float* sc, int j) {
-    const bool live = j < nitems;
-    const int rb = blockIdx.x + (j / nbat) * gridDim.x, bi = j % nbat;
-    const uint32_t base = (uint32_t)((size_t)rb * p.bbytes) + (uint32_t)t_lo * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int tt = bi * kU + i;
-      const bool real = live && tt < ntw;
-      dst[i] = ldw(wr, real ? vlane : vlane_oob, real ? base + (uint32_t)tt * kTileBytes : 0u);
-    }
-    if constexpr (FMT == M3_I8G128) {
-      // scales of this batch's kU/2 groups for row lane%16 ([row][group]
-      // layout); one dword each so a group past the slice reads a zero
-      const uint32_t g0 = (uint32_t)(t_lo + bi * kU) >> 1;
-      const uint32_t sbase = (uint32_t)((size_t)rb * p.bbytes) + (uint32_t)p.T * kTileBytes + g0 * 4u;
-      const uint32_t vrow = (uint32_t)(lane & 15) * (uint32_t)G * 4u;
-#pragma unroll
-      for (int q = 0; q < kU / 2; ++q) {
-        const bool real = live && bi * kU + 2 * q < ntw;
-        sc[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            wr, real ? vrow : vrow + kOob, real ? sbase + 4u * q : 0u, 0));
-      }
-    }
-  };
-
-  Accum<FMT, NB, MFMA> A;
-  A.reset();
-  auto compute = [&](const uint4* src, const float* scv, int j) {
-    const int rb = blockIdx.x + (j / nbat) * gridDim.x, bi = j % nbat;
-#pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int tt = bi * kU + i;
-      const bool real = tt < ntw;
-      A.template tile<LDS>(p, act, src[i], real ? (t_lo + tt) * TK : p.Kp);
-      if (FMT == M3_I8G128 && (i & 1)) {
-        // groups are tile pairs (t_lo and kU are even): scale the finished group
-        A.group_end(real ? scv[i >> 1] : 0.f);
-      }
-    }
-    if (bi == nbat - 1) {          // row block complete: cross-wave sum and epilogue
-      A.to_red(red, wave);
-      __syncthreads();
-      finish_block<FMT, NB, GLU>(p, p.w + (size_t)rb * p.bbytes, rb, red);
-      __syncthreads();
-      A.reset();
-    }
-  };
-
-  uint4 bufA[kU], bufB[kU];
-  float scA[kU / 2], scB[kU / 2];
-  load(bufA, scA, 0);
-  if (LDS) stage_activations(p, act, ss_buf, code_lds);
-  // the scheduling barriers keep each batch's loads ahead of the previous
-  // batch's arithmetic (the scheduler would otherwise sink them into it)
-  for (int j = 0; j < nitems; j += 2) {
-    load(bufB, scB, j + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(bufA, scA, j);
-    if (j + 1 >= nitems) break;
-    load(bufA, scA, j + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(bufB, scB, j + 1);
-  }
-}
 
 template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
 hipError_t configure_one() {
@@ -668,23 +22,15 @@ hipError_t launch_ku(const Params& p, int grid, size_t smem, hipStream_t s) {
   return hipGetLastError();
 }
 
-// short K slices take batches of 4 (only with staged activations)
 template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
-hipError_t launch_epi(const Params& p, int grid, size_t smem, hipStream_t s, bool ku4) {
-  if constexpr (LDS) {
-    if (ku4) return launch_ku<FMT, NB, MFMA, LDS, GLU, 4>(p, grid, smem, s);
-  }
-  return launch_ku<FMT, NB, MFMA, LDS, GLU, 8>(p, grid, smem, s);
+hipError_t launch_epi(const Params& p, int grid, size_t smem, hipStream_t s) {
+  return launch_ku<FMT, NB, MFMA, LDS, GLU, (LDS && FMT == M3_I8G128) ? 4 : 8>(p, grid, smem, s);
 }
 
 template <int FMT, int NB, bool MFMA, bool LDS>
 hipError_t launch_one(const Params& p, int grid, size_t smem, hipStream_t s) {
-  // padding tiles per wave with batches of 4 vs 8: prefer 4 when it pads less
-  const int tpu = FMT == M3_I8G128 ? 2 : 1;
-  const int tpw = (p.T / tpu + kWaves - 1) / kWaves * tpu;
-  const bool ku4 = (tpw + 3) / 4 * 4 < (tpw + 7) / 8 * 8;
-  if (p.epi == M3_EPI_SWIGLU) return launch_epi<FMT, NB, MFMA, LDS, true>(p, grid, smem, s, ku4);
-  return launch_epi<FMT, NB, MFMA, LDS, false>(p, grid, smem, s, ku4);
+  if (p.epi == M3_EPI_SWIGLU) return launch_epi<FMT, NB, MFMA, LDS, true>(p, grid, smem, s);
+  return launch_epi<FMT, NB, MFMA, LDS, false>(p, grid, smem, s);
 }
 
 template <int FMT, bool LDS>
@@ -693,7 +39,6 @@ hipError_t dispatch_b(const Params& p, int grid, size_t smem, hipStream_t s) {
   if (B <= 1) return launch_one<FMT, 1, false, LDS>(p, grid, smem, s);
   if (B <= 2) return launch_one<FMT, 2, false, LDS>(p, grid, smem, s);
   if (B <= 4) return launch_one<FMT, 4, false, LDS>(p, grid, smem, s);
-  if (B < 8) return launch_one<FMT, 8, false, LDS>(p, grid, smem, s);
   if (B <= 16) return launch_one<FMT, 16, true, LDS>(p, grid, smem, s);
   if (B <= 32) return launch_one<FMT, 32, true, LDS>(p, grid, smem, s);
   if (B <= 48) return launch_one<FMT, 48, true, LDS>(p, grid, smem, s);
@@ -704,7 +49,7 @@ template <int FMT, bool LDS, bool GLU, int KU>
 hipError_t configure_ku() {
   const hipError_t es[] = {
       configure_one<FMT, 1, false, LDS, GLU, KU>(),  configure_one<FMT, 2, false, LDS, GLU, KU>(),
-      configure_one<FMT, 4, false, LDS, GLU, KU>(),  configure_one<FMT, 8, false, LDS, GLU, KU>(),
+      configure_one<FMT, 4, false, LDS, GLU, KU>(),
       configure_one<FMT, 16, true, LDS, GLU, KU>(),  configure_one<FMT, 32, true, LDS, GLU, KU>(),
       configure_one<FMT, 48, true, LDS, GLU, KU>(),  configure_one<FMT, 64, true, LDS, GLU, KU>()};
   for (hipError_t e : es)
@@ -714,11 +59,7 @@ hipError_t configure_ku() {
 
 template <int FMT, bool LDS, bool GLU>
 hipError_t configure_epi() {
-  hipError_t e = configure_ku<FMT, LDS, GLU, 8>();
-  if constexpr (LDS) {
-    if (e == hipSuccess) e = configure_ku<FMT, LDS, GLU, 4>();
-  }
-  return e;
+  return configure_ku<FMT, LDS, GLU, (LDS && FMT == M3_I8G128) ? 4 : 8>();
 }
 
 template <int FMT, bool LDS>
@@ -729,25 +70,10 @@ hipError_t configure_fmt() {
   return hipSuccess;
 }
 
-int nb_of(int B) {
-  if (B <= 1) return 1;
-  if (B <= 2) return 2;
-  if (B <= 4) return 4;
-  if (B < 8) return 8;
-  return (B + 15) / 16 * 16;
-}
-
-size_t fixed_smem(int NB) {
-  return (size_t)kWaves * NB * 16 * 4 + (size_t)M3_MAX_B * kWaves * 4 + (size_t)M3_MAX_B * 4;
-}
-
 }  // namespace
 
 size_t gemv_smem_bytes(int fmt, int K, int B, bool has_gamma) {
-  const size_t fixed = fixed_smem(nb_of(B));
-  const size_t act = (size_t)B * (k_pad(fmt, K) + tile_k(fmt) + 8) * 2;
-  if (has_gamma || fixed + act <= 160 * 1024) return fixed + act;
-  return fixed;
+  return smem_bytes_of(fmt, K, B, has_gamma);
 }
 
 hipError_t gemv_prepare() {
@@ -760,37 +86,11 @@ hipError_t gemv_prepare() {
 }
 
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t s) {
-  Params p;
-  p.w = static_cast<const uint8_t*>(d.w);
-  p.N = d.N;
-  p.K = d.K;
-  p.Kp = k_pad(d.fmt, d.K);
-  p.T = n_tiles(d.fmt, d.K);
-  p.nblocks = n_blocks(d.N);
-  p.bbytes = block_bytes(d.fmt, d.K);
-  p.x = d.x;
-  p.ldx = d.ldx;
-  p.B = d.B;
-  p.gamma = d.gamma;
-  p.eps = d.eps;
-  p.stub_group = d.stub_group;
-  p.stub_voff = d.stub_voff;
-  p.y = d.y;
-  p.ldy = d.ldy;
-  p.out_f32 = d.out_f32;
-  p.epi = d.epi;
-  p.res = d.res;
-  p.ldr = d.ldr;
-  const size_t fixed = fixed_smem(nb_of(d.B));
-  const size_t smem = gemv_smem_bytes(d.fmt, d.K, d.B, d.gamma != nullptr);
-  const bool lds = smem > fixed;
-  p.lds_rows = lds ? d.B : 0;
-  p.lds_stride = p.Kp + tile_k(d.fmt) + 8;
-  p.has_sample = d.sample != nullptr;
-  p.has_gather = d.gather != nullptr;
-  if (d.sample) p.smp = *d.sample;
-  if (d.gather) p.gat = *d.gather;
+  bool lds;
+  int ku;      // fixed by the format (see ku_of); the instantiation below follows the same rule
+  const Params p = make_params(d, &lds, &ku);
   if (d.gather && !lds) return hipErrorInvalidValue;   // the gather stages through LDS
+  const size_t smem = smem_bytes_of(d.fmt, d.K, d.B, d.gamma != nullptr);
   // resident workgroups per CU from LDS (8 waves each, at most 2 per CU)
   int per_cu = (int)((160 * 1024) / (smem + 1024));
   per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);

@@ -115,6 +115,35 @@ hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const*
                            int32_t vocab_base, int n_slice, int code_vocab, int n_cb, int B,
                            int H, uint16_t* x_out, int32_t* ring, uint32_t* frame, hipStream_t s);
 hipError_t launch_copy_bf16(const uint16_t* src, uint16_t* dst, size_t n, hipStream_t s);
+
+// ---- persistent frame (persist.hip) -------------------------------------------
+// A frame recorded as a table of phases (one GEMV each, then the frame end)
+// and run as one cooperative launch.  Flags of workgroups that finished phase
+// i of frame f hold f * kPhaseStride + i + 1.
+constexpr uint32_t kPhaseStride = 512;
+constexpr int kPersistFlags = 256;       // flag words (one per workgroup, at most 256)
+struct PersistPlan;
+struct PersistLaunch;
+size_t persist_phase_bytes();
+int persist_max_phases();
+PersistPlan* persist_plan_new(int B);
+void persist_plan_free(PersistPlan* pl);
+int persist_plan_size(const PersistPlan* pl);
+hipError_t persist_add_gemv(PersistPlan* pl, const GemvDesc& d);
+hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
+                                const uint16_t* const* audio_emb, int32_t* codes,
+                                const Best* last_part, int last_nparts, int32_t vocab_base,
+                                int n_slice, int code_vocab, int n_cb, int B, int H,
+                                uint16_t* x_out, int32_t* ring, uint32_t* frame);
+PersistLaunch* persist_launch_new();
+void persist_launch_free(PersistLaunch* L);
+// copy the table into device memory, reset flags and the error word (synchronises `s`)
+hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
+                          const uint32_t* frame, hipStream_t s, PersistLaunch* out);
+hipError_t persist_launch(const PersistLaunch& L, hipStream_t s);
+// the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip) by row-count class
+const void* persist_kernel_bf16(int NB);
+const void* persist_kernel_i8row(int NB);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, size_t n, hipStream_t s);
 
 }  // namespace m3

@@ -1,0 +1,185 @@
+// persist.hip -- one whole decode frame as ONE persistent launch.
+//
+// The frame is a chain of ~270 dependent GEMVs (DiffSynth-Studio
+// MiniMax-Music3 stage 2: 36 body layers, the semantic draw, 7 depth-decoder
+// steps); launched one per kernel, each pays a launch gap plus a ramp-up and
+// a tail during which HBM idles.  Here one workgroup per CU walks a table of
+// phases (one GEMV each, then the frame end).  Phase i+1 depends on all of
+// phase i, but its weights do not: every workgroup requests its first two
+// batches of phase i+1 weight tiles, THEN waits until all workgroups have
+// published phase i, so the dependency latency overlaps the weight stream.
+//
+// Publication: a workgroup finishes its phase-i stores (system-coherent, see
+// gemv_impl.h), waits for them to complete, then writes its flag =
+// frame * 512 + i + 1 with a coherent store; a waiter's first wave polls all
+// flags with coherent loads.  Flags only grow within a frame and from frame to
+// frame, and are compared modulo 2^32.  Every wait is bounded: past the spin
+// limit the workgroup raises the error word and leaves, and every other
+// workgroup leaves at its next poll, so the launch always terminates; the
+// host reads the word from the frame state.
+//
+// The launch is cooperative, so all workgroups are resident at once (the
+// waits require it); the launch fails rather than run otherwise.
+#include "persist_kernel.h"
+
+#include <vector>
+
+namespace m3 {
+namespace {
+
+constexpr int kMaxPhases = (int)kPhaseStride - 1;
+
+__global__ void flags_init_kernel(uint32_t* flags, int n, const uint32_t* frame, uint32_t* err) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) flags[i] = *frame * kPhaseStride;
+  if (i == 0) *err = 0u;
+}
+
+}  // namespace
+
+// ---- host side ------------------------------------------------------------------
+struct PersistPlan {
+  std::vector<Phase> phases;
+  FeedbackArgs fb{};
+  size_t smem = 0;
+  int B = 0;
+  int fmt_body = -1;      // the kernel's class-0 format
+};
+
+size_t persist_phase_bytes() { return sizeof(Phase); }
+int persist_max_phases() { return kMaxPhases; }
+
+PersistPlan* persist_plan_new(int B) {
+  PersistPlan* pl = new PersistPlan;
+  pl->B = B;
+  return pl;
+}
+
+void persist_plan_free(PersistPlan* pl) { delete pl; }
+
+int persist_plan_size(const PersistPlan* pl) { return (int)pl->phases.size(); }
+
+hipError_t persist_add_gemv(PersistPlan* pl, const GemvDesc& d) {
+  if ((int)pl->phases.size() >= kMaxPhases || d.B != pl->B) return hipErrorInvalidValue;
+  Phase ph{};
+  bool lds;
+  int ku;
+  ph.p = make_params(d, &lds, &ku);
+  if (d.gather && !lds) return hipErrorInvalidValue;
+  // class 0: the body / lm_head format (bf16 or int8-row, one per frame); class 1: int8-g128
+  int cls;
+  if (d.fmt == M3_I8G128) {
+    cls = 1;
+  } else {
+    if (pl->fmt_body < 0) pl->fmt_body = d.fmt;
+    if (d.fmt != pl->fmt_body) return hipErrorInvalidValue;
+    cls = 0;
+  }
+  const int NB = nb_of(d.B);
+  int arm;
+  if (!lds) {
+    if (d.epi == M3_EPI_SWIGLU || NB < 16) return hipErrorInvalidValue;
+    arm = kArmGlobal;
+  } else {
+    arm = d.epi == M3_EPI_SWIGLU ? kArmGlu : kArmLds;
+  }
+  ph.variant = cls * 4 + arm;
+  const size_t smem = smem_bytes_of(d.fmt, d.K, d.B, d.gamma != nullptr);
+  if (smem > pl->smem) pl->smem = smem;
+  pl->phases.push_back(ph);
+  return hipSuccess;
+}
+
+hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
+                                const uint16_t* const* audio_emb, int32_t* codes,
+                                const Best* last_part, int last_nparts, int32_t vocab_base,
+                                int n_slice, int code_vocab, int n_cb, int B, int H,
+                                uint16_t* x_out, int32_t* ring, uint32_t* frame) {
+  if ((int)pl->phases.size() >= kMaxPhases) return hipErrorInvalidValue;
+  FeedbackArgs& a = pl->fb;
+  a.tok = tok_emb_audio;
+  for (int i = 0; i < 8; ++i) a.aemb[i] = (i < n_cb - 1) ? audio_emb[i] : nullptr;
+  a.codes = codes;
+  a.last_part = last_part;
+  a.last_nparts = last_nparts;
+  a.vocab_base = vocab_base;
+  a.n_slice = n_slice;
+  a.code_vocab = code_vocab;
+  a.n_cb = n_cb;
+  a.B = B;
+  a.H = H;
+  a.x = x_out;
+  a.ring = ring;
+  a.frame = frame;
+  Phase ph{};
+  ph.variant = kFeedbackVariant;
+  pl->phases.push_back(ph);
+  return hipSuccess;
+}
+
+// Persistent launch parameters once the phase table is in device memory.
+struct PersistLaunch {
+  const void* kernel;
+  const Phase* phases;
+  int nph;
+  uint32_t* flags;
+  uint32_t* err;
+  const uint32_t* frame;
+  FeedbackArgs fb;
+  size_t smem;
+  int nwg;
+};
+
+// Copy the table to `table` (device, persist_phase_bytes() * size), set the
+// flags to "phase -1 of the current frame done", clear the error word.
+hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
+                          const uint32_t* frame, hipStream_t s, PersistLaunch* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int ncu = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  int nwg = ncu < kPersistFlags ? ncu : kPersistFlags;
+  nwg &= ~3;
+  if (nwg < 4) return hipErrorInvalidValue;
+  const int NB = nb_of(pl->B);
+  const void* k = pl->fmt_body == M3_I8ROW ? persist_kernel_i8row(NB) : persist_kernel_bf16(NB);
+  e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl->smem);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(table, pl->phases.data(), pl->phases.size() * sizeof(Phase),
+                     hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(flags_init_kernel, dim3(1), dim3(kPersistFlags), 0, s, flags, kPersistFlags,
+                     frame, err);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipStreamSynchronize(s);      // the host table may go away after this
+  if (e != hipSuccess) return e;
+  out->kernel = k;
+  out->phases = static_cast<const Phase*>(table);
+  out->nph = (int)pl->phases.size();
+  out->flags = flags;
+  out->err = err;
+  out->frame = frame;
+  out->fb = pl->fb;
+  out->smem = pl->smem;
+  out->nwg = nwg;
+  return hipSuccess;
+}
+
+hipError_t persist_launch(const PersistLaunch& L, hipStream_t s) {
+  const Phase* ph = L.phases;
+  int nph = L.nph;
+  uint32_t* flags = L.flags;
+  uint32_t* err = L.err;
+  const uint32_t* frame = L.frame;
+  FeedbackArgs fb = L.fb;
+  void* args[] = {&ph, &nph, &flags, &err, &frame, &fb};
+  return hipLaunchCooperativeKernel(L.kernel, dim3(L.nwg), dim3(kThreads), args, (unsigned)L.smem, s);
+}
+
+PersistLaunch* persist_launch_new() { return new PersistLaunch; }
+void persist_launch_free(PersistLaunch* L) { delete L; }
+
+}  // namespace m3

@@ -115,6 +115,7 @@ class FrameState:
         self.state = self.buf[off:off + self.layout.total]
         self.codes = torch.zeros(B, 8, dtype=torch.int32, device=dev)
         self.graph = None
+        self.persistent = None
         check(lib().m3_frame_state_init(ctypes.byref(dm.config), B, ctypes.c_void_p(self.state.data_ptr()),
                                         ctypes.c_void_p(x0.contiguous().data_ptr()), int(frame0),
                                         m3._stream(stream)))
@@ -165,10 +166,30 @@ class FrameState:
     def replay(self, stream) -> None:
         check(lib().m3_frame_graph_launch(self.graph, ctypes.c_void_p(stream.cuda_stream)))
 
+    def persistent_create(self, stream=None) -> None:
+        """Record the frame as the phase table of one persistent launch."""
+        h = ctypes.c_void_p()
+        check(lib().m3_frame_persistent_create(ctypes.byref(self.dm.model),
+                                               ctypes.c_void_p(self.state.data_ptr()), self.B,
+                                               ctypes.c_void_p(self.codes.data_ptr()),
+                                               m3._stream(stream), ctypes.byref(h)))
+        self.persistent = h
+
+    def persistent_launch(self, stream=None) -> None:
+        check(lib().m3_frame_persistent_launch(self.persistent, m3._stream(stream)))
+
+    @property
+    def err(self) -> torch.Tensor:
+        """Nonzero once a persistent frame gave up waiting (its outputs are invalid)."""
+        return self.state[self.layout.err:self.layout.err + 4].view(torch.int32)
+
     def release(self) -> None:
         if self.graph is not None:
             check(lib().m3_frame_graph_destroy(self.graph))
             self.graph = None
+        if getattr(self, "persistent", None) is not None:
+            check(lib().m3_frame_persistent_destroy(self.persistent))
+            self.persistent = None
 
     def __del__(self):
         try:

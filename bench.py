@@ -85,6 +85,34 @@ def time_frames(dm, cfg, B, steps, warmup, stream, seed=0):
     return st, ms, wall
 
 
+def time_frames_persistent(dm, cfg, B, steps, warmup, stream, seed=0):
+    """Frames as one cooperative launch each; HIP events on the launch stream."""
+    import torch
+    from autoregressive_audio_lm_amd import runtime, synth
+    x0 = synth.activations(B, cfg["H"], 1000 + seed, device="cuda")
+    st = runtime.FrameState(dm, B, x0, frame0=0)
+    with torch.cuda.stream(stream):
+        st.persistent_create(stream)
+        for _ in range(warmup):
+            st.persistent_launch(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            st.persistent_launch(stream)
+        e1.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    if int(st.err.item()) != 0:
+        raise RuntimeError("a persistent frame gave up waiting")
+    ms = e0.elapsed_time(e1) / steps
+    return st, ms, wall
+
+
 def time_gate_up(dm, st, stream, reps=3):
     """Average duration of the body's gate/up GEMV (RMSNorm prologue + SwiGLU
     epilogue), the frame's dominant kernel, over every layer's matrix, with

@@ -231,6 +231,9 @@ typedef struct {
   size_t frame;    /* u32  frame counter (advanced on the GPU)                 */
   size_t part_sem; /* per-row-block winners of the semantic draw               */
   size_t part_dep; /* per-row-block winners of the latest depth draw           */
+  size_t flags;    /* u32  [256] per-workgroup progress of the persistent frame */
+  size_t err;      /* u32  nonzero: a persistent frame gave up waiting          */
+  size_t phases;   /* the persistent frame's phase table                       */
   size_t total;
 } m3_frame_layout;
 
@@ -267,6 +270,27 @@ int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* co
                           void* stream, void** graph_out /* host */);
 int m3_frame_graph_launch(void* graph, void* stream);
 int m3_frame_graph_destroy(void* graph);
+
+/* Persistent form of the frame: the same steps, with the same results, run as
+ * ONE cooperative launch per frame.  One workgroup per compute unit walks the
+ * frame's GEMVs in order; each workgroup requests the first weight tiles of
+ * the next GEMV before it waits for the previous GEMV's outputs (published
+ * through per-workgroup flags in the state), so HBM keeps streaming across the
+ * ~270 dependencies of a frame (TensorFold PR #987: one submission per frame;
+ * "MiniMax Music 3, local": the AR stages are bound by memory bandwidth).
+ * create records the frame into the state's phase table (it synchronises
+ * `stream` once); launch enqueues one frame; the handle keeps the model's and
+ * the state's device addresses.  Every wait inside the launch is bounded: if
+ * one gives up (the launch could not make progress), the state's err word
+ * becomes nonzero, the launch ends early and that frame's outputs are invalid.
+ * The frame state must have been initialised with m3_frame_state_init; eager,
+ * graph and persistent frames may be interleaved on one state.  The launch
+ * fails with M3_ERR_HIP if the device cannot hold one workgroup per compute
+ * unit at once. */
+int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_t* codes,
+                               void* stream, void** handle_out /* host */);
+int m3_frame_persistent_launch(void* handle, void* stream);
+int m3_frame_persistent_destroy(void* handle);
 
 #ifdef __cplusplus
 }

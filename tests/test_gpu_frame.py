@@ -145,3 +145,40 @@ def test_frame_repeat_byte_identical(small):
     torch.cuda.synchronize()
     assert torch.equal(a.codes, b.codes)
     assert a.state.cpu().numpy().tobytes() == b.state.cpu().numpy().tobytes()
+
+
+def _same_frame(a, b):
+    assert torch.equal(a.codes, b.codes)
+    for name in ("x", "h", "logits"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    assert torch.equal(a.ring, b.ring)
+    assert int(a.frame.item()) == int(b.frame.item())
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 16])
+def test_persistent_frame_equals_eager(small, B):
+    """One cooperative launch per frame gives the eager frame's bytes (codes,
+    fed-back input, residual stream, logits, ring, counter), also when eager
+    and persistent frames alternate on one state."""
+    cfg, dm, om = small
+    x0 = synth.activations(B, cfg["H"], 300 + B).to(DEV)
+    eager = runtime.FrameState(dm, B, x0, frame0=2)
+    pers = runtime.FrameState(dm, B, x0, frame0=2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        pers.persistent_create(s)
+        for _ in range(3):
+            eager.decode(s)
+            pers.persistent_launch(s)
+            s.synchronize()
+            assert int(pers.err.item()) == 0
+            _same_frame(eager, pers)
+        # alternate paths on the persistent state
+        pers.decode(s)
+        eager.decode(s)
+        pers.persistent_launch(s)
+        eager.decode(s)
+        s.synchronize()
+        assert int(pers.err.item()) == 0
+        _same_frame(eager, pers)
+    pers.release()

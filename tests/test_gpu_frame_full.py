@@ -84,3 +84,33 @@ def test_full_size_frame_within_rounding_envelope(preset, B):
     sure = stable & (tr["zgap"] > ENVELOPE_FACTOR * env_l)
     sure[:, 1:] &= sure[:, :1]           # the depth chain is conditioned on the semantic code
     assert np.all((codes == o_codes)[sure])
+
+
+@pytest.mark.parametrize("preset,B", [("A", 1), ("A", 16), ("B", 6)])
+def test_full_size_persistent_equals_graph(preset, B):
+    """The persistent frame (one cooperative launch) and the graph-replayed
+    frame give identical bytes at the full model size, including the B = 16
+    shapes whose down projection reads its operand from global memory."""
+    cfg = configs.config("frame-full")
+    md = synth.make_model(cfg, **configs.PRESETS[preset], seed=17, device=DEV)
+    dm = runtime.DecodeModel(md, seed=4, free_sources=True)
+    del md
+    torch.cuda.empty_cache()
+    x0 = synth.activations(B, cfg["H"], 900, device=DEV)
+    g = runtime.FrameState(dm, B, x0, frame0=40)
+    p = runtime.FrameState(dm, B, x0, frame0=40)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g.capture(s)
+        p.persistent_create(s)
+        for _ in range(2):
+            g.replay(s)
+            p.persistent_launch(s)
+            s.synchronize()
+            assert int(p.err.item()) == 0
+            assert torch.equal(g.codes, p.codes)
+            for name in ("x", "h", "logits"):
+                assert torch.equal(getattr(g, name), getattr(p, name)), name
+            assert torch.equal(g.ring, p.ring)
+    g.release()
+    p.release()
