@@ -63,7 +63,8 @@ class Model(ctypes.Structure):
 class FrameLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("x", "h", "qkv", "mlp", "logits", "u", "hd", "dqkv",
                                                "dmlp", "dlogits", "ring", "frame", "part_sem", "part_dep",
-                                               "flags", "err", "phases", "total")]
+                                               "flags", "err", "seq", "phases", "th", "tqkv", "tmlp", "tu",
+                                               "thd", "tdqkv", "tdmlp", "total")]
 
 
 _lib = None

@@ -191,7 +191,15 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.part_dep = take((size_t)B * n_blocks(d.CV) * sizeof(Best));
   L.flags = take((size_t)kPersistFlags * 4);
   L.err = take(4);
+  L.seq = take(4);
   L.phases = take((size_t)frame_phases(c) * persist_phase_bytes());
+  L.th = take((size_t)B * d.H * 4);
+  L.tqkv = take((size_t)B * d.nqkv * 4);
+  L.tmlp = take((size_t)B * d.F * 4);
+  L.tu = take((size_t)B * d.D * 4);
+  L.thd = take((size_t)B * d.D * 4);
+  L.tdqkv = take((size_t)B * d.dqkv * 4);
+  L.tdmlp = take((size_t)B * d.Fd * 4);
   L.total = off;
   return L;
 }
@@ -229,7 +237,7 @@ struct FrameSink {
   virtual hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                               const Best* last_part, int last_nparts, int32_t vocab_base,
                               int n_slice, int code_vocab, int n_cb, int B, int H, uint16_t* x,
-                              int32_t* ring, uint32_t* frame) = 0;
+                              int32_t* ring, uint32_t* frame, const FeedbackTags& ft) = 0;
 };
 
 struct LaunchSink final : FrameSink {
@@ -239,7 +247,7 @@ struct LaunchSink final : FrameSink {
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
-                      uint32_t* frame) override {
+                      uint32_t* frame, const FeedbackTags&) override {
     return launch_feedback(tok, aemb, codes, last_part, last_nparts, vocab_base, n_slice,
                            code_vocab, n_cb, B, H, x, ring, frame, s);
   }
@@ -252,61 +260,108 @@ struct PlanSink final : FrameSink {
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
-                      uint32_t* frame) override {
+                      uint32_t* frame, const FeedbackTags& ft) override {
     return persist_add_feedback(pl, tok, aemb, codes, last_part, last_nparts, vocab_base, n_slice,
-                                code_vocab, n_cb, B, H, x, ring, frame);
+                                code_vocab, n_cb, B, H, x, ring, frame, ft);
   }
 };
 
-int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink& sink) {
+// The frame's steps in order.  tagged: the steps of a persistent launch,
+// whose intermediate streams are the tagged buffers of the state (32-bit
+// words carrying the producing phase, see gemv_impl.h) and whose GEMVs are
+// told which phase produced each of their inputs.
+int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink& sink,
+                bool tagged = false) {
   const m3_config& c = m->cfg;
   const Dims d = dims_of(c);
   const m3_frame_layout L = layout_of(c, B);
+  auto buf = [&](size_t plain, size_t tag) {
+    return reinterpret_cast<uint16_t*>(S + (tagged ? tag : plain));
+  };
   uint16_t* x = reinterpret_cast<uint16_t*>(S + L.x);
-  uint16_t* h = reinterpret_cast<uint16_t*>(S + L.h);
-  uint16_t* qkv = reinterpret_cast<uint16_t*>(S + L.qkv);
-  uint16_t* mlp = reinterpret_cast<uint16_t*>(S + L.mlp);
+  uint16_t* h_plain = reinterpret_cast<uint16_t*>(S + L.h);
+  uint16_t* h = buf(L.h, L.th);
+  uint16_t* qkv = buf(L.qkv, L.tqkv);
+  uint16_t* mlp = buf(L.mlp, L.tmlp);
   float* logits = reinterpret_cast<float*>(S + L.logits);
-  uint16_t* u = reinterpret_cast<uint16_t*>(S + L.u);
-  uint16_t* hd = reinterpret_cast<uint16_t*>(S + L.hd);
-  uint16_t* dqkv = reinterpret_cast<uint16_t*>(S + L.dqkv);
-  uint16_t* dmlp = reinterpret_cast<uint16_t*>(S + L.dmlp);
+  uint16_t* u = buf(L.u, L.tu);
+  uint16_t* hd = buf(L.hd, L.thd);
+  uint16_t* dqkv = buf(L.dqkv, L.tdqkv);
+  uint16_t* dmlp = buf(L.dmlp, L.tdmlp);
   float* dlogits = reinterpret_cast<float*>(S + L.dlogits);
   int32_t* ring = reinterpret_cast<int32_t*>(S + L.ring);
   uint32_t* frame = reinterpret_cast<uint32_t*>(S + L.frame);
   Best* part_sem = reinterpret_cast<Best*>(S + L.part_sem);
   Best* part_dep = reinterpret_cast<Best*>(S + L.part_dep);
   const float eps = c.eps;
+  // index of the next step, and the step that last wrote each stream (-1:
+  // none in this frame; the frame input is a plain buffer)
+  int ph = 0;
+  int p_h = -1, p_qkv = -1, p_mlp = -1, p_u = -1, p_hd = -1, p_dqkv = -1, p_dmlp = -1;
+  int p_sem = -1, p_dep = -1;
+  struct Prod {
+    int x = -1, res = -1, u = -1, part = -1;
+  };
   auto gemv = [&](int fmt, const void* w, int N, int K, const uint16_t* xin, int ldx,
                   const float* gamma, int sg, int sv, void* y, int ldy, int f32, int epi,
-                  const uint16_t* res, int ldr, const SampleEpi* smp = nullptr,
+                  const uint16_t* res, int ldr, Prod pr, const SampleEpi* smp = nullptr,
                   const GatherPro* gat = nullptr) {
     GemvDesc g{fmt, w, N, K, xin, ldx, B, gamma, eps, sg, sv, y, ldy, f32, epi, res, ldr, smp, gat};
-    return sink.gemv(g);
+    if (tagged) {
+      g.px = pr.x;
+      g.pres = pr.res;
+      g.pu = pr.u;
+      g.ppart = pr.part;
+      g.ytag = 1;
+    }
+    const hipError_t e = sink.gemv(g);
+    ++ph;
+    return e;
   };
   // ---- body ----
   const int group = c.n_heads / c.n_kv_heads;
   for (int l = 0; l < c.n_layers; ++l) {
     const m3_layer_weights& W = m->layers[l];
     const uint16_t* xin = l == 0 ? x : h;
+    const int p_xin = l == 0 ? -1 : p_h;
+    Prod a;
+    a.x = p_xin;
+    p_qkv = ph;
     M3_TRY(gemv(c.fmt_body, W.qkv, d.nqkv, d.H, xin, d.H, W.attn_norm, 0, 0, qkv, d.nqkv, 0,
-                M3_EPI_NONE, nullptr, 0));
+                M3_EPI_NONE, nullptr, 0, a));
+    Prod o;
+    o.x = p_qkv;
+    o.res = p_xin;
+    p_h = ph;
     M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, qkv, d.nqkv, nullptr, group, d.nq + d.nkv, h, d.H, 0,
-                M3_EPI_RESIDUAL, xin, d.H));
+                M3_EPI_RESIDUAL, xin, d.H, o));
+    Prod gu;
+    gu.x = p_h;
+    p_mlp = ph;
     M3_TRY(gemv(c.fmt_body, W.gate_up, 2 * d.F, d.H, h, d.H, W.ffn_norm, 0, 0, mlp, d.F, 0,
-                M3_EPI_SWIGLU, nullptr, 0));
+                M3_EPI_SWIGLU, nullptr, 0, gu));
+    Prod dn;
+    dn.x = p_mlp;
+    dn.res = p_h;
+    p_h = ph;
     M3_TRY(gemv(c.fmt_body, W.down, d.H, d.F, mlp, d.F, nullptr, 0, 0, h, d.H, 0,
-                M3_EPI_RESIDUAL, h, d.H));
+                M3_EPI_RESIDUAL, h, d.H, dn));
   }
   // ---- sliced lm_head; its epilogue adds the Gumbel noise of draw 0 and
   // leaves each row block's winner; the draw completes in the next consumer
   SampleEpi sem{c.seed, frame, 0u, c.temperature, c.vocab_base, c.vocab_base,
                 c.vocab_base + c.n_slice, part_sem};
+  Prod lm;
+  lm.x = p_h;
+  p_sem = ph;
   M3_TRY(gemv(c.fmt_lm, m->lm_head, d.V0, d.H, h, d.H, m->final_norm, 0, 0, logits, d.V0, 1,
-              M3_EPI_NONE, nullptr, 0, &sem));
+              M3_EPI_NONE, nullptr, 0, lm, &sem));
   // ---- depth decoder ----
+  Prod pin;
+  pin.x = p_h;
+  p_u = ph;
   M3_TRY(gemv(c.fmt_depth, m->p_in, d.D, d.H, h, d.H, m->final_norm, 0, 0, u, d.D, 0,
-              M3_EPI_NONE, nullptr, 0));
+              M3_EPI_NONE, nullptr, 0, pin));
   for (int j = 1; j < d.ncb; ++j) {
     // step j's input: bf16(u + Emb_j[previous code]); the previous draw is
     // finished from its row-block winners in the prologue of the first GEMV
@@ -321,24 +376,56 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     gp.codes = codes;
     gp.code_col = j - 1;
     gp.out = hd;
+    const int p_prev_draw = j == 1 ? p_sem : p_dep;
     for (int l = 0; l < c.d_layers; ++l) {
       const m3_layer_weights& W = m->d_layers_w[l];
+      Prod q;
+      if (l == 0) {
+        q.u = p_u;
+        q.part = p_prev_draw;
+        p_hd = ph;              // the gather writes the step's residual stream
+      } else {
+        q.x = p_hd;
+      }
+      p_dqkv = ph;
       M3_TRY(gemv(c.fmt_depth, W.qkv, d.dqkv, d.D, hd, d.D, W.attn_norm, 0, 0, dqkv, d.dqkv, 0,
-                  M3_EPI_NONE, nullptr, 0, nullptr, l == 0 ? &gp : nullptr));
+                  M3_EPI_NONE, nullptr, 0, q, nullptr, l == 0 ? &gp : nullptr));
+      Prod o;
+      o.x = p_dqkv;
+      o.res = p_hd;
+      p_hd = ph;
       M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd, d.D, 0,
-                  M3_EPI_RESIDUAL, hd, d.D));
+                  M3_EPI_RESIDUAL, hd, d.D, o));
+      Prod gu;
+      gu.x = p_hd;
+      p_dmlp = ph;
       M3_TRY(gemv(c.fmt_depth, W.gate_up, 2 * d.Fd, d.D, hd, d.D, W.ffn_norm, 0, 0, dmlp, d.Fd, 0,
-                  M3_EPI_SWIGLU, nullptr, 0));
+                  M3_EPI_SWIGLU, nullptr, 0, gu));
+      Prod dn;
+      dn.x = p_dmlp;
+      dn.res = p_hd;
+      p_hd = ph;
       M3_TRY(gemv(c.fmt_depth, W.down, d.D, d.Fd, dmlp, d.Fd, nullptr, 0, 0, hd, d.D, 0,
-                  M3_EPI_RESIDUAL, hd, d.D));
+                  M3_EPI_RESIDUAL, hd, d.D, dn));
     }
     SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep};
+    Prod hp;
+    hp.x = p_hd;
+    p_dep = ph;
     M3_TRY(gemv(c.fmt_depth, m->heads[j - 1], d.CV, d.D, hd, d.D, m->d_final_norm, 0, 0, dlogits,
-                d.CV, 1, M3_EPI_NONE, nullptr, 0, &dep));
+                d.CV, 1, M3_EPI_NONE, nullptr, 0, hp, &dep));
   }
   // ---- last draw, feedback, code ring, frame counter ----
+  FeedbackTags ft;
+  if (tagged) {
+    ft.last_part_prod = p_dep;
+    ft.th = h;
+    ft.th_prod = p_h;
+    ft.h_out = h_plain;
+    ft.seq = reinterpret_cast<uint32_t*>(S + L.seq);
+  }
   M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, n_blocks(d.CV),
-                       c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame));
+                       c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame, ft));
   return M3_OK;
 }
 
@@ -500,8 +587,7 @@ int m3_frame_state_init(const m3_config* cfg, int B, void* state, const uint16_t
   M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S), 0u, L.total / 4, s));
   M3_TRY(launch_copy_bf16(x0, reinterpret_cast<uint16_t*>(S + L.x), (size_t)B * cfg->hidden, s));
   M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S + L.frame), frame0, 1, s));
-  M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S + L.flags), frame0 * kPhaseStride,
-                         kPersistFlags, s));
+  // (flags, error word, launch counter and the tagged streams start at zero)
   return M3_OK;
 }
 
@@ -581,12 +667,14 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   if ((c.fmt_body != M3_BF16 && c.fmt_body != M3_I8ROW) || c.fmt_lm != c.fmt_body ||
       c.fmt_depth != M3_I8G128)
     return M3_ERR_FORMAT;
+  // row-block winners carry their column in 16 bits next to the tag
+  if (c.n_slice > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;
   uint8_t* S = static_cast<uint8_t*>(state);
   const m3_frame_layout L = layout_of(model->cfg, B);
   PersistPlan* pl = persist_plan_new(B);
   if (!pl) return M3_ERR_HIP;
   PlanSink sink(pl);
-  st = build_frame(model, S, B, codes, sink);
+  st = build_frame(model, S, B, codes, sink, true);
   // recording makes no HIP call: a failure is a step the frame kernel does not carry
   if (st == M3_ERR_HIP) st = M3_ERR_SHAPE;
   if (st == M3_OK && persist_plan_size(pl) != frame_phases(model->cfg)) st = M3_ERR_SHAPE;
@@ -594,7 +682,7 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   if (st == M3_OK && PL) {
     const hipError_t e = persist_upload(pl, S + L.phases, reinterpret_cast<uint32_t*>(S + L.flags),
                                         reinterpret_cast<uint32_t*>(S + L.err),
-                                        reinterpret_cast<const uint32_t*>(S + L.frame),
+                                        reinterpret_cast<const uint32_t*>(S + L.seq),
                                         static_cast<hipStream_t>(stream), PL);
     if (e != hipSuccess) st = M3_ERR_HIP;
   } else if (st == M3_OK) {

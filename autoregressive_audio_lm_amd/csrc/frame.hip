@@ -9,7 +9,7 @@ namespace {
 // one workgroup of 256 threads per batch row
 __global__ __launch_bounds__(256) void feedback_kernel(FeedbackArgs a) {
   __shared__ int c_last[M3_MAX_B_FRAME];
-  feedback_run<false>(a, blockIdx.x, gridDim.x, c_last);
+  feedback_run<false>(a, blockIdx.x, gridDim.x, c_last, 0u);
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const uint16_t* src, uint16_t* dst, size_t n) {
@@ -43,6 +43,11 @@ hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const*
   a.x = x_out;
   a.ring = ring;
   a.frame = frame;
+  a.last_part_prod = -1;
+  a.th = nullptr;
+  a.th_prod = -1;
+  a.h_out = nullptr;
+  a.seq = nullptr;
   hipLaunchKernelGGL(feedback_kernel, dim3(B), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -65,6 +65,9 @@ struct Params {
   int has_sample, has_gather;
   SampleEpi smp;       // sampling epilogue (logits GEMVs)
   GatherPro gat;       // gather prologue (first GEMV of a depth step)
+  // persistent launch only: the phase that produced each input (-1: a plain
+  // bf16 buffer written before the launch) and whether outputs are tagged
+  int px, pres, pu, ppart, ytag;
 };
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -190,6 +193,134 @@ __device__ __forceinline__ void st_best(Best* base, size_t i, const Best& v) {
     base[i] = v;
 }
 
+// ---------------------------------------------------------------------------
+// Tagged activation words (persistent launch).  Inside one persistent launch
+// a GEMV's bf16 outputs are 32-bit words: bits 0..15 the value, bits 16..31
+// the tag of the phase that wrote it (the low 16 bits of launch * 512 + phase
+// + 1).  A consumer reads the words it needs and waits until every tag is the
+// one its producer writes, so a dependency costs one store and one load
+// instead of a store, a completion wait, a flag store, a flag poll and the
+// load.  Stores of 32-bit words are single-copy atomic, so a word with the
+// new tag always carries the new value.  No tag newer than the awaited one
+// can appear: a phase overwrites a buffer only after every workgroup that
+// read it has produced the data that phase waits for.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kPlain = 0xFFFFFFFFu;   // a plain bf16 buffer (no tags)
+constexpr long kSpinLimit = 1L << 21;      // tries (each a memory round trip) before giving up
+
+struct Tags {
+  uint32_t x, res, u, part;   // expected tags of the inputs (kPlain: plain buffer)
+  uint32_t y;                 // tag of this GEMV's outputs (kPlain: plain outputs)
+  uint32_t* err;              // raised when a wait gives up (persistent launch)
+};
+
+__device__ __forceinline__ uint32_t tag_of(int producer, uint32_t ebase) {
+  return producer < 0 ? kPlain : ((ebase + (uint32_t)producer + 1u) & 0xFFFFu);
+}
+
+// Retry loops: spin_more(n, err) is false (and raises *err) once the spin
+// limit has passed or another workgroup raised *err, so every wait ends.
+__device__ __forceinline__ bool spin_more(long& n, uint32_t* err) {
+  if ((++n & 255) == 0 && (n > kSpinLimit || (err && ld4<true>(err, 0) != 0u))) {
+    if (err) st4<true>(err, 0, 1u);
+    return false;
+  }
+  return true;
+}
+
+
+
+__device__ __forceinline__ uint4 untag8(const uint4& a, const uint4& b, uint32_t tag, bool& ok) {
+  ok = (a.x >> 16) == tag && (a.y >> 16) == tag && (a.z >> 16) == tag && (a.w >> 16) == tag &&
+       (b.x >> 16) == tag && (b.y >> 16) == tag && (b.z >> 16) == tag && (b.w >> 16) == tag;
+  return make_uint4((a.x & 0xffffu) | (a.y << 16), (a.z & 0xffffu) | (a.w << 16),
+                    (b.x & 0xffffu) | (b.y << 16), (b.z & 0xffffu) | (b.w << 16));
+}
+
+// one attempt at elements e .. e+7 of an activation row buffer
+template <bool COH>
+__device__ __forceinline__ uint4 act_try8(const void* base, size_t e, uint32_t tag, bool& ok) {
+  if constexpr (COH) {
+    if (tag != kPlain) {
+      const uint4 a = ld16<true>(base, e * 4), b = ld16<true>(base, e * 4 + 16);
+      return untag8(a, b, tag, ok);
+    }
+  }
+  ok = true;
+  return ld16<COH>(base, e * 2);
+}
+
+template <bool COH>
+__device__ __forceinline__ uint4 act_load8(const void* base, size_t e, uint32_t tag, uint32_t* err) {
+  bool ok;
+  uint4 v = act_try8<COH>(base, e, tag, ok);
+  if constexpr (COH) {
+    long n = 0;
+    while (!ok && spin_more(n, err)) v = act_try8<COH>(base, e, tag, ok);
+  }
+  return v;
+}
+
+template <bool COH>
+__device__ __forceinline__ void act_store8(void* base, size_t e, const uint4& v, uint32_t tag) {
+  if constexpr (COH) {
+    if (tag != kPlain) {
+      const uint32_t t = tag << 16;
+      st16<true>(base, e * 4, make_uint4((v.x & 0xffffu) | t, (v.x >> 16) | t,
+                                         (v.y & 0xffffu) | t, (v.y >> 16) | t));
+      st16<true>(base, e * 4 + 16, make_uint4((v.z & 0xffffu) | t, (v.z >> 16) | t,
+                                              (v.w & 0xffffu) | t, (v.w >> 16) | t));
+      return;
+    }
+  }
+  st16<COH>(base, e * 2, v);
+}
+
+template <bool COH>
+__device__ __forceinline__ uint32_t act_load1(const void* base, size_t e, uint32_t tag, uint32_t* err) {
+  if constexpr (COH) {
+    if (tag != kPlain) {
+      uint32_t w = ld4<true>(base, e * 4);
+      long n = 0;
+      while ((w >> 16) != tag && spin_more(n, err)) w = ld4<true>(base, e * 4);
+      return w & 0xffffu;
+    }
+  }
+  return ld2<COH>(base, e * 2);
+}
+
+template <bool COH>
+__device__ __forceinline__ void act_store1(void* base, size_t e, uint32_t bf, uint32_t tag) {
+  if constexpr (COH) {
+    if (tag != kPlain) {
+      st4<true>(base, e * 4, (bf & 0xffffu) | (tag << 16));
+      return;
+    }
+  }
+  st2<COH>(base, e * 2, bf);
+}
+
+// row-block winners: the column (< 65535; 0xffff = none) with the tag above it
+__device__ __forceinline__ Best part_tag(const Best& r, uint32_t tag) {
+  if (tag == kPlain) return r;
+  const uint32_t j = r.j == 0x7fffffff ? 0xffffu : ((uint32_t)r.j & 0xffffu);
+  return Best{r.z, (int)(j | (tag << 16))};
+}
+
+template <bool COH>
+__device__ __forceinline__ Best part_load(const Best* base, size_t i, uint32_t tag, uint32_t* err) {
+  Best r = ld_best<COH>(base, i);
+  if constexpr (COH) {
+    if (tag != kPlain) {
+      long n = 0;
+      while (((uint32_t)r.j >> 16) != tag && spin_more(n, err)) r = ld_best<true>(base, i);
+      const uint32_t j = (uint32_t)r.j & 0xffffu;
+      r.j = j == 0xffffu ? 0x7fffffff : (int)j;
+    }
+  }
+  return r;
+}
+
 // source column of operand element k (8-aligned chunk) in x
 __device__ __forceinline__ int src_col(const Params& p, int k) {
   if (p.stub_group <= 0) return k;
@@ -197,21 +328,26 @@ __device__ __forceinline__ int src_col(const Params& p, int k) {
 }
 
 template <bool COH>
-__device__ __forceinline__ uint4 load_x8(const Params& p, int b, int k) {
-  return ld16<COH>(p.x, ((size_t)b * p.ldx + src_col(p, k)) * 2);
+__device__ __forceinline__ uint4 load_x8(const Params& p, int b, int k, const Tags& tg) {
+  return act_load8<COH>(p.x, (size_t)b * p.ldx + src_col(p, k), tg.x, tg.err);
+}
+
+template <bool COH>
+__device__ __forceinline__ uint4 try_x8(const Params& p, int b, int k, const Tags& tg, bool& ok) {
+  return act_try8<COH>(p.x, (size_t)b * p.ldx + src_col(p, k), tg.x, ok);
 }
 
 // Gather prologue: the previous draw of every batch row, from the per-block
 // winners the head GEMV wrote (rows b = wave, wave + 8, ... per wave).
 template <bool COH>
-__device__ __forceinline__ void gather_codes(const Params& p, int* code_lds, int wg) {
+__device__ __forceinline__ void gather_codes(const Params& p, int* code_lds, int wg, const Tags& tg) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const GatherPro& g = p.gat;
   for (int b = wave; b < p.lds_rows; b += kWaves) {
     float bz = -INFINITY;
     int bj = 0x7fffffff;
     for (int c = lane; c < g.nparts; c += 64) {
-      const Best r = ld_best<COH>(g.part, (size_t)b * g.nparts + c);
+      const Best r = part_load<COH>(g.part, (size_t)b * g.nparts + c, tg.part, tg.err);
       if (above(r.z, r.j, bz, bj)) {
         bz = r.z;
         bj = r.j;
@@ -259,7 +395,7 @@ struct XPre {
 };
 
 template <bool COH>
-__device__ __forceinline__ void prefetch_x(const Params& p, XPre& pre) {
+__device__ __forceinline__ void prefetch_x(const Params& p, XPre& pre, const Tags& tg) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -267,34 +403,60 @@ __device__ __forceinline__ void prefetch_x(const Params& p, XPre& pre) {
     for (int r = 0; r < kPreRounds; ++r) {
       const int k = (r * kThreads + tid) << 3;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (b < p.lds_rows && k < p.K) v = load_x8<COH>(p, b, k);
+      if (b < p.lds_rows && k < p.K) v = load_x8<COH>(p, b, k, tg);
       pre.v[b][r] = v;
     }
   }
   pre.valid = true;
 }
 
+// The operand chunk of row b at k (8 values): x (attention-stub remap), or in
+// gather mode bf16(u[b] + emb row); k >= K is zero.  try: one attempt (ok =
+// the tags matched); settle: until it succeeds.
 template <bool COH>
-__device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, float* ss_buf, const int* code_lds,
-                               int wg, const XPre& pre) {
+struct OperandSource {
+  const Params& p;
+  const Tags& tg;
+  const int* code_lds;
+
+  __device__ __forceinline__ const uint16_t* emb_row(int b) const {
+    int c = code_lds[b] - p.gat.code_base;
+    if (c < 0 || c >= p.gat.n_codes) c = 0;
+    return p.gat.emb + (size_t)c * p.K;
+  }
+
+  __device__ __forceinline__ uint4 attempt(int b, int k, bool& ok) const {
+    ok = true;
+    if (k >= p.K) return make_uint4(0, 0, 0, 0);
+    if (p.has_gather) {
+      const uint4 uv = act_try8<COH>(p.gat.u, (size_t)b * p.K + k, tg.u, ok);
+      return bf16x8_add(uv, *reinterpret_cast<const uint4*>(emb_row(b) + k));
+    }
+    return try_x8<COH>(p, b, k, tg, ok);
+  }
+
+  __device__ __forceinline__ uint4 settle(int b, int k) const {
+    bool ok;
+    uint4 v = attempt(b, k, ok);
+    if constexpr (COH) {
+      long n = 0;
+      while (!ok && spin_more(n, tg.err)) v = attempt(b, k, ok);
+    }
+    return v;
+  }
+};
+
+template <bool COH>
+__device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, float* ss_buf,
+                                               const int* code_lds, int wg, const XPre& pre,
+                                               const Tags& tg) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int stride = p.lds_stride;
   const int nchunk = (stride - 8) >> 3;
-  auto fetch = [&](int b, int k, const uint16_t* erow) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (k < p.K) {
-      if (p.has_gather) {
-        v = bf16x8_add(ld16<COH>(p.gat.u, ((size_t)b * p.K + k) * 2),
-                       *reinterpret_cast<const uint4*>(erow + k));
-        if (wg == 0) st16<COH>(p.gat.out, ((size_t)b * p.K + k) * 2, v);
-      } else {
-        v = load_x8<COH>(p, b, k);
-      }
-    }
-    return v;
-  };
+  const OperandSource<COH> src{p, tg, code_lds};
   auto put = [&](int b, int k, const uint4& v, float& ss) {
     *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v;
+    if (p.has_gather && wg == 0 && k < p.K) act_store8<COH>(p.gat.out, (size_t)b * p.K + k, v, tg.y);
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -306,23 +468,43 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (b >= p.lds_rows) break;
-    const uint16_t* erow = nullptr;
-    if (p.has_gather) {
-      int c = code_lds[b] - p.gat.code_base;
-      if (c < 0 || c >= p.gat.n_codes) c = 0;
-      erow = p.gat.emb + (size_t)c * p.K;
-    }
     float ss = 0.f;
-    if (pre.valid) {
+    if constexpr (!COH) {
+      if (pre.valid) {
+#pragma unroll
+        for (int r = 0; r < kPreRounds; ++r) {
+          const int i = r * kThreads + tid;
+          if (i < nchunk) put(b, i << 3, pre.v[b][r], ss);
+        }
+        for (int i = kPreRounds * kThreads + tid; i < nchunk; i += kThreads)
+          put(b, i << 3, src.settle(b, i << 3), ss);
+      } else {
+        for (int i = tid; i < nchunk; i += kThreads) put(b, i << 3, src.settle(b, i << 3), ss);
+      }
+    } else {
+      // request every chunk first, then wait for the ones not yet written
+      uint4 v[kPreRounds];
+      bool ok[kPreRounds];
 #pragma unroll
       for (int r = 0; r < kPreRounds; ++r) {
         const int i = r * kThreads + tid;
-        if (i < nchunk) put(b, i << 3, pre.v[b][r], ss);
+        ok[r] = true;
+        v[r] = make_uint4(0, 0, 0, 0);
+        if (i < nchunk) v[r] = src.attempt(b, i << 3, ok[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < kPreRounds; ++r) {
+        const int k = (r * kThreads + tid) << 3;
+        long n = 0;
+        while (!ok[r] && spin_more(n, tg.err)) v[r] = src.attempt(b, k, ok[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < kPreRounds; ++r) {
+        const int i = r * kThreads + tid;
+        if (i < nchunk) put(b, i << 3, v[r], ss);
       }
       for (int i = kPreRounds * kThreads + tid; i < nchunk; i += kThreads)
-        put(b, i << 3, fetch(b, i << 3, erow), ss);
-    } else {
-      for (int i = tid; i < nchunk; i += kThreads) put(b, i << 3, fetch(b, i << 3, erow), ss);
+        put(b, i << 3, src.settle(b, i << 3), ss);
     }
     ss = wave_sum(ss);
     if (lane == 0) ss_buf[M3_MAX_B + b * kWaves + wave] = ss;
@@ -337,37 +519,40 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
 }
 
 template <bool COH>
-__device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf, int* code_lds, int wg,
-                                  const XPre& pre) {
+__device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf,
+                                                  int* code_lds, int wg, const XPre& pre,
+                                                  const Tags& tg) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int stride = p.lds_stride;
   const int cpr = (stride - 8) >> 3;            // chunks per row: K, padding, zero tile
   const int total = p.lds_rows * cpr;
-  if (p.has_gather) gather_codes<COH>(p, code_lds, wg);
+  if (p.has_gather) gather_codes<COH>(p, code_lds, wg, tg);
   if (p.lds_rows <= 2) {
-    stage_rows_few<COH>(p, act, ss_buf, code_lds, wg, pre);
+    stage_rows_few<COH>(p, act, ss_buf, code_lds, wg, pre, tg);
     if (!p.gamma) return;
   } else {
-  // pass 1: copy
+  // pass 1: copy (all requests of a group first; wait for late ones after)
+  const OperandSource<COH> src{p, tg, code_lds};
   for (int base = tid; base < total; base += kThreads * kStageUnroll) {
     uint4 v[kStageUnroll];
+    bool ok[kStageUnroll];
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
       const int it = base + u * kThreads;
       const int b = it / cpr, k = (it - b * cpr) * 8;
       const bool in = it < total && k < p.K;
-      const int bs = in ? b : 0, ks = in ? k : 0;
-      uint4 x;
-      if (p.has_gather) {
-        int c = code_lds[bs] - p.gat.code_base;
-        c = (c < 0 || c >= p.gat.n_codes) ? 0 : c;
-        const uint4 uv = ld16<COH>(p.gat.u, ((size_t)bs * p.K + ks) * 2);
-        const uint4 ev = *reinterpret_cast<const uint4*>(p.gat.emb + (size_t)c * p.K + ks);
-        x = bf16x8_add(uv, ev);
-      } else {
-        x = load_x8<COH>(p, bs, ks);
-      }
+      const uint4 x = src.attempt(in ? b : 0, in ? k : 0, ok[u]);
       v[u] = in ? x : make_uint4(0, 0, 0, 0);
+      ok[u] = ok[u] || !in;
+    }
+    if constexpr (COH) {
+#pragma unroll
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int it = base + u * kThreads;
+        const int b = it / cpr, k = (it - b * cpr) * 8;
+        long n = 0;
+        while (!ok[u] && spin_more(n, tg.err)) v[u] = src.attempt(b, k, ok[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
@@ -376,7 +561,7 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
         const int b = it / cpr, k = (it - b * cpr) * 8;
         *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v[u];
         if (p.has_gather && wg == 0 && k < p.K)
-          st16<COH>(p.gat.out, ((size_t)b * p.K + k) * 2, v[u]);
+          act_store8<COH>(p.gat.out, (size_t)b * p.K + k, v[u], tg.y);
       }
     }
   }
@@ -428,26 +613,28 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
 // 8 operand values of row b from k; k >= K reads zeros.  Branch-free, so the
 // waits for the weight stream are not made conservative by control flow.
 template <bool LDS, bool COH>
-__device__ __forceinline__ uint4 act8(const Params& p, const uint16_t* act, int b, int k) {
+__device__ __forceinline__ uint4 act8(const Params& p, const uint16_t* act, int b, int k,
+                                      const Tags& tg) {
   if constexpr (LDS) {
     return *reinterpret_cast<const uint4*>(act + (size_t)b * p.lds_stride + k);
   } else {
     const bool in = k < p.K;
-    const uint4 v = load_x8<COH>(p, b, in ? k : 0);
+    const uint4 v = load_x8<COH>(p, b, in ? k : 0, tg);
     return in ? v : make_uint4(0, 0, 0, 0);
   }
 }
 
 // Epilogue for one output element (or a gate/up pair) after the cross-wave sum.
 template <bool COH>
-__device__ __forceinline__ void store_out(const Params& p, int b, int n, float v) {
+__device__ __forceinline__ void store_out(const Params& p, int b, int n, float v, const Tags& tg) {
   if (p.out_f32) {
     st4<COH>(p.y, ((size_t)b * p.ldy + n) * 4, __float_as_uint(v));
     return;
   }
   uint32_t o = f2bf(v);
-  if (p.epi == M3_EPI_RESIDUAL) o = f2bf(bf2f(ld2<COH>(p.res, ((size_t)b * p.ldr + n) * 2)) + bf2f(o));
-  st2<COH>(p.y, ((size_t)b * p.ldy + n) * 2, o);
+  if (p.epi == M3_EPI_RESIDUAL)
+    o = f2bf(bf2f(act_load1<COH>(p.res, (size_t)b * p.ldr + n, tg.res, tg.err)) + bf2f(o));
+  act_store1<COH>(p.y, (size_t)b * p.ldy + n, o, tg.y);
 }
 
 template <int FMT>
@@ -457,11 +644,16 @@ __device__ __forceinline__ float row_scale(const uint8_t* blk, const Params& p, 
   return 1.0f;
 }
 
-// Cross-wave reduction in fixed wave order, scale, epilogue, store.
-template <int FMT, int NB, bool GLU, bool COH>
-__device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const float* red) {
+// Cross-wave reduction in fixed wave order, scale, epilogue, store.  GLU: 0
+// plain, 1 SwiGLU, 2 chosen at run time by p.epi (one code path for both in
+// the persistent kernel, where every compiled variant costs registers).
+constexpr int kGluRuntime = 2;
+
+template <int FMT, int NB, int GLU, bool COH>
+__device__ __forceinline__ void finish_block(const Params& p, const uint8_t* blk, int rb,
+                                             const float* red, const Tags& tg) {
   const int tid = threadIdx.x;
-  if constexpr (GLU) {
+  if (GLU == 1 || (GLU == kGluRuntime && p.epi == M3_EPI_SWIGLU)) {
     for (int t = tid; t < p.B * 8; t += kThreads) {
       const int b = t >> 3, pr = t & 7;
       const int n = rb * 16 + 2 * pr;
@@ -476,7 +668,7 @@ __device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const 
       vu *= row_scale<FMT>(blk, p, 2 * pr + 1);
       const float g = bf2f(f2bf(vg)), u = bf2f(f2bf(vu));
       const float s = g / (1.0f + expf(-g));
-      st2<COH>(p.y, ((size_t)b * p.ldy + (n >> 1)) * 2, f2bf(s * u));
+      act_store1<COH>(p.y, (size_t)b * p.ldy + (n >> 1), f2bf(s * u), tg.y);
     }
     return;
   }
@@ -506,7 +698,8 @@ __device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const 
           z = gumbel_z(v, inv_t, gumbel_noise(sm.seed, (uint32_t)b, frame, sm.draw, (uint32_t)id));
       }
       best_reduce(z, j, 16);
-      if (t < p.B * 16 && r == 0) st_best<COH>(sm.part, (size_t)b * p.nblocks + rb, Best{z, j});
+      if (t < p.B * 16 && r == 0)
+        st_best<COH>(sm.part, (size_t)b * p.nblocks + rb, part_tag(Best{z, j}, tg.y));
     }
     return;
   }
@@ -518,7 +711,7 @@ __device__ void finish_block(const Params& p, const uint8_t* blk, int rb, const 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += red[(w * NB + b) * 16 + r];
     v *= row_scale<FMT>(blk, p, r);
-    store_out<COH>(p, b, n, v);
+    store_out<COH>(p, b, n, v, tg);
   }
 }
 
@@ -562,7 +755,8 @@ struct Accum {
   }
 
   template <bool LDS, bool COH>
-  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0) {
+  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0,
+                                       const Tags& tg) {
     float* dst = FMT == M3_I8G128 ? gacc : acc;
     const int c = (threadIdx.x & 63) >> 4;
     if constexpr (FMT == M3_BF16) {
@@ -570,7 +764,7 @@ struct Accum {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         // rows past B repeat row B-1 (valid memory); their sums are never stored
-        const uint4 av = act8<LDS, COH>(p, act, min(b, p.B - 1), kk);
+        const uint4 av = act8<LDS, COH>(p, act, min(b, p.B - 1), kk, tg);
         float a = dst[b];
         a = dot2(wv.x, av.x, a);
         a = dot2(wv.y, av.y, a);
@@ -585,8 +779,8 @@ struct Accum {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int bb = min(b, p.B - 1);
-        const uint4 a0 = act8<LDS, COH>(p, act, bb, kk);
-        const uint4 a1 = act8<LDS, COH>(p, act, bb, kk + 8);
+        const uint4 a0 = act8<LDS, COH>(p, act, bb, kk, tg);
+        const uint4 a1 = act8<LDS, COH>(p, act, bb, kk + 8, tg);
         float a = dst[b];
         a = dot2(wb[0], a0.x, a);
         a = dot2(wb[1], a0.y, a);
@@ -639,7 +833,8 @@ struct Accum<FMT, NB, true> {
   }
 
   template <bool LDS, bool COH>
-  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0) {
+  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0,
+                                       const Tags& tg) {
     f32x4_t* dst = FMT == M3_I8G128 ? gacc : acc;
     const int lane = threadIdx.x & 63, c = lane >> 4, i = lane & 15;
     if constexpr (FMT == M3_BF16) {
@@ -648,7 +843,7 @@ struct Accum<FMT, NB, true> {
 #pragma unroll
       for (int bt = 0; bt < NT; ++bt) {
         const int b = min(bt * 16 + i, p.B - 1);
-        const uint4 av = act8<LDS, COH>(p, act, b, kk);
+        const uint4 av = act8<LDS, COH>(p, act, b, kk, tg);
         dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), bw,
                                                           dst[bt], 0, 0, 0);
       }
@@ -661,8 +856,8 @@ struct Accum<FMT, NB, true> {
 #pragma unroll
       for (int bt = 0; bt < NT; ++bt) {
         const int b = min(bt * 16 + i, p.B - 1);
-        const uint4 a0 = act8<LDS, COH>(p, act, b, kk);
-        const uint4 a1 = act8<LDS, COH>(p, act, b, kk + 8);
+        const uint4 a0 = act8<LDS, COH>(p, act, b, kk, tg);
+        const uint4 a1 = act8<LDS, COH>(p, act, b, kk + 8, tg);
         dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), blo,
                                                           dst[bt], 0, 0, 0);
         dst[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), bhi,
@@ -707,9 +902,12 @@ struct Accum<FMT, NB, true> {
 struct NoWait {
   __device__ bool probe() const { return true; }
   __device__ bool wait() const { return true; }
+  __device__ uint32_t ebase() const { return 0u; }
+  __device__ int phase() const { return 0; }
+  __device__ uint32_t* err() const { return nullptr; }
 };
 
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU, bool COH, class Wait>
+template <int FMT, int NB, bool MFMA, bool LDS, int GLU, int KU, bool COH, class Wait>
 __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg, int nwg, Wait&& wt) {
   constexpr int kU = KU;
   static_assert(kU % 2 == 0 && kU <= 16, "batches hold whole i8g128 groups");
@@ -727,6 +925,16 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   const int nbat = ((units + kWaves - 1) / kWaves * TPU + kU - 1) / kU;   // same for all waves
   const int my_blocks = wg < p.nblocks ? (p.nblocks - wg + nwg - 1) / nwg : 0;
   const int nitems = my_blocks * nbat;
+  Tags tg;
+  {
+    const uint32_t eb = wt.ebase();
+    tg.x = tag_of(p.px, eb);
+    tg.res = tag_of(p.pres, eb);
+    tg.u = tag_of(p.pu, eb);
+    tg.part = tag_of(p.ppart, eb);
+    tg.y = p.ytag ? tag_of(wt.phase(), eb) : kPlain;
+    tg.err = wt.err();
+  }
 
   // Every wave walks nbat * kU tiles per row block.  Tiles past the end of its
   // K-slice, and the prefetch past the last item, are out-of-range buffer
@@ -769,7 +977,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
     for (int i = 0; i < kU; ++i) {
       const int tt = bi * kU + i;
       const bool real = tt < ntw;
-      A.template tile<LDS, COH>(p, act, src[i], real ? (t_lo + tt) * TK : p.Kp);
+      A.template tile<LDS, COH>(p, act, src[i], real ? (t_lo + tt) * TK : p.Kp, tg);
       if (FMT == M3_I8G128 && (i & 1)) {
         // groups are tile pairs (t_lo and kU are even): scale the finished group
         A.group_end(real ? scv[i >> 1] : 0.f);
@@ -778,7 +986,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
     if (bi == nbat - 1) {          // row block complete: cross-wave sum and epilogue
       A.to_red(red, wave);
       __syncthreads();
-      finish_block<FMT, NB, GLU, COH>(p, p.w + (size_t)rb * p.bbytes, rb, red);
+      finish_block<FMT, NB, GLU, COH>(p, p.w + (size_t)rb * p.bbytes, rb, red, tg);
       __syncthreads();
       A.reset();
     }
@@ -792,7 +1000,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   if (ready) {
     // (persistent launches: only phase 0, whose operand is plain; not worth the registers)
     if constexpr (LDS && !COH) {
-      if (p.lds_rows <= 2 && !p.has_gather && nitems > 0) prefetch_x<COH>(p, pre);
+      if (p.lds_rows <= 2 && !p.has_gather && nitems > 0) prefetch_x<COH>(p, pre, tg);
     }
     load(bufA, scA, 0);
   } else {
@@ -801,7 +1009,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
     if (!wt.wait()) return;
   }
   if (nitems == 0) return;
-  if (LDS) stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre);
+  if (LDS) stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre, tg);
   if (ready) load(bufB, scB, 1);
   __builtin_amdgcn_sched_barrier(0);
   // the scheduling barriers keep each batch's loads ahead of the next batch's
@@ -823,7 +1031,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
 template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
   extern __shared__ __align__(16) uint8_t smem[];
-  gemv_run<FMT, NB, MFMA, LDS, GLU, KU, false>(p, smem, blockIdx.x, gridDim.x, NoWait{});
+  gemv_run<FMT, NB, MFMA, LDS, GLU ? 1 : 0, KU, false>(p, smem, blockIdx.x, gridDim.x, NoWait{});
 }
 
 // ---------------------------------------------------------------------------
@@ -888,6 +1096,11 @@ inline Params make_params(const GemvDesc& d, bool* lds, int* ku) {
   p.has_gather = d.gather != nullptr;
   if (d.sample) p.smp = *d.sample;
   if (d.gather) p.gat = *d.gather;
+  p.px = d.px;
+  p.pres = d.pres;
+  p.pu = d.pu;
+  p.ppart = d.ppart;
+  p.ytag = d.ytag;
   *ku = ku_of(d.fmt, *lds);
   return p;
 }

@@ -72,6 +72,9 @@ struct GemvDesc {
   int ldr;
   const SampleEpi* sample = nullptr;
   const GatherPro* gather = nullptr;
+  // persistent frame only: producing phase of x / residual / gather u /
+  // gather partials (-1: plain buffer), tagged outputs
+  int px = -1, pres = -1, pu = -1, ppart = -1, ytag = 0;
 };
 
 // Largest fused-norm activation block held in LDS (elements of B * K_pad).
@@ -118,12 +121,20 @@ hipError_t launch_copy_bf16(const uint16_t* src, uint16_t* dst, size_t n, hipStr
 
 // ---- persistent frame (persist.hip) -------------------------------------------
 // A frame recorded as a table of phases (one GEMV each, then the frame end)
-// and run as one cooperative launch.  Flags of workgroups that finished phase
-// i of frame f hold f * kPhaseStride + i + 1.
+// and run as one cooperative launch.  Epoch of phase i of launch n: n *
+// kPhaseStride + i + 1 (flags hold it, tagged words its low 16 bits).
 constexpr uint32_t kPhaseStride = 512;
 constexpr int kPersistFlags = 256;       // flag words (one per workgroup, at most 256)
 struct PersistPlan;
 struct PersistLaunch;
+// what the frame end of a persistent launch needs about the tagged streams
+struct FeedbackTags {
+  int last_part_prod = -1;       // step that wrote the last draw's row-block winners
+  const void* th = nullptr;      // tagged body residual stream
+  int th_prod = -1;              // step that last wrote it
+  uint16_t* h_out = nullptr;     // plain copy of it for the caller
+  uint32_t* seq = nullptr;       // launch counter
+};
 size_t persist_phase_bytes();
 int persist_max_phases();
 PersistPlan* persist_plan_new(int B);
@@ -134,12 +145,13 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
                                 const uint16_t* const* audio_emb, int32_t* codes,
                                 const Best* last_part, int last_nparts, int32_t vocab_base,
                                 int n_slice, int code_vocab, int n_cb, int B, int H,
-                                uint16_t* x_out, int32_t* ring, uint32_t* frame);
+                                uint16_t* x_out, int32_t* ring, uint32_t* frame,
+                                const FeedbackTags& ft);
 PersistLaunch* persist_launch_new();
 void persist_launch_free(PersistLaunch* L);
 // copy the table into device memory, reset flags and the error word (synchronises `s`)
 hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
-                          const uint32_t* frame, hipStream_t s, PersistLaunch* out);
+                          const uint32_t* seq, hipStream_t s, PersistLaunch* out);
 hipError_t persist_launch(const PersistLaunch& L, hipStream_t s);
 // the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip) by row-count class
 const void* persist_kernel_bf16(int NB);

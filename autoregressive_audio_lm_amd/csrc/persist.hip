@@ -29,9 +29,9 @@ namespace {
 
 constexpr int kMaxPhases = (int)kPhaseStride - 1;
 
-__global__ void flags_init_kernel(uint32_t* flags, int n, const uint32_t* frame, uint32_t* err) {
+__global__ void flags_init_kernel(uint32_t* flags, int n, const uint32_t* seq, uint32_t* err) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) flags[i] = *frame * kPhaseStride;
+  if (i < n) flags[i] = *seq * kPhaseStride;
   if (i == 0) *err = 0u;
 }
 
@@ -75,15 +75,10 @@ hipError_t persist_add_gemv(PersistPlan* pl, const GemvDesc& d) {
     if (d.fmt != pl->fmt_body) return hipErrorInvalidValue;
     cls = 0;
   }
-  const int NB = nb_of(d.B);
-  int arm;
-  if (!lds) {
-    if (d.epi == M3_EPI_SWIGLU || NB < 16) return hipErrorInvalidValue;
-    arm = kArmGlobal;
-  } else {
-    arm = d.epi == M3_EPI_SWIGLU ? kArmGlu : kArmLds;
-  }
-  ph.variant = cls * 4 + arm;
+  // every operand is staged in LDS (the tagged waits happen while staging)
+  if (!lds) return hipErrorInvalidValue;
+  ph.variant = cls;
+  ph.signal = 0;
   const size_t smem = smem_bytes_of(d.fmt, d.K, d.B, d.gamma != nullptr);
   if (smem > pl->smem) pl->smem = smem;
   pl->phases.push_back(ph);
@@ -94,8 +89,9 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
                                 const uint16_t* const* audio_emb, int32_t* codes,
                                 const Best* last_part, int last_nparts, int32_t vocab_base,
                                 int n_slice, int code_vocab, int n_cb, int B, int H,
-                                uint16_t* x_out, int32_t* ring, uint32_t* frame) {
-  if ((int)pl->phases.size() >= kMaxPhases) return hipErrorInvalidValue;
+                                uint16_t* x_out, int32_t* ring, uint32_t* frame,
+                                const FeedbackTags& ft) {
+  if ((int)pl->phases.size() >= kMaxPhases || pl->phases.empty()) return hipErrorInvalidValue;
   FeedbackArgs& a = pl->fb;
   a.tok = tok_emb_audio;
   for (int i = 0; i < 8; ++i) a.aemb[i] = (i < n_cb - 1) ? audio_emb[i] : nullptr;
@@ -111,8 +107,16 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
   a.x = x_out;
   a.ring = ring;
   a.frame = frame;
+  a.last_part_prod = ft.last_part_prod;
+  a.th = ft.th;
+  a.th_prod = ft.th_prod;
+  a.h_out = ft.h_out;
+  a.seq = ft.seq;
+  // the frame end waits (on the flags) for every workgroup to finish the step before it
+  pl->phases.back().signal = 1;
   Phase ph{};
   ph.variant = kFeedbackVariant;
+  ph.signal = 0;
   pl->phases.push_back(ph);
   return hipSuccess;
 }
@@ -124,7 +128,7 @@ struct PersistLaunch {
   int nph;
   uint32_t* flags;
   uint32_t* err;
-  const uint32_t* frame;
+  const uint32_t* seq;
   FeedbackArgs fb;
   size_t smem;
   int nwg;
@@ -133,7 +137,7 @@ struct PersistLaunch {
 // Copy the table to `table` (device, persist_phase_bytes() * size), set the
 // flags to "phase -1 of the current frame done", clear the error word.
 hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
-                          const uint32_t* frame, hipStream_t s, PersistLaunch* out) {
+                          const uint32_t* seq, hipStream_t s, PersistLaunch* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -151,7 +155,7 @@ hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, u
                      hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(flags_init_kernel, dim3(1), dim3(kPersistFlags), 0, s, flags, kPersistFlags,
-                     frame, err);
+                     seq, err);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipStreamSynchronize(s);      // the host table may go away after this
@@ -161,7 +165,7 @@ hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, u
   out->nph = (int)pl->phases.size();
   out->flags = flags;
   out->err = err;
-  out->frame = frame;
+  out->seq = seq;
   out->fb = pl->fb;
   out->smem = pl->smem;
   out->nwg = nwg;
@@ -173,9 +177,9 @@ hipError_t persist_launch(const PersistLaunch& L, hipStream_t s) {
   int nph = L.nph;
   uint32_t* flags = L.flags;
   uint32_t* err = L.err;
-  const uint32_t* frame = L.frame;
+  const uint32_t* seq = L.seq;
   FeedbackArgs fb = L.fb;
-  void* args[] = {&ph, &nph, &flags, &err, &frame, &fb};
+  void* args[] = {&ph, &nph, &flags, &err, &seq, &fb};
   return hipLaunchCooperativeKernel(L.kernel, dim3(L.nwg), dim3(kThreads), args, (unsigned)L.smem, s);
 }
 

@@ -5,26 +5,19 @@
 namespace m3 {
 namespace {
 
-constexpr long kSpinLimit = 1L << 21;        // polls (each a memory round trip) before giving up
-
 // Phase kinds.  A frame kernel is compiled for one body format FB (bf16 or
 // int8-row, also the lm_head's) with the depth decoder in int8-g128: every
-// variant it carries costs registers in all of them, so it carries only
-// these.  variant = class * 4 + arm; class 0 = FB, 1 = int8-g128; arm 0 =
-// operand staged in LDS, 1 = the same with the SwiGLU epilogue, 2 = operand
-// read from global memory (only compiled for 16-row tiles: below 5 rows every
-// operand of the frame fits LDS).
-constexpr int kArmLds = 0, kArmGlu = 1, kArmGlobal = 2;
+// variant it carries costs registers in all of them, so it carries only two:
+// variant 0 = FB, 1 = int8-g128, the epilogue chosen at run time and the
+// operand always staged in LDS (the frame is recorded only when it fits).
 constexpr int kFeedbackVariant = -1;
 
 struct Phase {
   Params p;
   int variant;
-  int pad[3];
+  int signal;          // publish completion through the flags (the frame end waits for it)
+  int pad[2];
 };
-
-template <int NB>
-constexpr bool global_arm(int) { return NB >= 16; }
 
 // has every workgroup's flag reached `target`?  (wave 0; one coherent load per lane)
 __device__ __forceinline__ bool flags_reached(const uint32_t* flags, int nwg, uint32_t target) {
@@ -38,43 +31,40 @@ __device__ __forceinline__ bool flags_reached(const uint32_t* flags, int nwg, ui
   return __all(done);
 }
 
-// The producer of phase i's operand is phase i-1 (all workgroups).  wait():
-// wave 0 polls until done, or until the spin limit passed or another
-// workgroup raised the error word.
-struct PhaseWait {
-  const uint32_t* flags;
-  uint32_t* err;
-  uint32_t target;
-  int nwg;
-  bool first;          // phase 0: the operand was written before the launch
-  int* s_ok;
-  bool* ok;
+// GEMV phases wait inside their loads (tagged words): nothing to do before
+// the weight stream but report whether the operand is plain and ready (phase
+// 0 reads the launch's plain input).
+struct TagWait {
+  uint32_t eb;
+  int i;
+  uint32_t* er;
+  __device__ bool probe() const { return i == 0; }
+  __device__ bool wait() const { return true; }
+  __device__ uint32_t ebase() const { return eb; }
+  __device__ int phase() const { return i; }
+  __device__ uint32_t* err() const { return er; }
+};
 
-  // Looking costs a round trip before the weight stream starts, and most
-  // workgroups find the producer still running: report "not ready" without
-  // looking (except for phase 0) so that two batches stream during the wait.
-  __device__ bool probe() { return first; }
-
-  __device__ bool wait() {
-    if (threadIdx.x < 64) {
-      int good = 1;
-      long spins = 0;
-      while (!flags_reached(flags, nwg, target)) {
-        if ((++spins & 63) == 0 && (spins > kSpinLimit || ld4<true>(err, 0) != 0u)) {
-          good = 0;
-          break;
-        }
-      }
-      if (threadIdx.x == 0) {
-        *s_ok = good;
-        if (!good) st4<true>(err, 0, 1u);
+// The frame end waits for every workgroup's flag of the phase before it:
+// wave 0 polls until done, the spin limit passed or the error word is raised.
+__device__ bool wait_flags(const uint32_t* flags, int nwg, uint32_t target, uint32_t* err, int* s_ok) {
+  if (threadIdx.x < 64) {
+    int good = 1;
+    long spins = 0;
+    while (!flags_reached(flags, nwg, target)) {
+      if ((++spins & 63) == 0 && (spins > kSpinLimit || ld4<true>(err, 0) != 0u)) {
+        good = 0;
+        break;
       }
     }
-    __syncthreads();
-    *ok = *s_ok != 0;
-    return *ok;
+    if (threadIdx.x == 0) {
+      *s_ok = good;
+      if (!good) st4<true>(err, 0, 1u);
+    }
   }
-};
+  __syncthreads();
+  return *s_ok != 0;
+}
 
 __device__ __forceinline__ void signal_epoch(uint32_t* flags, int wg, uint32_t epoch) {
   __builtin_amdgcn_s_waitcnt(0);        // this thread's stores have completed
@@ -86,48 +76,36 @@ typedef const __attribute__((address_space(4))) Phase* CPhasePtr;
 
 // the phase's parameters are read from the (read-only) table in the
 // constant address space, i.e. with scalar loads into wave-uniform registers
-template <int FMT, int NB, bool LDS, bool GLU, class W>
+template <int FMT, int NB, class W>
 __device__ __forceinline__ void run_variant(CPhasePtr ph, uint8_t* smem, int wg, int nwg, W& wait) {
-  gemv_run<FMT, NB, (NB >= 16), LDS, GLU, (LDS && FMT == M3_I8G128) ? 4 : 8, true>(
+  gemv_run<FMT, NB, (NB >= 16), true, kGluRuntime, FMT == M3_I8G128 ? 4 : 8, true>(
       *(const Params*)&ph->p, smem, wg, nwg, wait);
-}
-
-template <int FMT, int NB, int CLS, class W>
-__device__ __forceinline__ void run_class(CPhasePtr ph, uint8_t* smem, int wg, int nwg, int arm,
-                                          W& wait) {
-  if (arm == kArmLds) {
-    run_variant<FMT, NB, true, false>(ph, smem, wg, nwg, wait);
-  } else if (arm == kArmGlu) {
-    run_variant<FMT, NB, true, true>(ph, smem, wg, nwg, wait);
-  } else {
-    if constexpr (global_arm<NB>(CLS)) run_variant<FMT, NB, false, false>(ph, smem, wg, nwg, wait);
-  }
 }
 
 template <int NB, int FB>
 __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int nph, uint32_t* flags,
-                                                         uint32_t* err, const uint32_t* frame,
+                                                         uint32_t* err, const uint32_t* seq,
                                                          FeedbackArgs fb) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_ok;
   __shared__ int c_last[M3_MAX_B_FRAME];
   const int wg = blockIdx.x, nwg = gridDim.x;
-  const uint32_t ebase = __builtin_amdgcn_readfirstlane(ld4<true>(frame, 0)) * kPhaseStride;
+  // epochs of this launch: launch counter * 512 + phase + 1
+  const uint32_t ebase = __builtin_amdgcn_readfirstlane(ld4<true>(seq, 0)) * kPhaseStride;
   for (int i = 0; i < nph; ++i) {
     const int variant = __builtin_amdgcn_readfirstlane(ph[i].variant);
-    bool ok = true;
-    PhaseWait wait{flags, err, ebase + (uint32_t)i, nwg, i == 0, &s_ok, &ok};
     if (variant == kFeedbackVariant) {
-      if (wait.probe() || wait.wait()) feedback_run<true>(fb, wg, nwg, c_last);
+      if (!wait_flags(flags, nwg, ebase + (uint32_t)i, err, &s_ok)) return;
+      feedback_run<true>(fb, wg, nwg, c_last, ebase);
     } else {
+      TagWait wait{ebase, i, err};
       const CPhasePtr cp = (CPhasePtr)(ph + i);
-      if (variant < 4)
-        run_class<FB, NB, 0>(cp, smem, wg, nwg, variant, wait);
+      if (variant == 0)
+        run_variant<FB, NB>(cp, smem, wg, nwg, wait);
       else
-        run_class<M3_I8G128, NB, 1>(cp, smem, wg, nwg, variant - 4, wait);
+        run_variant<M3_I8G128, NB>(cp, smem, wg, nwg, wait);
     }
-    if (!ok) return;
-    signal_epoch(flags, wg, ebase + (uint32_t)i + 1u);
+    if (__builtin_amdgcn_readfirstlane(ph[i].signal)) signal_epoch(flags, wg, ebase + (uint32_t)i + 1u);
   }
 }
 

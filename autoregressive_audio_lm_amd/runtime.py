@@ -38,6 +38,12 @@ class DecodeModel:
     def __init__(self, md: dict, seed: int = 0, temperature: float = 1.0,
                  free_sources: bool = False):
         cfg = md["cfg"]
+        # the C side reads host arrays of these lengths from the config
+        nsteps = cfg["n_codebooks"] - 1
+        if (len(md["layers"]) != cfg["n_layers"] or len(md["d_layers"]) != cfg["d_layers"]
+                or len(md["heads"]) != nsteps or len(md["audio_emb"]) != nsteps
+                or len(md["emb"]) != max(nsteps - 1, 0)):
+            raise ValueError("model arrays do not match the config's layer and codebook counts")
         self.cfg_dict = cfg
         self.fmt_body, self.fmt_lm, self.fmt_depth = md["fmt_body"], md["fmt_lm"], md["fmt_depth"]
         self.config = make_config(cfg, self.fmt_body, self.fmt_lm, self.fmt_depth, seed, temperature)

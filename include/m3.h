@@ -233,7 +233,12 @@ typedef struct {
   size_t part_dep; /* per-row-block winners of the latest depth draw           */
   size_t flags;    /* u32  [256] per-workgroup progress of the persistent frame */
   size_t err;      /* u32  nonzero: a persistent frame gave up waiting          */
+  size_t seq;      /* u32  persistent launches so far                          */
   size_t phases;   /* the persistent frame's phase table                       */
+  size_t th, tqkv, tmlp, tu, thd, tdqkv, tdmlp;
+                   /* u32 words (bf16 value | 16-bit producer tag): the
+                      persistent frame's intermediate streams; h, qkv, mlp, u,
+                      hd, dqkv, dmlp above belong to the eager/graph frames   */
   size_t total;
 } m3_frame_layout;
 

@@ -86,11 +86,12 @@ def test_full_size_frame_within_rounding_envelope(preset, B):
     assert np.all((codes == o_codes)[sure])
 
 
-@pytest.mark.parametrize("preset,B", [("A", 1), ("A", 16), ("B", 6)])
+@pytest.mark.parametrize("preset,B", [("A", 1), ("A", 6), ("B", 2)])
 def test_full_size_persistent_equals_graph(preset, B):
-    """The persistent frame (one cooperative launch) and the graph-replayed
-    frame give identical bytes at the full model size, including the B = 16
-    shapes whose down projection reads its operand from global memory."""
+    """The persistent frame (one cooperative launch, tagged intermediate
+    streams) and the graph-replayed frame give identical bytes at the full
+    model size, up to B = 6, the largest row count whose down-projection
+    operand (K = 12288) is staged in LDS."""
     cfg = configs.config("frame-full")
     md = synth.make_model(cfg, **configs.PRESETS[preset], seed=17, device=DEV)
     dm = runtime.DecodeModel(md, seed=4, free_sources=True)
@@ -114,3 +115,15 @@ def test_full_size_persistent_equals_graph(preset, B):
             assert torch.equal(g.ring, p.ring)
     g.release()
     p.release()
+
+
+def test_full_size_persistent_refuses_unstaged_operands():
+    """At B = 16 the body down projection's operand does not fit LDS: the
+    persistent frame is refused (the graph-replayed frame serves it)."""
+    from autoregressive_audio_lm_amd import _lib
+    cfg = configs.config("frame-full", n_layers=1)
+    md = synth.make_model(cfg, **configs.PRESETS["A"], seed=17, device=DEV)
+    dm = runtime.DecodeModel(md, seed=4, free_sources=True)
+    st = runtime.FrameState(dm, 16, synth.activations(16, cfg["H"], 901, device=DEV))
+    with pytest.raises(_lib.M3ValueError):
+        st.persistent_create()
