@@ -6,9 +6,11 @@ Qwen3-8B-shaped body (per layer: RMSNorm+QKV, identity attention stub + O +
 residual, RMSNorm + gate/up + SwiGLU, down + residual), final RMSNorm + sliced
 lm_head over the 16384 reachable rows, Philox Gumbel-argmax draw, depth-decoder
 input projection, 7 codebook steps of the 4-layer depth decoder (int8 groups
-of 128) each with its head and draw, and the frame-embedding feedback.  The
-frame is replayed as a HIP graph; weights are seeded synthetic values already
-resident in HBM.
+of 128) each with its head and draw, and the frame-embedding feedback.
+Weights are seeded synthetic values already resident in HBM.  Both frame paths
+of the library are timed on the same state shape -- a replayed HIP graph of
+one kernel per GEMV, and one cooperative persistent launch per frame -- and
+the faster one is the reported value (its name is in config.path).
 
 value = algorithmic weight bytes per frame x frames/s (GB/s).  The headline
 workload is preset A (bf16 body and lm_head, int8-g128 depth) at B = 1.
@@ -29,10 +31,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode weight-stream GB/s (% of HBM peak) and frames/s at B=1/6/16"
 HBM_PEAK_GBS = 8000.0
-# Counter-derived HBM bytes of the dominant kernel; valid only for the kernel
-# sources it was measured on (their sha256 is recorded beside the figures).
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_gate_up_bf16_B1.txt")
-KERNEL_SOURCES = ("gemv.hip", "m3_internal.h", "m3_sampling.h")
+# Counter-derived HBM bytes of a kernel; valid only for the kernel sources it
+# was measured on (their sha256 is recorded beside the figures).
+TRAFFIC = {
+    "frame": (os.path.join(ROOT, "profiles", "traffic_frame_kernel_presetA_B1.txt"),
+              ("gemv_impl.h", "frame_impl.h", "persist_kernel.h", "persist_bf16.hip",
+               "m3_internal.h", "m3_sampling.h")),
+    "gate_up": (os.path.join(ROOT, "profiles", "traffic_gemv_gate_up_bf16_B1.txt"),
+                ("gemv_impl.h", "gemv.hip", "m3_internal.h", "m3_sampling.h")),
+}
+TRAFFIC_FILE = TRAFFIC["gate_up"][0]
+
+
+def m3nb(B: int) -> int:
+    """Rows per accumulator tile the kernels use for B rows."""
+    return 1 if B <= 1 else 2 if B <= 2 else 4 if B <= 4 else (B + 15) // 16 * 16
 
 
 def log(*a):
@@ -85,8 +98,10 @@ def time_frames(dm, cfg, B, steps, warmup, stream, seed=0):
     return st, ms, wall
 
 
-def time_frames_persistent(dm, cfg, B, steps, warmup, stream, seed=0):
-    """Frames as one cooperative launch each; HIP events on the launch stream."""
+def time_frames_persistent(dm, cfg, B, steps, warmup, stream, seed=0, per_launch=False):
+    """Frames as one cooperative launch each; HIP events on the launch stream.
+    per_launch: also time every launch alone (event pair around it) and
+    return the mean kernel duration in ms."""
     import torch
     from autoregressive_audio_lm_amd import runtime, synth
     x0 = synth.activations(B, cfg["H"], 1000 + seed, device="cuda")
@@ -107,9 +122,21 @@ def time_frames_persistent(dm, cfg, B, steps, warmup, stream, seed=0):
         stream.synchronize()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
+        kernel_ms = None
+        if per_launch:
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(min(steps, 50))]
+            for a, b in pairs:
+                a.record(stream)
+                st.persistent_launch(stream)
+                b.record(stream)
+            stream.synchronize()
+            kernel_ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
     if int(st.err.item()) != 0:
         raise RuntimeError("a persistent frame gave up waiting")
     ms = e0.elapsed_time(e1) / steps
+    if per_launch:
+        return st, ms, wall, kernel_ms
     return st, ms, wall
 
 
@@ -149,28 +176,29 @@ def time_gate_up(dm, st, stream, reps=3):
     return us, wbytes + 4 * H, n
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(which: str = "gate_up") -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in TRAFFIC[which][1]:
         with open(os.path.join(ROOT, "autoregressive_audio_lm_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the body gate/up GEMV from the committed
-    FETCH_SIZE/WRITE_SIZE passes, or None when the kernel sources changed
-    since those counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(which: str = "gate_up"):
+    """HBM bytes per launch of a kernel from the committed FETCH_SIZE /
+    WRITE_SIZE passes, or None when its sources changed since those counters
+    were taken."""
+    path = TRAFFIC[which][0]
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != kernel_source_hash():
+    if kv.get("source_sha256") != kernel_source_hash(which):
         return None
     try:
         return int(kv["traffic_bytes_per_launch"])
@@ -239,7 +267,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the B = 2/6/16 and int8 context points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 256 MiB elementwise copy (counter calibration runs)")
     args = ap.parse_args()
@@ -261,48 +289,87 @@ def main():
 
     cfg, dm, L0 = build_model(args.preset, args.seed, dev, keep_layer0=not args.no_cpu_baseline)
     fbytes = dm.weight_bytes()
-    st, ms, wall = time_frames(dm, cfg, args.B, args.steps, args.warmup, stream, args.seed)
+
+    def best_frame(dm_, B, steps, warmup, per_launch=False):
+        """Both frame paths on the same state shape; the faster one wins."""
+        out = {}
+        s_g, ms_g, wall_g = time_frames(dm_, cfg, B, steps, warmup, stream, args.seed)
+        out["graph"] = {"ms": ms_g, "wall": wall_g, "state": s_g}
+        try:
+            r = time_frames_persistent(dm_, cfg, B, steps, warmup, stream, args.seed,
+                                       per_launch=per_launch)
+            out["persistent"] = {"ms": r[1], "wall": r[2], "state": r[0],
+                                 "kernel_ms": r[3] if per_launch else None}
+        except _lib.M3ValueError:
+            pass      # the persistent frame does not take this shape
+        best = min(out, key=lambda k: out[k]["ms"])
+        return best, out
+
+    path, res = best_frame(dm, args.B, args.steps, args.warmup, per_launch=True)
+    ms, wall = res[path]["ms"], res[path]["wall"]
     fps = 1e3 / ms
     gbs = fbytes * fps / 1e9
-    log(f"[bench] preset {args.preset} B={args.B}: {ms:.4f} ms/frame, {fps:.1f} frames/s, "
-        f"{gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); wall {wall:.3f} s")
+    for k, v in res.items():
+        log(f"[bench] preset {args.preset} B={args.B} {k}: {v['ms']:.4f} ms/frame, "
+            f"{fbytes / v['ms'] / 1e6:.1f} GB/s")
+    log(f"[bench] -> {path}: {fps:.1f} frames/s, {gbs:.1f} GB/s "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); wall {wall:.3f} s")
 
+    st = res["graph"]["state"]
     us, kbytes, n = time_gate_up(dm, st, stream)
     k_gbs = kbytes / (us * 1e-6) / 1e9
     log(f"[bench] gate/up GEMV: {us:.2f} us per launch over {n} launches, {k_gbs:.1f} GB/s")
-    traffic = measured_traffic() if (args.preset == "A" and args.B == 1) else None
-    roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "gemv_kernel<bf16, VALU, SwiGLU> (body gate/up, RMSNorm fused)"
-                          if dm.fmt_body == 0 else "gemv_kernel<int8, SwiGLU> (body gate/up)",
-                "avg_us": round(us, 3), "bytes_per_launch": kbytes}
-    st.release()
+    gate_up = {"kernel": "gemv_kernel<bf16, VALU, SwiGLU> (body gate/up, RMSNorm fused)"
+                         if dm.fmt_body == 0 else "gemv_kernel<int8, SwiGLU> (body gate/up)",
+               "avg_us": round(us, 3), "bytes_per_launch": kbytes, "GB_s": round(k_gbs, 1),
+               "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+               "traffic": measured_traffic("gate_up") if (args.preset == "A" and args.B == 1) else None}
+    if path == "persistent":
+        kus = res[path]["kernel_ms"] * 1e3
+        ach = fbytes / (kus * 1e-6) / 1e9
+        log(f"[bench] frame kernel: {kus:.1f} us per launch, {ach:.1f} GB/s")
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("frame") if (args.preset == "A" and args.B == 1) else None,
+                    "kernel": f"frame_kernel<{m3nb(args.B)}, {'bf16' if dm.fmt_body == 0 else 'i8row'}> "
+                              "(the whole frame, one cooperative launch)",
+                    "avg_us": round(kus, 2), "bytes_per_launch": fbytes, "gate_up_gemv": gate_up}
+    else:
+        roofline = {"bound": "hbm", "achieved": gate_up["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gate_up["frac"], "traffic": gate_up["traffic"], "kernel": gate_up["kernel"],
+                    "avg_us": gate_up["avg_us"], "bytes_per_launch": kbytes}
+    paths_ms = {k: round(v["ms"], 4) for k, v in res.items()}
+    for v in res.values():
+        v["state"].release()
+    del res, st
     if args.calib_copy:
         calib_copy(stream)
+
+    def point(preset, B, dm_, fb):
+        p_, r_ = best_frame(dm_, B, max(20, args.steps // 4), 3)
+        m = r_[p_]["ms"]
+        for v in r_.values():
+            v["state"].release()
+        pt = {"preset": preset, "B": B, "path": p_, "ms_per_frame": round(m, 4),
+              "frames_per_s": round(1e3 / m, 2), "GB_s": round(fb * 1e3 / m / 1e9, 1),
+              "frac_of_hbm_peak": round(fb * 1e3 / m / 1e9 / HBM_PEAK_GBS, 4),
+              "ms_by_path": {k: round(v["ms"], 4) for k, v in r_.items()}}
+        if fb != fbytes:
+            pt["bytes_per_frame"] = fb
+        log(f"[bench] sweep {pt}")
+        return pt
 
     sweep = []
     if not args.no_sweep:
         for B in (2, 6, 16):
-            s2, ms2, _ = time_frames(dm, cfg, B, max(20, args.steps // 4), 3, stream, args.seed)
-            s2.release()
-            sweep.append({"preset": args.preset, "B": B, "ms_per_frame": round(ms2, 4),
-                          "frames_per_s": round(1e3 / ms2, 2),
-                          "GB_s": round(fbytes * 1e3 / ms2 / 1e9, 1),
-                          "frac_of_hbm_peak": round(fbytes * 1e3 / ms2 / 1e9 / HBM_PEAK_GBS, 4)})
-            log(f"[bench] sweep {sweep[-1]}")
+            sweep.append(point(args.preset, B, dm, fbytes))
         other = "B" if args.preset == "A" else "A"
-        del st, dm
+        del dm
         torch.cuda.empty_cache()
         _, dm2, _ = build_model(other, args.seed, dev)
         fb2 = dm2.weight_bytes()
         for B in (1, 6, 16):
-            s2, ms2, _ = time_frames(dm2, cfg, B, max(20, args.steps // 4), 3, stream, args.seed)
-            s2.release()
-            sweep.append({"preset": other, "B": B, "bytes_per_frame": fb2,
-                          "ms_per_frame": round(ms2, 4), "frames_per_s": round(1e3 / ms2, 2),
-                          "GB_s": round(fb2 * 1e3 / ms2 / 1e9, 1),
-                          "frac_of_hbm_peak": round(fb2 * 1e3 / ms2 / 1e9 / HBM_PEAK_GBS, 4)})
-            log(f"[bench] sweep {sweep[-1]}")
+            sweep.append(point(other, B, dm2, fb2))
         del dm2
         torch.cuda.empty_cache()
 
@@ -335,7 +402,9 @@ def main():
                          f"attention stubbed as identity"),
             "B": args.B,
             "bytes_per_frame": fbytes,
-            "graph": "one HIP graph per frame, replayed",
+            "path": ("one cooperative persistent launch per frame" if path == "persistent"
+                     else "one HIP graph per frame, replayed"),
+            "ms_by_path": paths_ms,
         },
         "frames_per_s": round(fps, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),

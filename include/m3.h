@@ -279,19 +279,27 @@ int m3_frame_graph_destroy(void* graph);
 /* Persistent form of the frame: the same steps, with the same results, run as
  * ONE cooperative launch per frame.  One workgroup per compute unit walks the
  * frame's GEMVs in order; each workgroup requests the first weight tiles of
- * the next GEMV before it waits for the previous GEMV's outputs (published
- * through per-workgroup flags in the state), so HBM keeps streaming across the
- * ~270 dependencies of a frame (TensorFold PR #987: one submission per frame;
+ * the next GEMV before it waits for the previous GEMV's outputs, so HBM keeps
+ * streaming across the ~270 dependencies of a frame (TensorFold PR #987: one submission per frame;
  * "MiniMax Music 3, local": the AR stages are bound by memory bandwidth).
  * create records the frame into the state's phase table (it synchronises
  * `stream` once); launch enqueues one frame; the handle keeps the model's and
  * the state's device addresses.  Every wait inside the launch is bounded: if
  * one gives up (the launch could not make progress), the state's err word
  * becomes nonzero, the launch ends early and that frame's outputs are invalid.
- * The frame state must have been initialised with m3_frame_state_init; eager,
- * graph and persistent frames may be interleaved on one state.  The launch
- * fails with M3_ERR_HIP if the device cannot hold one workgroup per compute
- * unit at once. */
+ * Inside the launch the intermediate streams (body and depth residuals, QKV,
+ * MLP, depth input) are the state's tagged buffers: 32-bit words holding the
+ * bf16 value and the tag of the step that wrote it; a step waits for its
+ * operand by reading it until the tags are the ones its producer writes (one
+ * store and one load per dependency, no barrier).  x, h, logits, codes, the
+ * ring and the frame counter are updated exactly as by the other paths, with
+ * the same bytes.  Supported: bf16 or int8-row body with the same lm_head
+ * format and an int8-g128 depth decoder (else M3_ERR_FORMAT), every GEMV
+ * operand staged in LDS (at the full model: B <= 6; else M3_ERR_SHAPE), vocab
+ * slice and code vocabulary below 65536.  The frame state must have been
+ * initialised with m3_frame_state_init; eager, graph and persistent frames may
+ * be interleaved on one state.  The launch fails with M3_ERR_HIP if the device
+ * cannot hold one workgroup per compute unit at once. */
 int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_t* codes,
                                void* stream, void** handle_out /* host */);
 int m3_frame_persistent_launch(void* handle, void* stream);

@@ -15,18 +15,19 @@ def test_multi_gpu_request_exits_with_message():
     assert "one MI355X" in r.stderr and r.stdout == ""
 
 
-def test_traffic_record_is_tied_to_the_kernel_sources():
+def test_traffic_records_are_tied_to_the_kernel_sources():
     import bench
-    rec = {}
-    with open(bench.TRAFFIC_FILE) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                rec[k.strip()] = v.strip()
-    assert int(rec["traffic_bytes_per_launch"]) == (int(rec["fetch_bytes_per_launch"])
-                                                     + int(rec["write_bytes_per_launch"]))
-    # the figure is reported only while the sources match the ones it was measured on
-    if rec["source_sha256"] == bench.kernel_source_hash():
-        assert bench.measured_traffic() == int(rec["traffic_bytes_per_launch"])
-    else:
-        assert bench.measured_traffic() is None
+    for which, (path, _) in bench.TRAFFIC.items():
+        rec = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    rec[k.strip()] = v.strip()
+        assert int(rec["traffic_bytes_per_launch"]) == (int(rec["fetch_bytes_per_launch"])
+                                                         + int(rec["write_bytes_per_launch"]))
+        # the figure is reported only while the sources match the ones it was measured on
+        if rec["source_sha256"] == bench.kernel_source_hash(which):
+            assert bench.measured_traffic(which) == int(rec["traffic_bytes_per_launch"])
+        else:
+            assert bench.measured_traffic(which) is None
