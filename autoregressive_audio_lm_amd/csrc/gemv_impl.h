@@ -25,11 +25,11 @@
 //    workgroup in LDS (row stride padded by 16 B against bank conflicts) and
 //    re-used for every tile; workgroups loop over row blocks when there are
 //    more blocks than resident workgroups.
-//  * Few rows (B <= 4): VALU path, v_dot2_f32_bf16 on bf16 pairs; lane l holds
+//  * Few rows (B <= 2): VALU path, v_dot2_f32_bf16 on bf16 pairs; lane l holds
 //    row l%16 and one 16-byte K-chunk of each tile, partial sums meet with two
-//    cross-lane exchanges.  B >= 5: the product is a dense contraction and
-//    goes to v_mfma_f32_16x16x32_bf16 (A = 16 activation rows, B = the
-//    weight tile, exactly the packed lane layout).
+//    cross-lane exchanges.  B >= 3: the product goes to
+//    v_mfma_f32_16x16x32_bf16 (A = 16 activation rows, B = the weight tile,
+//    exactly the packed lane layout).
 //  * int8 is dequantised to bf16 exactly (|q| <= 127 has 7 significant bits)
 //    with one SDWA sign-extending convert per byte; scales are applied per row
 //    (i8row) or per group of 128 along K (i8g128).
@@ -518,9 +518,33 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
   }
 }
 
+// One launch per GEMV, more than two rows: the first group of the copy pass
+// (kStageUnroll chunks per thread), requested ahead of the weight stream.
+struct XGroup {
+  uint4 v[kStageUnroll];
+  bool valid;
+};
+
+template <bool COH>
+__device__ __forceinline__ void prefetch_group(const Params& p, XGroup& g, const Tags& tg) {
+  const int tid = threadIdx.x;
+  const int cpr = (p.lds_stride - 8) >> 3;
+  const int total = p.lds_rows * cpr;
+#pragma unroll
+  for (int u = 0; u < kStageUnroll; ++u) {
+    const int it = tid + u * kThreads;
+    const int b = it / cpr, k = (it - b * cpr) * 8;
+    const bool in = it < total && k < p.K;
+    g.v[u] = make_uint4(0, 0, 0, 0);
+    if (in) g.v[u] = load_x8<COH>(p, b, k, tg);
+  }
+  g.valid = true;
+}
+
 template <bool COH>
 __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf,
                                                   int* code_lds, int wg, const XPre& pre,
+                                                  const XGroup& grp,
                                                   const Tags& tg) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int stride = p.lds_stride;
@@ -536,14 +560,22 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
   for (int base = tid; base < total; base += kThreads * kStageUnroll) {
     uint4 v[kStageUnroll];
     bool ok[kStageUnroll];
+    if (!COH && grp.valid && base == tid) {
 #pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int it = base + u * kThreads;
-      const int b = it / cpr, k = (it - b * cpr) * 8;
-      const bool in = it < total && k < p.K;
-      const uint4 x = src.attempt(in ? b : 0, in ? k : 0, ok[u]);
-      v[u] = in ? x : make_uint4(0, 0, 0, 0);
-      ok[u] = ok[u] || !in;
+      for (int u = 0; u < kStageUnroll; ++u) {
+        v[u] = grp.v[u];
+        ok[u] = true;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int it = base + u * kThreads;
+        const int b = it / cpr, k = (it - b * cpr) * 8;
+        const bool in = it < total && k < p.K;
+        const uint4 x = src.attempt(in ? b : 0, in ? k : 0, ok[u]);
+        v[u] = in ? x : make_uint4(0, 0, 0, 0);
+        ok[u] = ok[u] || !in;
+      }
     }
     if constexpr (COH) {
 #pragma unroll
@@ -996,11 +1028,18 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   float scA[kU / 2], scB[kU / 2];
   XPre pre;
   pre.valid = false;
+  XGroup grp;
+  grp.valid = false;
   const bool ready = wt.probe();
   if (ready) {
     // (persistent launches: only phase 0, whose operand is plain; not worth the registers)
     if constexpr (LDS && !COH) {
-      if (p.lds_rows <= 2 && !p.has_gather && nitems > 0) prefetch_x<COH>(p, pre, tg);
+      if (!p.has_gather && nitems > 0) {
+        if (p.lds_rows <= 2)
+          prefetch_x<COH>(p, pre, tg);
+        else
+          prefetch_group<COH>(p, grp, tg);
+      }
     }
     load(bufA, scA, 0);
   } else {
@@ -1009,7 +1048,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
     if (!wt.wait()) return;
   }
   if (nitems == 0) return;
-  if (LDS) stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre, tg);
+  if (LDS) stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre, grp, tg);
   if (ready) load(bufB, scB, 1);
   __builtin_amdgcn_sched_barrier(0);
   // the scheduling barriers keep each batch's loads ahead of the next batch's
@@ -1037,12 +1076,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Host-side helpers shared by the launch paths.
 // ---------------------------------------------------------------------------
-// Rows per accumulator tile: up to 4 rows on the VALU (dot2), from 5 rows on
-// the MFMA path in tiles of 16 (rows past B repeat row B-1 and are not stored).
+// Rows per accumulator tile: one or two rows on the VALU (dot2), from three
+// rows on the MFMA path in tiles of 16 (rows past B repeat row B-1 and are not
+// stored; measured, a 16-row MFMA tile beats a 4-row VALU tile already at 3).
 inline int nb_of(int B) {
   if (B <= 1) return 1;
   if (B <= 2) return 2;
-  if (B <= 4) return 4;
   return (B + 15) / 16 * 16;
 }
 

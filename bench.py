@@ -45,7 +45,7 @@ TRAFFIC_FILE = TRAFFIC["gate_up"][0]
 
 def m3nb(B: int) -> int:
     """Rows per accumulator tile the kernels use for B rows."""
-    return 1 if B <= 1 else 2 if B <= 2 else 4 if B <= 4 else (B + 15) // 16 * 16
+    return 1 if B <= 1 else 2 if B <= 2 else (B + 15) // 16 * 16
 
 
 def log(*a):
