@@ -125,6 +125,8 @@ def _declare(L):
                              ctypes.c_uint32, ctypes.c_uint32]
     L.m3o_gumbel_argmax.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.POINTER(SampleParams), _P, _P, _P]
+    L.m3o_cfg_topk_draw.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_float, ctypes.c_int, ctypes.POINTER(SampleParams), _P, _P]
     L.m3o_decode_frame.argtypes = [ctypes.POINTER(Model), _P, ctypes.c_int, ctypes.c_uint64,
                                    ctypes.c_uint32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(FrameTrace)]
@@ -296,6 +298,28 @@ def gumbel_argmax(logits, seed=0, frame=0, draw=0, temperature=1.0, index_base=0
     lib().m3o_gumbel_argmax(_ptr(lg), B, V, V, ctypes.byref(p), _ptr(out), _ptr(zb), _ptr(z2))
     if with_margin:
         return out, zb, z2
+    return out
+
+
+def cfg_topk_draw(logits, scale=1.5, top_k=50, seed=0, frame=0, draw=0, temperature=1.0,
+                  index_base=0, ids=None, valid=(0, 0), noise=None, with_kept=False):
+    """The reference's draw over (conditional, unconditional) row pairs;
+    logits [2S, V] -> ids [2S] (both rows of a song carry its draw)."""
+    lg = _c(logits, np.float32)
+    B, V = lg.shape
+    if B % 2:
+        raise ValueError("rows come in (conditional, unconditional) pairs")
+    S = B // 2
+    ids_a = None if ids is None else _c(ids, np.int32)
+    nz = None if noise is None else _c(noise, np.float32)
+    p = SampleParams(int(seed), int(frame), int(draw), float(temperature), int(index_base),
+                     _ptr(ids_a), int(valid[0]), int(valid[1]), _ptr(nz))
+    out = np.empty(B, np.int32)
+    kept = np.empty(S, np.int32)
+    lib().m3o_cfg_topk_draw(_ptr(lg), S, V, V, float(scale), int(top_k), ctypes.byref(p),
+                            _ptr(out), _ptr(kept))
+    if with_kept:
+        return out, kept
     return out
 
 

@@ -336,6 +336,80 @@ void m3o_gumbel_argmax(const float* logits, int B, int V, int ldl,
 }
 
 /* ------------------------------------------------------------------ */
+/* The reference's own draw ([ds] stage 2: classifier-free guidance     */
+/* with scale 1.5 over the conditional and unconditional rows, a top-k  */
+/* filter with k = 50, then multinomial sampling; [metal] "What it      */
+/* adds": the CFG top-k draw on the same Philox counters).              */
+/*                                                                      */
+/* Song s owns rows 2s (conditional, c) and 2s+1 (unconditional, u).    */
+/*  1. guided g_j = u_j + fl32(scale * fl32(c_j - u_j)), three IEEE     */
+/*     fp32 operations in this order; ids outside [valid_lo, valid_hi)  */
+/*     and NaN guided values take no part;                              */
+/*  2. the survivors are the k candidates with the largest g, ties      */
+/*     to the lower column (all candidates when fewer than k);          */
+/*  3. the multinomial draw from softmax(g/T) over the survivors is     */
+/*     taken as Gumbel-argmax over them ([hf] item 3: the same law),    */
+/*     z = fl32(g * fl32(1/T)) + G(seed, s, frame, draw, id), the       */
+/*     highest z winning, ties to the lower column;                     */
+/*  4. the drawn id is written to both rows of the song.                */
+/* A song without candidates draws its first column's id.               */
+/* ------------------------------------------------------------------ */
+typedef struct { float g; int j; } m3o_cand;
+
+static int cand_order(const void* a, const void* b) {
+  const m3o_cand* x = (const m3o_cand*)a;
+  const m3o_cand* y = (const m3o_cand*)b;
+  if (x->g > y->g) return -1;
+  if (x->g < y->g) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, int top_k,
+                       const m3o_sample_params* p, int32_t* out, int32_t* n_kept) {
+  float invT = 1.0f / p->temperature;
+  m3o_cand* cand = (m3o_cand*)malloc((size_t)V * sizeof *cand);
+  for (int s = 0; s < S; ++s) {
+    const float* c = logits + (size_t)(2 * s) * ldl;
+    const float* u = logits + (size_t)(2 * s + 1) * ldl;
+    int n = 0;
+    for (int j = 0; j < V; ++j) {
+      int32_t id = p->ids ? p->ids[j] : p->index_base + j;
+      if (p->valid_lo < p->valid_hi && (id < p->valid_lo || id >= p->valid_hi)) continue;
+      float d = c[j] - u[j];
+      float sd = scale * d;
+      float g = u[j] + sd;
+      if (isnan(g)) continue;
+      cand[n].g = g;
+      cand[n].j = j;
+      ++n;
+    }
+    int keep = n < top_k ? n : top_k;
+    int best = -1;
+    float zb = 0.0f;
+    if (keep > 0) qsort(cand, (size_t)n, sizeof *cand, cand_order);
+    for (int r = 0; r < keep; ++r) {
+      int j = cand[r].j;
+      int32_t id = p->ids ? p->ids[j] : p->index_base + j;
+      float g = p->noise_override ? p->noise_override[(size_t)s * V + j]
+                                  : m3o_gumbel(p->seed, (uint32_t)s, p->frame, p->draw,
+                                               (uint32_t)id);
+      float lt = cand[r].g * invT;
+      float z = lt + g;
+      if (best < 0 || z > zb || (z == zb && j < best)) {
+        best = j;
+        zb = z;
+      }
+    }
+    if (best < 0) best = 0;
+    int32_t id = p->ids ? p->ids[best] : p->index_base + best;
+    out[2 * s] = id;
+    out[2 * s + 1] = id;
+    if (n_kept) n_kept[s] = keep;
+  }
+  free(cand);
+}
+
+/* ------------------------------------------------------------------ */
 /* One frame ([ds] stage 2; [metal] frame bookkeeping).                 */
 /* ------------------------------------------------------------------ */
 static void run_layer(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads,

@@ -91,6 +91,12 @@ typedef struct {
 void m3o_gumbel_argmax(const float* logits, int B, int V, int ldl,
                        const m3o_sample_params* p, int32_t* out,
                        float* zbest, float* zsecond);
+/* CFG + top-k draw over song pairs (rows 2s conditional, 2s+1
+   unconditional): guided g = u + scale (c - u), the top_k largest g (ties to
+   the lower column), Gumbel-argmax over them with counter row s; out[2s] =
+   out[2s+1] = the drawn id.  n_kept (optional [S]) receives the survivor count. */
+void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, int top_k,
+                       const m3o_sample_params* p, int32_t* out, int32_t* n_kept);
 
 /* ---- one decode frame ------------------------------------------------ */
 typedef struct {

@@ -1,0 +1,153 @@
+"""Pins of the oracle's CFG + top-k draw (DiffSynth-Studio MiniMax-Music3
+article, stage 2: guidance u + 1.5 (c - u) over the conditional and
+unconditional rows, top-k 50, multinomial sampling; TensorFold PR #987 "What
+it adds": the CFG top-k draw on the same Philox counters).
+
+Pinned by: a closed form of the guidance on integer logits (k = 1 makes the
+draw the guided argmax), the sampling law over the survivors (softmax of the
+top-k guided logits, L1 <= 0.02 over 200k draws, non-survivors never drawn),
+the reduction to the plain Gumbel-argmax draw when k covers every candidate,
+tie order at the top-k boundary, masking, NaN and empty songs.  CPU only."""
+import numpy as np
+import pytest
+
+
+def _pairs(c, u):
+    """Interleave conditional rows c [S, V] and unconditional rows u [S, V]."""
+    S, V = c.shape
+    L = np.empty((2 * S, V), np.float32)
+    L[0::2] = c
+    L[1::2] = u
+    return L
+
+
+def test_k1_is_the_guided_argmax_closed_form(oracle):
+    """Integer logits make every guidance step exact: g = 1.5 c - 0.5 u, and
+    with k = 1 the only survivor is the lowest column of the largest g,
+    whatever the noise."""
+    rng = np.random.default_rng(40)
+    S, V = 64, 37
+    c = rng.integers(-8, 9, (S, V)).astype(np.float32)
+    u = rng.integers(-8, 9, (S, V)).astype(np.float32)
+    g = 1.5 * c.astype(np.float64) - 0.5 * u.astype(np.float64)
+    want = 500 + np.argmax(g, axis=1)             # first maximal column
+    for f in range(4):
+        out = oracle.cfg_topk_draw(_pairs(c, u), scale=1.5, top_k=1, seed=f, frame=f,
+                                   index_base=500)
+        assert np.array_equal(out[0::2], want) and np.array_equal(out[1::2], want)
+    # swapping the two rows of a pair is not the same guidance
+    swapped = oracle.cfg_topk_draw(_pairs(u, c), scale=1.5, top_k=1, index_base=500)
+    g2 = 1.5 * u.astype(np.float64) - 0.5 * c.astype(np.float64)
+    assert np.array_equal(swapped[0::2], 500 + np.argmax(g2, axis=1))
+
+
+@pytest.mark.parametrize("T,k", [(1.0, 5), (0.8, 3)])
+def test_law_is_softmax_over_the_top_k(oracle, T, k):
+    """200k draws: the frequencies match softmax(g/T) restricted to the k
+    largest guided logits (L1 <= 0.02); other ids are never drawn."""
+    V = 16
+    # the first seed whose guidance changes which ids survive (else the test
+    # would not see the guidance)
+    for seed in range(41, 100):
+        rng = np.random.default_rng(seed)
+        c = (rng.standard_normal(V) * 1.2).astype(np.float32)
+        u = (rng.standard_normal(V) * 1.2).astype(np.float32)
+        g = u.astype(np.float64) + 1.5 * (c.astype(np.float64) - u.astype(np.float64))
+        top = np.argsort(-g, kind="stable")[:k]
+        if set(top) != set(np.argsort(-c, kind="stable")[:k]):
+            break
+    else:
+        raise AssertionError("no seed separates the guided top-k from the conditional one")
+    S, frames = 1000, 200
+    L = _pairs(np.repeat(c[None], S, 0), np.repeat(u[None], S, 0))
+    counts = np.zeros(V)
+    for f in range(frames):
+        out = oracle.cfg_topk_draw(L, scale=1.5, top_k=k, seed=77, frame=f, temperature=T)
+        assert np.array_equal(out[0::2], out[1::2])
+        counts += np.bincount(out[0::2], minlength=V)
+    p = np.zeros(V)
+    e = np.exp((g[top] - g[top].max()) / T)
+    p[top] = e / e.sum()
+    assert np.all(counts[p == 0] == 0)
+    l1 = np.abs(counts / counts.sum() - p).sum()
+    assert l1 <= 0.02, l1
+
+
+def test_k_covering_every_candidate_is_the_plain_draw(oracle):
+    """With k >= the candidate count nothing is filtered: the draw is the
+    plain Gumbel-argmax of the guided logits with counter row = song."""
+    rng = np.random.default_rng(42)
+    S, V = 12, 300
+    c = rng.standard_normal((S, V)).astype(np.float32)
+    u = rng.standard_normal((S, V)).astype(np.float32)
+    # guided logits by plain fp32 numpy arithmetic, one rounding per step
+    g = u + np.float32(1.5) * (c - u)
+    for f in range(6):
+        out = oracle.cfg_topk_draw(_pairs(c, u), scale=1.5, top_k=V, seed=9, frame=f, draw=3,
+                                   temperature=0.9, index_base=1000)
+        ref = oracle.gumbel_argmax(g, seed=9, frame=f, draw=3, temperature=0.9, index_base=1000)
+        assert np.array_equal(out[0::2], ref) and np.array_equal(out[1::2], ref)
+        # with a mask: k at least the number of unmasked ids
+        out = oracle.cfg_topk_draw(_pairs(c, u), scale=1.5, top_k=40, seed=9, frame=f,
+                                   index_base=1000, valid=(1100, 1140))
+        ref = oracle.gumbel_argmax(g, seed=9, frame=f, index_base=1000, valid=(1100, 1140))
+        assert np.array_equal(out[0::2], ref)
+
+
+def test_ties_at_the_boundary_keep_lower_columns(oracle):
+    V = 10
+    noise = np.zeros((3, V), np.float32)
+    # song 0: all guided values equal, k = 3 -> columns 0..2 survive; the
+    # largest noise among them (column 1) wins, not the global one (column 7)
+    c0 = np.zeros(V, np.float32)
+    noise[0] = [0.1, 0.5, 0.2, 0, 0, 0, 0, 9.0, 0, 0]
+    # song 1: g = [5, 4, 4, 4, 3, ...], k = 2 -> columns 0 and 1 survive
+    c1 = np.array([5, 4, 4, 4, 3, 3, 3, 3, 3, 3], np.float32)
+    noise[1] = [0, 2.0, 8.0, 8.0, 0, 0, 0, 0, 0, 0]
+    # song 2: equal z among survivors -> the lower column
+    c2 = np.array([1, 2, 2, 0, 0, 0, 0, 0, 0, 0], np.float32)
+    c = np.stack([c0, c1, c2])
+    out, kept = oracle.cfg_topk_draw(_pairs(c, c), top_k=3, noise=noise, with_kept=True)
+    assert kept.tolist() == [3, 3, 3]
+    assert out[0] == 1
+    assert out[4] == 1                 # song 2: columns 1 and 2 tie at z = 2
+    out = oracle.cfg_topk_draw(_pairs(c, c), top_k=2, noise=noise)
+    assert out[0] == 1 and out[2] == 1 and out[4] == 1
+
+
+def test_mask_nan_and_empty_songs(oracle):
+    rng = np.random.default_rng(43)
+    S, V = 8, 64
+    c = rng.standard_normal((S, V)).astype(np.float32)
+    u = rng.standard_normal((S, V)).astype(np.float32)
+    c[:, 5] = 50.0                     # the best guided id lies outside the mask
+    for f in range(20):
+        out, kept = oracle.cfg_topk_draw(_pairs(c, u), top_k=50, seed=2, frame=f,
+                                         index_base=100, valid=(120, 140), with_kept=True)
+        assert np.all((out >= 120) & (out < 140))
+        assert np.all(kept == 20)
+    # NaN guidance (inf - inf) takes no part; a song with nothing left draws its first id
+    c2 = np.zeros((2, 4), np.float32)
+    u2 = np.zeros((2, 4), np.float32)
+    c2[0, 2] = u2[0, 2] = np.inf       # NaN guided value at column 2
+    c2[0, 3] = 1.0
+    c2[1, :] = u2[1, :] = np.inf       # every column NaN
+    out, kept = oracle.cfg_topk_draw(_pairs(c2, u2), top_k=1, index_base=7, with_kept=True)
+    assert out.tolist() == [10, 10, 7, 7]
+    assert kept.tolist() == [1, 0]
+    out = oracle.cfg_topk_draw(np.zeros((2, 4), np.float32), top_k=2, index_base=7,
+                               valid=(100, 200))
+    assert out.tolist() == [7, 7]
+
+
+def test_sliced_equals_masked_full(oracle):
+    rng = np.random.default_rng(44)
+    S, Vfull, base, V0 = 4, 2000, 1500, 320
+    c = rng.standard_normal((S, Vfull)).astype(np.float32)
+    u = rng.standard_normal((S, Vfull)).astype(np.float32)
+    full = _pairs(c, u)
+    sl = np.ascontiguousarray(full[:, base:base + V0])
+    for f in range(10):
+        a = oracle.cfg_topk_draw(full, top_k=50, seed=4, frame=f, valid=(base, base + V0))
+        b = oracle.cfg_topk_draw(sl, top_k=50, seed=4, frame=f, index_base=base)
+        assert np.array_equal(a, b)
