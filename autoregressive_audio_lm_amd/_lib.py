@@ -81,6 +81,7 @@ _SIGS = {
     "m3_lmhead_sliced": (_I, [_I, _P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _P, _I, _P]),
     "m3_gumbel_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "m3_gumbel_argmax": (_I, [_P, _I, _I, _I, ctypes.POINTER(SampleParams), _P, _P, ctypes.c_size_t, _P]),
+    "m3_cfg_topk_draw": (_I, [_P, _I, _I, _I, ctypes.c_float, _I, ctypes.POINTER(SampleParams), _P, _P]),
     "m3_frame_weight_bytes": (ctypes.c_uint64, [ctypes.POINTER(Config)]),
     "m3_frame_layout_get": (_I, [ctypes.POINTER(Config), _I, ctypes.POINTER(FrameLayout)]),
     "m3_frame_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Config), _I]),

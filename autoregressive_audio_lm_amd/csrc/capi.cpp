@@ -545,6 +545,40 @@ int m3_gumbel_argmax(const float* logits, int B, int V, int ldl, const m3_sample
   return hip_status(launch_sample(d, static_cast<hipStream_t>(stream)));
 }
 
+int m3_cfg_topk_draw(const float* logits, int n_songs, int V, int ldl, float cfg_scale,
+                     int top_k, const m3_sample_params* p, int32_t* out, void* stream) {
+  if (!logits || !p || !out) return M3_ERR_NULL;
+  if (n_songs < 1 || n_songs > M3_MAX_SONGS_CFG || V < 1 || V > kCfgMaxV || ldl < V || top_k < 1)
+    return M3_ERR_SHAPE;
+  if (!std::isfinite(cfg_scale)) return M3_ERR_SHAPE;
+  if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return M3_ERR_SHAPE;
+  if (!aligned(logits, 4) || !aligned(out, 4)) return M3_ERR_ALIGN;
+  if ((p->ids && !aligned(p->ids, 4)) || (p->noise_override && !aligned(p->noise_override, 4)) ||
+      (p->frame_dev && !aligned(p->frame_dev, 4)))
+    return M3_ERR_ALIGN;
+  CfgDesc d{};
+  d.logits = logits;
+  d.S = n_songs;
+  d.V = V;
+  d.ldl = ldl;
+  d.scale = cfg_scale;
+  d.top_k = top_k;
+  d.seed = p->seed;
+  d.frame = p->frame;
+  d.frame_dev = p->frame_dev;
+  d.draw = p->draw;
+  d.temperature = p->temperature;
+  d.index_base = p->index_base;
+  d.ids = p->ids;
+  d.valid_lo = p->valid_lo;
+  d.valid_hi = p->valid_hi;
+  d.noise = p->noise_override;
+  d.out = out;
+  d.out_stride = 1;
+  d.vec4 = aligned(logits, 16) && ldl % 4 == 0;
+  return hip_status(launch_cfg_draw(d, static_cast<hipStream_t>(stream)));
+}
+
 uint64_t m3_frame_weight_bytes(const m3_config* c) {
   if (!c) return 0;
   const Dims d = dims_of(*c);

@@ -108,6 +108,30 @@ struct SampleDesc {
 size_t sample_ws_bytes(int B, int V);
 hipError_t launch_sample(const SampleDesc& d, hipStream_t s);
 
+// CFG + top-k draw: one workgroup per song; rows 2s / 2s+1 are the song's
+// conditional / unconditional logits; out[(2s) * out_stride] and
+// out[(2s+1) * out_stride] receive its id.  V <= kCfgMaxV (32 keys per thread).
+constexpr int kCfgMaxV = M3_MAX_V_CFG;
+struct CfgDesc {
+  const float* logits;
+  int S, V, ldl;
+  float scale;
+  int top_k;
+  uint64_t seed;
+  uint32_t frame;
+  const uint32_t* frame_dev;
+  uint32_t draw;
+  float temperature;
+  int32_t index_base;
+  const int32_t* ids;
+  int32_t valid_lo, valid_hi;
+  const float* noise;   // [S, V] or null
+  int32_t* out;
+  int out_stride;
+  int vec4;             // logits rows 16-byte aligned (float4 loads)
+};
+hipError_t launch_cfg_draw(const CfgDesc& d, hipStream_t s);
+
 // ---- frame helpers -------------------------------------------------------------
 // audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)
 // Final draw of the last codebook from the head's per-block winners, then the

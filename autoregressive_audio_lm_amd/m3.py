@@ -130,3 +130,26 @@ def gumbel_argmax(logits: torch.Tensor, seed: int = 0, frame: int = 0, draw: int
     check(lib().m3_gumbel_argmax(_ptr(logits), B, V, logits.stride(0), ctypes.byref(p), _ptr(out),
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def cfg_topk_draw(logits: torch.Tensor, scale: float = 1.5, top_k: int = 50, seed: int = 0,
+                  frame: int = 0, draw: int = 0, temperature: float = 1.0, index_base: int = 0,
+                  ids: torch.Tensor | None = None, valid=(0, 0),
+                  noise: torch.Tensor | None = None, frame_dev: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_cfg_topk_draw: logits float32 [2S, V] (rows 2s conditional, 2s+1
+    unconditional) -> int32 [2S], both rows of a song holding its draw."""
+    for t, n in ((logits, "logits"), (ids, "ids"), (noise, "noise"), (frame_dev, "frame_dev"),
+                 (out, "out")):
+        _cuda(t, n)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.shape[0] % 2:
+        raise ValueError("logits must be a float32 [2S, V] tensor of row pairs")
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    p = _lib.SampleParams(int(seed) & (2**64 - 1), int(frame), _ptr(frame_dev), int(draw),
+                          float(temperature), int(index_base), _ptr(ids), int(valid[0]),
+                          int(valid[1]), _ptr(noise))
+    check(lib().m3_cfg_topk_draw(_ptr(logits), B // 2, V, logits.stride(0), float(scale),
+                                 int(top_k), ctypes.byref(p), _ptr(out), _stream(stream)))
+    return out

@@ -56,6 +56,8 @@ enum { M3_PACK_GLU_INTERLEAVE = 1 };
 #define M3_MAX_B_NORM_4K 16  /* rows when a 4096-wide norm is fused         */
 #define M3_MAX_B_FRAME 16    /* rows per frame                              */
 #define M3_MAX_B_SAMPLE 65535 /* rows per sampler call                      */
+#define M3_MAX_SONGS_CFG 32767 /* songs (row pairs) per CFG draw call       */
+#define M3_MAX_V_CFG 32768   /* columns per CFG draw call                   */
 
 const char* m3_status_str(int status);
 /* library version string (host) */
@@ -179,6 +181,32 @@ size_t m3_gumbel_workspace_bytes(int B, int V);
 int m3_gumbel_argmax(const float* logits, int B, int V, int ldl,
                      const m3_sample_params* params, int32_t* out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- the reference's draw: guidance, top-k, multinomial ------------------ */
+/* DiffSynth-Studio MiniMax-Music3 stage 2: each song's conditional row c and
+ * unconditional row u are combined as u + cfg_scale (c - u) (scale 1.5 there),
+ * filtered to the top_k largest (50 there) and sampled from the softmax of the
+ * survivors; TensorFold PR #987 "What it adds" draws this on the same Philox
+ * counters.  Song s owns logits rows 2s (conditional) and 2s+1
+ * (unconditional), row stride ldl.  Per song:
+ *   g_j = u_j + fl32(cfg_scale * fl32(c_j - u_j)) (three fp32 operations, no
+ *         contraction); masked ids (params' valid range) and NaN g take no part;
+ *   the survivors are the top_k largest g, ties to the lower column (all of
+ *         them when fewer remain);
+ *   the draw is Gumbel-argmax over the survivors, z = fl32(g * fl32(1/T)) + G
+ *         with G as in m3_gumbel_argmax but counter row word = s (one draw
+ *         per song), ranked as there (NaN on top, ties to the lower column);
+ *         Gumbel-argmax draws from exactly the survivors' softmax(g/T);
+ *   out[2s] = out[2s+1] = the drawn absolute id (a song with nothing left
+ *         draws column 0's id).
+ * noise_override (optional, device [n_songs, V]) replaces G.  Sizes:
+ * 1 <= n_songs <= M3_MAX_SONGS_CFG, 1 <= V <= M3_MAX_V_CFG, ldl >= V,
+ * top_k >= 1, cfg_scale finite, T > 0; logits, out, ids, noise_override,
+ * frame_dev 4-byte aligned; params is a HOST struct.  Needs no workspace.
+ * Errors: M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_ALIGN before any launch;
+ * M3_ERR_HIP if the launch fails. */
+int m3_cfg_topk_draw(const float* logits, int n_songs, int V, int ldl, float cfg_scale,
+                     int top_k, const m3_sample_params* params, int32_t* out, void* stream);
 
 /* ---- one decode frame ------------------------------------------------------ */
 typedef struct {

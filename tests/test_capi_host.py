@@ -112,6 +112,26 @@ def test_sampler_refusals(L):
     assert L.m3_gumbel_argmax(*arg(p=bad)) == _lib.M3_ERR_SHAPE
 
 
+def test_cfg_draw_refusals(L):
+    p = _lib.SampleParams(0, 0, None, 0, 1.0, 0, None, 0, 0, None)
+    arg = lambda **k: (k.get("lg", FAKE), k.get("S", 4), k.get("V", 5000), k.get("ldl", 5000),
+                       k.get("scale", 1.5), k.get("k", 50), ctypes.byref(k.get("p", p)),
+                       k.get("out", FAKE2), None)
+    assert L.m3_cfg_topk_draw(*arg(lg=None)) == _lib.M3_ERR_NULL
+    assert L.m3_cfg_topk_draw(*arg(out=None)) == _lib.M3_ERR_NULL
+    assert L.m3_cfg_topk_draw(*arg(S=0)) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(S=32768)) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(V=0, ldl=0)) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(V=32769, ldl=32769)) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(ldl=4999)) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(k=0)) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(scale=float("inf"))) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(scale=float("nan"))) == _lib.M3_ERR_SHAPE
+    assert L.m3_cfg_topk_draw(*arg(lg=ctypes.c_void_p(0x100002))) == _lib.M3_ERR_ALIGN
+    bad = _lib.SampleParams(0, 0, None, 0, -1.0, 0, None, 0, 0, None)
+    assert L.m3_cfg_topk_draw(*arg(p=bad)) == _lib.M3_ERR_SHAPE
+
+
 @pytest.mark.parametrize("preset", ["A", "B"])
 @pytest.mark.parametrize("name", ["frame-full", "frame-small"])
 def test_frame_weight_bytes_matches_oracle_formula(L, oracle, preset, name):
