@@ -349,8 +349,8 @@ void m3o_gumbel_argmax(const float* logits, int B, int V, int ldl,
 /*     to the lower column (all candidates when fewer than k);          */
 /*  3. the multinomial draw from softmax(g/T) over the survivors is     */
 /*     taken as Gumbel-argmax over them ([hf] item 3: the same law),    */
-/*     z = fl32(g * fl32(1/T)) + G(seed, s, frame, draw, id), the       */
-/*     highest z winning, ties to the lower column;                     */
+/*     z = fl32(g * fl32(1/T)) + G(seed, s, frame, draw, id), ranked    */
+/*     as in the plain draw (NaN on top, ties to the lower column);     */
 /*  4. the drawn id is written to both rows of the song.                */
 /* A song without candidates draws its first column's id.               */
 /* ------------------------------------------------------------------ */
@@ -395,7 +395,8 @@ void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, 
                                                (uint32_t)id);
       float lt = cand[r].g * invT;
       float z = lt + g;
-      if (best < 0 || z > zb || (z == zb && j < best)) {
+      /* the plain draw's order: NaN above every number, ties to the lower column */
+      if (best < 0 || ranks_above(z, zb) || (!ranks_above(zb, z) && j < best)) {
         best = j;
         zb = z;
       }
