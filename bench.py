@@ -176,6 +176,39 @@ def time_gate_up(dm, st, stream, reps=3):
     return us, wbytes + 4 * H, n
 
 
+def time_cfg_draw(stream, S, V, top_k=50, calls=50, reps=5):
+    """Average duration of m3_cfg_topk_draw (guidance over S row pairs,
+    top-k, Gumbel-argmax) on seeded logits, from a captured graph of `calls`
+    launches replayed `reps` times, HIP events on the launch stream."""
+    import torch
+    from autoregressive_audio_lm_amd import m3
+    g = torch.Generator(device="cuda").manual_seed(7)
+    L = torch.randn(2 * S, V, device="cuda", generator=g) * 2.0
+    out = torch.empty(2 * S, dtype=torch.int32, device="cuda")
+    frame = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            m3.cfg_topk_draw(L, top_k=top_k, frame_dev=frame, out=out, stream=stream)
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(calls):
+                m3.cfg_topk_draw(L, top_k=top_k, frame_dev=frame, out=out, stream=stream)
+        graph.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (calls * reps)
+    del graph
+    return {"songs": S, "V": V, "top_k": top_k, "avg_us": round(us, 2),
+            "logit_bytes": 2 * S * V * 4, "GB_s": round(2 * S * V * 4 / (us * 1e-6) / 1e9, 1)}
+
+
 def kernel_source_hash(which: str = "gate_up") -> str:
     import hashlib
     h = hashlib.sha256()
@@ -338,6 +371,10 @@ def main():
         roofline = {"bound": "hbm", "achieved": gate_up["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": gate_up["frac"], "traffic": gate_up["traffic"], "kernel": gate_up["kernel"],
                     "avg_us": gate_up["avg_us"], "bytes_per_launch": kbytes}
+    # the reference's draw (guidance + top-k 50 + Gumbel-argmax) at the lm_head's
+    # B = 16 (8 songs, 16384 codes) and the depth heads' B = 6 (3 songs, 1024 codes)
+    cfg_draw = [time_cfg_draw(stream, 8, cfg["V0"]), time_cfg_draw(stream, 3, cfg["code_vocab"])]
+    log(f"[bench] cfg draw {cfg_draw}")
     paths_ms = {k: round(v["ms"], 4) for k, v in res.items()}
     for v in res.values():
         v["state"].release()
@@ -411,6 +448,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "cfg_draw": {"kernel": "cfg_topk_kernel (guidance 1.5, top-k 50, Gumbel-argmax; "
+                               "one workgroup per song)", "points": cfg_draw},
         "gpu": f"{props.name} {props.gcnArchName} x{props.multi_processor_count} CU",
     }
     print(json.dumps(out), flush=True)
