@@ -1039,9 +1039,12 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
     // (persistent launches: only phase 0, whose operand is plain; not worth the registers)
     if constexpr (LDS && !COH) {
       if (!p.has_gather && nitems > 0) {
+        // (not for int8-g128: its 16 extra VGPRs would take the 16-row depth
+        // kernels past 128, i.e. from two resident workgroups per CU to one;
+        // measured +6..8 us per normed depth GEMV at B = 16)
         if (p.lds_rows <= 2)
           prefetch_x<COH>(p, pre, tg);
-        else
+        else if constexpr (FMT != M3_I8G128)
           prefetch_group<COH>(p, grp, tg);
       }
     }
