@@ -79,6 +79,16 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return u >> 16;
 }
 
+// two fp32 -> packed bf16 pair with the hardware's round-to-nearest-even
+// convert (v_cvt_pk_bf16_f32; one instruction for two values; finite values
+// round exactly as f2bf, NaN stays NaN)
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf_pair(float lo, float hi) {
+  const f32x2v_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
+}
+
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
                                          __builtin_bit_cast(bf16x2_t, a), acc, false);
@@ -459,11 +469,7 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
     if (p.has_gather && wg == 0 && k < p.K) act_store8<COH>(p.gat.out, (size_t)b * p.K + k, v, tg.y);
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a0 = bf2f(wv[j] & 0xffffu), a1 = bf2f(wv[j] >> 16);
-      ss = fmaf(a0, a0, ss);
-      ss = fmaf(a1, a1, ss);
-    }
+    for (int j = 0; j < 4; ++j) ss = dot2(wv[j], wv[j], ss);
   };
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -518,10 +524,14 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
   }
 }
 
-// One launch per GEMV, more than two rows: the first group of the copy pass
-// (kStageUnroll chunks per thread), requested ahead of the weight stream.
+// One launch per GEMV, more than two rows: the first kPreGroups groups of the
+// copy pass (kStageUnroll chunks per thread each), requested ahead of the
+// weight stream (vector loads retire in issue order: a group requested after
+// the first weight batch would wait for it).  Two groups cover 16 rows of
+// K = 4096.
+constexpr int kPreGroups = 2;
 struct XGroup {
-  uint4 v[kStageUnroll];
+  uint4 v[kPreGroups][kStageUnroll];
   bool valid;
 };
 
@@ -531,12 +541,15 @@ __device__ __forceinline__ void prefetch_group(const Params& p, XGroup& g, const
   const int cpr = (p.lds_stride - 8) >> 3;
   const int total = p.lds_rows * cpr;
 #pragma unroll
-  for (int u = 0; u < kStageUnroll; ++u) {
-    const int it = tid + u * kThreads;
-    const int b = it / cpr, k = (it - b * cpr) * 8;
-    const bool in = it < total && k < p.K;
-    g.v[u] = make_uint4(0, 0, 0, 0);
-    if (in) g.v[u] = load_x8<COH>(p, b, k, tg);
+  for (int q = 0; q < kPreGroups; ++q) {
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int it = tid + (q * kStageUnroll + u) * kThreads;
+      const int b = it / cpr, k = (it - b * cpr) * 8;
+      const bool in = it < total && k < p.K;
+      g.v[q][u] = make_uint4(0, 0, 0, 0);
+      if (in) g.v[q][u] = load_x8<COH>(p, b, k, tg);
+    }
   }
   g.valid = true;
 }
@@ -560,10 +573,11 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
   for (int base = tid; base < total; base += kThreads * kStageUnroll) {
     uint4 v[kStageUnroll];
     bool ok[kStageUnroll];
-    if (!COH && grp.valid && base == tid) {
+    const int group = (base - tid) / (kThreads * kStageUnroll);
+    if (!COH && grp.valid && group < kPreGroups) {
 #pragma unroll
       for (int u = 0; u < kStageUnroll; ++u) {
-        v[u] = grp.v[u];
+        v[u] = group == 0 ? grp.v[0][u] : grp.v[1][u];
         ok[u] = true;
       }
     } else {
@@ -599,20 +613,29 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
   }
   __syncthreads();
   if (!p.gamma) return;
-  // pass 2: r_b from the sum of squares of row b
+  // pass 2: r_b from the sum of squares of row b: lane l sums chunks
+  // l + 64 m into accumulator m % 4 (four independent chains whose LDS reads
+  // are in flight together; v_dot2 squares and adds a bf16 pair in one
+  // instruction), then (s0 + s1) + (s2 + s3), then across the wave
   for (int b = wave; b < p.lds_rows; b += kWaves) {
     const int kc = p.K >> 3;
-    float ss = 0.f;
-    for (int c = lane; c < kc; c += 64) {
-      const uint4 v = *reinterpret_cast<const uint4*>(act + (size_t)b * stride + c * 8);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = lane; c0 < kc; c0 += 256) {
+      uint4 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = bf2f(wv[j] & 0xffffu), a1 = bf2f(wv[j] >> 16);
-        ss = fmaf(a0, a0, ss);
-        ss = fmaf(a1, a1, ss);
+      for (int m = 0; m < 4; ++m) {
+        const int c = c0 + 64 * m;
+        v[m] = c < kc ? *reinterpret_cast<const uint4*>(act + (size_t)b * stride + c * 8)
+                      : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t wv[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m] = dot2(wv[j], wv[j], acc[m]);
       }
     }
+    float ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     ss = wave_sum(ss);
     if (lane == 0) ss_buf[b] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
   }
@@ -625,18 +648,29 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
     const float4 g0 = *reinterpret_cast<const float4*>(p.gamma + k);
     const float4 g1 = *reinterpret_cast<const float4*>(p.gamma + k + 4);
     const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    for (int b = 0; b < p.lds_rows; ++b) {
-      const float r = ss_buf[b];
-      uint4* ptr = reinterpret_cast<uint4*>(act + (size_t)b * stride + k);
-      const uint4 v = *ptr;
-      uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    // rows in groups of four: the group's LDS reads are issued together
+    for (int b0 = 0; b0 < p.lds_rows; b0 += 4) {
+      uint4 v[4];
+      float r[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = (bf2f(wv[j] & 0xffffu) * r) * g[2 * j];
-        const float a1 = (bf2f(wv[j] >> 16) * r) * g[2 * j + 1];
-        wv[j] = f2bf(a0) | (f2bf(a1) << 16);
+      for (int e = 0; e < 4; ++e) {
+        const int b = b0 + e < p.lds_rows ? b0 + e : b0;
+        v[e] = *reinterpret_cast<const uint4*>(act + (size_t)b * stride + k);
+        r[e] = ss_buf[b];
       }
-      *ptr = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t wv[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a0 = (bf2f(wv[j] & 0xffffu) * r[e]) * g[2 * j];
+          const float a1 = (bf2f(wv[j] >> 16) * r[e]) * g[2 * j + 1];
+          wv[j] = f2bf_pair(a0, a1);
+        }
+        if (b0 + e < p.lds_rows)
+          *reinterpret_cast<uint4*>(act + (size_t)(b0 + e) * stride + k) =
+              make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
     }
   }
   __syncthreads();
