@@ -111,9 +111,32 @@ __device__ __forceinline__ void i8x16_to_bf16(const uint4& q, uint32_t* o) {
   i8x4_to_bf16x4(q.w, o[6], o[7]);
 }
 
+// Sum over the wave, left in every lane, without LDS round trips: lane l
+// and l^32, then l and l^16, with the permlane swaps (each adds the same two
+// values in the same order in both lanes), then the 16 lanes of a row with
+// DPP quad exchanges and half-row / row mirrors.  Every lane of the wave must
+// be active.
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = pair_sum16(pair_sum32(v));
+  v += dpp_f<0xB1>(v);     // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);    // row_half_mirror
+  v += dpp_f<0x140>(v);    // row_mirror
   return v;
 }
 
@@ -878,9 +901,7 @@ struct Accum {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      float v = acc[b];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
+      const float v = pair_sum16(pair_sum32(acc[b]));   // lanes l, l^16, l^32, l^48
       if (lane < 16) red[(wave * NB + b) * 16 + lane] = v;
     }
   }

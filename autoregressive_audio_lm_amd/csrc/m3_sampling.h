@@ -105,15 +105,46 @@ __device__ __forceinline__ bool above(float za, int ia, float zb, int ib) {
   return ia < ib;
 }
 
-// butterfly over `width` lanes (power of two <= 64)
+// The best (z, j) over groups of `width` lanes (16 or 64), left in every
+// lane of the group.  The order is total, so any pairing gives the same
+// winner: DPP quad exchanges and half-row / row mirrors inside a row of 16
+// lanes, then (width 64) the permlane swaps between rows.  Every lane of the
+// wave must be active.
+template <int CTRL>
+__device__ __forceinline__ void best_dpp(float& z, int& j) {
+  const float oz = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), CTRL, 0xF, 0xF, false));
+  const int oj = __builtin_amdgcn_update_dpp(0, j, CTRL, 0xF, 0xF, false);
+  if (above(oz, oj, z, j)) {
+    z = oz;
+    j = oj;
+  }
+}
+
+__device__ __forceinline__ void best_swap(float& z, int& j, bool rows32) {
+  // the swap of a register with itself returns the two partners' values in
+  // r[0] / r[1]; this lane's partner is whichever is not its own
+  const auto rz = rows32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false)
+                         : __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  const auto rj = rows32 ? __builtin_amdgcn_permlane32_swap((uint32_t)j, (uint32_t)j, false, false)
+                         : __builtin_amdgcn_permlane16_swap((uint32_t)j, (uint32_t)j, false, false);
+  const int lane = threadIdx.x & 63;
+  const bool low = rows32 ? lane < 32 : (lane & 16) == 0;
+  const float oz = __uint_as_float(low ? rz[1] : rz[0]);
+  const int oj = (int)(low ? rj[1] : rj[0]);
+  if (above(oz, oj, z, j)) {
+    z = oz;
+    j = oj;
+  }
+}
+
 __device__ __forceinline__ void best_reduce(float& z, int& j, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) {
-    const float oz = __shfl_xor(z, o, 64);
-    const int oj = __shfl_xor(j, o, 64);
-    if (above(oz, oj, z, j)) {
-      z = oz;
-      j = oj;
-    }
+  best_dpp<0xB1>(z, j);
+  best_dpp<0x4E>(z, j);
+  best_dpp<0x141>(z, j);
+  best_dpp<0x140>(z, j);
+  if (width > 16) {
+    best_swap(z, j, false);
+    best_swap(z, j, true);
   }
 }
 
