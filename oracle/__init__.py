@@ -33,7 +33,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "m3_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-BF16, I8ROW, I8G128 = 0, 1, 2
+BF16, I8ROW, I8G128, FP8ROW = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:
@@ -125,6 +125,11 @@ def _declare(L):
                              ctypes.c_uint32, ctypes.c_uint32]
     L.m3o_gumbel_argmax.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.POINTER(SampleParams), _P, _P, _P]
+    L.m3o_fp8_decode.restype = ctypes.c_double
+    L.m3o_fp8_decode.argtypes = [ctypes.c_uint8]
+    L.m3o_fp8_encode.restype = ctypes.c_uint8
+    L.m3o_fp8_encode.argtypes = [ctypes.c_double]
+    L.m3o_quant_fp8row.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P]
     L.m3o_cfg_topk_draw.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_float, ctypes.c_int, ctypes.POINTER(SampleParams), _P, _P]
     L.m3o_decode_frame.argtypes = [ctypes.POINTER(Model), _P, ctypes.c_int, ctypes.c_uint64,
@@ -192,8 +197,25 @@ def quant_i8g128(W):
     return q, s
 
 
+def fp8_decode(c) -> float:
+    return float(lib().m3o_fp8_decode(int(c) & 0xFF))
+
+
+def fp8_encode(v) -> int:
+    return int(lib().m3o_fp8_encode(float(v)))
+
+
+def quant_fp8row(W):
+    W = _c(W, np.uint16)
+    N, K = W.shape
+    q = np.empty((N, K), np.uint8)
+    s = np.empty((N,), np.float32)
+    lib().m3o_quant_fp8row(_ptr(W), N, K, _ptr(q), _ptr(s))
+    return q, s
+
+
 class Matrix:
-    """A weight matrix in one of the three formats, built from bf16 W by the
+    """A weight matrix in one of the four formats, built from bf16 W by the
     oracle's own quantiser.  Keeps the numpy buffers alive for ctypes."""
 
     def __init__(self, W, fmt):
@@ -206,6 +228,8 @@ class Matrix:
             self.q, self.s = quant_i8row(W)
         elif fmt == I8G128:
             self.q, self.s = quant_i8g128(W)
+        elif fmt == FP8ROW:
+            self.q, self.s = quant_fp8row(W)
         else:
             raise ValueError(fmt)
 
@@ -394,14 +418,16 @@ def decode_frame(om: OracleModel, x_in, seed, frame, temperature=1.0, trace=Fals
 
 # ----------------------------------------------------------- weight bytes ---
 def matrix_bytes(fmt: int, N: int, K: int) -> int:
-    """Algorithmic bytes of one weight matrix: bf16 2NK; int8-row NK + 4N;
-    int8-g128 NK + 4N*K/128 (weights plus fp32 scales)."""
+    """Algorithmic bytes of one weight matrix: bf16 2NK; int8-row and fp8-row
+    NK + 4N; int8-g128 NK + 4N*K/128 (weights plus fp32 scales)."""
     if fmt == BF16:
         return 2 * N * K
     if fmt == I8ROW:
         return N * K + 4 * N
     if fmt == I8G128:
         return N * K + 4 * N * (K // 128)
+    if fmt == FP8ROW:
+        return N * K + 4 * N
     raise ValueError(fmt)
 
 

@@ -147,6 +147,59 @@ void m3o_quant_i8g128(const uint16_t* W, int N, int K, int8_t* q, float* s) {
 }
 
 /* ------------------------------------------------------------------ */
+/* fp8 weight-only (the next format after int8: [hf] and [mm] list fp8  */
+/* weight-only only as a result measured on another stack; the format   */
+/* is this build's reading): OCP FP8 E4M3 -- sign, 4 exponent bits with */
+/* bias 7, 3 mantissa bits; exponent 0 holds the subnormals m * 2^-9;   */
+/* S.1111.111 is NaN; there is no infinity; the largest finite is 448.  */
+/* One fp32 scale per row: s = absmax / 448 as one fp32 division, q =   */
+/* the nearest E4M3 value of W / s (ties to the even mantissa),         */
+/* saturated to +-448; an all-zero row gets s = 0 and q = 0.            */
+/* ------------------------------------------------------------------ */
+double m3o_fp8_decode(uint8_t c) {
+  int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? (double)m * ldexp(1.0, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+uint8_t m3o_fp8_encode(double v) {
+  if (isnan(v)) return 0x7F;
+  uint8_t sgn = signbit(v) ? 0x80 : 0x00;
+  double a = fabs(v);
+  if (a >= 448.0) return sgn | 0x7E;                 /* saturate at the largest finite */
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: multiples of 2^-9; 8 * 2^-9 is the smallest normal,
+       whose code is 8 as well */
+    return sgn | (uint8_t)nearbyint(a * 512.0);
+  }
+  int x;
+  frexp(a, &x);                                      /* a = f 2^x, f in [0.5, 1) */
+  int E = x - 1;                                     /* a in [2^E, 2^(E+1)) */
+  double m = nearbyint((ldexp(a, -E) - 1.0) * 8.0);  /* exact scaling, then RNE */
+  if (m == 8.0) { m = 0.0; E += 1; }
+  int e = E + 7;
+  if (e > 15 || (e == 15 && m == 7.0)) return sgn | 0x7E;
+  return sgn | (uint8_t)(e << 3) | (uint8_t)m;
+}
+
+void m3o_quant_fp8row(const uint16_t* W, int N, int K, uint8_t* q, float* s) {
+  #pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    const uint16_t* w = W + (size_t)n * K;
+    double amax = 0.0;
+    for (int k = 0; k < K; ++k) {
+      double v = fabs(m3o_bf16_to_f64(w[k]));
+      if (v > amax) amax = v;
+    }
+    float sc = (float)amax / 448.0f;   /* amax is exact in fp32 */
+    s[n] = sc;
+    for (int k = 0; k < K; ++k)
+      q[(size_t)n * K + k] = sc == 0.0f ? 0 : m3o_fp8_encode(m3o_bf16_to_f64(w[k]) / (double)sc);
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* y = Wdeq . a, summed in float64.  Each bf16*bf16 product is exact in */
 /* float64, int8*bf16 too; only the running sum rounds (at 2^-53).      */
 /* ------------------------------------------------------------------ */
@@ -157,6 +210,12 @@ static double dot_row(const m3o_mat* m, int n, const uint16_t* a) {
     double acc = 0.0;
     for (int k = 0; k < K; ++k) acc += m3o_bf16_to_f64(w[k]) * m3o_bf16_to_f64(a[k]);
     return acc;
+  }
+  if (m->fmt == M3O_FP8ROW) {
+    const uint8_t* c = (const uint8_t*)m->q + (size_t)n * K;
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) acc += m3o_fp8_decode(c[k]) * m3o_bf16_to_f64(a[k]);
+    return (double)m->s[n] * acc;
   }
   const int8_t* q = m->q + (size_t)n * K;
   if (m->fmt == M3O_I8ROW) {

@@ -29,7 +29,7 @@ extern "C" {
 
 /* weight formats (MiniMax Music 3 Metal port, precision section: bf16,
    int8 with one scale per row, int8 with one scale per group of 128) */
-enum { M3O_BF16 = 0, M3O_I8ROW = 1, M3O_I8G128 = 2 };
+enum { M3O_BF16 = 0, M3O_I8ROW = 1, M3O_I8G128 = 2, M3O_FP8ROW = 3 };
 
 /* ---- bf16 ---------------------------------------------------------- */
 uint16_t m3o_f64_to_bf16(double v);      /* one round-to-nearest-even */
@@ -49,13 +49,19 @@ void m3o_quant_i8row(const uint16_t* W, int N, int K, int8_t* q, float* s);
 /* the same per (row, group of 128 along K); s is [N, K/128] */
 void m3o_quant_i8g128(const uint16_t* W, int N, int K, int8_t* q, float* s);
 
+/* ---- fp8 weight-only (OCP FP8 E4M3, bias 7, no infinity, max 448) -- */
+double  m3o_fp8_decode(uint8_t c);        /* NaN for S.1111.111 */
+uint8_t m3o_fp8_encode(double v);         /* nearest, ties to even mantissa; |v| >= 448 -> +-448; NaN -> 0x7F */
+/* s_n = fl32(absmax_n / 448); q = encode(W / s); zero row: s = q = 0 */
+void m3o_quant_fp8row(const uint16_t* W, int N, int K, uint8_t* q, float* s);
+
 /* ---- matrix-vector products (exact fp64 sums, unrounded) ------------ */
 typedef struct {
-  int fmt;              /* M3O_BF16 / M3O_I8ROW / M3O_I8G128 */
+  int fmt;              /* M3O_BF16 / M3O_I8ROW / M3O_I8G128 / M3O_FP8ROW */
   int N, K;
   const uint16_t* w;    /* bf16 [N,K]            (fmt == M3O_BF16) */
-  const int8_t* q;      /* int8 [N,K]            (int8 formats)    */
-  const float* s;       /* [N] or [N, K/128]     (int8 formats)    */
+  const int8_t* q;      /* int8 [N,K] (int8 formats); fp8 codes [N,K] (M3O_FP8ROW) */
+  const float* s;       /* [N] or [N, K/128]     (int8 and fp8 formats) */
 } m3o_mat;
 
 /* y[b*N + n] = sum_k Wdeq[n,k] * a[b,k]; Wdeq = w, s_n*q or s_{n,g}*q */
