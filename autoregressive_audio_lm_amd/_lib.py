@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libm3.so")
 
 M3_OK, M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_ALIGN = 0, -1, -2, -3
 M3_ERR_FORMAT, M3_ERR_WORKSPACE, M3_ERR_HIP, M3_ERR_ALIAS = -4, -5, -6, -7
-BF16, I8ROW, I8G128 = 0, 1, 2
+BF16, I8ROW, I8G128, FP8ROW = 0, 1, 2, 3
 EPI_NONE, EPI_SWIGLU, EPI_RESIDUAL = 0, 1, 2
 OUT_BF16, OUT_F32 = 0, 1
 PACK_GLU_INTERLEAVE = 1
@@ -78,6 +78,7 @@ _SIGS = {
     "m3_rmsnorm_gemv": (_I, [_P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _I, _I, _P, _I, _I, _I, _P, _I, _P]),
     "m3_gemv_i8row": (_I, [_P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _I, _I, _P, _I, _I, _I, _P, _I, _P]),
     "m3_gemv_i8g128": (_I, [_P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _I, _I, _P, _I, _I, _I, _P, _I, _P]),
+    "m3_gemv_fp8row": (_I, [_P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _I, _I, _P, _I, _I, _I, _P, _I, _P]),
     "m3_lmhead_sliced": (_I, [_I, _P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _P, _I, _P]),
     "m3_gumbel_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "m3_gumbel_argmax": (_I, [_P, _I, _I, _I, ctypes.POINTER(SampleParams), _P, _P, ctypes.c_size_t, _P]),

@@ -30,12 +30,16 @@ SMALL = dict(
 )
 
 # weight formats (mirror of the C enum)
-BF16, I8ROW, I8G128 = 0, 1, 2
+BF16, I8ROW, I8G128, FP8ROW = 0, 1, 2, 3
 
 # Frame presets: (body, lm_head, depth) formats.
 PRESETS = {
     "A": dict(fmt_body=BF16, fmt_lm=BF16, fmt_depth=I8G128),    # bf16 body (headline)
     "B": dict(fmt_body=I8ROW, fmt_lm=I8ROW, fmt_depth=I8G128),  # int8 everywhere
+    # fp8 (OCP E4M3, one scale per row) body and lm_head: the fp8 weight-only
+    # variant, an assumed format (the pages list fp8 only as a result on
+    # another stack)
+    "C": dict(fmt_body=FP8ROW, fmt_lm=FP8ROW, fmt_depth=I8G128),
 }
 
 

@@ -26,13 +26,19 @@ int k_ok(int fmt, int K) {
   if (K < 8) return 0;
   switch (fmt) {
     case M3_BF16: return K % 8 == 0;
-    case M3_I8ROW: return K % 16 == 0;
+    case M3_I8ROW:
+    case M3_FP8ROW: return K % 16 == 0;
     case M3_I8G128: return K % 128 == 0;
     default: return 0;
   }
 }
 
-bool fmt_ok(int fmt) { return fmt == M3_BF16 || fmt == M3_I8ROW || fmt == M3_I8G128; }
+bool fmt_ok(int fmt) {
+  return fmt == M3_BF16 || fmt == M3_I8ROW || fmt == M3_I8G128 || fmt == M3_FP8ROW;
+}
+
+// formats of a whole-row-scale matrix (body, lm_head)
+bool row_fmt(int fmt) { return fmt == M3_BF16 || fmt == M3_I8ROW || fmt == M3_FP8ROW; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? M3_OK : M3_ERR_HIP; }
 
@@ -120,14 +126,14 @@ Dims dims_of(const m3_config& c) {
 
 uint64_t mat_bytes(int fmt, uint64_t N, uint64_t K) {
   if (fmt == M3_BF16) return 2 * N * K;
-  if (fmt == M3_I8ROW) return N * K + 4 * N;
+  if (fmt == M3_I8ROW || fmt == M3_FP8ROW) return N * K + 4 * N;
   return N * K + 4 * N * (K / 128);
 }
 
 int validate_config(const m3_config* c, int B) {
   if (!c) return M3_ERR_NULL;
   if (!fmt_ok(c->fmt_body) || !fmt_ok(c->fmt_depth)) return M3_ERR_FORMAT;
-  if (c->fmt_lm != M3_BF16 && c->fmt_lm != M3_I8ROW) return M3_ERR_FORMAT;
+  if (!row_fmt(c->fmt_lm)) return M3_ERR_FORMAT;
   if (B < 1 || B > M3_MAX_B_FRAME) return M3_ERR_SHAPE;
   if (c->n_layers < 1 || c->d_layers < 1) return M3_ERR_SHAPE;
   if (c->head_dim != 128 || c->d_head_dim != 128) return M3_ERR_SHAPE;
@@ -489,6 +495,13 @@ int m3_gemv_i8row(const void* w, int N, int K, const uint16_t* x, int B, int ldx
                     out_dtype, epi, res, ldr, stream);
 }
 
+int m3_gemv_fp8row(const void* w, int N, int K, const uint16_t* x, int B, int ldx,
+                   const float* gamma, float eps, int stub_group, int stub_voff, void* y, int ldy,
+                   int out_dtype, int epi, const uint16_t* res, int ldr, void* stream) {
+  return gemv_entry(M3_FP8ROW, w, N, K, x, B, ldx, gamma, eps, stub_group, stub_voff, y, ldy,
+                    out_dtype, epi, res, ldr, stream);
+}
+
 int m3_gemv_i8g128(const void* w, int N, int K, const uint16_t* x, int B, int ldx,
                    const float* gamma, float eps, int stub_group, int stub_voff, void* y, int ldy,
                    int out_dtype, int epi, const uint16_t* res, int ldr, void* stream) {
@@ -499,7 +512,7 @@ int m3_gemv_i8g128(const void* w, int N, int K, const uint16_t* x, int B, int ld
 int m3_lmhead_sliced(int fmt, const void* packed_slice, int n_rows, int K, const uint16_t* x,
                      int B, int ldx, const float* gamma, float eps, float* logits, int ldl,
                      void* stream) {
-  if (fmt != M3_BF16 && fmt != M3_I8ROW) return M3_ERR_FORMAT;
+  if (!row_fmt(fmt)) return M3_ERR_FORMAT;
   if (ldl % 4 != 0) return M3_ERR_ALIGN;
   const int st = validate_gemv(fmt, packed_slice, n_rows, K, x, B, ldx, gamma, eps, 0, 0, logits,
                                ldl, M3_OUT_F32, M3_EPI_NONE, nullptr, 0);
@@ -696,10 +709,10 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   if (st != M3_OK) return st;
   if (!aligned(state, 256) || !aligned(codes, 16)) return M3_ERR_ALIGN;
   if (frame_phases(model->cfg) > persist_max_phases()) return M3_ERR_SHAPE;
-  // one frame kernel per body format: bf16 or int8-row body and lm_head, int8-g128 depth
+  // one frame kernel per body format: bf16, int8-row or fp8-row body and the
+  // same lm_head format, int8-g128 depth
   const m3_config& c = model->cfg;
-  if ((c.fmt_body != M3_BF16 && c.fmt_body != M3_I8ROW) || c.fmt_lm != c.fmt_body ||
-      c.fmt_depth != M3_I8G128)
+  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128)
     return M3_ERR_FORMAT;
   // row-block winners carry their column in 16 bits next to the tag
   if (c.n_slice > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;

@@ -77,7 +77,8 @@ size_t gemv_smem_bytes(int fmt, int K, int B, bool has_gamma) {
 hipError_t gemv_prepare() {
   const hipError_t es[] = {configure_fmt<M3_BF16, true>(),   configure_fmt<M3_BF16, false>(),
                            configure_fmt<M3_I8ROW, true>(),  configure_fmt<M3_I8ROW, false>(),
-                           configure_fmt<M3_I8G128, true>(), configure_fmt<M3_I8G128, false>()};
+                           configure_fmt<M3_I8G128, true>(), configure_fmt<M3_I8G128, false>(),
+                           configure_fmt<M3_FP8ROW, true>(), configure_fmt<M3_FP8ROW, false>()};
   for (hipError_t e : es)
     if (e != hipSuccess) return e;
   return hipSuccess;
@@ -101,6 +102,9 @@ hipError_t launch_gemv(const GemvDesc& d, hipStream_t s) {
     case M3_I8ROW:
       return lds ? dispatch_b<M3_I8ROW, true>(p, grid, smem, s)
                  : dispatch_b<M3_I8ROW, false>(p, grid, smem, s);
+    case M3_FP8ROW:
+      return lds ? dispatch_b<M3_FP8ROW, true>(p, grid, smem, s)
+                 : dispatch_b<M3_FP8ROW, false>(p, grid, smem, s);
     default:
       return lds ? dispatch_b<M3_I8G128, true>(p, grid, smem, s)
                  : dispatch_b<M3_I8G128, false>(p, grid, smem, s);

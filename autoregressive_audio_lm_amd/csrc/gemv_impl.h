@@ -111,6 +111,28 @@ __device__ __forceinline__ void i8x16_to_bf16(const uint4& q, uint32_t* o) {
   i8x4_to_bf16x4(q.w, o[6], o[7]);
 }
 
+// four fp8 (OCP E4M3) codes -> two dwords of bf16 pairs, exact: every E4M3
+// value (subnormals included) is a bf16; the hardware pair convert with scale
+// 1 does it in one instruction per pair
+typedef __bf16 bf16x2p_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void f8x16_to_bf16(const uint4& q, uint32_t* o) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+  }
+}
+
+// one-byte codes of format FMT -> bf16 pairs
+template <int FMT>
+__device__ __forceinline__ void bytes16_to_bf16(const uint4& q, uint32_t* o) {
+  if constexpr (FMT == M3_FP8ROW)
+    f8x16_to_bf16(q, o);
+  else
+    i8x16_to_bf16(q, o);
+}
+
 // Sum over the wave, left in every lane, without LDS round trips: lane l
 // and l^32, then l and l^16, with the permlane swaps (each adds the same two
 // values in the same order in both lanes), then the 16 lanes of a row with
@@ -728,7 +750,7 @@ __device__ __forceinline__ void store_out(const Params& p, int b, int n, float v
 
 template <int FMT>
 __device__ __forceinline__ float row_scale(const uint8_t* blk, const Params& p, int r) {
-  if constexpr (FMT == M3_I8ROW)
+  if constexpr (FMT == M3_I8ROW || FMT == M3_FP8ROW)
     return reinterpret_cast<const float*>(blk + (size_t)p.T * kTileBytes)[r];
   return 1.0f;
 }
@@ -868,7 +890,7 @@ struct Accum {
     } else {
       const int kk = k0 + c * 16;
       uint32_t wb[8];
-      i8x16_to_bf16(wv, wb);
+      bytes16_to_bf16<FMT>(wv, wb);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int bb = min(b, p.B - 1);
@@ -941,7 +963,7 @@ struct Accum<FMT, NB, true> {
     } else {
       const int kk = k0 + c * 16;
       uint32_t wb[8];
-      i8x16_to_bf16(wv, wb);
+      bytes16_to_bf16<FMT>(wv, wb);
       const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, make_uint4(wb[0], wb[1], wb[2], wb[3]));
       const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, make_uint4(wb[4], wb[5], wb[6], wb[7]));
 #pragma unroll

@@ -20,7 +20,8 @@ __host__ __device__ inline int k_pad(int fmt, int K) { return round_up(K, tile_k
 __host__ __device__ inline int n_tiles(int fmt, int K) { return k_pad(fmt, K) / tile_k(fmt); }
 __host__ __device__ inline int n_blocks(int N) { return (N + kRowsPerBlock - 1) / kRowsPerBlock; }
 __host__ __device__ inline int scale_bytes(int fmt, int K) {
-  return fmt == M3_I8ROW ? 128 : (fmt == M3_I8G128 ? round_up((K / 128) * 64, 128) : 0);
+  return (fmt == M3_I8ROW || fmt == M3_FP8ROW) ? 128
+                                               : (fmt == M3_I8G128 ? round_up((K / 128) * 64, 128) : 0);
 }
 __host__ __device__ inline size_t block_bytes(int fmt, int K) {
   return (size_t)n_tiles(fmt, K) * kTileBytes + scale_bytes(fmt, K);
@@ -180,6 +181,7 @@ hipError_t persist_launch(const PersistLaunch& L, hipStream_t s);
 // the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip) by row-count class
 const void* persist_kernel_bf16(int NB);
 const void* persist_kernel_i8row(int NB);
+const void* persist_kernel_fp8row(int NB);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, size_t n, hipStream_t s);
 
 }  // namespace m3

@@ -1,5 +1,8 @@
 // pack.hip -- load-time quantise + pack into the tiled layout of m3.h.
 //
+// fp8 (OCP E4M3) weight-only with one scale per row as a further format:
+// scale = absmax/448, codes nearest with ties to even (see qf8).
+//
 // int8 weight-only quantisation on the GPU at load (TensorFold PR #987,
 // precision list: a scale per row for the body and lm_head, per group of 128
 // for the depth decoder): scale = absmax/127 (one IEEE fp32 division), q =
@@ -34,6 +37,7 @@ __global__ __launch_bounds__(256) void scale_kernel(PackParams p) {
   const int lane = threadIdx.x & 63;
   const int G = FMT == M3_I8G128 ? p.K / 128 : 1;
   const int gsz = FMT == M3_I8G128 ? 128 : p.K;
+  const float qmax = FMT == M3_FP8ROW ? 448.0f : 127.0f;   // largest code value
   const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long ntask = (long)p.nblocks * 16 * G;
   if (task >= ntask) return;
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(256) void scale_kernel(PackParams p) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   if (lane == 0) {
-    const float s = __fdiv_rn(amax, 127.0f);
+    const float s = __fdiv_rn(amax, qmax);
     const int rb = n >> 4, r = n & 15;
     float* sc = reinterpret_cast<float*>(p.out + (size_t)rb * p.bbytes + (size_t)p.T * kTileBytes);
     sc[FMT == M3_I8G128 ? r * G + g : r] = s;
@@ -58,6 +62,29 @@ __device__ __forceinline__ uint32_t q8(float w, float s) {
   double t = rint((double)w / (double)s);
   t = t > 127.0 ? 127.0 : (t < -127.0 ? -127.0 : t);
   return (uint32_t)((int)t & 0xff);
+}
+
+// fp8 weight-only: the OCP FP8 E4M3 code nearest to w/s (ties to the even
+// mantissa), saturated to +-448 (the format has no infinity).  E4M3: sign,
+// 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 holds m * 2^-9.
+// The quotient is formed in float64 (as for int8, its rounding cannot move
+// it across a midpoint between two codes).
+__device__ __forceinline__ uint32_t qf8(float w, float s) {
+  if (s == 0.0f) return 0u;
+  const double t = (double)w / (double)s;
+  if (t != t) return 0x7Fu;                                  // NaN code
+  const uint32_t sign = t < 0.0 || (t == 0.0 && signbit(t)) ? 0x80u : 0u;
+  const double a = fabs(t);
+  if (!(a < 448.0)) return sign | 0x7Eu;
+  if (a < 0.015625) return sign | (uint32_t)rint(a * 512.0);   // below 2^-6: steps of 2^-9
+  int ex = ilogb(a);                                         // a in [2^ex, 2^(ex+1))
+  double mant = rint(scalbn(a, 3 - ex)) - 8.0;               // 3 fraction bits, ties to even
+  if (mant >= 8.0) {
+    mant = 0.0;
+    ++ex;
+  }
+  if (ex + 7 > 15 || (ex + 7 == 15 && mant >= 7.0)) return sign | 0x7Eu;
+  return sign | (uint32_t)((ex + 7) << 3) | (uint32_t)mant;
 }
 
 // One thread per 16 packed bytes: (block, tile, lane).
@@ -88,7 +115,9 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
       uint32_t o[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t lo = q8(bf2f(h[j] & 0xffffu), s), hi = q8(bf2f(h[j] >> 16), s);
+        const float wl = bf2f(h[j] & 0xffffu), wh = bf2f(h[j] >> 16);
+        const uint32_t lo = FMT == M3_FP8ROW ? qf8(wl, s) : q8(wl, s);
+        const uint32_t hi = FMT == M3_FP8ROW ? qf8(wh, s) : q8(wh, s);
         o[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
       }
       v = make_uint4(o[0], o[1], o[2], o[3]);
@@ -97,7 +126,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   *reinterpret_cast<uint4*>(blk + (size_t)t * kTileBytes + l * 16) = v;
 }
 
-// zero the padding after the scales of each block (i8row: 64 B; g128: rounding)
+// zero the padding after the scales of each block (i8row, fp8-row: 64 B; g128: rounding)
 __global__ __launch_bounds__(256) void pad_kernel(uint8_t* out, int nblocks, size_t bbytes,
                                                   size_t used, size_t pad) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -139,6 +168,9 @@ hipError_t launch_pack(int fmt, const uint16_t* W, int N, int K, int flags, void
   if (fmt == M3_I8ROW) {
     hipLaunchKernelGGL(scale_kernel<M3_I8ROW>, dim3(sgrid), dim3(256), 0, s, p);
     hipLaunchKernelGGL(pack_kernel<M3_I8ROW>, dim3(grid), dim3(256), 0, s, p);
+  } else if (fmt == M3_FP8ROW) {
+    hipLaunchKernelGGL(scale_kernel<M3_FP8ROW>, dim3(sgrid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(pack_kernel<M3_FP8ROW>, dim3(grid), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL(scale_kernel<M3_I8G128>, dim3(sgrid), dim3(256), 0, s, p);
     hipLaunchKernelGGL(pack_kernel<M3_I8G128>, dim3(grid), dim3(256), 0, s, p);

@@ -148,7 +148,9 @@ hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, u
   nwg &= ~3;
   if (nwg < 4) return hipErrorInvalidValue;
   const int NB = nb_of(pl->B);
-  const void* k = pl->fmt_body == M3_I8ROW ? persist_kernel_i8row(NB) : persist_kernel_bf16(NB);
+  const void* k = pl->fmt_body == M3_I8ROW    ? persist_kernel_i8row(NB)
+                  : pl->fmt_body == M3_FP8ROW ? persist_kernel_fp8row(NB)
+                                              : persist_kernel_bf16(NB);
   e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl->smem);
   if (e != hipSuccess) return e;
   e = hipMemcpyAsync(table, pl->phases.data(), pl->phases.size() * sizeof(Phase),

@@ -11,11 +11,11 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (BF16, I8ROW, I8G128, EPI_NONE, EPI_SWIGLU, EPI_RESIDUAL, OUT_BF16, OUT_F32,
+from ._lib import (BF16, I8ROW, I8G128, FP8ROW, EPI_NONE, EPI_SWIGLU, EPI_RESIDUAL, OUT_BF16, OUT_F32,
                    PACK_GLU_INTERLEAVE, check, lib)
 
-__all__ = ["packed_bytes", "pack", "rmsnorm_gemv", "gemv_i8row", "gemv_i8g128", "gemv",
-           "lmhead_sliced", "gumbel_workspace_bytes", "gumbel_argmax", "BF16", "I8ROW", "I8G128",
+__all__ = ["packed_bytes", "pack", "rmsnorm_gemv", "gemv_i8row", "gemv_i8g128", "gemv_fp8row", "gemv", "cfg_topk_draw",
+           "lmhead_sliced", "gumbel_workspace_bytes", "gumbel_argmax", "BF16", "I8ROW", "I8G128", "FP8ROW",
            "EPI_NONE", "EPI_SWIGLU", "EPI_RESIDUAL", "OUT_BF16", "OUT_F32", "PACK_GLU_INTERLEAVE"]
 
 
@@ -53,7 +53,8 @@ def pack(fmt: int, W: torch.Tensor, flags: int = 0, out: torch.Tensor | None = N
     return out
 
 
-_GEMV = {BF16: "m3_rmsnorm_gemv", I8ROW: "m3_gemv_i8row", I8G128: "m3_gemv_i8g128"}
+_GEMV = {BF16: "m3_rmsnorm_gemv", I8ROW: "m3_gemv_i8row", I8G128: "m3_gemv_i8g128",
+         FP8ROW: "m3_gemv_fp8row"}
 
 
 def gemv(fmt: int, packed: torch.Tensor, N: int, K: int, x: torch.Tensor,
@@ -87,6 +88,10 @@ def gemv_i8row(packed, N, K, x, **kw):
 
 def gemv_i8g128(packed, N, K, x, **kw):
     return gemv(I8G128, packed, N, K, x, **kw)
+
+
+def gemv_fp8row(packed, N, K, x, **kw):
+    return gemv(FP8ROW, packed, N, K, x, **kw)
 
 
 def lmhead_sliced(fmt: int, packed: torch.Tensor, n_rows: int, K: int, x: torch.Tensor,

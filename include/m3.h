@@ -47,7 +47,7 @@ typedef enum {
 } m3_status;
 
 /* ---- enums ------------------------------------------------------------ */
-enum { M3_BF16 = 0, M3_I8ROW = 1, M3_I8G128 = 2 };          /* weight formats */
+enum { M3_BF16 = 0, M3_I8ROW = 1, M3_I8G128 = 2, M3_FP8ROW = 3 };  /* weight formats */
 enum { M3_EPI_NONE = 0, M3_EPI_SWIGLU = 1, M3_EPI_RESIDUAL = 2 };
 enum { M3_OUT_BF16 = 0, M3_OUT_F32 = 1 };
 enum { M3_PACK_GLU_INTERLEAVE = 1 };
@@ -66,12 +66,13 @@ const char* m3_version(void);
 /* ---- packing (a load-time step) --------------------------------------- */
 /* Packed layout, identical for all formats: the rows are cut into blocks of
  * 16; each block is a run of 1024-byte tiles along K, each tile holding 64
- * bytes of each of the 16 rows (32 bf16 or 64 int8 values per row).  Byte
+ * bytes of each of the 16 rows (32 bf16, or 64 int8 or fp8 values per row).  Byte
  * 16*l .. 16*l+15 of a tile belongs to row (l mod 16), K-bytes 16*(l/16) ..
  * 16*(l/16)+15 of the tile's 64-byte K-segment, so that one 16-byte load per
  * lane of a 64-lane wave reads the whole tile contiguously.  K is zero-padded
- * to a whole tile and N to a whole block.  int8 blocks end with their fp32
- * scales: i8row: scale[r] for r = 0..15 (64 B, then 64 B padding);
+ * to a whole tile and N to a whole block.  int8 and fp8 blocks end with
+ * their fp32 scales: i8row and fp8row: scale[r] for r = 0..15 (64 B, then
+ * 64 B padding);
  * i8g128: scale[r][g] for the 16 rows and every group g of 128 along K
  * (16 x K/128 floats, rounded up to 128 B).  int8 codes are two's-complement
  * bytes in [-127, 127].  A packed matrix must be smaller than 2 GiB.
@@ -80,12 +81,20 @@ const char* m3_version(void);
  * nearest integer of W/scale (ties to even), clamped to [-127, 127]; an
  * all-zero row or group gets scale 0.  Weights must be finite.
  *
+ * Quantisation (fp8row, OCP FP8 E4M3: sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, exponent 0 = subnormals m * 2^-9, no infinity, largest
+ * finite 448; the pages list fp8 weight-only only as a result on another
+ * stack, diffusers issue #14486 and MiniMax-Music3 issue #2): scale =
+ * absmax / 448 as one fp32 division per row; the code is the E4M3 value
+ * nearest W/scale (ties to the even mantissa), saturated to +-448; an
+ * all-zero row gets scale 0 and codes 0.
+ *
  * flags & M3_PACK_GLU_INTERLEAVE: W is a stacked [gate; up] matrix [2F, K];
  * packed row 2i is gate row i and row 2i+1 is up row i, so one GEMV with the
  * SwiGLU epilogue produces both halves of each pair (TensorFold PR #987, "What
  * it adds": a gate and an up row whose SwiGLU the GEMV writes).  N = 2F.
  *
- * Sizes: bf16 K % 8 == 0; i8row K % 16 == 0; i8g128 K % 128 == 0; N >= 1.
+ * Sizes: bf16 K % 8 == 0; i8row, fp8row K % 16 == 0; i8g128 K % 128 == 0; N >= 1.
  * W_bf16 is [N, K] row-major (leading dimension K); W and packed must be
  * 16-byte aligned.  packed must hold m3_packed_bytes(fmt, N, K, flags). */
 size_t m3_packed_bytes(int fmt, int N, int K, int flags);   /* host only; 0 = refused */
@@ -126,6 +135,14 @@ int m3_gemv_i8row(const void* packed_i8row, int N, int K,
                   const float* gamma, float eps, int stub_group, int stub_voff,
                   void* y, int ldy, int out_dtype,
                   int epi, const uint16_t* residual, int ldr, void* stream);
+/* fp8row: W[n, k] = scale[n] * E4M3(code[n, k]); the codes are converted to
+ * bf16 exactly (every E4M3 value is a bf16) and multiplied in fp32, as for
+ * int8.  Same parameters and bounds as m3_rmsnorm_gemv. */
+int m3_gemv_fp8row(const void* packed_fp8row, int N, int K,
+                   const uint16_t* x, int B, int ldx,
+                   const float* gamma, float eps, int stub_group, int stub_voff,
+                   void* y, int ldy, int out_dtype,
+                   int epi, const uint16_t* residual, int ldr, void* stream);
 int m3_gemv_i8g128(const void* packed_i8g128, int N, int K,
                    const uint16_t* x, int B, int ldx,
                    const float* gamma, float eps, int stub_group, int stub_voff,
@@ -140,7 +157,7 @@ int m3_gemv_i8g128(const void* packed_i8g128, int N, int K,
  * #14486 item 3; "MiniMax Music 3, local", where the time went).  Each
  * logit's summation order depends only on K, never on n_rows, the batch or
  * the slice offset, so a slice reproduces the full matrix's logits bit for
- * bit.  fmt is M3_BF16 or M3_I8ROW.  Sizes as m3_rmsnorm_gemv; ldl >= n_rows,
+ * bit.  fmt is M3_BF16, M3_I8ROW or M3_FP8ROW.  Sizes as m3_rmsnorm_gemv; ldl >= n_rows,
  * ldl % 4 == 0. */
 int m3_lmhead_sliced(int fmt, const void* packed_slice, int n_rows, int K,
                      const uint16_t* x, int B, int ldx, const float* gamma, float eps,
@@ -321,7 +338,7 @@ int m3_frame_graph_destroy(void* graph);
  * operand by reading it until the tags are the ones its producer writes (one
  * store and one load per dependency, no barrier).  x, h, logits, codes, the
  * ring and the frame counter are updated exactly as by the other paths, with
- * the same bytes.  Supported: bf16 or int8-row body with the same lm_head
+ * the same bytes.  Supported: bf16, int8-row or fp8-row body with the same lm_head
  * format and an int8-g128 depth decoder (else M3_ERR_FORMAT), every GEMV
  * operand staged in LDS (at the full model: B <= 6; else M3_ERR_SHAPE), vocab
  * slice and code vocabulary below 65536.  The frame state must have been

@@ -91,21 +91,23 @@ def classes(v):
 
 def unpack(packed: np.ndarray, fmt: int, N: int, K: int):
     """Decode the packed tile layout (include/m3.h) back to row-major arrays:
-    bf16 -> uint16 [N, K]; int8 -> (q int8 [N, K], scales [N] or [N, K/128])."""
+    bf16 -> uint16 [N, K]; int8 -> (q int8 [N, K], scales [N] or [N, K/128]);
+    fp8-row -> (codes uint8 [N, K], scales [N])."""
     TK = 32 if fmt == O.BF16 else 64
     Kp = -(-K // TK) * TK
     T = Kp // TK
     nb = -(-N // 16)
-    sb = {O.BF16: 0, O.I8ROW: 128, O.I8G128: -(-(K // 128) * 64 // 128) * 128}[fmt]
+    sb = {O.BF16: 0, O.I8ROW: 128, O.FP8ROW: 128, O.I8G128: -(-(K // 128) * 64 // 128) * 128}[fmt]
     bb = T * 1024 + sb
     blocks = np.ascontiguousarray(packed[: nb * bb]).reshape(nb, bb)
     tiles = np.ascontiguousarray(blocks[:, : T * 1024]).reshape(nb, T, 4, 16, 16)
     if fmt == O.BF16:
         w = tiles.view(np.uint16).reshape(nb, T, 4, 16, 8).transpose(0, 3, 1, 2, 4)
         return w.reshape(nb * 16, Kp)[:N, :K]
-    q = tiles.view(np.int8).reshape(nb, T, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(nb * 16, Kp)
+    q = tiles.view(np.uint8 if fmt == O.FP8ROW else np.int8).reshape(nb, T, 4, 16, 16)
+    q = q.transpose(0, 3, 1, 2, 4).reshape(nb * 16, Kp)
     sc = np.ascontiguousarray(blocks[:, T * 1024:])
-    if fmt == O.I8ROW:
+    if fmt in (O.I8ROW, O.FP8ROW):
         s = sc[:, :64].view(np.float32).reshape(nb * 16)
     else:
         G = K // 128

@@ -47,7 +47,7 @@ FAKE2 = ctypes.c_void_p(0x900000)
 
 def gemv(L, fmt=0, N=64, K=256, x=FAKE, B=1, ldx=256, gamma=None, eps=1e-6, sg=0, sv=0, y=FAKE2,
          ldy=64, out=0, epi=0, res=None, ldr=0):
-    f = {0: L.m3_rmsnorm_gemv, 1: L.m3_gemv_i8row, 2: L.m3_gemv_i8g128}[fmt]
+    f = {0: L.m3_rmsnorm_gemv, 1: L.m3_gemv_i8row, 2: L.m3_gemv_i8g128, 3: L.m3_gemv_fp8row}[fmt]
     return f(FAKE, N, K, x, B, ldx, gamma, eps, sg, sv, y, ldy, out, epi, res, ldr, None)
 
 
@@ -60,6 +60,7 @@ def gemv(L, fmt=0, N=64, K=256, x=FAKE, B=1, ldx=256, gamma=None, eps=1e-6, sg=0
     (dict(K=4, ldx=8), _lib.M3_ERR_SHAPE),
     (dict(K=250), _lib.M3_ERR_SHAPE),
     (dict(fmt=1, K=248, ldx=248), _lib.M3_ERR_SHAPE),       # i8row needs K % 16
+    (dict(fmt=3, K=248, ldx=248), _lib.M3_ERR_SHAPE),       # fp8row needs K % 16
     (dict(fmt=2, K=192, ldx=192), _lib.M3_ERR_SHAPE),       # g128 needs K % 128
     (dict(ldx=128), _lib.M3_ERR_SHAPE),
     (dict(ldy=32), _lib.M3_ERR_SHAPE),
@@ -89,7 +90,8 @@ def test_pack_and_sizes(L):
     assert L.m3_packed_bytes(2, 16, 256, 0) == 4 * 1024 + 128       # 2 groups x 64 B -> 128
     assert L.m3_packed_bytes(2, 16, 200, 0) == 0
     assert L.m3_packed_bytes(0, 15, 64, 1) == 0                     # GLU needs even N
-    assert L.m3_packed_bytes(3, 16, 64, 0) == 0
+    assert L.m3_packed_bytes(3, 16, 64, 0) == 1024 + 128            # fp8-row: as int8-row
+    assert L.m3_packed_bytes(4, 16, 64, 0) == 0                     # unknown format
     assert L.m3_pack(0, None, 16, 32, 0, FAKE, None) == _lib.M3_ERR_NULL
     assert L.m3_pack(0, FAKE, 16, 30, 0, FAKE2, None) == _lib.M3_ERR_SHAPE
     assert L.m3_pack(5, FAKE, 16, 32, 0, FAKE2, None) == _lib.M3_ERR_FORMAT
@@ -132,7 +134,7 @@ def test_cfg_draw_refusals(L):
     assert L.m3_cfg_topk_draw(*arg(p=bad)) == _lib.M3_ERR_SHAPE
 
 
-@pytest.mark.parametrize("preset", ["A", "B"])
+@pytest.mark.parametrize("preset", ["A", "B", "C"])
 @pytest.mark.parametrize("name", ["frame-full", "frame-small"])
 def test_frame_weight_bytes_matches_oracle_formula(L, oracle, preset, name):
     cfg = configs.config(name)

@@ -18,7 +18,7 @@ DEV = "cuda"
 MARGIN = 0.05     # z margin below which a draw may legitimately differ
 
 
-@pytest.fixture(scope="module", params=["A", "B"])
+@pytest.fixture(scope="module", params=["A", "B", "C"])
 def small(request):
     cfg = configs.config("frame-small")
     p = configs.PRESETS[request.param]

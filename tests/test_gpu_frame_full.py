@@ -86,7 +86,7 @@ def test_full_size_frame_within_rounding_envelope(preset, B):
     assert np.all((codes == o_codes)[sure])
 
 
-@pytest.mark.parametrize("preset,B", [("A", 1), ("A", 6), ("B", 2)])
+@pytest.mark.parametrize("preset,B", [("A", 1), ("A", 6), ("B", 2), ("C", 1)])
 def test_full_size_persistent_equals_graph(preset, B):
     """The persistent frame (one cooperative launch, tagged intermediate
     streams) and the graph-replayed frame give identical bytes at the full

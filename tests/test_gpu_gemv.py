@@ -1,7 +1,8 @@
 """GPU parity of the packer and the RMSNorm-fused GEMV family against the CPU
 oracle (TensorFold PR #987 precision list: bf16, int8 per row, int8 per group
 of 128; fused RMS norm; SwiGLU and residual epilogues; identity attention
-stub).  Every call goes through the C ABI."""
+stub), and of the fp8 (OCP E4M3, one scale per row) weight-only format.
+Every call goes through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -55,7 +56,7 @@ def oracle_y(fmt, W, x, gamma=None):
 
 # ----------------------------------------------------------------- pack ---
 @pytest.mark.parametrize("fmt,N,K", [(0, 37, 72), (1, 37, 80), (2, 37, 384), (0, 16, 4096),
-                                     (1, 48, 4096), (2, 40, 2048)])
+                                     (1, 48, 4096), (2, 40, 2048), (3, 37, 80), (3, 48, 4096)])
 def test_pack_bit_exact(fmt, N, K):
     W = rand_w(N, K, 1)
     W[3] = 0                                  # an all-zero row
@@ -65,7 +66,7 @@ def test_pack_bit_exact(fmt, N, K):
         assert np.array_equal(P.unpack(pk, fmt, N, K), W)
     else:
         q, s = P.unpack(pk, fmt, N, K)
-        qo, so = (O.quant_i8row if fmt == 1 else O.quant_i8g128)(W)
+        qo, so = {1: O.quant_i8row, 2: O.quant_i8g128, 3: O.quant_fp8row}[fmt](W)
         assert np.array_equal(q, qo)
         assert np.array_equal(s.view(np.uint32), so.view(np.uint32))
 
@@ -79,10 +80,10 @@ def test_pack_glu_interleave():
 
 
 # ------------------------------------------------------------ GEMV parity --
-SHAPES = {0: (200, 520), 1: (200, 528), 2: (200, 640)}   # several tiles, ragged N and K
+SHAPES = {0: (200, 520), 1: (200, 528), 2: (200, 640), 3: (200, 528)}   # several tiles, ragged N and K
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("B", [1, 2, 3, 6, 8, 16, 33, 64])
 def test_gemv_norm_parity(fmt, B):
     N, K = SHAPES[fmt]
@@ -94,7 +95,7 @@ def test_gemv_norm_parity(fmt, B):
     P.check_f32(run_gemv(fmt, W, x, g, out_f32=True), y_ex)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("B", [1, 6, 16])
 def test_gemv_plain_and_residual(fmt, B):
     N, K = SHAPES[fmt]
@@ -106,7 +107,7 @@ def test_gemv_plain_and_residual(fmt, B):
     P.check_residual(run_gemv(fmt, W, x, epi=m3.EPI_RESIDUAL, res=h), h, y_ex)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("B", [1, 6, 16])
 def test_gemv_swiglu(fmt, B):
     F, K = 104, SHAPES[fmt][1]
@@ -120,7 +121,7 @@ def test_gemv_swiglu(fmt, B):
     P.check_swiglu(m, y_gu)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("B,group", [(1, 4), (6, 4), (16, 1)])
 def test_gemv_attention_stub(fmt, B, group):
     n_heads, hd = 8, 128
@@ -184,7 +185,7 @@ def test_depth_shapes_g128(which):
 
 
 # ---------------------------------------------- determinism and classes ----
-@pytest.mark.parametrize("fmt,B", [(0, 1), (1, 6), (2, 16)])
+@pytest.mark.parametrize("fmt,B", [(0, 1), (1, 6), (2, 16), (3, 3)])
 def test_repeat_byte_identical_and_rows_independent(fmt, B):
     N, K = SHAPES[fmt]
     W = rand_w(N, K, 500)
@@ -203,7 +204,7 @@ def test_repeat_byte_identical_and_rows_independent(fmt, B):
         assert d[0].tobytes() == a[0].tobytes()
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("norm", [False, True])
 def test_nonfinite_classes(fmt, norm):
     """Non-finite outputs match the oracle's classes (TensorFold PR #987,

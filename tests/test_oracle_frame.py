@@ -131,7 +131,7 @@ def test_frame_codes_in_range(oracle, small):
         assert np.all(np.isfinite(oracle.bf16_to_f64(xn)))
 
 
-@pytest.mark.parametrize("preset", ["A", "B"])
+@pytest.mark.parametrize("preset", ["A", "B", "C"])
 def test_weight_bytes_formula_counts_the_arrays(oracle, preset):
     """The per-frame weight-byte formula equals the byte count of the arrays
     a frame actually reads (quantised by the oracle's pinned quantisers)."""
@@ -142,7 +142,8 @@ def test_weight_bytes_formula_counts_the_arrays(oracle, preset):
     def nbytes(W, fmt):
         if fmt == configs.BF16:
             return W.nbytes
-        q, s = (oracle.quant_i8row if fmt == configs.I8ROW else oracle.quant_i8g128)(W)
+        q, s = {configs.I8ROW: oracle.quant_i8row, configs.I8G128: oracle.quant_i8g128,
+                configs.FP8ROW: oracle.quant_fp8row}[fmt](W)
         return q.nbytes + s.nbytes
 
     def layer_bytes(L, fmt):
