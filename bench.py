@@ -296,7 +296,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--B", type=int, default=1)
-    ap.add_argument("--preset", default="A", choices=["A", "B"])
+    ap.add_argument("--preset", default="A", choices=["A", "B", "C"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the B = 2/6/16 and int8 context points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -400,15 +400,15 @@ def main():
     if not args.no_sweep:
         for B in (2, 6, 16):
             sweep.append(point(args.preset, B, dm, fbytes))
-        other = "B" if args.preset == "A" else "A"
         del dm
         torch.cuda.empty_cache()
-        _, dm2, _ = build_model(other, args.seed, dev)
-        fb2 = dm2.weight_bytes()
-        for B in (1, 6, 16):
-            sweep.append(point(other, B, dm2, fb2))
-        del dm2
-        torch.cuda.empty_cache()
+        for other in [q for q in ("A", "B", "C") if q != args.preset]:
+            _, dm2, _ = build_model(other, args.seed, dev)
+            fb2 = dm2.weight_bytes()
+            for B in (1, 6, 16):
+                sweep.append(point(other, B, dm2, fb2))
+            del dm2
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -416,7 +416,7 @@ def main():
         cpu = cpu_baseline(cfg, L0, args.cpu_seconds)
         log(f"[bench] cpu_baseline {cpu}")
 
-    fmt_name = {0: "bf16", 1: "int8 per-row", 2: "int8 per-group-128"}
+    fmt_name = {0: "bf16", 1: "int8 per-row", 2: "int8 per-group-128", 3: "fp8 E4M3 per-row"}
     p = __import__("autoregressive_audio_lm_amd.configs", fromlist=["PRESETS"]).PRESETS[args.preset]
     out = {
         "metric": METRIC,
@@ -429,7 +429,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if p["fmt_body"] == 0 else "int8xbf16",
+        "dtype": {0: "bf16", 1: "int8xbf16", 3: "fp8xbf16"}[p["fmt_body"]],
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) input rows; no checkpoint)",
         "config": {
             "workload": (f"one decode frame, preset {args.preset}: 36-layer Qwen3-8B-shaped body "
