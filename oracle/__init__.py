@@ -90,7 +90,8 @@ class Model(ctypes.Structure):
                 ("n_codebooks", ctypes.c_int), ("code_vocab", ctypes.c_int),
                 ("p_in", Mat), ("emb1", _P), ("emb", _P), ("d_layers_w", _P),
                 ("d_final_norm", _P), ("heads", _P), ("tok_emb_audio", _P),
-                ("audio_emb", _P), ("eps", ctypes.c_float)]
+                ("audio_emb", _P), ("eps", ctypes.c_float), ("cfg_scale", ctypes.c_float),
+                ("top_k", ctypes.c_int)]
 
 
 class FrameTrace(ctypes.Structure):
@@ -131,7 +132,8 @@ def _declare(L):
     L.m3o_fp8_encode.argtypes = [ctypes.c_double]
     L.m3o_quant_fp8row.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P]
     L.m3o_cfg_topk_draw.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_float, ctypes.c_int, ctypes.POINTER(SampleParams), _P, _P]
+                                    ctypes.c_float, ctypes.c_int, ctypes.POINTER(SampleParams), _P, _P,
+                                    _P]
     L.m3o_decode_frame.argtypes = [ctypes.POINTER(Model), _P, ctypes.c_int, ctypes.c_uint64,
                                    ctypes.c_uint32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(FrameTrace)]
@@ -326,7 +328,8 @@ def gumbel_argmax(logits, seed=0, frame=0, draw=0, temperature=1.0, index_base=0
 
 
 def cfg_topk_draw(logits, scale=1.5, top_k=50, seed=0, frame=0, draw=0, temperature=1.0,
-                  index_base=0, ids=None, valid=(0, 0), noise=None, with_kept=False):
+                  index_base=0, ids=None, valid=(0, 0), noise=None, with_kept=False,
+                  with_gap=False):
     """The reference's draw over (conditional, unconditional) row pairs;
     logits [2S, V] -> ids [2S] (both rows of a song carry its draw)."""
     lg = _c(logits, np.float32)
@@ -340,11 +343,11 @@ def cfg_topk_draw(logits, scale=1.5, top_k=50, seed=0, frame=0, draw=0, temperat
                      _ptr(ids_a), int(valid[0]), int(valid[1]), _ptr(nz))
     out = np.empty(B, np.int32)
     kept = np.empty(S, np.int32)
+    gap = np.empty(S, np.float32)
     lib().m3o_cfg_topk_draw(_ptr(lg), S, V, V, float(scale), int(top_k), ctypes.byref(p),
-                            _ptr(out), _ptr(kept))
-    if with_kept:
-        return out, kept
-    return out
+                            _ptr(out), _ptr(kept), _ptr(gap))
+    res = (out,) + ((kept,) if with_kept else ()) + ((gap,) if with_gap else ())
+    return res[0] if len(res) == 1 else res
 
 
 # ----------------------------------------------------------------- frame ---
@@ -352,7 +355,9 @@ class OracleModel:
     """Wraps a model dict (see autoregressive_audio_lm_amd.synth) into the C
     struct.  The oracle quantises int8 formats itself from the bf16 sources."""
 
-    def __init__(self, md: dict):
+    def __init__(self, md: dict, cfg_scale: float = 1.5, top_k: int = 0):
+        """top_k == 0: per-row draws; top_k > 0: the reference's draw over
+        (conditional, unconditional) row pairs with guidance cfg_scale."""
         self._keep = []
         cfg = md["cfg"]
         fb, fl, fd = md["fmt_body"], md["fmt_lm"], md["fmt_depth"]
@@ -393,7 +398,7 @@ class OracleModel:
             ctypes.cast(emb_arr, ctypes.c_void_p), ctypes.cast(DL, ctypes.c_void_p),
             _ptr(keep(md["d_final_norm"], np.float32)), ctypes.cast(heads, ctypes.c_void_p),
             _ptr(keep(md["tok_emb_audio"], np.uint16)), ctypes.cast(aemb_arr, ctypes.c_void_p),
-            float(cfg["eps"]))
+            float(cfg["eps"]), float(cfg_scale), int(top_k))
 
 
 def decode_frame(om: OracleModel, x_in, seed, frame, temperature=1.0, trace=False):

@@ -424,7 +424,8 @@ static int cand_order(const void* a, const void* b) {
 }
 
 void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, int top_k,
-                       const m3o_sample_params* p, int32_t* out, int32_t* n_kept) {
+                       const m3o_sample_params* p, int32_t* out, int32_t* n_kept,
+                       float* zgap) {
   float invT = 1.0f / p->temperature;
   m3o_cand* cand = (m3o_cand*)malloc((size_t)V * sizeof *cand);
   for (int s = 0; s < S; ++s) {
@@ -444,7 +445,7 @@ void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, 
     }
     int keep = n < top_k ? n : top_k;
     int best = -1;
-    float zb = 0.0f;
+    float zb = 0.0f, z2 = -INFINITY;
     if (keep > 0) qsort(cand, (size_t)n, sizeof *cand, cand_order);
     for (int r = 0; r < keep; ++r) {
       int j = cand[r].j;
@@ -456,8 +457,11 @@ void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, 
       float z = lt + g;
       /* the plain draw's order: NaN above every number, ties to the lower column */
       if (best < 0 || ranks_above(z, zb) || (!ranks_above(zb, z) && j < best)) {
+        if (best >= 0) z2 = zb;
         best = j;
         zb = z;
+      } else if (ranks_above(z, z2)) {
+        z2 = z;
       }
     }
     if (best < 0) best = 0;
@@ -465,6 +469,7 @@ void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, 
     out[2 * s] = id;
     out[2 * s + 1] = id;
     if (n_kept) n_kept[s] = keep;
+    if (zgap) zgap[s] = keep > 0 ? zb - z2 : INFINITY;
   }
   free(cand);
 }
@@ -490,6 +495,26 @@ static void run_layer(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_head
   m3o_swiglu_interleaved(y, B, F, mm);
   m3o_gemv(&L->down, mm, B, F, y);
   m3o_residual(y, h, B * Hd, h);
+}
+
+/* The frame's draws: per row (Gumbel-argmax), or, with top_k > 0, the
+   reference's draw over (conditional, unconditional) row pairs, one draw per
+   song written to both of its rows ([ds] stage 2: guidance 1.5, top-k 50).
+   zb - z2 receives each row's decision margin. */
+static void draw_rows(const m3o_model* m, const float* lg, int B, int V,
+                      const m3o_sample_params* p, int32_t* out, float* zb, float* z2) {
+  if (m->top_k <= 0) {
+    m3o_gumbel_argmax(lg, B, V, V, p, out, zb, z2);
+    return;
+  }
+  int S = B / 2;
+  float* gap = (float*)malloc((size_t)(S > 0 ? S : 1) * 4);
+  m3o_cfg_topk_draw(lg, S, V, V, m->cfg_scale, m->top_k, p, out, NULL, gap);
+  for (int b = 0; b < B; ++b) {
+    zb[b] = gap[b / 2];
+    z2[b] = 0.0f;
+  }
+  free(gap);
 }
 
 void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
@@ -525,7 +550,7 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
   if (tr && tr->logits0) memcpy(tr->logits0, lg, (size_t)B * m->V0 * 4);
   m3o_sample_params sp = {seed, frame, 0u, temperature, m->vocab_base, NULL,
                           m->vocab_base, m->vocab_base + m->V0, NULL};
-  m3o_gumbel_argmax(lg, B, m->V0, m->V0, &sp, draw_out, zb, z2);
+  draw_rows(m, lg, B, m->V0, &sp, draw_out, zb, z2);
   for (int b = 0; b < B; ++b) {
     codes[b * 8 + 0] = draw_out[b];
     if (tr && tr->zgap) tr->zgap[b * 8 + 0] = zb[b] - z2[b];
@@ -559,7 +584,7 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
     m3o_gemv(&m->heads[j - 1], a, B, D, y);
     for (size_t i = 0; i < (size_t)B * m->code_vocab; ++i) lg[i] = (float)y[i];
     m3o_sample_params dp = {seed, frame, (uint32_t)j, temperature, 0, NULL, 0, 0, NULL};
-    m3o_gumbel_argmax(lg, B, m->code_vocab, m->code_vocab, &dp, draw_out, zb, z2);
+    draw_rows(m, lg, B, m->code_vocab, &dp, draw_out, zb, z2);
     for (int b = 0; b < B; ++b) {
       codes[b * 8 + j] = draw_out[b];
       if (tr && tr->zgap) tr->zgap[b * 8 + j] = zb[b] - z2[b];

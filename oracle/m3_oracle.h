@@ -100,9 +100,12 @@ void m3o_gumbel_argmax(const float* logits, int B, int V, int ldl,
 /* CFG + top-k draw over song pairs (rows 2s conditional, 2s+1
    unconditional): guided g = u + scale (c - u), the top_k largest g (ties to
    the lower column), Gumbel-argmax over them with counter row s; out[2s] =
-   out[2s+1] = the drawn id.  n_kept (optional [S]) receives the survivor count. */
+   out[2s+1] = the drawn id.  n_kept (optional [S]) receives the survivor count,
+   zgap (optional [S]) the best survivor's z minus the second best (inf with
+   one survivor). */
 void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, int top_k,
-                       const m3o_sample_params* p, int32_t* out, int32_t* n_kept);
+                       const m3o_sample_params* p, int32_t* out, int32_t* n_kept,
+                       float* zgap);
 
 /* ---- one decode frame ------------------------------------------------ */
 typedef struct {
@@ -130,6 +133,10 @@ typedef struct {
   const uint16_t* tok_emb_audio; /* [V0, H]: embed_tokens rows of the audio codes */
   const uint16_t* const* audio_emb; /* audio_emb[j-1], [code_vocab, H]  */
   float eps;
+  /* draws: top_k == 0 per row; top_k > 0 the reference's draw over row
+     pairs (B even) with guidance scale cfg_scale ([ds] stage 2) */
+  float cfg_scale;
+  int top_k;
 } m3o_model;
 
 typedef struct {

@@ -151,3 +151,36 @@ def test_sliced_equals_masked_full(oracle):
         a = oracle.cfg_topk_draw(full, top_k=50, seed=4, frame=f, valid=(base, base + V0))
         b = oracle.cfg_topk_draw(sl, top_k=50, seed=4, frame=f, index_base=base)
         assert np.array_equal(a, b)
+
+
+def test_margin_is_the_gap_between_the_two_best_survivors(oracle):
+    V = 6
+    noise = np.zeros((2, V), np.float32)
+    noise[0] = [3.0, 1.0, 0.5, 0, 0, 9.0]      # column 5 is cut by k = 3
+    noise[1] = [0, 0, 0, 0, 0, 0]
+    L = np.zeros((4, V), np.float32)
+    L[2:] = -np.inf
+    L[2, 4] = L[3, 4] = 0.0                    # song 1: a single candidate
+    out, gap = oracle.cfg_topk_draw(L, top_k=3, noise=noise, with_gap=True)
+    assert out.tolist() == [0, 0, 4, 4]
+    assert gap[0] == 2.0 and gap[1] == np.inf
+
+
+def test_guided_frame_draws_once_per_song(oracle):
+    """The frame in the reference's draw mode (guidance over row pairs, top-k):
+    both rows of a song carry the same codes, and the semantic code is the
+    guided draw (draw 0, counter row = song) over the frame's own logits."""
+    from autoregressive_audio_lm_amd import configs, synth
+    cfg = configs.config("frame-small")
+    md = synth.model_to_numpy(synth.make_model(cfg, configs.BF16, configs.BF16, configs.I8G128,
+                                               seed=3))
+    om = oracle.OracleModel(md, cfg_scale=1.5, top_k=50)
+    x = synth.bits(synth.activations(4, cfg["H"], seed=6))
+    for f in range(3):
+        codes, xn, tr = oracle.decode_frame(om, x, seed=8, frame=f, trace=True)
+        assert np.array_equal(codes[0::2], codes[1::2])
+        sem = oracle.cfg_topk_draw(tr["logits0"], scale=1.5, top_k=50, seed=8, frame=f, draw=0,
+                                   index_base=cfg["vocab_base"])
+        assert np.array_equal(codes[:, 0], sem)
+        assert np.all((codes[:, 1:] >= 0) & (codes[:, 1:] < cfg["code_vocab"]))
+        x = xn
