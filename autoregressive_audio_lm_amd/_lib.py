@@ -46,7 +46,8 @@ class Config(ctypes.Structure):
                                   "vocab_base", "n_slice", "d_hidden", "d_layers", "d_heads",
                                   "d_head_dim", "d_ffn", "n_codebooks", "code_vocab", "fmt_body",
                                   "fmt_lm", "fmt_depth")] + \
-               [("eps", ctypes.c_float), ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64)]
+               [("eps", ctypes.c_float), ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64),
+                ("cfg_scale", ctypes.c_float), ("top_k", _I)]
 
 
 class LayerWeights(ctypes.Structure):

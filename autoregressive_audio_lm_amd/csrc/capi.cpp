@@ -136,6 +136,11 @@ int validate_config(const m3_config* c, int B) {
   if (!row_fmt(c->fmt_lm)) return M3_ERR_FORMAT;
   if (B < 1 || B > M3_MAX_B_FRAME) return M3_ERR_SHAPE;
   if (c->n_layers < 1 || c->d_layers < 1) return M3_ERR_SHAPE;
+  // the reference's draw: rows in (conditional, unconditional) pairs
+  if (c->top_k < 0) return M3_ERR_SHAPE;
+  if (c->top_k > 0 && (B % 2 != 0 || !std::isfinite(c->cfg_scale) || c->n_slice > M3_MAX_V_CFG ||
+                       c->code_vocab > M3_MAX_V_CFG))
+    return M3_ERR_SHAPE;
   if (c->head_dim != 128 || c->d_head_dim != 128) return M3_ERR_SHAPE;
   if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return M3_ERR_SHAPE;
   if (c->d_heads < 1) return M3_ERR_SHAPE;
@@ -240,6 +245,7 @@ int validate_model(const m3_model* m) {
 // as the phases of one persistent launch.
 struct FrameSink {
   virtual hipError_t gemv(const GemvDesc& d) = 0;
+  virtual hipError_t cfg_draw(const CfgDesc& d) = 0;
   virtual hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                               const Best* last_part, int last_nparts, int32_t vocab_base,
                               int n_slice, int code_vocab, int n_cb, int B, int H, uint16_t* x,
@@ -250,6 +256,7 @@ struct LaunchSink final : FrameSink {
   hipStream_t s;
   explicit LaunchSink(hipStream_t st) : s(st) {}
   hipError_t gemv(const GemvDesc& d) override { return launch_gemv(d, s); }
+  hipError_t cfg_draw(const CfgDesc& d) override { return launch_cfg_draw(d, s); }
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
@@ -263,6 +270,8 @@ struct PlanSink final : FrameSink {
   PersistPlan* pl;
   explicit PlanSink(PersistPlan* p) : pl(p) {}
   hipError_t gemv(const GemvDesc& d) override { return persist_add_gemv(pl, d); }
+  // (the persistent frame carries the per-row draws only)
+  hipError_t cfg_draw(const CfgDesc&) override { return hipErrorInvalidValue; }
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
@@ -353,6 +362,29 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     M3_TRY(gemv(c.fmt_body, W.down, d.H, d.F, mlp, d.F, nullptr, 0, 0, h, d.H, 0,
                 M3_EPI_RESIDUAL, h, d.H, dn));
   }
+  // The reference's draw (top_k > 0): guidance over (conditional,
+  // unconditional) row pairs, top-k, Gumbel-argmax; one draw per song, left
+  // as a one-entry winner record per row for the same consumers.
+  const bool guided = c.top_k > 0;
+  auto guided_draw = [&](const float* lg, int V, uint32_t draw, int32_t base, Best* part) {
+    CfgDesc g{};
+    g.logits = lg;
+    g.S = B / 2;
+    g.V = V;
+    g.ldl = V;
+    g.scale = c.cfg_scale;
+    g.top_k = c.top_k;
+    g.seed = c.seed;
+    g.frame_dev = frame;
+    g.draw = draw;
+    g.temperature = c.temperature;
+    g.index_base = base;
+    g.part = part;
+    g.out_stride = 1;
+    g.vec4 = V % 4 == 0;
+    ++ph;
+    return sink.cfg_draw(g);
+  };
   // ---- sliced lm_head; its epilogue adds the Gumbel noise of draw 0 and
   // leaves each row block's winner; the draw completes in the next consumer
   SampleEpi sem{c.seed, frame, 0u, c.temperature, c.vocab_base, c.vocab_base,
@@ -361,7 +393,8 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   lm.x = p_h;
   p_sem = ph;
   M3_TRY(gemv(c.fmt_lm, m->lm_head, d.V0, d.H, h, d.H, m->final_norm, 0, 0, logits, d.V0, 1,
-              M3_EPI_NONE, nullptr, 0, lm, &sem));
+              M3_EPI_NONE, nullptr, 0, lm, guided ? nullptr : &sem));
+  if (guided) M3_TRY(guided_draw(logits, d.V0, 0u, c.vocab_base, part_sem));
   // ---- depth decoder ----
   Prod pin;
   pin.x = p_h;
@@ -375,7 +408,7 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     gp.u = u;
     gp.emb = j == 1 ? m->emb1 : m->emb[j - 2];
     gp.part = j == 1 ? part_sem : part_dep;
-    gp.nparts = j == 1 ? n_blocks(d.V0) : n_blocks(d.CV);
+    gp.nparts = guided ? 1 : (j == 1 ? n_blocks(d.V0) : n_blocks(d.CV));
     gp.index_base = j == 1 ? c.vocab_base : 0;
     gp.code_base = j == 1 ? c.vocab_base : 0;
     gp.n_codes = j == 1 ? c.n_slice : c.code_vocab;
@@ -419,7 +452,8 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     hp.x = p_hd;
     p_dep = ph;
     M3_TRY(gemv(c.fmt_depth, m->heads[j - 1], d.CV, d.D, hd, d.D, m->d_final_norm, 0, 0, dlogits,
-                d.CV, 1, M3_EPI_NONE, nullptr, 0, hp, &dep));
+                d.CV, 1, M3_EPI_NONE, nullptr, 0, hp, guided ? nullptr : &dep));
+    if (guided) M3_TRY(guided_draw(dlogits, d.CV, (uint32_t)j, 0, part_dep));
   }
   // ---- last draw, feedback, code ring, frame counter ----
   FeedbackTags ft;
@@ -430,7 +464,7 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     ft.h_out = h_plain;
     ft.seq = reinterpret_cast<uint32_t*>(S + L.seq);
   }
-  M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, n_blocks(d.CV),
+  M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, guided ? 1 : n_blocks(d.CV),
                        c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame, ft));
   return M3_OK;
 }
@@ -712,7 +746,7 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   // one frame kernel per body format: bf16, int8-row or fp8-row body and the
   // same lm_head format, int8-g128 depth
   const m3_config& c = model->cfg;
-  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128)
+  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128 || c.top_k > 0)
     return M3_ERR_FORMAT;
   // row-block winners carry their column in 16 bits next to the tag
   if (c.n_slice > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;

@@ -130,6 +130,7 @@ struct CfgDesc {
   int32_t* out;
   int out_stride;
   int vec4;             // logits rows 16-byte aligned (float4 loads)
+  Best* part;           // non-null: write {0, column} to part[2s], part[2s+1] instead of ids
 };
 hipError_t launch_cfg_draw(const CfgDesc& d, hipStream_t s);
 

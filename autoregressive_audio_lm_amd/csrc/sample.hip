@@ -231,6 +231,20 @@ __device__ __forceinline__ int column_ranks(const bool (&f)[G][W], int (&start)[
   return base;
 }
 
+// The song's draw (column j) to both of its rows: the absolute id, or, for the
+// frame's consumers (the gather prologue, the frame end), a one-entry winner
+// record {0, j} per row.
+__device__ __forceinline__ void cfg_write(const CfgDesc& d, int s, int j) {
+  if (d.part) {
+    d.part[2 * s] = Best{0.0f, j};
+    d.part[2 * s + 1] = Best{0.0f, j};
+    return;
+  }
+  const int32_t id = d.ids ? d.ids[j] : d.index_base + j;
+  d.out[(size_t)(2 * s) * d.out_stride] = id;
+  d.out[(size_t)(2 * s + 1) * d.out_stride] = id;
+}
+
 // Search state shared by both phases of the kernel.
 struct CfgSearch {
   uint32_t T;   // lower bound of the k-th largest key
@@ -344,11 +358,7 @@ __device__ __forceinline__ void cfg_finish(const CfgDesc& d, int s, const uint32
   bz = sh.wbest[lw].z;
   bj = sh.wbest[lw].j;
   best_row16(bz, bj);
-  if (tid == 0) {
-    const int32_t id = d.ids ? d.ids[bj] : d.index_base + bj;
-    d.out[(size_t)(2 * s) * d.out_stride] = id;
-    d.out[(size_t)(2 * s + 1) * d.out_stride] = id;
-  }
+  if (tid == 0) cfg_write(d, s, bj);
 }
 
 template <int E>
@@ -405,11 +415,7 @@ __global__ __launch_bounds__(kCfgThreads) void cfg_topk_kernel(CfgDesc d) {
   int par = 0;
   const int n = block_sum3(nv, 0, 0, sh, par).x;
   if (n == 0) {   // nothing to draw from: the first column's id
-    if (tid == 0) {
-      const int32_t id0 = d.ids ? d.ids[0] : d.index_base;
-      d.out[(size_t)(2 * s) * d.out_stride] = id0;
-      d.out[(size_t)(2 * s + 1) * d.out_stride] = id0;
-    }
+    if (tid == 0) cfg_write(d, s, 0);
     return;
   }
   const int kk = d.top_k < n ? d.top_k : n;

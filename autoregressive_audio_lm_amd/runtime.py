@@ -12,7 +12,9 @@ from ._lib import check, lib
 
 
 def make_config(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int = 0,
-                temperature: float = 1.0) -> _lib.Config:
+                temperature: float = 1.0, cfg_scale: float = 1.5, top_k: int = 0) -> _lib.Config:
+    """top_k == 0: one draw per row; top_k > 0: the reference's draw over
+    (conditional, unconditional) row pairs with guidance cfg_scale."""
     return _lib.Config(
         hidden=cfg["H"], n_layers=cfg["n_layers"], n_heads=cfg["n_heads"],
         n_kv_heads=cfg["n_kv_heads"], head_dim=cfg["head_dim"], ffn=cfg["F"],
@@ -20,7 +22,8 @@ def make_config(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int
         d_layers=cfg["d_layers"], d_heads=cfg["d_heads"], d_head_dim=cfg["d_head_dim"],
         d_ffn=cfg["Fd"], n_codebooks=cfg["n_codebooks"], code_vocab=cfg["code_vocab"],
         fmt_body=fmt_body, fmt_lm=fmt_lm, fmt_depth=fmt_depth, eps=float(cfg["eps"]),
-        temperature=float(temperature), seed=int(seed))
+        temperature=float(temperature), seed=int(seed), cfg_scale=float(cfg_scale),
+        top_k=int(top_k))
 
 
 def frame_weight_bytes(c: _lib.Config) -> int:
@@ -36,7 +39,7 @@ class DecodeModel:
     packing."""
 
     def __init__(self, md: dict, seed: int = 0, temperature: float = 1.0,
-                 free_sources: bool = False):
+                 free_sources: bool = False, cfg_scale: float = 1.5, top_k: int = 0):
         cfg = md["cfg"]
         # the C side reads host arrays of these lengths from the config
         nsteps = cfg["n_codebooks"] - 1
@@ -46,7 +49,8 @@ class DecodeModel:
             raise ValueError("model arrays do not match the config's layer and codebook counts")
         self.cfg_dict = cfg
         self.fmt_body, self.fmt_lm, self.fmt_depth = md["fmt_body"], md["fmt_lm"], md["fmt_depth"]
-        self.config = make_config(cfg, self.fmt_body, self.fmt_lm, self.fmt_depth, seed, temperature)
+        self.config = make_config(cfg, self.fmt_body, self.fmt_lm, self.fmt_depth, seed, temperature,
+                                  cfg_scale, top_k)
         self._keep = []
 
         def keep(t):

@@ -234,6 +234,15 @@ typedef struct {
   int fmt_body, fmt_lm, fmt_depth;
   float eps, temperature;
   uint64_t seed;
+  /* The frame's draws.  top_k == 0: one Gumbel-argmax draw per row (the
+   * benchmark configuration).  top_k > 0: the reference's draw
+   * (DiffSynth-Studio MiniMax-Music3 stage 2: guidance u + cfg_scale (c - u)
+   * over each (conditional, unconditional) row pair, top-k, multinomial), as
+   * m3_cfg_topk_draw: rows 2s and 2s+1 form song s (B even), every one of the
+   * 8 draws is made once per song and both rows take it.  Eager and graph
+   * frames only; n_slice and code_vocab <= M3_MAX_V_CFG. */
+  float cfg_scale;
+  int top_k;
 } m3_config;
 
 typedef struct {

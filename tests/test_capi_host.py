@@ -155,6 +155,14 @@ def test_frame_layout_and_refusals(L):
     assert L.m3_frame_layout_get(ctypes.byref(c2), 1, ctypes.byref(lay)) == _lib.M3_ERR_FORMAT
     c3 = make_config(dict(cfg, head_dim=64), **configs.PRESETS["A"])
     assert L.m3_frame_layout_get(ctypes.byref(c3), 1, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
+    # the reference's draw: rows come in (conditional, unconditional) pairs
+    g = make_config(cfg, **configs.PRESETS["A"], top_k=50)
+    assert L.m3_frame_layout_get(ctypes.byref(g), 4, ctypes.byref(lay)) == 0
+    assert L.m3_frame_layout_get(ctypes.byref(g), 3, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
+    g_bad = make_config(cfg, **configs.PRESETS["A"], top_k=-1)
+    assert L.m3_frame_layout_get(ctypes.byref(g_bad), 2, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
+    g_nan = make_config(cfg, **configs.PRESETS["A"], top_k=50, cfg_scale=float("nan"))
+    assert L.m3_frame_layout_get(ctypes.byref(g_nan), 2, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
     m = _lib.Model(cfg=c)
     codes = ctypes.c_void_p(0x300000)
     assert L.m3_decode_frame_weights(ctypes.byref(m), FAKE, 1, codes, None, None) == _lib.M3_ERR_NULL

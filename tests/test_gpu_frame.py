@@ -182,3 +182,65 @@ def test_persistent_frame_equals_eager(small, B):
         assert int(pers.err.item()) == 0
         _same_frame(eager, pers)
     pers.release()
+
+
+# ------------------------------------------------ the reference's draw ----
+@pytest.fixture(scope="module")
+def guided():
+    """The frame in the reference's draw mode (DiffSynth-Studio MiniMax-Music3
+    stage 2: guidance 1.5 over each (conditional, unconditional) row pair,
+    top-k 50, one draw per song taken by both rows)."""
+    cfg = configs.config("frame-small")
+    md_dev = synth.make_model(cfg, **configs.PRESETS["A"], seed=23, device="cpu")
+    md_np = synth.model_to_numpy(md_dev)
+    dm = runtime.DecodeModel(_to(md_dev, DEV), seed=5, temperature=1.0, cfg_scale=1.5, top_k=50)
+    om = O.OracleModel(md_np, cfg_scale=1.5, top_k=50)
+    return cfg, dm, om
+
+
+def test_guided_frames_match_oracle(guided):
+    cfg, dm, om = guided
+    B = 4
+    x0 = synth.activations(B, cfg["H"], 61)
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=7)
+    x = synth.bits(x0)
+    for f in range(7, 10):
+        st.decode()
+        torch.cuda.synchronize()
+        codes = st.codes.cpu().numpy()
+        assert np.array_equal(codes[0::2], codes[1::2])
+        o_codes, o_xn, o_tr = O.decode_frame(om, x, seed=5, frame=f, trace=True)
+        _check_frame(codes, synth.bits(st.x), synth.bits(st.h), o_codes, o_xn, o_tr)
+        if not np.array_equal(codes, o_codes):
+            break
+        x = o_xn
+        st.x.copy_(synth.from_bits(x, DEV))
+    assert int(st.frame.item()) >= 8
+
+
+def test_guided_graph_replay_equals_eager_and_persistent_refused(guided):
+    from autoregressive_audio_lm_amd import _lib
+    cfg, dm, om = guided
+    B = 6
+    x0 = synth.activations(B, cfg["H"], 62).to(DEV)
+    eager = runtime.FrameState(dm, B, x0, frame0=0)
+    seq = []
+    for _ in range(4):
+        eager.decode()
+        seq.append(eager.codes.clone())
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    graphed = runtime.FrameState(dm, B, x0, frame0=0)
+    with torch.cuda.stream(s):
+        graphed.capture(s)
+        for k in range(4):
+            graphed.replay(s)
+            s.synchronize()
+            assert torch.equal(graphed.codes, seq[k])
+            torch.cuda.synchronize()
+    assert torch.equal(eager.x, graphed.x)
+    graphed.release()
+    with pytest.raises(_lib.M3Error):
+        runtime.FrameState(dm, B, x0).persistent_create()
+    with pytest.raises(_lib.M3ValueError):
+        runtime.FrameState(dm, 3, x0[:3])
