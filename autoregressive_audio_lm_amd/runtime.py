@@ -110,6 +110,14 @@ class DecodeModel:
     def weight_bytes(self) -> int:
         return frame_weight_bytes(self.config)
 
+    def set_draw(self, cfg_scale: float = 1.5, top_k: int = 0) -> None:
+        """Switch the frame's draws (per row, or with top_k > 0 the
+        reference's draw over row pairs) for frame states made from now on;
+        the packed weights are shared."""
+        for c in (self.config, self.model.cfg):
+            c.cfg_scale = float(cfg_scale)
+            c.top_k = int(top_k)
+
 
 class FrameState:
     """Caller-owned frame state (device) for B lockstep rows, plus the [B, 8]

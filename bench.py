@@ -397,9 +397,21 @@ def main():
         return pt
 
     sweep = []
+    guided = []
     if not args.no_sweep:
         for B in (2, 6, 16):
             sweep.append(point(args.preset, B, dm, fbytes))
+        # the frame with the reference's draw (guidance 1.5 over each row pair,
+        # top-k 50, one draw per song): graph-replayed frames
+        dm.set_draw(1.5, 50)
+        for B in (2, 6, 16):
+            st_g, ms_g, _ = time_frames(dm, cfg, B, max(20, args.steps // 4), 3, stream, args.seed)
+            st_g.release()
+            guided.append({"preset": args.preset, "B": B, "songs": B // 2, "path": "graph",
+                           "ms_per_frame": round(ms_g, 4), "frames_per_s": round(1e3 / ms_g, 2),
+                           "GB_s": round(fbytes * 1e3 / ms_g / 1e9, 1)})
+            log(f"[bench] guided {guided[-1]}")
+        dm.set_draw(1.5, 0)
         del dm
         torch.cuda.empty_cache()
         for other in [q for q in ("A", "B", "C") if q != args.preset]:
@@ -450,6 +462,7 @@ def main():
         "sweep": sweep,
         "cfg_draw": {"kernel": "cfg_topk_kernel (guidance 1.5, top-k 50, Gumbel-argmax; "
                                "one workgroup per song)", "points": cfg_draw},
+        "guided_frame": guided,
         "gpu": f"{props.name} {props.gcnArchName} x{props.multi_processor_count} CU",
     }
     print(json.dumps(out), flush=True)
