@@ -626,6 +626,39 @@ int m3_cfg_topk_draw(const float* logits, int n_songs, int V, int ldl, float cfg
   return hip_status(launch_cfg_draw(d, static_cast<hipStream_t>(stream)));
 }
 
+int m3_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const float* gamma, float eps,
+                    uint16_t* a, int lda, void* stream) {
+  if (!x || !gamma || !a) return M3_ERR_NULL;
+  if (M < 1 || M > M3_MAX_M_PREFILL || K < 8 || K % 8 != 0 || ldx < K || lda < K) return M3_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return M3_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(a, 16) || !aligned(gamma, 16) || ldx % 8 || lda % 8)
+    return M3_ERR_ALIGN;
+  if (overlap(x, ((size_t)(M - 1) * ldx + K) * 2, a, ((size_t)(M - 1) * lda + K) * 2))
+    return M3_ERR_ALIAS;
+  return hip_status(
+      launch_rmsnorm_rows(x, M, K, ldx, gamma, eps, a, lda, static_cast<hipStream_t>(stream)));
+}
+
+int m3_prefill_gemm(const void* w, int N, int K, const uint16_t* a, int M, int lda, void* y,
+                    int ldy, int out_dtype, int epi, const uint16_t* res, int ldr, void* stream) {
+  if (!w || !a || !y) return M3_ERR_NULL;
+  if (out_dtype != M3_OUT_BF16 && out_dtype != M3_OUT_F32) return M3_ERR_FORMAT;
+  if (epi != M3_EPI_NONE && epi != M3_EPI_SWIGLU && epi != M3_EPI_RESIDUAL) return M3_ERR_FORMAT;
+  if (epi != M3_EPI_NONE && out_dtype != M3_OUT_BF16) return M3_ERR_FORMAT;
+  if (epi == M3_EPI_RESIDUAL && !res) return M3_ERR_NULL;
+  if (M < 1 || M > M3_MAX_M_PREFILL || N < 1 || K < 64 || K % 64 != 0 || lda < K) return M3_ERR_SHAPE;
+  if (epi == M3_EPI_SWIGLU && N % 2 != 0) return M3_ERR_SHAPE;
+  const int ncols = epi == M3_EPI_SWIGLU ? N / 2 : N;
+  if (ldy < ncols || (epi == M3_EPI_RESIDUAL && ldr < N)) return M3_ERR_SHAPE;
+  if ((size_t)n_blocks(N) * block_bytes(M3_BF16, K) >= ((size_t)1 << 31)) return M3_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(a, 16) || !aligned(y, 16) || lda % 8) return M3_ERR_ALIGN;
+  const size_t esz = out_dtype == M3_OUT_F32 ? 4 : 2;
+  if (overlap(a, ((size_t)(M - 1) * lda + K) * 2, y, ((size_t)(M - 1) * ldy + ncols) * esz))
+    return M3_ERR_ALIAS;
+  PrefillDesc d{w, N, K, a, M, lda, y, ldy, out_dtype == M3_OUT_F32, epi, res, ldr};
+  return hip_status(launch_prefill_gemm(d, static_cast<hipStream_t>(stream)));
+}
+
 uint64_t m3_frame_weight_bytes(const m3_config* c) {
   if (!c) return 0;
   const Dims d = dims_of(*c);

@@ -134,6 +134,22 @@ struct CfgDesc {
 };
 hipError_t launch_cfg_draw(const CfgDesc& d, hipStream_t s);
 
+// ---- prompt prefill (prefill.hip) ---------------------------------------------
+// Y[M, N] = epi(A[M, K] . W^T), W packed bf16 (m3_pack), K % 64 == 0.
+struct PrefillDesc {
+  const void* w;
+  int N, K;
+  const uint16_t* a;
+  int M, lda;
+  void* y;
+  int ldy, out_f32, epi;
+  const uint16_t* res;
+  int ldr;
+};
+hipError_t launch_prefill_gemm(const PrefillDesc& d, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const float* gamma,
+                               float eps, uint16_t* a, int lda, hipStream_t s);
+
 // ---- frame helpers -------------------------------------------------------------
 // audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)
 // Final draw of the last codebook from the head's per-block winners, then the

@@ -14,7 +14,7 @@ from . import _lib
 from ._lib import (BF16, I8ROW, I8G128, FP8ROW, EPI_NONE, EPI_SWIGLU, EPI_RESIDUAL, OUT_BF16, OUT_F32,
                    PACK_GLU_INTERLEAVE, check, lib)
 
-__all__ = ["packed_bytes", "pack", "rmsnorm_gemv", "gemv_i8row", "gemv_i8g128", "gemv_fp8row", "gemv", "cfg_topk_draw",
+__all__ = ["packed_bytes", "pack", "rmsnorm_gemv", "gemv_i8row", "gemv_i8g128", "gemv_fp8row", "gemv", "cfg_topk_draw", "rmsnorm_rows", "prefill_gemm",
            "lmhead_sliced", "gumbel_workspace_bytes", "gumbel_argmax", "BF16", "I8ROW", "I8G128", "FP8ROW",
            "EPI_NONE", "EPI_SWIGLU", "EPI_RESIDUAL", "OUT_BF16", "OUT_F32", "PACK_GLU_INTERLEAVE"]
 
@@ -158,3 +158,35 @@ def cfg_topk_draw(logits: torch.Tensor, scale: float = 1.5, top_k: int = 50, see
     check(lib().m3_cfg_topk_draw(_ptr(logits), B // 2, V, logits.stride(0), float(scale),
                                  int(top_k), ctypes.byref(p), _ptr(out), _stream(stream)))
     return out
+
+
+def rmsnorm_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                 a: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_rmsnorm_rows: bf16 [M, K] -> bf16 [M, K] (the prefill's norm)."""
+    for t, n in ((x, "x"), (gamma, "gamma"), (a, "a")):
+        _cuda(t, n)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a bf16 [M, K] tensor")
+    M, K = x.shape
+    if a is None:
+        a = torch.empty(M, K, dtype=torch.bfloat16, device=x.device)
+    check(lib().m3_rmsnorm_rows(_ptr(x), M, K, x.stride(0), _ptr(gamma), float(eps), _ptr(a),
+                                a.stride(0), _stream(stream)))
+    return a
+
+
+def prefill_gemm(packed: torch.Tensor, N: int, K: int, a: torch.Tensor, y: torch.Tensor | None = None,
+                 out_dtype: int = OUT_BF16, epi: int = EPI_NONE,
+                 residual: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_prefill_gemm: y[M, N] (N/2 for SwiGLU) = epi(a[M, K] . W^T)."""
+    for t, n in ((packed, "packed"), (a, "a"), (y, "y"), (residual, "residual")):
+        _cuda(t, n)
+    M = a.shape[0]
+    ncols = N // 2 if epi == EPI_SWIGLU else N
+    if y is None:
+        dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+        y = torch.empty(M, ncols, dtype=dt, device=a.device)
+    ldr = residual.stride(0) if residual is not None else 0
+    check(lib().m3_prefill_gemm(_ptr(packed), N, K, _ptr(a), M, a.stride(0), _ptr(y), y.stride(0),
+                                out_dtype, epi, _ptr(residual), ldr, _stream(stream)))
+    return y

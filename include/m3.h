@@ -58,6 +58,7 @@ enum { M3_PACK_GLU_INTERLEAVE = 1 };
 #define M3_MAX_B_SAMPLE 65535 /* rows per sampler call                      */
 #define M3_MAX_SONGS_CFG 32767 /* songs (row pairs) per CFG draw call       */
 #define M3_MAX_V_CFG 32768   /* columns per CFG draw call                   */
+#define M3_MAX_M_PREFILL 65536 /* rows per prefill GEMM / RMSNorm call      */
 
 const char* m3_status_str(int status);
 /* library version string (host) */
@@ -224,6 +225,31 @@ int m3_gumbel_argmax(const float* logits, int B, int V, int ldl,
  * M3_ERR_HIP if the launch fails. */
 int m3_cfg_topk_draw(const float* logits, int n_songs, int V, int ldl, float cfg_scale,
                      int top_k, const m3_sample_params* params, int32_t* out, void* stream);
+
+/* ---- prompt prefill --------------------------------------------------------- */
+/* A prompt of about 300 tokens for each of the two CFG rows ("MiniMax Music 3,
+ * local"; TensorFold PR #987: 300 tokens a CFG row) runs every body matrix on
+ * 600 rows at once: a dense contraction on the matrix cores.
+ *
+ * m3_rmsnorm_rows: a[m, k] = bf16((x[m, k] * r_m) * gamma[k]) with
+ * r_m = 1 / sqrt(mean_k x[m, k]^2 + eps) in fp32 (the GEMV prologue's
+ * arithmetic).  1 <= M <= M3_MAX_M_PREFILL; K % 8 == 0; ldx, lda >= K and
+ * multiples of 8; x, a, gamma 16-byte aligned; x must not overlap a.
+ *
+ * m3_prefill_gemm: y[m, n] = epi( sum_k W[n, k] * a[m, k] ), fp32 accumulation
+ * on v_mfma_f32_16x16x32_bf16, W packed bf16 by m3_pack (gate/up interleaved
+ * for M3_EPI_SWIGLU).  Epilogues and outputs as m3_rmsnorm_gemv (SwiGLU and
+ * residual write bf16; the residual may be y itself).  1 <= M <=
+ * M3_MAX_M_PREFILL; N >= 1 (even for SwiGLU); K % 64 == 0; lda >= K, a
+ * multiple of 8; ldy >= N (N/2 for SwiGLU); ldr >= N; W, a, y 16-byte
+ * aligned; a must not overlap y.  Errors: M3_ERR_NULL, M3_ERR_SHAPE,
+ * M3_ERR_ALIGN, M3_ERR_FORMAT, M3_ERR_ALIAS before any launch; M3_ERR_HIP if
+ * the launch fails. */
+int m3_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const float* gamma, float eps,
+                    uint16_t* a, int lda, void* stream);
+int m3_prefill_gemm(const void* packed_bf16, int N, int K, const uint16_t* a, int M, int lda,
+                    void* y, int ldy, int out_dtype, int epi, const uint16_t* residual, int ldr,
+                    void* stream);
 
 /* ---- one decode frame ------------------------------------------------------ */
 typedef struct {

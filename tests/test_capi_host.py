@@ -114,6 +114,29 @@ def test_sampler_refusals(L):
     assert L.m3_gumbel_argmax(*arg(p=bad)) == _lib.M3_ERR_SHAPE
 
 
+def test_prefill_refusals(L):
+    arg = lambda **k: (k.get("w", FAKE), k.get("N", 256), k.get("K", 512), k.get("a", FAKE2),
+                       k.get("M", 600), k.get("lda", 512), k.get("y", ctypes.c_void_p(0x4000000)),
+                       k.get("ldy", 256), k.get("out", 0), k.get("epi", 0), k.get("res", None),
+                       k.get("ldr", 0), None)
+    assert L.m3_prefill_gemm(*arg(w=None)) == _lib.M3_ERR_NULL
+    assert L.m3_prefill_gemm(*arg(M=0)) == _lib.M3_ERR_SHAPE
+    assert L.m3_prefill_gemm(*arg(K=480, lda=480)) == _lib.M3_ERR_SHAPE     # K % 64
+    assert L.m3_prefill_gemm(*arg(lda=256)) == _lib.M3_ERR_SHAPE
+    assert L.m3_prefill_gemm(*arg(ldy=128)) == _lib.M3_ERR_SHAPE
+    assert L.m3_prefill_gemm(*arg(epi=1, N=255)) == _lib.M3_ERR_SHAPE      # SwiGLU pairs
+    assert L.m3_prefill_gemm(*arg(epi=2)) == _lib.M3_ERR_NULL               # residual missing
+    assert L.m3_prefill_gemm(*arg(epi=1, out=1)) == _lib.M3_ERR_FORMAT
+    assert L.m3_prefill_gemm(*arg(out=7)) == _lib.M3_ERR_FORMAT
+    assert L.m3_prefill_gemm(*arg(a=ctypes.c_void_p(0x900008))) == _lib.M3_ERR_ALIGN
+    assert L.m3_prefill_gemm(*arg(y=FAKE2)) == _lib.M3_ERR_ALIAS
+    g = ctypes.c_void_p(0x5000000)
+    assert L.m3_rmsnorm_rows(None, 4, 64, 64, g, 1e-6, FAKE2, 64, None) == _lib.M3_ERR_NULL
+    assert L.m3_rmsnorm_rows(FAKE, 4, 60, 64, g, 1e-6, FAKE2, 64, None) == _lib.M3_ERR_SHAPE
+    assert L.m3_rmsnorm_rows(FAKE, 4, 64, 64, g, -1.0, FAKE2, 64, None) == _lib.M3_ERR_SHAPE
+    assert L.m3_rmsnorm_rows(FAKE, 4, 64, 64, g, 1e-6, FAKE, 64, None) == _lib.M3_ERR_ALIAS
+
+
 def test_cfg_draw_refusals(L):
     p = _lib.SampleParams(0, 0, None, 0, 1.0, 0, None, 0, 0, None)
     arg = lambda **k: (k.get("lg", FAKE), k.get("S", 4), k.get("V", 5000), k.get("ldl", 5000),
