@@ -651,6 +651,7 @@ int m3_prefill_gemm(const void* w, int N, int K, const uint16_t* a, int M, int l
   const int ncols = epi == M3_EPI_SWIGLU ? N / 2 : N;
   if (ldy < ncols || (epi == M3_EPI_RESIDUAL && ldr < N)) return M3_ERR_SHAPE;
   if ((size_t)n_blocks(N) * block_bytes(M3_BF16, K) >= ((size_t)1 << 31)) return M3_ERR_SHAPE;
+  if (((size_t)(M - 1) * lda + K) * 2 >= ((size_t)1 << 31)) return M3_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(a, 16) || !aligned(y, 16) || lda % 8) return M3_ERR_ALIGN;
   const size_t esz = out_dtype == M3_OUT_F32 ? 4 : 2;
   if (overlap(a, ((size_t)(M - 1) * lda + K) * 2, y, ((size_t)(M - 1) * ldy + ncols) * esz))

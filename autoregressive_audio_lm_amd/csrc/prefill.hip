@@ -7,14 +7,15 @@
 // dense contraction: at 600 rows a bf16 weight byte meets 600 multiply-adds,
 // above the matrix cores' ridge, so the bound is the MFMA rate, not HBM.
 //
-// GEMM.  A workgroup of 4 waves computes a 128 x 128 tile of Y; wave w holds
-// rows 64 (w & 1) .. +63 and columns 64 (w >> 1) .. +63 as 4 x 4
-// accumulators of v_mfma_f32_16x16x32_bf16.  The weights stay in the packed
-// tile layout of m3_pack: one 16-byte load per lane of a 1 KB tile is
-// exactly the MFMA B operand (column = row l % 16 of the block, k = 8 (l /
-// 16) .. +7), so weight fragments go from memory straight to registers.  The
-// A tile (128 rows x 64 K) is staged in LDS, double-buffered; the next K
-// step's A and weight loads are issued before the current step's MFMAs.
+// GEMM.  A workgroup of 4 waves computes a 64 x 128 or 64 x 256 tile of Y as
+// accumulators of v_mfma_f32_16x16x32_bf16; each wave owns a strip of
+// columns over all 64 rows.  The weights stay in the packed tile layout of
+// m3_pack: one 16-byte load per lane of a 1 KB tile is exactly the MFMA B
+// operand (column = row l % 16 of the block, k = 8 (l / 16) .. +7), so weight
+// fragments go from memory straight to registers, each loaded by one wave.
+// The A tile (64 rows x 64 K) is staged in LDS (XOR-swizzled, free of bank
+// conflicts), shared by the 4 waves and double-buffered; loads run two K
+// steps ahead of the MFMAs.
 // Tile order: workgroups are handed to the 8 XCDs in turn, so the mapping
 // puts the M tiles of one N tile on one XCD in neighbouring slots, where
 // they share that XCD's L2 for the weight tiles.
@@ -26,21 +27,32 @@
 namespace m3 {
 namespace {
 
-constexpr int kPM = 128, kPN = 128, kPK = 64;   // workgroup tile of Y, K step
-constexpr int kPThreads = 256;                  // 4 waves: 2 (M) x 2 (N) of 64 x 64
-constexpr int kALd = kPK + 8;                   // LDS row stride of the A tile (bf16)
+constexpr int kPThreads = 256;                  // 4 waves
+
+// A tile in LDS: rows of 32 KT bf16 (the K step) as 16-byte chunks, chunk ch
+// of row r stored at position ch ^ (r % chunks): the 16 lanes of an MFMA
+// fragment read (rows r .. r + 15, one chunk) and the 8 lanes that store one
+// row hit distinct banks.
+template <int KT>
+__device__ __forceinline__ int a_off(int r, int ch) {
+  constexpr int CH = 4 * KT;
+  return r * (8 * CH) + ((ch ^ (r & (CH - 1))) * 8);
+}
+constexpr int kStages = 3;                      // K steps held in registers (2 in flight)
 
 struct PrefillParams {
   const uint16_t* a;
   int lda;
   const uint8_t* w;
   uint32_t wbytes;
+  uint32_t abytes;      // bytes of A from its first row through the end of row M - 1
   uint32_t bbytes;      // bytes per packed row block
   int M, N, K;
   void* y;
   int ldy, out_f32, epi;
   const uint16_t* res;
   int ldr;
+  int vec;              // y (and the residual) rows allow 16-byte accesses
   int mtiles, ntiles;
 };
 
@@ -53,125 +65,231 @@ __device__ __forceinline__ void tile_of(const PrefillParams& p, int& mt, int& nt
   nt = logical / p.mtiles;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kPThreads) void prefill_gemm_kernel(PrefillParams p) {
-  __shared__ __align__(16) uint16_t As[2][kPM * kALd];
+// A (16 MT WGM) x (16 WNB WGN) tile per workgroup, WGM x WGN = 4 waves.  Wave
+// w = (wm, wn) = (w % WGM, w / WGM) holds MT x WNB accumulator tiles of 16 x
+// 16: rows 16 MT wm .. +16 MT - 1, columns 16 WNB wn .. +16 WNB - 1.  Each A
+// fragment read from LDS feeds WNB MFMAs and each weight fragment MT; with
+// WGM = 1 no two waves load the same weight fragment.
+//
+// Pipeline over K steps of 32 KT: registers hold the weight fragments and the A
+// chunks of three steps; at step ks the loads of step ks + 2 are issued, the
+// A chunks of step ks + 1 are written to the LDS buffer that step ks - 1 read,
+// and the MFMAs of step ks read LDS buffer ks & 1.  The step count is rounded
+// up to a multiple of 3; the extra steps load zeros (offsets past the end of
+// the buffers) and add nothing.  A rows past M read zeros the same way.
+template <int WGM, int MT, int WNB, int KT, int EPI>
+__global__ __launch_bounds__(kPThreads, 2) void prefill_gemm_kernel(PrefillParams p) {
+  constexpr int WGN = 4 / WGM;
+  constexpr int BM = 16 * MT * WGM, BN = 16 * WNB * WGN;
+  constexpr int PK = 32 * KT, CH = PK / 8;       // K step; 16-byte chunks per A row
+  constexpr int AC = BM * CH / kPThreads;        // A chunks per thread per K step
+  constexpr int KG = MT <= 4 ? 2 : 1;            // K tiles whose A fragments are read at once
+  static_assert(AC * kPThreads == BM * CH && KT % KG == 0, "tile shape");
+  constexpr int TR = 16 * MT, TC = 16 * WNB, SLD = TC + 8;   // a wave's tile; its staging row stride
+  constexpr int LDS_A = 2 * BM * PK, LDS_E = 4 * TR * SLD;
+  __shared__ __align__(16) uint16_t lds[LDS_A > LDS_E ? LDS_A : LDS_E];   // A buffers, then the epilogue
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   int mt, nt;
   tile_of(p, mt, nt);
-  const int m0 = mt * kPM, n0 = nt * kPN;
+  const int m0 = mt * BM, n0 = nt * BN;
   const __amdgpu_buffer_rsrc_t wr = weight_rsrc(p.w, p.wbytes);
-  const int rb0 = (n0 + wn * 64) >> 4;          // this wave's first row block
-  const int nk = p.K / kPK;
-
-  // A tile (128 x 64 bf16): 1024 chunks of 16 B, 4 per thread, rows past M zero
-  uint4 areg[4];
-  auto load_a = [&](int ks) {
+  const __amdgpu_buffer_rsrc_t ar = weight_rsrc(p.a, p.abytes);
+  // this wave's first row block of W; a block past N reads zeros
+  const uint32_t wbase = (uint32_t)((n0 >> 4) + WNB * wn) * p.bbytes + (uint32_t)lane * 16u;
+  const uint32_t woob = p.wbytes + (uint32_t)lane * 16u;
+  uint32_t abase[AC];                            // byte offset of this thread's A chunks at K step 0
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < AC; ++i) {
+    const int c = tid + i * kPThreads, m = m0 + c / CH;
+    abase[i] = m < p.M ? (uint32_t)m * (uint32_t)p.lda * 2u + (uint32_t)(c % CH) * 16u : p.abytes;
+  }
+  const int nk = p.K / PK;
+  const int nsteps = (nk + kStages - 1) / kStages * kStages;
+
+  uint4 wreg[kStages][WNB][KT];                  // [stage][row block][K tile]
+  uint4 areg[kStages][AC];
+  auto load = [&](int st, int ks) {
+    const bool in = ks < nk;
+#pragma unroll
+    for (int j = 0; j < WNB; ++j)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const uint32_t off = wbase + (uint32_t)j * p.bbytes + (uint32_t)(KT * ks + kt) * kTileBytes;
+        wreg[st][j][kt] = ldw<0>(wr, in ? off : woob, 0u);
+      }
+#pragma unroll
+    for (int i = 0; i < AC; ++i)
+      areg[st][i] = ldw<0>(ar, in ? abase[i] : p.abytes, (uint32_t)ks * (PK * 2));
+  };
+  auto store_a = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
       const int c = tid + i * kPThreads;
-      const int r = c >> 3, cc = c & 7;
-      const int m = m0 + r;
-      areg[i] = m < p.M ? *reinterpret_cast<const uint4*>(p.a + (size_t)m * p.lda + ks * kPK + cc * 8)
-                        : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&lds[buf * (BM * PK) + a_off<KT>(c / CH, c % CH)]) = areg[st][i];
     }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kPThreads;
-      const int r = c >> 3, cc = c & 7;
-      *reinterpret_cast<uint4*>(&As[buf][r * kALd + cc * 8]) = areg[i];
-    }
-  };
-  // weight fragments of K step ks: 4 row blocks x 2 tiles (block past N: zeros)
-  uint4 wcur[4][2], wnext[4][2];
-  auto load_w = [&](uint4 (&dst)[4][2], int ks) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const uint32_t off = (uint32_t)(rb0 + j) * p.bbytes + (uint32_t)(2 * ks + kt) * kTileBytes;
-        dst[j][kt] = ldw<2>(wr, (uint32_t)lane * 16u + off, 0u);
-      }
   };
 
-  f32x4_t acc[4][4];
+  // this lane's A fragment offsets (row 16 MT wm + lane % 16, K chunk 4 kt +
+  // lane / 16) in a buffer, for the K tiles of a step
+  int aoff[KT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < KT; ++kt) aoff[kt] = a_off<KT>(16 * MT * wm + (lane & 15), 4 * kt + (lane >> 4));
 
-  load_a(0);
-  load_w(wcur, 0);
-  store_a(0);
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) {
-      load_a(ks + 1);
-      load_w(wnext, ks + 1);
-    }
-    __syncthreads();               // A tile ks is in LDS; buffer cur^1 is free
+  f32x4_t acc[MT][WNB];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      bf16x8_t af[4];
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + (lane & 15);
-        af[i] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&As[cur][r * kALd + kt * 32 + 8 * (lane >> 4)]));
+    for (int j = 0; j < WNB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load(0, 0);
+  load(1, 1);
+  store_a(0, 0);
+  for (int k0 = 0; k0 < nsteps; k0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      const int ks = k0 + u;
+      load((u + 2) % kStages, ks + 2);
+      __builtin_amdgcn_sched_barrier(0);       // keep the loads ahead of this step's MFMAs
+      __syncthreads();             // A of step ks is in LDS; the other buffer is free
+      const uint16_t* at = &lds[(ks & 1) * (BM * PK)];
+      // the A fragments of KG K tiles are read before their MFMAs, so that
+      // LDS latency overlaps the matrix work instead of preceding each MFMA
+#pragma unroll
+      for (int k0t = 0; k0t < KT; k0t += KG) {
+        bf16x8_t af[KG][MT];
+#pragma unroll
+        for (int kt = 0; kt < KG; ++kt)
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            af[kt][i] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const uint4*>(at + i * 16 * PK + aoff[k0t + kt]));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kt = 0; kt < KG; ++kt)
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < WNB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  af[kt][i], __builtin_bit_cast(bf16x8_t, wreg[u][j][k0t + kt]), acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wcur[j][kt]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw, acc[i][j], 0, 0, 0);
-      }
-    }
-    if (more) {
-      store_a(cur ^ 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) wcur[j][kt] = wnext[j][kt];
+      store_a((u + 1) % kStages, (ks + 1) & 1);
     }
   }
 
   // epilogue: lane holds D[4 (l / 16) + q][l % 16] of each 16 x 16 tile
+  const int mw = m0 + 16 * MT * wm, nw = n0 + 16 * WNB * wn;   // this wave's tile origin
+  if constexpr (EPI == M3_EPI_NONE) {
+    if (p.out_f32) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < WNB; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
-        const int n = n0 + wn * 64 + j * 16 + (lane & 15);
-        const float v = acc[i][j][q];
-        if constexpr (EPI == M3_EPI_SWIGLU) {
-          // interleaved gate/up rows: columns 2c (gate) and 2c+1 (up) are
-          // neighbouring lanes; the even lane writes column c of the output
-          const float partner = dpp_f<0xB1>(v);
-          if ((lane & 1) == 0 && m < p.M && n + 1 < p.N) {
-            const float g = bf2f(f2bf(v)), u = bf2f(f2bf(partner));
-            const float s = g / (1.0f + expf(-g));
-            reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.ldy + (n >> 1)] = (uint16_t)f2bf(s * u);
+          for (int q = 0; q < 4; ++q) {
+            const int m = mw + i * 16 + 4 * (lane >> 4) + q, n = nw + j * 16 + (lane & 15);
+            if (m < p.M && n < p.N) reinterpret_cast<float*>(p.y)[(size_t)m * p.ldy + n] = acc[i][j][q];
           }
+      return;
+    }
+  }
+  // bf16 outputs: the wave's tile, rounded to bf16 (every epilogue starts
+  // from bf16(acc)), is staged in LDS and leaves as whole 16-byte row chunks,
+  // with the residual read the same way
+  __syncthreads();                 // every wave is done with the A buffers
+  uint16_t* stg = lds + wave * (TR * SLD);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        stg[(i * 16 + 4 * (lane >> 4) + q) * SLD + j * 16 + (lane & 15)] = (uint16_t)f2bf(acc[i][j][q]);
+  constexpr int CPR = TC / 8;      // 16-byte chunks per staged row
+#pragma unroll
+  for (int c = lane; c < TR * CPR; c += 64) {
+    const int r = c / CPR, ch = c % CPR;
+    const int m = mw + r, n = nw + ch * 8;
+    if (m >= p.M || n >= p.N) continue;
+    const uint4 v4 = *reinterpret_cast<const uint4*>(&stg[r * SLD + ch * 8]);
+    const uint32_t vw[4] = {v4.x, v4.y, v4.z, v4.w};
+    const bool whole = p.vec && n + 8 <= p.N;
+    if constexpr (EPI == M3_EPI_SWIGLU) {
+      // interleaved gate/up rows: staged columns 2t (gate) and 2t + 1 (up)
+      // give output column n / 2 + t
+      uint16_t* yo = reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.ldy + (n >> 1);
+      uint16_t o[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float g = bf2f(vw[t] & 0xffffu), u = bf2f(vw[t] >> 16);
+        o[t] = (uint16_t)f2bf((g / (1.0f + expf(-g))) * u);
+      }
+      if (whole) {
+        *reinterpret_cast<uint2*>(yo) = make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (n + 2 * t < p.N) yo[t] = o[t];
+      }
+    } else {
+      uint16_t* yo = reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.ldy + n;
+      uint32_t ow[4] = {vw[0], vw[1], vw[2], vw[3]};
+      if constexpr (EPI == M3_EPI_RESIDUAL) {
+        const uint16_t* ro = p.res + (size_t)m * p.ldr + n;
+        uint32_t rw[4];
+        if (whole) {
+          const uint4 r4 = *reinterpret_cast<const uint4*>(ro);
+          rw[0] = r4.x; rw[1] = r4.y; rw[2] = r4.z; rw[3] = r4.w;
         } else {
-          if (m < p.M && n < p.N) {
-            if (EPI == M3_EPI_RESIDUAL) {
-              const uint32_t o = f2bf(bf2f(p.res[(size_t)m * p.ldr + n]) + bf2f(f2bf(v)));
-              reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.ldy + n] = (uint16_t)o;
-            } else if (p.out_f32) {
-              reinterpret_cast<float*>(p.y)[(size_t)m * p.ldy + n] = v;
-            } else {
-              reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.ldy + n] = (uint16_t)f2bf(v);
-            }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t lo = n + 2 * t < p.N ? ro[2 * t] : 0u;
+            const uint32_t hi = n + 2 * t + 1 < p.N ? ro[2 * t + 1] : 0u;
+            rw[t] = lo | (hi << 16);
           }
         }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t lo = f2bf(bf2f(rw[t] & 0xffffu) + bf2f(vw[t] & 0xffffu));
+          const uint32_t hi = f2bf(bf2f(rw[t] >> 16) + bf2f(vw[t] >> 16));
+          ow[t] = lo | (hi << 16);
+        }
       }
+      if (whole) {
+        *reinterpret_cast<uint4*>(yo) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (n + k < p.N) yo[k] = (uint16_t)(ow[k >> 1] >> (16 * (k & 1)));
+      }
+    }
+  }
+}
+
+template <int WGM, int MT, int WNB, int KT>
+hipError_t launch_tile(PrefillParams p, hipStream_t s) {
+  constexpr int BM = 16 * MT * WGM, BN = 16 * WNB * (4 / WGM);
+  p.mtiles = (p.M + BM - 1) / BM;
+  p.ntiles = (p.N + BN - 1) / BN;
+  const int grid = p.mtiles * p.ntiles;
+  if (p.epi == M3_EPI_SWIGLU)
+    hipLaunchKernelGGL((prefill_gemm_kernel<WGM, MT, WNB, KT, M3_EPI_SWIGLU>), dim3(grid), dim3(kPThreads), 0, s, p);
+  else if (p.epi == M3_EPI_RESIDUAL)
+    hipLaunchKernelGGL((prefill_gemm_kernel<WGM, MT, WNB, KT, M3_EPI_RESIDUAL>), dim3(grid), dim3(kPThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefill_gemm_kernel<WGM, MT, WNB, KT, M3_EPI_NONE>), dim3(grid), dim3(kPThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// Tile shape, measured at 600 rows on the body shapes: 64 x 256 where that
+// still gives every CU a tile, or where K is long (fewer, longer workgroups
+// won for K = 12288); else 64 x 128, whose 155 registers let three
+// workgroups share a CU.  Wider M tiles (128 rows), a 2 x 2 wave arrangement
+// (weight fragments loaded twice) and 128-wide K steps all measured slower.
+bool wide_tile(int M, int N, int K) {
+  const int t = ((M + 63) / 64) * ((N + 255) / 256);
+  return t >= 256 || K >= 8192;
 }
 
 constexpr int kNThreads = 256;
@@ -220,6 +338,7 @@ hipError_t launch_prefill_gemm(const PrefillDesc& d, hipStream_t s) {
   PrefillParams p{};
   p.a = d.a;
   p.lda = d.lda;
+  p.abytes = (uint32_t)(((size_t)(d.M - 1) * d.lda + d.K) * 2);
   p.w = static_cast<const uint8_t*>(d.w);
   p.bbytes = (uint32_t)block_bytes(M3_BF16, d.K);
   p.wbytes = (uint32_t)((size_t)n_blocks(d.N) * p.bbytes);
@@ -232,16 +351,8 @@ hipError_t launch_prefill_gemm(const PrefillDesc& d, hipStream_t s) {
   p.epi = d.epi;
   p.res = d.res;
   p.ldr = d.ldr;
-  p.mtiles = (d.M + kPM - 1) / kPM;
-  p.ntiles = (d.N + kPN - 1) / kPN;
-  const int grid = p.mtiles * p.ntiles;
-  if (d.epi == M3_EPI_SWIGLU)
-    hipLaunchKernelGGL(prefill_gemm_kernel<M3_EPI_SWIGLU>, dim3(grid), dim3(kPThreads), 0, s, p);
-  else if (d.epi == M3_EPI_RESIDUAL)
-    hipLaunchKernelGGL(prefill_gemm_kernel<M3_EPI_RESIDUAL>, dim3(grid), dim3(kPThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(prefill_gemm_kernel<M3_EPI_NONE>, dim3(grid), dim3(kPThreads), 0, s, p);
-  return hipGetLastError();
+  p.vec = d.ldy % 8 == 0 && (!d.res || (d.ldr % 8 == 0 && reinterpret_cast<uintptr_t>(d.res) % 16 == 0));
+  return wide_tile(d.M, d.N, d.K) ? launch_tile<1, 4, 4, 2>(p, s) : launch_tile<1, 4, 2, 2>(p, s);
 }
 
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const float* gamma,

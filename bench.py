@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode weight-stream GB/s (% of HBM peak) and frames/s at B=1/6/16"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0          # dense bf16 matrix-core peak (no sparsity)
 # Counter-derived HBM bytes of a kernel; valid only for the kernel sources it
 # was measured on (their sha256 is recorded beside the figures).
 TRAFFIC = {
@@ -209,6 +210,83 @@ def time_cfg_draw(stream, S, V, top_k=50, calls=50, reps=5):
             "logit_bytes": 2 * S * V * 4, "GB_s": round(2 * S * V * 4 / (us * 1e-6) / 1e9, 1)}
 
 
+def time_prefill(c, stream, M=600, reps=10):
+    """One body layer of the prompt prefill at M rows (300 prompt tokens per
+    CFG row, two rows): RMSNorm rows, the QKV GEMM, the o-projection GEMM
+    with the residual epilogue (attention stubbed as identity, as in the
+    frame: it reads the q columns), RMSNorm rows, the gate/up GEMM with the
+    SwiGLU epilogue, the down GEMM with the residual epilogue.  Average
+    durations with HIP events on the launch stream; seeded bf16 weights."""
+    import torch
+    from autoregressive_audio_lm_amd import m3, synth
+    H, F = c.hidden, c.ffn
+    nq = c.n_heads * c.head_dim
+    nqkv = nq + 2 * c.n_kv_heads * c.head_dim
+    dev = "cuda"
+    W = {}
+    for name, (N, K, flags) in {"qkv": (nqkv, H, 0), "o": (H, nq, 0),
+                                "gate_up": (2 * F, H, m3.PACK_GLU_INTERLEAVE),
+                                "down": (H, F, 0)}.items():
+        Wd = synth.normal_bf16((N, K), 50 + len(W), 0.02, dev)
+        W[name] = (m3.pack(0, Wd, flags), N, K)
+        del Wd
+    g1, g2 = synth.gamma_f32(H, 60, dev), synth.gamma_f32(H, 61, dev)
+    h = synth.activations(M, H, 62, device=dev)
+    a = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty(M, nqkv, dtype=torch.bfloat16, device=dev)
+    mlp = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+
+    def step(which=None):
+        if which in (None, "norm"):
+            m3.rmsnorm_rows(h, g1, c.eps, a=a, stream=stream)
+        if which in (None, "qkv"):
+            m3.prefill_gemm(*W["qkv"], a, y=qkv, stream=stream)
+        if which in (None, "o"):
+            m3.prefill_gemm(*W["o"], qkv[:, :nq], y=h, epi=m3.EPI_RESIDUAL, residual=h, stream=stream)
+        if which is None:
+            m3.rmsnorm_rows(h, g2, c.eps, a=a, stream=stream)
+        if which in (None, "gate_up"):
+            m3.prefill_gemm(*W["gate_up"], a, y=mlp, epi=m3.EPI_SWIGLU, stream=stream)
+        if which in (None, "down"):
+            m3.prefill_gemm(*W["down"], mlp, y=h, epi=m3.EPI_RESIDUAL, residual=h, stream=stream)
+
+    def timed(which):
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                step(which)
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                step(which)
+            e1.record(stream)
+            stream.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    layer_us = timed(None)
+    gemms = []
+    flops = 0
+    for name in ("qkv", "o", "gate_up", "down"):
+        us = timed(name)
+        _, N, K = W[name]
+        fl = 2 * M * N * K
+        flops += fl
+        tf = fl / (us * 1e-6) / 1e12
+        gemms.append({"name": name, "N": N, "K": K, "avg_us": round(us, 2),
+                      "TFLOP_s": round(tf, 1), "frac": round(tf / MFMA_BF16_PEAK_TFS, 4)})
+    norm_us = timed("norm")
+    gemm_us = sum(g["avg_us"] for g in gemms)
+    tf = flops / (gemm_us * 1e-6) / 1e12
+    del W
+    return {"rows": M, "layer_us": round(layer_us, 2), "rmsnorm_rows_us": round(norm_us, 2),
+            "gemms": gemms,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                         "kernel": "prefill_gemm_kernel (the four body GEMMs of a layer)"},
+            "prompt_prefill_ms_36_layers": round(36 * layer_us / 1e3, 3)}
+
+
 def kernel_source_hash(which: str = "gate_up") -> str:
     import hashlib
     h = hashlib.sha256()
@@ -375,6 +453,8 @@ def main():
     # B = 16 (8 songs, 16384 codes) and the depth heads' B = 6 (3 songs, 1024 codes)
     cfg_draw = [time_cfg_draw(stream, 8, cfg["V0"]), time_cfg_draw(stream, 3, cfg["code_vocab"])]
     log(f"[bench] cfg draw {cfg_draw}")
+    prefill = time_prefill(dm.config, stream)
+    log(f"[bench] prefill {prefill}")
     paths_ms = {k: round(v["ms"], 4) for k, v in res.items()}
     for v in res.values():
         v["state"].release()
@@ -463,6 +543,7 @@ def main():
         "cfg_draw": {"kernel": "cfg_topk_kernel (guidance 1.5, top-k 50, Gumbel-argmax; "
                                "one workgroup per song)", "points": cfg_draw},
         "guided_frame": guided,
+        "prefill": prefill,
         "gpu": f"{props.name} {props.gcnArchName} x{props.multi_processor_count} CU",
     }
     print(json.dumps(out), flush=True)

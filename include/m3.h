@@ -241,7 +241,8 @@ int m3_cfg_topk_draw(const float* logits, int n_songs, int V, int ldl, float cfg
  * for M3_EPI_SWIGLU).  Epilogues and outputs as m3_rmsnorm_gemv (SwiGLU and
  * residual write bf16; the residual may be y itself).  1 <= M <=
  * M3_MAX_M_PREFILL; N >= 1 (even for SwiGLU); K % 64 == 0; lda >= K, a
- * multiple of 8; ldy >= N (N/2 for SwiGLU); ldr >= N; W, a, y 16-byte
+ * multiple of 8; ldy >= N (N/2 for SwiGLU); ldr >= N; the packed W and
+ * the span of a ((M - 1) lda + K elements) each under 2 GiB; W, a, y 16-byte
  * aligned; a must not overlap y.  Errors: M3_ERR_NULL, M3_ERR_SHAPE,
  * M3_ERR_ALIGN, M3_ERR_FORMAT, M3_ERR_ALIAS before any launch; M3_ERR_HIP if
  * the launch fails. */

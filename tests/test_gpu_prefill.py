@@ -1,9 +1,10 @@
 """GPU parity of the prompt prefill (about 300 tokens for each of the two CFG
 rows: "MiniMax Music 3, local"; TensorFold PR #987) against the oracle: the
 row-wise RMSNorm (m3_rmsnorm_rows) and the dense GEMM on the matrix cores
-(m3_prefill_gemm) with its epilogues, at sizes that span several 128 x 128
-tiles with ragged M and N, and at the full body shapes on sampled output
-columns the oracle computes one row block at a time.  Every call goes
+(m3_prefill_gemm) with its epilogues, at sizes that span several tiles of
+both tile shapes (64 x 128 and 64 x 256) with ragged M, N and K step counts,
+and at the full body shapes on sampled output columns the oracle computes
+one row block at a time.  Every call goes
 through the C ABI."""
 import numpy as np
 import pytest
@@ -35,8 +36,9 @@ def gemm(W, a, epi=m3.EPI_NONE, out_f32=False, res=None, flags=0):
     return y.cpu().numpy() if out_f32 else synth.bits(y)
 
 
+# the last two reach the 64 x 256 tiles (K >= 8192), the others 64 x 128
 @pytest.mark.parametrize("M,N,K", [(1, 16, 64), (37, 200, 512), (600, 256, 512), (129, 130, 1024),
-                                   (300, 520, 256)])
+                                   (300, 520, 256), (37, 300, 8192), (130, 272, 8320)])
 def test_prefill_gemm_parity(M, N, K):
     W = rand_w(N, K, M + N)
     a = rand_x(M, K, K + 3)
@@ -45,18 +47,26 @@ def test_prefill_gemm_parity(M, N, K):
     P.check_bf16(gemm(W, a), y_ex)
 
 
-@pytest.mark.parametrize("M", [1, 150, 600])
-def test_prefill_epilogues(M):
-    F, K = 100, 512
+@pytest.mark.parametrize("M,K", [(1, 512), (150, 512), (600, 512), (70, 8192)])
+@pytest.mark.parametrize("F,N", [(100, 200), (99, 203)])
+def test_prefill_epilogues(M, K, F, N):
+    """SwiGLU and residual epilogues; F = 100 / N = 200 give rows of whole
+    16-byte chunks, F = 99 / N = 203 ragged tails and unaligned row strides."""
     Wg, Wu = rand_w(F, K, 11), rand_w(F, K, 12)
     a = rand_x(M, K, 13)
     m = gemm(np.concatenate([Wg, Wu], 0), a, epi=m3.EPI_SWIGLU, flags=m3.PACK_GLU_INTERLEAVE)
     assert m.shape == (M, F)
     P.check_swiglu(m, O.gemv(O.Matrix(O.interleave_gate_up(Wg, Wu), O.BF16), a))
-    N = 200
     W = rand_w(N, K, 14)
     h = rand_x(M, N, 15)
-    P.check_residual(gemm(W, a, epi=m3.EPI_RESIDUAL, res=h), h, O.gemv(O.Matrix(W, O.BF16), a))
+    y_ex = O.gemv(O.Matrix(W, O.BF16), a)
+    P.check_residual(gemm(W, a, epi=m3.EPI_RESIDUAL, res=h), h, y_ex)
+    # in place: the residual stream is the output
+    hd = synth.from_bits(h, DEV)
+    m3.prefill_gemm(m3.pack(0, synth.from_bits(W, DEV)), N, K, synth.from_bits(a, DEV), y=hd,
+                    epi=m3.EPI_RESIDUAL, residual=hd)
+    torch.cuda.synchronize()
+    P.check_residual(synth.bits(hd), h, y_ex)
 
 
 @pytest.mark.parametrize("M,K", [(1, 64), (600, 4096), (37, 2048)])
