@@ -114,6 +114,12 @@ def _declare(L):
                                 ctypes.c_int, ctypes.c_int, _P]
     L.m3o_swiglu_interleaved.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P]
     L.m3o_residual.argtypes = [_P, _P, ctypes.c_int, _P]
+    L.m3o_rope_table.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, _P]
+    L.m3o_qk_norm_rope.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, _P, _P, ctypes.c_float, _P, ctypes.c_int, _P,
+                                   _P, _P, ctypes.c_int]
+    L.m3o_decode_attention.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int, _P]
     L.m3o_attn_stub.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]
     L.m3o_philox4x32_10.argtypes = [_P, _P, _P]
@@ -278,6 +284,43 @@ def attn_stub(qkv, voff, n_heads, group, hd):
     o = np.empty((B, n_heads * hd), np.uint16)
     lib().m3o_attn_stub(_ptr(qkv), B, ldq, int(voff), n_heads, group, hd, _ptr(o))
     return o
+
+
+# ------------------------------------------------------ decode attention ---
+def rope_table(max_pos, head_dim=128, theta=1e6):
+    """[max_pos, head_dim/2, 2] fp32: cos, sin of p * theta^(-i/half), in float64."""
+    t = np.empty((max_pos, head_dim // 2, 2), np.float32)
+    lib().m3o_rope_table(int(max_pos), int(head_dim), float(theta), _ptr(t))
+    return t
+
+
+def qk_norm_rope(qkv, n_q, n_kv, q_gamma, k_gamma, eps, rope, pos, k_cache, v_cache, hd=128):
+    """Per-head RMSNorm + RoPE of the q and k heads of qkv [B, ldq] at position
+    pos; returns q [B, n_q*hd]; writes k and v into the caches (uint16 arrays
+    [B, n_kv, max_pos, hd], modified in place)."""
+    qkv = _c(qkv, np.uint16)
+    B, ldq = qkv.shape
+    assert k_cache.dtype == np.uint16 and k_cache.flags.c_contiguous
+    assert v_cache.dtype == np.uint16 and v_cache.flags.c_contiguous
+    max_pos = k_cache.shape[2]
+    q = np.empty((B, n_q * hd), np.uint16)
+    lib().m3o_qk_norm_rope(_ptr(qkv), B, ldq, int(n_q), int(n_kv), int(hd),
+                           _ptr(_c(q_gamma, np.float32)), _ptr(_c(k_gamma, np.float32)),
+                           float(eps), _ptr(_c(rope, np.float32)), int(pos), _ptr(q),
+                           _ptr(k_cache), _ptr(v_cache), int(max_pos))
+    return q
+
+
+def decode_attention(q, k_cache, v_cache, T, n_q, n_kv, hd=128):
+    """out [B, n_q*hd] bf16 = softmax(q k^T / sqrt(hd)) v over positions < T."""
+    q = _c(q, np.uint16)
+    B = q.shape[0]
+    k_cache = _c(k_cache, np.uint16)
+    v_cache = _c(v_cache, np.uint16)
+    out = np.empty((B, n_q * hd), np.uint16)
+    lib().m3o_decode_attention(_ptr(q), B, int(n_q), int(n_kv), int(hd), _ptr(k_cache),
+                               _ptr(v_cache), int(k_cache.shape[2]), int(T), _ptr(out))
+    return out
 
 
 def interleave_gate_up(W_gate, W_up):

@@ -279,6 +279,97 @@ void m3o_attn_stub(const uint16_t* qkv, int B, int ldq, int voff, int n_heads,
 }
 
 /* ------------------------------------------------------------------ */
+/* Decode attention ("MiniMax Music 3, local" and TensorFold PR #987's    */
+/* kernel list: per-head q/k norm and RoPE, decode attention over the     */
+/* cached keys, the depth decoder's attention over its codebook positions;*/
+/* the precision contract there: fp32 norms, softmax, rope and attention  */
+/* sums with bf16 activations).  The body is Qwen3-shaped: RoPE base 1e6, */
+/* rotation of the pairs (i, i + hd/2).                                   */
+/* ------------------------------------------------------------------ */
+void m3o_rope_table(int max_pos, int head_dim, double theta, float* t) {
+  const int half = head_dim / 2;
+  for (int p = 0; p < max_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double inv = pow(theta, -(double)i / (double)half);
+      const double ang = (double)p * inv;
+      t[((size_t)p * half + i) * 2] = (float)cos(ang);
+      t[((size_t)p * half + i) * 2 + 1] = (float)sin(ang);
+    }
+}
+
+/* RMSNorm of one head's hd values, then its rotation at position pos */
+static void norm_rope_head(const uint16_t* x, int hd, const float* gamma, float eps,
+                           const float* rope_pos, uint16_t* y) {
+  const int half = hd / 2;
+  uint16_t xn[512];
+  double ss = 0.0;
+  for (int d = 0; d < hd; ++d) {
+    const double v = m3o_bf16_to_f64(x[d]);
+    ss += v * v;
+  }
+  const double r = 1.0 / sqrt(ss / (double)hd + (double)eps);
+  for (int d = 0; d < hd; ++d)
+    xn[d] = m3o_f64_to_bf16(m3o_bf16_to_f64(x[d]) * r * (double)gamma[d]);
+  for (int i = 0; i < half; ++i) {
+    const double c = (double)rope_pos[2 * i], s = (double)rope_pos[2 * i + 1];
+    const double a = m3o_bf16_to_f64(xn[i]), b = m3o_bf16_to_f64(xn[i + half]);
+    y[i] = m3o_f64_to_bf16(a * c - b * s);
+    y[i + half] = m3o_f64_to_bf16(b * c + a * s);
+  }
+}
+
+void m3o_qk_norm_rope(const uint16_t* qkv, int B, int ldq, int n_q, int n_kv, int hd,
+                      const float* q_gamma, const float* k_gamma, float eps, const float* rope,
+                      int pos, uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache,
+                      int max_pos) {
+  const float* rp = rope + (size_t)pos * (hd / 2) * 2;
+  for (int b = 0; b < B; ++b) {
+    const uint16_t* row = qkv + (size_t)b * ldq;
+    for (int h = 0; h < n_q; ++h)
+      norm_rope_head(row + h * hd, hd, q_gamma, eps, rp, q_out + ((size_t)b * n_q + h) * hd);
+    for (int h = 0; h < n_kv; ++h) {
+      const size_t slot = (((size_t)b * n_kv + h) * max_pos + pos) * hd;
+      norm_rope_head(row + (n_q + h) * hd, hd, k_gamma, eps, rp, k_cache + slot);
+      for (int d = 0; d < hd; ++d) v_cache[slot + d] = row[(n_q + n_kv + h) * hd + d];
+    }
+  }
+}
+
+void m3o_decode_attention(const uint16_t* q, int B, int n_q, int n_kv, int hd,
+                          const uint16_t* k_cache, const uint16_t* v_cache, int max_pos, int T,
+                          uint16_t* out) {
+  const int g = n_q / n_kv;
+  const double scale = 1.0 / sqrt((double)hd);
+  double* sc = (double*)malloc(sizeof(double) * (size_t)T);
+  double acc[512];
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < n_q; ++h) {
+      const uint16_t* qh = q + ((size_t)b * n_q + h) * hd;
+      const size_t base = ((size_t)b * n_kv + h / g) * max_pos * hd;
+      double mx = -INFINITY;
+      for (int t = 0; t < T; ++t) {
+        const uint16_t* kt = k_cache + base + (size_t)t * hd;
+        double dot = 0.0;
+        for (int d = 0; d < hd; ++d) dot += m3o_bf16_to_f64(qh[d]) * m3o_bf16_to_f64(kt[d]);
+        sc[t] = dot * scale;
+        if (sc[t] > mx) mx = sc[t];
+      }
+      double sum = 0.0;
+      for (int t = 0; t < T; ++t) {
+        sc[t] = exp(sc[t] - mx);
+        sum += sc[t];
+      }
+      for (int d = 0; d < hd; ++d) acc[d] = 0.0;
+      for (int t = 0; t < T; ++t) {
+        const uint16_t* vt = v_cache + base + (size_t)t * hd;
+        for (int d = 0; d < hd; ++d) acc[d] += sc[t] * m3o_bf16_to_f64(vt[d]);
+      }
+      for (int d = 0; d < hd; ++d) out[((size_t)b * n_q + h) * hd + d] = m3o_f64_to_bf16(acc[d] / sum);
+    }
+  free(sc);
+}
+
+/* ------------------------------------------------------------------ */
 /* Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers:*/
 /* As Easy as 1, 2, 3", SC'11): 10 rounds of two 32x32->64 multiplies   */
 /* (multipliers 0xD2511F53, 0xCD9E8D57) with a Weyl key schedule        */

@@ -80,6 +80,29 @@ void m3o_residual(const double* y, const uint16_t* h, int n, uint16_t* h_out);
 void m3o_attn_stub(const uint16_t* qkv, int B, int ldq, int voff, int n_heads,
                    int group, int hd, uint16_t* o);
 
+/* ---- decode attention (q/k norm, RoPE, KV cache, softmax attention) --- */
+/* RoPE table, theta^(-i/half) frequencies over pair i < half = head_dim/2:
+ * t[(p*half + i)*2] = fl32(cos(p * theta^(-i/half))), [..+1] = fl32(sin(..)),
+ * angle and trig in float64. */
+void m3o_rope_table(int max_pos, int head_dim, double theta, float* t);
+/* For every row b of qkv [B, ldq] (q heads at columns h*hd, k heads after the
+ * n_q q heads, v heads after the k heads): per head RMSNorm over its hd values
+ * (x' = bf16(x * r * gamma), as m3o_rmsnorm), then the rotation of pairs
+ * (i, i + hd/2) by the table's angle of position pos:
+ *   y_i = bf16(x'_i c - x'_{i+half} s),  y_{i+half} = bf16(x'_{i+half} c + x'_i s)
+ * (float64 from the fp32 c, s).  q goes to q_out [B, n_q*hd]; k and the raw v
+ * go to the caches [B][n_kv][max_pos][hd] at position pos. */
+void m3o_qk_norm_rope(const uint16_t* qkv, int B, int ldq, int n_q, int n_kv, int hd,
+                      const float* q_gamma, const float* k_gamma, float eps, const float* rope,
+                      int pos, uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache,
+                      int max_pos);
+/* out[b, h*hd + d] = bf16( sum_{t<T} p_t * v[b][h/g][t][d] ),
+ * p = softmax_t( q[b,h] . k[b][h/g][t] / sqrt(hd) ), g = n_q / n_kv;
+ * float64 throughout, one rounding. */
+void m3o_decode_attention(const uint16_t* q, int B, int n_q, int n_kv, int hd,
+                          const uint16_t* k_cache, const uint16_t* v_cache, int max_pos, int T,
+                          uint16_t* out);
+
 /* ---- sampler -------------------------------------------------------- */
 void  m3o_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 float m3o_logf(float x);                       /* fixed-sequence fp32 log   */
