@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libm3.so")
-SOURCES = ["capi.cpp", "gemv.hip", "persist.hip", "persist_bf16.hip", "persist_i8row.hip", "persist_fp8row.hip", "pack.hip", "prefill.hip", "sample.hip", "frame.hip"]
+SOURCES = ["capi.cpp", "gemv.hip", "persist.hip", "persist_bf16.hip", "persist_i8row.hip", "persist_fp8row.hip", "pack.hip", "prefill.hip", "attention.hip", "sample.hip", "frame.hip"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

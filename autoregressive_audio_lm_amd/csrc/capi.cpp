@@ -660,6 +660,84 @@ int m3_prefill_gemm(const void* w, int N, int K, const uint16_t* a, int M, int l
   return hip_status(launch_prefill_gemm(d, static_cast<hipStream_t>(stream)));
 }
 
+// ---- decode attention ------------------------------------------------------------
+int m3_rope_table(float* table, int max_pos, int head_dim, float theta, void* stream) {
+  if (!table) return M3_ERR_NULL;
+  if (max_pos < 1 || max_pos > M3_MAX_POS || head_dim != M3_HEAD_DIM) return M3_ERR_SHAPE;
+  if (!(theta > 1.0f) || !std::isfinite(theta)) return M3_ERR_SHAPE;
+  if (!aligned(table, 16)) return M3_ERR_ALIGN;
+  return hip_status(launch_rope_table(table, max_pos, head_dim, (double)theta,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+static bool attn_heads_ok(int n_q, int n_kv) {
+  if (n_kv < 1 || n_q < n_kv || n_q % n_kv != 0 || n_q > M3_MAX_HEADS) return false;
+  const int g = n_q / n_kv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+static size_t cache_bytes(int B, int n_kv, int max_pos) {
+  return (size_t)B * n_kv * max_pos * M3_HEAD_DIM * 2;
+}
+
+int m3_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv, int head_dim,
+                    const float* q_gamma, const float* k_gamma, float eps, const float* rope,
+                    int pos, uint16_t* q_out, int ldq, uint16_t* k_cache, uint16_t* v_cache,
+                    int max_pos, void* stream) {
+  if (!qkv || !q_gamma || !k_gamma || !rope || !q_out || !k_cache || !v_cache) return M3_ERR_NULL;
+  if (head_dim != M3_HEAD_DIM || !attn_heads_ok(n_q, n_kv)) return M3_ERR_SHAPE;
+  if (B < 1 || B > M3_MAX_B || max_pos < 1 || max_pos > M3_MAX_POS || pos < 0 || pos >= max_pos)
+    return M3_ERR_SHAPE;
+  if (ldqkv < (n_q + 2 * n_kv) * M3_HEAD_DIM || ldq < n_q * M3_HEAD_DIM) return M3_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return M3_ERR_SHAPE;
+  if (!aligned(qkv, 16) || !aligned(q_out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(q_gamma, 4) || !aligned(k_gamma, 4) || !aligned(rope, 16) || ldqkv % 8 || ldq % 8)
+    return M3_ERR_ALIGN;
+  const size_t qkv_b = ((size_t)(B - 1) * ldqkv + (n_q + 2 * n_kv) * M3_HEAD_DIM) * 2;
+  const size_t q_b = ((size_t)(B - 1) * ldq + n_q * M3_HEAD_DIM) * 2;
+  const size_t c_b = cache_bytes(B, n_kv, max_pos);
+  if (overlap(qkv, qkv_b, q_out, q_b) || overlap(qkv, qkv_b, k_cache, c_b) ||
+      overlap(qkv, qkv_b, v_cache, c_b) || overlap(q_out, q_b, k_cache, c_b) ||
+      overlap(q_out, q_b, v_cache, c_b) || overlap(k_cache, c_b, v_cache, c_b))
+    return M3_ERR_ALIAS;
+  return hip_status(launch_qk_norm_rope(qkv, B, ldqkv, n_q, n_kv, q_gamma, k_gamma, eps, rope, pos,
+                                        q_out, ldq, k_cache, v_cache, max_pos,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t m3_attention_workspace_bytes(int B, int n_q, int T) {
+  if (B < 1 || n_q < 1 || T < 1) return 0;
+  const int nc = attn_chunks(T);
+  return nc == 1 ? 0 : (size_t)B * n_q * nc * (2 + M3_HEAD_DIM) * sizeof(float);
+}
+
+int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, int head_dim,
+                        const uint16_t* k_cache, const uint16_t* v_cache, int max_pos, int T,
+                        uint16_t* out, int ldo, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!q || !k_cache || !v_cache || !out) return M3_ERR_NULL;
+  if (head_dim != M3_HEAD_DIM || !attn_heads_ok(n_q, n_kv)) return M3_ERR_SHAPE;
+  if (B < 1 || B > M3_MAX_B || max_pos < 1 || max_pos > M3_MAX_POS || T < 1 || T > max_pos)
+    return M3_ERR_SHAPE;
+  if (ldq < n_q * M3_HEAD_DIM || ldo < n_q * M3_HEAD_DIM) return M3_ERR_SHAPE;
+  const size_t need = m3_attention_workspace_bytes(B, n_q, T);
+  if (need && !workspace) return M3_ERR_NULL;
+  if (workspace_bytes < need) return M3_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      (need && !aligned(workspace, 16)) || ldq % 8 || ldo % 8)
+    return M3_ERR_ALIGN;
+  const size_t q_b = ((size_t)(B - 1) * ldq + n_q * M3_HEAD_DIM) * 2;
+  const size_t o_b = ((size_t)(B - 1) * ldo + n_q * M3_HEAD_DIM) * 2;
+  const size_t c_b = cache_bytes(B, n_kv, max_pos);
+  if (overlap(out, o_b, q, q_b) || overlap(out, o_b, k_cache, c_b) || overlap(out, o_b, v_cache, c_b) ||
+      (need && (overlap(workspace, need, out, o_b) || overlap(workspace, need, q, q_b) ||
+                overlap(workspace, need, k_cache, c_b) || overlap(workspace, need, v_cache, c_b))))
+    return M3_ERR_ALIAS;
+  return hip_status(launch_decode_attention(q, B, ldq, n_q, n_kv, k_cache, v_cache, max_pos, T, out,
+                                            ldo, static_cast<float*>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 uint64_t m3_frame_weight_bytes(const m3_config* c) {
   if (!c) return 0;
   const Dims d = dims_of(*c);

@@ -150,6 +150,17 @@ hipError_t launch_prefill_gemm(const PrefillDesc& d, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const float* gamma,
                                float eps, uint16_t* a, int lda, hipStream_t s);
 
+// ---- decode attention (attention.hip) --------------------------------------------
+int attn_chunks(int T);   // workgroups per (row, KV head): ceil(T / 128)
+hipError_t launch_rope_table(float* t, int max_pos, int head_dim, double theta, hipStream_t s);
+hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
+                               const float* q_gamma, const float* k_gamma, float eps,
+                               const float* rope, int pos, uint16_t* q_out, int ldq,
+                               uint16_t* k_cache, uint16_t* v_cache, int max_pos, hipStream_t s);
+hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv,
+                                   const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
+                                   int T, uint16_t* out, int ldo, float* ws, hipStream_t s);
+
 // ---- frame helpers -------------------------------------------------------------
 // audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)
 // Final draw of the last codebook from the head's per-block winners, then the

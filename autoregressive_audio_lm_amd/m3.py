@@ -190,3 +190,69 @@ def prefill_gemm(packed: torch.Tensor, N: int, K: int, a: torch.Tensor, y: torch
     check(lib().m3_prefill_gemm(_ptr(packed), N, K, _ptr(a), M, a.stride(0), _ptr(y), y.stride(0),
                                 out_dtype, epi, _ptr(residual), ldr, _stream(stream)))
     return y
+
+
+# ---- decode attention ---------------------------------------------------------
+HEAD_DIM = 128
+
+
+def rope_table(max_pos: int, theta: float = 1e6, device="cuda", stream=None) -> torch.Tensor:
+    """m3_rope_table: fp32 [max_pos, 64, 2] (cos, sin of p * theta^(-i/64))."""
+    t = torch.empty(max_pos, HEAD_DIM // 2, 2, dtype=torch.float32, device=device)
+    check(lib().m3_rope_table(_ptr(t), int(max_pos), HEAD_DIM, float(theta), _stream(stream)))
+    return t
+
+
+def kv_cache(B: int, n_kv: int, max_pos: int, device="cuda") -> tuple[torch.Tensor, torch.Tensor]:
+    """Zeroed bf16 K and V caches [B, n_kv, max_pos, 128]."""
+    shape = (B, n_kv, max_pos, HEAD_DIM)
+    return (torch.zeros(shape, dtype=torch.bfloat16, device=device),
+            torch.zeros(shape, dtype=torch.bfloat16, device=device))
+
+
+def qk_norm_rope(qkv: torch.Tensor, n_q: int, n_kv: int, q_gamma: torch.Tensor,
+                 k_gamma: torch.Tensor, rope: torch.Tensor, pos: int, k_cache: torch.Tensor,
+                 v_cache: torch.Tensor, eps: float = 1e-6, q_out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """m3_qk_norm_rope: q [B, n_q*128] bf16; k and v written into the caches at pos."""
+    for t, n in ((qkv, "qkv"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"), (rope, "rope"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache"), (q_out, "q_out")):
+        _cuda(t, n)
+    B = qkv.shape[0]
+    if q_out is None:
+        q_out = torch.empty(B, n_q * HEAD_DIM, dtype=torch.bfloat16, device=qkv.device)
+    for c in (k_cache, v_cache):
+        if c.dim() != 4 or c.shape[0] != B or c.shape[1] != n_kv or c.shape[3] != HEAD_DIM \
+                or not c.is_contiguous():
+            raise ValueError("caches must be contiguous [B, n_kv, max_pos, 128]")
+    check(lib().m3_qk_norm_rope(_ptr(qkv), B, qkv.stride(0), int(n_q), int(n_kv), HEAD_DIM,
+                                _ptr(q_gamma), _ptr(k_gamma), float(eps), _ptr(rope), int(pos),
+                                _ptr(q_out), q_out.stride(0), _ptr(k_cache), _ptr(v_cache),
+                                k_cache.shape[2], _stream(stream)))
+    return q_out
+
+
+def attention_workspace_bytes(B: int, n_q: int, T: int) -> int:
+    return int(lib().m3_attention_workspace_bytes(int(B), int(n_q), int(T)))
+
+
+def decode_attention(q: torch.Tensor, n_q: int, n_kv: int, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, T: int, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_decode_attention: out [B, n_q*128] bf16 over cached positions < T."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out"),
+                 (workspace, "workspace")):
+        _cuda(t, n)
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty(B, n_q * HEAD_DIM, dtype=torch.bfloat16, device=q.device)
+    need = attention_workspace_bytes(B, n_q, T)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().m3_decode_attention(_ptr(q), B, q.stride(0), int(n_q), int(n_kv), HEAD_DIM,
+                                    _ptr(k_cache), _ptr(v_cache), k_cache.shape[2], int(T),
+                                    _ptr(out), out.stride(0), _ptr(workspace), wbytes,
+                                    _stream(stream)))
+    return out
+

@@ -59,6 +59,9 @@ enum { M3_PACK_GLU_INTERLEAVE = 1 };
 #define M3_MAX_SONGS_CFG 32767 /* songs (row pairs) per CFG draw call       */
 #define M3_MAX_V_CFG 32768   /* columns per CFG draw call                   */
 #define M3_MAX_M_PREFILL 65536 /* rows per prefill GEMM / RMSNorm call      */
+#define M3_HEAD_DIM 128      /* attention head width (body and depth decoder) */
+#define M3_MAX_POS 65536     /* cached positions per KV cache               */
+#define M3_MAX_HEADS 256     /* query heads per attention call              */
 
 const char* m3_status_str(int status);
 /* library version string (host) */
@@ -251,6 +254,54 @@ int m3_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const float* gamma
 int m3_prefill_gemm(const void* packed_bf16, int N, int K, const uint16_t* a, int M, int lda,
                     void* y, int ldy, int out_dtype, int epi, const uint16_t* residual, int ldr,
                     void* stream);
+
+/* ---- decode attention -------------------------------------------------------- */
+/* Attention of each batch row's new query over its cached positions, in place of
+ * the identity stub ("MiniMax Music 3, local" and TensorFold PR #987 list per-head
+ * q/k norm + RoPE, split-key decode attention with a merge, and the depth
+ * decoder's attention over its codebook positions; fp32 norms, RoPE, softmax and
+ * sums over bf16 activations).  Head width 128 (M3_HEAD_DIM).  KV caches are bf16
+ * [B][n_kv][max_pos][128], caller-allocated.  Query head h reads KV head
+ * h / (n_q / n_kv); n_q / n_kv must be 1, 2, 4 or 8.
+ *
+ * m3_rope_table: table[(p * 64 + i) * 2 + {0, 1}] = fl32(cos / sin(p * theta^(-i/64)))
+ * for p < max_pos, i < 64, angle and trig in float64 (Qwen3: theta = 1e6).
+ * table: device, 16-byte aligned, max_pos * 128 floats.
+ *
+ * m3_qk_norm_rope: for every row b of qkv (q heads at columns h*128, then the
+ * n_kv k heads, then the n_kv v heads): per head RMSNorm over its 128 values,
+ * x' = bf16((x * r) * gamma) with r = 1 / sqrt(mean x^2 + eps) in fp32 (q_gamma
+ * for q heads, k_gamma for k heads; 128 floats each), then the rotation of the
+ * pairs (i, i + 64) by the table's angle at position pos:
+ *   y_i = bf16(x'_i c - x'_{i+64} s),  y_{i+64} = bf16(x'_{i+64} c + x'_i s).
+ * q goes to q_out [B, ldq]; k and the unnormed v go to the caches at position pos.
+ * rope is a table from m3_rope_table with more than pos positions.
+ * 1 <= B <= M3_MAX_B; 0 <= pos < max_pos <= M3_MAX_POS; ldqkv >= (n_q + 2 n_kv)
+ * * 128, ldq >= n_q * 128, both multiples of 8; qkv, q_out, caches, rope 16-byte
+ * aligned; no two of qkv, q_out, k_cache, v_cache overlap.
+ *
+ * m3_decode_attention: out[b, h*128 + d] = bf16( sum_{t<T} p_t v[b][h/g][t][d] ),
+ * p = softmax_t( q[b,h] . k[b][h/g][t] / sqrt(128) ), fp32 sums and softmax
+ * (base-2 exponentials with the scale folded in).  Positions are split into
+ * chunks of 128; with more than one chunk the partial softmax states go to the
+ * workspace (m3_attention_workspace_bytes(B, n_q, T) bytes, 0 when T <= 128,
+ * 16-byte aligned, caller-owned, no contents kept between calls) and a second
+ * launch merges them in chunk order.  1 <= T <= max_pos; ldq, ldo >= n_q * 128,
+ * multiples of 8; q, caches, out 16-byte aligned; out and the workspace overlap
+ * nothing else.
+ *
+ * Errors (all three calls): M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_ALIGN,
+ * M3_ERR_WORKSPACE, M3_ERR_ALIAS before any launch; M3_ERR_HIP if a launch fails. */
+int m3_rope_table(float* table, int max_pos, int head_dim, float theta, void* stream);
+int m3_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv, int head_dim,
+                    const float* q_gamma, const float* k_gamma, float eps, const float* rope,
+                    int pos, uint16_t* q_out, int ldq, uint16_t* k_cache, uint16_t* v_cache,
+                    int max_pos, void* stream);
+size_t m3_attention_workspace_bytes(int B, int n_q, int T);
+int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, int head_dim,
+                        const uint16_t* k_cache, const uint16_t* v_cache, int max_pos, int T,
+                        uint16_t* out, int ldo, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ---- one decode frame ------------------------------------------------------ */
 typedef struct {

@@ -113,3 +113,22 @@ def unpack(packed: np.ndarray, fmt: int, N: int, K: int):
         G = K // 128
         s = sc[:, : G * 64].view(np.float32).reshape(nb * 16, G)
     return q[:N, :K], s[:N]
+
+
+def check_bf16_vs_bf16(got_bits, want_bits, agree=0.99, rel=REL, width=None):
+    """bf16 against the oracle's own bf16 result (rounded once from its float64
+    value): per row of `width` values (the last axis by default),
+    |got - want| <= 2 half-ulps of want (the oracle's rounding and ours) +
+    rel * rms(row), which covers outputs that cancel towards zero, and at
+    least `agree` of them identical (zeros of either sign equal)."""
+    g = np.asarray(got_bits, np.uint16)
+    w = np.asarray(want_bits, np.uint16)
+    if width is not None:
+        g, w = g.reshape(-1, width), w.reshape(-1, width)
+    gv, wv = O.bf16_to_f64(g), O.bf16_to_f64(w)
+    err = np.abs(gv - wv)
+    bound = 2 * half_ulp(wv) * (1 + 1e-9) + rel * row_rms(wv)
+    bad = err > bound
+    assert not bad.any(), f"{bad.sum()} of {bad.size} bf16 outputs off; worst {np.max(err / bound):.3g}x bound"
+    same = np.mean(gv == wv)
+    assert same >= agree, f"only {same:.4f} equal to the oracle's rounding"

@@ -137,6 +137,58 @@ def test_prefill_refusals(L):
     assert L.m3_rmsnorm_rows(FAKE, 4, 64, 64, g, 1e-6, FAKE, 64, None) == _lib.M3_ERR_ALIAS
 
 
+def test_attention_refusals(L):
+    """Decode attention: sizes, head groups, alignment, workspace and aliasing
+    are refused on the host, before any launch."""
+    P = ctypes.c_void_p
+    assert L.m3_attention_workspace_bytes(1, 32, 128) == 0
+    assert L.m3_attention_workspace_bytes(2, 32, 129) == 2 * 32 * 2 * 130 * 4
+    assert L.m3_attention_workspace_bytes(1, 32, 1800) == 32 * 15 * 130 * 4
+    tab = P(0x1000000)
+    assert L.m3_rope_table(None, 16, 128, 1e6, None) == _lib.M3_ERR_NULL
+    assert L.m3_rope_table(tab, 16, 64, 1e6, None) == _lib.M3_ERR_SHAPE
+    assert L.m3_rope_table(tab, 0, 128, 1e6, None) == _lib.M3_ERR_SHAPE
+    assert L.m3_rope_table(tab, 16, 128, 0.5, None) == _lib.M3_ERR_SHAPE
+    assert L.m3_rope_table(P(0x1000004), 16, 128, 1e6, None) == _lib.M3_ERR_ALIGN
+    # qk norm + rope: B = 2, 32 q heads over 8 KV heads, caches of 64 positions
+    cb = 2 * 8 * 64 * 128 * 2
+    q_arg = lambda **k: (k.get("qkv", P(0x10000000)), k.get("B", 2), k.get("ldqkv", 6144),
+                         k.get("nq", 32), k.get("nkv", 8), k.get("hd", 128), k.get("qg", P(0x30000000)),
+                         k.get("kg", P(0x30001000)), k.get("eps", 1e-6), k.get("rope", tab),
+                         k.get("pos", 5), k.get("qo", P(0x20000000)), k.get("ldq", 4096),
+                         k.get("kc", P(0x40000000)), k.get("vc", P(0x40000000 + cb)),
+                         k.get("mp", 64), None)
+    assert L.m3_qk_norm_rope(*q_arg(qkv=None)) == _lib.M3_ERR_NULL
+    assert L.m3_qk_norm_rope(*q_arg(hd=64)) == _lib.M3_ERR_SHAPE
+    assert L.m3_qk_norm_rope(*q_arg(nq=24)) == _lib.M3_ERR_SHAPE        # 3 q heads per KV head
+    assert L.m3_qk_norm_rope(*q_arg(nq=4, nkv=8)) == _lib.M3_ERR_SHAPE
+    assert L.m3_qk_norm_rope(*q_arg(pos=64)) == _lib.M3_ERR_SHAPE
+    assert L.m3_qk_norm_rope(*q_arg(ldqkv=6000)) == _lib.M3_ERR_SHAPE
+    assert L.m3_qk_norm_rope(*q_arg(B=0)) == _lib.M3_ERR_SHAPE
+    assert L.m3_qk_norm_rope(*q_arg(qo=P(0x20000008))) == _lib.M3_ERR_ALIGN
+    assert L.m3_qk_norm_rope(*q_arg(vc=P(0x40000000 + cb - 256))) == _lib.M3_ERR_ALIAS
+    assert L.m3_qk_norm_rope(*q_arg(qo=P(0x10000000 + 4096))) == _lib.M3_ERR_ALIAS
+    # attention: T = 300 needs three chunks of workspace
+    need = L.m3_attention_workspace_bytes(2, 32, 300)
+    a_arg = lambda **k: (k.get("q", P(0x20000000)), k.get("B", 2), k.get("ldq", 4096), k.get("nq", 32),
+                         k.get("nkv", 8), k.get("hd", 128), k.get("kc", P(0x40000000)),
+                         k.get("vc", P(0x48000000)), k.get("mp", 512), k.get("T", 300),
+                         k.get("out", P(0x50000000)), k.get("ldo", 4096), k.get("ws", P(0x60000000)),
+                         k.get("wsb", need), None)
+    assert L.m3_decode_attention(*a_arg(out=None)) == _lib.M3_ERR_NULL
+    assert L.m3_decode_attention(*a_arg(ws=None)) == _lib.M3_ERR_NULL
+    assert L.m3_decode_attention(*a_arg(wsb=need - 1)) == _lib.M3_ERR_WORKSPACE
+    assert L.m3_decode_attention(*a_arg(T=0)) == _lib.M3_ERR_SHAPE
+    assert L.m3_decode_attention(*a_arg(T=513)) == _lib.M3_ERR_SHAPE
+    assert L.m3_decode_attention(*a_arg(nq=48, nkv=3)) == _lib.M3_ERR_SHAPE   # 16 per KV head
+    assert L.m3_decode_attention(*a_arg(ldo=4000)) == _lib.M3_ERR_SHAPE
+    assert L.m3_decode_attention(*a_arg(out=P(0x50000002))) == _lib.M3_ERR_ALIGN
+    assert L.m3_decode_attention(*a_arg(out=P(0x20000000 + 64))) == _lib.M3_ERR_ALIAS
+    assert L.m3_decode_attention(*a_arg(ws=P(0x40000000))) == _lib.M3_ERR_ALIAS
+    # one chunk: no workspace needed
+    assert L.m3_attention_workspace_bytes(2, 32, 128) == 0
+
+
 def test_cfg_draw_refusals(L):
     p = _lib.SampleParams(0, 0, None, 0, 1.0, 0, None, 0, 0, None)
     arg = lambda **k: (k.get("lg", FAKE), k.get("S", 4), k.get("V", 5000), k.get("ldl", 5000),

@@ -1,0 +1,135 @@
+"""GPU parity of decode attention against the oracle ("MiniMax Music 3,
+local" and TensorFold PR #987's kernel list: per-head q/k norm + RoPE, decode
+attention over the cached keys with split keys and a merge, the depth
+decoder's attention over its codebook positions): the RoPE table, the q/k
+norm + RoPE with its cache writes, and the attention at the body's 32:8 heads,
+the depth decoder's 16:16 and the other supported groupings, from one cached
+position to 1800 (60 s of frames plus a prompt), across the one-chunk and
+split-and-merge paths.  Both sides build their own RoPE tables and caches;
+every call goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import parity as P
+from autoregressive_audio_lm_amd import m3, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+HD = 128
+
+
+def rnd_bf16(shape, seed, std=1.0):
+    return synth.bits(synth.normal_bf16(shape, seed, std))
+
+
+def dev(bits):
+    return synth.from_bits(np.ascontiguousarray(bits), DEV)
+
+
+def test_rope_table_matches_the_oracle():
+    got = m3.rope_table(4096).cpu().numpy()
+    want = O.rope_table(4096)
+    gi, wi = got.view(np.int32), want.view(np.int32)
+    assert np.abs(gi - wi).max() <= 1                  # float64 trig on both sides
+    assert np.mean(gi == wi) >= 0.9999
+
+
+@pytest.mark.parametrize("n_q,n_kv,B,pos", [(32, 8, 3, 0), (32, 8, 2, 7), (32, 8, 1, 1799),
+                                            (16, 16, 4, 6), (8, 4, 2, 300)])
+def test_qk_norm_rope_and_cache_writes(n_q, n_kv, B, pos):
+    max_pos = pos + 3
+    ldqkv = (n_q + 2 * n_kv) * HD + 64                # a padded row stride
+    qkv = rnd_bf16((B, ldqkv), 100 + pos, 1.5)
+    qg = (1.0 + 0.1 * np.random.default_rng(1).standard_normal(HD)).astype(np.float32)
+    kg = (1.0 + 0.1 * np.random.default_rng(2).standard_normal(HD)).astype(np.float32)
+    kc, vc = m3.kv_cache(B, n_kv, max_pos)
+    q = m3.qk_norm_rope(dev(qkv), n_q, n_kv, torch.from_numpy(qg).to(DEV),
+                        torch.from_numpy(kg).to(DEV), m3.rope_table(max_pos), pos, kc, vc)
+    torch.cuda.synchronize()
+    okc = np.zeros((B, n_kv, max_pos, HD), np.uint16)
+    ovc = np.zeros_like(okc)
+    oq = O.qk_norm_rope(qkv, n_q, n_kv, qg, kg, 1e-6, O.rope_table(max_pos), pos, okc, ovc)
+    P.check_bf16_vs_bf16(synth.bits(q), oq, width=HD)
+    gk, gv = synth.bits(kc), synth.bits(vc)
+    P.check_bf16_vs_bf16(gk[:, :, pos], okc[:, :, pos], width=HD)
+    assert np.array_equal(gv, ovc)                     # v copied bit for bit; nothing else written
+    others = np.delete(gk, pos, axis=2)
+    assert not others.any()
+
+
+def fill_cache(B, n_kv, max_pos, T, seed, kscale):
+    kc = np.zeros((B, n_kv, max_pos, HD), np.uint16)
+    vc = np.zeros_like(kc)
+    kc[:, :, :T] = rnd_bf16((B, n_kv, T, HD), seed, kscale)
+    vc[:, :, :T] = rnd_bf16((B, n_kv, T, HD), seed + 1)
+    return kc, vc
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (16, 16), (8, 4), (16, 2)])
+@pytest.mark.parametrize("T", [1, 2, 37, 128, 129, 300])
+def test_attention_parity(n_q, n_kv, T):
+    B, max_pos = 3, T + 5
+    kc, vc = fill_cache(B, n_kv, max_pos, T, 10 * T + n_kv, 3.0)
+    # positions past T hold values that would show if read
+    kc[:, :, T:] = 0x7F00
+    vc[:, :, T:] = 0x7FC0
+    q = rnd_bf16((B, n_q * HD), T + 7)
+    got = m3.decode_attention(dev(q), n_q, n_kv, dev(kc), dev(vc), T)
+    torch.cuda.synchronize()
+    want = O.decode_attention(q, kc, vc, T, n_q, n_kv)
+    P.check_bf16_vs_bf16(synth.bits(got), want, width=HD)
+
+
+def test_attention_full_size_body():
+    """The body at 16 rows (8 songs) and 1800 cached positions: 15 chunks
+    merged; checked in full against the oracle."""
+    B, n_q, n_kv, T = 16, 32, 8, 1800
+    kc, vc = fill_cache(B, n_kv, T, T, 77, 2.0)
+    q = rnd_bf16((B, n_q * HD), 78)
+    got = m3.decode_attention(dev(q), n_q, n_kv, dev(kc), dev(vc), T)
+    torch.cuda.synchronize()
+    P.check_bf16_vs_bf16(synth.bits(got), O.decode_attention(q, kc, vc, T, n_q, n_kv), width=HD)
+
+
+def test_strides_and_workspace_reuse():
+    B, n_q, n_kv, T = 2, 32, 8, 300
+    kc, vc = fill_cache(B, n_kv, 512, T, 5, 2.0)
+    q = rnd_bf16((B, n_q * HD + 128), 6)
+    ws = torch.empty(m3.attention_workspace_bytes(B, n_q, T) + 256, dtype=torch.uint8, device=DEV)
+    out = torch.zeros(B, n_q * HD + 64, dtype=torch.bfloat16, device=DEV)
+    kd, vd, qd = dev(kc), dev(vc), dev(q)
+    for T_ in (T, 129, 40):
+        m3.decode_attention(qd[:, :n_q * HD], n_q, n_kv, kd, vd, T_, out=out[:, :n_q * HD],
+                            workspace=ws)
+        torch.cuda.synchronize()
+        want = O.decode_attention(q[:, :n_q * HD], kc, vc, T_, n_q, n_kv)
+        P.check_bf16_vs_bf16(synth.bits(out[:, :n_q * HD]), want, width=HD)
+        assert not synth.bits(out[:, n_q * HD:]).any()
+
+
+def test_decode_steps_build_the_cache():
+    """Twenty decode steps: each step's QKV row goes through the norm + RoPE
+    at its position into the cache, then attention over the positions so far;
+    both sides keep their own caches."""
+    B, n_q, n_kv, steps = 2, 32, 8, 20
+    ldqkv = (n_q + 2 * n_kv) * HD
+    qg = (1.0 + 0.1 * np.random.default_rng(3).standard_normal(HD)).astype(np.float32)
+    kg = (1.0 + 0.1 * np.random.default_rng(4).standard_normal(HD)).astype(np.float32)
+    qgd, kgd = torch.from_numpy(qg).to(DEV), torch.from_numpy(kg).to(DEV)
+    rope, orope = m3.rope_table(steps), O.rope_table(steps)
+    kc, vc = m3.kv_cache(B, n_kv, steps)
+    okc = np.zeros((B, n_kv, steps, HD), np.uint16)
+    ovc = np.zeros_like(okc)
+    for pos in range(steps):
+        qkv = rnd_bf16((B, ldqkv), 500 + pos, 1.5)
+        q = m3.qk_norm_rope(dev(qkv), n_q, n_kv, qgd, kgd, rope, pos, kc, vc)
+        o = m3.decode_attention(q, n_q, n_kv, kc, vc, pos + 1)
+        torch.cuda.synchronize()
+        oq = O.qk_norm_rope(qkv, n_q, n_kv, qg, kg, 1e-6, orope, pos, okc, ovc)
+        # the oracle attends from its own q and cache; both agree to a bf16 ulp
+        # at every step (the caches themselves are compared too)
+        P.check_bf16_vs_bf16(synth.bits(kc[:, :, :pos + 1]), okc[:, :, :pos + 1], width=HD)
+        P.check_bf16_vs_bf16(synth.bits(o), O.decode_attention(oq, okc, ovc, pos + 1, n_q, n_kv),
+                             agree=0.97, width=HD)
