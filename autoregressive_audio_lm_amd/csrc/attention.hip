@@ -13,37 +13,28 @@
 // Cache layout (bf16): [B][n_kv][max_pos][128], so the keys of one KV head
 // are contiguous rows of 256 bytes.
 //
-// Attention.  A workgroup takes one (batch row, KV head, chunk of kChunk
-// positions).  A wave is four groups of 16 lanes; a group owns one position
-// at a time and a lane 8 of its 128 dimensions (one 16-byte load), so a wave
-// load covers four neighbouring cache rows, 1 KB contiguous.  The group's
-// score for each of the G query heads of the KV head is a 16-lane DPP row
-// sum; the group keeps a running maximum, sum and weighted V (online
-// softmax in base 2) over its positions.  The 16 group states of the
-// workgroup are merged in LDS; with one chunk the result is the output,
-// otherwise it goes to the workspace and attn_merge_kernel combines the
-// chunks in order.  The bound is HBM: each position's key and value are read
-// once (512 bytes per KV head and batch row).
+// Attention.  A workgroup takes one (batch row, KV head, chunk of 64 or 128
+// positions) and issues all of the chunk's key and value loads up front.
+// Pass 1: four lanes per position, each holding 32 of the 128 dimensions as
+// bf16 pairs; v_dot2 products against the G query heads of the KV head, a
+// two-step DPP sum, the scores (base 2, scale folded in) to LDS.  One wave
+// per head then takes the chunk's maximum, exponentials and sum.  Pass 2:
+// each lane owns 4 dimensions of 16 positions (a wave load reads two whole
+// value rows) and accumulates P.V; the 8 half-wave partials are summed in
+// LDS.  With one chunk the result is the output; otherwise (maximum, sum,
+// P.V) goes to the workspace and attn_merge_kernel combines the chunks in
+// order.  (Merging in the last workgroup to finish, behind an atomic count,
+// measured ten times slower: the device-scope fences it needs write back and
+// invalidate the L2 under every other workgroup.)  The bound is HBM: each position's key and value are read once (512
+// bytes per KV head and batch row).
 #include "gemv_impl.h"
 
 namespace m3 {
 namespace {
 
 constexpr int kHD = 128;
-constexpr int kChunk = 128;                      // positions per workgroup
 constexpr int kAThreads = 256;
-constexpr int kGroups = kAThreads / 16;          // 16-lane groups per workgroup
-constexpr int kPerGroup = kChunk / kGroups;      // positions per group
 constexpr float kLog2e = 1.4426950408889634f;
-
-// sum over the 16 lanes of a DPP row
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xB1>(v);     // quad_perm [1,0,3,2]
-  v += dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]
-  v += dpp_f<0x141>(v);    // row_half_mirror
-  v += dpp_f<0x140>(v);    // row_mirror
-  return v;
-}
 
 __global__ void rope_table_kernel(float* t, int max_pos, int half, double theta) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -93,134 +84,207 @@ struct AttnParams {
   float scale2;                                  // log2(e) / sqrt(head_dim)
   uint16_t* out;
   int ldo;
-  float* ws;                                     // [B][n_q][nchunks][2 + 128]
+  float* ws;                                     // [B][n_kv][nchunks][G][2 + 128]
 };
 
-template <int G>
-__global__ __launch_bounds__(kAThreads) void attn_partial_kernel(AttnParams p) {
-  __shared__ float sm[kGroups][G], sl[kGroups][G];
-  __shared__ float sacc[kGroups][G][kHD];
+template <int G, int CH>
+__global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
+  constexpr int PJ = CH / 64;                    // pass-1 positions per 4-lane group
+  constexpr int PI = CH / 8;                     // pass-2 positions per lane
+  constexpr int WP = CH / 4;                     // pass-2 positions per wave
+  __shared__ __align__(16) float S[CH][G];       // scores, then probabilities
+  __shared__ float Ms[G], Ls[G];
+  __shared__ __align__(16) float pacc[8][G][kHD];   // P.V partials of the 8 half-waves
   const int chunk = blockIdx.x % p.nchunks;
   const int kvh = (blockIdx.x / p.nchunks) % p.n_kv;
   const int b = blockIdx.x / (p.nchunks * p.n_kv);
-  const int tid = threadIdx.x, lane = tid & 63, grp = tid >> 4, ds = lane & 15;
-  const int t0 = chunk * kChunk;
-  const int t_end = min(p.T, t0 + kChunk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = chunk * CH;
+  const int n = min(p.T - t0, CH);               // positions of this chunk
+  const size_t base = ((size_t)b * p.n_kv + kvh) * (size_t)p.max_pos * kHD;
+  const uint16_t* kb = p.k + base;
+  const uint16_t* vb = p.v + base;
 
-  // this lane's 8 dimensions of the G query heads, in fp32
-  float q[G][8];
+  // pass 1 layout: a group of 4 lanes per position, lane li holding the
+  // 16-byte chunks 4 c + li (c < 4) of the row: positions grp + 64 j
+  const int grp = tid >> 2, li = tid & 3;
+  // loads retire in issue order: q first, then the keys pass 1 needs, then
+  // the values pass 2 needs
+  uint4 qr[G][4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p.q + (size_t)b * p.ldq +
-                                                     (size_t)(kvh * G + h) * kHD + 8 * ds);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q[h][2 * j] = bf2f(w[j] & 0xffffu);
-      q[h][2 * j + 1] = bf2f(w[j] >> 16);
-    }
+    for (int c = 0; c < 4; ++c)
+      qr[h][c] = *reinterpret_cast<const uint4*>(p.q + (size_t)b * p.ldq + (size_t)(kvh * G + h) * kHD +
+                                                 8 * (4 * c + li));
+  uint4 kr[PJ][4];
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    const int t = t0 + min(grp + 64 * j, n - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      kr[j][c] = *reinterpret_cast<const uint4*>(kb + (size_t)t * kHD + 8 * (4 * c + li));
   }
-  // the group's positions: t0 + grp + kGroups * j (a wave's four groups read
-  // four neighbouring rows); loads are clamped into [0, T) and masked below
-  const size_t base = ((size_t)b * p.n_kv + kvh) * (size_t)p.max_pos * kHD + 8 * ds;
-  uint4 kr[kPerGroup], vr[kPerGroup];
+  // pass 2 layout: lane owns dimensions 4 dq .. 4 dq + 3 of positions
+  // WP w + 2 i + sub (i < PI), so a wave load reads two whole rows
+  const int dq = lane & 31, sub = lane >> 5;
+  uint2 vr[PI];
 #pragma unroll
-  for (int j = 0; j < kPerGroup; ++j) {
-    const int t = min(t0 + grp + kGroups * j, p.T - 1);
-    kr[j] = *reinterpret_cast<const uint4*>(p.k + base + (size_t)t * kHD);
-    vr[j] = *reinterpret_cast<const uint4*>(p.v + base + (size_t)t * kHD);
+  for (int i = 0; i < PI; ++i) {
+    const int t = t0 + min(WP * wave + 2 * i + sub, n - 1);
+    vr[i] = *reinterpret_cast<const uint2*>(vb + (size_t)t * kHD + 4 * dq);
   }
-  float m[G], l[G], acc[G][8];
+
+  // pass 1: scores (base 2, scale folded in); masked positions get -inf
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kPerGroup; ++j) {
-    if (t0 + grp + kGroups * j >= t_end) break;  // uniform within the group
-    const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
-    const uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-    float kf[8], vf[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kf[2 * e] = bf2f(kw[e] & 0xffffu);
-      kf[2 * e + 1] = bf2f(kw[e] >> 16);
-      vf[2 * e] = bf2f(vw[e] & 0xffffu);
-      vf[2 * e + 1] = bf2f(vw[e] >> 16);
-    }
+  for (int j = 0; j < PJ; ++j) {
+    const int tc = grp + 64 * j;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float s = 0.f;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) s = fmaf(q[h][d], kf[d], s);
-      s = row16_sum(s) * p.scale2;
-      const float mn = fmaxf(m[h], s);
-      const float corr = exp2f(m[h] - mn), pr = exp2f(s - mn);
-      m[h] = mn;
-      l[h] = l[h] * corr + pr;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] = fmaf(pr, vf[d], acc[h][d] * corr);
+      for (int c = 0; c < 4; ++c) {
+        s = dot2(qr[h][c].x, kr[j][c].x, s);
+        s = dot2(qr[h][c].y, kr[j][c].y, s);
+        s = dot2(qr[h][c].z, kr[j][c].z, s);
+        s = dot2(qr[h][c].w, kr[j][c].w, s);
+      }
+      s += dpp_f<0xB1>(s);                       // the 4 lanes of the group
+      s += dpp_f<0x4E>(s);
+      if (li == 0) S[tc][h] = tc < n ? s * p.scale2 : -INFINITY;
     }
-  }
-  // the 16 group states of the workgroup, merged in LDS
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (ds == 0) {
-      sm[grp][h] = m[h];
-      sl[grp][h] = l[h];
-    }
-#pragma unroll
-    for (int d = 0; d < 8; ++d) sacc[grp][h][8 * ds + d] = acc[h][d];
   }
   __syncthreads();
+  // softmax over the chunk, one wave per head
+  for (int h = wave; h < G; h += 4) {
+    float e[PJ], m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) m = fmaxf(m, S[lane + 64 * j][h]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.f;
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) {
+      e[j] = exp2f(S[lane + 64 * j][h] - m);
+      S[lane + 64 * j][h] = e[j];
+      l += e[j];
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      Ms[h] = m;
+      Ls[h] = l;
+    }
+  }
+  __syncthreads();
+  // pass 2: P.V over this lane's positions and 4 dimensions
+  float acc[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < PI; ++i) {
+    const int tc = WP * wave + 2 * i + sub;
+    const float v0 = bf2f(vr[i].x & 0xffffu), v1 = bf2f(vr[i].x >> 16);
+    const float v2 = bf2f(vr[i].y & 0xffffu), v3 = bf2f(vr[i].y >> 16);
+    float prs[G];                                // 0 for masked positions
+#pragma unroll
+    for (int h = 0; h < G; ++h) prs[h] = S[tc][h];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pr = prs[h];
+      acc[h][0] = fmaf(pr, v0, acc[h][0]);
+      acc[h][1] = fmaf(pr, v1, acc[h][1]);
+      acc[h][2] = fmaf(pr, v2, acc[h][2]);
+      acc[h][3] = fmaf(pr, v3, acc[h][3]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    *reinterpret_cast<float4*>(&pacc[2 * wave + sub][h][4 * dq]) =
+        make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+  __syncthreads();
+  float* wrec = p.ws + (((size_t)b * p.n_kv + kvh) * p.nchunks) * (G * (2 + kHD));
   for (int o = tid; o < G * kHD; o += kAThreads) {
     const int h = o / kHD, d = o % kHD;
-    float M = -INFINITY;
+    float A = 0.f;
 #pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) M = fmaxf(M, sm[gi][h]);
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) {
-      const float e = sm[gi][h] == -INFINITY ? 0.f : exp2f(sm[gi][h] - M);
-      L = fmaf(sl[gi][h], e, L);
-      A = fmaf(sacc[gi][h][d], e, A);
-    }
-    const int qh = kvh * G + h;
+    for (int k = 0; k < 8; ++k) A += pacc[k][h][d];
     if (p.nchunks == 1) {
-      p.out[(size_t)b * p.ldo + (size_t)qh * kHD + d] = (uint16_t)f2bf(A / L);
+      p.out[(size_t)b * p.ldo + (size_t)(kvh * G + h) * kHD + d] = (uint16_t)f2bf(A / Ls[h]);
     } else {
-      float* w = p.ws + (((size_t)b * p.n_q + qh) * p.nchunks + chunk) * (2 + kHD);
+      float* w = wrec + ((size_t)chunk * G + h) * (2 + kHD);
       if (d == 0) {
-        w[0] = M;
-        w[1] = L;
+        w[0] = Ms[h];
+        w[1] = Ls[h];
       }
       w[2 + d] = A;
     }
   }
 }
 
-// chunks combined in order: one workgroup of 128 threads per (row, head)
+// chunks combined in order: one workgroup of 128 threads per (row, query
+// head).  The chunk maxima and sums are loaded in parallel into LDS; the P.V
+// sums are read eight chunks at a time, so their loads overlap.
+constexpr int kMaxChunks = M3_MAX_POS / 64;
+
+template <int G>
 __global__ __launch_bounds__(kHD) void attn_merge_kernel(AttnParams p) {
+  __shared__ float mc[kMaxChunks], lc[kMaxChunks];
+  __shared__ float red[2];
   const int qh = blockIdx.x % p.n_q, b = blockIdx.x / p.n_q, d = threadIdx.x;
-  const float* w = p.ws + ((size_t)b * p.n_q + qh) * p.nchunks * (2 + kHD);
-  float M = -INFINITY;
-  for (int c = 0; c < p.nchunks; ++c) M = fmaxf(M, w[c * (2 + kHD)]);
+  const int kvh = qh / G, h = qh % G;
+  const float* wrec = p.ws + (((size_t)b * p.n_kv + kvh) * p.nchunks) * (G * (2 + kHD)) + h * (2 + kHD);
+  constexpr size_t kStride = (size_t)G * (2 + kHD);   // floats from one chunk's record to the next
+  float mloc = -INFINITY;
+  for (int c = d; c < p.nchunks; c += kHD) {
+    mc[c] = wrec[c * kStride];
+    lc[c] = wrec[c * kStride + 1];
+    mloc = fmaxf(mloc, mc[c]);
+  }
+  // workgroup maximum of the chunk maxima (two waves)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+  if ((d & 63) == 0) red[d >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
   float L = 0.f, A = 0.f;
-  for (int c = 0; c < p.nchunks; ++c) {
-    const float* wc = w + c * (2 + kHD);
-    const float e = wc[0] == -INFINITY ? 0.f : exp2f(wc[0] - M);
-    L = fmaf(wc[1], e, L);
-    A = fmaf(wc[2 + d], e, A);
+  for (int c0 = 0; c0 < p.nchunks; c0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < p.nchunks ? wrec[(c0 + u) * kStride + 2 + d] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c0 + u >= p.nchunks) break;
+      const float e = exp2f(mc[c0 + u] - M);     // every chunk holds a position
+      L = fmaf(lc[c0 + u], e, L);
+      A = fmaf(v[u], e, A);
+    }
   }
   p.out[(size_t)b * p.ldo + (size_t)qh * kHD + d] = (uint16_t)f2bf(A / L);
 }
 
+template <int G>
+void launch_attn_g(const AttnParams& p, int CH, int B, hipStream_t s) {
+  const dim3 grid(B * p.n_kv * p.nchunks);
+  if (CH == 64)
+    hipLaunchKernelGGL((attn_kernel<G, 64>), grid, dim3(kAThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<G, 128>), grid, dim3(kAThreads), 0, s, p);
+  if (p.nchunks > 1) hipLaunchKernelGGL((attn_merge_kernel<G>), dim3(B * p.n_q), dim3(kHD), 0, s, p);
+}
+
 }  // namespace
 
-int attn_chunks(int T) { return (T + kChunk - 1) / kChunk; }
+// positions per workgroup: 128, or 64 where 128 would leave most CUs idle
+int attn_chunk_size(int B, int n_kv, int T) {
+  return (size_t)B * n_kv * ((T + 127) / 128) < 256 ? 64 : 128;
+}
+
+size_t attn_workspace_bytes(int B, int n_q, int n_kv, int T) {
+  const int ch = attn_chunk_size(B, n_kv, T), nc = (T + ch - 1) / ch;
+  return nc == 1 ? 0 : (size_t)B * n_q * nc * (2 + kHD) * sizeof(float);
+}
 
 hipError_t launch_rope_table(float* t, int max_pos, int head_dim, double theta, hipStream_t s) {
   const int half = head_dim / 2, n = max_pos * half;
@@ -242,19 +306,17 @@ hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, i
 
 hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv,
                                    const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
-                                   int T, uint16_t* out, int ldo, float* ws, hipStream_t s) {
-  AttnParams p{q, ldq, k_cache, v_cache, n_q, n_kv, max_pos, T, attn_chunks(T),
-               kLog2e / sqrtf((float)kHD), out, ldo, ws};
-  const dim3 grid(B * n_kv * p.nchunks);
+                                   int T, uint16_t* out, int ldo, void* ws, hipStream_t s) {
+  const int ch = attn_chunk_size(B, n_kv, T);
+  const int nc = (T + ch - 1) / ch;
+  AttnParams p{q, ldq, k_cache, v_cache, n_q, n_kv, max_pos, T, nc, kLog2e / sqrtf((float)kHD),
+               out, ldo, static_cast<float*>(ws)};
   switch (n_q / n_kv) {
-    case 1: hipLaunchKernelGGL(attn_partial_kernel<1>, grid, dim3(kAThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(attn_partial_kernel<2>, grid, dim3(kAThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(attn_partial_kernel<4>, grid, dim3(kAThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL(attn_partial_kernel<8>, grid, dim3(kAThreads), 0, s, p); break;
+    case 1: launch_attn_g<1>(p, ch, B, s); break;
+    case 2: launch_attn_g<2>(p, ch, B, s); break;
+    case 4: launch_attn_g<4>(p, ch, B, s); break;
+    default: launch_attn_g<8>(p, ch, B, s); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nchunks == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(B * n_q), dim3(kHD), 0, s, p);
   return hipGetLastError();
 }
 

@@ -705,10 +705,9 @@ int m3_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv, in
                                         static_cast<hipStream_t>(stream)));
 }
 
-size_t m3_attention_workspace_bytes(int B, int n_q, int T) {
-  if (B < 1 || n_q < 1 || T < 1) return 0;
-  const int nc = attn_chunks(T);
-  return nc == 1 ? 0 : (size_t)B * n_q * nc * (2 + M3_HEAD_DIM) * sizeof(float);
+size_t m3_attention_workspace_bytes(int B, int n_q, int n_kv, int T) {
+  if (B < 1 || B > M3_MAX_B || !attn_heads_ok(n_q, n_kv) || T < 1 || T > M3_MAX_POS) return 0;
+  return attn_workspace_bytes(B, n_q, n_kv, T);
 }
 
 int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, int head_dim,
@@ -720,7 +719,7 @@ int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, in
   if (B < 1 || B > M3_MAX_B || max_pos < 1 || max_pos > M3_MAX_POS || T < 1 || T > max_pos)
     return M3_ERR_SHAPE;
   if (ldq < n_q * M3_HEAD_DIM || ldo < n_q * M3_HEAD_DIM) return M3_ERR_SHAPE;
-  const size_t need = m3_attention_workspace_bytes(B, n_q, T);
+  const size_t need = attn_workspace_bytes(B, n_q, n_kv, T);
   if (need && !workspace) return M3_ERR_NULL;
   if (workspace_bytes < need) return M3_ERR_WORKSPACE;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
@@ -734,8 +733,7 @@ int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, in
                 overlap(workspace, need, k_cache, c_b) || overlap(workspace, need, v_cache, c_b))))
     return M3_ERR_ALIAS;
   return hip_status(launch_decode_attention(q, B, ldq, n_q, n_kv, k_cache, v_cache, max_pos, T, out,
-                                            ldo, static_cast<float*>(workspace),
-                                            static_cast<hipStream_t>(stream)));
+                                            ldo, workspace, static_cast<hipStream_t>(stream)));
 }
 
 uint64_t m3_frame_weight_bytes(const m3_config* c) {

@@ -151,7 +151,8 @@ hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const f
                                float eps, uint16_t* a, int lda, hipStream_t s);
 
 // ---- decode attention (attention.hip) --------------------------------------------
-int attn_chunks(int T);   // workgroups per (row, KV head): ceil(T / 128)
+int attn_chunk_size(int B, int n_kv, int T);
+size_t attn_workspace_bytes(int B, int n_q, int n_kv, int T);
 hipError_t launch_rope_table(float* t, int max_pos, int head_dim, double theta, hipStream_t s);
 hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
                                const float* q_gamma, const float* k_gamma, float eps,
@@ -159,7 +160,7 @@ hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, i
                                uint16_t* k_cache, uint16_t* v_cache, int max_pos, hipStream_t s);
 hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv,
                                    const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
-                                   int T, uint16_t* out, int ldo, float* ws, hipStream_t s);
+                                   int T, uint16_t* out, int ldo, void* ws, hipStream_t s);
 
 // ---- frame helpers -------------------------------------------------------------
 // audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)

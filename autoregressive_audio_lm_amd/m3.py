@@ -232,8 +232,14 @@ def qk_norm_rope(qkv: torch.Tensor, n_q: int, n_kv: int, q_gamma: torch.Tensor,
     return q_out
 
 
-def attention_workspace_bytes(B: int, n_q: int, T: int) -> int:
-    return int(lib().m3_attention_workspace_bytes(int(B), int(n_q), int(T)))
+def attention_workspace_bytes(B: int, n_q: int, n_kv: int, T: int) -> int:
+    return int(lib().m3_attention_workspace_bytes(int(B), int(n_q), int(n_kv), int(T)))
+
+
+def attention_workspace(B: int, n_q: int, n_kv: int, T: int, device="cuda") -> torch.Tensor:
+    """A workspace for m3_decode_attention at these sizes."""
+    return torch.empty(max(16, attention_workspace_bytes(B, n_q, n_kv, T)), dtype=torch.uint8,
+                       device=device)
 
 
 def decode_attention(q: torch.Tensor, n_q: int, n_kv: int, k_cache: torch.Tensor,
@@ -246,9 +252,9 @@ def decode_attention(q: torch.Tensor, n_q: int, n_kv: int, k_cache: torch.Tensor
     B = q.shape[0]
     if out is None:
         out = torch.empty(B, n_q * HEAD_DIM, dtype=torch.bfloat16, device=q.device)
-    need = attention_workspace_bytes(B, n_q, T)
+    need = attention_workspace_bytes(B, n_q, n_kv, T)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = attention_workspace(B, n_q, n_kv, T, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().m3_decode_attention(_ptr(q), B, q.stride(0), int(n_q), int(n_kv), HEAD_DIM,
                                     _ptr(k_cache), _ptr(v_cache), k_cache.shape[2], int(T),

@@ -287,6 +287,63 @@ def time_prefill(c, stream, M=600, reps=10):
             "prompt_prefill_ms_36_layers": round(36 * layer_us / 1e3, 3)}
 
 
+def time_attention(c, stream, B, T=1800, layers=36, reps=5):
+    """Decode attention of one frame: for each of the body's layers, the q/k
+    norm + RoPE with the cache write, then attention over T cached positions
+    (60 s of frames at 25 per second plus a 300-token prompt), each layer with
+    its own cache (so the caches stream from HBM).  Timed as a captured graph
+    of all layers, replayed, HIP events on the launch stream."""
+    import torch
+    from autoregressive_audio_lm_amd import m3, synth
+    n_q, n_kv = c.n_heads, c.n_kv_heads
+    dev = "cuda"
+    ldqkv = (n_q + 2 * n_kv) * 128
+    qkv = synth.normal_bf16((B, ldqkv), 70, 1.5, dev)
+    qg, kg = synth.gamma_f32(128, 71, dev), synth.gamma_f32(128, 72, dev)
+    rope = m3.rope_table(T)
+    caches = []
+    for L in range(layers):
+        kc = synth.normal_bf16((B, n_kv, T, 128), 80 + L, 1.0, dev)
+        vc = synth.normal_bf16((B, n_kv, T, 128), 180 + L, 1.0, dev)
+        caches.append((kc, vc))
+    q = torch.empty(B, n_q * 128, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    ws = m3.attention_workspace(B, n_q, n_kv, T)
+
+    def frame(attn_only):
+        for kc, vc in caches:
+            if not attn_only:
+                m3.qk_norm_rope(qkv, n_q, n_kv, qg, kg, rope, T - 1, kc, vc, q_out=q, stream=stream)
+            m3.decode_attention(q, n_q, n_kv, kc, vc, T, out=out, workspace=ws, stream=stream)
+
+    res = {}
+    with torch.cuda.stream(stream):
+        for attn_only in (False, True):
+            frame(attn_only)
+            stream.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                frame(attn_only)
+            g.replay()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            stream.synchronize()
+            res[attn_only] = e0.elapsed_time(e1) * 1e3 / reps
+            del g
+    del caches
+    kv_bytes = layers * B * n_kv * T * 128 * 2 * 2
+    us = res[True]
+    return {"B": B, "T": T, "layers": layers, "frame_us": round(res[False], 1),
+            "attention_only_us": round(us, 1), "kv_bytes": kv_bytes,
+            "GB_s": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def kernel_source_hash(which: str = "gate_up") -> str:
     import hashlib
     h = hashlib.sha256()
@@ -455,6 +512,8 @@ def main():
     log(f"[bench] cfg draw {cfg_draw}")
     prefill = time_prefill(dm.config, stream)
     log(f"[bench] prefill {prefill}")
+    attention = [time_attention(dm.config, stream, b) for b in (1, 16)]
+    log(f"[bench] attention {attention}")
     paths_ms = {k: round(v["ms"], 4) for k, v in res.items()}
     for v in res.values():
         v["state"].release()
@@ -544,6 +603,8 @@ def main():
                                "one workgroup per song)", "points": cfg_draw},
         "guided_frame": guided,
         "prefill": prefill,
+        "attention": {"kernel": "attn_partial_kernel + attn_merge_kernel (body, 32:8 heads; "
+                                "caches [B, 8, T, 128] bf16, one per layer)", "points": attention},
         "gpu": f"{props.name} {props.gcnArchName} x{props.multi_processor_count} CU",
     }
     print(json.dumps(out), flush=True)

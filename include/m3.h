@@ -283,12 +283,14 @@ int m3_prefill_gemm(const void* packed_bf16, int N, int K, const uint16_t* a, in
  * m3_decode_attention: out[b, h*128 + d] = bf16( sum_{t<T} p_t v[b][h/g][t][d] ),
  * p = softmax_t( q[b,h] . k[b][h/g][t] / sqrt(128) ), fp32 sums and softmax
  * (base-2 exponentials with the scale folded in).  Positions are split into
- * chunks of 128; with more than one chunk the partial softmax states go to the
- * workspace (m3_attention_workspace_bytes(B, n_q, T) bytes, 0 when T <= 128,
- * 16-byte aligned, caller-owned, no contents kept between calls) and a second
- * launch merges them in chunk order.  1 <= T <= max_pos; ldq, ldo >= n_q * 128,
- * multiples of 8; q, caches, out 16-byte aligned; out and the workspace overlap
- * nothing else.
+ * chunks of 128 (64 when B * n_kv * ceil(T / 128) < 256); with more than one
+ * chunk the partial softmax states go to the workspace and a second launch
+ * merges them in chunk order.  The workspace (m3_attention_workspace_bytes(B,
+ * n_q, n_kv, T) bytes, 0 for a single chunk; device, 16-byte aligned,
+ * caller-owned, no contents kept between calls) may be shared by calls that
+ * do not overlap in time.  1 <= T <= max_pos; ldq, ldo >= n_q *
+ * 128, multiples of 8; q, caches, out 16-byte aligned; out and the workspace
+ * overlap nothing else.
  *
  * Errors (all three calls): M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_ALIGN,
  * M3_ERR_WORKSPACE, M3_ERR_ALIAS before any launch; M3_ERR_HIP if a launch fails. */
@@ -297,7 +299,7 @@ int m3_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv, in
                     const float* q_gamma, const float* k_gamma, float eps, const float* rope,
                     int pos, uint16_t* q_out, int ldq, uint16_t* k_cache, uint16_t* v_cache,
                     int max_pos, void* stream);
-size_t m3_attention_workspace_bytes(int B, int n_q, int T);
+size_t m3_attention_workspace_bytes(int B, int n_q, int n_kv, int T);
 int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, int head_dim,
                         const uint16_t* k_cache, const uint16_t* v_cache, int max_pos, int T,
                         uint16_t* out, int ldo, void* workspace, size_t workspace_bytes,

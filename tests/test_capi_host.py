@@ -141,9 +141,13 @@ def test_attention_refusals(L):
     """Decode attention: sizes, head groups, alignment, workspace and aliasing
     are refused on the host, before any launch."""
     P = ctypes.c_void_p
-    assert L.m3_attention_workspace_bytes(1, 32, 128) == 0
-    assert L.m3_attention_workspace_bytes(2, 32, 129) == 2 * 32 * 2 * 130 * 4
-    assert L.m3_attention_workspace_bytes(1, 32, 1800) == 32 * 15 * 130 * 4
+
+    assert L.m3_attention_workspace_bytes(1, 32, 8, 64) == 0                    # one chunk of 64
+    assert L.m3_attention_workspace_bytes(1, 32, 8, 65) == 32 * 2 * 130 * 4
+    assert L.m3_attention_workspace_bytes(1, 32, 8, 1800) == 32 * 29 * 130 * 4   # 64 wide
+    assert L.m3_attention_workspace_bytes(16, 32, 8, 1800) == 16 * 32 * 15 * 130 * 4
+    assert L.m3_attention_workspace_bytes(2, 32, 8, 128) == 2 * 32 * 2 * 130 * 4
+    assert L.m3_attention_workspace_bytes(2, 24, 8, 300) == 0                   # unsupported heads
     tab = P(0x1000000)
     assert L.m3_rope_table(None, 16, 128, 1e6, None) == _lib.M3_ERR_NULL
     assert L.m3_rope_table(tab, 16, 64, 1e6, None) == _lib.M3_ERR_SHAPE
@@ -168,8 +172,8 @@ def test_attention_refusals(L):
     assert L.m3_qk_norm_rope(*q_arg(qo=P(0x20000008))) == _lib.M3_ERR_ALIGN
     assert L.m3_qk_norm_rope(*q_arg(vc=P(0x40000000 + cb - 256))) == _lib.M3_ERR_ALIAS
     assert L.m3_qk_norm_rope(*q_arg(qo=P(0x10000000 + 4096))) == _lib.M3_ERR_ALIAS
-    # attention: T = 300 needs three chunks of workspace
-    need = L.m3_attention_workspace_bytes(2, 32, 300)
+    # attention: T = 300 needs workspace (five chunks of 64 at B * n_kv = 16)
+    need = L.m3_attention_workspace_bytes(2, 32, 8, 300)
     a_arg = lambda **k: (k.get("q", P(0x20000000)), k.get("B", 2), k.get("ldq", 4096), k.get("nq", 32),
                          k.get("nkv", 8), k.get("hd", 128), k.get("kc", P(0x40000000)),
                          k.get("vc", P(0x48000000)), k.get("mp", 512), k.get("T", 300),
@@ -186,7 +190,7 @@ def test_attention_refusals(L):
     assert L.m3_decode_attention(*a_arg(out=P(0x20000000 + 64))) == _lib.M3_ERR_ALIAS
     assert L.m3_decode_attention(*a_arg(ws=P(0x40000000))) == _lib.M3_ERR_ALIAS
     # one chunk: no workspace needed
-    assert L.m3_attention_workspace_bytes(2, 32, 128) == 0
+    assert L.m3_attention_workspace_bytes(2, 16, 16, 64) == 0
 
 
 def test_cfg_draw_refusals(L):

@@ -97,7 +97,7 @@ def test_strides_and_workspace_reuse():
     B, n_q, n_kv, T = 2, 32, 8, 300
     kc, vc = fill_cache(B, n_kv, 512, T, 5, 2.0)
     q = rnd_bf16((B, n_q * HD + 128), 6)
-    ws = torch.empty(m3.attention_workspace_bytes(B, n_q, T) + 256, dtype=torch.uint8, device=DEV)
+    ws = m3.attention_workspace(B, n_q, n_kv, T)
     out = torch.zeros(B, n_q * HD + 64, dtype=torch.bfloat16, device=DEV)
     kd, vd, qd = dev(kc), dev(vc), dev(q)
     for T_ in (T, 129, 40):
