@@ -77,7 +77,7 @@ class SampleParams(ctypes.Structure):
 
 class Layer(ctypes.Structure):
     _fields_ = [("qkv", Mat), ("o", Mat), ("gu", Mat), ("down", Mat),
-                ("attn_norm", _P), ("ffn_norm", _P)]
+                ("attn_norm", _P), ("ffn_norm", _P), ("q_norm", _P), ("k_norm", _P)]
 
 
 class Model(ctypes.Structure):
@@ -91,7 +91,9 @@ class Model(ctypes.Structure):
                 ("p_in", Mat), ("emb1", _P), ("emb", _P), ("d_layers_w", _P),
                 ("d_final_norm", _P), ("heads", _P), ("tok_emb_audio", _P),
                 ("audio_emb", _P), ("eps", ctypes.c_float), ("cfg_scale", ctypes.c_float),
-                ("top_k", ctypes.c_int)]
+                ("top_k", ctypes.c_int), ("attention", ctypes.c_int), ("max_pos", ctypes.c_int),
+                ("pos0", ctypes.c_int), ("rope", _P), ("kcache", _P), ("vcache", _P),
+                ("dkcache", _P), ("dvcache", _P)]
 
 
 class FrameTrace(ctypes.Structure):
@@ -398,9 +400,13 @@ class OracleModel:
     """Wraps a model dict (see autoregressive_audio_lm_amd.synth) into the C
     struct.  The oracle quantises int8 formats itself from the bf16 sources."""
 
-    def __init__(self, md: dict, cfg_scale: float = 1.5, top_k: int = 0):
+    def __init__(self, md: dict, cfg_scale: float = 1.5, top_k: int = 0, attention: int = 0,
+                 max_pos: int = 0, pos0: int = 0):
         """top_k == 0: per-row draws; top_k > 0: the reference's draw over
-        (conditional, unconditional) row pairs with guidance cfg_scale."""
+        (conditional, unconditional) row pairs with guidance cfg_scale.
+        attention == 1: decode attention over KV caches of max_pos positions
+        (frame f at position pos0 + f); the caches are made zeroed for the
+        batch size of the first frame (and again by reset_attention)."""
         self._keep = []
         cfg = md["cfg"]
         fb, fl, fd = md["fmt_body"], md["fmt_lm"], md["fmt_depth"]
@@ -417,9 +423,11 @@ class OracleModel:
 
         def layer(Ld, fmt):
             gu = interleave_gate_up(Ld["gate"], Ld["up"])
+            qn = _ptr(keep(Ld["q_norm"], np.float32)) if "q_norm" in Ld else None
+            kn = _ptr(keep(Ld["k_norm"], np.float32)) if "k_norm" in Ld else None
             return Layer(mat(Ld["qkv"], fmt), mat(Ld["o"], fmt), mat(gu, fmt),
                          mat(Ld["down"], fmt), _ptr(keep(Ld["attn_norm"], np.float32)),
-                         _ptr(keep(Ld["ffn_norm"], np.float32)))
+                         _ptr(keep(Ld["ffn_norm"], np.float32)), qn, kn)
 
         nl = len(md["layers"])
         LA = (Layer * max(nl, 1))(*[layer(L, fb) for L in md["layers"]])
@@ -441,7 +449,30 @@ class OracleModel:
             ctypes.cast(emb_arr, ctypes.c_void_p), ctypes.cast(DL, ctypes.c_void_p),
             _ptr(keep(md["d_final_norm"], np.float32)), ctypes.cast(heads, ctypes.c_void_p),
             _ptr(keep(md["tok_emb_audio"], np.uint16)), ctypes.cast(aemb_arr, ctypes.c_void_p),
-            float(cfg["eps"]), float(cfg_scale), int(top_k))
+            float(cfg["eps"]), float(cfg_scale), int(top_k), int(attention), int(max_pos),
+            int(pos0))
+        self.cache_B = None
+        if attention:
+            self._rope = rope_table(max(max_pos, 8), cfg["head_dim"])
+            self.m.rope = _ptr(self._rope)
+
+    def reset_attention(self, B: int) -> None:
+        """Fresh zeroed KV caches for B rows (attention mode)."""
+        cfg, mp = self.cfg, self.m.max_pos
+        self.kcache = [np.zeros((B, cfg["n_kv_heads"], mp, cfg["head_dim"]), np.uint16)
+                       for _ in range(self.m.n_layers)]
+        self.vcache = [np.zeros_like(c) for c in self.kcache]
+        self.dkcache = [np.zeros((B, cfg["d_heads"], 8, cfg["d_head_dim"]), np.uint16)
+                        for _ in range(self.m.d_layers)]
+        self.dvcache = [np.zeros_like(c) for c in self.dkcache]
+        arrs = []
+        for name in ("kcache", "vcache", "dkcache", "dvcache"):
+            lst = getattr(self, name)
+            arr = (ctypes.c_void_p * max(len(lst), 1))(*[c.ctypes.data for c in lst])
+            arrs.append(arr)
+            setattr(self.m, name, ctypes.cast(arr, ctypes.c_void_p))
+        self._cache_arrs = arrs
+        self.cache_B = B
 
 
 def decode_frame(om: OracleModel, x_in, seed, frame, temperature=1.0, trace=False):
@@ -450,6 +481,8 @@ def decode_frame(om: OracleModel, x_in, seed, frame, temperature=1.0, trace=Fals
     x = _c(x_in, np.uint16)
     B, H = x.shape
     cfg = om.cfg
+    if om.m.attention and om.cache_B != B:
+        om.reset_attention(B)
     codes = np.empty((B, 8), np.int32)
     xn = np.empty((B, H), np.uint16)
     tr_d = None

@@ -568,16 +568,33 @@ void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, 
 /* ------------------------------------------------------------------ */
 /* One frame ([ds] stage 2; [metal] frame bookkeeping).                 */
 /* ------------------------------------------------------------------ */
+/* one layer's attention over a KV cache: the new position pos is written,
+   positions 0 .. pos are attended (NULL: the identity stub) */
+typedef struct {
+  const float* rope;
+  uint16_t* kc;
+  uint16_t* vc;
+  int max_pos, pos;
+  uint16_t* qbuf;                /* [B, n_heads * hd] */
+} m3o_attn_at;
+
 static void run_layer(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads,
                       int n_kv, int hd, int F, float eps, uint16_t* a, uint16_t* qkvb,
-                      uint16_t* o, uint16_t* mm, double* y) {
+                      uint16_t* o, uint16_t* mm, double* y, const m3o_attn_at* at) {
   int nq = n_heads * hd, nkv = n_kv * hd;
   int nqkv = nq + 2 * nkv;
   /* attention block */
   m3o_rmsnorm(h, B, Hd, Hd, L->attn_norm, eps, a, Hd);
   m3o_gemv(&L->qkv, a, B, Hd, y);
   m3o_f64_to_bf16_n(y, qkvb, (size_t)B * nqkv);
-  m3o_attn_stub(qkvb, B, nqkv, nq + nkv, n_heads, n_heads / n_kv, hd, o);
+  if (at) {
+    m3o_qk_norm_rope(qkvb, B, nqkv, n_heads, n_kv, hd, L->q_norm, L->k_norm, eps, at->rope,
+                     at->pos, at->qbuf, at->kc, at->vc, at->max_pos);
+    m3o_decode_attention(at->qbuf, B, n_heads, n_kv, hd, at->kc, at->vc, at->max_pos, at->pos + 1,
+                         o);
+  } else {
+    m3o_attn_stub(qkvb, B, nqkv, nq + nkv, n_heads, n_heads / n_kv, hd, o);
+  }
   m3o_gemv(&L->o, o, B, nq, y);
   m3o_residual(y, h, B * Hd, h);
   /* MLP block */
@@ -628,10 +645,18 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
   float* zb = (float*)malloc((size_t)B * 4);
   float* z2 = (float*)malloc((size_t)B * 4);
 
+  uint16_t* qbuf = (uint16_t*)malloc((size_t)B * (nq > dq ? nq : dq) * 2);
+  /* the body position of this frame (held below max_pos, as the GPU does) */
+  long bpos = (long)m->pos0 + (long)frame;
+  if (m->attention && bpos >= m->max_pos) bpos = m->max_pos - 1;
+
   memcpy(h, x_in, (size_t)B * H * 2);
-  for (int l = 0; l < m->n_layers; ++l)
+  for (int l = 0; l < m->n_layers; ++l) {
+    m3o_attn_at at = {m->rope, m->attention ? m->kcache[l] : NULL,
+                      m->attention ? m->vcache[l] : NULL, m->max_pos, (int)bpos, qbuf};
     run_layer(&m->layers[l], h, B, H, m->n_heads, m->n_kv_heads, m->head_dim, m->F,
-              m->eps, a, qkvb, o, mm, y);
+              m->eps, a, qkvb, o, mm, y, m->attention ? &at : NULL);
+  }
   if (tr && tr->h_body) memcpy(tr->h_body, h, (size_t)B * H * 2);
 
   /* final norm -> sliced lm_head -> draw 0 over the reachable rows */
@@ -668,9 +693,13 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
         hd[(size_t)b * D + k] = m3o_f64_to_bf16(m3o_bf16_to_f64(u[(size_t)b * D + k]) +
                                                 m3o_bf16_to_f64(E[(size_t)prev * D + k]));
     }
-    for (int l = 0; l < m->d_layers; ++l)
+    for (int l = 0; l < m->d_layers; ++l) {
+      /* step j attends over the frame's codebook positions 0 .. j - 1 */
+      m3o_attn_at at = {m->rope, m->attention ? m->dkcache[l] : NULL,
+                        m->attention ? m->dvcache[l] : NULL, 8, j - 1, qbuf};
       run_layer(&m->d_layers_w[l], hd, B, D, m->d_heads, m->d_heads, m->d_head_dim, m->Fd,
-                m->eps, a, qkvb, o, mm, y);
+                m->eps, a, qkvb, o, mm, y, m->attention ? &at : NULL);
+    }
     m3o_rmsnorm(hd, B, D, D, m->d_final_norm, m->eps, a, D);
     m3o_gemv(&m->heads[j - 1], a, B, D, y);
     for (size_t i = 0; i < (size_t)B * m->code_vocab; ++i) lg[i] = (float)y[i];
@@ -695,5 +724,5 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
     }
   }
   free(y); free(h); free(a); free(qkvb); free(o); free(mm); free(u); free(hd);
-  free(lg); free(draw_out); free(zb); free(z2);
+  free(lg); free(draw_out); free(zb); free(z2); free(qbuf);
 }

@@ -134,6 +134,7 @@ void m3o_cfg_topk_draw(const float* logits, int S, int V, int ldl, float scale, 
 typedef struct {
   m3o_mat qkv, o, gu, down;      /* gu: interleaved gate/up rows [2F, H] */
   const float* attn_norm; const float* ffn_norm;
+  const float* q_norm; const float* k_norm;   /* [head_dim]; attention only */
 } m3o_layer;
 
 typedef struct {
@@ -160,6 +161,18 @@ typedef struct {
      pairs (B even) with guidance scale cfg_scale ([ds] stage 2) */
   float cfg_scale;
   int top_k;
+  /* attention: 0 the identity stub; 1 decode attention (m3o_qk_norm_rope,
+     m3o_decode_attention) with frame f at body position pos0 + f over the
+     caches kcache[l], vcache[l] ([B][n_kv][max_pos][hd], kept across frames),
+     and the depth decoder's step j at position j - 1 over dkcache[l],
+     dvcache[l] ([B][d_heads][8][d_head_dim], rewritten every frame); rope is
+     an m3o_rope_table of at least max(max_pos, 8) positions */
+  int attention, max_pos, pos0;
+  const float* rope;
+  uint16_t* const* kcache;
+  uint16_t* const* vcache;
+  uint16_t* const* dkcache;
+  uint16_t* const* dvcache;
 } m3o_model;
 
 typedef struct {

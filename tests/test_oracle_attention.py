@@ -208,3 +208,47 @@ def test_matches_torch_sdpa_float64(oracle, T):
     ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).numpy()
     want = bf16(ref.reshape(B, n_q * HD))
     assert np.mean(out == want) >= 0.99 and ulps_apart(out, want).max() <= 1
+
+
+def _small_model(seed=3):
+    from autoregressive_audio_lm_amd import configs, synth
+    cfg = configs.config("frame-small")
+    md = synth.model_to_numpy(synth.make_model(cfg, configs.BF16, configs.BF16, configs.I8G128,
+                                               seed=seed))
+    return cfg, md, synth
+
+
+def test_frame_at_position_zero_has_the_stub_body(oracle):
+    """Attention over one cached position is the identity stub: the first
+    frame at position 0 has the stub frame's body output, semantic code and
+    first depth code (the depth step 1 also attends over one position)."""
+    cfg, md, synth = _small_model()
+    x = synth.bits(synth.activations(3, cfg["H"], seed=6))
+    stub = oracle.OracleModel(md)
+    att = oracle.OracleModel(md, attention=1, max_pos=16, pos0=0)
+    c_s, x_s, t_s = oracle.decode_frame(stub, x, seed=8, frame=0, trace=True)
+    c_a, x_a, t_a = oracle.decode_frame(att, x, seed=8, frame=0, trace=True)
+    assert np.array_equal(t_s["h_body"], t_a["h_body"])
+    assert np.array_equal(c_s[:, :2], c_a[:, :2])
+
+
+def test_frames_fill_the_cache_at_their_positions(oracle):
+    """Frame f writes k and v at body position pos0 + f of every layer; later
+    frames read the earlier positions (so their body output changes)."""
+    cfg, md, synth = _small_model()
+    x = synth.bits(synth.activations(2, cfg["H"], seed=7))
+    att = oracle.OracleModel(md, attention=1, max_pos=16, pos0=4)
+    stub = oracle.OracleModel(md)
+    for f in range(3):
+        _, _, ta = oracle.decode_frame(att, x, seed=1, frame=f, trace=True)
+        _, _, ts = oracle.decode_frame(stub, x, seed=1, frame=f, trace=True)
+        # position 4 + f attends over 5 + f positions (the prompt's, zero here, and the
+        # frames' own), so the body differs from the stub's
+        assert not np.array_equal(ta["h_body"], ts["h_body"])
+    for kc, vc in zip(att.kcache, att.vcache):
+        filled = np.any(kc != 0, axis=(0, 1, 3))
+        assert filled.tolist() == [p in (4, 5, 6) for p in range(16)]
+        assert np.array_equal(np.any(vc != 0, axis=(0, 1, 3)), filled)
+    # the depth caches hold the 7 codebook positions of the last frame
+    for dk in att.dkcache:
+        assert np.any(dk != 0, axis=(0, 1, 3)).tolist() == [True] * 7 + [False]
