@@ -47,12 +47,13 @@ class Config(ctypes.Structure):
                                   "d_head_dim", "d_ffn", "n_codebooks", "code_vocab", "fmt_body",
                                   "fmt_lm", "fmt_depth")] + \
                [("eps", ctypes.c_float), ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64),
-                ("cfg_scale", ctypes.c_float), ("top_k", _I)]
+                ("cfg_scale", ctypes.c_float), ("top_k", _I),
+                ("attention", _I), ("max_pos", _I), ("pos0", _I)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [("qkv", _P), ("o", _P), ("gate_up", _P), ("down", _P),
-                ("attn_norm", _P), ("ffn_norm", _P)]
+                ("attn_norm", _P), ("ffn_norm", _P), ("q_norm", _P), ("k_norm", _P)]
 
 
 class Model(ctypes.Structure):
@@ -65,8 +66,11 @@ class FrameLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("x", "h", "qkv", "mlp", "logits", "u", "hd", "dqkv",
                                                "dmlp", "dlogits", "ring", "frame", "part_sem", "part_dep",
                                                "flags", "err", "seq", "phases", "th", "tqkv", "tmlp", "tu",
-                                               "thd", "tdqkv", "tdmlp", "total")]
+                                               "thd", "tdqkv", "tdmlp", "rope", "aq", "ao", "kcache",
+                                               "vcache", "dkcache", "dvcache", "attn_ws", "total")]
 
+
+M3_ERR_ATTN_FULL = 2      # frame state err word: the frame position reached max_pos
 
 _lib = None
 

@@ -45,14 +45,27 @@ __global__ void rope_table_kernel(float* t, int max_pos, int half, double theta)
   t[2 * idx + 1] = (float)sin(ang);
 }
 
+// position of a frame-driven call: pos0 + the frame counter, held below
+// max_pos (a frame past the cache rewrites the last slot and flags err)
+__device__ __forceinline__ int frame_pos(const uint32_t* frame_dev, int pos0, int max_pos,
+                                         uint32_t* err) {
+  const long p = (long)pos0 + (long)*frame_dev;
+  if (p < max_pos) return (int)p;
+  if (err && threadIdx.x == 0) atomicOr(err, M3_ERR_ATTN_FULL);
+  return max_pos - 1;
+}
+
 // One wave per head: lane l holds elements l and l + 64 (a rotation pair).
+// frame_dev (optional): the position is pos0 + *frame_dev instead of pos.
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv, const float* q_gamma,
     const float* k_gamma, float eps, const float* rope, int pos, uint16_t* q_out, int ldq,
-    uint16_t* k_cache, uint16_t* v_cache, int max_pos) {
+    uint16_t* k_cache, uint16_t* v_cache, int max_pos, const uint32_t* frame_dev, int pos0,
+    uint32_t* err) {
   const int heads = n_q + 2 * n_kv;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (w >= B * heads) return;
+  if (frame_dev) pos = frame_pos(frame_dev, pos0, max_pos, blockIdx.x == 0 ? err : nullptr);
   const int b = w / heads, hh = w % heads;
   const uint16_t* x = qkv + (size_t)b * ldqkv + (size_t)hh * kHD;
   const uint32_t x0 = x[lane], x1 = x[lane + 64];
@@ -85,7 +98,18 @@ struct AttnParams {
   uint16_t* out;
   int ldo;
   float* ws;                                     // [B][n_kv][nchunks][G][2 + 128]
+  const uint32_t* frame_dev;                     // optional: T = pos0 + *frame_dev + 1
+  int pos0;
+  int ch;                                        // positions per chunk
 };
+
+// positions attended: T, or the frame's position + 1 (grid and records are
+// sized for p.T = max_pos then)
+__device__ __forceinline__ int attn_T(const AttnParams& p) {
+  if (!p.frame_dev) return p.T;
+  const long t = (long)p.pos0 + (long)*p.frame_dev + 1;
+  return t < p.max_pos ? (int)t : p.max_pos;
+}
 
 template <int G, int CH>
 __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
@@ -99,8 +123,10 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
   const int kvh = (blockIdx.x / p.nchunks) % p.n_kv;
   const int b = blockIdx.x / (p.nchunks * p.n_kv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = attn_T(p), nc = (T + CH - 1) / CH;
+  if (chunk >= nc) return;                       // past the frame's position
   const int t0 = chunk * CH;
-  const int n = min(p.T - t0, CH);               // positions of this chunk
+  const int n = min(T - t0, CH);                 // positions of this chunk
   const size_t base = ((size_t)b * p.n_kv + kvh) * (size_t)p.max_pos * kHD;
   const uint16_t* kb = p.k + base;
   const uint16_t* vb = p.v + base;
@@ -210,7 +236,7 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
     float A = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) A += pacc[k][h][d];
-    if (p.nchunks == 1) {
+    if (nc == 1) {
       p.out[(size_t)b * p.ldo + (size_t)(kvh * G + h) * kHD + d] = (uint16_t)f2bf(A / Ls[h]);
     } else {
       float* w = wrec + ((size_t)chunk * G + h) * (2 + kHD);
@@ -234,10 +260,12 @@ __global__ __launch_bounds__(kHD) void attn_merge_kernel(AttnParams p) {
   __shared__ float red[2];
   const int qh = blockIdx.x % p.n_q, b = blockIdx.x / p.n_q, d = threadIdx.x;
   const int kvh = qh / G, h = qh % G;
+  const int nc = (attn_T(p) + p.ch - 1) / p.ch;
+  if (nc == 1) return;                           // the chunk kernel wrote the output
   const float* wrec = p.ws + (((size_t)b * p.n_kv + kvh) * p.nchunks) * (G * (2 + kHD)) + h * (2 + kHD);
   constexpr size_t kStride = (size_t)G * (2 + kHD);   // floats from one chunk's record to the next
   float mloc = -INFINITY;
-  for (int c = d; c < p.nchunks; c += kHD) {
+  for (int c = d; c < nc; c += kHD) {
     mc[c] = wrec[c * kStride];
     lc[c] = wrec[c * kStride + 1];
     mloc = fmaxf(mloc, mc[c]);
@@ -249,13 +277,13 @@ __global__ __launch_bounds__(kHD) void attn_merge_kernel(AttnParams p) {
   __syncthreads();
   const float M = fmaxf(red[0], red[1]);
   float L = 0.f, A = 0.f;
-  for (int c0 = 0; c0 < p.nchunks; c0 += 8) {
+  for (int c0 = 0; c0 < nc; c0 += 8) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = c0 + u < p.nchunks ? wrec[(c0 + u) * kStride + 2 + d] : 0.f;
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nc ? wrec[(c0 + u) * kStride + 2 + d] : 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (c0 + u >= p.nchunks) break;
+      if (c0 + u >= nc) break;
       const float e = exp2f(mc[c0 + u] - M);     // every chunk holds a position
       L = fmaf(lc[c0 + u], e, L);
       A = fmaf(v[u], e, A);
@@ -296,21 +324,25 @@ hipError_t launch_rope_table(float* t, int max_pos, int head_dim, double theta, 
 hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
                                const float* q_gamma, const float* k_gamma, float eps,
                                const float* rope, int pos, uint16_t* q_out, int ldq,
-                               uint16_t* k_cache, uint16_t* v_cache, int max_pos, hipStream_t s) {
+                               uint16_t* k_cache, uint16_t* v_cache, int max_pos, hipStream_t s,
+                               const uint32_t* frame_dev, int pos0, uint32_t* err) {
   const int waves = B * (n_q + 2 * n_kv);
   hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, B, ldqkv,
                      n_q, n_kv, q_gamma, k_gamma, eps, rope, pos, q_out, ldq, k_cache, v_cache,
-                     max_pos);
+                     max_pos, frame_dev, pos0, err);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv,
                                    const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
-                                   int T, uint16_t* out, int ldo, void* ws, hipStream_t s) {
-  const int ch = attn_chunk_size(B, n_kv, T);
-  const int nc = (T + ch - 1) / ch;
-  AttnParams p{q, ldq, k_cache, v_cache, n_q, n_kv, max_pos, T, nc, kLog2e / sqrtf((float)kHD),
-               out, ldo, static_cast<float*>(ws)};
+                                   int T, uint16_t* out, int ldo, void* ws, hipStream_t s,
+                                   const uint32_t* frame_dev, int pos0) {
+  // a frame-driven call sizes its grid and records for every position
+  const int Tg = frame_dev ? max_pos : T;
+  const int ch = attn_chunk_size(B, n_kv, Tg);
+  const int nc = (Tg + ch - 1) / ch;
+  AttnParams p{q, ldq, k_cache, v_cache, n_q, n_kv, max_pos, Tg, nc, kLog2e / sqrtf((float)kHD),
+               out, ldo, static_cast<float*>(ws), frame_dev, pos0, ch};
   switch (n_q / n_kv) {
     case 1: launch_attn_g<1>(p, ch, B, s); break;
     case 2: launch_attn_g<2>(p, ch, B, s); break;

@@ -166,6 +166,16 @@ int validate_config(const m3_config* c, int B) {
       gemv_smem_bytes(fd, d.H, B, true) > kLdsMax || gemv_smem_bytes(fd, d.D, B, true) > kLdsMax)
     return M3_ERR_SHAPE;
   if (c->n_layers > 1000 || c->d_layers > 1000) return M3_ERR_SHAPE;
+  // decode attention over the frame state's caches
+  if (c->attention != 0 && c->attention != 1) return M3_ERR_SHAPE;
+  if (c->attention) {
+    if (c->max_pos < 1 || c->max_pos > M3_MAX_POS || c->pos0 < 0 || c->pos0 >= c->max_pos)
+      return M3_ERR_SHAPE;
+    const int g = c->n_heads / c->n_kv_heads;
+    if ((g != 1 && g != 2 && g != 4 && g != 8) || c->n_heads > M3_MAX_HEADS ||
+        c->d_heads > M3_MAX_HEADS)
+      return M3_ERR_SHAPE;
+  }
   return M3_OK;
 }
 
@@ -211,6 +221,18 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.thd = take((size_t)B * d.D * 4);
   L.tdqkv = take((size_t)B * d.dqkv * 4);
   L.tdmlp = take((size_t)B * d.Fd * 4);
+  const bool at = c.attention != 0;
+  const int rope_pos = at ? std::max(c.max_pos, 8) : 0;
+  L.rope = take((size_t)rope_pos * 64 * 2 * 4);
+  L.aq = take(at ? (size_t)B * std::max(d.nq, d.dq) * 2 : 0);
+  L.ao = take(at ? (size_t)B * std::max(d.nq, d.dq) * 2 : 0);
+  const size_t kv = at ? (size_t)c.n_layers * B * c.n_kv_heads * c.max_pos * 128 * 2 : 0;
+  L.kcache = take(kv);
+  L.vcache = take(kv);
+  const size_t dkv = at ? (size_t)c.d_layers * B * c.d_heads * 8 * 128 * 2 : 0;
+  L.dkcache = take(dkv);
+  L.dvcache = take(dkv);
+  L.attn_ws = take(at ? attn_workspace_bytes(B, c.n_heads, c.n_kv_heads, c.max_pos) : 0);
   L.total = off;
   return L;
 }
@@ -228,6 +250,12 @@ int validate_model(const m3_model* m) {
     const m3_layer_weights& L = m->d_layers_w[l];
     if (!L.qkv || !L.o || !L.gate_up || !L.down || !L.attn_norm || !L.ffn_norm) return M3_ERR_NULL;
   }
+  if (m->cfg.attention) {
+    for (int l = 0; l < m->cfg.n_layers; ++l)
+      if (!m->layers[l].q_norm || !m->layers[l].k_norm) return M3_ERR_NULL;
+    for (int l = 0; l < m->cfg.d_layers; ++l)
+      if (!m->d_layers_w[l].q_norm || !m->d_layers_w[l].k_norm) return M3_ERR_NULL;
+  }
   for (int j = 0; j < m->cfg.n_codebooks - 1; ++j)
     if (!m->heads[j] || !m->audio_emb[j]) return M3_ERR_NULL;
   for (int j = 0; j < m->cfg.n_codebooks - 2; ++j)
@@ -243,9 +271,28 @@ int validate_model(const m3_model* m) {
 
 // Where the frame's steps go: launched one kernel each on a stream, or recorded
 // as the phases of one persistent launch.
+// one attention step of the frame: q/k norm + RoPE with the cache write, then
+// attention over the cache (frame_dev set: the position comes from the frame
+// counter; otherwise pos)
+struct AttnStep {
+  const uint16_t* qkv;
+  int ldqkv, n_q, n_kv;
+  const float *q_gamma, *k_gamma;
+  float eps;
+  const float* rope;
+  int pos;
+  uint16_t *q, *k_cache, *v_cache, *out;
+  int max_pos;
+  const uint32_t* frame_dev;
+  int pos0;
+  uint32_t* err;
+  void* ws;
+};
+
 struct FrameSink {
   virtual hipError_t gemv(const GemvDesc& d) = 0;
   virtual hipError_t cfg_draw(const CfgDesc& d) = 0;
+  virtual hipError_t attention(const AttnStep& a, int B) = 0;
   virtual hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                               const Best* last_part, int last_nparts, int32_t vocab_base,
                               int n_slice, int code_vocab, int n_cb, int B, int H, uint16_t* x,
@@ -257,6 +304,15 @@ struct LaunchSink final : FrameSink {
   explicit LaunchSink(hipStream_t st) : s(st) {}
   hipError_t gemv(const GemvDesc& d) override { return launch_gemv(d, s); }
   hipError_t cfg_draw(const CfgDesc& d) override { return launch_cfg_draw(d, s); }
+  hipError_t attention(const AttnStep& a, int B) override {
+    const int ld = a.n_q * 128;
+    hipError_t e = launch_qk_norm_rope(a.qkv, B, a.ldqkv, a.n_q, a.n_kv, a.q_gamma, a.k_gamma, a.eps,
+                                       a.rope, a.pos, a.q, ld, a.k_cache, a.v_cache, a.max_pos, s,
+                                       a.frame_dev, a.pos0, a.err);
+    if (e != hipSuccess) return e;
+    return launch_decode_attention(a.q, B, ld, a.n_q, a.n_kv, a.k_cache, a.v_cache, a.max_pos,
+                                   a.pos + 1, a.out, ld, a.ws, s, a.frame_dev, a.pos0);
+  }
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
@@ -270,8 +326,9 @@ struct PlanSink final : FrameSink {
   PersistPlan* pl;
   explicit PlanSink(PersistPlan* p) : pl(p) {}
   hipError_t gemv(const GemvDesc& d) override { return persist_add_gemv(pl, d); }
-  // (the persistent frame carries the per-row draws only)
+  // (the persistent frame carries the per-row draws and the attention stub only)
   hipError_t cfg_draw(const CfgDesc&) override { return hipErrorInvalidValue; }
+  hipError_t attention(const AttnStep&, int) override { return hipErrorInvalidValue; }
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
@@ -333,6 +390,21 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     ++ph;
     return e;
   };
+  // ---- attention (c.attention == 1): caches and buffers of the state ----
+  const bool attn = c.attention != 0;
+  const float* rope = reinterpret_cast<const float*>(S + L.rope);
+  uint16_t* aq = reinterpret_cast<uint16_t*>(S + L.aq);
+  uint16_t* ao = reinterpret_cast<uint16_t*>(S + L.ao);
+  uint32_t* err = reinterpret_cast<uint32_t*>(S + L.err);
+  auto attention = [&](const uint16_t* qkv_in, int ldq_in, int n_q, int n_kv,
+                       const m3_layer_weights& W, uint16_t* kc, uint16_t* vc, int max_pos,
+                       int pos, bool from_frame) {
+    AttnStep a{qkv_in, ldq_in, n_q, n_kv, W.q_norm, W.k_norm, eps, rope, pos, aq, kc, vc, ao,
+               max_pos, from_frame ? frame : nullptr, from_frame ? c.pos0 : 0, err,
+               S + L.attn_ws};
+    ++ph;
+    return sink.attention(a, B);
+  };
   // ---- body ----
   const int group = c.n_heads / c.n_kv_heads;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -347,9 +419,19 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     Prod o;
     o.x = p_qkv;
     o.res = p_xin;
-    p_h = ph;
-    M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, qkv, d.nqkv, nullptr, group, d.nq + d.nkv, h, d.H, 0,
-                M3_EPI_RESIDUAL, xin, d.H, o));
+    if (attn) {
+      const size_t lay = (size_t)B * c.n_kv_heads * c.max_pos * 128 * 2;
+      M3_TRY(attention(qkv, d.nqkv, c.n_heads, c.n_kv_heads, W,
+                       reinterpret_cast<uint16_t*>(S + L.kcache + l * lay),
+                       reinterpret_cast<uint16_t*>(S + L.vcache + l * lay), c.max_pos, 0, true));
+      p_h = ph;
+      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, ao, d.nq, nullptr, 0, 0, h, d.H, 0, M3_EPI_RESIDUAL,
+                  xin, d.H, o));
+    } else {
+      p_h = ph;
+      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, qkv, d.nqkv, nullptr, group, d.nq + d.nkv, h, d.H,
+                  0, M3_EPI_RESIDUAL, xin, d.H, o));
+    }
     Prod gu;
     gu.x = p_h;
     p_mlp = ph;
@@ -432,9 +514,20 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
       Prod o;
       o.x = p_dqkv;
       o.res = p_hd;
-      p_hd = ph;
-      M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd, d.D, 0,
-                  M3_EPI_RESIDUAL, hd, d.D, o));
+      if (attn) {
+        // step j attends over the frame's codebook positions 0 .. j - 1
+        const size_t lay = (size_t)B * c.d_heads * 8 * 128 * 2;
+        M3_TRY(attention(dqkv, d.dqkv, c.d_heads, c.d_heads, W,
+                         reinterpret_cast<uint16_t*>(S + L.dkcache + l * lay),
+                         reinterpret_cast<uint16_t*>(S + L.dvcache + l * lay), 8, j - 1, false));
+        p_hd = ph;
+        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, ao, d.dq, nullptr, 0, 0, hd, d.D, 0,
+                    M3_EPI_RESIDUAL, hd, d.D, o));
+      } else {
+        p_hd = ph;
+        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd, d.D, 0,
+                    M3_EPI_RESIDUAL, hd, d.D, o));
+      }
       Prod gu;
       gu.x = p_hd;
       p_dmlp = ph;
@@ -778,7 +871,10 @@ int m3_frame_state_init(const m3_config* cfg, int B, void* state, const uint16_t
   M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S), 0u, L.total / 4, s));
   M3_TRY(launch_copy_bf16(x0, reinterpret_cast<uint16_t*>(S + L.x), (size_t)B * cfg->hidden, s));
   M3_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(S + L.frame), frame0, 1, s));
-  // (flags, error word, launch counter and the tagged streams start at zero)
+  if (cfg->attention)
+    M3_TRY(launch_rope_table(reinterpret_cast<float*>(S + L.rope), std::max(cfg->max_pos, 8), 128,
+                             1e6, s));
+  // (flags, error word, launch counter, tagged streams and caches start at zero)
   return M3_OK;
 }
 
@@ -856,7 +952,8 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   // one frame kernel per body format: bf16, int8-row or fp8-row body and the
   // same lm_head format, int8-g128 depth
   const m3_config& c = model->cfg;
-  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128 || c.top_k > 0)
+  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128 || c.top_k > 0 ||
+      c.attention)
     return M3_ERR_FORMAT;
   // row-block winners carry their column in 16 bits next to the tag
   if (c.n_slice > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;

@@ -12,9 +12,12 @@ from ._lib import check, lib
 
 
 def make_config(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int = 0,
-                temperature: float = 1.0, cfg_scale: float = 1.5, top_k: int = 0) -> _lib.Config:
+                temperature: float = 1.0, cfg_scale: float = 1.5, top_k: int = 0,
+                attention: int = 0, max_pos: int = 0, pos0: int = 0) -> _lib.Config:
     """top_k == 0: one draw per row; top_k > 0: the reference's draw over
-    (conditional, unconditional) row pairs with guidance cfg_scale."""
+    (conditional, unconditional) row pairs with guidance cfg_scale.
+    attention == 0: the identity stub; 1: decode attention over caches of
+    max_pos positions, frame f at position pos0 + f."""
     return _lib.Config(
         hidden=cfg["H"], n_layers=cfg["n_layers"], n_heads=cfg["n_heads"],
         n_kv_heads=cfg["n_kv_heads"], head_dim=cfg["head_dim"], ffn=cfg["F"],
@@ -23,7 +26,7 @@ def make_config(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int
         d_ffn=cfg["Fd"], n_codebooks=cfg["n_codebooks"], code_vocab=cfg["code_vocab"],
         fmt_body=fmt_body, fmt_lm=fmt_lm, fmt_depth=fmt_depth, eps=float(cfg["eps"]),
         temperature=float(temperature), seed=int(seed), cfg_scale=float(cfg_scale),
-        top_k=int(top_k))
+        top_k=int(top_k), attention=int(attention), max_pos=int(max_pos), pos0=int(pos0))
 
 
 def frame_weight_bytes(c: _lib.Config) -> int:
@@ -39,7 +42,8 @@ class DecodeModel:
     packing."""
 
     def __init__(self, md: dict, seed: int = 0, temperature: float = 1.0,
-                 free_sources: bool = False, cfg_scale: float = 1.5, top_k: int = 0):
+                 free_sources: bool = False, cfg_scale: float = 1.5, top_k: int = 0,
+                 attention: int = 0, max_pos: int = 0, pos0: int = 0):
         cfg = md["cfg"]
         # the C side reads host arrays of these lengths from the config
         nsteps = cfg["n_codebooks"] - 1
@@ -50,7 +54,7 @@ class DecodeModel:
         self.cfg_dict = cfg
         self.fmt_body, self.fmt_lm, self.fmt_depth = md["fmt_body"], md["fmt_lm"], md["fmt_depth"]
         self.config = make_config(cfg, self.fmt_body, self.fmt_lm, self.fmt_depth, seed, temperature,
-                                  cfg_scale, top_k)
+                                  cfg_scale, top_k, attention, max_pos, pos0)
         self._keep = []
 
         def keep(t):
@@ -73,6 +77,8 @@ class DecodeModel:
             # the four packed tensors just appended, the two gammas after them
             dst.append(dict(zip(("qkv", "o", "gate_up", "down", "attn_norm", "ffn_norm"),
                                 self._keep[-6:])))
+            if "q_norm" in L:                # per-head q/k norms (decode attention)
+                lw.q_norm, lw.k_norm = keep(L["q_norm"]), keep(L["k_norm"])
             del gu
             if free_sources:
                 for k in ("qkv", "o", "gate", "up", "down"):
@@ -117,6 +123,14 @@ class DecodeModel:
         for c in (self.config, self.model.cfg):
             c.cfg_scale = float(cfg_scale)
             c.top_k = int(top_k)
+
+    def set_attention(self, attention: int = 1, max_pos: int = 2048, pos0: int = 0) -> None:
+        """Switch the frame states made from now on between the identity stub
+        (attention 0) and decode attention over caches of max_pos positions,
+        frame f at position pos0 + f (attention 1); the packed weights are
+        shared."""
+        for c in (self.config, self.model.cfg):
+            c.attention, c.max_pos, c.pos0 = int(attention), int(max_pos), int(pos0)
 
 
 class FrameState:
@@ -198,7 +212,9 @@ class FrameState:
 
     @property
     def err(self) -> torch.Tensor:
-        """Nonzero once a persistent frame gave up waiting (its outputs are invalid)."""
+        """Nonzero once a persistent frame gave up waiting (its outputs are
+        invalid), or with M3_ERR_ATTN_FULL set once an attention frame's
+        position reached max_pos."""
         return self.state[self.layout.err:self.layout.err + 4].view(torch.int32)
 
     def release(self) -> None:

@@ -54,7 +54,7 @@ def from_bits(a: np.ndarray, device="cpu") -> torch.Tensor:
 
 
 # tensor ids
-_T = dict(qkv=1, o=2, gate=3, up=4, down=5, attn_norm=6, ffn_norm=7)
+_T = dict(qkv=1, o=2, gate=3, up=4, down=5, attn_norm=6, ffn_norm=7, q_norm=8, k_norm=9)
 
 
 def make_model(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int = 0,
@@ -78,6 +78,9 @@ def make_model(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int 
             "down": normal_bf16((h, f), tensor_seed(base, li, _T["down"]), W_STD, device),
             "attn_norm": gamma_f32(h, tensor_seed(base, li, _T["attn_norm"]), device),
             "ffn_norm": gamma_f32(h, tensor_seed(base, li, _T["ffn_norm"]), device),
+            # per-head q/k RMSNorm gammas (decode attention)
+            "q_norm": gamma_f32(cfg["head_dim"], tensor_seed(base, li, _T["q_norm"]), device),
+            "k_norm": gamma_f32(cfg["head_dim"], tensor_seed(base, li, _T["k_norm"]), device),
         }
 
     md = {"cfg": dict(cfg), "fmt_body": fmt_body, "fmt_lm": fmt_lm, "fmt_depth": fmt_depth}

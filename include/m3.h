@@ -323,7 +323,25 @@ typedef struct {
    * frames only; n_slice and code_vocab <= M3_MAX_V_CFG. */
   float cfg_scale;
   int top_k;
+  /* Attention.  0: the identity stub (one cached position, softmax over one
+   * key is 1; the benchmark configuration).  1: decode attention over KV
+   * caches kept in the frame state: in every body layer, q/k RMSNorm with the
+   * layer's q_norm / k_norm, RoPE (base 1e6) at position pos0 + frame counter
+   * (read on the GPU, so graph replays advance it), the k/v cache write and
+   * softmax attention over the positions up to it, as m3_qk_norm_rope and
+   * m3_decode_attention; in the depth decoder, the same over the frame's
+   * codebook positions (position j - 1 at step j, a cache per layer reused
+   * every frame).  max_pos: cached positions per body layer (1 ..
+   * M3_MAX_POS); 0 <= pos0 < max_pos.  A frame whose position reaches max_pos
+   * is refused on the GPU: it rewrites slot max_pos - 1, attends over max_pos
+   * positions and sets the state's err word to M3_ERR_ATTN_FULL.  Eager and
+   * graph frames only. */
+  int attention;
+  int max_pos;
+  int pos0;
 } m3_config;
+
+#define M3_ERR_ATTN_FULL 2u  /* state err word: the frame position reached max_pos */
 
 typedef struct {
   const void* qkv;        /* packed [nq + 2 nkv, hidden]              */
@@ -332,6 +350,8 @@ typedef struct {
   const void* down;       /* packed [hidden, ffn]                     */
   const float* attn_norm; /* [hidden] */
   const float* ffn_norm;  /* [hidden] */
+  const float* q_norm;    /* [head_dim] per-head q RMSNorm (attention = 1 only) */
+  const float* k_norm;    /* [head_dim] per-head k RMSNorm (attention = 1 only) */
 } m3_layer_weights;
 
 typedef struct {
@@ -373,6 +393,12 @@ typedef struct {
                    /* u32 words (bf16 value | 16-bit producer tag): the
                       persistent frame's intermediate streams; h, qkv, mlp, u,
                       hd, dqkv, dmlp above belong to the eager/graph frames   */
+  /* attention = 1 only (zero-sized otherwise): */
+  size_t rope;     /* f32  [max(max_pos, 8), 64, 2] RoPE table                 */
+  size_t aq, ao;   /* bf16 [B, max(nq, d_hidden)] rotated q; attention output  */
+  size_t kcache, vcache;   /* bf16 [n_layers][B][n_kv][max_pos][128]          */
+  size_t dkcache, dvcache; /* bf16 [d_layers][B][d_heads][8][128]             */
+  size_t attn_ws;  /* m3_decode_attention's workspace at T = max_pos           */
   size_t total;
 } m3_frame_layout;
 

@@ -68,7 +68,7 @@ def fill_cache(B, n_kv, max_pos, T, seed, kscale):
 
 
 @pytest.mark.parametrize("n_q,n_kv", [(32, 8), (16, 16), (8, 4), (16, 2)])
-@pytest.mark.parametrize("T", [1, 2, 37, 128, 129, 300])
+@pytest.mark.parametrize("T", [1, 2, 8, 37, 128, 129, 300])
 def test_attention_parity(n_q, n_kv, T):
     B, max_pos = 3, T + 5
     kc, vc = fill_cache(B, n_kv, max_pos, T, 10 * T + n_kv, 3.0)
