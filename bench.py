@@ -236,46 +236,56 @@ def time_prefill(c, stream, M=600, reps=10):
     qkv = torch.empty(M, nqkv, dtype=torch.bfloat16, device=dev)
     mlp = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
 
-    def step(which=None):
-        if which in (None, "norm"):
+    names = ("norm1", "qkv", "o", "norm2", "gate_up", "down")
+
+    def launch(name):
+        if name == "norm1":
             m3.rmsnorm_rows(h, g1, c.eps, a=a, stream=stream)
-        if which in (None, "qkv"):
+        elif name == "qkv":
             m3.prefill_gemm(*W["qkv"], a, y=qkv, stream=stream)
-        if which in (None, "o"):
+        elif name == "o":
             m3.prefill_gemm(*W["o"], qkv[:, :nq], y=h, epi=m3.EPI_RESIDUAL, residual=h, stream=stream)
-        if which is None:
+        elif name == "norm2":
             m3.rmsnorm_rows(h, g2, c.eps, a=a, stream=stream)
-        if which in (None, "gate_up"):
+        elif name == "gate_up":
             m3.prefill_gemm(*W["gate_up"], a, y=mlp, epi=m3.EPI_SWIGLU, stream=stream)
-        if which in (None, "down"):
+        else:
             m3.prefill_gemm(*W["down"], mlp, y=h, epi=m3.EPI_RESIDUAL, residual=h, stream=stream)
 
-    def timed(which):
-        with torch.cuda.stream(stream):
-            for _ in range(2):
-                step(which)
-            stream.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                step(which)
-            e1.record(stream)
-            stream.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-
-    layer_us = timed(None)
+    # the layer's launches in order, each between its own pair of events, so
+    # every kernel is timed where it runs in a real prefill (its weights
+    # coming from HBM, not left in the Infinity Cache by a repeat of itself)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            for name in names:
+                launch(name)
+        stream.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in names] for _ in range(reps)]
+        l0 = torch.cuda.Event(enable_timing=True)
+        l1 = torch.cuda.Event(enable_timing=True)
+        l0.record(stream)
+        for r in range(reps):
+            for i, name in enumerate(names):
+                ev[r][i][0].record(stream)
+                launch(name)
+                ev[r][i][1].record(stream)
+        l1.record(stream)
+        stream.synchronize()
+    layer_us = l0.elapsed_time(l1) * 1e3 / reps
+    per = {name: sum(ev[r][i][0].elapsed_time(ev[r][i][1]) for r in range(reps)) * 1e3 / reps
+           for i, name in enumerate(names)}
     gemms = []
     flops = 0
     for name in ("qkv", "o", "gate_up", "down"):
-        us = timed(name)
+        us = per[name]
         _, N, K = W[name]
         fl = 2 * M * N * K
         flops += fl
         tf = fl / (us * 1e-6) / 1e12
         gemms.append({"name": name, "N": N, "K": K, "avg_us": round(us, 2),
                       "TFLOP_s": round(tf, 1), "frac": round(tf / MFMA_BF16_PEAK_TFS, 4)})
-    norm_us = timed("norm")
+    norm_us = (per["norm1"] + per["norm2"]) / 2
     gemm_us = sum(g["avg_us"] for g in gemms)
     tf = flops / (gemm_us * 1e-6) / 1e12
     del W
@@ -537,6 +547,7 @@ def main():
 
     sweep = []
     guided = []
+    attention_frames = []
     if not args.no_sweep:
         for B in (2, 6, 16):
             sweep.append(point(args.preset, B, dm, fbytes))
@@ -551,6 +562,25 @@ def main():
                            "GB_s": round(fbytes * 1e3 / ms_g / 1e9, 1)})
             log(f"[bench] guided {guided[-1]}")
         dm.set_draw(1.5, 0)
+        # the frame with decode attention in place of the stub, near the end
+        # of a 60 s song (1500 frames after a 300-token prompt: T about 1800),
+        # graph-replayed; the cache bytes come on top of the weights
+        n_att = 20
+        dm.set_attention(1, max_pos=2048, pos0=1800 - 3 - n_att // 2)
+        for B in (1, 16):
+            st_a, ms_a, _ = time_frames(dm, cfg, B, n_att, 3, stream, args.seed)
+            err = int(st_a.err.item())
+            st_a.release()
+            del st_a
+            kv = 36 * B * 8 * 1800 * 128 * 2 * 2
+            attention_frames.append({"preset": args.preset, "B": B, "T": 1800, "path": "graph",
+                                     "ms_per_frame": round(ms_a, 4),
+                                     "frames_per_s": round(1e3 / ms_a, 2),
+                                     "weight_plus_kv_GB_s": round((fbytes + kv) * 1e3 / ms_a / 1e9, 1),
+                                     "kv_bytes_per_frame": kv, "err": err})
+            log(f"[bench] attention frame {attention_frames[-1]}")
+            torch.cuda.empty_cache()
+        dm.set_attention(0, 0, 0)
         del dm
         torch.cuda.empty_cache()
         for other in [q for q in ("A", "B", "C") if q != args.preset]:
@@ -603,6 +633,7 @@ def main():
                                "one workgroup per song)", "points": cfg_draw},
         "guided_frame": guided,
         "prefill": prefill,
+        "attention_frame": attention_frames,
         "attention": {"kernel": "attn_partial_kernel + attn_merge_kernel (body, 32:8 heads; "
                                 "caches [B, 8, T, 128] bf16, one per layer)", "points": attention},
         "gpu": f"{props.name} {props.gcnArchName} x{props.multi_processor_count} CU",
