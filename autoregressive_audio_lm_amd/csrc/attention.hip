@@ -250,43 +250,50 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
 }
 
 // chunks combined in order: one workgroup of 128 threads per (row, query
-// head).  The chunk maxima and sums are loaded in parallel into LDS; the P.V
-// sums are read eight chunks at a time, so their loads overlap.
-constexpr int kMaxChunks = M3_MAX_POS / 64;
+// head).  Every load of a batch of up to 32 chunks (their maxima, sums and
+// this thread's P.V dimension) is issued before the first is used, so a
+// merge of up to 32 chunks (4096 positions) waits for memory once.
+constexpr int kMergeBatch = 32;
 
 template <int G>
 __global__ __launch_bounds__(kHD) void attn_merge_kernel(AttnParams p) {
-  __shared__ float mc[kMaxChunks], lc[kMaxChunks];
-  __shared__ float red[2];
   const int qh = blockIdx.x % p.n_q, b = blockIdx.x / p.n_q, d = threadIdx.x;
   const int kvh = qh / G, h = qh % G;
   const int nc = (attn_T(p) + p.ch - 1) / p.ch;
   if (nc == 1) return;                           // the chunk kernel wrote the output
   const float* wrec = p.ws + (((size_t)b * p.n_kv + kvh) * p.nchunks) * (G * (2 + kHD)) + h * (2 + kHD);
   constexpr size_t kStride = (size_t)G * (2 + kHD);   // floats from one chunk's record to the next
-  float mloc = -INFINITY;
-  for (int c = d; c < nc; c += kHD) {
-    mc[c] = wrec[c * kStride];
-    lc[c] = wrec[c * kStride + 1];
-    mloc = fmaxf(mloc, mc[c]);
-  }
-  // workgroup maximum of the chunk maxima (two waves)
+  float mv[kMergeBatch], lv[kMergeBatch], av[kMergeBatch];
+  auto load = [&](int c0) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-  if ((d & 63) == 0) red[d >> 6] = mloc;
-  __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  float L = 0.f, A = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += 8) {
-    float v[8];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const bool in = c0 + u < nc;
+      const float* wc = wrec + (c0 + u) * kStride;
+      mv[u] = in ? wc[0] : -INFINITY;
+      lv[u] = in ? wc[1] : 0.f;
+      av[u] = in ? wc[2 + d] : 0.f;
+    }
+  };
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  auto add = [&]() {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nc ? wrec[(c0 + u) * kStride + 2 + d] : 0.f;
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float e = exp2f(mv[u] - M);          // 0 past the last chunk
+      L = fmaf(lv[u], e, L);
+      A = fmaf(av[u], e, A);
+    }
+  };
+  if (nc <= kMergeBatch) {                       // one batch: a single wait for memory
+    load(0);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (c0 + u >= nc) break;
-      const float e = exp2f(mc[c0 + u] - M);     // every chunk holds a position
-      L = fmaf(lc[c0 + u], e, L);
-      A = fmaf(v[u], e, A);
+    for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, mv[u]);
+    add();
+  } else {                                       // the maximum over every chunk first
+    for (int c0 = 0; c0 < nc; c0 += kMergeBatch)
+      for (int c = c0; c < min(nc, c0 + kMergeBatch); ++c) M = fmaxf(M, wrec[c * kStride]);
+    for (int c0 = 0; c0 < nc; c0 += kMergeBatch) {
+      load(c0);
+      add();
     }
   }
   p.out[(size_t)b * p.ldo + (size_t)qh * kHD + d] = (uint16_t)f2bf(A / L);
