@@ -416,7 +416,9 @@ size_t m3_frame_workspace_bytes(const m3_config* cfg /* host */, int B);
 int m3_frame_state_init(const m3_config* cfg, int B, void* state, const uint16_t* x0,
                         uint32_t frame0, void* stream);
 /* Enqueue one frame: body (per layer: norm+QKV, stub+O+residual, norm+gate/up
- * +SwiGLU, down+residual) -> final norm + sliced lm_head -> draw 0 -> depth
+ * +SwiGLU, down+residual; with attention = 1 the stub is q/k norm + RoPE, the
+ * cache write and attention at the frame's position, then O+residual) -> final
+ * norm + sliced lm_head -> draw 0 -> depth
  * input projection -> 7 x (embedding of the previous code, depth layers, final
  * norm + head_j, draw j) -> feedback x' = bf16((E_tok[c0] + sum_j A_j[c_j]) *
  * 8^-1/2) into the state's input, codes into `codes` (device [B, 8]: absolute
