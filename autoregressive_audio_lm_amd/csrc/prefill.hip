@@ -282,14 +282,13 @@ hipError_t launch_tile(PrefillParams p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile shape, measured at 600 rows on the body shapes: 64 x 256 where that
-// still gives every CU a tile, or where K is long (fewer, longer workgroups
-// won for K = 12288); else 64 x 128, whose 155 registers let three
+// Tile shape, measured at 600 rows on the body shapes, each GEMM timed inside
+// the layer sequence (weights from HBM): 64 x 256 where that still gives
+// every CU a tile (gate/up), else 64 x 128, whose 155 registers let three
 // workgroups share a CU.  Wider M tiles (128 rows), a 2 x 2 wave arrangement
 // (weight fragments loaded twice) and 128-wide K steps all measured slower.
-bool wide_tile(int M, int N, int K) {
-  const int t = ((M + 63) / 64) * ((N + 255) / 256);
-  return t >= 256 || K >= 8192;
+bool wide_tile(int M, int N) {
+  return ((M + 63) / 64) * ((N + 255) / 256) >= 256;
 }
 
 constexpr int kNThreads = 256;
@@ -352,7 +351,7 @@ hipError_t launch_prefill_gemm(const PrefillDesc& d, hipStream_t s) {
   p.res = d.res;
   p.ldr = d.ldr;
   p.vec = d.ldy % 8 == 0 && (!d.res || (d.ldr % 8 == 0 && reinterpret_cast<uintptr_t>(d.res) % 16 == 0));
-  return wide_tile(d.M, d.N, d.K) ? launch_tile<1, 4, 4, 2>(p, s) : launch_tile<1, 4, 2, 2>(p, s);
+  return wide_tile(d.M, d.N) ? launch_tile<1, 4, 4, 2>(p, s) : launch_tile<1, 4, 2, 2>(p, s);
 }
 
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, int ldx, const float* gamma,

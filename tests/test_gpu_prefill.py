@@ -36,9 +36,10 @@ def gemm(W, a, epi=m3.EPI_NONE, out_f32=False, res=None, flags=0):
     return y.cpu().numpy() if out_f32 else synth.bits(y)
 
 
-# the last two reach the 64 x 256 tiles (K >= 8192), the others 64 x 128
+# the last two reach the 64 x 256 tiles (at least 256 of them), the others 64 x 128
 @pytest.mark.parametrize("M,N,K", [(1, 16, 64), (37, 200, 512), (600, 256, 512), (129, 130, 1024),
-                                   (300, 520, 256), (37, 300, 8192), (130, 272, 8320)])
+                                   (300, 520, 256), (37, 300, 8192), (1000, 4100, 128),
+                                   (1024, 4096, 192)])
 def test_prefill_gemm_parity(M, N, K):
     W = rand_w(N, K, M + N)
     a = rand_x(M, K, K + 3)
@@ -47,11 +48,14 @@ def test_prefill_gemm_parity(M, N, K):
     P.check_bf16(gemm(W, a), y_ex)
 
 
-@pytest.mark.parametrize("M,K", [(1, 512), (150, 512), (600, 512), (70, 8192)])
-@pytest.mark.parametrize("F,N", [(100, 200), (99, 203)])
+@pytest.mark.parametrize("M,K,F,N", [(1, 512, 100, 200), (150, 512, 100, 200), (600, 512, 100, 200),
+                                     (70, 8192, 100, 200), (1, 512, 99, 203), (150, 512, 99, 203),
+                                     (600, 512, 99, 203), (70, 8192, 99, 203),
+                                     (1000, 64, 2050, 4100), (1024, 64, 2051, 4099)])
 def test_prefill_epilogues(M, K, F, N):
     """SwiGLU and residual epilogues; F = 100 / N = 200 give rows of whole
-    16-byte chunks, F = 99 / N = 203 ragged tails and unaligned row strides."""
+    16-byte chunks, F = 99 / N = 203 ragged tails and unaligned row strides;
+    the last two run on the 64 x 256 tiles (the SwiGLU GEMM has N = 2F)."""
     Wg, Wu = rand_w(F, K, 11), rand_w(F, K, 12)
     a = rand_x(M, K, 13)
     m = gemm(np.concatenate([Wg, Wu], 0), a, epi=m3.EPI_SWIGLU, flags=m3.PACK_GLU_INTERLEAVE)
