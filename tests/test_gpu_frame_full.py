@@ -127,3 +127,66 @@ def test_full_size_persistent_refuses_unstaged_operands():
     st = runtime.FrameState(dm, 16, synth.activations(16, cfg["H"], 901, device=DEV))
     with pytest.raises(_lib.M3ValueError):
         st.persistent_create()
+
+
+def test_full_size_attention_frame_within_rounding_envelope():
+    """The frame with decode attention at the full model size and position
+    1797 (the end of a 60 s song): both sides start from the same seeded
+    keys and values at the 1797 earlier positions of every layer's cache; the
+    GPU's graph-replayed frame stays within the oracle's rounding envelope
+    and its stable draws are identical."""
+    cfg = configs.config("frame-full")
+    B, max_pos, pos0 = 1, 2048, 1797
+    md = synth.make_model(cfg, **configs.PRESETS["A"], seed=19, device=DEV)
+    md_np = synth.model_to_numpy(md)
+    dm = runtime.DecodeModel(md, seed=9, free_sources=True, attention=1, max_pos=max_pos,
+                             pos0=pos0)
+    del md
+    torch.cuda.empty_cache()
+    om = O.OracleModel(md_np, attention=1, max_pos=max_pos, pos0=pos0)
+    del md_np
+    om.reset_attention(B)
+    x0 = synth.activations(B, cfg["H"], 510)
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
+    L, nkv = cfg["n_layers"], cfg["n_kv_heads"]
+    n = L * B * nkv * max_pos * 128
+    for name, seed in (("kcache", 700), ("vcache", 701)):
+        off = getattr(st.layout, name)
+        cache = st.state[off:off + 2 * n].view(torch.bfloat16).view(L, B, nkv, max_pos, 128)
+        cache[:, :, :, :pos0] = synth.normal_bf16((L, B, nkv, pos0, 128), seed, 1.0, DEV)
+        host = synth.bits(cache)
+        for l in range(L):
+            getattr(om, name)[l][...] = host[l]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        st.capture(s)
+        st.replay(s)
+        s.synchronize()
+    torch.cuda.synchronize()
+    codes = st.codes.cpu().numpy()
+    h_gpu = synth.bits(st.h)
+    lg_gpu = st.logits.cpu().numpy().astype(np.float64)
+    assert int(st.err.item()) == 0
+    st.release()
+
+    x = synth.bits(x0)
+    o_codes, _, tr = O.decode_frame(om, x, seed=9, frame=0, trace=True)
+    env_h, env_l, stable = 0.0, 0.0, np.ones_like(o_codes, dtype=bool)
+    for (b, k) in FLIPS:
+        xp = x.copy()
+        xp[b % B, k] ^= 1
+        c2, _, t2 = O.decode_frame(om, xp, seed=9, frame=0, trace=True)
+        env_h = max(env_h, _dev(t2["h_body"], tr["h_body"]))
+        env_l = max(env_l, float(np.max(np.abs(t2["logits0"].astype(np.float64) - tr["logits0"]))))
+        stable &= c2 == o_codes
+    dev_h = _dev(h_gpu, tr["h_body"])
+    dev_l = float(np.max(np.abs(lg_gpu - tr["logits0"])))
+    print(f"attention frame at position {pos0}: h_body dev {dev_h:.3e} (envelope {env_h:.3e}); "
+          f"logits dev {dev_l:.3e} (envelope {env_l:.3e}); codes {codes.tolist()} "
+          f"oracle {o_codes.tolist()}", flush=True)
+    assert dev_h <= ENVELOPE_FACTOR * env_h
+    assert dev_l <= ENVELOPE_FACTOR * env_l
+    sure = stable & (tr["zgap"] > ENVELOPE_FACTOR * env_l)
+    sure[:, 1:] &= sure[:, :1]
+    assert np.all((codes == o_codes)[sure])
