@@ -86,12 +86,12 @@ def test_rmsnorm_rows_parity(M, K):
     assert np.all(np.abs(av - rv) <= 2 * P.half_ulp(rv) + 1e-30)
 
 
-@pytest.mark.parametrize("which", ["qkv", "gate_up", "down"])
+@pytest.mark.parametrize("which", ["qkv", "o", "gate_up", "down"])
 def test_prefill_full_size_sampled(which):
-    """Full body shapes at M = 600: every output column of the first and the
-    last row block of W checked against the oracle."""
-    N, K, epi = {"qkv": (6144, 4096, m3.EPI_NONE), "gate_up": (24576, 4096, m3.EPI_NONE),
-                 "down": (4096, 12288, m3.EPI_NONE)}[which]
+    """Full body shapes at M = 600: every output column of the first, a
+    middle and the last row block of W checked against the oracle."""
+    N, K, epi = {"qkv": (6144, 4096, m3.EPI_NONE), "o": (4096, 4096, m3.EPI_NONE),
+                 "gate_up": (24576, 4096, m3.EPI_NONE), "down": (4096, 12288, m3.EPI_NONE)}[which]
     M = 600
     Wd = synth.normal_bf16((N, K), 30, 0.02, DEV)
     a = rand_x(M, K, 31)
@@ -101,6 +101,6 @@ def test_prefill_full_size_sampled(which):
     y = y.cpu().numpy()
     W = synth.bits(Wd)
     M_ = O.Matrix(W, O.BF16)
-    for r0 in (0, N - 16):
+    for r0 in (0, N // 2 + 16, N - 16):
         y_ex = O.gemv(M_, a, rows=(r0, 16))
         P.check_f32(y[:, r0:r0 + 16], y_ex)
