@@ -19,14 +19,15 @@
 // bf16 pairs; v_dot2 products against the G query heads of the KV head, a
 // two-step DPP sum, the scores (base 2, scale folded in) to LDS.  One wave
 // per head then takes the chunk's maximum, exponentials and sum.  Pass 2:
-// each lane owns 4 dimensions of 16 positions (a wave load reads two whole
-// value rows) and accumulates P.V; the 8 half-wave partials are summed in
-// LDS.  With one chunk the result is the output; otherwise (maximum, sum,
+// each lane owns 4 dimensions of CH / 8 positions (a wave load reads two
+// whole value rows) and accumulates P.V; the 8 half-wave partials are summed
+// in LDS.  With one chunk the result is the output; otherwise (maximum, sum,
 // P.V) goes to the workspace and attn_merge_kernel combines the chunks in
 // order.  (Merging in the last workgroup to finish, behind an atomic count,
 // measured ten times slower: the device-scope fences it needs write back and
-// invalidate the L2 under every other workgroup.)  The bound is HBM: each position's key and value are read once (512
-// bytes per KV head and batch row).
+// invalidate the L2 under every other workgroup.)  The bound is HBM: each
+// position's key and value are read once (512 bytes per KV head and batch
+// row).
 #include "gemv_impl.h"
 
 namespace m3 {
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
 // chunks combined in order: one workgroup of 128 threads per (row, query
 // head).  Every load of a batch of up to 32 chunks (their maxima, sums and
 // this thread's P.V dimension) is issued before the first is used, so a
-// merge of up to 32 chunks (4096 positions) waits for memory once.
+// merge of up to 32 chunks (2048 or 4096 positions) waits for memory once.
 constexpr int kMergeBatch = 32;
 
 template <int G>

@@ -4,8 +4,9 @@
 // A prompt of about 300 tokens for each of the two CFG rows is 600 rows
 // through every body matrix at once ("MiniMax Music 3, local": a prompt of
 // 300 tokens per CFG row; TensorFold PR #987: 300 tokens a CFG row), a real
-// dense contraction: at 600 rows a bf16 weight byte meets 600 multiply-adds,
-// above the matrix cores' ridge, so the bound is the MFMA rate, not HBM.
+// dense contraction: at 600 rows each bf16 weight meets 600 multiply-adds
+// (600 flops per byte), above the matrix cores' ridge of about 310 flops per
+// byte, so the bound is the MFMA rate, not HBM.
 //
 // GEMM.  A workgroup of 4 waves computes a 64 x 128 or 64 x 256 tile of Y as
 // accumulators of v_mfma_f32_16x16x32_bf16; each wave owns a strip of
@@ -69,7 +70,9 @@ __device__ __forceinline__ void tile_of(const PrefillParams& p, int& mt, int& nt
 // w = (wm, wn) = (w % WGM, w / WGM) holds MT x WNB accumulator tiles of 16 x
 // 16: rows 16 MT wm .. +16 MT - 1, columns 16 WNB wn .. +16 WNB - 1.  Each A
 // fragment read from LDS feeds WNB MFMAs and each weight fragment MT; with
-// WGM = 1 no two waves load the same weight fragment.
+// WGM = 1 no two waves load the same weight fragment.  Instantiated: <1, 4,
+// 2, 2> (64 x 128) and <1, 4, 4, 2> (64 x 256); WGM = 2 and KT = 4 are the
+// measured alternatives the parameters still express.
 //
 // Pipeline over K steps of 32 KT: registers hold the weight fragments and the A
 // chunks of three steps; at step ks the loads of step ks + 2 are issued, the
