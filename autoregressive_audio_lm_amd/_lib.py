@@ -90,6 +90,11 @@ _SIGS = {
     "m3_qk_norm_rope": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _I, _P, _I, _P, _P,
                              _I, _P]),
     "m3_attention_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "m3_prefill_qk_norm_rope": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _I, _P,
+                                     _I, _P, _P, _I, _P]),
+    "m3_prefill_attention_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "m3_prefill_attention": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P,
+                                  ctypes.c_size_t, _P]),
     "m3_decode_attention": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P, ctypes.c_size_t,
                                  _P]),
     "m3_lmhead_sliced": (_I, [_I, _P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _P, _I, _P]),

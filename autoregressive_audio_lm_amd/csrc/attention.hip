@@ -57,18 +57,22 @@ __device__ __forceinline__ int frame_pos(const uint32_t* frame_dev, int pos0, in
 }
 
 // One wave per head: lane l holds elements l and l + 64 (a rotation pair).
-// frame_dev (optional): the position is pos0 + *frame_dev instead of pos.
+// Row r belongs to cache sequence r / P at position pos + r % P (P = 1: one
+// position for every row).  frame_dev (optional, P = 1): the position is
+// pos0 + *frame_dev instead of pos.
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv, const float* q_gamma,
     const float* k_gamma, float eps, const float* rope, int pos, uint16_t* q_out, int ldq,
     uint16_t* k_cache, uint16_t* v_cache, int max_pos, const uint32_t* frame_dev, int pos0,
-    uint32_t* err) {
+    uint32_t* err, int P) {
   const int heads = n_q + 2 * n_kv;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (w >= B * heads) return;
   if (frame_dev) pos = frame_pos(frame_dev, pos0, max_pos, blockIdx.x == 0 ? err : nullptr);
-  const int b = w / heads, hh = w % heads;
-  const uint16_t* x = qkv + (size_t)b * ldqkv + (size_t)hh * kHD;
+  const int row = w / heads, hh = w % heads;
+  const int b = row / P;                          // cache sequence
+  pos += row % P;
+  const uint16_t* x = qkv + (size_t)row * ldqkv + (size_t)hh * kHD;
   const uint32_t x0 = x[lane], x1 = x[lane + 64];
   if (hh >= n_q + n_kv) {                         // v: copied into the cache
     uint16_t* dst = v_cache + (((size_t)b * n_kv + (hh - n_q - n_kv)) * max_pos + pos) * kHD;
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
   const float a0 = bf2f(f2bf((a0f * r) * g[lane])), a1 = bf2f(f2bf((a1f * r) * g[lane + 64]));
   const float c = rope[((size_t)pos * 64 + lane) * 2], s = rope[((size_t)pos * 64 + lane) * 2 + 1];
   const uint32_t y0 = f2bf(a0 * c - a1 * s), y1 = f2bf(a1 * c + a0 * s);
-  uint16_t* dst = hh < n_q ? q_out + (size_t)b * ldq + (size_t)hh * kHD
+  uint16_t* dst = hh < n_q ? q_out + (size_t)row * ldq + (size_t)hh * kHD
                            : k_cache + (((size_t)b * n_kv + (hh - n_q)) * max_pos + pos) * kHD;
   dst[lane] = (uint16_t)y0;
   dst[lane + 64] = (uint16_t)y1;
@@ -102,12 +106,15 @@ struct AttnParams {
   const uint32_t* frame_dev;                     // optional: T = pos0 + *frame_dev + 1
   int pos0;
   int ch;                                        // positions per chunk
+  int P;                                         // rows per cache sequence
+  int T0;                                        // positions attended by a sequence's first row
 };
 
-// positions attended: T, or the frame's position + 1 (grid and records are
-// sized for p.T = max_pos then)
-__device__ __forceinline__ int attn_T(const AttnParams& p) {
-  if (!p.frame_dev) return p.T;
+// positions attended by row r: T0 + r % P (row r of cache sequence r / P; P =
+// 1 and T0 = T for one position per row), or the frame's position + 1 (grid
+// and records are sized for p.T = max_pos then)
+__device__ __forceinline__ int attn_T(const AttnParams& p, int r) {
+  if (!p.frame_dev) return p.T0 + r % p.P;
   const long t = (long)p.pos0 + (long)*p.frame_dev + 1;
   return t < p.max_pos ? (int)t : p.max_pos;
 }
@@ -124,11 +131,11 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
   const int kvh = (blockIdx.x / p.nchunks) % p.n_kv;
   const int b = blockIdx.x / (p.nchunks * p.n_kv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = attn_T(p), nc = (T + CH - 1) / CH;
-  if (chunk >= nc) return;                       // past the frame's position
+  const int T = attn_T(p, b), nc = (T + CH - 1) / CH;
+  if (chunk >= nc) return;                       // past this row's position
   const int t0 = chunk * CH;
   const int n = min(T - t0, CH);                 // positions of this chunk
-  const size_t base = ((size_t)b * p.n_kv + kvh) * (size_t)p.max_pos * kHD;
+  const size_t base = ((size_t)(b / p.P) * p.n_kv + kvh) * (size_t)p.max_pos * kHD;
   const uint16_t* kb = p.k + base;
   const uint16_t* vb = p.v + base;
 
@@ -260,7 +267,7 @@ template <int G>
 __global__ __launch_bounds__(kHD) void attn_merge_kernel(AttnParams p) {
   const int qh = blockIdx.x % p.n_q, b = blockIdx.x / p.n_q, d = threadIdx.x;
   const int kvh = qh / G, h = qh % G;
-  const int nc = (attn_T(p) + p.ch - 1) / p.ch;
+  const int nc = (attn_T(p, b) + p.ch - 1) / p.ch;
   if (nc == 1) return;                           // the chunk kernel wrote the output
   const float* wrec = p.ws + (((size_t)b * p.n_kv + kvh) * p.nchunks) * (G * (2 + kHD)) + h * (2 + kHD);
   constexpr size_t kStride = (size_t)G * (2 + kHD);   // floats from one chunk's record to the next
@@ -333,24 +340,25 @@ hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, i
                                const float* q_gamma, const float* k_gamma, float eps,
                                const float* rope, int pos, uint16_t* q_out, int ldq,
                                uint16_t* k_cache, uint16_t* v_cache, int max_pos, hipStream_t s,
-                               const uint32_t* frame_dev, int pos0, uint32_t* err) {
+                               const uint32_t* frame_dev, int pos0, uint32_t* err, int P) {
   const int waves = B * (n_q + 2 * n_kv);
   hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, B, ldqkv,
                      n_q, n_kv, q_gamma, k_gamma, eps, rope, pos, q_out, ldq, k_cache, v_cache,
-                     max_pos, frame_dev, pos0, err);
+                     max_pos, frame_dev, pos0, err, P);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv,
                                    const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
                                    int T, uint16_t* out, int ldo, void* ws, hipStream_t s,
-                                   const uint32_t* frame_dev, int pos0) {
-  // a frame-driven call sizes its grid and records for every position
-  const int Tg = frame_dev ? max_pos : T;
+                                   const uint32_t* frame_dev, int pos0, int P) {
+  // the grid and the records are sized for the longest row: T + P - 1, or
+  // every position for a frame-driven call
+  const int Tg = frame_dev ? max_pos : T + P - 1;
   const int ch = attn_chunk_size(B, n_kv, Tg);
   const int nc = (Tg + ch - 1) / ch;
   AttnParams p{q, ldq, k_cache, v_cache, n_q, n_kv, max_pos, Tg, nc, kLog2e / sqrtf((float)kHD),
-               out, ldo, static_cast<float*>(ws), frame_dev, pos0, ch};
+               out, ldo, static_cast<float*>(ws), frame_dev, pos0, ch, P, T};
   switch (n_q / n_kv) {
     case 1: launch_attn_g<1>(p, ch, B, s); break;
     case 2: launch_attn_g<2>(p, ch, B, s); break;

@@ -829,6 +829,71 @@ int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, in
                                             ldo, workspace, static_cast<hipStream_t>(stream)));
 }
 
+// ---- the prompt's attention (S sequences of P positions, rows [s][t]) ------------
+int m3_prefill_qk_norm_rope(const uint16_t* qkv, int S, int P, int ldqkv, int n_q, int n_kv,
+                            int head_dim, const float* q_gamma, const float* k_gamma, float eps,
+                            const float* rope, int pos_base, uint16_t* q_out, int ldq,
+                            uint16_t* k_cache, uint16_t* v_cache, int max_pos, void* stream) {
+  if (!qkv || !q_gamma || !k_gamma || !rope || !q_out || !k_cache || !v_cache) return M3_ERR_NULL;
+  if (head_dim != M3_HEAD_DIM || !attn_heads_ok(n_q, n_kv)) return M3_ERR_SHAPE;
+  if (S < 1 || S > M3_MAX_B || P < 1 || (long)S * P > M3_MAX_M_PREFILL || max_pos < 1 ||
+      max_pos > M3_MAX_POS || pos_base < 0 || (long)pos_base + P > max_pos)
+    return M3_ERR_SHAPE;
+  if (ldqkv < (n_q + 2 * n_kv) * M3_HEAD_DIM || ldq < n_q * M3_HEAD_DIM) return M3_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return M3_ERR_SHAPE;
+  if (!aligned(qkv, 16) || !aligned(q_out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(q_gamma, 4) || !aligned(k_gamma, 4) || !aligned(rope, 16) || ldqkv % 8 || ldq % 8)
+    return M3_ERR_ALIGN;
+  const int R = S * P;
+  const size_t qkv_b = ((size_t)(R - 1) * ldqkv + (n_q + 2 * n_kv) * M3_HEAD_DIM) * 2;
+  const size_t q_b = ((size_t)(R - 1) * ldq + n_q * M3_HEAD_DIM) * 2;
+  const size_t c_b = cache_bytes(S, n_kv, max_pos);
+  if (overlap(qkv, qkv_b, q_out, q_b) || overlap(qkv, qkv_b, k_cache, c_b) ||
+      overlap(qkv, qkv_b, v_cache, c_b) || overlap(q_out, q_b, k_cache, c_b) ||
+      overlap(q_out, q_b, v_cache, c_b) || overlap(k_cache, c_b, v_cache, c_b))
+    return M3_ERR_ALIAS;
+  return hip_status(launch_qk_norm_rope(qkv, R, ldqkv, n_q, n_kv, q_gamma, k_gamma, eps, rope,
+                                        pos_base, q_out, ldq, k_cache, v_cache, max_pos,
+                                        static_cast<hipStream_t>(stream), nullptr, 0, nullptr, P));
+}
+
+size_t m3_prefill_attention_workspace_bytes(int S, int P, int n_q, int n_kv, int pos_base) {
+  if (S < 1 || P < 1 || (long)S * P > M3_MAX_M_PREFILL || !attn_heads_ok(n_q, n_kv) ||
+      pos_base < 0 || (long)pos_base + P > M3_MAX_POS)
+    return 0;
+  return attn_workspace_bytes(S * P, n_q, n_kv, pos_base + P);
+}
+
+int m3_prefill_attention(const uint16_t* q, int S, int P, int ldq, int n_q, int n_kv, int head_dim,
+                         const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
+                         int pos_base, uint16_t* out, int ldo, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !out) return M3_ERR_NULL;
+  if (head_dim != M3_HEAD_DIM || !attn_heads_ok(n_q, n_kv)) return M3_ERR_SHAPE;
+  if (S < 1 || S > M3_MAX_B || P < 1 || (long)S * P > M3_MAX_M_PREFILL || max_pos < 1 ||
+      max_pos > M3_MAX_POS || pos_base < 0 || (long)pos_base + P > max_pos)
+    return M3_ERR_SHAPE;
+  if (ldq < n_q * M3_HEAD_DIM || ldo < n_q * M3_HEAD_DIM) return M3_ERR_SHAPE;
+  const int R = S * P;
+  const size_t need = attn_workspace_bytes(R, n_q, n_kv, pos_base + P);
+  if (need && !workspace) return M3_ERR_NULL;
+  if (workspace_bytes < need) return M3_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      (need && !aligned(workspace, 16)) || ldq % 8 || ldo % 8)
+    return M3_ERR_ALIGN;
+  const size_t q_b = ((size_t)(R - 1) * ldq + n_q * M3_HEAD_DIM) * 2;
+  const size_t o_b = ((size_t)(R - 1) * ldo + n_q * M3_HEAD_DIM) * 2;
+  const size_t c_b = cache_bytes(S, n_kv, max_pos);
+  if (overlap(out, o_b, q, q_b) || overlap(out, o_b, k_cache, c_b) || overlap(out, o_b, v_cache, c_b) ||
+      (need && (overlap(workspace, need, out, o_b) || overlap(workspace, need, q, q_b) ||
+                overlap(workspace, need, k_cache, c_b) || overlap(workspace, need, v_cache, c_b))))
+    return M3_ERR_ALIAS;
+  // row (s, t) attends over positions 0 .. pos_base + t of sequence s
+  return hip_status(launch_decode_attention(q, R, ldq, n_q, n_kv, k_cache, v_cache, max_pos,
+                                            pos_base + 1, out, ldo, workspace,
+                                            static_cast<hipStream_t>(stream), nullptr, 0, P));
+}
+
 uint64_t m3_frame_weight_bytes(const m3_config* c) {
   if (!c) return 0;
   const Dims d = dims_of(*c);

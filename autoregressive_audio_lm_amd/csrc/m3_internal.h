@@ -155,17 +155,19 @@ int attn_chunk_size(int B, int n_kv, int T);
 size_t attn_workspace_bytes(int B, int n_q, int n_kv, int T);
 hipError_t launch_rope_table(float* t, int max_pos, int head_dim, double theta, hipStream_t s);
 // frame_dev (optional, device): the position is pos0 + *frame_dev (held below
-// max_pos; past it, err gets M3_ERR_ATTN_FULL) and T = position + 1
+// max_pos; past it, err gets M3_ERR_ATTN_FULL) and T = position + 1.
+// P > 1 (prompt rows): row r is position pos + r % P of cache sequence r / P
+// and attends over T + r % P positions.
 hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
                                const float* q_gamma, const float* k_gamma, float eps,
                                const float* rope, int pos, uint16_t* q_out, int ldq,
                                uint16_t* k_cache, uint16_t* v_cache, int max_pos, hipStream_t s,
                                const uint32_t* frame_dev = nullptr, int pos0 = 0,
-                               uint32_t* err = nullptr);
+                               uint32_t* err = nullptr, int P = 1);
 hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv,
                                    const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
                                    int T, uint16_t* out, int ldo, void* ws, hipStream_t s,
-                                   const uint32_t* frame_dev = nullptr, int pos0 = 0);
+                                   const uint32_t* frame_dev = nullptr, int pos0 = 0, int P = 1);
 
 // ---- frame helpers -------------------------------------------------------------
 // audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)

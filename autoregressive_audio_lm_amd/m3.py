@@ -262,3 +262,50 @@ def decode_attention(q: torch.Tensor, n_q: int, n_kv: int, k_cache: torch.Tensor
                                     _stream(stream)))
     return out
 
+
+def prefill_qk_norm_rope(qkv: torch.Tensor, S: int, n_q: int, n_kv: int, q_gamma: torch.Tensor,
+                         k_gamma: torch.Tensor, rope: torch.Tensor, pos_base: int,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, eps: float = 1e-6,
+                         q_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_prefill_qk_norm_rope: rows [S * P] ordered [s][t]; row (s, t) at
+    position pos_base + t of cache s.  Returns q [S * P, n_q * 128]."""
+    for t, n in ((qkv, "qkv"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"), (rope, "rope"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache"), (q_out, "q_out")):
+        _cuda(t, n)
+    R = qkv.shape[0]
+    if R % S:
+        raise ValueError("rows must be S sequences of equal length")
+    if q_out is None:
+        q_out = torch.empty(R, n_q * HEAD_DIM, dtype=torch.bfloat16, device=qkv.device)
+    check(lib().m3_prefill_qk_norm_rope(_ptr(qkv), S, R // S, qkv.stride(0), int(n_q), int(n_kv),
+                                        HEAD_DIM, _ptr(q_gamma), _ptr(k_gamma), float(eps),
+                                        _ptr(rope), int(pos_base), _ptr(q_out), q_out.stride(0),
+                                        _ptr(k_cache), _ptr(v_cache), k_cache.shape[2],
+                                        _stream(stream)))
+    return q_out
+
+
+def prefill_attention(q: torch.Tensor, S: int, n_q: int, n_kv: int, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, pos_base: int, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_prefill_attention: causal attention of rows [S * P] (ordered [s][t])
+    over their caches; row (s, t) attends over positions 0 .. pos_base + t."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out"),
+                 (workspace, "workspace")):
+        _cuda(t, n)
+    R = q.shape[0]
+    if R % S:
+        raise ValueError("rows must be S sequences of equal length")
+    P = R // S
+    if out is None:
+        out = torch.empty(R, n_q * HEAD_DIM, dtype=torch.bfloat16, device=q.device)
+    need = int(lib().m3_prefill_attention_workspace_bytes(S, P, int(n_q), int(n_kv), int(pos_base)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().m3_prefill_attention(_ptr(q), S, P, q.stride(0), int(n_q), int(n_kv), HEAD_DIM,
+                                     _ptr(k_cache), _ptr(v_cache), k_cache.shape[2], int(pos_base),
+                                     _ptr(out), out.stride(0), _ptr(workspace), wbytes,
+                                     _stream(stream)))
+    return out
+

@@ -212,9 +212,9 @@ def time_cfg_draw(stream, S, V, top_k=50, calls=50, reps=5):
 
 def time_prefill(c, stream, M=600, reps=10):
     """One body layer of the prompt prefill at M rows (300 prompt tokens per
-    CFG row, two rows): RMSNorm rows, the QKV GEMM, the o-projection GEMM
-    with the residual epilogue (attention stubbed as identity, as in the
-    frame: it reads the q columns), RMSNorm rows, the gate/up GEMM with the
+    CFG row, two rows): RMSNorm rows, the QKV GEMM, q/k norm + RoPE with the
+    KV-cache write and causal attention over the prompt, the o-projection
+    GEMM with the residual epilogue, RMSNorm rows, the gate/up GEMM with the
     SwiGLU epilogue, the down GEMM with the residual epilogue.  Average
     durations with HIP events on the launch stream; seeded bf16 weights."""
     import torch
@@ -231,20 +231,35 @@ def time_prefill(c, stream, M=600, reps=10):
         W[name] = (m3.pack(0, Wd, flags), N, K)
         del Wd
     g1, g2 = synth.gamma_f32(H, 60, dev), synth.gamma_f32(H, 61, dev)
+    qg, kg = synth.gamma_f32(128, 63, dev), synth.gamma_f32(128, 64, dev)
     h = synth.activations(M, H, 62, device=dev)
     a = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
     qkv = torch.empty(M, nqkv, dtype=torch.bfloat16, device=dev)
     mlp = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    # the prompt's attention: 2 sequences (the CFG rows) of M / 2 positions
+    S = 2
+    rope = m3.rope_table(2048)
+    kc, vc = m3.kv_cache(S, c.n_kv_heads, 2048)
+    q = torch.empty(M, nq, dtype=torch.bfloat16, device=dev)
+    att = torch.empty(M, nq, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, int(m3.lib().m3_prefill_attention_workspace_bytes(
+        S, M // S, c.n_heads, c.n_kv_heads, 0))), dtype=torch.uint8, device=dev)
 
-    names = ("norm1", "qkv", "o", "norm2", "gate_up", "down")
+    names = ("norm1", "qkv", "qk_rope", "attention", "o", "norm2", "gate_up", "down")
 
     def launch(name):
         if name == "norm1":
             m3.rmsnorm_rows(h, g1, c.eps, a=a, stream=stream)
         elif name == "qkv":
             m3.prefill_gemm(*W["qkv"], a, y=qkv, stream=stream)
+        elif name == "qk_rope":
+            m3.prefill_qk_norm_rope(qkv, S, c.n_heads, c.n_kv_heads, qg, kg, rope, 0, kc, vc,
+                                    eps=c.eps, q_out=q, stream=stream)
+        elif name == "attention":
+            m3.prefill_attention(q, S, c.n_heads, c.n_kv_heads, kc, vc, 0, out=att, workspace=ws,
+                                 stream=stream)
         elif name == "o":
-            m3.prefill_gemm(*W["o"], qkv[:, :nq], y=h, epi=m3.EPI_RESIDUAL, residual=h, stream=stream)
+            m3.prefill_gemm(*W["o"], att, y=h, epi=m3.EPI_RESIDUAL, residual=h, stream=stream)
         elif name == "norm2":
             m3.rmsnorm_rows(h, g2, c.eps, a=a, stream=stream)
         elif name == "gate_up":
@@ -286,10 +301,14 @@ def time_prefill(c, stream, M=600, reps=10):
         gemms.append({"name": name, "N": N, "K": K, "avg_us": round(us, 2),
                       "TFLOP_s": round(tf, 1), "frac": round(tf / MFMA_BF16_PEAK_TFS, 4)})
     norm_us = (per["norm1"] + per["norm2"]) / 2
+    attn_us = per["qk_rope"] + per["attention"]
     gemm_us = sum(g["avg_us"] for g in gemms)
     tf = flops / (gemm_us * 1e-6) / 1e12
     del W
     return {"rows": M, "layer_us": round(layer_us, 2), "rmsnorm_rows_us": round(norm_us, 2),
+            "attention_us": round(attn_us, 2),
+            "attention": "q/k norm + RoPE + cache write, then causal attention of 2 sequences "
+                         f"of {M // S} positions (32:8 heads)",
             "gemms": gemms,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),

@@ -305,6 +305,33 @@ int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, in
                         uint16_t* out, int ldo, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* ---- the prompt's attention ------------------------------------------------- */
+/* The prompt's rows through the same steps as one decode row, all positions at
+ * once: S sequences (the CFG rows) of P prompt positions, rows ordered [s][t],
+ * row (s, t) at position pos_base + t of sequence s's cache.
+ *
+ * m3_prefill_qk_norm_rope: as m3_qk_norm_rope for every row at its own
+ * position; k and v of row (s, t) go to slot pos_base + t of cache s ([S][n_kv]
+ * [max_pos][128]).  The caches then hold the prompt for decode attention.
+ *
+ * m3_prefill_attention: causal attention, row (s, t) over positions 0 ..
+ * pos_base + t of cache s, with m3_decode_attention's arithmetic and
+ * chunking; workspace of m3_prefill_attention_workspace_bytes(S, P, n_q, n_kv,
+ * pos_base) bytes (0 when every row fits one chunk).
+ *
+ * 1 <= S <= M3_MAX_B; S * P <= M3_MAX_M_PREFILL; 0 <= pos_base, pos_base + P
+ * <= max_pos <= M3_MAX_POS; the other sizes, alignment and aliasing rules and
+ * the errors as for the decode calls. */
+int m3_prefill_qk_norm_rope(const uint16_t* qkv, int S, int P, int ldqkv, int n_q, int n_kv,
+                            int head_dim, const float* q_gamma, const float* k_gamma, float eps,
+                            const float* rope, int pos_base, uint16_t* q_out, int ldq,
+                            uint16_t* k_cache, uint16_t* v_cache, int max_pos, void* stream);
+size_t m3_prefill_attention_workspace_bytes(int S, int P, int n_q, int n_kv, int pos_base);
+int m3_prefill_attention(const uint16_t* q, int S, int P, int ldq, int n_q, int n_kv, int head_dim,
+                         const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
+                         int pos_base, uint16_t* out, int ldo, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* ---- one decode frame ------------------------------------------------------ */
 typedef struct {
   int hidden, n_layers, n_heads, n_kv_heads, head_dim, ffn;

@@ -193,6 +193,33 @@ def test_attention_refusals(L):
     assert L.m3_attention_workspace_bytes(2, 16, 16, 64) == 0
 
 
+def test_prompt_attention_refusals(L):
+    P = ctypes.c_void_p
+    need = L.m3_prefill_attention_workspace_bytes(2, 300, 32, 8, 0)
+    assert need == 600 * 32 * 3 * 130 * 4                # three chunks of 128 for the last rows
+    assert L.m3_prefill_attention_workspace_bytes(2, 300, 24, 8, 0) == 0   # unsupported heads
+    tab = P(0x1000000)
+    cb = 2 * 8 * 512 * 128 * 2
+    q_arg = lambda **k: (k.get("qkv", P(0x10000000)), k.get("S", 2), k.get("L", 300),
+                         k.get("ld", 6144), 32, 8, 128, P(0x30000000), P(0x30001000), 1e-6, tab,
+                         k.get("pb", 0), k.get("qo", P(0x20000000)), 4096, P(0x40000000),
+                         P(0x40000000 + cb), k.get("mp", 512), None)
+    assert L.m3_prefill_qk_norm_rope(*q_arg(qkv=None)) == _lib.M3_ERR_NULL
+    assert L.m3_prefill_qk_norm_rope(*q_arg(pb=300)) == _lib.M3_ERR_SHAPE    # past max_pos
+    assert L.m3_prefill_qk_norm_rope(*q_arg(S=65)) == _lib.M3_ERR_SHAPE
+    assert L.m3_prefill_qk_norm_rope(*q_arg(ld=6000)) == _lib.M3_ERR_SHAPE
+    assert L.m3_prefill_qk_norm_rope(*q_arg(qo=P(0x20000004))) == _lib.M3_ERR_ALIGN
+    assert L.m3_prefill_qk_norm_rope(*q_arg(qo=P(0x10000000 + 8192))) == _lib.M3_ERR_ALIAS
+    a_arg = lambda **k: (P(0x20000000), k.get("S", 2), k.get("L", 300), 4096, 32, 8, 128,
+                         P(0x40000000), P(0x40000000 + cb), k.get("mp", 512), k.get("pb", 0),
+                         k.get("out", P(0x50000000)), 4096, k.get("ws", P(0x60000000)),
+                         k.get("wsb", need), None)
+    assert L.m3_prefill_attention(*a_arg(out=None)) == _lib.M3_ERR_NULL
+    assert L.m3_prefill_attention(*a_arg(wsb=need - 4)) == _lib.M3_ERR_WORKSPACE
+    assert L.m3_prefill_attention(*a_arg(pb=213)) == _lib.M3_ERR_SHAPE        # 213 + 300 > 512
+    assert L.m3_prefill_attention(*a_arg(out=P(0x20000000 + 64))) == _lib.M3_ERR_ALIAS
+
+
 def test_cfg_draw_refusals(L):
     p = _lib.SampleParams(0, 0, None, 0, 1.0, 0, None, 0, 0, None)
     arg = lambda **k: (k.get("lg", FAKE), k.get("S", 4), k.get("V", 5000), k.get("ldl", 5000),

@@ -132,4 +132,78 @@ def test_decode_steps_build_the_cache():
         # at every step (the caches themselves are compared too)
         P.check_bf16_vs_bf16(synth.bits(kc[:, :, :pos + 1]), okc[:, :, :pos + 1], width=HD)
         P.check_bf16_vs_bf16(synth.bits(o), O.decode_attention(oq, okc, ovc, pos + 1, n_q, n_kv),
+                             agree=0.97, rel=1e-2, width=HD)
+
+
+# ---- the prompt's attention: S sequences of L positions at once ----------------
+def _prompt_case(S, L, n_q, n_kv, pos_base, max_pos, seed):
+    ldqkv = (n_q + 2 * n_kv) * HD
+    qkv = rnd_bf16((S * L, ldqkv), seed, 1.5)
+    qg = (1.0 + 0.1 * np.random.default_rng(seed + 1).standard_normal(HD)).astype(np.float32)
+    kg = (1.0 + 0.1 * np.random.default_rng(seed + 2).standard_normal(HD)).astype(np.float32)
+    # earlier positions (a previous chunk of the prompt) hold the same seeded values on both sides
+    kc, vc = fill_cache(S, n_kv, max_pos, pos_base, seed + 3, 1.0)
+    return qkv, qg, kg, kc, vc
+
+
+def _oracle_prompt(qkv, S, L, n_q, n_kv, qg, kg, pos_base, kc, vc, max_pos):
+    """The per-row oracle functions, row by row in position order: each row's
+    norm + RoPE writes its cache slot, then it attends over the positions so far."""
+    rope = O.rope_table(max_pos)
+    q = np.empty((S * L, n_q * HD), np.uint16)
+    out = np.empty_like(q)
+    for s in range(S):
+        for t in range(L):
+            r = s * L + t
+            q[r] = O.qk_norm_rope(qkv[r:r + 1], n_q, n_kv, qg, kg, 1e-6, rope, pos_base + t,
+                                  kc[s:s + 1], vc[s:s + 1])[0]
+            out[r] = O.decode_attention(q[r:r + 1], kc[s:s + 1], vc[s:s + 1], pos_base + t + 1,
+                                        n_q, n_kv)[0]
+    return q, out
+
+
+@pytest.mark.parametrize("S,L,n_q,n_kv,pos_base", [(2, 37, 32, 8, 0), (2, 50, 32, 8, 100),
+                                                    (1, 130, 16, 16, 3), (3, 7, 8, 4, 250)])
+def test_prompt_attention_matches_the_rows_one_by_one(S, L, n_q, n_kv, pos_base):
+    max_pos = pos_base + L + 5
+    qkv, qg, kg, kc, vc = _prompt_case(S, L, n_q, n_kv, pos_base, max_pos, 40 + L)
+    kd, vd = dev(kc), dev(vc)
+    q = m3.prefill_qk_norm_rope(dev(qkv), S, n_q, n_kv, torch.from_numpy(qg).to(DEV),
+                                torch.from_numpy(kg).to(DEV), m3.rope_table(max_pos), pos_base,
+                                kd, vd)
+    out = m3.prefill_attention(q, S, n_q, n_kv, kd, vd, pos_base)
+    torch.cuda.synchronize()
+    okc, ovc = kc.copy(), vc.copy()
+    oq, oout = _oracle_prompt(qkv, S, L, n_q, n_kv, qg, kg, pos_base, okc, ovc, max_pos)
+    new = slice(pos_base, pos_base + L)
+    P.check_bf16_vs_bf16(synth.bits(q), oq, width=HD)
+    gk, gv = synth.bits(kd), synth.bits(vd)
+    P.check_bf16_vs_bf16(gk[:, :, new], okc[:, :, new], width=HD)
+    assert np.array_equal(gv, ovc)
+    assert np.array_equal(gk[:, :, :pos_base], kc[:, :, :pos_base])    # earlier slots untouched
+    # each side attends with its own q and keys, which may differ by a bf16 ulp,
+    # so the outputs get a wider row-scaled term than a single rounding
+    P.check_bf16_vs_bf16(synth.bits(out), oout, agree=0.98, rel=1e-2, width=HD)
+
+
+def test_prompt_then_decode_steps():
+    """A 24-position prompt for 2 sequences fills the caches; three decode
+    steps at positions 24, 25, 26 then attend over prompt and steps alike."""
+    S, L, n_q, n_kv, max_pos = 2, 24, 32, 8, 32
+    qkv, qg, kg, kc, vc = _prompt_case(S, L, n_q, n_kv, 0, max_pos, 77)
+    qgd, kgd = torch.from_numpy(qg).to(DEV), torch.from_numpy(kg).to(DEV)
+    rope = m3.rope_table(max_pos)
+    kd, vd = dev(kc), dev(vc)
+    q = m3.prefill_qk_norm_rope(dev(qkv), S, n_q, n_kv, qgd, kgd, rope, 0, kd, vd)
+    m3.prefill_attention(q, S, n_q, n_kv, kd, vd, 0)
+    okc, ovc = kc.copy(), vc.copy()
+    _oracle_prompt(qkv, S, L, n_q, n_kv, qg, kg, 0, okc, ovc, max_pos)
+    orope = O.rope_table(max_pos)
+    for pos in (24, 25, 26):
+        step = rnd_bf16((S, (n_q + 2 * n_kv) * HD), 900 + pos, 1.5)
+        qs = m3.qk_norm_rope(dev(step), n_q, n_kv, qgd, kgd, rope, pos, kd, vd)
+        o = m3.decode_attention(qs, n_q, n_kv, kd, vd, pos + 1)
+        torch.cuda.synchronize()
+        oq = O.qk_norm_rope(step, n_q, n_kv, qg, kg, 1e-6, orope, pos, okc, ovc)
+        P.check_bf16_vs_bf16(synth.bits(o), O.decode_attention(oq, okc, ovc, pos + 1, n_q, n_kv),
                              agree=0.97, width=HD)
