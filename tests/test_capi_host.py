@@ -272,3 +272,35 @@ def test_frame_layout_and_refusals(L):
     m = _lib.Model(cfg=c)
     codes = ctypes.c_void_p(0x300000)
     assert L.m3_decode_frame_weights(ctypes.byref(m), FAKE, 1, codes, None, None) == _lib.M3_ERR_NULL
+
+
+def test_frame_layout_with_attention(L):
+    """attention = 1 adds the RoPE table, q/out buffers, the body and depth
+    caches and the attention workspace to the state (zero-sized otherwise);
+    the sizes follow the documented layouts."""
+    cfg = configs.config("frame-full")
+    B, max_pos = 2, 2048
+    plain = make_config(cfg, **configs.PRESETS["A"])
+    att = make_config(cfg, **configs.PRESETS["A"], attention=1, max_pos=max_pos, pos0=300)
+    lp, la = _lib.FrameLayout(), _lib.FrameLayout()
+    assert L.m3_frame_layout_get(ctypes.byref(plain), B, ctypes.byref(lp)) == 0
+    assert L.m3_frame_layout_get(ctypes.byref(att), B, ctypes.byref(la)) == 0
+    # the plain layout is unchanged by the attention fields
+    assert lp.total == lp.rope == lp.kcache == lp.attn_ws
+    kv = cfg["n_layers"] * B * cfg["n_kv_heads"] * max_pos * 128 * 2
+    assert la.vcache - la.kcache >= kv and la.dkcache - la.vcache >= kv
+    dkv = cfg["d_layers"] * B * cfg["d_heads"] * 8 * 128 * 2
+    assert la.dvcache - la.dkcache >= dkv and la.attn_ws - la.dvcache >= dkv
+    assert la.aq - la.rope >= max_pos * 64 * 2 * 4
+    assert la.total - la.attn_ws == L.m3_attention_workspace_bytes(B, cfg["n_heads"],
+                                                                   cfg["n_kv_heads"], max_pos)
+    assert la.total > lp.total + 2 * kv
+    # attention settings out of range are refused
+    for bad in (dict(attention=2, max_pos=16), dict(attention=1, max_pos=0),
+                dict(attention=1, max_pos=16, pos0=16), dict(attention=1, max_pos=70000),
+                dict(attention=1, max_pos=16, pos0=-1)):
+        c = make_config(cfg, **configs.PRESETS["A"], **bad)
+        assert L.m3_frame_layout_get(ctypes.byref(c), B, ctypes.byref(la)) == _lib.M3_ERR_SHAPE
+    # GQA groups other than 1, 2, 4, 8 query heads per KV head are refused
+    c = make_config(dict(cfg, n_heads=24), **configs.PRESETS["A"], attention=1, max_pos=16)
+    assert L.m3_frame_layout_get(ctypes.byref(c), B, ctypes.byref(la)) == _lib.M3_ERR_SHAPE
