@@ -95,6 +95,41 @@ def test_gemv_norm_parity(fmt, B):
     P.check_f32(run_gemv(fmt, W, x, g, out_f32=True), y_ex)
 
 
+@pytest.mark.parametrize("fmt", [0, 2])
+@pytest.mark.parametrize("B", [1, 2])
+def test_gemv_norm_long_rows(fmt, B):
+    """One or two normed rows of K = 8320 (more than one 8-value chunk per
+    thread in the copy and in the normalising pass)."""
+    N, K = 136, 8320
+    W = rand_w(N, K, 15 + fmt)
+    x = rand_x(B, K, 25 + B)
+    g = rand_gamma(K, 35)
+    y_ex = oracle_y(fmt, W, x, g)
+    P.check_bf16(run_gemv(fmt, W, x, g), y_ex)
+    P.check_f32(run_gemv(fmt, W, x, g, out_f32=True), y_ex)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("B,K", [(16, 5248), (11, 7296)])
+def test_gemv_operand_from_memory(fmt, B, K):
+    """Rows too long for LDS (B * K * 2 bytes over 160 KB): the 16-row MFMA
+    kernel reads each batch's operand from memory next to its weights;
+    ragged N, a partial 16-row tile at B = 11, plain, residual and SwiGLU
+    outputs."""
+    N = 136
+    W = rand_w(N, K, 45 + fmt)
+    x = rand_x(B, K, 55 + B)
+    y_ex = oracle_y(fmt, W, x)
+    P.check_f32(run_gemv(fmt, W, x, out_f32=True), y_ex)
+    h = rand_x(B, N, 65 + B)
+    P.check_residual(run_gemv(fmt, W, x, epi=m3.EPI_RESIDUAL, res=h), h, y_ex)
+    F = 56
+    Wg, Wu = rand_w(F, K, 75 + fmt), rand_w(F, K, 85 + fmt)
+    m = run_gemv(fmt, np.concatenate([Wg, Wu], 0), x, epi=m3.EPI_SWIGLU,
+                 flags=m3.PACK_GLU_INTERLEAVE)
+    P.check_swiglu(m, oracle_y(fmt, O.interleave_gate_up(Wg, Wu), x))
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("B", [1, 6, 16])
 def test_gemv_plain_and_residual(fmt, B):
