@@ -374,10 +374,18 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   struct Prod {
     int x = -1, res = -1, u = -1, part = -1;
   };
+  // Scheduling of a persistent launch (values unchanged): with the attention
+  // stub, O reads only the V rows of QKV, so QKV takes its V row blocks first
+  // (rot) and O starts while the workgroups with a second QKV block finish
+  // it; the depth decoder's O (fewer blocks than workgroups) goes to the
+  // workgroups that had one QKV block (follow).
+  struct Sched {
+    int rot = 0, follow = 0;
+  };
   auto gemv = [&](int fmt, const void* w, int N, int K, const uint16_t* xin, int ldx,
                   const float* gamma, int sg, int sv, void* y, int ldy, int f32, int epi,
                   const uint16_t* res, int ldr, Prod pr, const SampleEpi* smp = nullptr,
-                  const GatherPro* gat = nullptr) {
+                  const GatherPro* gat = nullptr, Sched sc = Sched{}) {
     GemvDesc g{fmt, w, N, K, xin, ldx, B, gamma, eps, sg, sv, y, ldy, f32, epi, res, ldr, smp, gat};
     if (tagged) {
       g.px = pr.x;
@@ -385,6 +393,8 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
       g.pu = pr.u;
       g.ppart = pr.part;
       g.ytag = 1;
+      g.rot = sc.rot;
+      g.follow = sc.follow;
     }
     const hipError_t e = sink.gemv(g);
     ++ph;
@@ -414,8 +424,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     Prod a;
     a.x = p_xin;
     p_qkv = ph;
+    Sched qs;
+    if (!attn) qs.rot = (d.nq + d.nkv) / 16;      // the first V row block
     M3_TRY(gemv(c.fmt_body, W.qkv, d.nqkv, d.H, xin, d.H, W.attn_norm, 0, 0, qkv, d.nqkv, 0,
-                M3_EPI_NONE, nullptr, 0, a));
+                M3_EPI_NONE, nullptr, 0, a, nullptr, nullptr, qs));
     Prod o;
     o.x = p_qkv;
     o.res = p_xin;
@@ -509,8 +521,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
         q.x = p_hd;
       }
       p_dqkv = ph;
+      Sched qs;
+      if (!attn) qs.rot = 2 * d.dq / 16;           // the first V row block
       M3_TRY(gemv(c.fmt_depth, W.qkv, d.dqkv, d.D, hd, d.D, W.attn_norm, 0, 0, dqkv, d.dqkv, 0,
-                  M3_EPI_NONE, nullptr, 0, q, nullptr, l == 0 ? &gp : nullptr));
+                  M3_EPI_NONE, nullptr, 0, q, nullptr, l == 0 ? &gp : nullptr, qs));
       Prod o;
       o.x = p_dqkv;
       o.res = p_hd;
@@ -525,8 +539,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
                     M3_EPI_RESIDUAL, hd, d.D, o));
       } else {
         p_hd = ph;
+        Sched os;
+        os.follow = (d.dqkv + 15) / 16;
         M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd, d.D, 0,
-                    M3_EPI_RESIDUAL, hd, d.D, o));
+                    M3_EPI_RESIDUAL, hd, d.D, o, nullptr, nullptr, os));
       }
       Prod gu;
       gu.x = p_hd;

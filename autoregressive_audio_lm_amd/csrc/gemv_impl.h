@@ -68,6 +68,7 @@ struct Params {
   // persistent launch only: the phase that produced each input (-1: a plain
   // bf16 buffer written before the launch) and whether outputs are tagged
   int px, pres, pu, ppart, ytag;
+  int rot, follow;     // block order and workgroup offset (GemvDesc)
 };
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -1036,8 +1037,22 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   const int t_lo = (units * wave / kWaves) * TPU;
   const int ntw = (units * (wave + 1) / kWaves) * TPU - t_lo;       // tiles of this wave
   const int nbat = ((units + kWaves - 1) / kWaves * TPU + kU - 1) / kU;   // same for all waves
-  const int my_blocks = wg < p.nblocks ? (p.nblocks - wg + nwg - 1) / nwg : 0;
+  // workgroup wg works as ewg: with follow = the block count F of the phase
+  // before (nwg < F < 2 nwg), the workgroups that had one block there (wg >=
+  // F - nwg) come first
+  int ewg = wg;
+  if (p.follow > nwg && p.follow < 2 * nwg) {
+    ewg = wg + 2 * nwg - p.follow;
+    if (ewg >= nwg) ewg -= nwg;
+  }
+  const int my_blocks = ewg < p.nblocks ? (p.nblocks - ewg + nwg - 1) / nwg : 0;
   const int nitems = my_blocks * nbat;
+  // item j's row block: ewg + (j / nbat) nwg, rotated by rot
+  auto block_of = [&](int j) {
+    int rb = ewg + (j / nbat) * nwg + p.rot;
+    if (rb >= p.nblocks) rb -= p.nblocks;
+    return rb;
+  };
   Tags tg;
   {
     const uint32_t eb = wt.ebase();
@@ -1059,7 +1074,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   const int G = p.K / 128;                 // groups per row (i8g128)
   auto load = [&](uint4* dst, float* sc, int j) {
     const bool live = j < nitems;
-    const int rb = wg + (j / nbat) * nwg, bi = j % nbat;
+    const int rb = block_of(j), bi = j % nbat;
     const uint32_t base = (uint32_t)((size_t)rb * p.bbytes) + (uint32_t)t_lo * kTileBytes;
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
@@ -1085,7 +1100,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   Accum<FMT, NB, MFMA> A;
   A.reset();
   auto compute = [&](const uint4* src, const float* scv, int j) {
-    const int rb = wg + (j / nbat) * nwg, bi = j % nbat;
+    const int rb = block_of(j), bi = j % nbat;
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
       const int tt = bi * kU + i;
@@ -1224,6 +1239,8 @@ inline Params make_params(const GemvDesc& d, bool* lds, int* ku) {
   p.pu = d.pu;
   p.ppart = d.ppart;
   p.ytag = d.ytag;
+  p.rot = d.rot;
+  p.follow = d.follow;
   *ku = ku_of(d.fmt, *lds);
   return p;
 }

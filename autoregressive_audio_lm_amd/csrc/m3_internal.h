@@ -76,6 +76,11 @@ struct GemvDesc {
   // persistent frame only: producing phase of x / residual / gather u /
   // gather partials (-1: plain buffer), tagged outputs
   int px = -1, pres = -1, pu = -1, ppart = -1, ytag = 0;
+  // persistent frame only, scheduling (no effect on any value): rot = the
+  // row block taken first (blocks in the order rot, rot + 1, ... mod the
+  // count); follow = the block count of the phase before, whose workgroups
+  // with one block fewer take this phase's blocks first (0: workgroup 0)
+  int rot = 0, follow = 0;
 };
 
 // Largest fused-norm activation block held in LDS (elements of B * K_pad).

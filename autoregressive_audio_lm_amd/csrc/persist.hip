@@ -61,6 +61,7 @@ int persist_plan_size(const PersistPlan* pl) { return (int)pl->phases.size(); }
 
 hipError_t persist_add_gemv(PersistPlan* pl, const GemvDesc& d) {
   if ((int)pl->phases.size() >= kMaxPhases || d.B != pl->B) return hipErrorInvalidValue;
+  if (d.rot < 0 || d.rot >= n_blocks(d.N) || d.follow < 0) return hipErrorInvalidValue;
   Phase ph{};
   bool lds;
   int ku;
