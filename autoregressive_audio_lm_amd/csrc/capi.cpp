@@ -221,6 +221,8 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.thd = take((size_t)B * d.D * 4);
   L.tdqkv = take((size_t)B * d.dqkv * 4);
   L.tdmlp = take((size_t)B * d.Fd * 4);
+  L.th2 = take((size_t)B * d.H * 4);
+  L.thd2 = take((size_t)B * d.D * 4);
   const bool at = c.attention != 0;
   const int rope_pos = at ? std::max(c.max_pos, 8) : 0;
   L.rope = take((size_t)rope_pos * 64 * 2 * 4);
@@ -358,6 +360,12 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   float* logits = reinterpret_cast<float*>(S + L.logits);
   uint16_t* u = buf(L.u, L.tu);
   uint16_t* hd = buf(L.hd, L.thd);
+  // O's output: in place in the eager/graph frames (a kernel boundary
+  // separates every step); in a persistent launch a second stream, since a
+  // workgroup may still be staging QKV's input (the residual stream) when
+  // another has its V rows and writes O's rows; down writes the stream back
+  uint16_t* h_o = tagged ? reinterpret_cast<uint16_t*>(S + L.th2) : h;
+  uint16_t* hd_o = tagged ? reinterpret_cast<uint16_t*>(S + L.thd2) : hd;
   uint16_t* dqkv = buf(L.dqkv, L.tdqkv);
   uint16_t* dmlp = buf(L.dmlp, L.tdmlp);
   float* dlogits = reinterpret_cast<float*>(S + L.dlogits);
@@ -431,30 +439,31 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     Prod o;
     o.x = p_qkv;
     o.res = p_xin;
+    int p_ho;
     if (attn) {
       const size_t lay = (size_t)B * c.n_kv_heads * c.max_pos * 128 * 2;
       M3_TRY(attention(qkv, d.nqkv, c.n_heads, c.n_kv_heads, W,
                        reinterpret_cast<uint16_t*>(S + L.kcache + l * lay),
                        reinterpret_cast<uint16_t*>(S + L.vcache + l * lay), c.max_pos, 0, true));
-      p_h = ph;
-      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, ao, d.nq, nullptr, 0, 0, h, d.H, 0, M3_EPI_RESIDUAL,
-                  xin, d.H, o));
+      p_ho = ph;
+      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, ao, d.nq, nullptr, 0, 0, h_o, d.H, 0,
+                  M3_EPI_RESIDUAL, xin, d.H, o));
     } else {
-      p_h = ph;
-      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, qkv, d.nqkv, nullptr, group, d.nq + d.nkv, h, d.H,
+      p_ho = ph;
+      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, qkv, d.nqkv, nullptr, group, d.nq + d.nkv, h_o, d.H,
                   0, M3_EPI_RESIDUAL, xin, d.H, o));
     }
     Prod gu;
-    gu.x = p_h;
+    gu.x = p_ho;
     p_mlp = ph;
-    M3_TRY(gemv(c.fmt_body, W.gate_up, 2 * d.F, d.H, h, d.H, W.ffn_norm, 0, 0, mlp, d.F, 0,
+    M3_TRY(gemv(c.fmt_body, W.gate_up, 2 * d.F, d.H, h_o, d.H, W.ffn_norm, 0, 0, mlp, d.F, 0,
                 M3_EPI_SWIGLU, nullptr, 0, gu));
     Prod dn;
     dn.x = p_mlp;
-    dn.res = p_h;
+    dn.res = p_ho;
     p_h = ph;
     M3_TRY(gemv(c.fmt_body, W.down, d.H, d.F, mlp, d.F, nullptr, 0, 0, h, d.H, 0,
-                M3_EPI_RESIDUAL, h, d.H, dn));
+                M3_EPI_RESIDUAL, h_o, d.H, dn));
   }
   // The reference's draw (top_k > 0): guidance over (conditional,
   // unconditional) row pairs, top-k, Gumbel-argmax; one draw per song, left
@@ -528,33 +537,34 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
       Prod o;
       o.x = p_dqkv;
       o.res = p_hd;
+      int p_hdo;
       if (attn) {
         // step j attends over the frame's codebook positions 0 .. j - 1
         const size_t lay = (size_t)B * c.d_heads * 8 * 128 * 2;
         M3_TRY(attention(dqkv, d.dqkv, c.d_heads, c.d_heads, W,
                          reinterpret_cast<uint16_t*>(S + L.dkcache + l * lay),
                          reinterpret_cast<uint16_t*>(S + L.dvcache + l * lay), 8, j - 1, false));
-        p_hd = ph;
-        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, ao, d.dq, nullptr, 0, 0, hd, d.D, 0,
+        p_hdo = ph;
+        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, ao, d.dq, nullptr, 0, 0, hd_o, d.D, 0,
                     M3_EPI_RESIDUAL, hd, d.D, o));
       } else {
-        p_hd = ph;
+        p_hdo = ph;
         Sched os;
         os.follow = (d.dqkv + 15) / 16;
-        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd, d.D, 0,
+        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, dqkv, d.dqkv, nullptr, 1, 2 * d.dq, hd_o, d.D, 0,
                     M3_EPI_RESIDUAL, hd, d.D, o, nullptr, nullptr, os));
       }
       Prod gu;
-      gu.x = p_hd;
+      gu.x = p_hdo;
       p_dmlp = ph;
-      M3_TRY(gemv(c.fmt_depth, W.gate_up, 2 * d.Fd, d.D, hd, d.D, W.ffn_norm, 0, 0, dmlp, d.Fd, 0,
-                  M3_EPI_SWIGLU, nullptr, 0, gu));
+      M3_TRY(gemv(c.fmt_depth, W.gate_up, 2 * d.Fd, d.D, hd_o, d.D, W.ffn_norm, 0, 0, dmlp, d.Fd,
+                  0, M3_EPI_SWIGLU, nullptr, 0, gu));
       Prod dn;
       dn.x = p_dmlp;
-      dn.res = p_hd;
+      dn.res = p_hdo;
       p_hd = ph;
       M3_TRY(gemv(c.fmt_depth, W.down, d.D, d.Fd, dmlp, d.Fd, nullptr, 0, 0, hd, d.D, 0,
-                  M3_EPI_RESIDUAL, hd, d.D, dn));
+                  M3_EPI_RESIDUAL, hd_o, d.D, dn));
     }
     SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep};
     Prod hp;

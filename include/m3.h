@@ -420,6 +420,10 @@ typedef struct {
                    /* u32 words (bf16 value | 16-bit producer tag): the
                       persistent frame's intermediate streams; h, qkv, mlp, u,
                       hd, dqkv, dmlp above belong to the eager/graph frames   */
+  size_t th2, thd2; /* u32 words [B, hidden], [B, d_hidden]: the persistent
+                      frame's residual streams after O (O writes here, not in
+                      place, so that no workgroup still staging QKV's input
+                      can see a newer tag)                                     */
   /* attention = 1 only (zero-sized otherwise): */
   size_t rope;     /* f32  [max(max_pos, 8), 64, 2] RoPE table                 */
   size_t aq, ao;   /* bf16 [B, max(nq, d_hidden)] rotated q; attention output  */

@@ -255,6 +255,12 @@ def test_frame_layout_and_refusals(L):
     lay = _lib.FrameLayout()
     assert L.m3_frame_layout_get(ctypes.byref(c), 16, ctypes.byref(lay)) == 0
     assert lay.total % 256 == 0 and lay.x == 0 and lay.total > lay.part_dep > lay.part_sem > lay.frame
+    # the persistent frame's streams: tagged 32-bit words, O's outputs in their own regions
+    names = ("th", "tqkv", "tmlp", "tu", "thd", "tdqkv", "tdmlp", "th2", "thd2", "rope")
+    offs = [getattr(lay, n) for n in names]
+    assert offs == sorted(offs) and len(set(offs)) == len(offs)
+    assert lay.thd2 - lay.th2 >= 16 * cfg["H"] * 4 and lay.rope - lay.thd2 >= 16 * cfg["D"] * 4
+    assert lay.tqkv - lay.th >= 16 * cfg["H"] * 4 and lay.tdqkv - lay.thd >= 16 * cfg["D"] * 4
     assert L.m3_frame_workspace_bytes(ctypes.byref(c), 17) == 0
     assert L.m3_frame_layout_get(ctypes.byref(c), 0, ctypes.byref(lay)) == _lib.M3_ERR_SHAPE
     c2 = make_config(cfg, 0, 2, 2)                                   # lm_head must be bf16/i8row
