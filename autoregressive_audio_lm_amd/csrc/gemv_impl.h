@@ -293,12 +293,15 @@ __device__ __forceinline__ uint4 untag8(const uint4& a, const uint4& b, uint32_t
                     (b.x & 0xffffu) | (b.y << 16), (b.z & 0xffffu) | (b.w << 16));
 }
 
-// one attempt at elements e .. e+7 of an activation row buffer
-template <bool COH>
+// one attempt at elements e .. e+7 of an activation row buffer.  FIRST: a
+// first attempt at tagged words through the caches (a workgroup of the same
+// XCD may have brought the line in; a stale or torn line fails the tag check
+// like an early read), later attempts bypass them
+template <bool COH, bool FIRST = false>
 __device__ __forceinline__ uint4 act_try8(const void* base, size_t e, uint32_t tag, bool& ok) {
   if constexpr (COH) {
     if (tag != kPlain) {
-      const uint4 a = ld16<true>(base, e * 4), b = ld16<true>(base, e * 4 + 16);
+      const uint4 a = ld16<!FIRST>(base, e * 4), b = ld16<!FIRST>(base, e * 4 + 16);
       return untag8(a, b, tag, ok);
     }
   }
@@ -309,7 +312,7 @@ __device__ __forceinline__ uint4 act_try8(const void* base, size_t e, uint32_t t
 template <bool COH>
 __device__ __forceinline__ uint4 act_load8(const void* base, size_t e, uint32_t tag, uint32_t* err) {
   bool ok;
-  uint4 v = act_try8<COH>(base, e, tag, ok);
+  uint4 v = act_try8<COH, true>(base, e, tag, ok);
   if constexpr (COH) {
     long n = 0;
     while (!ok && spin_more(n, err)) v = act_try8<COH>(base, e, tag, ok);
@@ -388,9 +391,9 @@ __device__ __forceinline__ uint4 load_x8(const Params& p, int b, int k, const Ta
   return act_load8<COH>(p.x, (size_t)b * p.ldx + src_col(p, k), tg.x, tg.err);
 }
 
-template <bool COH>
+template <bool COH, bool FIRST = false>
 __device__ __forceinline__ uint4 try_x8(const Params& p, int b, int k, const Tags& tg, bool& ok) {
-  return act_try8<COH>(p.x, (size_t)b * p.ldx + src_col(p, k), tg.x, ok);
+  return act_try8<COH, FIRST>(p.x, (size_t)b * p.ldx + src_col(p, k), tg.x, ok);
 }
 
 // Gather prologue: the previous draw of every batch row, from the per-block
@@ -481,14 +484,15 @@ struct OperandSource {
     return p.gat.emb + (size_t)c * p.K;
   }
 
+  template <bool FIRST = false>
   __device__ __forceinline__ uint4 attempt(int b, int k, bool& ok) const {
     ok = true;
     if (k >= p.K) return make_uint4(0, 0, 0, 0);
     if (p.has_gather) {
-      const uint4 uv = act_try8<COH>(p.gat.u, (size_t)b * p.K + k, tg.u, ok);
+      const uint4 uv = act_try8<COH, FIRST>(p.gat.u, (size_t)b * p.K + k, tg.u, ok);
       return bf16x8_add(uv, *reinterpret_cast<const uint4*>(emb_row(b) + k));
     }
-    return try_x8<COH>(p, b, k, tg, ok);
+    return try_x8<COH, FIRST>(p, b, k, tg, ok);
   }
 
   __device__ __forceinline__ uint4 settle(int b, int k) const {
@@ -542,7 +546,7 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
         const int i = r * kThreads + tid;
         ok[r] = true;
         v[r] = make_uint4(0, 0, 0, 0);
-        if (i < nchunk) v[r] = src.attempt(b, i << 3, ok[r]);
+        if (i < nchunk) v[r] = src.template attempt<true>(b, i << 3, ok[r]);
       }
 #pragma unroll
       for (int r = 0; r < kPreRounds; ++r) {
@@ -632,7 +636,7 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
         const int it = base + u * kThreads;
         const int b = it / cpr, k = (it - b * cpr) * 8;
         const bool in = it < total && k < p.K;
-        const uint4 x = src.attempt(in ? b : 0, in ? k : 0, ok[u]);
+        const uint4 x = src.template attempt<true>(in ? b : 0, in ? k : 0, ok[u]);
         v[u] = in ? x : make_uint4(0, 0, 0, 0);
         ok[u] = ok[u] || !in;
       }
