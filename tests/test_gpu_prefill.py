@@ -36,10 +36,13 @@ def gemm(W, a, epi=m3.EPI_NONE, out_f32=False, res=None, flags=0):
     return y.cpu().numpy() if out_f32 else synth.bits(y)
 
 
-# the last two reach the 64 x 256 tiles (at least 256 of them), the others 64 x 128
+# (1000, 4100) and (1024, 4096) reach the 64 x 256 tiles (at least 256 of
+# them); (600, 4096) and (650, 3000) the 96 x 128 tiles (more than 256 tiles
+# of 64 x 128, at most 256 of 96 x 128; 650 rows end in a partial tile); the
+# others 64 x 128
 @pytest.mark.parametrize("M,N,K", [(1, 16, 64), (37, 200, 512), (600, 256, 512), (129, 130, 1024),
                                    (300, 520, 256), (37, 300, 8192), (1000, 4100, 128),
-                                   (1024, 4096, 192)])
+                                   (1024, 4096, 192), (600, 4096, 128), (650, 3000, 192)])
 def test_prefill_gemm_parity(M, N, K):
     W = rand_w(N, K, M + N)
     a = rand_x(M, K, K + 3)
