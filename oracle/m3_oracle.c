@@ -149,7 +149,7 @@ void m3o_quant_i8g128(const uint16_t* W, int N, int K, int8_t* q, float* s) {
 /* ------------------------------------------------------------------ */
 /* fp8 weight-only (the next format after int8: [hf] and [mm] list fp8  */
 /* weight-only only as a result measured on another stack; the format   */
-/* is this build's reading): OCP FP8 E4M3 -- sign, 4 exponent bits with */
+/* is a reading made here): OCP FP8 E4M3 -- sign, 4 exponent bits with */
 /* bias 7, 3 mantissa bits; exponent 0 holds the subnormals m * 2^-9;   */
 /* S.1111.111 is NaN; there is no infinity; the largest finite is 448.  */
 /* One fp32 scale per row: s = absmax / 448 as one fp32 division, q =   */

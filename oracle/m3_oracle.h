@@ -116,7 +116,7 @@ typedef struct {
 } m3o_sample_params;
 /* out[b] = absolute id of argmax_j z[b,j]; z = fl32(l*fl32(1/T)) + g.
    zbest/zsecond (optional) receive the best and second-best z of each row
-   (used by tests to judge how close a decision was). */
+   (used by tests to measure how close a decision was). */
 void m3o_gumbel_argmax(const float* logits, int B, int V, int ldl,
                        const m3o_sample_params* p, int32_t* out,
                        float* zbest, float* zsecond);

@@ -1,6 +1,6 @@
 """Comparison rules shared by the GPU parity tests (imported by tests only).
 
-Tolerances (spec: GEMV outputs within 1e-2 * rms(y) for bf16 out and
+Tolerances (target: GEMV outputs within 1e-2 * rms(y) for bf16 out and
 2e-3 * rms(y) for fp32 out; sampling bit-exact):
 
 * fp32 out:  |y_gpu - y_exact| <= 2e-3 * rms(y_exact) per batch row.

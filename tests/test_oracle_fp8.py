@@ -2,7 +2,7 @@
 infinity, largest finite 448; one fp32 scale per row, absmax / 448).  The
 pages list fp8 weight-only only as a result on another stack (diffusers
 issue #14486 and MiniMax-Music3 issue #2, negative results), so the format
-is this build's reading.
+is the reading taken here.
 
 Pinned by: torch's float8_e4m3fn as a library routine (every code decoded,
 float32 values encoded), round trips and tie-to-even midpoints from the
