@@ -117,6 +117,40 @@ def test_full_size_persistent_equals_graph(preset, B):
     p.release()
 
 
+@pytest.mark.parametrize("preset,B,frames", [("A", 1, 300), ("B", 2, 150)])
+def test_full_size_persistent_equals_graph_over_many_frames(preset, B, frames):
+    """A chained run: every frame feeds the next (codes -> embeddings -> x),
+    the persistent frame and the graph-replayed frame stay byte-identical
+    frame after frame, and the persistent launches never give up waiting.
+    300 launches take the 16-bit tags of the tagged streams (launch counter
+    * 512 + phase + 1) through their wrap-around twice."""
+    cfg = configs.config("frame-full")
+    md = synth.make_model(cfg, **configs.PRESETS[preset], seed=23, device=DEV)
+    dm = runtime.DecodeModel(md, seed=6, free_sources=True)
+    del md
+    torch.cuda.empty_cache()
+    x0 = synth.activations(B, cfg["H"], 902, device=DEV)
+    g = runtime.FrameState(dm, B, x0, frame0=3)
+    p = runtime.FrameState(dm, B, x0, frame0=3)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g.capture(s)
+        p.persistent_create(s)
+        for f in range(frames):
+            g.replay(s)
+            p.persistent_launch(s)
+            s.synchronize()
+            assert int(p.err.item()) == 0, f
+            assert torch.equal(g.codes, p.codes), f
+            if f % 50 == 49 or f == frames - 1:
+                for name in ("x", "h", "logits"):
+                    assert torch.equal(getattr(g, name), getattr(p, name)), (f, name)
+                assert torch.equal(g.ring, p.ring), f
+                assert int(g.frame.item()) == int(p.frame.item()) == 3 + f + 1
+    g.release()
+    p.release()
+
+
 def test_full_size_persistent_refuses_unstaged_operands():
     """At B = 16 the body down projection's operand does not fit LDS: the
     persistent frame is refused (the graph-replayed frame serves it)."""
