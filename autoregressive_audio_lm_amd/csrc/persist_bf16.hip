@@ -7,7 +7,6 @@ namespace m3 {
 const void* persist_kernel_bf16(int NB) {
   switch (NB) {
     case 1: return reinterpret_cast<const void*>(frame_kernel<1, M3_BF16>);
-    case 2: return reinterpret_cast<const void*>(frame_kernel<2, M3_BF16>);
     default: return reinterpret_cast<const void*>(frame_kernel<16, M3_BF16>);
   }
 }
