@@ -36,7 +36,6 @@ hipError_t launch_one(const Params& p, int grid, size_t smem, hipStream_t s) {
 template <int FMT, bool LDS>
 hipError_t dispatch_b(const Params& p, int grid, size_t smem, hipStream_t s) {
   const int B = p.B;
-  if (B <= 1) return launch_one<FMT, 1, false, LDS>(p, grid, smem, s);
   if (B <= 16) return launch_one<FMT, 16, true, LDS>(p, grid, smem, s);
   if (B <= 32) return launch_one<FMT, 32, true, LDS>(p, grid, smem, s);
   if (B <= 48) return launch_one<FMT, 48, true, LDS>(p, grid, smem, s);
@@ -46,7 +45,6 @@ hipError_t dispatch_b(const Params& p, int grid, size_t smem, hipStream_t s) {
 template <int FMT, bool LDS, bool GLU, int KU>
 hipError_t configure_ku() {
   const hipError_t es[] = {
-      configure_one<FMT, 1, false, LDS, GLU, KU>(),
       configure_one<FMT, 16, true, LDS, GLU, KU>(),  configure_one<FMT, 32, true, LDS, GLU, KU>(),
       configure_one<FMT, 48, true, LDS, GLU, KU>(),  configure_one<FMT, 64, true, LDS, GLU, KU>()};
   for (hipError_t e : es)

@@ -1179,12 +1179,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Host-side helpers shared by the launch paths.
 // ---------------------------------------------------------------------------
-// Rows per accumulator tile: one row on the VALU (dot2), from two rows on
-// the MFMA path in tiles of 16 (rows past B repeat row B-1 and are not
-// stored; measured, a 16-row MFMA tile beats a 4-row VALU tile already at 3,
-// and the 2-row VALU tile by 5% on the B = 2 frame).
+// Rows per accumulator tile: the MFMA path in tiles of 16 for every row
+// count (rows past B repeat row B-1 and are not stored).  Measured against
+// the VALU (dot2) tiles the parameters still express: 5% on the B = 2 frame,
+// 0.5% at B = 1, and more from B = 3 on.
 inline int nb_of(int B) {
-  if (B <= 1) return 1;
   return (B + 15) / 16 * 16;
 }
 

@@ -5,10 +5,8 @@
 namespace m3 {
 
 const void* persist_kernel_bf16(int NB) {
-  switch (NB) {
-    case 1: return reinterpret_cast<const void*>(frame_kernel<1, M3_BF16>);
-    default: return reinterpret_cast<const void*>(frame_kernel<16, M3_BF16>);
-  }
+  (void)NB;                 // every row count runs on 16-row tiles
+  return reinterpret_cast<const void*>(frame_kernel<16, M3_BF16>);
 }
 
 }  // namespace m3

@@ -46,7 +46,7 @@ TRAFFIC_FILE = TRAFFIC["gate_up"][0]
 
 def m3nb(B: int) -> int:
     """Rows per accumulator tile the kernels use for B rows."""
-    return 1 if B <= 1 else 2 if B <= 2 else (B + 15) // 16 * 16
+    return (B + 15) // 16 * 16
 
 
 def log(*a):
@@ -516,7 +516,7 @@ def main():
     us, kbytes, n = time_gate_up(dm, st, stream)
     k_gbs = kbytes / (us * 1e-6) / 1e9
     log(f"[bench] gate/up GEMV: {us:.2f} us per launch over {n} launches, {k_gbs:.1f} GB/s")
-    gate_up = {"kernel": "gemv_kernel<bf16, VALU, SwiGLU> (body gate/up, RMSNorm fused)"
+    gate_up = {"kernel": "gemv_kernel<bf16, MFMA 16-row tile, SwiGLU> (body gate/up, RMSNorm fused)"
                          if dm.fmt_body == 0 else "gemv_kernel<int8, SwiGLU> (body gate/up)",
                "avg_us": round(us, 3), "bytes_per_launch": kbytes, "GB_s": round(k_gbs, 1),
                "frac": round(k_gbs / HBM_PEAK_GBS, 4),
