@@ -66,7 +66,7 @@ class FrameLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("x", "h", "qkv", "mlp", "logits", "u", "hd", "dqkv",
                                                "dmlp", "dlogits", "ring", "frame", "part_sem", "part_dep",
                                                "flags", "err", "seq", "phases", "th", "tqkv", "tmlp", "tu",
-                                               "thd", "tdqkv", "tdmlp", "th2", "thd2", "rope", "aq", "ao", "kcache",
+                                               "thd", "tdqkv", "tdmlp", "th2", "thd2", "ho", "hdo", "rope", "aq", "ao", "dao", "kcache",
                                                "vcache", "dkcache", "dvcache", "attn_ws", "total")]
 
 

@@ -196,16 +196,24 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
     off += align256(bytes);
     return o;
   };
+  // Per-stage slots: every GEMV output of every body layer and of every
+  // depth layer of every codebook step has a slot of its own (nothing is
+  // overwritten within a frame), plus per depth step its input and each
+  // head's logits.
+  const size_t nL = (size_t)c.n_layers;
+  const size_t nS = (size_t)(d.ncb - 1);               // depth steps
+  const size_t nDL = nS * c.d_layers;                  // depth layers run per frame
+  const size_t nHD = nS * (c.d_layers + 1);            // depth residual slots
   L.x = take((size_t)B * d.H * 2);
-  L.h = take((size_t)B * d.H * 2);
-  L.qkv = take((size_t)B * d.nqkv * 2);
-  L.mlp = take((size_t)B * d.F * 2);
+  L.h = take(nL * B * d.H * 2);
+  L.qkv = take(nL * B * d.nqkv * 2);
+  L.mlp = take(nL * B * d.F * 2);
   L.logits = take((size_t)B * d.V0 * 4);
   L.u = take((size_t)B * d.D * 2);
-  L.hd = take((size_t)B * d.D * 2);
-  L.dqkv = take((size_t)B * d.dqkv * 2);
-  L.dmlp = take((size_t)B * d.Fd * 2);
-  L.dlogits = take((size_t)B * d.CV * 4);
+  L.hd = take(nHD * B * d.D * 2);
+  L.dqkv = take(nDL * B * d.dqkv * 2);
+  L.dmlp = take(nDL * B * d.Fd * 2);
+  L.dlogits = take(nS * B * d.CV * 4);
   L.ring = take((size_t)16 * B * 8 * 4);
   L.frame = take(4);
   L.part_sem = take((size_t)B * n_blocks(d.V0) * sizeof(Best));
@@ -214,20 +222,23 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.err = take(4);
   L.seq = take(4);
   L.phases = take((size_t)frame_phases(c) * persist_phase_bytes());
-  L.th = take((size_t)B * d.H * 4);
-  L.tqkv = take((size_t)B * d.nqkv * 4);
-  L.tmlp = take((size_t)B * d.F * 4);
+  L.th = take(nL * B * d.H * 4);
+  L.tqkv = take(nL * B * d.nqkv * 4);
+  L.tmlp = take(nL * B * d.F * 4);
   L.tu = take((size_t)B * d.D * 4);
-  L.thd = take((size_t)B * d.D * 4);
-  L.tdqkv = take((size_t)B * d.dqkv * 4);
-  L.tdmlp = take((size_t)B * d.Fd * 4);
-  L.th2 = take((size_t)B * d.H * 4);
-  L.thd2 = take((size_t)B * d.D * 4);
+  L.thd = take(nHD * B * d.D * 4);
+  L.tdqkv = take(nDL * B * d.dqkv * 4);
+  L.tdmlp = take(nDL * B * d.Fd * 4);
+  L.th2 = take(nL * B * d.H * 4);
+  L.thd2 = take(nDL * B * d.D * 4);
+  L.ho = take(nL * B * d.H * 2);
+  L.hdo = take(nDL * B * d.D * 2);
   const bool at = c.attention != 0;
   const int rope_pos = at ? std::max(c.max_pos, 8) : 0;
   L.rope = take((size_t)rope_pos * 64 * 2 * 4);
   L.aq = take(at ? (size_t)B * std::max(d.nq, d.dq) * 2 : 0);
-  L.ao = take(at ? (size_t)B * std::max(d.nq, d.dq) * 2 : 0);
+  L.ao = take(at ? nL * B * d.nq * 2 : 0);
+  L.dao = take(at ? nDL * B * d.dq * 2 : 0);
   const size_t kv = at ? (size_t)c.n_layers * B * c.n_kv_heads * c.max_pos * 128 * 2 : 0;
   L.kcache = take(kv);
   L.vcache = take(kv);
@@ -349,26 +360,37 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   const m3_config& c = m->cfg;
   const Dims d = dims_of(c);
   const m3_frame_layout L = layout_of(c, B);
-  auto buf = [&](size_t plain, size_t tag) {
-    return reinterpret_cast<uint16_t*>(S + (tagged ? tag : plain));
+  // Every stream has one slot per layer (body) or per depth step and layer
+  // (depth decoder): plain bf16 in the eager/graph frames, tagged 32-bit
+  // words in a persistent launch.  Nothing is written twice within a frame,
+  // so no consumer can see a buffer overwritten under it.
+  const size_t esz = tagged ? 4 : 2;
+  auto slot = [&](size_t plain, size_t tag, size_t i, size_t cols) {
+    return reinterpret_cast<uint16_t*>(S + (tagged ? tag : plain) + i * B * cols * esz);
   };
   uint16_t* x = reinterpret_cast<uint16_t*>(S + L.x);
-  uint16_t* h_plain = reinterpret_cast<uint16_t*>(S + L.h);
-  uint16_t* h = buf(L.h, L.th);
-  uint16_t* qkv = buf(L.qkv, L.tqkv);
-  uint16_t* mlp = buf(L.mlp, L.tmlp);
+  // body layer l: QKV output, the stream after O (h_o), SwiGLU output, the
+  // stream after down (h); the body output is the last layer's h
+  auto h_slot = [&](int l) { return slot(L.h, L.th, l, d.H); };
+  auto qkv_slot = [&](int l) { return slot(L.qkv, L.tqkv, l, d.nqkv); };
+  auto ho_slot = [&](int l) { return slot(L.ho, L.th2, l, d.H); };
+  auto mlp_slot = [&](int l) { return slot(L.mlp, L.tmlp, l, d.F); };
+  uint16_t* h_out = h_slot(c.n_layers - 1);
+  uint16_t* h_plain_out = reinterpret_cast<uint16_t*>(S + L.h + (size_t)(c.n_layers - 1) * B * d.H * 2);
   float* logits = reinterpret_cast<float*>(S + L.logits);
-  uint16_t* u = buf(L.u, L.tu);
-  uint16_t* hd = buf(L.hd, L.thd);
-  // O's output: in place in the eager/graph frames (a kernel boundary
-  // separates every step); in a persistent launch a second stream, since a
-  // workgroup may still be staging QKV's input (the residual stream) when
-  // another has its V rows and writes O's rows; down writes the stream back
-  uint16_t* h_o = tagged ? reinterpret_cast<uint16_t*>(S + L.th2) : h;
-  uint16_t* hd_o = tagged ? reinterpret_cast<uint16_t*>(S + L.thd2) : hd;
-  uint16_t* dqkv = buf(L.dqkv, L.tdqkv);
-  uint16_t* dmlp = buf(L.dmlp, L.tdmlp);
-  float* dlogits = reinterpret_cast<float*>(S + L.dlogits);
+  uint16_t* u = slot(L.u, L.tu, 0, d.D);
+  // depth step j (1-based): residual slot s (0 = the step input, l + 1 =
+  // after depth layer l) and the per-layer streams of layer l
+  auto hd_slot = [&](int j, int s) {
+    return slot(L.hd, L.thd, (size_t)(j - 1) * (c.d_layers + 1) + s, d.D);
+  };
+  auto dl_index = [&](int j, int l) { return (size_t)(j - 1) * c.d_layers + l; };
+  auto dqkv_slot = [&](int j, int l) { return slot(L.dqkv, L.tdqkv, dl_index(j, l), d.dqkv); };
+  auto hdo_slot = [&](int j, int l) { return slot(L.hdo, L.thd2, dl_index(j, l), d.D); };
+  auto dmlp_slot = [&](int j, int l) { return slot(L.dmlp, L.tdmlp, dl_index(j, l), d.Fd); };
+  auto dlogits_of = [&](int j) {
+    return reinterpret_cast<float*>(S + L.dlogits) + (size_t)(j - 1) * B * d.CV;
+  };
   int32_t* ring = reinterpret_cast<int32_t*>(S + L.ring);
   uint32_t* frame = reinterpret_cast<uint32_t*>(S + L.frame);
   Best* part_sem = reinterpret_cast<Best*>(S + L.part_sem);
@@ -378,6 +400,8 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   // none in this frame; the frame input is a plain buffer)
   int ph = 0;
   int p_h = -1, p_qkv = -1, p_mlp = -1, p_u = -1, p_hd = -1, p_dqkv = -1, p_dmlp = -1;
+  (void)p_mlp;
+  (void)p_dmlp;
   int p_sem = -1, p_dep = -1;
   struct Prod {
     int x = -1, res = -1, u = -1, part = -1;
@@ -412,11 +436,15 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   const bool attn = c.attention != 0;
   const float* rope = reinterpret_cast<const float*>(S + L.rope);
   uint16_t* aq = reinterpret_cast<uint16_t*>(S + L.aq);
-  uint16_t* ao = reinterpret_cast<uint16_t*>(S + L.ao);
   uint32_t* err = reinterpret_cast<uint32_t*>(S + L.err);
+  // attention outputs: one slot per body layer (ao) and per depth layer run (dao)
+  auto ao_slot = [&](int l) { return reinterpret_cast<uint16_t*>(S + L.ao + (size_t)l * B * d.nq * 2); };
+  auto dao_slot = [&](int j, int l) {
+    return reinterpret_cast<uint16_t*>(S + L.dao + dl_index(j, l) * B * d.dq * 2);
+  };
   auto attention = [&](const uint16_t* qkv_in, int ldq_in, int n_q, int n_kv,
                        const m3_layer_weights& W, uint16_t* kc, uint16_t* vc, int max_pos,
-                       int pos, bool from_frame) {
+                       int pos, bool from_frame, uint16_t* ao) {
     AttnStep a{qkv_in, ldq_in, n_q, n_kv, W.q_norm, W.k_norm, eps, rope, pos, aq, kc, vc, ao,
                max_pos, from_frame ? frame : nullptr, from_frame ? c.pos0 : 0, err,
                S + L.attn_ws};
@@ -427,7 +455,12 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   const int group = c.n_heads / c.n_kv_heads;
   for (int l = 0; l < c.n_layers; ++l) {
     const m3_layer_weights& W = m->layers[l];
-    const uint16_t* xin = l == 0 ? x : h;
+    const uint16_t* xin = l == 0 ? x : h_slot(l - 1);
+    uint16_t* h = h_slot(l);
+    uint16_t* qkv = qkv_slot(l);
+    uint16_t* h_o = ho_slot(l);
+    uint16_t* mlp = mlp_slot(l);
+    uint16_t* ao = attn ? ao_slot(l) : nullptr;
     const int p_xin = l == 0 ? -1 : p_h;
     Prod a;
     a.x = p_xin;
@@ -444,7 +477,8 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
       const size_t lay = (size_t)B * c.n_kv_heads * c.max_pos * 128 * 2;
       M3_TRY(attention(qkv, d.nqkv, c.n_heads, c.n_kv_heads, W,
                        reinterpret_cast<uint16_t*>(S + L.kcache + l * lay),
-                       reinterpret_cast<uint16_t*>(S + L.vcache + l * lay), c.max_pos, 0, true));
+                       reinterpret_cast<uint16_t*>(S + L.vcache + l * lay), c.max_pos, 0, true,
+                       ao));
       p_ho = ph;
       M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, ao, d.nq, nullptr, 0, 0, h_o, d.H, 0,
                   M3_EPI_RESIDUAL, xin, d.H, o));
@@ -495,16 +529,17 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   Prod lm;
   lm.x = p_h;
   p_sem = ph;
-  M3_TRY(gemv(c.fmt_lm, m->lm_head, d.V0, d.H, h, d.H, m->final_norm, 0, 0, logits, d.V0, 1,
+  M3_TRY(gemv(c.fmt_lm, m->lm_head, d.V0, d.H, h_out, d.H, m->final_norm, 0, 0, logits, d.V0, 1,
               M3_EPI_NONE, nullptr, 0, lm, guided ? nullptr : &sem));
   if (guided) M3_TRY(guided_draw(logits, d.V0, 0u, c.vocab_base, part_sem));
   // ---- depth decoder ----
   Prod pin;
   pin.x = p_h;
   p_u = ph;
-  M3_TRY(gemv(c.fmt_depth, m->p_in, d.D, d.H, h, d.H, m->final_norm, 0, 0, u, d.D, 0,
+  M3_TRY(gemv(c.fmt_depth, m->p_in, d.D, d.H, h_out, d.H, m->final_norm, 0, 0, u, d.D, 0,
               M3_EPI_NONE, nullptr, 0, pin));
   for (int j = 1; j < d.ncb; ++j) {
+    float* dlogits = dlogits_of(j);
     // step j's input: bf16(u + Emb_j[previous code]); the previous draw is
     // finished from its row-block winners in the prologue of the first GEMV
     GatherPro gp;
@@ -517,10 +552,16 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     gp.n_codes = j == 1 ? c.n_slice : c.code_vocab;
     gp.codes = codes;
     gp.code_col = j - 1;
-    gp.out = hd;
+    gp.out = hd_slot(j, 0);
     const int p_prev_draw = j == 1 ? p_sem : p_dep;
     for (int l = 0; l < c.d_layers; ++l) {
       const m3_layer_weights& W = m->d_layers_w[l];
+      uint16_t* hd = hd_slot(j, l);          // this layer's input
+      uint16_t* hd_next = hd_slot(j, l + 1);  // and its output
+      uint16_t* dqkv = dqkv_slot(j, l);
+      uint16_t* hd_o = hdo_slot(j, l);
+      uint16_t* dmlp = dmlp_slot(j, l);
+      uint16_t* ao = attn ? dao_slot(j, l) : nullptr;
       Prod q;
       if (l == 0) {
         q.u = p_u;
@@ -543,7 +584,8 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
         const size_t lay = (size_t)B * c.d_heads * 8 * 128 * 2;
         M3_TRY(attention(dqkv, d.dqkv, c.d_heads, c.d_heads, W,
                          reinterpret_cast<uint16_t*>(S + L.dkcache + l * lay),
-                         reinterpret_cast<uint16_t*>(S + L.dvcache + l * lay), 8, j - 1, false));
+                         reinterpret_cast<uint16_t*>(S + L.dvcache + l * lay), 8, j - 1, false,
+                         ao));
         p_hdo = ph;
         M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, ao, d.dq, nullptr, 0, 0, hd_o, d.D, 0,
                     M3_EPI_RESIDUAL, hd, d.D, o));
@@ -563,9 +605,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
       dn.x = p_dmlp;
       dn.res = p_hdo;
       p_hd = ph;
-      M3_TRY(gemv(c.fmt_depth, W.down, d.D, d.Fd, dmlp, d.Fd, nullptr, 0, 0, hd, d.D, 0,
+      M3_TRY(gemv(c.fmt_depth, W.down, d.D, d.Fd, dmlp, d.Fd, nullptr, 0, 0, hd_next, d.D, 0,
                   M3_EPI_RESIDUAL, hd_o, d.D, dn));
     }
+    uint16_t* hd = hd_slot(j, c.d_layers);    // the step's output
     SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep};
     Prod hp;
     hp.x = p_hd;
@@ -578,9 +621,9 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   FeedbackTags ft;
   if (tagged) {
     ft.last_part_prod = p_dep;
-    ft.th = h;
+    ft.th = h_out;
     ft.th_prod = p_h;
-    ft.h_out = h_plain;
+    ft.h_out = h_plain_out;
     ft.seq = reinterpret_cast<uint32_t*>(S + L.seq);
   }
   M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, guided ? 1 : n_blocks(d.CV),
@@ -1061,7 +1104,7 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   if (st == M3_OK && PL) {
     const hipError_t e = persist_upload(pl, S + L.phases, reinterpret_cast<uint32_t*>(S + L.flags),
                                         reinterpret_cast<uint32_t*>(S + L.err),
-                                        reinterpret_cast<const uint32_t*>(S + L.seq),
+                                        reinterpret_cast<uint32_t*>(S + L.seq),
                                         static_cast<hipStream_t>(stream), PL);
     if (e != hipSuccess) st = M3_ERR_HIP;
   } else if (st == M3_OK) {

@@ -90,6 +90,77 @@ __device__ __forceinline__ uint32_t f2bf_pair(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm rounding.  The normed operand a = bf16(x * r * gamma) is a rounding
+// decision: where x r gamma lies within a few fp32 ulps of a tie between two
+// bf16 values, an fp32 evaluation (r from an fp32 sum, two fp32 products)
+// rounds it to either side, and one operand element one ulp apart shifts every
+// output of its row by W[n, k] ulp(a_k), enough to change the rounding of a
+// few percent of them.  So r comes from a float64 sum of squares (each square
+// of a bf16 is exact in float64), and x r gamma is evaluated in fp32 first and
+// again in float64 wherever the fp32 value is within kTieWin fp32 ulps of a
+// tie; the fp32 value is within 3 ulps of the float64 one (three roundings),
+// so everywhere else both round to the same bf16.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kTieWin = 8;
+
+// |fp32 bits - nearest bf16 tie| <= kTieWin ulps (ties sit at low half 0x8000)
+__device__ __forceinline__ bool near_tie(float v) {
+  return ((__float_as_uint(v) & 0xFFFFu) - (0x8000u - kTieWin)) <= 2u * kTieWin;
+}
+
+// float64 -> fp32 rounded to odd: nearest, then, if inexact, toward zero with
+// the last bit set.  A second rounding of that to bf16 (8 of its 24 bits) to
+// nearest even gives the float64 value's own nearest-even bf16.
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+  float f = (float)d;
+  if ((double)f != d && d == d) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs((double)f) > fabs(d)) u -= 1u;
+    f = __uint_as_float(u | 1u);
+  }
+  return f;
+}
+
+// one bf16 pair (x in the low and high halves of w) normalised with the row's
+// r (fp32, and float64 read from *r64 only near a tie) and gammas g0, g1
+__device__ __forceinline__ uint32_t norm_pair(uint32_t w, float r32, const double* r64, float g0,
+                                              float g1) {
+  const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+  const float a0 = (x0 * r32) * g0, a1 = (x1 * r32) * g1;
+  if (__builtin_expect(near_tie(a0) || near_tie(a1), 0)) {
+    const double r = *r64;
+    return f2bf_pair(f64_to_f32_odd(((double)x0 * r) * (double)g0),
+                     f64_to_f32_odd(((double)x1 * r) * (double)g1));
+  }
+  return f2bf_pair(a0, a1);
+}
+
+// one value normalised with r (fp32; float64 near a tie) and gamma g
+__device__ __forceinline__ uint32_t norm_one(float x, float r32, double r64, float g) {
+  const float a = (x * r32) * g;
+  if (__builtin_expect(near_tie(a), 0)) return f2bf(f64_to_f32_odd(((double)x * r64) * (double)g));
+  return f2bf(a);
+}
+
+// sum of squares of a bf16 pair, added in float64 (each square is exact)
+__device__ __forceinline__ double sumsq_pair(uint32_t w, double ss) {
+  const double x0 = (double)__uint_as_float(w << 16), x1 = (double)__uint_as_float(w & 0xffff0000u);
+  return fma(x1, x1, fma(x0, x0, ss));
+}
+
+// sum over the wave; lane 0 holds the result (every lane of the wave active)
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// r = 1 / sqrt(ss / K + eps) in float64
+__device__ __forceinline__ double norm_r(double ss, int K, float eps) {
+  return 1.0 / sqrt(ss / (double)K + (double)eps);
+}
+
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
                                          __builtin_bit_cast(bf16x2_t, a), acc, false);
@@ -506,6 +577,21 @@ struct OperandSource {
   }
 };
 
+// The norm's per-row values in the LDS scratch ss_buf (floats): r as fp32 at
+// [0, M3_MAX_B), r as float64 at float offset 2 M3_MAX_B, and the few-row
+// path's per-wave partial sums (float64) after those.
+struct NormLds {
+  float* r32;
+  double* r64;
+  double* part;
+  __device__ explicit NormLds(float* ss_buf)
+      : r32(ss_buf), r64(reinterpret_cast<double*>(ss_buf + 2 * M3_MAX_B)), part(r64 + M3_MAX_B) {}
+  __device__ void set(int b, double r) {
+    r64[b] = r;
+    r32[b] = (float)r;
+  }
+};
+
 template <bool COH>
 __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, float* ss_buf,
                                                const int* code_lds, int wg, const XPre& pre,
@@ -514,17 +600,18 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
   const int stride = p.lds_stride;
   const int nchunk = (stride - 8) >> 3;
   const OperandSource<COH> src{p, tg, code_lds};
-  auto put = [&](int b, int k, const uint4& v, float& ss) {
+  NormLds nl(ss_buf);
+  auto put = [&](int b, int k, const uint4& v, double& ss) {
     *reinterpret_cast<uint4*>(act + (size_t)b * stride + k) = v;
     if (p.has_gather && wg == 0 && k < p.K) act_store8<COH>(p.gat.out, (size_t)b * p.K + k, v, tg.y);
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ss = dot2(wv[j], wv[j], ss);
+    for (int j = 0; j < 4; ++j) ss = sumsq_pair(wv[j], ss);
   };
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (b >= p.lds_rows) break;
-    float ss = 0.f;
+    double ss = 0.0;
     if constexpr (!COH) {
       if (pre.valid) {
 #pragma unroll
@@ -562,15 +649,15 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
       for (int i = kPreRounds * kThreads + tid; i < nchunk; i += kThreads)
         put(b, i << 3, src.settle(b, i << 3), ss);
     }
-    ss = wave_sum(ss);
-    if (lane == 0) ss_buf[M3_MAX_B + b * kWaves + wave] = ss;
+    ss = wave_sum_f64(ss);
+    if (lane == 0) nl.part[b * kWaves + wave] = ss;
   }
   __syncthreads();
   if (p.gamma && tid < p.lds_rows) {
-    float tot = 0.f;
+    double tot = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += ss_buf[M3_MAX_B + tid * kWaves + w];
-    ss_buf[tid] = 1.0f / sqrtf(tot / (float)p.K + p.eps);
+    for (int w = 0; w < kWaves; ++w) tot += nl.part[tid * kWaves + w];
+    nl.set(tid, norm_r(tot, p.K, p.eps));
   }
 }
 
@@ -663,13 +750,13 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
   }
   __syncthreads();
   if (!p.gamma) return;
-  // pass 2: r_b from the sum of squares of row b: lane l sums chunks
-  // l + 64 m into accumulator m % 4 (four independent chains whose LDS reads
-  // are in flight together; v_dot2 squares and adds a bf16 pair in one
-  // instruction), then (s0 + s1) + (s2 + s3), then across the wave
+  // pass 2: r_b from the sum of squares of row b (float64): lane l sums
+  // chunks l + 64 m into accumulator m % 4 (four independent chains whose LDS
+  // reads are in flight together), then (s0 + s1) + (s2 + s3), then across
+  // the wave
   for (int b = wave; b < p.lds_rows; b += kWaves) {
     const int kc = p.K >> 3;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
     for (int c0 = lane; c0 < kc; c0 += 256) {
       uint4 v[4];
 #pragma unroll
@@ -682,16 +769,18 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
       for (int m = 0; m < 4; ++m) {
         const uint32_t wv[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m] = dot2(wv[j], wv[j], acc[m]);
+        for (int j = 0; j < 4; ++j) acc[m] = sumsq_pair(wv[j], acc[m]);
       }
     }
-    float ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    ss = wave_sum(ss);
-    if (lane == 0) ss_buf[b] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+    double ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    ss = wave_sum_f64(ss);
+    if (lane == 0) NormLds(ss_buf).set(b, norm_r(ss, p.K, p.eps));
   }
   }
   __syncthreads();
-  // pass 3: a = bf16(x * r_b * gamma); gamma is loaded once per chunk
+  // pass 3: a = bf16(x * r_b * gamma) (see norm_pair); gamma is loaded once
+  // per chunk
+  const NormLds nl(ss_buf);
   const int kc = p.K >> 3;
   for (int i = tid; i < kc; i += kThreads) {
     const int k = i * 8;
@@ -706,17 +795,14 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
       for (int e = 0; e < 4; ++e) {
         const int b = b0 + e < p.lds_rows ? b0 + e : b0;
         v[e] = *reinterpret_cast<const uint4*>(act + (size_t)b * stride + k);
-        r[e] = ss_buf[b];
+        r[e] = nl.r32[b];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         uint32_t wv[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+        const int b = b0 + e < p.lds_rows ? b0 + e : b0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a0 = (bf2f(wv[j] & 0xffffu) * r[e]) * g[2 * j];
-          const float a1 = (bf2f(wv[j] >> 16) * r[e]) * g[2 * j + 1];
-          wv[j] = f2bf_pair(a0, a1);
-        }
+        for (int j = 0; j < 4; ++j) wv[j] = norm_pair(wv[j], r[e], nl.r64 + b, g[2 * j], g[2 * j + 1]);
         if (b0 + e < p.lds_rows)
           *reinterpret_cast<uint4*>(act + (size_t)(b0 + e) * stride + k) =
               make_uint4(wv[0], wv[1], wv[2], wv[3]);

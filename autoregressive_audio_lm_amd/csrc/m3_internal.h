@@ -215,9 +215,10 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
                                 const FeedbackTags& ft);
 PersistLaunch* persist_launch_new();
 void persist_launch_free(PersistLaunch* L);
-// copy the table into device memory, reset flags and the error word (synchronises `s`)
+// copy the table into device memory, start a new epoch (launch counter + 1),
+// set the flags to its start and clear the error word (synchronises `s`)
 hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
-                          const uint32_t* seq, hipStream_t s, PersistLaunch* out);
+                          uint32_t* seq, hipStream_t s, PersistLaunch* out);
 hipError_t persist_launch(const PersistLaunch& L, hipStream_t s);
 // the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip) by row-count class
 const void* persist_kernel_bf16(int NB);

@@ -29,10 +29,20 @@ namespace {
 
 constexpr int kMaxPhases = (int)kPhaseStride - 1;
 
-__global__ void flags_init_kernel(uint32_t* flags, int n, const uint32_t* seq, uint32_t* err) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) flags[i] = *seq * kPhaseStride;
-  if (i == 0) *err = 0u;
+// A fresh epoch for every recorded phase table: the launch counter advances
+// before the flags are set to "phase -1 of it done" and the error word is
+// cleared.  Words a launch that gave up left in the tagged streams carry the
+// old epoch's tags, which no launch of the new epoch waits for.  (One
+// workgroup: every thread reads the counter before thread 0 writes it.)
+__global__ void flags_init_kernel(uint32_t* flags, int n, uint32_t* seq, uint32_t* err) {
+  const int i = threadIdx.x;
+  const uint32_t epoch = *seq + 1u;
+  __syncthreads();
+  for (int w = i; w < n; w += blockDim.x) flags[w] = epoch * kPhaseStride;
+  if (i == 0) {
+    *seq = epoch;
+    *err = 0u;
+  }
 }
 
 }  // namespace
@@ -138,7 +148,7 @@ struct PersistLaunch {
 // Copy the table to `table` (device, persist_phase_bytes() * size), set the
 // flags to "phase -1 of the current frame done", clear the error word.
 hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
-                          const uint32_t* seq, hipStream_t s, PersistLaunch* out) {
+                          uint32_t* seq, hipStream_t s, PersistLaunch* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;

@@ -90,6 +90,9 @@ __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int np
   __shared__ int s_ok;
   __shared__ int c_last[M3_MAX_B_FRAME];
   const int wg = blockIdx.x, nwg = gridDim.x;
+  // a launch on a state whose error word is raised computes nothing: the
+  // state must be recorded again (persistent_create) first
+  if (__builtin_amdgcn_readfirstlane(ld4<true>(err, 0)) != 0u) return;
   // epochs of this launch: launch counter * 512 + phase + 1
   const uint32_t ebase = __builtin_amdgcn_readfirstlane(ld4<true>(seq, 0)) * kPhaseStride;
   for (int i = 0; i < nph; ++i) {

@@ -308,24 +308,28 @@ constexpr int kNThreads = 256;
 __global__ __launch_bounds__(kNThreads) void rmsnorm_rows_kernel(const uint16_t* x, int ldx,
                                                                  const float* gamma, float eps,
                                                                  int K, uint16_t* a, int lda) {
-  __shared__ float part[kNThreads / 64];
+  // the decode GEMV prologue's arithmetic (gemv_impl.h, "RMSNorm rounding"):
+  // float64 sum of squares and r, fp32 products re-taken in float64 near a tie
+  __shared__ double part[kNThreads / 64];
+  __shared__ double r64;
   const int row = blockIdx.x, tid = threadIdx.x;
   const uint16_t* xr = x + (size_t)row * ldx;
   uint16_t* ar = a + (size_t)row * lda;
   const int kc = K >> 3;
-  float ss = 0.f;
+  double ss = 0.0;
   for (int c = tid; c < kc; c += kNThreads) {
     const uint4 v = *reinterpret_cast<const uint4*>(xr + c * 8);
-    ss = dot2(v.x, v.x, ss);
-    ss = dot2(v.y, v.y, ss);
-    ss = dot2(v.z, v.z, ss);
-    ss = dot2(v.w, v.w, ss);
+    ss = sumsq_pair(v.x, ss);
+    ss = sumsq_pair(v.y, ss);
+    ss = sumsq_pair(v.z, ss);
+    ss = sumsq_pair(v.w, ss);
   }
-  ss = wave_sum(ss);
+  ss = wave_sum_f64(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float r = 1.0f / sqrtf(tot / (float)K + eps);
+  if (tid == 0) r64 = norm_r((part[0] + part[1]) + (part[2] + part[3]), K, eps);
+  __syncthreads();
+  const float r = (float)r64;
   for (int c = tid; c < kc; c += kNThreads) {
     const uint4 v = *reinterpret_cast<const uint4*>(xr + c * 8);
     const float4 g0 = *reinterpret_cast<const float4*>(gamma + c * 8);
@@ -335,9 +339,7 @@ __global__ __launch_bounds__(kNThreads) void rmsnorm_rows_kernel(const uint16_t*
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float a0 = (bf2f(wv[j] & 0xffffu) * r) * g[2 * j];
-      const float a1 = (bf2f(wv[j] >> 16) * r) * g[2 * j + 1];
-      o[j] = f2bf_pair(a0, a1);
+      o[j] = norm_pair(wv[j], r, &r64, g[2 * j], g[2 * j + 1]);
     }
     *reinterpret_cast<uint4*>(ar + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }

@@ -164,7 +164,60 @@ class FrameState:
 
     @property
     def h(self):
-        return self.view("h", torch.bfloat16, self.dm.config.hidden)
+        """The body output: the residual stream after the last body layer."""
+        return self.h_layers()[-1]
+
+    def _slots(self, name: str, dtype: torch.dtype, shape: tuple) -> torch.Tensor:
+        off = getattr(self.layout, name)
+        n = 1
+        for s in shape:
+            n *= s
+        esz = torch.tensor([], dtype=dtype).element_size()
+        return self.state[off:off + n * esz].view(dtype).view(*shape)
+
+    # per-stage slots of the state (m3_frame_layout): name -> (tagged name, shape)
+    def _slot_shapes(self) -> dict:
+        c, B = self.dm.config, self.B
+        L, S, DL = c.n_layers, c.n_codebooks - 1, c.d_layers
+        nq = c.n_heads * c.head_dim
+        nqkv = nq + 2 * c.n_kv_heads * c.head_dim
+        dq = c.d_heads * c.d_head_dim
+        return {"h": ("th", (L, B, c.hidden)), "qkv": ("tqkv", (L, B, nqkv)),
+                "ho": ("th2", (L, B, c.hidden)), "mlp": ("tmlp", (L, B, c.ffn)),
+                "ao": (None, (L, B, nq)), "u": ("tu", (B, c.d_hidden)),
+                "hd": ("thd", (S, DL + 1, B, c.d_hidden)), "dqkv": ("tdqkv", (S, DL, B, 3 * dq)),
+                "hdo": ("thd2", (S, DL, B, c.d_hidden)), "dmlp": ("tdmlp", (S, DL, B, c.d_ffn)),
+                "dao": (None, (S, DL, B, dq))}
+
+    def slots(self, name: str, tagged: bool = False) -> torch.Tensor:
+        """A per-stage stream of the last frame: body [n_layers, B, cols] for
+        h (after each layer), qkv, ho (after O + residual), mlp (SwiGLU) and ao
+        (attention output); u [B, d_hidden]; depth [steps, d_layers + 1, B, D]
+        for hd (slot 0 the step input, slot l + 1 after depth layer l) and
+        [steps, d_layers, B, cols] for dqkv, hdo, dmlp, dao.  bf16 after an
+        eager or graph frame; tagged=True: the persistent frame's 32-bit words
+        (bf16 value in the low 16 bits)."""
+        tname, shape = self._slot_shapes()[name]
+        if tagged:
+            if tname is None:
+                raise ValueError(f"{name} has no tagged form")
+            return self._slots(tname, torch.int32, shape)
+        return self._slots(name, torch.bfloat16, shape)
+
+    def h_layers(self, tagged: bool = False) -> torch.Tensor:
+        """[n_layers, B, hidden]: the residual stream after each body layer."""
+        return self.slots("h", tagged)
+
+    def depth_slots(self, tagged: bool = False) -> torch.Tensor:
+        """[n_codebooks-1, d_layers+1, B, d_hidden]: each depth step's input
+        and the residual stream after each of its layers."""
+        return self.slots("hd", tagged)
+
+    @property
+    def dlogits(self) -> torch.Tensor:
+        """[n_codebooks-1, B, code_vocab] fp32: each depth step's head logits."""
+        c = self.dm.config
+        return self._slots("dlogits", torch.float32, (c.n_codebooks - 1, self.B, c.code_vocab))
 
     @property
     def logits(self):

@@ -396,37 +396,50 @@ typedef struct {
   const uint16_t* const* audio_emb;   /* host array [n_codebooks-1] of [code_vocab, hidden] */
 } m3_model;
 
-/* Device buffers inside the frame state (byte offsets from its base). */
+/* Device buffers inside the frame state (byte offsets from its base).
+ * Every GEMV output of every body layer, and of every depth-decoder layer of
+ * every codebook step, has a slot of its own, as do each depth step's input
+ * and each depth head's logits: nothing is written twice within a frame, and
+ * each operation of a frame can be checked on its own from the input it was
+ * given (TensorFold PR #987, summary: parity at every stage, teacher-forced).
+ * Slots are plain bf16 after an eager or graph frame; a persistent frame
+ * writes the tagged buffers instead (and a plain copy of the body output).
+ * Shapes: L = n_layers, S = n_codebooks - 1 depth steps, DL = d_layers. */
 typedef struct {
   size_t x;        /* bf16 [B, hidden]   frame input; overwritten by x_next    */
-  size_t h;        /* bf16 [B, hidden]   body residual stream                  */
-  size_t qkv;      /* bf16 [B, nq+2nkv]                                        */
-  size_t mlp;      /* bf16 [B, ffn]                                            */
+  size_t h;        /* bf16 [L][B, hidden] residual stream after each body layer;
+                      the last slot is the body output                         */
+  size_t qkv;      /* bf16 [L][B, nq+2nkv] each layer's QKV output              */
+  size_t mlp;      /* bf16 [L][B, ffn]   each layer's SwiGLU output            */
   size_t logits;   /* f32  [B, n_slice]  semantic logits of the last frame     */
   size_t u;        /* bf16 [B, d_hidden] depth-decoder input projection        */
-  size_t hd;       /* bf16 [B, d_hidden] depth residual stream                 */
-  size_t dqkv;     /* bf16 [B, 3 d_hidden]                                     */
-  size_t dmlp;     /* bf16 [B, d_ffn]                                          */
-  size_t dlogits;  /* f32  [B, code_vocab] logits of the last depth draw       */
+  size_t hd;       /* bf16 [S][DL+1][B, d_hidden]: for step j (codebook j = 1..7,
+                      slot j-1) its input bf16(u + Emb_j[c]) in slot 0 and the
+                      residual stream after depth layer l in slot l+1          */
+  size_t dqkv;     /* bf16 [S][DL][B, 3 d_hidden]                              */
+  size_t dmlp;     /* bf16 [S][DL][B, d_ffn]                                   */
+  size_t dlogits;  /* f32  [S][B, code_vocab] each step's head logits          */
   size_t ring;     /* i32  [16, B, 8]    codes of the last 16 frames           */
   size_t frame;    /* u32  frame counter (advanced on the GPU)                 */
   size_t part_sem; /* per-row-block winners of the semantic draw               */
   size_t part_dep; /* per-row-block winners of the latest depth draw           */
   size_t flags;    /* u32  [256] per-workgroup progress of the persistent frame */
   size_t err;      /* u32  nonzero: a persistent frame gave up waiting          */
-  size_t seq;      /* u32  persistent launches so far                          */
+  size_t seq;      /* u32  the persistent frame's epoch (launch counter)       */
   size_t phases;   /* the persistent frame's phase table                       */
   size_t th, tqkv, tmlp, tu, thd, tdqkv, tdmlp;
                    /* u32 words (bf16 value | 16-bit producer tag): the
-                      persistent frame's intermediate streams; h, qkv, mlp, u,
-                      hd, dqkv, dmlp above belong to the eager/graph frames   */
-  size_t th2, thd2; /* u32 words [B, hidden], [B, d_hidden]: the persistent
-                      frame's residual streams after O (O writes here, not in
-                      place, so that no workgroup still staging QKV's input
-                      can see a newer tag)                                     */
+                      persistent frame's streams, shaped as h, qkv, mlp, u,
+                      hd, dqkv, dmlp above                                     */
+  size_t th2, thd2; /* u32 words [L][B, hidden], [S][DL][B, d_hidden]: the
+                      persistent frame's streams after O, shaped as ho, hdo   */
+  size_t ho, hdo;  /* bf16 [L][B, hidden], [S][DL][B, d_hidden]: the residual
+                      stream after O (+ residual) of each layer                 */
   /* attention = 1 only (zero-sized otherwise): */
   size_t rope;     /* f32  [max(max_pos, 8), 64, 2] RoPE table                 */
-  size_t aq, ao;   /* bf16 [B, max(nq, d_hidden)] rotated q; attention output  */
+  size_t aq;       /* bf16 [B, max(nq, d_hidden)] rotated q (scratch)          */
+  size_t ao;       /* bf16 [L][B, nq]    each body layer's attention output    */
+  size_t dao;      /* bf16 [S][DL][B, d_hidden] each depth layer's attention output */
   size_t kcache, vcache;   /* bf16 [n_layers][B][n_kv][max_pos][128]          */
   size_t dkcache, dvcache; /* bf16 [d_layers][B][d_heads][8][128]             */
   size_t attn_ws;  /* m3_decode_attention's workspace at T = max_pos           */
@@ -479,7 +492,11 @@ int m3_frame_graph_destroy(void* graph);
  * `stream` once); launch enqueues one frame; the handle keeps the model's and
  * the state's device addresses.  Every wait inside the launch is bounded: if
  * one gives up (the launch could not make progress), the state's err word
- * becomes nonzero, the launch ends early and that frame's outputs are invalid.
+ * becomes nonzero, the launch ends early and that frame's outputs are invalid;
+ * while the word is nonzero, launches on the state return at once and compute
+ * nothing.  m3_frame_persistent_create clears it: each create starts a new
+ * epoch of the tags (below), so nothing a launch that gave up left behind is
+ * taken for an operand later.
  * Inside the launch the intermediate streams (body and depth residuals, QKV,
  * MLP, depth input) are the state's tagged buffers: 32-bit words holding the
  * bf16 value and the tag of the step that wrote it; a step waits for its

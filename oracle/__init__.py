@@ -146,6 +146,14 @@ def _declare(L):
                                    ctypes.c_uint32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(FrameTrace)]
     L.m3o_num_threads.restype = ctypes.c_int
+    L.m3o_layer_stub.argtypes = [ctypes.POINTER(Layer), _P, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_float]
+    L.m3o_layer_attn.argtypes = [ctypes.POINTER(Layer), _P, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_float, _P, _P, _P, ctypes.c_int, ctypes.c_int]
+    L.m3o_step_input.argtypes = [ctypes.POINTER(Model), ctypes.c_int, _P, _P, ctypes.c_int, _P]
+    L.m3o_feedback.argtypes = [ctypes.POINTER(Model), _P, ctypes.c_int, _P]
 
 
 def _ptr(a):
@@ -408,12 +416,17 @@ class OracleModel:
         (frame f at position pos0 + f); the caches are made zeroed for the
         batch size of the first frame (and again by reset_attention)."""
         self._keep = []
+        self.md = md
         cfg = md["cfg"]
         fb, fl, fd = md["fmt_body"], md["fmt_lm"], md["fmt_depth"]
 
-        def mat(W, fmt):
+        self.mats = {}
+
+        def mat(W, fmt, key=None):
             M = Matrix(W, fmt)
             self._keep.append(M)
+            if key is not None:
+                self.mats[key] = M
             return M.c()
 
         def keep(a, dt):
@@ -421,18 +434,21 @@ class OracleModel:
             self._keep.append(a)
             return a
 
-        def layer(Ld, fmt):
+        def layer(Ld, fmt, kind, i):
             gu = interleave_gate_up(Ld["gate"], Ld["up"])
             qn = _ptr(keep(Ld["q_norm"], np.float32)) if "q_norm" in Ld else None
             kn = _ptr(keep(Ld["k_norm"], np.float32)) if "k_norm" in Ld else None
-            return Layer(mat(Ld["qkv"], fmt), mat(Ld["o"], fmt), mat(gu, fmt),
-                         mat(Ld["down"], fmt), _ptr(keep(Ld["attn_norm"], np.float32)),
+            return Layer(mat(Ld["qkv"], fmt, (kind, i, "qkv")), mat(Ld["o"], fmt, (kind, i, "o")),
+                         mat(gu, fmt, (kind, i, "gu")), mat(Ld["down"], fmt, (kind, i, "down")),
+                         _ptr(keep(Ld["attn_norm"], np.float32)),
                          _ptr(keep(Ld["ffn_norm"], np.float32)), qn, kn)
 
         nl = len(md["layers"])
-        LA = (Layer * max(nl, 1))(*[layer(L, fb) for L in md["layers"]])
-        DL = (Layer * len(md["d_layers"]))(*[layer(L, fd) for L in md["d_layers"]])
-        heads = (Mat * len(md["heads"]))(*[mat(W, fd) for W in md["heads"]])
+        LA = (Layer * max(nl, 1))(*[layer(L, fb, "body", i) for i, L in enumerate(md["layers"])])
+        DL = (Layer * len(md["d_layers"]))(*[layer(L, fd, "depth", i)
+                                            for i, L in enumerate(md["d_layers"])])
+        heads = (Mat * len(md["heads"]))(*[mat(W, fd, ("head", j + 1))
+                                           for j, W in enumerate(md["heads"])])
         embs = [keep(e, np.uint16) for e in md["emb"]]
         emb_arr = (ctypes.c_void_p * max(len(embs), 1))(*[e.ctypes.data for e in embs])
         aembs = [keep(e, np.uint16) for e in md["audio_emb"]]
@@ -442,10 +458,10 @@ class OracleModel:
         self.m = Model(
             cfg["H"], nl, cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["F"],
             ctypes.cast(LA, ctypes.c_void_p), _ptr(keep(md["final_norm"], np.float32)),
-            mat(md["lm_head"], fl), cfg["vocab_base"], cfg["V0"],
+            mat(md["lm_head"], fl, ("lm_head", 0)), cfg["vocab_base"], cfg["V0"],
             cfg["D"], len(md["d_layers"]), cfg["d_heads"], cfg["d_head_dim"], cfg["Fd"],
             cfg["n_codebooks"], cfg["code_vocab"],
-            mat(md["p_in"], fd), _ptr(keep(md["emb1"], np.uint16)),
+            mat(md["p_in"], fd, ("p_in", 0)), _ptr(keep(md["emb1"], np.uint16)),
             ctypes.cast(emb_arr, ctypes.c_void_p), ctypes.cast(DL, ctypes.c_void_p),
             _ptr(keep(md["d_final_norm"], np.float32)), ctypes.cast(heads, ctypes.c_void_p),
             _ptr(keep(md["tok_emb_audio"], np.uint16)), ctypes.cast(aemb_arr, ctypes.c_void_p),
@@ -473,6 +489,79 @@ class OracleModel:
             setattr(self.m, name, ctypes.cast(arr, ctypes.c_void_p))
         self._cache_arrs = arrs
         self.cache_B = B
+
+
+def body_layer(om: OracleModel, l: int, h_in):
+    """Body layer l of the frame (identity attention stub) on h_in [B, H]
+    (bf16 bits): the residual stream after it, as the oracle frame computes it."""
+    cfg = om.cfg
+    h = _c(h_in, np.uint16).copy()
+    layers = ctypes.cast(om.m.layers, ctypes.POINTER(Layer))
+    lib().m3o_layer_stub(ctypes.byref(layers[l]), _ptr(h), h.shape[0], cfg["H"], cfg["n_heads"],
+                         cfg["n_kv_heads"], cfg["head_dim"], cfg["F"], float(cfg["eps"]))
+    return h
+
+
+def depth_layer(om: OracleModel, l: int, hd_in):
+    """Depth-decoder layer l (identity attention stub) on hd_in [B, D]."""
+    cfg = om.cfg
+    h = _c(hd_in, np.uint16).copy()
+    layers = ctypes.cast(om.m.d_layers_w, ctypes.POINTER(Layer))
+    lib().m3o_layer_stub(ctypes.byref(layers[l]), _ptr(h), h.shape[0], cfg["D"], cfg["d_heads"],
+                         cfg["d_heads"], cfg["d_head_dim"], cfg["Fd"], float(cfg["eps"]))
+    return h
+
+
+def body_layer_attn(om: OracleModel, l: int, h_in, k_cache, v_cache, pos: int):
+    """Body layer l with decode attention at position pos: k_cache, v_cache
+    ([B, n_kv, max_pos, 128] bf16 bits) get slot pos written in place; returns
+    the residual stream after the layer."""
+    cfg = om.cfg
+    h = _c(h_in, np.uint16).copy()
+    layers = ctypes.cast(om.m.layers, ctypes.POINTER(Layer))
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    lib().m3o_layer_attn(ctypes.byref(layers[l]), _ptr(h), h.shape[0], cfg["H"], cfg["n_heads"],
+                         cfg["n_kv_heads"], cfg["head_dim"], cfg["F"], float(cfg["eps"]),
+                         om.m.rope, _ptr(k_cache), _ptr(v_cache), k_cache.shape[2], int(pos))
+    return h
+
+
+def depth_layer_attn(om: OracleModel, l: int, hd_in, k_cache, v_cache, pos: int):
+    """Depth layer l with attention at codebook position pos over caches
+    [B, d_heads, 8, 128] (slot pos written in place)."""
+    cfg = om.cfg
+    h = _c(hd_in, np.uint16).copy()
+    layers = ctypes.cast(om.m.d_layers_w, ctypes.POINTER(Layer))
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    lib().m3o_layer_attn(ctypes.byref(layers[l]), _ptr(h), h.shape[0], cfg["D"], cfg["d_heads"],
+                         cfg["d_heads"], cfg["d_head_dim"], cfg["Fd"], float(cfg["eps"]),
+                         om.m.rope, _ptr(k_cache), _ptr(v_cache), k_cache.shape[2], int(pos))
+    return h
+
+
+def step_input(om: OracleModel, j: int, codes, u):
+    """Depth step j's input bf16(u + Emb_j[c_{j-1}]) from the frame's codes [B, 8]."""
+    codes = _c(codes, np.int32)
+    u = _c(u, np.uint16)
+    out = np.empty_like(u)
+    lib().m3o_step_input(ctypes.byref(om.m), int(j), _ptr(codes), _ptr(u), u.shape[0], _ptr(out))
+    return out
+
+
+def feedback(om: OracleModel, codes):
+    """The next frame's input bf16((E_tok[c0] + sum_j A_j[c_j]) * 8^-1/2)."""
+    codes = _c(codes, np.int32)
+    B = codes.shape[0]
+    out = np.empty((B, om.cfg["H"]), np.uint16)
+    lib().m3o_feedback(ctypes.byref(om.m), _ptr(codes), B, _ptr(out))
+    return out
+
+
+def mat_of(om: OracleModel, which: str, j: int = 0, name: str | None = None) -> Matrix:
+    """The oracle's own matrix object, for stage checks: which = "lm_head",
+    "p_in" or "head" (depth head j, 1-based); or which = "body" / "depth" with
+    layer j and name = "qkv", "o", "gu" (gate/up rows interleaved) or "down"."""
+    return om.mats[(which, j) if name is None else (which, j, name)]
 
 
 def decode_frame(om: OracleModel, x_in, seed, frame, temperature=1.0, trace=False):

@@ -625,6 +625,85 @@ static void draw_rows(const m3o_model* m, const float* lg, int B, int V,
   free(gap);
 }
 
+/* One layer with the identity attention stub, in place on h [B, Hd]: the
+   step the frame takes per body layer and per depth layer ([ds] model
+   overview; BASELINE's stubbed attention). */
+void m3o_layer_stub(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads, int n_kv,
+                    int hd, int F, float eps) {
+  int nq = n_heads * hd, nkv = n_kv * hd;
+  int wide = F > nq + 2 * nkv ? F : nq + 2 * nkv;
+  double* y = (double*)malloc((size_t)B * (2 * (size_t)wide + 16) * sizeof(double));
+  uint16_t* a = (uint16_t*)malloc((size_t)B * Hd * 2);
+  uint16_t* qkvb = (uint16_t*)malloc((size_t)B * (nq + 2 * nkv) * 2);
+  uint16_t* o = (uint16_t*)malloc((size_t)B * nq * 2);
+  uint16_t* mm = (uint16_t*)malloc((size_t)B * F * 2);
+  run_layer(L, h, B, Hd, n_heads, n_kv, hd, F, eps, a, qkvb, o, mm, y, NULL);
+  free(y); free(a); free(qkvb); free(o); free(mm);
+}
+
+/* One layer with decode attention in place of the stub, in place on h: the
+   layer's q/k norm + RoPE at position pos writes k and v to slot pos of the
+   caches kc, vc ([B][n_kv][max_pos][hd]) and its heads attend over positions
+   0 .. pos ("MiniMax Music 3, local" and TensorFold PR #987, kernel lists). */
+void m3o_layer_attn(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads, int n_kv, int hd,
+                    int F, float eps, const float* rope, uint16_t* kc, uint16_t* vc, int max_pos,
+                    int pos) {
+  int nq = n_heads * hd, nkv = n_kv * hd;
+  int wide = F > nq + 2 * nkv ? F : nq + 2 * nkv;
+  double* y = (double*)malloc((size_t)B * (2 * (size_t)wide + 16) * sizeof(double));
+  uint16_t* a = (uint16_t*)malloc((size_t)B * Hd * 2);
+  uint16_t* qkvb = (uint16_t*)malloc((size_t)B * (nq + 2 * nkv) * 2);
+  uint16_t* o = (uint16_t*)malloc((size_t)B * nq * 2);
+  uint16_t* mm = (uint16_t*)malloc((size_t)B * F * 2);
+  uint16_t* qbuf = (uint16_t*)malloc((size_t)B * nq * 2);
+  m3o_attn_at at = {rope, kc, vc, max_pos, pos, qbuf};
+  run_layer(L, h, B, Hd, n_heads, n_kv, hd, F, eps, a, qkvb, o, mm, y, &at);
+  free(y); free(a); free(qkvb); free(o); free(mm); free(qbuf);
+}
+
+/* Input of depth step j ([ds] stage 2: the depth decoder draws codebook j
+   from the frame's body state and the code drawn before it):
+   hd[b] = bf16(u[b] + Emb_j[c_{j-1}]), with Emb_1 indexed by the semantic
+   code's position in the slice (0 when outside it) and Emb_j, j >= 2, by the
+   depth code of step j - 1.  codes: [B, 8] as the frame writes them. */
+void m3o_step_input(const m3o_model* m, int j, const int32_t* codes, const uint16_t* u, int B,
+                    uint16_t* hd) {
+  int D = m->D;
+  for (int b = 0; b < B; ++b) {
+    int32_t prev;
+    const uint16_t* E;
+    if (j == 1) {
+      prev = codes[b * 8] - m->vocab_base;
+      if (prev < 0 || prev >= m->V0) prev = 0;
+      E = m->emb1;
+    } else {
+      prev = codes[b * 8 + j - 1];
+      E = m->emb[j - 2];
+    }
+    for (int k = 0; k < D; ++k)
+      hd[(size_t)b * D + k] = m3o_f64_to_bf16(m3o_bf16_to_f64(u[(size_t)b * D + k]) +
+                                              m3o_bf16_to_f64(E[(size_t)prev * D + k]));
+  }
+}
+
+/* Next frame's input from the frame's 8 codes ([ds] stage 2: the codes are
+   embedded, summed and scaled by the square root of the codebook count):
+   x' = bf16((E_tok[c0] + sum_j A_j[c_j]) * 8^-1/2), summed in float64. */
+void m3o_feedback(const m3o_model* m, const int32_t* codes, int B, uint16_t* x_next) {
+  int H = m->H;
+  double scale = 1.0 / sqrt((double)m->n_codebooks);
+  for (int b = 0; b < B; ++b) {
+    int32_t c0 = codes[b * 8] - m->vocab_base;
+    if (c0 < 0 || c0 >= m->V0) c0 = 0;
+    for (int k = 0; k < H; ++k) {
+      double acc = m3o_bf16_to_f64(m->tok_emb_audio[(size_t)c0 * H + k]);
+      for (int j = 1; j < m->n_codebooks; ++j)
+        acc += m3o_bf16_to_f64(m->audio_emb[j - 1][(size_t)codes[b * 8 + j] * H + k]);
+      x_next[(size_t)b * H + k] = m3o_f64_to_bf16(acc * scale);
+    }
+  }
+}
+
 void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
                       uint64_t seed, uint32_t frame, float temperature,
                       int32_t* codes, uint16_t* x_next, m3o_frame_trace* tr) {
@@ -677,22 +756,7 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
   m3o_f64_to_bf16_n(y, u, (size_t)B * D);
 
   for (int j = 1; j < m->n_codebooks; ++j) {
-    /* d_j = bf16(u + Emb_j[c_{j-1}]) */
-    for (int b = 0; b < B; ++b) {
-      int32_t prev;
-      const uint16_t* E;
-      if (j == 1) {
-        prev = codes[b * 8] - m->vocab_base;
-        if (prev < 0 || prev >= m->V0) prev = 0;
-        E = m->emb1;
-      } else {
-        prev = codes[b * 8 + j - 1];
-        E = m->emb[j - 2];
-      }
-      for (int k = 0; k < D; ++k)
-        hd[(size_t)b * D + k] = m3o_f64_to_bf16(m3o_bf16_to_f64(u[(size_t)b * D + k]) +
-                                                m3o_bf16_to_f64(E[(size_t)prev * D + k]));
-    }
+    m3o_step_input(m, j, codes, u, B, hd);
     for (int l = 0; l < m->d_layers; ++l) {
       /* step j attends over the frame's codebook positions 0 .. j - 1 */
       m3o_attn_at at = {m->rope, m->attention ? m->dkcache[l] : NULL,
@@ -711,18 +775,7 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
     }
   }
 
-  /* feedback: x' = bf16((E_tok[c0] + sum_j A_j[c_j]) * 8^-1/2) */
-  double scale = 1.0 / sqrt((double)m->n_codebooks);
-  for (int b = 0; b < B; ++b) {
-    int32_t c0 = codes[b * 8] - m->vocab_base;
-    if (c0 < 0 || c0 >= m->V0) c0 = 0;
-    for (int k = 0; k < H; ++k) {
-      double acc = m3o_bf16_to_f64(m->tok_emb_audio[(size_t)c0 * H + k]);
-      for (int j = 1; j < m->n_codebooks; ++j)
-        acc += m3o_bf16_to_f64(m->audio_emb[j - 1][(size_t)codes[b * 8 + j] * H + k]);
-      x_next[(size_t)b * H + k] = m3o_f64_to_bf16(acc * scale);
-    }
-  }
+  m3o_feedback(m, codes, B, x_next);
   free(y); free(h); free(a); free(qkvb); free(o); free(mm); free(u); free(hd);
   free(lg); free(draw_out); free(zb); free(z2); free(qbuf);
 }

@@ -181,6 +181,21 @@ typedef struct {
   float* zgap;         /* [B, 8]  best - second-best z per draw (optional)    */
 } m3o_frame_trace;
 
+/* The frame's parts, as m3o_decode_frame runs them (stage checks call them
+   on the inputs a stage was given): one layer with the identity attention
+   stub, in place on h [B, Hd]; depth step j's input from u and the codes
+   [B, 8]; the next frame's input from the codes. */
+void m3o_layer_stub(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads, int n_kv,
+                    int hd, int F, float eps);
+/* the same layer with decode attention at position pos over the caches kc,
+   vc ([B][n_kv][max_pos][hd]; slot pos is written) */
+void m3o_layer_attn(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads, int n_kv, int hd,
+                    int F, float eps, const float* rope, uint16_t* kc, uint16_t* vc, int max_pos,
+                    int pos);
+void m3o_step_input(const m3o_model* m, int j, const int32_t* codes, const uint16_t* u, int B,
+                    uint16_t* hd);
+void m3o_feedback(const m3o_model* m, const int32_t* codes, int B, uint16_t* x_next);
+
 /* codes[b*8 + 0] = absolute semantic id; codes[b*8 + j] = code j in [0,1024).
    x_next = bf16( (E_tok[c0] + sum_j A_j[c_j]) * 8^-1/2 ). */
 void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,

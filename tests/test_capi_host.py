@@ -280,6 +280,40 @@ def test_frame_layout_and_refusals(L):
     assert L.m3_decode_frame_weights(ctypes.byref(m), FAKE, 1, codes, None, None) == _lib.M3_ERR_NULL
 
 
+@pytest.mark.parametrize("name,B", [("frame-full", 1), ("frame-full", 16), ("frame-small", 3)])
+def test_frame_layout_stage_slots(L, name, B):
+    """Every GEMV output of every body layer and of every depth layer of every
+    codebook step, every depth step's input and every depth head's logits has
+    a slot of its own in the state (plain and tagged), so each operation of a
+    frame can be checked from the input it was given; the slots are laid out
+    in the documented order and sizes."""
+    cfg = configs.config(name)
+    c = make_config(cfg, **configs.PRESETS["A"])
+    lay = _lib.FrameLayout()
+    assert L.m3_frame_layout_get(ctypes.byref(c), B, ctypes.byref(lay)) == 0
+    nL, S, DL = cfg["n_layers"], cfg["n_codebooks"] - 1, cfg["d_layers"]
+    nqkv = (cfg["n_heads"] + 2 * cfg["n_kv_heads"]) * 128
+    dqkv = 3 * cfg["d_heads"] * 128
+    order = ["x", "h", "qkv", "mlp", "logits", "u", "hd", "dqkv", "dmlp", "dlogits", "ring"]
+    need = {"x": B * cfg["H"] * 2, "h": nL * B * cfg["H"] * 2, "qkv": nL * B * nqkv * 2,
+            "mlp": nL * B * cfg["F"] * 2, "logits": B * cfg["V0"] * 4, "u": B * cfg["D"] * 2,
+            "hd": S * (DL + 1) * B * cfg["D"] * 2, "dqkv": S * DL * B * dqkv * 2,
+            "dmlp": S * DL * B * cfg["Fd"] * 2, "dlogits": S * B * cfg["code_vocab"] * 4}
+    for a, b in zip(order, order[1:]):
+        span = getattr(lay, b) - getattr(lay, a)
+        assert need[a] <= span < need[a] + 256, (a, span, need[a])
+    tagged = ["th", "tqkv", "tmlp", "tu", "thd", "tdqkv", "tdmlp", "th2", "thd2", "ho", "hdo", "rope"]
+    tneed = {"th": 2 * need["h"], "tqkv": 2 * need["qkv"], "tmlp": 2 * need["mlp"], "tu": 2 * need["u"],
+             "thd": 2 * need["hd"], "tdqkv": 2 * need["dqkv"], "tdmlp": 2 * need["dmlp"],
+             "th2": nL * B * cfg["H"] * 4, "thd2": S * DL * B * cfg["D"] * 4,
+             "ho": nL * B * cfg["H"] * 2, "hdo": S * DL * B * cfg["D"] * 2}
+    for a, b in zip(tagged, tagged[1:]):
+        span = getattr(lay, b) - getattr(lay, a)
+        assert tneed[a] <= span < tneed[a] + 256, (a, span, tneed[a])
+    # without attention the attention buffers take no room
+    assert lay.rope == lay.aq == lay.ao == lay.dao == lay.kcache == lay.total
+
+
 def test_frame_layout_with_attention(L):
     """attention = 1 adds the RoPE table, q/out buffers, the body and depth
     caches and the attention workspace to the state (zero-sized otherwise);
@@ -293,6 +327,8 @@ def test_frame_layout_with_attention(L):
     assert L.m3_frame_layout_get(ctypes.byref(att), B, ctypes.byref(la)) == 0
     # the plain layout is unchanged by the attention fields
     assert lp.total == lp.rope == lp.kcache == lp.attn_ws
+    assert la.dao - la.ao >= cfg["n_layers"] * B * cfg["n_heads"] * 128 * 2
+    assert la.kcache - la.dao >= (cfg["n_codebooks"] - 1) * cfg["d_layers"] * B * cfg["D"] * 2
     kv = cfg["n_layers"] * B * cfg["n_kv_heads"] * max_pos * 128 * 2
     assert la.vcache - la.kcache >= kv and la.dkcache - la.vcache >= kv
     dkv = cfg["d_layers"] * B * cfg["d_heads"] * 8 * 128 * 2
