@@ -80,15 +80,12 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     dst[lane + 64] = (uint16_t)x1;
     return;
   }
-  // the head's RMSNorm with the GEMV prologue's rounding (gemv_impl.h,
-  // "RMSNorm rounding": float64 sum of squares and r, products re-taken in
-  // float64 near a bf16 tie)
+  // the head's RMSNorm with the GEMV prologue's steps (gemv_impl.h, "RMSNorm"):
+  // r from a float64 sum of squares, rounded to fp32; two fp32 products
   const float* g = hh < n_q ? q_gamma : k_gamma;
   const float a0f = bf2f(x0), a1f = bf2f(x1);
-  const double tot = __shfl(wave_sum_f64((double)a0f * a0f + (double)a1f * a1f), 0, 64);
-  const double r64 = norm_r(tot, kHD, eps);
-  const float r = (float)r64;
-  const float a0 = bf2f(norm_one(a0f, r, r64, g[lane])), a1 = bf2f(norm_one(a1f, r, r64, g[lane + 64]));
+  const float r = norm_r(wave_sum_f64((double)a0f * a0f + (double)a1f * a1f), kHD, eps);
+  const float a0 = bf2f(f2bf((a0f * r) * g[lane])), a1 = bf2f(f2bf((a1f * r) * g[lane + 64]));
   const float c = rope[((size_t)pos * 64 + lane) * 2], s = rope[((size_t)pos * 64 + lane) * 2 + 1];
   const uint32_t y0 = f2bf(a0 * c - a1 * s), y1 = f2bf(a1 * c + a0 * s);
   uint16_t* dst = hh < n_q ? q_out + (size_t)row * ldq + (size_t)hh * kHD

@@ -91,56 +91,22 @@ __device__ __forceinline__ uint32_t f2bf_pair(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm rounding.  The normed operand a = bf16(x * r * gamma) is a rounding
-// decision: where x r gamma lies within a few fp32 ulps of a tie between two
-// bf16 values, an fp32 evaluation (r from an fp32 sum, two fp32 products)
-// rounds it to either side, and one operand element one ulp apart shifts every
-// output of its row by W[n, k] ulp(a_k), enough to change the rounding of a
-// few percent of them.  So r comes from a float64 sum of squares (each square
-// of a bf16 is exact in float64), and x r gamma is evaluated in fp32 first and
-// again in float64 wherever the fp32 value is within kTieWin fp32 ulps of a
-// tie; the fp32 value is within 3 ulps of the float64 one (three roundings),
-// so everywhere else both round to the same bf16.
+// RMSNorm (TensorFold PR #987 precision list: fp32 norms, bf16 operands).
+// r comes from a float64 sum of squares (each square of a bf16 is exact in
+// float64, and so is their sum over the ranges activations take, in any
+// order) and is rounded once to fp32; each element is then
+// bf16(fl32(fl32(x r) gamma)).  Every step is one IEEE operation, so the bf16
+// rounding of each element is fixed by the steps and not by the order of a
+// reduction: an operand element one ulp apart would shift every output of its
+// row by W[n, k] ulp(a_k), enough to change the rounding of a few percent of
+// them.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kTieWin = 8;
-
-// |fp32 bits - nearest bf16 tie| <= kTieWin ulps (ties sit at low half 0x8000)
-__device__ __forceinline__ bool near_tie(float v) {
-  return ((__float_as_uint(v) & 0xFFFFu) - (0x8000u - kTieWin)) <= 2u * kTieWin;
-}
-
-// float64 -> fp32 rounded to odd: nearest, then, if inexact, toward zero with
-// the last bit set.  A second rounding of that to bf16 (8 of its 24 bits) to
-// nearest even gives the float64 value's own nearest-even bf16.
-__device__ __forceinline__ float f64_to_f32_odd(double d) {
-  float f = (float)d;
-  if ((double)f != d && d == d) {
-    uint32_t u = __float_as_uint(f);
-    if (fabs((double)f) > fabs(d)) u -= 1u;
-    f = __uint_as_float(u | 1u);
-  }
-  return f;
-}
-
-// one bf16 pair (x in the low and high halves of w) normalised with the row's
-// r (fp32, and float64 read from *r64 only near a tie) and gammas g0, g1
-__device__ __forceinline__ uint32_t norm_pair(uint32_t w, float r32, const double* r64, float g0,
-                                              float g1) {
-  const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
-  const float a0 = (x0 * r32) * g0, a1 = (x1 * r32) * g1;
-  if (__builtin_expect(near_tie(a0) || near_tie(a1), 0)) {
-    const double r = *r64;
-    return f2bf_pair(f64_to_f32_odd(((double)x0 * r) * (double)g0),
-                     f64_to_f32_odd(((double)x1 * r) * (double)g1));
-  }
+// one bf16 pair (x in the low and high halves of w) normalised with r and
+// the gammas g0, g1 (two fp32 products each, one bf16 rounding)
+__device__ __forceinline__ uint32_t norm_pair(uint32_t w, float r, float g0, float g1) {
+  const float a0 = (__uint_as_float(w << 16) * r) * g0;
+  const float a1 = (__uint_as_float(w & 0xffff0000u) * r) * g1;
   return f2bf_pair(a0, a1);
-}
-
-// one value normalised with r (fp32; float64 near a tie) and gamma g
-__device__ __forceinline__ uint32_t norm_one(float x, float r32, double r64, float g) {
-  const float a = (x * r32) * g;
-  if (__builtin_expect(near_tie(a), 0)) return f2bf(f64_to_f32_odd(((double)x * r64) * (double)g));
-  return f2bf(a);
 }
 
 // sum of squares of a bf16 pair, added in float64 (each square is exact)
@@ -149,16 +115,9 @@ __device__ __forceinline__ double sumsq_pair(uint32_t w, double ss) {
   return fma(x1, x1, fma(x0, x0, ss));
 }
 
-// sum over the wave; lane 0 holds the result (every lane of the wave active)
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-// r = 1 / sqrt(ss / K + eps) in float64
-__device__ __forceinline__ double norm_r(double ss, int K, float eps) {
-  return 1.0 / sqrt(ss / (double)K + (double)eps);
+// r = 1 / sqrt(ss / K + eps) in float64, rounded once to fp32
+__device__ __forceinline__ float norm_r(double ss, int K, float eps) {
+  return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
 }
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc) {
@@ -231,6 +190,38 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]
   v += dpp_f<0x141>(v);    // row_half_mirror
   v += dpp_f<0x140>(v);    // row_mirror
+  return v;
+}
+
+// The same exchanges for a float64 value, moved as its two 32-bit halves.
+__device__ __forceinline__ double pair_sum32_f64(double v) {
+  const uint32_t lo = (uint32_t)__double2loint(v), hi = (uint32_t)__double2hiint(v);
+  const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return __hiloint2double((int)h[0], (int)l[0]) + __hiloint2double((int)h[1], (int)l[1]);
+}
+
+__device__ __forceinline__ double pair_sum16_f64(double v) {
+  const uint32_t lo = (uint32_t)__double2loint(v), hi = (uint32_t)__double2hiint(v);
+  const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  return __hiloint2double((int)h[0], (int)l[0]) + __hiloint2double((int)h[1], (int)l[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// sum over the wave, the same value left in every lane (every lane active)
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = pair_sum16_f64(pair_sum32_f64(v));
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  v += dpp_d<0x140>(v);
   return v;
 }
 
@@ -577,19 +568,14 @@ struct OperandSource {
   }
 };
 
-// The norm's per-row values in the LDS scratch ss_buf (floats): r as fp32 at
-// [0, M3_MAX_B), r as float64 at float offset 2 M3_MAX_B, and the few-row
-// path's per-wave partial sums (float64) after those.
+// The norm's per-row values in the LDS scratch ss_buf (floats): r at
+// [0, M3_MAX_B), then (from float offset 2 M3_MAX_B) the few-row path's
+// per-wave partial sums of squares (float64).
 struct NormLds {
-  float* r32;
-  double* r64;
+  float* r;
   double* part;
   __device__ explicit NormLds(float* ss_buf)
-      : r32(ss_buf), r64(reinterpret_cast<double*>(ss_buf + 2 * M3_MAX_B)), part(r64 + M3_MAX_B) {}
-  __device__ void set(int b, double r) {
-    r64[b] = r;
-    r32[b] = (float)r;
-  }
+      : r(ss_buf), part(reinterpret_cast<double*>(ss_buf + 2 * M3_MAX_B)) {}
 };
 
 template <bool COH>
@@ -657,7 +643,7 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
     double tot = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) tot += nl.part[tid * kWaves + w];
-    nl.set(tid, norm_r(tot, p.K, p.eps));
+    nl.r[tid] = norm_r(tot, p.K, p.eps);
   }
 }
 
@@ -774,12 +760,12 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
     }
     double ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     ss = wave_sum_f64(ss);
-    if (lane == 0) NormLds(ss_buf).set(b, norm_r(ss, p.K, p.eps));
+    if (lane == 0) NormLds(ss_buf).r[b] = norm_r(ss, p.K, p.eps);
   }
   }
   __syncthreads();
-  // pass 3: a = bf16(x * r_b * gamma) (see norm_pair); gamma is loaded once
-  // per chunk
+  // pass 3: a = bf16(fl32(fl32(x r_b) gamma)) (see norm_pair); gamma is
+  // loaded once per chunk
   const NormLds nl(ss_buf);
   const int kc = p.K >> 3;
   for (int i = tid; i < kc; i += kThreads) {
@@ -795,14 +781,13 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
       for (int e = 0; e < 4; ++e) {
         const int b = b0 + e < p.lds_rows ? b0 + e : b0;
         v[e] = *reinterpret_cast<const uint4*>(act + (size_t)b * stride + k);
-        r[e] = nl.r32[b];
+        r[e] = nl.r[b];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         uint32_t wv[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
-        const int b = b0 + e < p.lds_rows ? b0 + e : b0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wv[j] = norm_pair(wv[j], r[e], nl.r64 + b, g[2 * j], g[2 * j + 1]);
+        for (int j = 0; j < 4; ++j) wv[j] = norm_pair(wv[j], r[e], g[2 * j], g[2 * j + 1]);
         if (b0 + e < p.lds_rows)
           *reinterpret_cast<uint4*>(act + (size_t)(b0 + e) * stride + k) =
               make_uint4(wv[0], wv[1], wv[2], wv[3]);

@@ -308,10 +308,10 @@ constexpr int kNThreads = 256;
 __global__ __launch_bounds__(kNThreads) void rmsnorm_rows_kernel(const uint16_t* x, int ldx,
                                                                  const float* gamma, float eps,
                                                                  int K, uint16_t* a, int lda) {
-  // the decode GEMV prologue's arithmetic (gemv_impl.h, "RMSNorm rounding"):
-  // float64 sum of squares and r, fp32 products re-taken in float64 near a tie
+  // the decode GEMV prologue's steps (gemv_impl.h, "RMSNorm"): r from a
+  // float64 sum of squares, rounded to fp32; two fp32 products per element
   __shared__ double part[kNThreads / 64];
-  __shared__ double r64;
+  __shared__ float rs;
   const int row = blockIdx.x, tid = threadIdx.x;
   const uint16_t* xr = x + (size_t)row * ldx;
   uint16_t* ar = a + (size_t)row * lda;
@@ -327,9 +327,9 @@ __global__ __launch_bounds__(kNThreads) void rmsnorm_rows_kernel(const uint16_t*
   ss = wave_sum_f64(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
-  if (tid == 0) r64 = norm_r((part[0] + part[1]) + (part[2] + part[3]), K, eps);
+  if (tid == 0) rs = norm_r((part[0] + part[1]) + (part[2] + part[3]), K, eps);
   __syncthreads();
-  const float r = (float)r64;
+  const float r = rs;
   for (int c = tid; c < kc; c += kNThreads) {
     const uint4 v = *reinterpret_cast<const uint4*>(xr + c * 8);
     const float4 g0 = *reinterpret_cast<const float4*>(gamma + c * 8);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kNThreads) void rmsnorm_rows_kernel(const uint16_t*
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      o[j] = norm_pair(wv[j], r, &r64, g[2 * j], g[2 * j + 1]);
+      o[j] = norm_pair(wv[j], r, g[2 * j], g[2 * j + 1]);
     }
     *reinterpret_cast<uint4*>(ar + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }

@@ -88,6 +88,28 @@ void m3o_f32_to_bf16_n(const float* v, uint16_t* out, size_t n) {
 /* RMSNorm ([metal] precision list: fp32 norms, bf16 activations).      */
 /* The oracle evaluates r in float64; one bf16 rounding of x*r*gamma.   */
 /* ------------------------------------------------------------------ */
+/* The norm's steps, in the precision the Metal port's precision list gives
+   (fp32 norms, bf16 activations): r comes from a sum of squares taken in
+   float64 (each square of a bf16 is exact in float64, and so is their sum
+   over the ranges activations take, whatever the order) and is rounded once
+   to fp32; each element is then fl32(fl32(x * r) * gamma), two fp32
+   products, rounded once to bf16.  Every step is a single IEEE operation, so
+   the bf16 rounding decision of each element is fixed by the steps alone. */
+float m3o_norm_r(const uint16_t* x, int K, float eps) {
+  double ss = 0.0;
+  for (int k = 0; k < K; ++k) {
+    double v = m3o_bf16_to_f64(x[k]);
+    ss += v * v;
+  }
+  return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+}
+
+uint16_t m3o_norm_elem(uint16_t x, float r, float gamma) {
+  const float xr = (float)m3o_bf16_to_f64(x) * r;    /* exact conversion, one fp32 product */
+  const float a = xr * gamma;                          /* the second fp32 product */
+  return m3o_f64_to_bf16((double)a);
+}
+
 void m3o_rmsnorm(const uint16_t* x, int B, int K, int ldx, const float* gamma,
                  float eps, uint16_t* a, int lda) {
   for (int b = 0; b < B; ++b) {
@@ -97,14 +119,8 @@ void m3o_rmsnorm(const uint16_t* x, int B, int K, int ldx, const float* gamma,
       for (int k = 0; k < K; ++k) ar[k] = xr[k];
       continue;
     }
-    double ss = 0.0;
-    for (int k = 0; k < K; ++k) {
-      double v = m3o_bf16_to_f64(xr[k]);
-      ss += v * v;
-    }
-    double r = 1.0 / sqrt(ss / (double)K + (double)eps);
-    for (int k = 0; k < K; ++k)
-      ar[k] = m3o_f64_to_bf16(m3o_bf16_to_f64(xr[k]) * r * (double)gamma[k]);
+    const float r = m3o_norm_r(xr, K, eps);
+    for (int k = 0; k < K; ++k) ar[k] = m3o_norm_elem(xr[k], r, gamma[k]);
   }
 }
 
@@ -302,14 +318,9 @@ static void norm_rope_head(const uint16_t* x, int hd, const float* gamma, float 
                            const float* rope_pos, uint16_t* y) {
   const int half = hd / 2;
   uint16_t xn[512];
-  double ss = 0.0;
-  for (int d = 0; d < hd; ++d) {
-    const double v = m3o_bf16_to_f64(x[d]);
-    ss += v * v;
-  }
-  const double r = 1.0 / sqrt(ss / (double)hd + (double)eps);
-  for (int d = 0; d < hd; ++d)
-    xn[d] = m3o_f64_to_bf16(m3o_bf16_to_f64(x[d]) * r * (double)gamma[d]);
+  /* the head's RMSNorm: the same steps as m3o_rmsnorm */
+  const float r = m3o_norm_r(x, hd, eps);
+  for (int d = 0; d < hd; ++d) xn[d] = m3o_norm_elem(x[d], r, gamma[d]);
   for (int i = 0; i < half; ++i) {
     const double c = (double)rope_pos[2 * i], s = (double)rope_pos[2 * i + 1];
     const double a = m3o_bf16_to_f64(xn[i]), b = m3o_bf16_to_f64(xn[i + half]);

@@ -38,10 +38,15 @@ void     m3o_f64_to_bf16_n(const double* v, uint16_t* out, size_t n);
 void     m3o_f32_to_bf16_n(const float* v, uint16_t* out, size_t n);
 
 /* ---- RMSNorm ------------------------------------------------------- */
-/* a[b,k] = bf16( x[b,k] * r_b * gamma[k] ),  r_b = 1/sqrt(mean_k x^2 + eps).
-   gamma == NULL: a = x (no norm). */
+/* a[b,k] = bf16( fl32(fl32(x[b,k] * r_b) * gamma[k]) ),
+   r_b = fl32(1/sqrt(mean_k x^2 + eps)) with the sum and r in float64
+   (fp32 norm arithmetic, the Metal port's precision list).
+   gamma == NULL: a = x (no norm).  m3o_norm_r and m3o_norm_elem are its two
+   steps (r of one row of K values; one element). */
 void m3o_rmsnorm(const uint16_t* x, int B, int K, int ldx, const float* gamma,
                  float eps, uint16_t* a, int lda);
+float m3o_norm_r(const uint16_t* x, int K, float eps);
+uint16_t m3o_norm_elem(uint16_t x, float r, float gamma);
 
 /* ---- int8 quantisers ------------------------------------------------ */
 /* s_n = fl32(absmax_n / 127); q = clamp(rne(W/s), -127, 127); zero row: s=q=0 */
