@@ -641,6 +641,13 @@ struct FrameGraph {
   hipGraphExec_t exec;
 };
 
+// the Gumbel-argmax draw's checks and launch (with a caller's workspace or
+// the allocation-free scratch), defined after the entry points
+int gumbel_check(const float* logits, int B, int V, int ldl, const m3_sample_params* p,
+                 const int32_t* out);
+int gumbel_entry(const float* logits, int B, int V, int ldl, const m3_sample_params* p,
+                 int32_t* out, void* ws, size_t ws_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -725,13 +732,44 @@ size_t m3_gumbel_workspace_bytes(int B, int V) {
 
 int m3_gumbel_argmax(const float* logits, int B, int V, int ldl, const m3_sample_params* p,
                      int32_t* out, void* ws, size_t ws_bytes, void* stream) {
-  if (!logits || !p || !out || !ws) return M3_ERR_NULL;
+  if (!ws) return M3_ERR_NULL;
+  return gumbel_entry(logits, B, V, ldl, p, out, ws, ws_bytes, stream);
+}
+
+int m3_gumbel_argmax_noalloc(const float* logits, int B, int V, int ldl,
+                             const m3_sample_params* p, int32_t* out, void* stream) {
+  // every argument is checked before the scratch is looked up or anything runs
+  const int st = gumbel_check(logits, B, V, ldl, p, out);
+  if (st != M3_OK) return st;
+  if (sample_ws_bytes(B, V) > kSampleScratchBytes) return M3_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (sample_scratch(&ws) != hipSuccess) return M3_ERR_HIP;
+  return gumbel_entry(logits, B, V, ldl, p, out, ws, kSampleScratchBytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int gumbel_check(const float* logits, int B, int V, int ldl, const m3_sample_params* p,
+                 const int32_t* out) {
+  if (!logits || !p || !out) return M3_ERR_NULL;
   if (B < 1 || B > M3_MAX_B_SAMPLE || V < 1 || V > (1 << 24) || ldl < V) return M3_ERR_SHAPE;
   if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return M3_ERR_SHAPE;
-  if (!aligned(logits, 4) || !aligned(ws, 16) || !aligned(out, 4)) return M3_ERR_ALIGN;
+  if (!aligned(logits, 4) || !aligned(out, 4)) return M3_ERR_ALIGN;
   if ((p->ids && !aligned(p->ids, 4)) || (p->noise_override && !aligned(p->noise_override, 4)) ||
       (p->frame_dev && !aligned(p->frame_dev, 4)))
     return M3_ERR_ALIGN;
+  return M3_OK;
+}
+
+int gumbel_entry(const float* logits, int B, int V, int ldl, const m3_sample_params* p,
+                 int32_t* out, void* ws, size_t ws_bytes, void* stream) {
+  const int st = gumbel_check(logits, B, V, ldl, p, out);
+  if (st != M3_OK) return st;
+  if (!aligned(ws, 16)) return M3_ERR_ALIGN;
+  if (B < 1 || B > M3_MAX_B_SAMPLE || V < 1 || V > (1 << 24) || ldl < V) return M3_ERR_SHAPE;
+  if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return M3_ERR_SHAPE;
   if (ws_bytes < sample_ws_bytes(B, V)) return M3_ERR_WORKSPACE;
   SampleDesc d{};
   d.logits = logits;
@@ -753,6 +791,10 @@ int m3_gumbel_argmax(const float* logits, int B, int V, int ldl, const m3_sample
   d.ws = ws;
   return hip_status(launch_sample(d, static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
+
+extern "C" {
 
 int m3_cfg_topk_draw(const float* logits, int n_songs, int V, int ldl, float cfg_scale,
                      int top_k, const m3_sample_params* p, int32_t* out, void* stream) {

@@ -113,6 +113,12 @@ struct SampleDesc {
 };
 size_t sample_ws_bytes(int B, int V);
 hipError_t launch_sample(const SampleDesc& d, hipStream_t s);
+// The allocation-free draw: a file-scope device array of this many bytes
+// (each device holds its own copy) serves as the workspace; sample_scratch
+// returns the current device's address of it (looked up once per device).
+constexpr size_t kSampleScratchBytes = M3_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+hipError_t sample_scratch(void** ptr);
 
 // CFG + top-k draw: one workgroup per song; rows 2s / 2s+1 are the song's
 // conditional / unconditional logits; out[(2s) * out_stride] and

@@ -17,6 +17,8 @@
 #include "m3_internal.h"
 #include "m3_sampling.h"
 
+#include <mutex>
+
 #pragma clang fp contract(off)
 
 namespace m3 {
@@ -481,6 +483,34 @@ hipError_t launch_cfg_draw(const CfgDesc& d, hipStream_t s) {
   if (e <= 8) return launch_cfg_e<8>(d, s);
   if (e <= 16) return launch_cfg_e<16>(d, s);
   return launch_cfg_e<32>(d, s);
+}
+
+// ---- the allocation-free draw's scratch ------------------------------------------
+// One fixed array per device for the per-chunk winners of
+// m3_gumbel_argmax_noalloc (callers that cannot allocate).  In host code the
+// array's name is only a stand-in: its device address is looked up once per
+// device, with that device current, and that address is what kernels get.
+static __device__ __align__(256) uint8_t scratch[kSampleScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t sample_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_sample(const SampleDesc& d, hipStream_t s) {

@@ -15,7 +15,7 @@ from ._lib import (BF16, I8ROW, I8G128, FP8ROW, EPI_NONE, EPI_SWIGLU, EPI_RESIDU
                    PACK_GLU_INTERLEAVE, check, lib)
 
 __all__ = ["packed_bytes", "pack", "rmsnorm_gemv", "gemv_i8row", "gemv_i8g128", "gemv_fp8row", "gemv", "cfg_topk_draw", "rmsnorm_rows", "prefill_gemm",
-           "lmhead_sliced", "gumbel_workspace_bytes", "gumbel_argmax", "BF16", "I8ROW", "I8G128", "FP8ROW",
+           "lmhead_sliced", "gumbel_workspace_bytes", "gumbel_argmax", "gumbel_argmax_noalloc", "BF16", "I8ROW", "I8G128", "FP8ROW",
            "EPI_NONE", "EPI_SWIGLU", "EPI_RESIDUAL", "OUT_BF16", "OUT_F32", "PACK_GLU_INTERLEAVE"]
 
 
@@ -134,6 +134,30 @@ def gumbel_argmax(logits: torch.Tensor, seed: int = 0, frame: int = 0, draw: int
                           int(valid[1]), _ptr(noise))
     check(lib().m3_gumbel_argmax(_ptr(logits), B, V, logits.stride(0), ctypes.byref(p), _ptr(out),
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def gumbel_argmax_noalloc(logits: torch.Tensor, seed: int = 0, frame: int = 0, draw: int = 0,
+                          temperature: float = 1.0, index_base: int = 0,
+                          ids: torch.Tensor | None = None, valid=(0, 0),
+                          noise: torch.Tensor | None = None, frame_dev: torch.Tensor | None = None,
+                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_gumbel_argmax_noalloc: the same draw with the library's fixed
+    per-device scratch in place of a workspace (nothing is allocated when
+    `out` is given)."""
+    for t, n in ((logits, "logits"), (ids, "ids"), (noise, "noise"), (frame_dev, "frame_dev"),
+                 (out, "out")):
+        _cuda(t, n)
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be a float32 [B, V] tensor")
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    p = _lib.SampleParams(int(seed) & (2**64 - 1), int(frame), _ptr(frame_dev), int(draw),
+                          float(temperature), int(index_base), _ptr(ids), int(valid[0]),
+                          int(valid[1]), _ptr(noise))
+    check(lib().m3_gumbel_argmax_noalloc(_ptr(logits), B, V, logits.stride(0), ctypes.byref(p),
+                                         _ptr(out), _stream(stream)))
     return out
 
 

@@ -203,6 +203,21 @@ int m3_gumbel_argmax(const float* logits, int B, int V, int ldl,
                      const m3_sample_params* params, int32_t* out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* m3_gumbel_argmax without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The per-chunk winners go to a fixed
+ * array inside the library of M3_NOALLOC_SCRATCH_BYTES per device, held
+ * until the process ends; (B, V) whose m3_gumbel_workspace_bytes exceeds it
+ * are refused with M3_ERR_WORKSPACE before anything runs.  Every call on one
+ * device shares that array: calls that overlap in time on a device race, so
+ * keep them on one stream or order them with events.  Each call writes every
+ * entry it reads (nothing has to start at zero).  Arguments, results and the
+ * other errors as m3_gumbel_argmax; M3_ERR_HIP if the array's device address
+ * cannot be looked up.  It calls no allocating routine. */
+#define M3_NOALLOC_SCRATCH_BYTES (1u << 20)
+int m3_gumbel_argmax_noalloc(const float* logits, int B, int V, int ldl,
+                             const m3_sample_params* params, int32_t* out, void* stream);
+
 /* ---- the reference's draw: guidance, top-k, multinomial ------------------ */
 /* DiffSynth-Studio MiniMax-Music3 stage 2: each song's conditional row c and
  * unconditional row u are combined as u + cfg_scale (c - u) (scale 1.5 there),

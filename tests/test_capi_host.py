@@ -114,6 +114,25 @@ def test_sampler_refusals(L):
     assert L.m3_gumbel_argmax(*arg(p=bad)) == _lib.M3_ERR_SHAPE
 
 
+def test_noalloc_sampler_refusals(L):
+    """The allocation-free draw checks every argument, and refuses a draw
+    whose winners do not fit the library's fixed scratch, before it looks up
+    the scratch or launches anything."""
+    p = _lib.SampleParams(0, 0, None, 0, 1.0, 0, None, 0, 0, None)
+    f = L.m3_gumbel_argmax_noalloc
+    assert f(None, 4, 5000, 5000, ctypes.byref(p), FAKE2, None) == _lib.M3_ERR_NULL
+    assert f(FAKE, 4, 5000, 5000, None, FAKE2, None) == _lib.M3_ERR_NULL
+    assert f(FAKE, 0, 5000, 5000, ctypes.byref(p), FAKE2, None) == _lib.M3_ERR_SHAPE
+    assert f(FAKE, 4, 5000, 4000, ctypes.byref(p), FAKE2, None) == _lib.M3_ERR_SHAPE
+    assert f(ctypes.c_void_p(0x100002), 4, 5000, 5000, ctypes.byref(p), FAKE2, None) == _lib.M3_ERR_ALIGN
+    bad = _lib.SampleParams(0, 0, None, 0, 0.0, 0, None, 0, 0, None)
+    assert f(FAKE, 4, 5000, 5000, ctypes.byref(bad), FAKE2, None) == _lib.M3_ERR_SHAPE
+    # 16 rows of 2^24 columns: 16 * 16384 chunk winners of 8 bytes = 2 MiB > 1 MiB
+    assert L.m3_gumbel_workspace_bytes(16, 1 << 24) > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, 16, 1 << 24, 1 << 24, ctypes.byref(p), FAKE2, None) == _lib.M3_ERR_WORKSPACE
+    assert L.m3_gumbel_workspace_bytes(8, 1 << 24) == _lib.NOALLOC_SCRATCH_BYTES
+
+
 def test_prefill_refusals(L):
     arg = lambda **k: (k.get("w", FAKE), k.get("N", 256), k.get("K", 512), k.get("a", FAKE2),
                        k.get("M", 600), k.get("lda", 512), k.get("y", ctypes.c_void_p(0x4000000)),
