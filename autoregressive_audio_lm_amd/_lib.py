@@ -109,11 +109,15 @@ _SIGS = {
     "m3_frame_state_init": (_I, [ctypes.POINTER(Config), _I, _P, _P, ctypes.c_uint32, _P]),
     "m3_decode_frame_weights": (_I, [ctypes.POINTER(Model), _P, _I, _P, ctypes.POINTER(ctypes.c_uint64), _P]),
     "m3_frame_graph_create": (_I, [ctypes.POINTER(Model), _P, _I, _P, _P, ctypes.POINTER(_P)]),
+    "m3_depth_graph_create": (_I, [ctypes.POINTER(Model), _P, _I, _P, _P, ctypes.POINTER(_P)]),
     "m3_frame_graph_launch": (_I, [_P, _P]),
     "m3_frame_graph_destroy": (_I, [_P]),
     "m3_frame_persistent_create": (_I, [ctypes.POINTER(Model), _P, _I, _P, _P, ctypes.POINTER(_P)]),
     "m3_frame_persistent_launch": (_I, [_P, _P]),
     "m3_frame_persistent_destroy": (_I, [_P]),
+    "m3_frame_persistent_clock_bytes": (ctypes.c_size_t, [_P]),
+    "m3_stream_read": (_I, [_P, ctypes.c_size_t, _P, _I, _I, _P]),
+    "m3_frame_persistent_clock": (_I, [_P, _P, ctypes.c_size_t, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
 }
 
 SYMBOLS = tuple(_SIGS)

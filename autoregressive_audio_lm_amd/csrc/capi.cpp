@@ -636,6 +636,47 @@ int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStrea
   return build_frame(m, S, B, codes, sink);
 }
 
+// The depth decoder's part of a frame: every step before the depth input
+// projection (the body's GEMVs and attention, the lm_head and the semantic
+// draw; 4 GEMVs per body layer, then the lm_head) is dropped, the rest is
+// launched as in the whole frame.
+struct DepthOnlySink final : FrameSink {
+  LaunchSink inner;
+  int skip;                 // GEMVs still to drop
+  bool sem_draw = true;     // a guided semantic draw (after the lm_head) still to drop
+  DepthOnlySink(hipStream_t st, int n_skip) : inner(st), skip(n_skip) {}
+  hipError_t gemv(const GemvDesc& d) override {
+    if (skip > 0) {
+      --skip;
+      return hipSuccess;
+    }
+    return inner.gemv(d);
+  }
+  hipError_t cfg_draw(const CfgDesc& d) override {
+    if (skip > 0) return hipSuccess;
+    if (sem_draw) {
+      sem_draw = false;
+      return hipSuccess;
+    }
+    return inner.cfg_draw(d);
+  }
+  hipError_t attention(const AttnStep& a, int B) override {
+    return skip > 0 ? hipSuccess : inner.attention(a, B);
+  }
+  hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
+                      const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
+                      int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
+                      uint32_t* frame, const FeedbackTags& ft) override {
+    return inner.feedback(tok, aemb, codes, last_part, last_nparts, vocab_base, n_slice, code_vocab,
+                          n_cb, B, H, x, ring, frame, ft);
+  }
+};
+
+int enqueue_depth(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStream_t s) {
+  DepthOnlySink sink(s, 4 * m->cfg.n_layers + 1);
+  return build_frame(m, S, B, codes, sink);
+}
+
 struct FrameGraph {
   hipGraph_t graph;
   hipGraphExec_t exec;
@@ -1067,8 +1108,9 @@ int m3_decode_frame_weights(const m3_model* model, void* state, int B, int32_t* 
                        static_cast<hipStream_t>(stream));
 }
 
-int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* codes, void* stream,
-                          void** graph_out) {
+namespace {
+int graph_create(const m3_model* model, void* state, int B, int32_t* codes, void* stream,
+                 void** graph_out, bool depth_only) {
   if (!model || !state || !codes || !graph_out) return M3_ERR_NULL;
   int st = validate_config(&model->cfg, B);
   if (st != M3_OK) return st;
@@ -1079,7 +1121,8 @@ int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* co
   M3_TRY(gemv_prepare());
   hipStream_t s = static_cast<hipStream_t>(stream);
   M3_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-  const int est = enqueue_frame(model, static_cast<uint8_t*>(state), B, codes, s);
+  const int est = depth_only ? enqueue_depth(model, static_cast<uint8_t*>(state), B, codes, s)
+                             : enqueue_frame(model, static_cast<uint8_t*>(state), B, codes, s);
   hipGraph_t g = nullptr;
   const hipError_t ce = hipStreamEndCapture(s, &g);
   if (est != M3_OK || ce != hipSuccess) {
@@ -1099,6 +1142,17 @@ int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* co
   }
   *graph_out = fg;
   return M3_OK;
+}
+}  // namespace
+
+int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* codes, void* stream,
+                          void** graph_out) {
+  return graph_create(model, state, B, codes, stream, graph_out, false);
+}
+
+int m3_depth_graph_create(const m3_model* model, void* state, int B, int32_t* codes, void* stream,
+                          void** graph_out) {
+  return graph_create(model, state, B, codes, stream, graph_out, true);
 }
 
 int m3_frame_graph_launch(void* graph, void* stream) {
@@ -1165,6 +1219,37 @@ int m3_frame_persistent_launch(void* handle, void* stream) {
   if (!handle) return M3_ERR_NULL;
   return hip_status(persist_launch(*static_cast<PersistLaunch*>(handle),
                                    static_cast<hipStream_t>(stream)));
+}
+
+int m3_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, int nontemporal,
+                   void* stream) {
+  if (!buf || !sink) return M3_ERR_NULL;
+  if (bytes < 16 || bytes % 16 || bytes >= ((size_t)1 << 31) || workgroups < 1 || workgroups > 4096)
+    return M3_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return M3_ERR_ALIGN;
+  return hip_status(launch_stream_read(buf, bytes, sink, workgroups, nontemporal,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t m3_frame_persistent_clock_bytes(void* handle) {
+  if (!handle) return 0;
+  return persist_clock_words(*static_cast<PersistLaunch*>(handle)) * 8;
+}
+
+int m3_frame_persistent_clock(void* handle, uint64_t* clk, size_t clk_bytes, int* n_phases,
+                              int* n_workgroups) {
+  if (!handle) return M3_ERR_NULL;
+  PersistLaunch& PL = *static_cast<PersistLaunch*>(handle);
+  int nwg = 0;
+  const int nph = persist_launch_dims(PL, &nwg);
+  if (n_phases) *n_phases = nph;
+  if (n_workgroups) *n_workgroups = nwg;
+  if (clk) {
+    if (!aligned(clk, 8)) return M3_ERR_ALIGN;
+    if (clk_bytes < persist_clock_words(PL) * 8) return M3_ERR_WORKSPACE;
+  }
+  persist_set_clock(PL, clk);
+  return M3_OK;
 }
 
 int m3_frame_persistent_destroy(void* handle) {

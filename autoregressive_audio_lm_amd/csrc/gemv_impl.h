@@ -115,9 +115,21 @@ __device__ __forceinline__ double sumsq_pair(uint32_t w, double ss) {
   return fma(x1, x1, fma(x0, x0, ss));
 }
 
-// r = 1 / sqrt(ss / K + eps) in float64, rounded once to fp32
+// r = 1 / sqrt(ss / K + eps) in float64, rounded once to fp32: the hardware
+// reciprocal square root refined by two Newton steps, each of which doubles
+// its correct bits, so r is within a few float64 ulps before its fp32
+// rounding (which it changes only when r lies that close to a tie between
+// two fp32 values); a zero or infinite estimate (x infinite or zero, r = 0
+// or infinity) is exact as it stands.
 __device__ __forceinline__ float norm_r(double ss, int K, float eps) {
-  return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+  const double x = ss / (double)K + (double)eps;
+  double y = __builtin_amdgcn_rsq(x);
+  if (y > 0.0 && y < __builtin_huge_val()) {
+    const double h = 0.5 * x;
+    y = y * fma(-h * y, y, 1.5);
+    y = y * fma(-h * y, y, 1.5);
+  }
+  return (float)y;
 }
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc) {
@@ -1087,10 +1099,12 @@ struct Accum<FMT, NB, true> {
 // still running, two batches of weights are requested before waiting, so the
 // wait overlaps the weight stream.  The wait object: probe() (every thread;
 // one look at the producer's progress) and wait() (every thread; block until
-// the producer is done, false to abandon the GEMV when the launch gives up).
+// the producer is done, false to abandon the GEMV when the launch gives up);
+// staged() marks the operand staged (the persistent frame's phase clock).
 struct NoWait {
   __device__ bool probe() const { return true; }
   __device__ bool wait() const { return true; }
+  __device__ void staged() const {}
   __device__ uint32_t ebase() const { return 0u; }
   __device__ int phase() const { return 0; }
   __device__ uint32_t* err() const { return nullptr; }
@@ -1223,6 +1237,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   }
   if (nitems == 0) return;
   if (LDS) stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre, grp, tg);
+  wt.staged();
   if (ready) load(bufB, scB, 1);
   __builtin_amdgcn_sched_barrier(0);
   // the scheduling barriers keep each batch's loads ahead of the next batch's

@@ -219,6 +219,10 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
                                 int n_slice, int code_vocab, int n_cb, int B, int H,
                                 uint16_t* x_out, int32_t* ring, uint32_t* frame,
                                 const FeedbackTags& ft);
+// phase clock: words of the buffer (3 per phase and workgroup), attach/detach
+size_t persist_clock_words(const PersistLaunch& L);
+void persist_set_clock(PersistLaunch& L, uint64_t* clk);
+int persist_launch_dims(const PersistLaunch& L, int* nwg);   // phases; *nwg = workgroups
 PersistLaunch* persist_launch_new();
 void persist_launch_free(PersistLaunch* L);
 // copy the table into device memory, start a new epoch (launch counter + 1),
@@ -226,10 +230,16 @@ void persist_launch_free(PersistLaunch* L);
 hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
                           uint32_t* seq, hipStream_t s, PersistLaunch* out);
 hipError_t persist_launch(const PersistLaunch& L, hipStream_t s);
-// the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip) by row-count class
-const void* persist_kernel_bf16(int NB);
-const void* persist_kernel_i8row(int NB);
-const void* persist_kernel_fp8row(int NB);
+// the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip, persist_fp8row.hip)
+// (clock: the instantiation that writes the phase clock; every row count
+// runs on 16-row tiles)
+const void* persist_kernel_bf16(bool clock);
+const void* persist_kernel_i8row(bool clock);
+const void* persist_kernel_fp8row(bool clock);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, size_t n, hipStream_t s);
+// a plain streaming read of `bytes` (< 2 GiB) at buf by `workgroups` workgroups
+// (stream.hip); sink: workgroups words
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups,
+                              int nontemporal, hipStream_t s);
 
 }  // namespace m3

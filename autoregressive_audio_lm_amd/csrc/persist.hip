@@ -134,7 +134,8 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
 
 // Persistent launch parameters once the phase table is in device memory.
 struct PersistLaunch {
-  const void* kernel;
+  const void* kernel;          // the production frame kernel
+  const void* kernel_clock;    // the same with the phase clock (used while clk is set)
   const Phase* phases;
   int nph;
   uint32_t* flags;
@@ -143,6 +144,7 @@ struct PersistLaunch {
   FeedbackArgs fb;
   size_t smem;
   int nwg;
+  uint64_t* clk = nullptr;   // phase clock buffer, 3 * nph * nwg words (nullptr: off)
 };
 
 // Copy the table to `table` (device, persist_phase_bytes() * size), set the
@@ -158,12 +160,14 @@ hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, u
   int nwg = ncu < kPersistFlags ? ncu : kPersistFlags;
   nwg &= ~3;
   if (nwg < 4) return hipErrorInvalidValue;
-  const int NB = nb_of(pl->B);
-  const void* k = pl->fmt_body == M3_I8ROW    ? persist_kernel_i8row(NB)
-                  : pl->fmt_body == M3_FP8ROW ? persist_kernel_fp8row(NB)
-                                              : persist_kernel_bf16(NB);
-  e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl->smem);
-  if (e != hipSuccess) return e;
+  const void* kern[2];
+  for (int c = 0; c < 2; ++c) {
+    kern[c] = pl->fmt_body == M3_I8ROW    ? persist_kernel_i8row(c != 0)
+              : pl->fmt_body == M3_FP8ROW ? persist_kernel_fp8row(c != 0)
+                                          : persist_kernel_bf16(c != 0);
+    e = hipFuncSetAttribute(kern[c], hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl->smem);
+    if (e != hipSuccess) return e;
+  }
   e = hipMemcpyAsync(table, pl->phases.data(), pl->phases.size() * sizeof(Phase),
                      hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return e;
@@ -173,7 +177,8 @@ hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, u
   if (e != hipSuccess) return e;
   e = hipStreamSynchronize(s);      // the host table may go away after this
   if (e != hipSuccess) return e;
-  out->kernel = k;
+  out->kernel = kern[0];
+  out->kernel_clock = kern[1];
   out->phases = static_cast<const Phase*>(table);
   out->nph = (int)pl->phases.size();
   out->flags = flags;
@@ -192,8 +197,17 @@ hipError_t persist_launch(const PersistLaunch& L, hipStream_t s) {
   uint32_t* err = L.err;
   const uint32_t* seq = L.seq;
   FeedbackArgs fb = L.fb;
-  void* args[] = {&ph, &nph, &flags, &err, &seq, &fb};
-  return hipLaunchCooperativeKernel(L.kernel, dim3(L.nwg), dim3(kThreads), args, (unsigned)L.smem, s);
+  uint64_t* clk = L.clk;
+  void* args[] = {&ph, &nph, &flags, &err, &seq, &fb, &clk};
+  return hipLaunchCooperativeKernel(clk ? L.kernel_clock : L.kernel, dim3(L.nwg), dim3(kThreads),
+                                    args, (unsigned)L.smem, s);
+}
+
+size_t persist_clock_words(const PersistLaunch& L) { return (size_t)3 * L.nph * L.nwg; }
+void persist_set_clock(PersistLaunch& L, uint64_t* clk) { L.clk = clk; }
+int persist_launch_dims(const PersistLaunch& L, int* nwg) {
+  *nwg = L.nwg;
+  return L.nph;
 }
 
 PersistLaunch* persist_launch_new() { return new PersistLaunch; }

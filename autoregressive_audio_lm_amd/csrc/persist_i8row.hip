@@ -1,12 +1,13 @@
-// persist_i8row.hip -- persistent frame kernels for a i8row body and lm_head (the
-// depth decoder in int8-g128), one per row-count class; see persist.hip.
+// persist_i8row.hip -- persistent frame kernels for an int8-row body and lm_head
+// (the depth decoder in int8-g128): the production kernel and the one that
+// also writes the phase clock; see persist.hip.
 #include "persist_kernel.h"
 
 namespace m3 {
 
-const void* persist_kernel_i8row(int NB) {
-  (void)NB;                 // every row count runs on 16-row tiles
-  return reinterpret_cast<const void*>(frame_kernel<16, M3_I8ROW>);
+const void* persist_kernel_i8row(bool clock) {
+  return clock ? reinterpret_cast<const void*>(frame_kernel<16, M3_I8ROW, true>)
+               : reinterpret_cast<const void*>(frame_kernel<16, M3_I8ROW, false>);
 }
 
 }  // namespace m3

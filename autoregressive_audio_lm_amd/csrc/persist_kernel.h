@@ -31,6 +31,15 @@ __device__ __forceinline__ bool flags_reached(const uint32_t* flags, int nwg, ui
   return __all(done);
 }
 
+// Phase clock (optional, m3_frame_persistent_clock): thread 0 of each
+// workgroup writes the constant-rate real-time counter at the phase's entry
+// (slot 0), when its operand is staged (slot 1) and at the phase's end
+// (slot 2), to clk[(slot * nph + phase) * nwg + wg]; `at` points at slot 0's
+// entry of the phase and workgroup, `stride` = nph * nwg.
+__device__ __forceinline__ void clock_mark(uint64_t* at, size_t stride, int slot) {
+  if (at && threadIdx.x == 0) at[slot * stride] = __builtin_amdgcn_s_memrealtime();
+}
+
 // GEMV phases wait inside their loads (tagged words): nothing to do before
 // the weight stream but report whether the operand is plain and ready (phase
 // 0 reads the launch's plain input).
@@ -38,8 +47,12 @@ struct TagWait {
   uint32_t eb;
   int i;
   uint32_t* er;
+  uint64_t* clk;       // phase clock: slot 0 entry of this phase and workgroup (nullptr: off)
+  size_t cstride;
   __device__ bool probe() const { return i == 0; }
   __device__ bool wait() const { return true; }
+  // phase clock: this workgroup's operand is staged
+  __device__ void staged() const { clock_mark(clk, cstride, 1); }
   __device__ uint32_t ebase() const { return eb; }
   __device__ int phase() const { return i; }
   __device__ uint32_t* err() const { return er; }
@@ -82,10 +95,10 @@ __device__ __forceinline__ void run_variant(CPhasePtr ph, uint8_t* smem, int wg,
       *(const Params*)&ph->p, smem, wg, nwg, wait);
 }
 
-template <int NB, int FB>
+template <int NB, int FB, bool CLK>
 __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int nph, uint32_t* flags,
                                                          uint32_t* err, const uint32_t* seq,
-                                                         FeedbackArgs fb) {
+                                                         FeedbackArgs fb, uint64_t* clk) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_ok;
   __shared__ int c_last[M3_MAX_B_FRAME];
@@ -95,13 +108,17 @@ __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int np
   if (__builtin_amdgcn_readfirstlane(ld4<true>(err, 0)) != 0u) return;
   // epochs of this launch: launch counter * 512 + phase + 1
   const uint32_t ebase = __builtin_amdgcn_readfirstlane(ld4<true>(seq, 0)) * kPhaseStride;
+  const size_t cstride = (size_t)nph * nwg;
   for (int i = 0; i < nph; ++i) {
     const int variant = __builtin_amdgcn_readfirstlane(ph[i].variant);
+    uint64_t* at = CLK ? clk + (size_t)i * nwg + wg : nullptr;   // (CLK: clk is set)
+    clock_mark(at, cstride, 0);
     if (variant == kFeedbackVariant) {
       if (!wait_flags(flags, nwg, ebase + (uint32_t)i, err, &s_ok)) return;
+      clock_mark(at, cstride, 1);
       feedback_run<true>(fb, wg, nwg, c_last, ebase);
     } else {
-      TagWait wait{ebase, i, err};
+      TagWait wait{ebase, i, err, at, cstride};
       const CPhasePtr cp = (CPhasePtr)(ph + i);
       if (variant == 0)
         run_variant<FB, NB>(cp, smem, wg, nwg, wait);
@@ -109,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int np
         run_variant<M3_I8G128, NB>(cp, smem, wg, nwg, wait);
     }
     if (__builtin_amdgcn_readfirstlane(ph[i].signal)) signal_epoch(flags, wg, ebase + (uint32_t)i + 1u);
+    clock_mark(at, cstride, 2);
   }
 }
 

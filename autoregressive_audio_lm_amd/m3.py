@@ -161,6 +161,20 @@ def gumbel_argmax_noalloc(logits: torch.Tensor, seed: int = 0, frame: int = 0, d
     return out
 
 
+def stream_read(buf: torch.Tensor, workgroups: int, nontemporal: bool = True,
+                sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """m3_stream_read: a plain streaming read of buf (a contiguous device
+    tensor) by `workgroups` workgroups; returns the sink words."""
+    _cuda(buf, "buf")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if sink is None:
+        sink = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    check(lib().m3_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                               int(workgroups), int(bool(nontemporal)), _stream(stream)))
+    return sink
+
+
 def cfg_topk_draw(logits: torch.Tensor, scale: float = 1.5, top_k: int = 50, seed: int = 0,
                   frame: int = 0, draw: int = 0, temperature: float = 1.0, index_base: int = 0,
                   ids: torch.Tensor | None = None, valid=(0, 0),

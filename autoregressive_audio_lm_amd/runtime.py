@@ -239,13 +239,16 @@ class FrameState:
                                             ctypes.byref(nbytes), m3._stream(stream)))
         return int(nbytes.value)
 
-    def capture(self, stream) -> None:
-        """Capture one frame into a HIP graph on `stream` (not the default stream)."""
+    def capture(self, stream, depth_only: bool = False) -> None:
+        """Capture one frame into a HIP graph on `stream` (not the default
+        stream); depth_only: the depth decoder's part of the frame alone
+        (m3_depth_graph_create), reading the body output and semantic draw of
+        the state's last whole frame."""
         g = ctypes.c_void_p()
-        check(lib().m3_frame_graph_create(ctypes.byref(self.dm.model),
-                                          ctypes.c_void_p(self.state.data_ptr()), self.B,
-                                          ctypes.c_void_p(self.codes.data_ptr()),
-                                          ctypes.c_void_p(stream.cuda_stream), ctypes.byref(g)))
+        create = lib().m3_depth_graph_create if depth_only else lib().m3_frame_graph_create
+        check(create(ctypes.byref(self.dm.model), ctypes.c_void_p(self.state.data_ptr()), self.B,
+                     ctypes.c_void_p(self.codes.data_ptr()), ctypes.c_void_p(stream.cuda_stream),
+                     ctypes.byref(g)))
         self.graph = g
 
     def replay(self, stream) -> None:
@@ -262,6 +265,27 @@ class FrameState:
 
     def persistent_launch(self, stream=None) -> None:
         check(lib().m3_frame_persistent_launch(self.persistent, m3._stream(stream)))
+
+    def persistent_clock(self, on: bool = True) -> None:
+        """Attach (on) or detach the phase clock of the persistent frame
+        (m3_frame_persistent_clock): later launches record per workgroup the
+        real-time counter at each phase's entry, operand staged and end."""
+        if not on:
+            check(lib().m3_frame_persistent_clock(self.persistent, None, 0, None, None))
+            self._clk = None
+            return
+        nb = int(lib().m3_frame_persistent_clock_bytes(self.persistent))
+        self._clk = torch.zeros(nb // 8, dtype=torch.int64, device=self.state.device)
+        nph, nwg = ctypes.c_int(), ctypes.c_int()
+        check(lib().m3_frame_persistent_clock(self.persistent, ctypes.c_void_p(self._clk.data_ptr()),
+                                              nb, ctypes.byref(nph), ctypes.byref(nwg)))
+        self._clk_dims = (nph.value, nwg.value)
+
+    def phase_clock(self):
+        """The last launch's phase clock as an int64 array [3, n_phases,
+        n_workgroups] (slots: entry, operand staged, end; 0 = not written)."""
+        nph, nwg = self._clk_dims
+        return self._clk.view(3, nph, nwg).cpu().numpy()
 
     @property
     def err(self) -> torch.Tensor:

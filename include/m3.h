@@ -496,6 +496,18 @@ int m3_frame_graph_create(const m3_model* model, void* state, int B, int32_t* co
                           void* stream, void** graph_out /* host */);
 int m3_frame_graph_launch(void* graph, void* stream);
 int m3_frame_graph_destroy(void* graph);
+/* The RVQ depth decoder of a frame alone, as a graph for
+ * m3_frame_graph_launch / _destroy (DiffSynth-Studio MiniMax-Music3 stage 2:
+ * the depth input projection, then 7 codebook steps of the depth layers, each
+ * with its head and draw, then the feedback): the same launches as the
+ * frame's from the depth input projection on.  It reads the body output and
+ * the semantic draw that the state holds from its last whole frame (run one
+ * first; until then they are zeros); each replay writes codes 1..7, the
+ * 16-frame ring, the fed-back input and the frame counter like a whole frame
+ * (the semantic code in `codes` is the last whole frame's).  For timing the
+ * depth decoder on its own. */
+int m3_depth_graph_create(const m3_model* model, void* state, int B, int32_t* codes,
+                          void* stream, void** graph_out /* host */);
 
 /* Persistent form of the frame: the same steps, with the same results, run as
  * ONE cooperative launch per frame.  One workgroup per compute unit walks the
@@ -529,6 +541,34 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
                                void* stream, void** handle_out /* host */);
 int m3_frame_persistent_launch(void* handle, void* stream);
 int m3_frame_persistent_destroy(void* handle);
+
+/* Phase clock of a persistent frame (profiling; off by default).  With a
+ * device buffer attached, every later launch on the handle has thread 0 of
+ * each workgroup write the GPU's constant-rate real-time counter
+ * (s_memrealtime) at three points of every phase i: entry (slot 0), its
+ * operand staged (slot 1; the frame end: every workgroup's flag seen) and
+ * the phase's end (slot 2), to clk[(slot * n_phases + i) * n_workgroups +
+ * wg]; a workgroup with no rows in a phase writes no slot 1 there.  clk ==
+ * NULL detaches the buffer.  clk_bytes >= m3_frame_persistent_clock_bytes;
+ * the buffer is caller-owned, 8-byte aligned.  n_phases and n_workgroups
+ * (host, optional) receive the table's dimensions.  Values are unchanged
+ * with the clock attached; the frame takes slightly longer. */
+size_t m3_frame_persistent_clock_bytes(void* handle);
+int m3_frame_persistent_clock(void* handle, uint64_t* clk, size_t clk_bytes, int* n_phases,
+                              int* n_workgroups);
+
+/* ---- measurement ------------------------------------------------------------ */
+/* A plain streaming read of `bytes` at buf (16-byte aligned, a multiple of 16,
+ * below 2 GiB): `workgroups` (1..4096) workgroups of 512 lanes read it with 16-byte
+ * buffer loads, the GEMVs' weight-tile loads (nontemporal: their cache
+ * policy for weights read once per frame; 0: the default policy), and each
+ * writes one word of what it read to sink[workgroup] (device, 4-byte
+ * aligned).  The read rate this reaches on the device is the ceiling the
+ * decode's weight stream is compared with, next to the HBM spec peak.
+ * Errors: M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_ALIGN before the launch; the HIP
+ * launch status otherwise. */
+int m3_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, int nontemporal,
+                   void* stream);
 
 #ifdef __cplusplus
 }

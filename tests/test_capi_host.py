@@ -133,6 +133,22 @@ def test_noalloc_sampler_refusals(L):
     assert L.m3_gumbel_workspace_bytes(8, 1 << 24) == _lib.NOALLOC_SCRATCH_BYTES
 
 
+def test_stream_read_and_depth_graph_refusals(L):
+    """The streaming-read measurement and the depth decoder's graph check
+    their arguments before anything is launched or captured."""
+    f = L.m3_stream_read
+    assert f(None, 1 << 20, FAKE2, 256, 1, None) == _lib.M3_ERR_NULL
+    assert f(FAKE, 1 << 20, None, 256, 1, None) == _lib.M3_ERR_NULL
+    assert f(FAKE, 0, FAKE2, 256, 1, None) == _lib.M3_ERR_SHAPE
+    assert f(FAKE, (1 << 20) + 8, FAKE2, 256, 1, None) == _lib.M3_ERR_SHAPE
+    assert f(FAKE, 1 << 31, FAKE2, 256, 1, None) == _lib.M3_ERR_SHAPE
+    assert f(FAKE, 1 << 20, FAKE2, 0, 1, None) == _lib.M3_ERR_SHAPE
+    assert f(FAKE, 1 << 20, FAKE2, 4097, 1, None) == _lib.M3_ERR_SHAPE
+    assert f(ctypes.c_void_p(0x100008), 1 << 20, FAKE2, 256, 1, None) == _lib.M3_ERR_ALIGN
+    g = ctypes.c_void_p()
+    assert L.m3_depth_graph_create(None, FAKE, 1, FAKE2, FAKE, ctypes.byref(g)) == _lib.M3_ERR_NULL
+
+
 def test_prefill_refusals(L):
     arg = lambda **k: (k.get("w", FAKE), k.get("N", 256), k.get("K", 512), k.get("a", FAKE2),
                        k.get("M", 600), k.get("lda", 512), k.get("y", ctypes.c_void_p(0x4000000)),

@@ -189,6 +189,39 @@ def test_frame_repeat_byte_identical(small):
     assert a.state.cpu().numpy().tobytes() == b.state.cpu().numpy().tobytes()
 
 
+def _depth_graph_equals_frame(dm, cfg, B, x0, f0):
+    """A whole frame from x0 at frame f0, then the depth decoder's graph
+    replayed on a second state that ran the same frame, with its counter set
+    back to f0: the depth part alone gives the frame's codes, depth logits,
+    fed-back input, ring and counter bit for bit, and leaves the body output
+    as it was."""
+    ref = runtime.FrameState(dm, B, x0, frame0=f0)
+    dep = runtime.FrameState(dm, B, x0, frame0=f0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ref.decode(s)
+        dep.decode(s)
+        dep.capture(s, depth_only=True)
+        s.synchronize()
+        h_before = dep.h.clone()
+        for k in range(2):
+            dep.frame.fill_(f0)
+            dep.x.zero_()
+            dep.codes.zero_()
+            dep.dlogits.zero_()
+            dep.replay(s)
+            s.synchronize()
+            _same_frame(ref, dep)
+            assert torch.equal(ref.dlogits, dep.dlogits)
+            assert torch.equal(dep.h, h_before)
+    dep.release()
+
+
+def test_depth_graph_equals_the_frames_depth_part(small):
+    cfg, dm, om = small
+    _depth_graph_equals_frame(dm, cfg, 6, synth.activations(6, cfg["H"], 77).to(DEV), 3)
+
+
 def _same_frame(a, b):
     assert torch.equal(a.codes, b.codes)
     for name in ("x", "h", "logits"):
@@ -223,6 +256,41 @@ def test_persistent_frame_equals_eager(small, B):
         s.synchronize()
         assert int(pers.err.item()) == 0
         _same_frame(eager, pers)
+    pers.release()
+
+
+def test_persistent_phase_clock(small):
+    """With the phase clock attached the persistent frame gives the same bytes
+    as the eager frame, and every workgroup's marks are in order: each phase's
+    entry, operand staged (where it had rows) and end, phase after phase."""
+    cfg, dm, om = small
+    B = 2
+    x0 = synth.activations(B, cfg["H"], 420).to(DEV)
+    eager = runtime.FrameState(dm, B, x0, frame0=5)
+    pers = runtime.FrameState(dm, B, x0, frame0=5)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        pers.persistent_create(s)
+        pers.persistent_clock(True)
+        for _ in range(2):
+            eager.decode(s)
+            pers.persistent_launch(s)
+            s.synchronize()
+            assert int(pers.err.item()) == 0
+            _same_frame(eager, pers)
+        clk = pers.phase_clock()
+        pers.persistent_clock(False)
+        eager.decode(s)
+        pers.persistent_launch(s)
+        s.synchronize()
+        _same_frame(eager, pers)
+    entry, staged, end = clk
+    assert np.all(entry > 0) and np.all(end >= entry)
+    had = staged > 0
+    assert had.any(axis=1).all()                    # every phase has rows somewhere
+    assert np.all((staged >= entry)[had]) and np.all((end >= staged)[had])
+    assert np.all(entry[1:] >= end[:-1])             # phase after phase, per workgroup
     pers.release()
 
 
@@ -307,6 +375,11 @@ def test_guided_frame_stages_match_oracle(guided, B):
         print(f"guided B={B} frame {f}: {stats.summary()}", flush=True)
         x = got["x"]
     assert int(st.frame.item()) == 10
+
+
+def test_guided_depth_graph_equals_the_frames_depth_part(guided):
+    cfg, dm, om = guided
+    _depth_graph_equals_frame(dm, cfg, 4, synth.activations(4, cfg["H"], 78).to(DEV), 11)
 
 
 def test_guided_graph_replay_equals_eager_and_persistent_refused(guided):
