@@ -5,48 +5,48 @@
 namespace m3 {
 namespace {
 
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
+template <int FMT, int NB, bool LDS, bool GLU, int KU>
 hipError_t configure_one() {
   static hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(gemv_kernel<FMT, NB, MFMA, LDS, GLU, KU>),
+      reinterpret_cast<const void*>(gemv_kernel<FMT, NB, LDS, GLU, KU>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   return status;
 }
 
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
+template <int FMT, int NB, bool LDS, bool GLU, int KU>
 hipError_t launch_ku(const Params& p, int grid, size_t smem, hipStream_t s) {
-  const hipError_t e = configure_one<FMT, NB, MFMA, LDS, GLU, KU>();
+  const hipError_t e = configure_one<FMT, NB, LDS, GLU, KU>();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_kernel<FMT, NB, MFMA, LDS, GLU, KU>), dim3(grid), dim3(kThreads), smem,
+  hipLaunchKernelGGL((gemv_kernel<FMT, NB, LDS, GLU, KU>), dim3(grid), dim3(kThreads), smem,
                      s, p);
   return hipGetLastError();
 }
 
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU>
+template <int FMT, int NB, bool LDS, bool GLU>
 hipError_t launch_epi(const Params& p, int grid, size_t smem, hipStream_t s) {
-  return launch_ku<FMT, NB, MFMA, LDS, GLU, (LDS && FMT == M3_I8G128) ? 4 : 8>(p, grid, smem, s);
+  return launch_ku<FMT, NB, LDS, GLU, (LDS && FMT == M3_I8G128) ? 4 : 8>(p, grid, smem, s);
 }
 
-template <int FMT, int NB, bool MFMA, bool LDS>
+template <int FMT, int NB, bool LDS>
 hipError_t launch_one(const Params& p, int grid, size_t smem, hipStream_t s) {
-  if (p.epi == M3_EPI_SWIGLU) return launch_epi<FMT, NB, MFMA, LDS, true>(p, grid, smem, s);
-  return launch_epi<FMT, NB, MFMA, LDS, false>(p, grid, smem, s);
+  if (p.epi == M3_EPI_SWIGLU) return launch_epi<FMT, NB, LDS, true>(p, grid, smem, s);
+  return launch_epi<FMT, NB, LDS, false>(p, grid, smem, s);
 }
 
 template <int FMT, bool LDS>
 hipError_t dispatch_b(const Params& p, int grid, size_t smem, hipStream_t s) {
   const int B = p.B;
-  if (B <= 16) return launch_one<FMT, 16, true, LDS>(p, grid, smem, s);
-  if (B <= 32) return launch_one<FMT, 32, true, LDS>(p, grid, smem, s);
-  if (B <= 48) return launch_one<FMT, 48, true, LDS>(p, grid, smem, s);
-  return launch_one<FMT, 64, true, LDS>(p, grid, smem, s);
+  if (B <= 16) return launch_one<FMT, 16, LDS>(p, grid, smem, s);
+  if (B <= 32) return launch_one<FMT, 32, LDS>(p, grid, smem, s);
+  if (B <= 48) return launch_one<FMT, 48, LDS>(p, grid, smem, s);
+  return launch_one<FMT, 64, LDS>(p, grid, smem, s);
 }
 
 template <int FMT, bool LDS, bool GLU, int KU>
 hipError_t configure_ku() {
   const hipError_t es[] = {
-      configure_one<FMT, 16, true, LDS, GLU, KU>(),  configure_one<FMT, 32, true, LDS, GLU, KU>(),
-      configure_one<FMT, 48, true, LDS, GLU, KU>(),  configure_one<FMT, 64, true, LDS, GLU, KU>()};
+      configure_one<FMT, 16, LDS, GLU, KU>(),  configure_one<FMT, 32, LDS, GLU, KU>(),
+      configure_one<FMT, 48, LDS, GLU, KU>(),  configure_one<FMT, 64, LDS, GLU, KU>()};
   for (hipError_t e : es)
     if (e != hipSuccess) return e;
   return hipSuccess;

@@ -25,11 +25,9 @@
 //    workgroup in LDS (row stride padded by 16 B against bank conflicts) and
 //    re-used for every tile; workgroups loop over row blocks when there are
 //    more blocks than resident workgroups.
-//  * Few rows (B <= 2): VALU path, v_dot2_f32_bf16 on bf16 pairs; lane l holds
-//    row l%16 and one 16-byte K-chunk of each tile, partial sums meet with two
-//    cross-lane exchanges.  B >= 3: the product goes to
-//    v_mfma_f32_16x16x32_bf16 (A = 16 activation rows, B = the weight tile,
-//    exactly the packed lane layout).
+//  * Every row count runs on v_mfma_f32_16x16x32_bf16 in tiles of 16
+//    activation rows (A = 16 activation rows, B = the weight tile, exactly
+//    the packed lane layout); rows past B repeat row B-1 and are not stored.
 //  * int8 is dequantised to bf16 exactly (|q| <= 127 has 7 significant bits)
 //    with one SDWA sign-extending convert per byte; scales are applied per row
 //    (i8row) or per group of 128 along K (i8g128).
@@ -945,86 +943,13 @@ __device__ __forceinline__ uint4 ldw(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
 // flight.
 
 // ---------------------------------------------------------------------------
-// VALU accumulators: NB activation rows (B <= NB); lane = (row l%16, K-chunk
-// l/16); partial sums of the 4 lanes of a row meet with two exchanges.
-// ---------------------------------------------------------------------------
-template <int FMT, int NB, bool MFMA>
-struct Accum {
-  float acc[NB], gacc[NB];
-
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = gacc[b] = 0.f;
-  }
-
-  template <bool LDS, bool COH>
-  __device__ __forceinline__ void tile(const Params& p, const uint16_t* act, const uint4& wv, int k0,
-                                       const Tags& tg) {
-    float* dst = FMT == M3_I8G128 ? gacc : acc;
-    const int c = (threadIdx.x & 63) >> 4;
-    if constexpr (FMT == M3_BF16) {
-      const int kk = k0 + c * 8;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        // rows past B repeat row B-1 (valid memory); their sums are never stored
-        const uint4 av = act8<LDS, COH>(p, act, min(b, p.B - 1), kk, tg);
-        float a = dst[b];
-        a = dot2(wv.x, av.x, a);
-        a = dot2(wv.y, av.y, a);
-        a = dot2(wv.z, av.z, a);
-        a = dot2(wv.w, av.w, a);
-        dst[b] = a;
-      }
-    } else {
-      const int kk = k0 + c * 16;
-      uint32_t wb[8];
-      bytes16_to_bf16<FMT>(wv, wb);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int bb = min(b, p.B - 1);
-        const uint4 a0 = act8<LDS, COH>(p, act, bb, kk, tg);
-        const uint4 a1 = act8<LDS, COH>(p, act, bb, kk + 8, tg);
-        float a = dst[b];
-        a = dot2(wb[0], a0.x, a);
-        a = dot2(wb[1], a0.y, a);
-        a = dot2(wb[2], a0.z, a);
-        a = dot2(wb[3], a0.w, a);
-        a = dot2(wb[4], a1.x, a);
-        a = dot2(wb[5], a1.y, a);
-        a = dot2(wb[6], a1.z, a);
-        a = dot2(wb[7], a1.w, a);
-        dst[b] = a;
-      }
-    }
-  }
-
-  // end of a group of 128 (i8g128): scale the group's partial sums
-  __device__ __forceinline__ void group_end(float s) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      acc[b] = fmaf(s, gacc[b], acc[b]);
-      gacc[b] = 0.f;
-    }
-  }
-
-  __device__ __forceinline__ void to_red(float* red, int wave) const {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float v = pair_sum16(pair_sum32(acc[b]));   // lanes l, l^16, l^32, l^48
-      if (lane < 16) red[(wave * NB + b) * 16 + lane] = v;
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
 // MFMA accumulators: NB/16 tiles of 16 activation rows.  D[i][j] += sum_k
 // A[i][k] B[k][j] with A = activations (row i = lane%16 of a tile), B = the
 // weight tile (column j = weight row lane%16); lane l supplies k = 8*(l/16)
 // .. +7 of each operand and receives D[4*(l/16) + q][l%16], q = 0..3.
 // ---------------------------------------------------------------------------
 template <int FMT, int NB>
-struct Accum<FMT, NB, true> {
+struct Accum {
   static constexpr int NT = NB / 16;
   f32x4_t acc[NT], gacc[NT];
 
@@ -1110,7 +1035,7 @@ struct NoWait {
   __device__ uint32_t* err() const { return nullptr; }
 };
 
-template <int FMT, int NB, bool MFMA, bool LDS, int GLU, int KU, bool COH, class Wait>
+template <int FMT, int NB, bool LDS, int GLU, int KU, bool COH, class Wait>
 __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg, int nwg, Wait&& wt) {
   constexpr int kU = KU;
   static_assert(kU % 2 == 0 && kU <= 16, "batches hold whole i8g128 groups");
@@ -1186,7 +1111,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
     }
   };
 
-  Accum<FMT, NB, MFMA> A;
+  Accum<FMT, NB> A;
   A.reset();
   auto compute = [&](const uint4* src, const float* scv, int j) {
     const int rb = block_of(j), bi = j % nbat;
@@ -1256,10 +1181,10 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
 // One GEMV per launch (the C-ABI entry points and the graph-replayed frame).
 // GLU selects the SwiGLU epilogue at compile time (its own kernel symbol, so
 // the gate/up GEMVs can be told apart in a profile).
-template <int FMT, int NB, bool MFMA, bool LDS, bool GLU, int KU>
+template <int FMT, int NB, bool LDS, bool GLU, int KU>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(Params p) {
   extern __shared__ __align__(16) uint8_t smem[];
-  gemv_run<FMT, NB, MFMA, LDS, GLU ? 1 : 0, KU, false>(p, smem, blockIdx.x, gridDim.x, NoWait{});
+  gemv_run<FMT, NB, LDS, GLU ? 1 : 0, KU, false>(p, smem, blockIdx.x, gridDim.x, NoWait{});
 }
 
 // ---------------------------------------------------------------------------

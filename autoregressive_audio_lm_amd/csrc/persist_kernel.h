@@ -91,7 +91,7 @@ typedef const __attribute__((address_space(4))) Phase* CPhasePtr;
 // constant address space, i.e. with scalar loads into wave-uniform registers
 template <int FMT, int NB, class W>
 __device__ __forceinline__ void run_variant(CPhasePtr ph, uint8_t* smem, int wg, int nwg, W& wait) {
-  gemv_run<FMT, NB, (NB >= 16), true, kGluRuntime, FMT == M3_I8G128 ? 4 : 8, true>(
+  gemv_run<FMT, NB, true, kGluRuntime, FMT == M3_I8G128 ? 4 : 8, true>(
       *(const Params*)&ph->p, smem, wg, nwg, wait);
 }
 
