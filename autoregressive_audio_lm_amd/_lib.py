@@ -71,6 +71,21 @@ class FrameLayout(ctypes.Structure):
                                                "vcache", "dkcache", "dvcache", "attn_ws", "total")]
 
 
+class PhaseRegion(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_uint64), ("stride", ctypes.c_uint64), ("rows", _I),
+                ("c0", ctypes.c_uint32), ("c1", ctypes.c_uint32), ("producer", _I), ("tagged", _I),
+                ("pad", _I)]
+
+
+PHASE_MAX_REGIONS = 4
+PHASE_GEMV, PHASE_FRAME_END = 0, 1
+
+
+class PhaseRecord(ctypes.Structure):
+    _fields_ = [("kind", _I), ("n_in", _I), ("n_out", _I), ("pad", _I),
+                ("inp", PhaseRegion * PHASE_MAX_REGIONS), ("out", PhaseRegion * PHASE_MAX_REGIONS)]
+
+
 M3_ERR_ATTN_FULL = 2      # frame state err word: the frame position reached max_pos
 
 _lib = None
@@ -117,6 +132,7 @@ _SIGS = {
     "m3_frame_persistent_destroy": (_I, [_P]),
     "m3_frame_persistent_clock_bytes": (ctypes.c_size_t, [_P]),
     "m3_stream_read": (_I, [_P, ctypes.c_size_t, _P, _I, _I, _P]),
+    "m3_frame_phase_table": (_I, [ctypes.POINTER(Model), _P, _I, _P, ctypes.POINTER(PhaseRecord), _I]),
     "m3_frame_persistent_clock": (_I, [_P, _P, ctypes.c_size_t, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
 }
 

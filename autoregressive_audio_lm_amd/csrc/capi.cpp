@@ -14,6 +14,8 @@
 
 #include "m3_internal.h"
 
+#include <vector>
+
 using namespace m3;
 
 namespace {
@@ -217,7 +219,9 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.ring = take((size_t)16 * B * 8 * 4);
   L.frame = take(4);
   L.part_sem = take((size_t)B * n_blocks(d.V0) * sizeof(Best));
-  L.part_dep = take((size_t)B * n_blocks(d.CV) * sizeof(Best));
+  // one set of row-block winners per depth step (each is read by the next
+  // step's gather and the frame end; none is written twice in a frame)
+  L.part_dep = take((size_t)(d.ncb - 1) * B * n_blocks(d.CV) * sizeof(Best));
   L.flags = take((size_t)kPersistFlags * 4);
   L.err = take(4);
   L.seq = take(4);
@@ -394,7 +398,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   int32_t* ring = reinterpret_cast<int32_t*>(S + L.ring);
   uint32_t* frame = reinterpret_cast<uint32_t*>(S + L.frame);
   Best* part_sem = reinterpret_cast<Best*>(S + L.part_sem);
-  Best* part_dep = reinterpret_cast<Best*>(S + L.part_dep);
+  // depth step j's (1-based) row-block winners
+  auto part_dep = [&](int j) {
+    return reinterpret_cast<Best*>(S + L.part_dep) + (size_t)(j - 1) * B * n_blocks(d.CV);
+  };
   const float eps = c.eps;
   // index of the next step, and the step that last wrote each stream (-1:
   // none in this frame; the frame input is a plain buffer)
@@ -545,7 +552,7 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     GatherPro gp;
     gp.u = u;
     gp.emb = j == 1 ? m->emb1 : m->emb[j - 2];
-    gp.part = j == 1 ? part_sem : part_dep;
+    gp.part = j == 1 ? part_sem : part_dep(j - 1);
     gp.nparts = guided ? 1 : (j == 1 ? n_blocks(d.V0) : n_blocks(d.CV));
     gp.index_base = j == 1 ? c.vocab_base : 0;
     gp.code_base = j == 1 ? c.vocab_base : 0;
@@ -609,13 +616,13 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
                   M3_EPI_RESIDUAL, hd_o, d.D, dn));
     }
     uint16_t* hd = hd_slot(j, c.d_layers);    // the step's output
-    SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep};
+    SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep(j)};
     Prod hp;
     hp.x = p_hd;
     p_dep = ph;
     M3_TRY(gemv(c.fmt_depth, m->heads[j - 1], d.CV, d.D, hd, d.D, m->d_final_norm, 0, 0, dlogits,
                 d.CV, 1, M3_EPI_NONE, nullptr, 0, hp, guided ? nullptr : &dep));
-    if (guided) M3_TRY(guided_draw(dlogits, d.CV, (uint32_t)j, 0, part_dep));
+    if (guided) M3_TRY(guided_draw(dlogits, d.CV, (uint32_t)j, 0, part_dep(j)));
   }
   // ---- last draw, feedback, code ring, frame counter ----
   FeedbackTags ft;
@@ -626,10 +633,81 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     ft.h_out = h_plain_out;
     ft.seq = reinterpret_cast<uint32_t*>(S + L.seq);
   }
-  M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep, guided ? 1 : n_blocks(d.CV),
+  M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep(d.ncb - 1),
+                       guided ? 1 : n_blocks(d.CV),
                        c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame, ft));
   return M3_OK;
 }
+
+// The persistent frame's steps as plain records of the memory each reads and
+// writes (m3_frame_phase_table): byte ranges [lo, hi) with the producing
+// step of what is read (-1: written before the launch or, for the frame end,
+// earlier in the same launch) and whether the words carry tags.
+struct RecordSink final : FrameSink {
+  std::vector<m3_phase_record> recs;
+  static m3_phase_region rows(const void* base, int B, size_t ld, size_t c0, size_t c1, size_t esz,
+                              int producer, int tagged) {
+    m3_phase_region r{};
+    r.base = reinterpret_cast<uint64_t>(base);
+    r.stride = ld * esz;
+    r.rows = B;
+    r.c0 = (uint32_t)(c0 * esz);
+    r.c1 = (uint32_t)(c1 * esz);
+    r.producer = producer;
+    r.tagged = tagged;
+    return r;
+  }
+  static void add(m3_phase_region* list, int32_t& n, const m3_phase_region& r) {
+    if (n < M3_PHASE_MAX_REGIONS) list[n++] = r;
+  }
+  hipError_t gemv(const GemvDesc& d) override {
+    m3_phase_record r{};
+    r.kind = M3_PHASE_GEMV;
+    const int B = d.B;
+    if (d.gather) {
+      const GatherPro& g = *d.gather;
+      add(r.in, r.n_in, rows(g.u, B, d.K, 0, d.K, d.pu >= 0 ? 4 : 2, d.pu, d.pu >= 0));
+      add(r.in, r.n_in, rows(g.part, B, g.nparts, 0, g.nparts, sizeof(Best), d.ppart, d.ppart >= 0));
+      add(r.out, r.n_out, rows(g.out, B, d.K, 0, d.K, d.ytag ? 4 : 2, -1, d.ytag));
+      add(r.out, r.n_out, rows(g.codes, B, 8, g.code_col, g.code_col + 1, 4, -1, 0));
+    } else {
+      // the attention stub reads the value heads only
+      const size_t c0 = d.stub_group > 0 ? (size_t)d.stub_voff : 0;
+      const size_t c1 = d.stub_group > 0 ? c0 + (size_t)d.K / d.stub_group : (size_t)d.K;
+      add(r.in, r.n_in, rows(d.x, B, d.ldx, c0, c1, d.px >= 0 ? 4 : 2, d.px, d.px >= 0));
+    }
+    if (d.epi == M3_EPI_RESIDUAL)
+      add(r.in, r.n_in, rows(d.res, B, d.ldr, 0, d.N, d.pres >= 0 ? 4 : 2, d.pres, d.pres >= 0));
+    const size_t ncols = d.epi == M3_EPI_SWIGLU ? (size_t)d.N / 2 : (size_t)d.N;
+    const size_t esz = d.out_f32 ? 4 : (d.ytag ? 4 : 2);
+    add(r.out, r.n_out, rows(d.y, B, d.ldy, 0, ncols, esz, -1, d.out_f32 ? 0 : d.ytag));
+    if (d.sample) {
+      const int nb = n_blocks(d.N);
+      add(r.out, r.n_out, rows(d.sample->part, B, nb, 0, nb, sizeof(Best), -1, d.ytag));
+    }
+    recs.push_back(r);
+    return hipSuccess;
+  }
+  hipError_t cfg_draw(const CfgDesc&) override { return hipErrorInvalidValue; }
+  hipError_t attention(const AttnStep&, int) override { return hipErrorInvalidValue; }
+  hipError_t feedback(const uint16_t*, const uint16_t* const*, int32_t* codes, const Best* last_part,
+                      int last_nparts, int32_t, int, int, int, int B, int H, uint16_t* x,
+                      int32_t* ring, uint32_t* frame, const FeedbackTags& ft) override {
+    m3_phase_record r{};
+    r.kind = M3_PHASE_FRAME_END;
+    add(r.in, r.n_in, rows(last_part, B, last_nparts, 0, last_nparts, sizeof(Best),
+                           ft.last_part_prod, ft.last_part_prod >= 0));
+    add(r.in, r.n_in, rows(ft.th, B, H, 0, H, ft.th_prod >= 0 ? 4 : 2, ft.th_prod, ft.th_prod >= 0));
+    add(r.in, r.n_in, rows(codes, B, 8, 0, 7, 4, -1, 0));
+    add(r.out, r.n_out, rows(x, B, H, 0, H, 2, -1, 0));
+    add(r.out, r.n_out, rows(ft.h_out, B, H, 0, H, 2, -1, 0));
+    add(r.out, r.n_out, rows(codes, B, 8, 7, 8, 4, -1, 0));
+    add(r.out, r.n_out, rows(ring, 16 * B, 8, 0, 8, 4, -1, 0));
+    (void)frame;
+    recs.push_back(r);
+    return hipSuccess;
+  }
+};
 
 int enqueue_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, hipStream_t s) {
   LaunchSink sink(s);
@@ -1213,6 +1291,27 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   }
   *handle_out = PL;
   return M3_OK;
+}
+
+int m3_frame_phase_table(const m3_model* model, void* state, int B, int32_t* codes,
+                         m3_phase_record* out, int max_records) {
+  if (!model || !state || !codes) return M3_ERR_NULL;
+  int st = validate_config(&model->cfg, B);
+  if (st != M3_OK) return st;
+  st = validate_model(model);
+  if (st != M3_OK) return st;
+  const m3_config& c = model->cfg;
+  if (c.top_k > 0 || c.attention) return M3_ERR_FORMAT;
+  RecordSink sink;
+  st = build_frame(model, static_cast<uint8_t*>(state), B, codes, sink, true);
+  if (st == M3_ERR_HIP) st = M3_ERR_SHAPE;
+  if (st != M3_OK) return st;
+  const int n = (int)sink.recs.size();
+  if (out) {
+    if (max_records < n) return M3_ERR_WORKSPACE;
+    for (int i = 0; i < n; ++i) out[i] = sink.recs[i];
+  }
+  return n;
 }
 
 int m3_frame_persistent_launch(void* handle, void* stream) {

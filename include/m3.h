@@ -557,6 +557,40 @@ size_t m3_frame_persistent_clock_bytes(void* handle);
 int m3_frame_persistent_clock(void* handle, uint64_t* clk, size_t clk_bytes, int* n_phases,
                               int* n_workgroups);
 
+/* The persistent frame's steps as records of the memory each step reads and
+ * writes (host only: nothing is launched and no memory is touched; the state
+ * and model pointers only fix addresses).  Record i is step i of the
+ * persistent launch (a GEMV, or the frame end, which runs after every
+ * workgroup has finished every GEMV); a region is `rows` rows of bytes
+ * [base + r stride + c0, base + r stride + c1), with the step that produced
+ * what is read (-1: written
+ * before the launch, or by an earlier GEMV of the frame for the frame end)
+ * and whether its 32-bit words carry the producer's tag.  A consumer waits
+ * for the tags of its producer, so the ordering this rests on can be checked
+ * from the table: every tagged input is written by its producer, earlier,
+ * and no byte is written twice in a frame.  Returns the number of steps, or
+ * M3_ERR_* (M3_ERR_WORKSPACE: out has fewer than that many records; out may
+ * be NULL to count; M3_ERR_FORMAT: the frame has no persistent form). */
+#define M3_PHASE_MAX_REGIONS 4
+enum { M3_PHASE_GEMV = 0, M3_PHASE_FRAME_END = 1 };
+typedef struct {
+  uint64_t base, stride;
+  int32_t rows;
+  uint32_t c0, c1;
+  int32_t producer;
+  int32_t tagged;
+  int32_t pad;
+} m3_phase_region;
+typedef struct {
+  int32_t kind;
+  int32_t n_in, n_out;
+  int32_t pad;
+  m3_phase_region in[M3_PHASE_MAX_REGIONS];
+  m3_phase_region out[M3_PHASE_MAX_REGIONS];
+} m3_phase_record;
+int m3_frame_phase_table(const m3_model* model, void* state, int B, int32_t* codes,
+                         m3_phase_record* out /* host */, int max_records);
+
 /* ---- measurement ------------------------------------------------------------ */
 /* A plain streaming read of `bytes` at buf (16-byte aligned, a multiple of 16,
  * below 2 GiB): `workgroups` (1..4096) workgroups of 512 lanes read it with 16-byte
