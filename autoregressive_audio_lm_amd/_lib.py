@@ -49,7 +49,7 @@ class Config(ctypes.Structure):
                                   "fmt_lm", "fmt_depth")] + \
                [("eps", ctypes.c_float), ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64),
                 ("cfg_scale", ctypes.c_float), ("top_k", _I),
-                ("attention", _I), ("max_pos", _I), ("pos0", _I)]
+                ("attention", _I), ("max_pos", _I), ("pos0", _I), ("end_id", _I)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -68,7 +68,7 @@ class FrameLayout(ctypes.Structure):
                                                "dmlp", "dlogits", "ring", "frame", "part_sem", "part_dep",
                                                "flags", "err", "seq", "phases", "th", "tqkv", "tmlp", "tu",
                                                "thd", "tdqkv", "tdmlp", "th2", "thd2", "ho", "hdo", "rope", "aq", "ao", "dao", "kcache",
-                                               "vcache", "dkcache", "dvcache", "attn_ws", "total")]
+                                               "vcache", "dkcache", "dvcache", "attn_ws", "stop", "total")]
 
 
 class PhaseRegion(ctypes.Structure):

@@ -107,6 +107,8 @@ int gemv_entry(int fmt, const void* w, int N, int K, const uint16_t* x, int B, i
 // ---- frame -------------------------------------------------------------------
 struct Dims {
   int H, nq, nkv, nqkv, F, D, dq, dqkv, Fd, V0, CV, ncb;
+  int e;       // 1: the lm_head's row 0 is the end token
+  int VL, ldl; // lm_head rows (V0 + e) and the logits' row stride
 };
 
 Dims dims_of(const m3_config& c) {
@@ -123,6 +125,9 @@ Dims dims_of(const m3_config& c) {
   d.V0 = c.n_slice;
   d.CV = c.code_vocab;
   d.ncb = c.n_codebooks;
+  d.e = c.end_id >= 0 ? 1 : 0;
+  d.VL = d.V0 + d.e;
+  d.ldl = (d.VL + 7) / 8 * 8;
   return d;
 }
 
@@ -148,6 +153,9 @@ int validate_config(const m3_config* c, int B) {
   if (c->d_heads < 1) return M3_ERR_SHAPE;
   if (c->n_codebooks < 2 || c->n_codebooks > 8) return M3_ERR_SHAPE;
   if (c->n_slice < 1 || c->code_vocab < 1 || c->vocab_base < 0) return M3_ERR_SHAPE;
+  // the end token sorts before the codes (row 0 of the lm_head)
+  if (c->end_id >= c->vocab_base || (c->end_id >= 0 && c->top_k > 0 && c->n_slice + 1 > M3_MAX_V_CFG))
+    return M3_ERR_SHAPE;
   if (!(c->temperature > 0.0f) || !std::isfinite(c->temperature)) return M3_ERR_SHAPE;
   if (!(c->eps >= 0.0f) || !std::isfinite(c->eps)) return M3_ERR_SHAPE;
   const Dims d = dims_of(*c);
@@ -210,7 +218,7 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.h = take(nL * B * d.H * 2);
   L.qkv = take(nL * B * d.nqkv * 2);
   L.mlp = take(nL * B * d.F * 2);
-  L.logits = take((size_t)B * d.V0 * 4);
+  L.logits = take((size_t)B * d.ldl * 4);
   L.u = take((size_t)B * d.D * 2);
   L.hd = take(nHD * B * d.D * 2);
   L.dqkv = take(nDL * B * d.dqkv * 2);
@@ -218,7 +226,7 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.dlogits = take(nS * B * d.CV * 4);
   L.ring = take((size_t)16 * B * 8 * 4);
   L.frame = take(4);
-  L.part_sem = take((size_t)B * n_blocks(d.V0) * sizeof(Best));
+  L.part_sem = take((size_t)B * n_blocks(d.VL) * sizeof(Best));
   // one set of row-block winners per depth step (each is read by the next
   // step's gather and the frame end; none is written twice in a frame)
   L.part_dep = take((size_t)(d.ncb - 1) * B * n_blocks(d.CV) * sizeof(Best));
@@ -250,6 +258,7 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.dkcache = take(dkv);
   L.dvcache = take(dkv);
   L.attn_ws = take(at ? attn_workspace_bytes(B, c.n_heads, c.n_kv_heads, c.max_pos) : 0);
+  L.stop = take((size_t)B * 4);
   L.total = off;
   return L;
 }
@@ -333,9 +342,9 @@ struct LaunchSink final : FrameSink {
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
-                      uint32_t* frame, const FeedbackTags&) override {
+                      uint32_t* frame, const FeedbackTags& ft) override {
     return launch_feedback(tok, aemb, codes, last_part, last_nparts, vocab_base, n_slice,
-                           code_vocab, n_cb, B, H, x, ring, frame, s);
+                           code_vocab, n_cb, B, H, x, ring, frame, ft.end_id, ft.stop, s);
   }
 };
 
@@ -510,12 +519,14 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   // unconditional) row pairs, top-k, Gumbel-argmax; one draw per song, left
   // as a one-entry winner record per row for the same consumers.
   const bool guided = c.top_k > 0;
-  auto guided_draw = [&](const float* lg, int V, uint32_t draw, int32_t base, Best* part) {
+  auto guided_draw = [&](const float* lg, int V, int ldl, uint32_t draw, int32_t base,
+                         int32_t end_id, Best* part) {
     CfgDesc g{};
     g.logits = lg;
     g.S = B / 2;
     g.V = V;
-    g.ldl = V;
+    g.ldl = ldl;
+    g.end_id = end_id;
     g.scale = c.cfg_scale;
     g.top_k = c.top_k;
     g.seed = c.seed;
@@ -525,20 +536,23 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     g.index_base = base;
     g.part = part;
     g.out_stride = 1;
-    g.vec4 = V % 4 == 0;
+    g.vec4 = ldl % 4 == 0;
     ++ph;
     return sink.cfg_draw(g);
   };
   // ---- sliced lm_head; its epilogue adds the Gumbel noise of draw 0 and
   // leaves each row block's winner; the draw completes in the next consumer
-  SampleEpi sem{c.seed, frame, 0u, c.temperature, c.vocab_base, c.vocab_base,
-                c.vocab_base + c.n_slice, part_sem};
+  // (with the end token: column 0 is it, column 1 + i code i)
+  const int32_t end_id = d.e ? c.end_id : -1;
+  const int32_t lm_base = c.vocab_base - d.e;     // absolute id of column n >= e is lm_base + n
+  SampleEpi sem{c.seed, frame, 0u, c.temperature, lm_base, c.vocab_base,
+                c.vocab_base + c.n_slice, part_sem, end_id};
   Prod lm;
   lm.x = p_h;
   p_sem = ph;
-  M3_TRY(gemv(c.fmt_lm, m->lm_head, d.V0, d.H, h_out, d.H, m->final_norm, 0, 0, logits, d.V0, 1,
+  M3_TRY(gemv(c.fmt_lm, m->lm_head, d.VL, d.H, h_out, d.H, m->final_norm, 0, 0, logits, d.ldl, 1,
               M3_EPI_NONE, nullptr, 0, lm, guided ? nullptr : &sem));
-  if (guided) M3_TRY(guided_draw(logits, d.V0, 0u, c.vocab_base, part_sem));
+  if (guided) M3_TRY(guided_draw(logits, d.VL, d.ldl, 0u, lm_base, end_id, part_sem));
   // ---- depth decoder ----
   Prod pin;
   pin.x = p_h;
@@ -553,8 +567,9 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     gp.u = u;
     gp.emb = j == 1 ? m->emb1 : m->emb[j - 2];
     gp.part = j == 1 ? part_sem : part_dep(j - 1);
-    gp.nparts = guided ? 1 : (j == 1 ? n_blocks(d.V0) : n_blocks(d.CV));
-    gp.index_base = j == 1 ? c.vocab_base : 0;
+    gp.nparts = guided ? 1 : (j == 1 ? n_blocks(d.VL) : n_blocks(d.CV));
+    gp.index_base = j == 1 ? lm_base : 0;
+    gp.end_id = j == 1 ? end_id : -1;
     gp.code_base = j == 1 ? c.vocab_base : 0;
     gp.n_codes = j == 1 ? c.n_slice : c.code_vocab;
     gp.codes = codes;
@@ -616,13 +631,13 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
                   M3_EPI_RESIDUAL, hd_o, d.D, dn));
     }
     uint16_t* hd = hd_slot(j, c.d_layers);    // the step's output
-    SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep(j)};
+    SampleEpi dep{c.seed, frame, (uint32_t)j, c.temperature, 0, 0, 0, part_dep(j), -1};
     Prod hp;
     hp.x = p_hd;
     p_dep = ph;
     M3_TRY(gemv(c.fmt_depth, m->heads[j - 1], d.CV, d.D, hd, d.D, m->d_final_norm, 0, 0, dlogits,
                 d.CV, 1, M3_EPI_NONE, nullptr, 0, hp, guided ? nullptr : &dep));
-    if (guided) M3_TRY(guided_draw(dlogits, d.CV, (uint32_t)j, 0, part_dep(j)));
+    if (guided) M3_TRY(guided_draw(dlogits, d.CV, d.CV, (uint32_t)j, 0, -1, part_dep(j)));
   }
   // ---- last draw, feedback, code ring, frame counter ----
   FeedbackTags ft;
@@ -633,6 +648,8 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     ft.h_out = h_plain_out;
     ft.seq = reinterpret_cast<uint32_t*>(S + L.seq);
   }
+  ft.end_id = end_id;
+  ft.stop = end_id >= 0 ? reinterpret_cast<uint32_t*>(S + L.stop) : nullptr;
   M3_TRY(sink.feedback(m->tok_emb_audio, m->audio_emb, codes, part_dep(d.ncb - 1),
                        guided ? 1 : n_blocks(d.CV),
                        c.vocab_base, c.n_slice, c.code_vocab, d.ncb, B, d.H, x, ring, frame, ft));
@@ -1131,7 +1148,7 @@ uint64_t m3_frame_weight_bytes(const m3_config* c) {
   const uint64_t layer = mat_bytes(fb, d.nqkv, d.H) + mat_bytes(fb, d.H, d.nq) +
                          mat_bytes(fb, 2ull * d.F, d.H) + mat_bytes(fb, d.H, d.F);
   uint64_t total = (uint64_t)c->n_layers * layer + 4ull * d.H * (2ull * c->n_layers + 1);
-  total += mat_bytes(c->fmt_lm, d.V0, d.H);
+  total += mat_bytes(c->fmt_lm, d.VL, d.H);
   total += mat_bytes(fd, d.D, d.H);
   const uint64_t dlayer = mat_bytes(fd, d.dqkv, d.D) + mat_bytes(fd, d.D, d.dq) +
                           mat_bytes(fd, 2ull * d.Fd, d.D) + mat_bytes(fd, d.D, d.Fd);
@@ -1264,7 +1281,7 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
       c.attention)
     return M3_ERR_FORMAT;
   // row-block winners carry their column in 16 bits next to the tag
-  if (c.n_slice > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;
+  if (c.n_slice + 1 > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;
   uint8_t* S = static_cast<uint8_t*>(state);
   const m3_frame_layout L = layout_of(model->cfg, B);
   PersistPlan* pl = persist_plan_new(B);

@@ -27,7 +27,8 @@ __global__ __launch_bounds__(256) void fill_kernel(uint32_t* dst, uint32_t v, si
 hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const* audio_emb,
                            int32_t* codes, const Best* last_part, int last_nparts,
                            int32_t vocab_base, int n_slice, int code_vocab, int n_cb, int B,
-                           int H, uint16_t* x_out, int32_t* ring, uint32_t* frame, hipStream_t s) {
+                           int H, uint16_t* x_out, int32_t* ring, uint32_t* frame,
+                           int32_t end_id, uint32_t* stop, hipStream_t s) {
   FeedbackArgs a;
   a.code_vocab = code_vocab;
   a.last_part = last_part;
@@ -48,6 +49,8 @@ hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const*
   a.th_prod = -1;
   a.h_out = nullptr;
   a.seq = nullptr;
+  a.end_id = end_id;
+  a.stop = stop;
   hipLaunchKernelGGL(feedback_kernel, dim3(B), dim3(256), 0, s, a);
   return hipGetLastError();
 }

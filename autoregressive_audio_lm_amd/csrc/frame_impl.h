@@ -34,6 +34,8 @@ struct FeedbackArgs {
   int th_prod;
   uint16_t* h_out;
   uint32_t* seq;                 // nullptr: no launch counter
+  int32_t end_id;                // >= 0: the end token's id
+  uint32_t* stop;                // [B] stop words (nullptr: no end token)
 };
 
 // the last codebook's draw for row b, by one wave (same total order as the sampler)
@@ -120,6 +122,12 @@ __device__ __forceinline__ void feedback_run(const FeedbackArgs& a, int wg, int 
   }
   if (leader) {
     const uint32_t f = ld4<COH>(a.frame, 0);
+    // a row's first end token: its stop word becomes the frame number + 1
+    if (a.stop)
+      for (int b = threadIdx.x; b < a.B; b += nthreads)
+        if ((int32_t)ld4<COH>(a.codes, (size_t)b * 8 * 4) == a.end_id &&
+            ld4<COH>(a.stop, (size_t)b * 4) == 0u)
+          st4<COH>(a.stop, (size_t)b * 4, f + 1u);
     for (int i = threadIdx.x; i < a.B * 8; i += nthreads) {
       const int b = i >> 3, cb = i & 7;
       const int32_t v = cb == a.n_cb - 1 ? c_last[b] : (int32_t)ld4<COH>(a.codes, (size_t)i * 4);

@@ -486,7 +486,7 @@ __device__ __forceinline__ void gather_codes(const Params& p, int* code_lds, int
     }
     best_reduce(bz, bj, 64);
     if (lane == 0) {
-      const int32_t id = g.index_base + bj;
+      const int32_t id = (g.end_id >= 0 && bj == 0) ? g.end_id : g.index_base + bj;
       code_lds[b] = id;
       if (wg == 0) st4<COH>(g.codes, (size_t)(b * 8 + g.code_col) * 4, (uint32_t)id);
     }
@@ -887,9 +887,9 @@ __device__ __forceinline__ void finish_block(const Params& p, const uint8_t* blk
         for (int w = 0; w < kWaves; ++w) v += red[(w * NB + b) * 16 + r];
         v *= row_scale<FMT>(blk, p, r);
         st4<COH>(p.y, ((size_t)b * p.ldy + n) * 4, __float_as_uint(v));
-        const int32_t id = sm.index_base + n;
+        const int32_t id = (sm.end_id >= 0 && n == 0) ? sm.end_id : sm.index_base + n;
         j = n;
-        if (sm.valid_lo < sm.valid_hi && (id < sm.valid_lo || id >= sm.valid_hi))
+        if (sm.valid_lo < sm.valid_hi && (id < sm.valid_lo || id >= sm.valid_hi) && id != sm.end_id)
           z = -INFINITY;
         else
           z = gumbel_z(v, inv_t, gumbel_noise(sm.seed, (uint32_t)b, frame, sm.draw, (uint32_t)id));

@@ -39,6 +39,7 @@ struct SampleEpi {
   int32_t index_base;           // absolute id of output row 0
   int32_t valid_lo, valid_hi;   // lo == hi: no mask
   Best* part;
+  int32_t end_id;               // >= 0: output row 0 is this id (the end token; never masked)
 };
 
 // Gather prologue of the first GEMV of a depth-decoder step: the operand row
@@ -55,6 +56,7 @@ struct GatherPro {
   int32_t* codes;
   int code_col;
   uint16_t* out;
+  int32_t end_id;               // >= 0: part's column 0 is this id (the end token)
 };
 
 struct GemvDesc {
@@ -142,6 +144,7 @@ struct CfgDesc {
   int out_stride;
   int vec4;             // logits rows 16-byte aligned (float4 loads)
   Best* part;           // non-null: write {0, column} to part[2s], part[2s+1] instead of ids
+  int32_t end_id = -1;  // >= 0: column 0 is this id (the end token; never masked)
 };
 hipError_t launch_cfg_draw(const CfgDesc& d, hipStream_t s);
 
@@ -188,7 +191,8 @@ hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, i
 hipError_t launch_feedback(const uint16_t* tok_emb_audio, const uint16_t* const* audio_emb,
                            int32_t* codes, const Best* last_part, int last_nparts,
                            int32_t vocab_base, int n_slice, int code_vocab, int n_cb, int B,
-                           int H, uint16_t* x_out, int32_t* ring, uint32_t* frame, hipStream_t s);
+                           int H, uint16_t* x_out, int32_t* ring, uint32_t* frame, int32_t end_id, uint32_t* stop,
+                           hipStream_t s);
 hipError_t launch_copy_bf16(const uint16_t* src, uint16_t* dst, size_t n, hipStream_t s);
 
 // ---- persistent frame (persist.hip) -------------------------------------------
@@ -206,6 +210,9 @@ struct FeedbackTags {
   int th_prod = -1;              // step that last wrote it
   uint16_t* h_out = nullptr;     // plain copy of it for the caller
   uint32_t* seq = nullptr;       // launch counter
+  // (every frame path) the end token and the rows' stop words
+  int32_t end_id = -1;
+  uint32_t* stop = nullptr;
 };
 size_t persist_phase_bytes();
 int persist_max_phases();

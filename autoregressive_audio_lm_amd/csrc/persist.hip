@@ -123,6 +123,8 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
   a.th_prod = ft.th_prod;
   a.h_out = ft.h_out;
   a.seq = ft.seq;
+  a.end_id = ft.end_id;
+  a.stop = ft.stop;
   // the frame end waits (on the flags) for every workgroup to finish the step before it
   pl->phases.back().signal = 1;
   Phase ph{};

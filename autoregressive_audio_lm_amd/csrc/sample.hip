@@ -233,6 +233,12 @@ __device__ __forceinline__ int column_ranks(const bool (&f)[G][W], int (&start)[
   return base;
 }
 
+// absolute id of column j (an id list, the end token in column 0, or index_base + j)
+__device__ __forceinline__ int32_t cfg_id(const CfgDesc& d, int j) {
+  if (d.ids) return d.ids[j];
+  return (d.end_id >= 0 && j == 0) ? d.end_id : d.index_base + j;
+}
+
 // The song's draw (column j) to both of its rows: the absolute id, or, for the
 // frame's consumers (the gather prologue, the frame end), a one-entry winner
 // record {0, j} per row.
@@ -242,7 +248,7 @@ __device__ __forceinline__ void cfg_write(const CfgDesc& d, int s, int j) {
     d.part[2 * s + 1] = Best{0.0f, j};
     return;
   }
-  const int32_t id = d.ids ? d.ids[j] : d.index_base + j;
+  const int32_t id = cfg_id(d, j);
   d.out[(size_t)(2 * s) * d.out_stride] = id;
   d.out[(size_t)(2 * s + 1) * d.out_stride] = id;
 }
@@ -327,7 +333,7 @@ __device__ __forceinline__ void cfg_finish(const CfgDesc& d, int s, const uint32
       }
       if (keep) {
         const int j = cols[g][q];
-        const int32_t id = d.ids ? d.ids[j] : d.index_base + j;
+        const int32_t id = cfg_id(d, j);
         const float gn = d.noise ? d.noise[(size_t)s * d.V + j]
                                  : gumbel_noise(d.seed, (uint32_t)s, frame, d.draw, (uint32_t)id);
         const float z = gumbel_z(cfg_value(k[g][q]), invT, gn);
@@ -397,8 +403,8 @@ __global__ __launch_bounds__(kCfgThreads) void cfg_topk_kernel(CfgDesc d) {
       cols[g][q] = j;
       uint32_t key = 0u;
       if (j < d.V) {
-        const int32_t id = d.ids ? d.ids[j] : d.index_base + j;
-        if (!(d.valid_lo < d.valid_hi && (id < d.valid_lo || id >= d.valid_hi))) {
+        const int32_t id = cfg_id(d, j);
+        if (!(d.valid_lo < d.valid_hi && (id < d.valid_lo || id >= d.valid_hi)) || id == d.end_id) {
           const float dl = cv[q] - uv[q];
           const float sd = d.scale * dl;
           const float gv = uv[q] + sd;

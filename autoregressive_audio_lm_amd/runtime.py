@@ -13,7 +13,8 @@ from ._lib import check, lib
 
 def make_config(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int = 0,
                 temperature: float = 1.0, cfg_scale: float = 1.5, top_k: int = 0,
-                attention: int = 0, max_pos: int = 0, pos0: int = 0) -> _lib.Config:
+                attention: int = 0, max_pos: int = 0, pos0: int = 0,
+                end_token: bool = False) -> _lib.Config:
     """top_k == 0: one draw per row; top_k > 0: the reference's draw over
     (conditional, unconditional) row pairs with guidance cfg_scale.
     attention == 0: the identity stub; 1: decode attention over caches of
@@ -26,7 +27,8 @@ def make_config(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int
         d_ffn=cfg["Fd"], n_codebooks=cfg["n_codebooks"], code_vocab=cfg["code_vocab"],
         fmt_body=fmt_body, fmt_lm=fmt_lm, fmt_depth=fmt_depth, eps=float(cfg["eps"]),
         temperature=float(temperature), seed=int(seed), cfg_scale=float(cfg_scale),
-        top_k=int(top_k), attention=int(attention), max_pos=int(max_pos), pos0=int(pos0))
+        top_k=int(top_k), attention=int(attention), max_pos=int(max_pos), pos0=int(pos0),
+        end_id=int(cfg["end_token"]) if end_token else -1)
 
 
 def frame_weight_bytes(c: _lib.Config) -> int:
@@ -43,7 +45,9 @@ class DecodeModel:
 
     def __init__(self, md: dict, seed: int = 0, temperature: float = 1.0,
                  free_sources: bool = False, cfg_scale: float = 1.5, top_k: int = 0,
-                 attention: int = 0, max_pos: int = 0, pos0: int = 0):
+                 attention: int = 0, max_pos: int = 0, pos0: int = 0, end_token: bool = False):
+        """end_token: the semantic draw also takes the end token (its lm_head
+        row md["lm_end"] packed first), and frames set the rows' stop words."""
         cfg = md["cfg"]
         # the C side reads host arrays of these lengths from the config
         nsteps = cfg["n_codebooks"] - 1
@@ -54,7 +58,7 @@ class DecodeModel:
         self.cfg_dict = cfg
         self.fmt_body, self.fmt_lm, self.fmt_depth = md["fmt_body"], md["fmt_lm"], md["fmt_depth"]
         self.config = make_config(cfg, self.fmt_body, self.fmt_lm, self.fmt_depth, seed, temperature,
-                                  cfg_scale, top_k, attention, max_pos, pos0)
+                                  cfg_scale, top_k, attention, max_pos, pos0, end_token)
         self._keep = []
 
         def keep(t):
@@ -100,7 +104,8 @@ class DecodeModel:
             cfg=self.config,
             layers=ctypes.cast(self._layers, ctypes.c_void_p),
             final_norm=keep(md["final_norm"]),
-            lm_head=packed(md["lm_head"], self.fmt_lm),
+            lm_head=packed(torch.cat([md["lm_end"], md["lm_head"]], 0) if end_token
+                           else md["lm_head"], self.fmt_lm),
             p_in=packed(md["p_in"], self.fmt_depth),
             emb1=keep(md["emb1"]),
             emb=ctypes.cast(self._emb, ctypes.c_void_p),
@@ -221,7 +226,17 @@ class FrameState:
 
     @property
     def logits(self):
-        return self.view("logits", torch.float32, self.dm.config.n_slice)
+        """[B, n_slice] fp32 semantic logits ([B, 1 + n_slice] with the end
+        token, column 0)."""
+        c = self.dm.config
+        n = c.n_slice + (1 if c.end_id >= 0 else 0)
+        ld = (n + 7) // 8 * 8
+        return self.view("logits", torch.float32, ld)[:, :n]
+
+    @property
+    def stop(self) -> torch.Tensor:
+        """[B] int32 stop words: 0, or 1 + the frame that drew the end token."""
+        return self.view("stop", torch.int32, 1).view(self.B)
 
     @property
     def frame(self) -> torch.Tensor:

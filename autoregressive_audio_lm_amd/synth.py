@@ -87,6 +87,8 @@ def make_model(cfg: dict, fmt_body: int, fmt_lm: int, fmt_depth: int, seed: int 
     md["layers"] = [layer(li, H, nq, nkv, F, seed) for li in range(L)]
     md["final_norm"] = gamma_f32(H, tensor_seed(seed, 900, 1), device)
     md["lm_head"] = normal_bf16((cfg["V0"], H), tensor_seed(seed, 900, 2), W_STD, device)
+    # the lm_head row of the end token (used when a frame draws it)
+    md["lm_end"] = normal_bf16((1, H), tensor_seed(seed, 900, 5), W_STD, device)
     dseed = seed + 7777
     md["d_layers"] = [layer(li, D, dq, dq, Fd, dseed) for li in range(cfg["d_layers"])]
     md["d_final_norm"] = gamma_f32(D, tensor_seed(dseed, 900, 1), device)

@@ -381,6 +381,20 @@ typedef struct {
   int attention;
   int max_pos;
   int pos0;
+  /* The end of a song (DiffSynth-Studio MiniMax-Music3 stage 2: the semantic
+   * draw is masked to the audio codes and the end token, and generation
+   * stops once the end token is drawn).  end_id < 0: no end token, the draw
+   * is over the n_slice codes (the benchmark configuration).  0 <= end_id <
+   * vocab_base: the lm_head holds n_slice + 1 rows, row 0 the end token's
+   * and row 1 + i code i's, and the draw takes the end token like any other
+   * id (Gumbel noise keyed by end_id; an exact tie goes to the lower id,
+   * i.e. to it).  A row that draws it gets end_id as its semantic code; its
+   * depth step 1 input and frame embedding use code 0's rows (the frame is
+   * still computed, in lockstep with the other rows), and the state's stop
+   * word of the row becomes the frame number + 1 the first time.  The host
+   * reads the stop words (or the end token in the ring) every 16 frames
+   * (TensorFold PR #987, frame pipelining). */
+  int end_id;
 } m3_config;
 
 #define M3_ERR_ATTN_FULL 2u  /* state err word: the frame position reached max_pos */
@@ -400,7 +414,9 @@ typedef struct {
   m3_config cfg;
   const m3_layer_weights* layers;     /* host array [n_layers]                   */
   const float* final_norm;            /* [hidden]                                */
-  const void* lm_head;                /* packed slice [n_slice, hidden] (fmt_lm) */
+  const void* lm_head;                /* packed slice [n_slice, hidden] (fmt_lm);
+                                         [1 + n_slice, hidden] with the end token's
+                                         row first when cfg.end_id >= 0          */
   const void* p_in;                   /* packed [d_hidden, hidden] (fmt_depth)   */
   const uint16_t* emb1;               /* bf16 [n_slice, d_hidden]                */
   const uint16_t* const* emb;         /* host array [n_codebooks-2] of [code_vocab, d_hidden] */
@@ -426,7 +442,8 @@ typedef struct {
                       the last slot is the body output                         */
   size_t qkv;      /* bf16 [L][B, nq+2nkv] each layer's QKV output              */
   size_t mlp;      /* bf16 [L][B, ffn]   each layer's SwiGLU output            */
-  size_t logits;   /* f32  [B, n_slice]  semantic logits of the last frame     */
+  size_t logits;   /* f32  [B, n_slice (+1 with the end token, column 0)]
+                      semantic logits of the last frame                        */
   size_t u;        /* bf16 [B, d_hidden] depth-decoder input projection        */
   size_t hd;       /* bf16 [S][DL+1][B, d_hidden]: for step j (codebook j = 1..7,
                       slot j-1) its input bf16(u + Emb_j[c]) in slot 0 and the
@@ -437,7 +454,7 @@ typedef struct {
   size_t ring;     /* i32  [16, B, 8]    codes of the last 16 frames           */
   size_t frame;    /* u32  frame counter (advanced on the GPU)                 */
   size_t part_sem; /* per-row-block winners of the semantic draw               */
-  size_t part_dep; /* per-row-block winners of the latest depth draw           */
+  size_t part_dep; /* [S]: per-row-block winners of each depth step's draw     */
   size_t flags;    /* u32  [256] per-workgroup progress of the persistent frame */
   size_t err;      /* u32  nonzero: a persistent frame gave up waiting          */
   size_t seq;      /* u32  the persistent frame's epoch (launch counter)       */
@@ -458,6 +475,7 @@ typedef struct {
   size_t kcache, vcache;   /* bf16 [n_layers][B][n_kv][max_pos][128]          */
   size_t dkcache, dvcache; /* bf16 [d_layers][B][d_heads][8][128]             */
   size_t attn_ws;  /* m3_decode_attention's workspace at T = max_pos           */
+  size_t stop;     /* int32 [B]: 0, or 1 + the frame that drew the end token    */
   size_t total;
 } m3_frame_layout;
 

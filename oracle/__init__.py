@@ -93,7 +93,7 @@ class Model(ctypes.Structure):
                 ("audio_emb", _P), ("eps", ctypes.c_float), ("cfg_scale", ctypes.c_float),
                 ("top_k", ctypes.c_int), ("attention", ctypes.c_int), ("max_pos", ctypes.c_int),
                 ("pos0", ctypes.c_int), ("rope", _P), ("kcache", _P), ("vcache", _P),
-                ("dkcache", _P), ("dvcache", _P)]
+                ("dkcache", _P), ("dvcache", _P), ("end_id", ctypes.c_int32)]
 
 
 class FrameTrace(ctypes.Structure):
@@ -409,12 +409,14 @@ class OracleModel:
     struct.  The oracle quantises int8 formats itself from the bf16 sources."""
 
     def __init__(self, md: dict, cfg_scale: float = 1.5, top_k: int = 0, attention: int = 0,
-                 max_pos: int = 0, pos0: int = 0):
+                 max_pos: int = 0, pos0: int = 0, end_token: bool = False):
         """top_k == 0: per-row draws; top_k > 0: the reference's draw over
         (conditional, unconditional) row pairs with guidance cfg_scale.
         attention == 1: decode attention over KV caches of max_pos positions
         (frame f at position pos0 + f); the caches are made zeroed for the
-        batch size of the first frame (and again by reset_attention)."""
+        batch size of the first frame (and again by reset_attention).
+        end_token: the semantic draw also takes the end token, whose lm_head
+        row is md["lm_end"] (m3o_decode_frame)."""
         self._keep = []
         self.md = md
         cfg = md["cfg"]
@@ -458,7 +460,8 @@ class OracleModel:
         self.m = Model(
             cfg["H"], nl, cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["F"],
             ctypes.cast(LA, ctypes.c_void_p), _ptr(keep(md["final_norm"], np.float32)),
-            mat(md["lm_head"], fl, ("lm_head", 0)), cfg["vocab_base"], cfg["V0"],
+            mat(np.concatenate([md["lm_end"], md["lm_head"]], 0) if end_token else md["lm_head"],
+                fl, ("lm_head", 0)), cfg["vocab_base"], cfg["V0"],
             cfg["D"], len(md["d_layers"]), cfg["d_heads"], cfg["d_head_dim"], cfg["Fd"],
             cfg["n_codebooks"], cfg["code_vocab"],
             mat(md["p_in"], fd, ("p_in", 0)), _ptr(keep(md["emb1"], np.uint16)),
@@ -467,6 +470,7 @@ class OracleModel:
             _ptr(keep(md["tok_emb_audio"], np.uint16)), ctypes.cast(aemb_arr, ctypes.c_void_p),
             float(cfg["eps"]), float(cfg_scale), int(top_k), int(attention), int(max_pos),
             int(pos0))
+        self.m.end_id = int(cfg["end_token"]) if end_token else -1
         self.cache_B = None
         if attention:
             self._rope = rope_table(max(max_pos, 8), cfg["head_dim"])
@@ -578,7 +582,7 @@ def decode_frame(om: OracleModel, x_in, seed, frame, temperature=1.0, trace=Fals
     tr = FrameTrace(None, None, None)
     if trace:
         tr_d = {"h_body": np.empty((B, H), np.uint16),
-                "logits0": np.empty((B, cfg["V0"]), np.float32),
+                "logits0": np.empty((B, cfg["V0"] + (om.m.end_id >= 0)), np.float32),
                 "zgap": np.empty((B, 8), np.float32)}
         tr = FrameTrace(_ptr(tr_d["h_body"]), _ptr(tr_d["logits0"]), _ptr(tr_d["zgap"]))
     lib().m3o_decode_frame(ctypes.byref(om.m), _ptr(x), B, int(seed), int(frame),

@@ -721,7 +721,7 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
   int H = m->H, D = m->D;
   int nq = m->n_heads * m->head_dim, nkv = m->n_kv_heads * m->head_dim;
   int dq = m->d_heads * m->d_head_dim;
-  size_t big = (size_t)B * (size_t)(2 * (m->F > m->Fd ? m->F : m->Fd) + nq + 2 * nkv + 3 * dq + m->V0 + 16);
+  size_t big = (size_t)B * (size_t)(2 * (m->F > m->Fd ? m->F : m->Fd) + nq + 2 * nkv + 3 * dq + m->V0 + 17);
   double* y = (double*)malloc(big * sizeof(double));
   uint16_t* h = (uint16_t*)malloc((size_t)B * H * 2);
   uint16_t* a = (uint16_t*)malloc((size_t)B * (H > D ? H : D) * 2);
@@ -730,7 +730,7 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
   uint16_t* mm = (uint16_t*)malloc((size_t)B * (m->F > m->Fd ? m->F : m->Fd) * 2);
   uint16_t* u = (uint16_t*)malloc((size_t)B * D * 2);
   uint16_t* hd = (uint16_t*)malloc((size_t)B * D * 2);
-  float* lg = (float*)malloc((size_t)B * (m->V0 > m->code_vocab ? m->V0 : m->code_vocab) * 4);
+  float* lg = (float*)malloc((size_t)B * (m->V0 + 1 > m->code_vocab ? m->V0 + 1 : m->code_vocab) * 4);
   int32_t* draw_out = (int32_t*)malloc((size_t)B * 4);
   float* zb = (float*)malloc((size_t)B * 4);
   float* z2 = (float*)malloc((size_t)B * 4);
@@ -749,14 +749,19 @@ void m3o_decode_frame(const m3o_model* m, const uint16_t* x_in, int B,
   }
   if (tr && tr->h_body) memcpy(tr->h_body, h, (size_t)B * H * 2);
 
-  /* final norm -> sliced lm_head -> draw 0 over the reachable rows */
+  /* final norm -> sliced lm_head -> draw 0 over the reachable ids: the
+     audio codes, and the end token when the model has it (its own row, its
+     noise keyed by its id, which is below every code's) */
+  int e = m->end_id >= 0 ? 1 : 0, VL = m->V0 + e;
   m3o_rmsnorm(h, B, H, H, m->final_norm, m->eps, a, H);
   m3o_gemv(&m->lm_head, a, B, H, y);
-  for (size_t i = 0; i < (size_t)B * m->V0; ++i) lg[i] = (float)y[i];
-  if (tr && tr->logits0) memcpy(tr->logits0, lg, (size_t)B * m->V0 * 4);
-  m3o_sample_params sp = {seed, frame, 0u, temperature, m->vocab_base, NULL,
-                          m->vocab_base, m->vocab_base + m->V0, NULL};
-  draw_rows(m, lg, B, m->V0, &sp, draw_out, zb, z2);
+  for (size_t i = 0; i < (size_t)B * VL; ++i) lg[i] = (float)y[i];
+  if (tr && tr->logits0) memcpy(tr->logits0, lg, (size_t)B * VL * 4);
+  int32_t* ids = (int32_t*)malloc((size_t)VL * 4);
+  for (int n = 0; n < VL; ++n) ids[n] = (e && n == 0) ? m->end_id : m->vocab_base + n - e;
+  m3o_sample_params sp = {seed, frame, 0u, temperature, 0, ids, 0, 0, NULL};
+  draw_rows(m, lg, B, VL, &sp, draw_out, zb, z2);
+  free(ids);
   for (int b = 0; b < B; ++b) {
     codes[b * 8 + 0] = draw_out[b];
     if (tr && tr->zgap) tr->zgap[b * 8 + 0] = zb[b] - z2[b];

@@ -178,11 +178,17 @@ typedef struct {
   uint16_t* const* vcache;
   uint16_t* const* dkcache;
   uint16_t* const* dvcache;
+  /* the end token ([ds] stage 2: the semantic draw is masked to the audio
+     codes and the end token, and a song ends when it is drawn): end_id < 0
+     none; else lm_head has V0 + 1 rows, row 0 the end token's (id end_id)
+     and row 1 + i code i's */
+  int32_t end_id;
 } m3o_model;
 
 typedef struct {
   uint16_t* h_body;    /* [B, H]  body output before the final norm (optional) */
-  float* logits0;      /* [B, V0] semantic logits (optional)                 */
+  float* logits0;      /* [B, V0] semantic logits ([B, 1 + V0] with the end
+                          token, column 0) (optional)                         */
   float* zgap;         /* [B, 8]  best - second-best z per draw (optional)    */
 } m3o_frame_trace;
 

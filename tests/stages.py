@@ -200,7 +200,15 @@ def check_frame(om, got, x0, seed, frame, body_layers=None, depth_steps=None, ro
                                    frame=frame, draw=j, index_base=base, valid=valid)
         return O.gumbel_argmax(lg, seed=seed, frame=frame, draw=j, index_base=base, valid=valid)
 
-    c0 = draw(got["logits"], 0, base, (base, base + V0))
+    if om.m.end_id >= 0:
+        # column 0 is the end token, column 1 + i code i
+        ids = np.concatenate([[om.m.end_id], base + np.arange(V0)]).astype(np.int32)
+        c0 = (O.cfg_topk_draw(got["logits"], scale=om.m.cfg_scale, top_k=om.m.top_k, seed=seed,
+                              frame=frame, draw=0, ids=ids)
+              if om.m.top_k > 0 else
+              O.gumbel_argmax(got["logits"], seed=seed, frame=frame, draw=0, ids=ids))
+    else:
+        c0 = draw(got["logits"], 0, base, (base, base + V0))
     assert np.array_equal(c0, codes[:, 0]), ("draw 0", c0, codes[:, 0])
     for j in range(1, cfg["n_codebooks"]):
         d_in = O.step_input(om, j, codes, got["u"])

@@ -345,8 +345,18 @@ def test_frame_layout_stage_slots(L, name, B):
     for a, b in zip(tagged, tagged[1:]):
         span = getattr(lay, b) - getattr(lay, a)
         assert tneed[a] <= span < tneed[a] + 256, (a, span, tneed[a])
-    # without attention the attention buffers take no room
-    assert lay.rope == lay.aq == lay.ao == lay.dao == lay.kcache == lay.total
+    # without attention the attention buffers take no room; the rows' stop words come last
+    assert lay.rope == lay.aq == lay.ao == lay.dao == lay.kcache == lay.stop
+    assert lay.total == lay.stop + (B * 4 + 255) // 256 * 256
+    # with the end token the semantic logits have one more column (rows padded to 8)
+    ce = make_config(cfg, **configs.PRESETS["A"], end_token=True)
+    le = _lib.FrameLayout()
+    assert L.m3_frame_layout_get(ctypes.byref(ce), B, ctypes.byref(le)) == 0
+    ldl = (cfg["V0"] + 1 + 7) // 8 * 8
+    assert B * ldl * 4 <= le.u - le.logits < B * ldl * 4 + 256
+    bad = make_config(cfg, **configs.PRESETS["A"])
+    bad.end_id = cfg["vocab_base"]                  # the end token sorts before the codes
+    assert L.m3_frame_layout_get(ctypes.byref(bad), B, ctypes.byref(le)) == _lib.M3_ERR_SHAPE
 
 
 def test_frame_layout_with_attention(L):
@@ -361,7 +371,7 @@ def test_frame_layout_with_attention(L):
     assert L.m3_frame_layout_get(ctypes.byref(plain), B, ctypes.byref(lp)) == 0
     assert L.m3_frame_layout_get(ctypes.byref(att), B, ctypes.byref(la)) == 0
     # the plain layout is unchanged by the attention fields
-    assert lp.total == lp.rope == lp.kcache == lp.attn_ws
+    assert lp.stop == lp.rope == lp.kcache == lp.attn_ws
     assert la.dao - la.ao >= cfg["n_layers"] * B * cfg["n_heads"] * 128 * 2
     assert la.kcache - la.dao >= (cfg["n_codebooks"] - 1) * cfg["d_layers"] * B * cfg["D"] * 2
     kv = cfg["n_layers"] * B * cfg["n_kv_heads"] * max_pos * 128 * 2
@@ -369,7 +379,7 @@ def test_frame_layout_with_attention(L):
     dkv = cfg["d_layers"] * B * cfg["d_heads"] * 8 * 128 * 2
     assert la.dvcache - la.dkcache >= dkv and la.attn_ws - la.dvcache >= dkv
     assert la.aq - la.rope >= max_pos * 64 * 2 * 4
-    assert la.total - la.attn_ws == L.m3_attention_workspace_bytes(B, cfg["n_heads"],
+    assert la.stop - la.attn_ws == L.m3_attention_workspace_bytes(B, cfg["n_heads"],
                                                                    cfg["n_kv_heads"], max_pos)
     assert la.total > lp.total + 2 * kv
     # attention settings out of range are refused

@@ -494,3 +494,87 @@ def test_attention_frame_past_the_cache_sets_err(attn):
     st.decode()
     torch.cuda.synchronize()
     assert int(st.err.item()) == _lib.M3_ERR_ATTN_FULL
+
+
+# ---- the end token (DiffSynth-Studio MiniMax-Music3 stage 2: the semantic
+# draw is over the audio codes and the end token; a song ends when it is drawn)
+def _end_model(cfg, preset, x0, rows_on, rows_off, top_k=0):
+    """A small model whose end-token row makes rows_on draw it at the first
+    frame from x0 and keeps it out of reach for rows_off (built from the
+    oracle's normalised body output), on the GPU and in the oracle."""
+    md_dev = synth.make_model(cfg, **configs.PRESETS[preset], seed=27, device="cpu")
+    md_np = synth.model_to_numpy(md_dev)
+    _, _, tr = O.decode_frame(O.OracleModel(md_np), synth.bits(x0), seed=5, frame=0, trace=True)
+    a = O.bf16_to_f64(O.rmsnorm(tr["h_body"], md_np["final_norm"], cfg["eps"]))
+    row = 0.1 * (a[rows_on].sum(0) - a[rows_off].sum(0))
+    md_np["lm_end"] = O.f64_to_bf16(row).reshape(1, -1)
+    md_dev["lm_end"] = torch.from_numpy(md_np["lm_end"].view(np.int16)).view(torch.bfloat16)
+    dm = runtime.DecodeModel(_to(md_dev, DEV), seed=5, temperature=1.0, top_k=top_k,
+                             end_token=True)
+    om = O.OracleModel(md_np, top_k=top_k, end_token=True)
+    return dm, om
+
+
+@pytest.mark.parametrize("path", ["eager", "graph", "persistent"])
+def test_end_token_frames_match_oracle(path):
+    """Rows 0 and 2 draw the end token at the first frame: every stage of
+    three chained frames against the oracle (the semantic draw over the codes
+    and the end token), and each row's stop word is 1 + the frame of its first
+    end token, after every frame."""
+    import stages
+    cfg = configs.config("frame-small")
+    B, f0 = 4, 0
+    x0 = synth.activations(B, cfg["H"], 91)
+    dm, om = _end_model(cfg, "A", x0, [0, 2], [1, 3])
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=f0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        if path == "graph":
+            st.capture(s)
+        elif path == "persistent":
+            st.persistent_create(s)
+    x = synth.bits(x0)
+    first = np.zeros(B, np.int64)
+    for f in range(f0, f0 + 3):
+        with torch.cuda.stream(s):
+            {"eager": lambda: st.decode(s), "graph": lambda: st.replay(s),
+             "persistent": lambda: st.persistent_launch(s)}[path]()
+        s.synchronize()
+        assert int(st.err.item()) == 0
+        got = stages.read_frame(st, tagged=path == "persistent")
+        stats = stages.check_frame(om, got, x, seed=5, frame=f)
+        ended = got["codes"][:, 0] == cfg["end_token"]
+        if f == f0:
+            assert ended.tolist() == [True, False, True, False], got["codes"][:, 0]
+        first[(first == 0) & ended] = f + 1
+        assert np.array_equal(st.stop.cpu().numpy(), first), (f, st.stop.cpu().numpy(), first)
+        print(f"end token {path} frame {f}: {stats.summary()}; code0 {got['codes'][:, 0].tolist()}",
+              flush=True)
+        x = got["x"]
+    st.release()
+
+
+def test_guided_end_token_frames_match_oracle():
+    """The reference's draw with the end token: guidance over the row pair
+    makes song 0 (rows 0, 1) draw it; stages against the oracle, both rows of
+    a song carry the draw and its stop word."""
+    import stages
+    cfg = configs.config("frame-small")
+    B = 4
+    x0 = synth.activations(B, cfg["H"], 92)
+    dm, om = _end_model(cfg, "A", x0, [0], [1], top_k=50)
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
+    torch.cuda.synchronize()
+    x = synth.bits(x0)
+    for f in range(2):
+        st.decode()
+        torch.cuda.synchronize()
+        got = stages.read_frame(st, tagged=False)
+        stages.check_frame(om, got, x, seed=5, frame=f)
+        assert np.array_equal(got["codes"][0::2], got["codes"][1::2])
+        if f == 0:
+            assert got["codes"][0, 0] == cfg["end_token"]
+        stop = st.stop.cpu().numpy()
+        assert stop[0] == stop[1] == 1 and stop[2] == stop[3]
+        x = got["x"]
