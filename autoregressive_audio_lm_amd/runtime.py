@@ -35,6 +35,25 @@ def frame_weight_bytes(c: _lib.Config) -> int:
     return int(lib().m3_frame_weight_bytes(ctypes.byref(c)))
 
 
+class NoFramesError(RuntimeError):
+    """A song drew the end token at its first frame: nothing was generated."""
+
+
+def frames_generated(stop, frame0: int):
+    """From the rows' stop words (0, or 1 + the frame of the first end token):
+    the frames each row generated before its end token, or -1 while it is
+    still running.  A row whose end token came at its first frame (frame0)
+    generated nothing, which stops the whole request (DiffSynth-Studio
+    MiniMax-Music3 stage 2)."""
+    import numpy as np
+    stop = np.asarray(stop, np.int64)
+    n = np.where(stop > 0, stop - 1 - int(frame0), -1)
+    if np.any(n == 0):
+        raise NoFramesError(f"rows {np.flatnonzero(n == 0).tolist()} drew the end token at "
+                            f"their first frame")
+    return n
+
+
 class DecodeModel:
     """All weights of one decode frame, packed on the device.
 
@@ -143,7 +162,7 @@ class FrameState:
     code output of the last frame."""
 
     def __init__(self, dm: DecodeModel, B: int, x0: torch.Tensor, frame0: int = 0, stream=None):
-        self.dm, self.B = dm, B
+        self.dm, self.B, self.frame0 = dm, B, int(frame0)
         self.layout = _lib.FrameLayout()
         check(lib().m3_frame_layout_get(ctypes.byref(dm.config), B, ctypes.byref(self.layout)))
         dev = x0.device
@@ -232,6 +251,11 @@ class FrameState:
         n = c.n_slice + (1 if c.end_id >= 0 else 0)
         ld = (n + 7) // 8 * 8
         return self.view("logits", torch.float32, ld)[:, :n]
+
+    def poll_stop(self):
+        """The host's read of the stop words (every 16 frames, alongside the
+        code ring): frames_generated for each row."""
+        return frames_generated(self.stop.cpu().numpy(), self.frame0)
 
     @property
     def stop(self) -> torch.Tensor:

@@ -83,3 +83,13 @@ def test_end_token_drawn_everywhere_embeds_code_zero(oracle, small):
     assert np.array_equal(xn, O.feedback(om, codes))
     u = np.zeros((4, cfg["D"]), np.uint16)
     assert np.array_equal(O.step_input(om, 1, codes, u), O.step_input(om, 1, zero, u))
+
+
+def test_frames_generated_from_stop_words():
+    """The host's reading of the stop words: frames before the end token, -1
+    while running, and an end token at the first frame is an error."""
+    from autoregressive_audio_lm_amd import runtime
+    n = runtime.frames_generated([0, 8, 13, 0], frame0=5)
+    assert n.tolist() == [-1, 2, 7, -1]
+    with pytest.raises(runtime.NoFramesError):
+        runtime.frames_generated([0, 6], frame0=5)
