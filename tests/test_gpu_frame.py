@@ -549,6 +549,9 @@ def test_end_token_frames_match_oracle(path):
             assert ended.tolist() == [True, False, True, False], got["codes"][:, 0]
         first[(first == 0) & ended] = f + 1
         assert np.array_equal(st.stop.cpu().numpy(), first), (f, st.stop.cpu().numpy(), first)
+        # rows 0 and 2 ended at their first frame: the host's poll reports it
+        with pytest.raises(runtime.NoFramesError):
+            st.poll_stop()
         print(f"end token {path} frame {f}: {stats.summary()}; code0 {got['codes'][:, 0].tolist()}",
               flush=True)
         x = got["x"]
