@@ -102,6 +102,7 @@ class DecodeModel:
                                 self._keep[-6:])))
             if "q_norm" in L:                # per-head q/k norms (decode attention)
                 lw.q_norm, lw.k_norm = keep(L["q_norm"]), keep(L["k_norm"])
+                dst[-1]["q_norm"], dst[-1]["k_norm"] = self._keep[-2], self._keep[-1]
             del gu
             if free_sources:
                 for k in ("qkv", "o", "gate", "up", "down"):
@@ -251,6 +252,56 @@ class FrameState:
         n = c.n_slice + (1 if c.end_id >= 0 else 0)
         ld = (n + 7) // 8 * 8
         return self.view("logits", torch.float32, ld)[:, :n]
+
+    def prefill(self, xp: torch.Tensor, stream=None, trace: bool = False):
+        """The prompt before the first frame (attention = 1, bf16 body): rows
+        xp [B, P, hidden] bf16 (row b's prompt embeddings, P = the config's
+        pos0, so that frame 0 continues at position P) run through every body
+        layer as the prompt prefill (m3_rmsnorm_rows, m3_prefill_gemm,
+        m3_prefill_qk_norm_rope writing each layer's keys and values at
+        positions 0 .. P-1 straight into this state's caches,
+        m3_prefill_attention), so the frames attend over the prompt with no
+        copy.  trace: return per layer the QKV, attention output, residual
+        stream after O, SwiGLU output and residual stream after down
+        ([B * P, *] host bf16 bits, rows ordered [b][t]; the launches go to
+        the current stream then)."""
+        c, B = self.dm.config, self.B
+        if not c.attention:
+            raise ValueError("prefill fills the caches of an attention frame state")
+        if self.dm.fmt_body != m3.BF16:
+            raise ValueError("the prompt prefill GEMM takes bf16 body weights")
+        if xp.dim() != 3 or xp.shape[0] != B or xp.shape[2] != c.hidden or xp.shape[1] != c.pos0:
+            raise ValueError(f"prompt rows must be [B, pos0={c.pos0}, hidden]")
+        P, H, F = xp.shape[1], c.hidden, c.ffn
+        nq, nkv = c.n_heads * 128, c.n_kv_heads * 128
+        dev = self.state.device
+        h = xp.reshape(B * P, H).contiguous().clone()
+        a = torch.empty(B * P, H, dtype=torch.bfloat16, device=dev)
+        qkv = torch.empty(B * P, nq + 2 * nkv, dtype=torch.bfloat16, device=dev)
+        att = torch.empty(B * P, nq, dtype=torch.bfloat16, device=dev)
+        mlp = torch.empty(B * P, F, dtype=torch.bfloat16, device=dev)
+        rope = self.view("rope", torch.float32, 128, rows=max(c.max_pos, 8))
+        n = B * c.n_kv_heads * c.max_pos * 128
+        kall = self.state[self.layout.kcache:self.layout.kcache + 2 * n * c.n_layers]
+        vall = self.state[self.layout.vcache:self.layout.vcache + 2 * n * c.n_layers]
+        out = []
+        for l, W in enumerate(self.dm.packed_layers):
+            kc = kall[2 * n * l:2 * n * (l + 1)].view(torch.bfloat16).view(B, c.n_kv_heads, c.max_pos, 128)
+            vc = vall[2 * n * l:2 * n * (l + 1)].view(torch.bfloat16).view(B, c.n_kv_heads, c.max_pos, 128)
+            m3.rmsnorm_rows(h, W["attn_norm"], c.eps, a=a, stream=stream)
+            m3.prefill_gemm(W["qkv"], nq + 2 * nkv, H, a, y=qkv, stream=stream)
+            q = m3.prefill_qk_norm_rope(qkv, B, c.n_heads, c.n_kv_heads, W["q_norm"], W["k_norm"],
+                                        rope, 0, kc, vc, eps=c.eps, stream=stream)
+            m3.prefill_attention(q, B, c.n_heads, c.n_kv_heads, kc, vc, 0, out=att, stream=stream)
+            ho = m3.prefill_gemm(W["o"], H, nq, att, epi=m3.EPI_RESIDUAL, residual=h, stream=stream)
+            m3.rmsnorm_rows(ho, W["ffn_norm"], c.eps, a=a, stream=stream)
+            m3.prefill_gemm(W["gate_up"], 2 * F, H, a, y=mlp, epi=m3.EPI_SWIGLU, stream=stream)
+            h = m3.prefill_gemm(W["down"], H, F, mlp, epi=m3.EPI_RESIDUAL, residual=ho, stream=stream)
+            if trace:
+                from . import synth
+                out.append({k: synth.bits(v) for k, v in
+                            (("qkv", qkv), ("ao", att), ("ho", ho), ("mlp", mlp), ("h", h))})
+        return out if trace else None
 
     def poll_stop(self):
         """The host's read of the stop words (every 16 frames, alongside the

@@ -581,3 +581,73 @@ def test_guided_end_token_frames_match_oracle():
         stop = st.stop.cpu().numpy()
         assert stop[0] == stop[1] == 1 and stop[2] == stop[3]
         x = got["x"]
+
+
+# ---- prompt prefill -> frames: the prompt's keys and values are written
+# straight into the frame state's caches, and the frames continue after it
+PROMPT = 9
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_prompt_prefill_then_frames_match_oracle(B):
+    """A prompt of 9 positions per row through every body layer as the
+    prompt prefill (the keys and values go straight into the frame state's
+    caches), then three frames at positions 9, 10, 11 over prompt and frames
+    alike.  Every operation of every prefill layer at every position, and
+    every stage of the frames, against the oracle on the GPU's own input of
+    that operation (the oracle's attention at position t over the GPU's cached
+    positions before t and its own slot t), and the cache slots written."""
+    import stages
+    # (the prompt prefill's GEMMs contract over K % 64 == 0: FFN 1024)
+    cfg = dict(configs.config("frame-small"), F=1024)
+    md_dev = synth.make_model(cfg, **configs.PRESETS["A"], seed=29, device="cpu")
+    md_np = synth.model_to_numpy(md_dev)
+    dm = runtime.DecodeModel(_to(md_dev, DEV), seed=5, temperature=1.0, attention=1,
+                             max_pos=ATTN_MAX_POS, pos0=PROMPT)
+    om = O.OracleModel(md_np, attention=1, max_pos=ATTN_MAX_POS, pos0=PROMPT)
+    xp = synth.activations(B * PROMPT, cfg["H"], 700 + B).view(B, PROMPT, cfg["H"])
+    x0 = synth.activations(B, cfg["H"], 800 + B)
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
+    torch.cuda.synchronize()
+    tr = st.prefill(xp.to(DEV), trace=True)
+    torch.cuda.synchronize()
+    caches = stages.read_caches(st)
+    xpb = synth.bits(xp)
+    nh, nkv = cfg["n_heads"], cfg["n_kv_heads"]
+    stats = stages.Stats()
+    for l in range(cfg["n_layers"]):
+        ln = md_np["layers"][l]
+        for t in range(PROMPT):
+            rows = np.arange(B) * PROMPT + t
+            h_in = xpb[:, t] if l == 0 else tr[l - 1]["h"][rows]
+            kc = caches["kcache"][l].copy()        # the oracle writes its own slot t here
+            vc = caches["vcache"][l].copy()
+
+            def step(qkv_gpu, kc=kc, vc=vc, t=t, rows=rows):
+                q = O.qk_norm_rope(qkv_gpu, nh, nkv, ln["q_norm"], ln["k_norm"], cfg["eps"],
+                                   om._rope, t, kc, vc)
+                o = O.decode_attention(q, kc, vc, t + 1, nh, nkv)
+                P.check_bf16_vs_bf16(tr[l]["ao"][rows], o, agree=0.97, rel=1e-2, width=128)
+                # the slot the prefill wrote at t, against the oracle's from the same QKV
+                P.check_bf16_vs_bf16(caches["kcache"][l][:, :, t], kc[:, :, t], width=128)
+                assert np.array_equal(caches["vcache"][l][:, :, t], vc[:, :, t])
+                return tr[l]["ao"][rows]
+
+            g = dict(qkv=tr[l]["qkv"][rows], ho=tr[l]["ho"][rows], mlp=tr[l]["mlp"][rows],
+                     h_out=tr[l]["h"][rows])
+            stages._layer(om, stats, "body", l, ln, f"prefill layer {l} position {t}", g, h_in,
+                          step)
+    print(f"prefill B={B}: {stats.summary()}", flush=True)
+    # positions past the prompt are untouched before the first frame
+    assert not caches["kcache"][:, :, :, PROMPT:].any()
+    x = synth.bits(x0)
+    for f in range(3):
+        before = stages.read_caches(st)
+        st.decode()
+        torch.cuda.synchronize()
+        got = stages.read_frame(st, tagged=False)
+        s = stages.check_frame(om, got, x, seed=5, frame=f,
+                               attn=dict(pos=PROMPT + f, before=before, after=stages.read_caches(st)))
+        print(f"after the prompt B={B} frame {f}: {s.summary()}", flush=True)
+        x = got["x"]
+    assert int(st.err.item()) == 0
