@@ -141,8 +141,9 @@ __device__ __forceinline__ void i8x4_to_bf16x4(uint32_t v, uint32_t& lo, uint32_
   float f1 = (float)(int8_t)((v >> 8) & 0xffu);
   float f2 = (float)(int8_t)((v >> 16) & 0xffu);
   float f3 = (float)((int32_t)v >> 24);
-  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  // the upper halves of two floats side by side: one byte permute per pair
+  lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
 
 __device__ __forceinline__ void i8x16_to_bf16(const uint4& q, uint32_t* o) {
