@@ -480,10 +480,12 @@ typedef struct {
 } m3_frame_layout;
 
 /* Algorithmic weight bytes one frame streams: every body matrix once, the
- * lm_head slice once, the depth input projection once, the depth layers and
+ * lm_head slice once (with the end token's row when end_id >= 0), the depth
+ * input projection once, the depth layers and
  * one head per codebook step (7 steps), plus the fp32 gammas of every norm
  * application.  bf16: 2NK; i8row: NK + 4N; i8g128: NK + 4N*K/128.
- * (TensorFold PR #987 asks the engine for "the weight bytes a frame reads".) */
+ * (TensorFold PR #987, frame anatomy: the engine accounts for each frame's
+ * weight traffic.) */
 uint64_t m3_frame_weight_bytes(const m3_config* cfg /* host */);
 /* layout of the caller-allocated frame state; 0 / M3_ERR_* on refusal */
 int m3_frame_layout_get(const m3_config* cfg /* host */, int B, m3_frame_layout* out /* host */);
