@@ -68,7 +68,8 @@ class FrameLayout(ctypes.Structure):
                                                "dmlp", "dlogits", "ring", "frame", "part_sem", "part_dep",
                                                "flags", "err", "seq", "phases", "th", "tqkv", "tmlp", "tu",
                                                "thd", "tdqkv", "tdmlp", "th2", "thd2", "ho", "hdo", "rope", "aq", "ao", "dao", "kcache",
-                                               "vcache", "dkcache", "dvcache", "attn_ws", "stop", "total")]
+                                               "vcache", "dkcache", "dvcache", "attn_ws", "tao", "tdao", "trec", "stop",
+                                               "total")]
 
 
 class PhaseRegion(ctypes.Structure):
@@ -78,7 +79,7 @@ class PhaseRegion(ctypes.Structure):
 
 
 PHASE_MAX_REGIONS = 4
-PHASE_GEMV, PHASE_FRAME_END = 0, 1
+PHASE_GEMV, PHASE_FRAME_END, PHASE_ATTENTION = 0, 1, 2
 
 
 class PhaseRecord(ctypes.Structure):

@@ -14,28 +14,18 @@
 // are contiguous rows of 256 bytes.
 //
 // Attention.  A workgroup takes one (batch row, KV head, chunk of 64 or 128
-// positions) and issues all of the chunk's key and value loads up front.
-// Pass 1: four lanes per position, each holding 32 of the 128 dimensions as
-// bf16 pairs; v_dot2 products against the G query heads of the KV head, a
-// two-step DPP sum, the scores (base 2, scale folded in) to LDS.  One wave
-// per head then takes the chunk's maximum, exponentials and sum.  Pass 2:
-// each lane owns 4 dimensions of CH / 8 positions (a wave load reads two
-// whole value rows) and accumulates P.V; the 8 half-wave partials are summed
-// in LDS.  With one chunk the result is the output; otherwise (maximum, sum,
-// P.V) goes to the workspace and attn_merge_kernel combines the chunks in
-// order.  (Merging in the last workgroup to finish, behind an atomic count,
-// measured ten times slower: the device-scope fences it needs write back and
-// invalidate the L2 under every other workgroup.)  The bound is HBM: each
-// position's key and value are read once (512 bytes per KV head and batch
-// row).
-#include "gemv_impl.h"
+// positions) and issues all of the chunk's query, key and value loads up
+// front; the chunk's arithmetic is attn_compute (attn_impl.h).  With one
+// chunk the result is the output; otherwise (maximum, sum, P.V) goes to the
+// workspace and attn_merge_kernel combines the chunks in order.  (Merging in
+// the last workgroup to finish, behind an atomic count, measured ten times
+// slower: the device-scope fences it needs write back and invalidate the L2
+// under every other workgroup.)  The bound is HBM: each position's key and
+// value are read once (512 bytes per KV head and batch row).
+#include "attn_impl.h"
 
 namespace m3 {
 namespace {
-
-constexpr int kHD = 128;
-constexpr int kAThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
 
 __global__ void rope_table_kernel(float* t, int max_pos, int half, double theta) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -80,14 +70,10 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     dst[lane + 64] = (uint16_t)x1;
     return;
   }
-  // the head's RMSNorm with the GEMV prologue's steps (gemv_impl.h, "RMSNorm"):
-  // r from a float64 sum of squares, rounded to fp32; two fp32 products
+  // the head's RMSNorm with the GEMV prologue's steps, then RoPE
   const float* g = hh < n_q ? q_gamma : k_gamma;
-  const float a0f = bf2f(x0), a1f = bf2f(x1);
-  const float r = norm_r(wave_sum_f64((double)a0f * a0f + (double)a1f * a1f), kHD, eps);
-  const float a0 = bf2f(f2bf((a0f * r) * g[lane])), a1 = bf2f(f2bf((a1f * r) * g[lane + 64]));
-  const float c = rope[((size_t)pos * 64 + lane) * 2], s = rope[((size_t)pos * 64 + lane) * 2 + 1];
-  const uint32_t y0 = f2bf(a0 * c - a1 * s), y1 = f2bf(a1 * c + a0 * s);
+  uint32_t y0, y1;
+  head_norm_rope(x0, x1, g, eps, rope, pos, lane, y0, y1);
   uint16_t* dst = hh < n_q ? q_out + (size_t)row * ldq + (size_t)hh * kHD
                            : k_cache + (((size_t)b * n_kv + (hh - n_q)) * max_pos + pos) * kHD;
   dst[lane] = (uint16_t)y0;
@@ -122,140 +108,34 @@ __device__ __forceinline__ int attn_T(const AttnParams& p, int r) {
 
 template <int G, int CH>
 __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
-  constexpr int PJ = CH / 64;                    // pass-1 positions per 4-lane group
-  constexpr int PI = CH / 8;                     // pass-2 positions per lane
-  constexpr int WP = CH / 4;                     // pass-2 positions per wave
-  __shared__ __align__(16) float S[CH][G];       // scores, then probabilities
-  __shared__ float Ms[G], Ls[G];
-  __shared__ __align__(16) float pacc[8][G][kHD];   // P.V partials of the 8 half-waves
+  __shared__ AttnLds<G, CH> L;
   const int chunk = blockIdx.x % p.nchunks;
   const int kvh = (blockIdx.x / p.nchunks) % p.n_kv;
   const int b = blockIdx.x / (p.nchunks * p.n_kv);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int T = attn_T(p, b), nc = (T + CH - 1) / CH;
   if (chunk >= nc) return;                       // past this row's position
   const int t0 = chunk * CH;
   const int n = min(T - t0, CH);                 // positions of this chunk
   const size_t base = ((size_t)(b / p.P) * p.n_kv + kvh) * (size_t)p.max_pos * kHD;
-  const uint16_t* kb = p.k + base;
-  const uint16_t* vb = p.v + base;
-
-  // pass 1 layout: a group of 4 lanes per position, lane li holding the
-  // 16-byte chunks 4 c + li (c < 4) of the row: positions grp + 64 j
-  const int grp = tid >> 2, li = tid & 3;
   // loads retire in issue order: q first, then the keys pass 1 needs, then
   // the values pass 2 needs
-  uint4 qr[G][4];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qr[h][c] = *reinterpret_cast<const uint4*>(p.q + (size_t)b * p.ldq + (size_t)(kvh * G + h) * kHD +
-                                                 8 * (4 * c + li));
-  uint4 kr[PJ][4];
-#pragma unroll
-  for (int j = 0; j < PJ; ++j) {
-    const int t = t0 + min(grp + 64 * j, n - 1);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      kr[j][c] = *reinterpret_cast<const uint4*>(kb + (size_t)t * kHD + 8 * (4 * c + li));
-  }
-  // pass 2 layout: lane owns dimensions 4 dq .. 4 dq + 3 of positions
-  // WP w + 2 i + sub (i < PI), so a wave load reads two whole rows
-  const int dq = lane & 31, sub = lane >> 5;
-  uint2 vr[PI];
-#pragma unroll
-  for (int i = 0; i < PI; ++i) {
-    const int t = t0 + min(WP * wave + 2 * i + sub, n - 1);
-    vr[i] = *reinterpret_cast<const uint2*>(vb + (size_t)t * kHD + 4 * dq);
-  }
-
-  // pass 1: scores (base 2, scale folded in); masked positions get -inf
-#pragma unroll
-  for (int j = 0; j < PJ; ++j) {
-    const int tc = grp + 64 * j;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s = dot2(qr[h][c].x, kr[j][c].x, s);
-        s = dot2(qr[h][c].y, kr[j][c].y, s);
-        s = dot2(qr[h][c].z, kr[j][c].z, s);
-        s = dot2(qr[h][c].w, kr[j][c].w, s);
-      }
-      s += dpp_f<0xB1>(s);                       // the 4 lanes of the group
-      s += dpp_f<0x4E>(s);
-      if (li == 0) S[tc][h] = tc < n ? s * p.scale2 : -INFINITY;
-    }
-  }
-  __syncthreads();
-  // softmax over the chunk, one wave per head
-  for (int h = wave; h < G; h += 4) {
-    float e[PJ], m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < PJ; ++j) m = fmaxf(m, S[lane + 64 * j][h]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float l = 0.f;
-#pragma unroll
-    for (int j = 0; j < PJ; ++j) {
-      e[j] = exp2f(S[lane + 64 * j][h] - m);
-      S[lane + 64 * j][h] = e[j];
-      l += e[j];
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      Ms[h] = m;
-      Ls[h] = l;
-    }
-  }
-  __syncthreads();
-  // pass 2: P.V over this lane's positions and 4 dimensions
-  float acc[G][4];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
-#pragma unroll
-  for (int i = 0; i < PI; ++i) {
-    const int tc = WP * wave + 2 * i + sub;
-    const float v0 = bf2f(vr[i].x & 0xffffu), v1 = bf2f(vr[i].x >> 16);
-    const float v2 = bf2f(vr[i].y & 0xffffu), v3 = bf2f(vr[i].y >> 16);
-    float prs[G];                                // 0 for masked positions
-#pragma unroll
-    for (int h = 0; h < G; ++h) prs[h] = S[tc][h];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float pr = prs[h];
-      acc[h][0] = fmaf(pr, v0, acc[h][0]);
-      acc[h][1] = fmaf(pr, v1, acc[h][1]);
-      acc[h][2] = fmaf(pr, v2, acc[h][2]);
-      acc[h][3] = fmaf(pr, v3, acc[h][3]);
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    *reinterpret_cast<float4*>(&pacc[2 * wave + sub][h][4 * dq]) =
-        make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-  __syncthreads();
+  AttnRegs<G, CH> R;
+  attn_load_q(R, p.q + (size_t)b * p.ldq + (size_t)kvh * G * kHD, tid);
+  attn_load_kv(R, p.k + base, p.v + base, t0, n, tid);
   float* wrec = p.ws + (((size_t)b * p.n_kv + kvh) * p.nchunks) * (G * (2 + kHD));
-  for (int o = tid; o < G * kHD; o += kAThreads) {
-    const int h = o / kHD, d = o % kHD;
-    float A = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) A += pacc[k][h][d];
+  attn_compute(R, n, p.scale2, tid, L, [&](int h, int d, float A, float M, float Lh) {
     if (nc == 1) {
-      p.out[(size_t)b * p.ldo + (size_t)(kvh * G + h) * kHD + d] = (uint16_t)f2bf(A / Ls[h]);
+      p.out[(size_t)b * p.ldo + (size_t)(kvh * G + h) * kHD + d] = (uint16_t)f2bf(A / Lh);
     } else {
       float* w = wrec + ((size_t)chunk * G + h) * (2 + kHD);
       if (d == 0) {
-        w[0] = Ms[h];
-        w[1] = Ls[h];
+        w[0] = M;
+        w[1] = Lh;
       }
       w[2 + d] = A;
     }
-  }
+  });
 }
 
 // chunks combined in order: one workgroup of 128 threads per (row, query

@@ -192,9 +192,19 @@ int validate_config(const m3_config* c, int B) {
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // phases of one frame: 4 GEMVs per body layer, lm_head, depth input, per depth
-// step 4 GEMVs per layer and the head, then the frame end
+// step 4 GEMVs per layer and the head, then the frame end; with decode
+// attention one attention phase per body layer and per depth layer run
 int frame_phases(const m3_config& c) {
-  return 4 * c.n_layers + 2 + (c.n_codebooks - 1) * (4 * c.d_layers + 1) + 1;
+  const int per_layer = c.attention ? 5 : 4;
+  return per_layer * c.n_layers + 2 + (c.n_codebooks - 1) * (per_layer * c.d_layers + 1) + 1;
+}
+
+// the body's decode attention at T = max_pos: positions per chunk and chunks
+// (the chunk records of a persistent frame are sized for them)
+int body_attn_chunk(const m3_config& c, int B) { return attn_chunk_size(B, c.n_kv_heads, c.max_pos); }
+int body_attn_chunks(const m3_config& c, int B) {
+  const int ch = body_attn_chunk(c, B);
+  return (c.max_pos + ch - 1) / ch;
 }
 
 m3_frame_layout layout_of(const m3_config& c, int B) {
@@ -258,6 +268,12 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   L.dkcache = take(dkv);
   L.dvcache = take(dkv);
   L.attn_ws = take(at ? attn_workspace_bytes(B, c.n_heads, c.n_kv_heads, c.max_pos) : 0);
+  // the persistent frame's attention outputs (u32 words) and, per body layer,
+  // its chunk records (tagged 64-bit words)
+  L.tao = take(at ? nL * B * d.nq * 4 : 0);
+  L.tdao = take(at ? nDL * B * d.dq * 4 : 0);
+  const int nch = at ? body_attn_chunks(c, B) : 0;
+  L.trec = take(at && nch > 1 ? nL * B * c.n_heads * nch * (2 + 128) * 8 : 0);
   L.stop = take((size_t)B * 4);
   L.total = off;
   return L;
@@ -313,6 +329,12 @@ struct AttnStep {
   int pos0;
   uint32_t* err;
   void* ws;
+  // a persistent frame's step: the phase that wrote qkv (tagged words), the
+  // output words, the chunk records (body) and this layer's index
+  int pqkv = -1;
+  uint32_t* tout = nullptr;
+  uint64_t* rec = nullptr;
+  int B = 0;
 };
 
 struct FrameSink {
@@ -348,13 +370,47 @@ struct LaunchSink final : FrameSink {
   }
 };
 
+// chunks of a frame-position (body) attention step's records
+int body_attn_chunks_of(const AttnStep& s, int B) {
+  const int ch = attn_chunk_size(B, s.n_kv, s.max_pos);
+  return (s.max_pos + ch - 1) / ch;
+}
+
+// a persistent frame's attention phase, chunked as the decode attention
+// launches chunk (T = max_pos for a body layer, pos + 1 for a depth layer)
+AttnArgs attn_args(const AttnStep& s, int B) {
+  AttnArgs a{};
+  a.qkv = reinterpret_cast<const uint32_t*>(s.qkv);
+  a.q_gamma = s.q_gamma;
+  a.k_gamma = s.k_gamma;
+  a.rope = s.rope;
+  a.k_cache = s.k_cache;
+  a.v_cache = s.v_cache;
+  a.out = s.tout;
+  a.rec = s.rec;
+  a.frame = s.frame_dev;
+  a.ldqkv = s.ldqkv;
+  a.n_q = s.n_q;
+  a.n_kv = s.n_kv;
+  a.max_pos = s.max_pos;
+  a.pos0 = s.pos0;
+  a.pos = s.pos;
+  const int Tg = s.frame_dev ? s.max_pos : s.pos + 1;
+  a.ch = attn_chunk_size(B, s.n_kv, Tg);
+  a.nchunks = (Tg + a.ch - 1) / a.ch;
+  a.B = B;
+  a.pqkv = s.pqkv;
+  a.eps = s.eps;
+  return a;
+}
+
 struct PlanSink final : FrameSink {
   PersistPlan* pl;
   explicit PlanSink(PersistPlan* p) : pl(p) {}
   hipError_t gemv(const GemvDesc& d) override { return persist_add_gemv(pl, d); }
-  // (the persistent frame carries the per-row draws and the attention stub only)
+  // (the persistent frame carries the per-row draws only)
   hipError_t cfg_draw(const CfgDesc&) override { return hipErrorInvalidValue; }
-  hipError_t attention(const AttnStep&, int) override { return hipErrorInvalidValue; }
+  hipError_t attention(const AttnStep& s, int B) override { return persist_add_attention(pl, attn_args(s, B)); }
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
                       int code_vocab, int n_cb, int B, int H, uint16_t* x, int32_t* ring,
@@ -458,12 +514,28 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   auto dao_slot = [&](int j, int l) {
     return reinterpret_cast<uint16_t*>(S + L.dao + dl_index(j, l) * B * d.dq * 2);
   };
+  // (a persistent frame: the output words tao / tdao, the chunk records trec)
+  auto tao_slot = [&](int l) { return reinterpret_cast<uint32_t*>(S + L.tao) + (size_t)l * B * d.nq; };
+  auto tdao_slot = [&](int j, int l) {
+    return reinterpret_cast<uint32_t*>(S + L.tdao) + dl_index(j, l) * B * d.dq;
+  };
+  auto rec_slot = [&](int l) {
+    const size_t per = (size_t)B * c.n_heads * body_attn_chunks(c, B) * (2 + 128);
+    return L.trec ? reinterpret_cast<uint64_t*>(S + L.trec) + (size_t)l * per : nullptr;
+  };
   auto attention = [&](const uint16_t* qkv_in, int ldq_in, int n_q, int n_kv,
                        const m3_layer_weights& W, uint16_t* kc, uint16_t* vc, int max_pos,
-                       int pos, bool from_frame, uint16_t* ao) {
+                       int pos, bool from_frame, uint16_t* ao, int pq, uint32_t* tout,
+                       uint64_t* rec) {
     AttnStep a{qkv_in, ldq_in, n_q, n_kv, W.q_norm, W.k_norm, eps, rope, pos, aq, kc, vc, ao,
                max_pos, from_frame ? frame : nullptr, from_frame ? c.pos0 : 0, err,
                S + L.attn_ws};
+    if (tagged) {
+      a.pqkv = pq;
+      a.tout = tout;
+      a.rec = rec;
+    }
+    a.B = B;
     ++ph;
     return sink.attention(a, B);
   };
@@ -491,13 +563,14 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     int p_ho;
     if (attn) {
       const size_t lay = (size_t)B * c.n_kv_heads * c.max_pos * 128 * 2;
+      o.x = ph;                                    // O reads the attention's output
       M3_TRY(attention(qkv, d.nqkv, c.n_heads, c.n_kv_heads, W,
                        reinterpret_cast<uint16_t*>(S + L.kcache + l * lay),
                        reinterpret_cast<uint16_t*>(S + L.vcache + l * lay), c.max_pos, 0, true,
-                       ao));
+                       ao, p_qkv, tao_slot(l), rec_slot(l)));
       p_ho = ph;
-      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, ao, d.nq, nullptr, 0, 0, h_o, d.H, 0,
-                  M3_EPI_RESIDUAL, xin, d.H, o));
+      M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, tagged ? reinterpret_cast<uint16_t*>(tao_slot(l)) : ao,
+                  d.nq, nullptr, 0, 0, h_o, d.H, 0, M3_EPI_RESIDUAL, xin, d.H, o));
     } else {
       p_ho = ph;
       M3_TRY(gemv(c.fmt_body, W.o, d.H, d.nq, qkv, d.nqkv, nullptr, group, d.nq + d.nkv, h_o, d.H,
@@ -604,13 +677,15 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
       if (attn) {
         // step j attends over the frame's codebook positions 0 .. j - 1
         const size_t lay = (size_t)B * c.d_heads * 8 * 128 * 2;
+        o.x = ph;                                  // O reads the attention's output
         M3_TRY(attention(dqkv, d.dqkv, c.d_heads, c.d_heads, W,
                          reinterpret_cast<uint16_t*>(S + L.dkcache + l * lay),
                          reinterpret_cast<uint16_t*>(S + L.dvcache + l * lay), 8, j - 1, false,
-                         ao));
+                         ao, p_dqkv, tdao_slot(j, l), nullptr));
         p_hdo = ph;
-        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq, ao, d.dq, nullptr, 0, 0, hd_o, d.D, 0,
-                    M3_EPI_RESIDUAL, hd, d.D, o));
+        M3_TRY(gemv(c.fmt_depth, W.o, d.D, d.dq,
+                    tagged ? reinterpret_cast<uint16_t*>(tdao_slot(j, l)) : ao, d.dq, nullptr, 0,
+                    0, hd_o, d.D, 0, M3_EPI_RESIDUAL, hd, d.D, o));
       } else {
         p_hdo = ph;
         Sched os;
@@ -706,7 +781,32 @@ struct RecordSink final : FrameSink {
     return hipSuccess;
   }
   hipError_t cfg_draw(const CfgDesc&) override { return hipErrorInvalidValue; }
-  hipError_t attention(const AttnStep&, int) override { return hipErrorInvalidValue; }
+  hipError_t attention(const AttnStep& s, int B) override {
+    m3_phase_record r{};
+    r.kind = M3_PHASE_ATTENTION;
+    const size_t nqkv = (size_t)(s.n_q + 2 * s.n_kv) * 128, nq = (size_t)s.n_q * 128;
+    add(r.in, r.n_in, rows(s.qkv, B, s.ldqkv, 0, nqkv, 4, s.pqkv, 1));
+    // the caches ([row][KV head] sequences of max_pos rows of 128): a body
+    // layer's whole cache (the frame's position is written and read back by
+    // this step, the rest was written before the launch); a depth layer's
+    // positions 0 .. pos (pos written here, the others by the layer's
+    // attention at the frame's earlier codebook steps)
+    const int seqs = B * s.n_kv;
+    const size_t ld = (size_t)s.max_pos * 128;
+    const size_t r0 = s.frame_dev ? 0 : (size_t)s.pos * 128;
+    const size_t r1 = s.frame_dev ? ld : (size_t)(s.pos + 1) * 128;
+    add(r.in, r.n_in, rows(s.k_cache, seqs, ld, 0, r1, 2, -1, 0));
+    add(r.in, r.n_in, rows(s.v_cache, seqs, ld, 0, r1, 2, -1, 0));
+    add(r.out, r.n_out, rows(s.k_cache, seqs, ld, r0, r1, 2, -1, 0));
+    add(r.out, r.n_out, rows(s.v_cache, seqs, ld, r0, r1, 2, -1, 0));
+    add(r.out, r.n_out, rows(s.tout, B, nq, 0, nq, 4, -1, 1));
+    if (s.rec) {
+      const size_t per = (size_t)s.n_q * body_attn_chunks_of(s, B) * (2 + 128);
+      add(r.out, r.n_out, rows(s.rec, B, per, 0, per, 8, -1, 1));
+    }
+    recs.push_back(r);
+    return hipSuccess;
+  }
   hipError_t feedback(const uint16_t*, const uint16_t* const*, int32_t* codes, const Best* last_part,
                       int last_nparts, int32_t, int, int, int, int B, int H, uint16_t* x,
                       int32_t* ring, uint32_t* frame, const FeedbackTags& ft) override {
@@ -1277,8 +1377,7 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   // one frame kernel per body format: bf16, int8-row or fp8-row body and the
   // same lm_head format, int8-g128 depth
   const m3_config& c = model->cfg;
-  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128 || c.top_k > 0 ||
-      c.attention)
+  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128 || c.top_k > 0)
     return M3_ERR_FORMAT;
   // row-block winners carry their column in 16 bits next to the tag
   if (c.n_slice + 1 > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;
@@ -1318,7 +1417,7 @@ int m3_frame_phase_table(const m3_model* model, void* state, int B, int32_t* cod
   st = validate_model(model);
   if (st != M3_OK) return st;
   const m3_config& c = model->cfg;
-  if (c.top_k > 0 || c.attention) return M3_ERR_FORMAT;
+  if (c.top_k > 0) return M3_ERR_FORMAT;
   RecordSink sink;
   st = build_frame(model, static_cast<uint8_t*>(state), B, codes, sink, true);
   if (st == M3_ERR_HIP) st = M3_ERR_SHAPE;

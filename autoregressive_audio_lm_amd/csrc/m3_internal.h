@@ -214,6 +214,23 @@ struct FeedbackTags {
   int32_t end_id = -1;
   uint32_t* stop = nullptr;
 };
+// An attention phase (persist_attn.h): q/k norm + RoPE with the cache write
+// at the position, the chunks' partial softmax and their merge, for one body
+// layer (position pos0 + *frame) or one depth layer (position pos).
+struct AttnArgs {
+  const uint32_t* qkv;     // the QKV GEMV's output words [B][ldqkv]
+  const float* q_gamma;    // [128] per-head norm weights
+  const float* k_gamma;
+  const float* rope;       // [>= max_pos][64] (cos, sin)
+  uint16_t* k_cache;       // bf16 [B][n_kv][max_pos][128]
+  uint16_t* v_cache;
+  uint32_t* out;           // output words [B][n_q * 128]
+  uint64_t* rec;           // chunk records [B][n_kv][nchunks][G][2 + 128] (unused at nchunks 1)
+  const uint32_t* frame;   // body: position pos0 + *frame; depth: nullptr (position pos)
+  int ldqkv, n_q, n_kv, max_pos, pos0, pos, nchunks, ch, B;
+  int pqkv;                // the phase that wrote qkv
+  float eps, scale2;       // norm epsilon; log2(e) / sqrt(128) (set when recorded)
+};
 size_t persist_phase_bytes();
 int persist_max_phases();
 PersistPlan* persist_plan_new(int B);
@@ -226,6 +243,7 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
                                 int n_slice, int code_vocab, int n_cb, int B, int H,
                                 uint16_t* x_out, int32_t* ring, uint32_t* frame,
                                 const FeedbackTags& ft);
+hipError_t persist_add_attention(PersistPlan* pl, const AttnArgs& a);
 // phase clock: words of the buffer (3 per phase and workgroup), attach/detach
 size_t persist_clock_words(const PersistLaunch& L);
 void persist_set_clock(PersistLaunch& L, uint64_t* clk);
@@ -237,12 +255,16 @@ void persist_launch_free(PersistLaunch* L);
 hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, uint32_t* err,
                           uint32_t* seq, hipStream_t s, PersistLaunch* out);
 hipError_t persist_launch(const PersistLaunch& L, hipStream_t s);
-// the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip, persist_fp8row.hip)
-// (clock: the instantiation that writes the phase clock; every row count
-// runs on 16-row tiles)
-const void* persist_kernel_bf16(bool clock);
-const void* persist_kernel_i8row(bool clock);
-const void* persist_kernel_fp8row(bool clock);
+// the cooperative frame kernels (persist_bf16.hip, persist_i8row.hip,
+// persist_fp8row.hip; with attention phases persist_*_attn.hip) (clock: the
+// instantiation that writes the phase clock; every row count runs on 16-row
+// tiles)
+const void* persist_kernel_bf16(bool clock, bool attn);
+const void* persist_kernel_i8row(bool clock, bool attn);
+const void* persist_kernel_fp8row(bool clock, bool attn);
+const void* persist_kernel_bf16_attn(bool clock);
+const void* persist_kernel_i8row_attn(bool clock);
+const void* persist_kernel_fp8row_attn(bool clock);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, size_t n, hipStream_t s);
 // a plain streaming read of `bytes` (< 2 GiB) at buf by `workgroups` workgroups
 // (stream.hip); sink: workgroups words

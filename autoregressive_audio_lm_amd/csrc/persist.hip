@@ -22,6 +22,7 @@
 // waits require it); the launch fails rather than run otherwise.
 #include "persist_kernel.h"
 
+#include <cstring>
 #include <vector>
 
 namespace m3 {
@@ -54,6 +55,7 @@ struct PersistPlan {
   size_t smem = 0;
   int B = 0;
   int fmt_body = -1;      // the kernel's class-0 format
+  bool attn = false;      // has attention phases (the kernels compiled with them)
 };
 
 size_t persist_phase_bytes() { return sizeof(Phase); }
@@ -92,6 +94,30 @@ hipError_t persist_add_gemv(PersistPlan* pl, const GemvDesc& d) {
   ph.signal = 0;
   const size_t smem = smem_bytes_of(d.fmt, d.K, d.B, d.gamma != nullptr);
   if (smem > pl->smem) pl->smem = smem;
+  pl->phases.push_back(ph);
+  return hipSuccess;
+}
+
+hipError_t persist_add_attention(PersistPlan* pl, const AttnArgs& a) {
+  if ((int)pl->phases.size() >= kMaxPhases || a.B != pl->B || a.n_kv < 1) return hipErrorInvalidValue;
+  const int g = a.n_q / a.n_kv;
+  if (a.n_q != g * a.n_kv || (g != 1 && g != 2 && g != 4) || (a.ch != 64 && a.ch != 128))
+    return hipErrorInvalidValue;
+  if (a.nchunks < 1 || (long)a.nchunks * a.ch < (long)a.max_pos || (a.nchunks > 1 && !a.rec))
+    return hipErrorInvalidValue;
+  Phase ph{};
+  static_assert(sizeof(AttnArgs) <= sizeof(Params), "attention arguments fit a phase");
+  AttnArgs args = a;
+  args.scale2 = kLog2e / sqrtf((float)kHD);       // as the decode attention launches
+  memcpy(&ph.p, &args, sizeof args);
+  ph.variant = kAttnVariant;
+  ph.signal = 0;
+  const size_t smem = a.ch == 64 ? (g == 1 ? attn_phase_smem<1, 64>() : g == 2 ? attn_phase_smem<2, 64>()
+                                                                            : attn_phase_smem<4, 64>())
+                                 : (g == 1 ? attn_phase_smem<1, 128>() : g == 2 ? attn_phase_smem<2, 128>()
+                                                                              : attn_phase_smem<4, 128>());
+  if (smem > pl->smem) pl->smem = smem;
+  pl->attn = true;
   pl->phases.push_back(ph);
   return hipSuccess;
 }
@@ -164,9 +190,9 @@ hipError_t persist_upload(const PersistPlan* pl, void* table, uint32_t* flags, u
   if (nwg < 4) return hipErrorInvalidValue;
   const void* kern[2];
   for (int c = 0; c < 2; ++c) {
-    kern[c] = pl->fmt_body == M3_I8ROW    ? persist_kernel_i8row(c != 0)
-              : pl->fmt_body == M3_FP8ROW ? persist_kernel_fp8row(c != 0)
-                                          : persist_kernel_bf16(c != 0);
+    kern[c] = pl->fmt_body == M3_I8ROW    ? persist_kernel_i8row(c != 0, pl->attn)
+              : pl->fmt_body == M3_FP8ROW ? persist_kernel_fp8row(c != 0, pl->attn)
+                                          : persist_kernel_bf16(c != 0, pl->attn);
     e = hipFuncSetAttribute(kern[c], hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl->smem);
     if (e != hipSuccess) return e;
   }

@@ -5,7 +5,8 @@
 
 namespace m3 {
 
-const void* persist_kernel_bf16(bool clock) {
+const void* persist_kernel_bf16(bool clock, bool attn) {
+  if (attn) return persist_kernel_bf16_attn(clock);
   return clock ? reinterpret_cast<const void*>(frame_kernel<16, M3_BF16, true>)
                : reinterpret_cast<const void*>(frame_kernel<16, M3_BF16, false>);
 }

@@ -1,0 +1,13 @@
+// persist_bf16_attn.hip -- persistent frame kernels for a bf16 body and
+// lm_head (the depth decoder in int8-g128) that also carry the attention
+// phases (frames with decode attention); see persist.hip and persist_attn.h.
+#include "persist_kernel.h"
+
+namespace m3 {
+
+const void* persist_kernel_bf16_attn(bool clock) {
+  return clock ? reinterpret_cast<const void*>(frame_kernel<16, M3_BF16, true, true>)
+               : reinterpret_cast<const void*>(frame_kernel<16, M3_BF16, false, true>);
+}
+
+}  // namespace m3

@@ -5,7 +5,8 @@
 
 namespace m3 {
 
-const void* persist_kernel_i8row(bool clock) {
+const void* persist_kernel_i8row(bool clock, bool attn) {
+  if (attn) return persist_kernel_i8row_attn(clock);
   return clock ? reinterpret_cast<const void*>(frame_kernel<16, M3_I8ROW, true>)
                : reinterpret_cast<const void*>(frame_kernel<16, M3_I8ROW, false>);
 }

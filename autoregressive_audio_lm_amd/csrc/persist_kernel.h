@@ -1,6 +1,7 @@
 #pragma once
 // persist_kernel.h -- device side of the persistent frame (see persist.hip).
 #include "frame_impl.h"
+#include "persist_attn.h"
 
 namespace m3 {
 namespace {
@@ -11,6 +12,10 @@ namespace {
 // variant 0 = FB, 1 = int8-g128, the epilogue chosen at run time and the
 // operand always staged in LDS (the frame is recorded only when it fits).
 constexpr int kFeedbackVariant = -1;
+// An attention phase (persist_attn.h), carried only by the kernels compiled
+// with ATT (frames with decode attention), so the frames with the identity
+// stub keep their registers.
+constexpr int kAttnVariant = -2;
 
 struct Phase {
   Params p;
@@ -95,7 +100,33 @@ __device__ __forceinline__ void run_variant(CPhasePtr ph, uint8_t* smem, int wg,
       *(const Params*)&ph->p, smem, wg, nwg, wait);
 }
 
-template <int NB, int FB, bool CLK>
+// an attention phase of a kernel compiled with ATT: G = 1, 2, 4 query heads
+// per KV head, chunks of 64 or 128 positions (false: not an attention phase)
+template <bool ATT>
+__device__ __forceinline__ bool run_attention(int variant, CPhasePtr ph, uint8_t* smem, int wg,
+                                              int nwg, uint32_t ebase, int i, uint32_t* err,
+                                              uint64_t* at, size_t cstride) {
+  if constexpr (ATT) {
+    if (variant != kAttnVariant) return false;
+    const AttnArgs& a = *(const AttnArgs*)&ph->p;
+    const int g = a.n_q / a.n_kv;
+    auto staged = [&]() { clock_mark(at, cstride, 1); };
+    if (a.ch == 64) {
+      if (g == 1) attn_phase<1, 64>(a, smem, wg, nwg, ebase, i, err, staged);
+      else if (g == 2) attn_phase<2, 64>(a, smem, wg, nwg, ebase, i, err, staged);
+      else attn_phase<4, 64>(a, smem, wg, nwg, ebase, i, err, staged);
+    } else {
+      if (g == 1) attn_phase<1, 128>(a, smem, wg, nwg, ebase, i, err, staged);
+      else if (g == 2) attn_phase<2, 128>(a, smem, wg, nwg, ebase, i, err, staged);
+      else attn_phase<4, 128>(a, smem, wg, nwg, ebase, i, err, staged);
+    }
+    return true;
+  } else {
+    return false;
+  }
+}
+
+template <int NB, int FB, bool CLK, bool ATT = false>
 __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int nph, uint32_t* flags,
                                                          uint32_t* err, const uint32_t* seq,
                                                          FeedbackArgs fb, uint64_t* clk) {
@@ -117,6 +148,7 @@ __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int np
       if (!wait_flags(flags, nwg, ebase + (uint32_t)i, err, &s_ok)) return;
       clock_mark(at, cstride, 1);
       feedback_run<true>(fb, wg, nwg, c_last, ebase);
+    } else if (run_attention<ATT>(variant, (CPhasePtr)(ph + i), smem, wg, nwg, ebase, i, err, at, cstride)) {
     } else {
       TagWait wait{ebase, i, err, at, cstride};
       const CPhasePtr cp = (CPhasePtr)(ph + i);

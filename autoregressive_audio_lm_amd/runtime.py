@@ -209,10 +209,10 @@ class FrameState:
         dq = c.d_heads * c.d_head_dim
         return {"h": ("th", (L, B, c.hidden)), "qkv": ("tqkv", (L, B, nqkv)),
                 "ho": ("th2", (L, B, c.hidden)), "mlp": ("tmlp", (L, B, c.ffn)),
-                "ao": (None, (L, B, nq)), "u": ("tu", (B, c.d_hidden)),
+                "ao": ("tao", (L, B, nq)), "u": ("tu", (B, c.d_hidden)),
                 "hd": ("thd", (S, DL + 1, B, c.d_hidden)), "dqkv": ("tdqkv", (S, DL, B, 3 * dq)),
                 "hdo": ("thd2", (S, DL, B, c.d_hidden)), "dmlp": ("tdmlp", (S, DL, B, c.d_ffn)),
-                "dao": (None, (S, DL, B, dq))}
+                "dao": ("tdao", (S, DL, B, dq))}
 
     def slots(self, name: str, tagged: bool = False) -> torch.Tensor:
         """A per-stage stream of the last frame: body [n_layers, B, cols] for

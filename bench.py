@@ -146,16 +146,18 @@ def time_frames_persistent(dm, cfg, B, steps, warmup, stream, seed=0, per_launch
     return st, ms, wall
 
 
-def phase_names(cfg):
-    """The persistent frame's phases in order (one GEMV each, then the end)."""
+def phase_names(cfg, attention=False):
+    """The persistent frame's phases in order (one GEMV or attention step
+    each, then the end)."""
+    att = lambda k: [k] if attention else []
     names = []
     for _ in range(cfg["n_layers"]):
-        names += ["body QKV", "body O", "body gate/up", "body down"]
+        names += ["body QKV"] + att("body attention") + ["body O", "body gate/up", "body down"]
     names += ["lm_head + draw 0", "depth input projection"]
     for j in range(1, cfg["n_codebooks"]):
         for l in range(cfg["d_layers"]):
-            names += ["depth QKV (+ gather)" if l == 0 else "depth QKV", "depth O",
-                      "depth gate/up", "depth down"]
+            names += (["depth QKV (+ gather)" if l == 0 else "depth QKV"] + att("depth attention") +
+                      ["depth O", "depth gate/up", "depth down"])
         names += ["depth head + draw"]
     names += ["frame end (draw 7, feedback)"]
     return names
@@ -175,7 +177,7 @@ def phase_clock_table(dm, cfg, B, stream, frames=20, seed=0):
     x0 = synth.activations(B, cfg["H"], 1000 + seed, device="cuda")
     st = runtime.FrameState(dm, B, x0, frame0=0)
     torch.cuda.synchronize()
-    names = phase_names(cfg)
+    names = phase_names(cfg, bool(dm.config.attention))
     rec, ev_ms = [], []
     with torch.cuda.stream(stream):
         st.persistent_create(stream)
@@ -886,16 +888,21 @@ def main():
         dm.set_draw(1.5, 0)
         # the frame with decode attention in place of the stub, near the end
         # of a 60 s song (1500 frames after a 300-token prompt: T about 1800),
-        # graph-replayed; the cache bytes come on top of the weights
+        # graph-replayed and as one persistent launch (B <= 6); the cache
+        # bytes come on top of the weights
         n_att = 20
         dm.set_attention(1, max_pos=2048, pos0=1800 - 3 - n_att // 2)
-        for B in (1, 16):
-            st_a, ms_a, _ = time_frames(dm, cfg, B, n_att, 3, stream, args.seed)
+        for B, path in ((1, "persistent"), (1, "graph"), (2, "persistent"), (2, "graph"),
+                        (6, "persistent"), (6, "graph"), (16, "graph")):
+            if path == "graph":
+                st_a, ms_a, _ = time_frames(dm, cfg, B, n_att, 3, stream, args.seed)
+            else:
+                st_a, ms_a, _ = time_frames_persistent(dm, cfg, B, n_att, 3, stream, args.seed)
             err = int(st_a.err.item())
             st_a.release()
             del st_a
             kv = 36 * B * 8 * 1800 * 128 * 2 * 2
-            attention_frames.append({"preset": args.preset, "B": B, "T": 1800, "path": "graph",
+            attention_frames.append({"preset": args.preset, "B": B, "T": 1800, "path": path,
                                      "ms_per_frame": round(ms_a, 4),
                                      "frames_per_s": round(1e3 / ms_a, 2),
                                      "weight_plus_kv_GB_s": round((fbytes + kv) * 1e3 / ms_a / 1e9, 1),

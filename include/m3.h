@@ -376,8 +376,8 @@ typedef struct {
    * every frame).  max_pos: cached positions per body layer (1 ..
    * M3_MAX_POS); 0 <= pos0 < max_pos.  A frame whose position reaches max_pos
    * is refused on the GPU: it rewrites slot max_pos - 1, attends over max_pos
-   * positions and sets the state's err word to M3_ERR_ATTN_FULL.  Eager and
-   * graph frames only. */
+   * positions and sets the state's err word to M3_ERR_ATTN_FULL (a
+   * persistent frame then ends its waits, as below). */
   int attention;
   int max_pos;
   int pos0;
@@ -475,6 +475,12 @@ typedef struct {
   size_t kcache, vcache;   /* bf16 [n_layers][B][n_kv][max_pos][128]          */
   size_t dkcache, dvcache; /* bf16 [d_layers][B][d_heads][8][128]             */
   size_t attn_ws;  /* m3_decode_attention's workspace at T = max_pos           */
+  size_t tao, tdao; /* u32 words [L][B, nq], [S][DL][B, d_hidden]: the
+                      persistent frame's attention outputs, shaped as ao, dao  */
+  size_t trec;     /* [L][B][n_kv][chunks][nq / n_kv][2 + 128] 64-bit words (fp32
+                      value | 16-bit producer tag << 32): the persistent frame's
+                      chunk records of each body layer's attention (zero-sized
+                      when one chunk covers max_pos)                          */
   size_t stop;     /* int32 [B]: 0, or 1 + the frame that drew the end token    */
   size_t total;
 } m3_frame_layout;
@@ -531,7 +537,10 @@ int m3_depth_graph_create(const m3_model* model, void* state, int B, int32_t* co
 
 /* Persistent form of the frame: the same steps, with the same results, run as
  * ONE cooperative launch per frame.  One workgroup per compute unit walks the
- * frame's GEMVs in order; each workgroup requests the first weight tiles of
+ * frame's steps in order (GEMVs and, with attention = 1, each layer's
+ * attention: q/k norm + RoPE, the cache write, the chunks' partial softmax
+ * and their merge as one step, with the decode attention calls' chunking and
+ * arithmetic; G = n_q / n_kv of 1, 2 or 4); each workgroup requests the first weight tiles of
  * the next GEMV before it waits for the previous GEMV's outputs, so HBM keeps
  * streaming across the ~270 dependencies of a frame (TensorFold PR #987: one submission per frame;
  * "MiniMax Music 3, local": the AR stages are bound by memory bandwidth).
@@ -545,7 +554,7 @@ int m3_depth_graph_create(const m3_model* model, void* state, int B, int32_t* co
  * epoch of the tags (below), so nothing a launch that gave up left behind is
  * taken for an operand later.
  * Inside the launch the intermediate streams (body and depth residuals, QKV,
- * MLP, depth input) are the state's tagged buffers: 32-bit words holding the
+ * MLP, depth input, attention outputs) are the state's tagged buffers: 32-bit words holding the
  * bf16 value and the tag of the step that wrote it; a step waits for its
  * operand by reading it until the tags are the ones its producer writes (one
  * store and one load per dependency, no barrier).  x, h, logits, codes, the
@@ -580,19 +589,21 @@ int m3_frame_persistent_clock(void* handle, uint64_t* clk, size_t clk_bytes, int
 /* The persistent frame's steps as records of the memory each step reads and
  * writes (host only: nothing is launched and no memory is touched; the state
  * and model pointers only fix addresses).  Record i is step i of the
- * persistent launch (a GEMV, or the frame end, which runs after every
- * workgroup has finished every GEMV); a region is `rows` rows of bytes
- * [base + r stride + c0, base + r stride + c1), with the step that produced
- * what is read (-1: written
- * before the launch, or by an earlier GEMV of the frame for the frame end)
- * and whether its 32-bit words carry the producer's tag.  A consumer waits
- * for the tags of its producer, so the ordering this rests on can be checked
- * from the table: every tagged input is written by its producer, earlier,
- * and no byte is written twice in a frame.  Returns the number of steps, or
- * M3_ERR_* (M3_ERR_WORKSPACE: out has fewer than that many records; out may
- * be NULL to count; M3_ERR_FORMAT: the frame has no persistent form). */
+ * persistent launch (a GEMV, an attention step, or the frame end, which runs
+ * after every workgroup has finished every other step); a region is `rows`
+ * rows of bytes [base + r stride + c0, base + r stride + c1), with the step
+ * that produced what is read (-1: written before the launch, or by an
+ * earlier step of the frame for the frame end; for an attention step's
+ * cache reads, by the step itself or by the same layer's attention at the
+ * frame's earlier codebook steps) and whether its words carry the producer's
+ * tag.  A consumer waits for the tags of its producer, so the ordering this
+ * rests on can be checked from the table: every tagged input is written by
+ * its producer, earlier, and no byte is written twice in a frame.  Returns
+ * the number of steps, or M3_ERR_* (M3_ERR_WORKSPACE: out has fewer than
+ * that many records; out may be NULL to count; M3_ERR_FORMAT: the frame has
+ * no persistent form). */
 #define M3_PHASE_MAX_REGIONS 4
-enum { M3_PHASE_GEMV = 0, M3_PHASE_FRAME_END = 1 };
+enum { M3_PHASE_GEMV = 0, M3_PHASE_FRAME_END = 1, M3_PHASE_ATTENTION = 2 };
 typedef struct {
   uint64_t base, stride;
   int32_t rows;

@@ -46,8 +46,8 @@ def read_frame(st, tagged: bool) -> dict:
     got = {k: rd(st.slots(k, tagged)) for k in ("h", "qkv", "ho", "mlp", "u", "hd", "dqkv", "hdo",
                                                  "dmlp")}
     if st.dm.config.attention:
-        got["ao"] = synth.bits(st.slots("ao"))
-        got["dao"] = synth.bits(st.slots("dao"))
+        got["ao"] = rd(st.slots("ao", tagged))
+        got["dao"] = rd(st.slots("dao", tagged))
     got.update(logits=st.logits.cpu().numpy(), dlogits=st.dlogits.cpu().numpy(),
                codes=st.codes.cpu().numpy(), x=synth.bits(st.x))
     return got

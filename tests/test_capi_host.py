@@ -346,7 +346,7 @@ def test_frame_layout_stage_slots(L, name, B):
         span = getattr(lay, b) - getattr(lay, a)
         assert tneed[a] <= span < tneed[a] + 256, (a, span, tneed[a])
     # without attention the attention buffers take no room; the rows' stop words come last
-    assert lay.rope == lay.aq == lay.ao == lay.dao == lay.kcache == lay.stop
+    assert lay.rope == lay.aq == lay.ao == lay.dao == lay.kcache == lay.trec == lay.stop
     assert lay.total == lay.stop + (B * 4 + 255) // 256 * 256
     # with the end token the semantic logits have one more column (rows padded to 8)
     ce = make_config(cfg, **configs.PRESETS["A"], end_token=True)
@@ -379,8 +379,16 @@ def test_frame_layout_with_attention(L):
     dkv = cfg["d_layers"] * B * cfg["d_heads"] * 8 * 128 * 2
     assert la.dvcache - la.dkcache >= dkv and la.attn_ws - la.dvcache >= dkv
     assert la.aq - la.rope >= max_pos * 64 * 2 * 4
-    assert la.stop - la.attn_ws == L.m3_attention_workspace_bytes(B, cfg["n_heads"],
-                                                                   cfg["n_kv_heads"], max_pos)
+    assert la.tao - la.attn_ws == L.m3_attention_workspace_bytes(B, cfg["n_heads"],
+                                                                  cfg["n_kv_heads"], max_pos)
+    # the persistent frame's attention outputs (u32 words) and chunk records:
+    # at B = 2 over 2048 positions, chunks of 128 (2 rows x 8 KV heads x 16
+    # chunks fill 256 workgroups), 16 chunks of [2 + 128] 64-bit words per
+    # row and query head
+    assert la.tdao - la.tao == cfg["n_layers"] * B * cfg["n_heads"] * 128 * 4
+    assert la.trec - la.tdao == (cfg["n_codebooks"] - 1) * cfg["d_layers"] * B * cfg["D"] * 4
+    assert la.stop - la.trec == cfg["n_layers"] * B * cfg["n_heads"] * 16 * 130 * 8
+    assert lp.tao == lp.tdao == lp.trec == lp.stop
     assert la.total > lp.total + 2 * kv
     # attention settings out of range are refused
     for bad in (dict(attention=2, max_pos=16), dict(attention=1, max_pos=0),

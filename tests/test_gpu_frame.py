@@ -426,63 +426,151 @@ def attn(request):
     return cfg, dm, om
 
 
+# a longer cache whose first 200 positions hold seeded keys and values, so
+# that the body's attention spans several chunks and merges them
+LONG_MAX_POS, LONG_POS0 = 300, 200
+
+
+@pytest.fixture(scope="module")
+def attn_long():
+    cfg = configs.config("frame-small")
+    md_dev = synth.make_model(cfg, **configs.PRESETS["A"], seed=29, device="cpu")
+    md_np = synth.model_to_numpy(md_dev)
+    dm = runtime.DecodeModel(_to(md_dev, DEV), seed=5, temperature=1.0, attention=1,
+                             max_pos=LONG_MAX_POS, pos0=LONG_POS0)
+    om = O.OracleModel(md_np, attention=1, max_pos=LONG_MAX_POS, pos0=LONG_POS0)
+    return cfg, dm, om
+
+
+def _seed_caches(st, seed):
+    """Seeded keys and values (bf16, unit normal) at every body cache position."""
+    c, B = st.dm.config, st.B
+    g = torch.Generator().manual_seed(seed)
+    for name in ("kcache", "vcache"):
+        n = c.n_layers * B * c.n_kv_heads * c.max_pos * 128
+        v = torch.randn(n, generator=g).to(torch.bfloat16).to(DEV)
+        off = getattr(st.layout, name)
+        st.state[off:off + 2 * n].view(torch.bfloat16).copy_(v)
+    torch.cuda.synchronize()
+
+
+def _attention_stages(cfg, dm, om, path, B, nframes, pos0, seed_caches):
+    import stages
+    from autoregressive_audio_lm_amd import _lib
+    x0 = synth.activations(B, cfg["H"], 50 + B)
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
+    if seed_caches:
+        _seed_caches(st, 70 + B)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    if path == "persistent":
+        try:
+            st.persistent_create(s)
+        except _lib.M3ValueError:
+            st.release()
+            pytest.skip(f"the persistent frame does not take B = {B} at this size")
+    x = synth.bits(x0)
+    for f in range(nframes):
+        before = stages.read_caches(st)
+        with torch.cuda.stream(s):
+            if path == "eager":
+                st.decode(s)
+            else:
+                st.persistent_launch(s)
+        s.synchronize()
+        assert int(st.err.item()) == 0
+        got = stages.read_frame(st, tagged=path == "persistent")
+        stats = stages.check_frame(om, got, x, seed=5, frame=f,
+                                   attn=dict(pos=pos0 + f, before=before,
+                                             after=stages.read_caches(st)))
+        print(f"attention {path} B={B} frame {f}: {stats.summary()}", flush=True)
+        x = got["x"]
+    st.release()
+
+
 @pytest.mark.parametrize("B", [1, 3, 6, 16])
-def test_attention_frame_stages_match_oracle(attn, B):
+@pytest.mark.parametrize("path", ["eager", "persistent"])
+def test_attention_frame_stages_match_oracle(attn, path, B):
     """Frames 0 .. 5 at body positions 9 .. 14 (the prompt's positions hold
     zeros), every stage against the oracle on the GPU's own input of that
     stage: body layers attend over the GPU's cache as it was before the frame
     plus the slot each side writes at the frame's position (the written
     slots compared too), depth steps over the GPU's slots of the frame's
     earlier codebook positions (tests/stages.py)."""
+    cfg, dm, om = attn
+    _attention_stages(cfg, dm, om, path, B, 6, ATTN_POS0, False)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+@pytest.mark.parametrize("path", ["eager", "persistent"])
+def test_long_attention_frame_stages_match_oracle(attn_long, path, B):
+    """The same at positions 200 .. 202 over seeded keys and values: the
+    body's attention takes four chunks of 64 positions and their merge."""
+    cfg, dm, om = attn_long
+    _attention_stages(cfg, dm, om, path, B, 3, LONG_POS0, True)
+
+
+def _untag_slots(st, names):
     import stages
-    cfg, dm, om = attn
-    x0 = synth.activations(B, cfg["H"], 50 + B)
-    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
-    torch.cuda.synchronize()
-    x = synth.bits(x0)
-    for f in range(6):
-        before = stages.read_caches(st)
-        st.decode()
-        torch.cuda.synchronize()
-        got = stages.read_frame(st, tagged=False)
-        stats = stages.check_frame(om, got, x, seed=5, frame=f,
-                                   attn=dict(pos=ATTN_POS0 + f, before=before,
-                                             after=stages.read_caches(st)))
-        print(f"attention B={B} frame {f}: {stats.summary()}", flush=True)
-        x = got["x"]
-    assert int(st.err.item()) == 0
+    return {k: stages.untag(st.slots(k, True)) for k in names}
 
 
-def test_attention_graph_replay_equals_eager_and_persistent_refused(attn):
-    from autoregressive_audio_lm_amd import _lib
-    cfg, dm, om = attn
-    B = 2
+@pytest.mark.parametrize("long", [False, True])
+@pytest.mark.parametrize("B", [1, 2, 5])
+def test_attention_graph_and_persistent_equal_eager(attn, attn_long, B, long):
+    """Graph replays and persistent launches of attention frames give the
+    eager frames' bytes: codes of every frame, every operation's output, the
+    logits and both KV caches (the persistent frame's attention phases use the
+    launches' arithmetic and chunking; long: several chunks and their merge)."""
+    import stages
+    cfg, dm, om = attn_long if long else attn
     x0 = synth.activations(B, cfg["H"], 63).to(DEV)
+    names = ("h", "qkv", "ho", "mlp", "ao", "u", "hd", "dqkv", "hdo", "dmlp", "dao")
     eager = runtime.FrameState(dm, B, x0, frame0=0)
+    if long:
+        _seed_caches(eager, 90 + B)
     seq = []
     for _ in range(4):
         eager.decode()
         seq.append(eager.codes.clone())
     torch.cuda.synchronize()
+    ref = {k: synth.bits(eager.slots(k)) for k in names}
+    ref_caches = stages.read_caches(eager)
     s = torch.cuda.Stream()
     graphed = runtime.FrameState(dm, B, x0, frame0=0)
+    pers = runtime.FrameState(dm, B, x0, frame0=0)
+    if long:
+        _seed_caches(graphed, 90 + B)
+        _seed_caches(pers, 90 + B)
     with torch.cuda.stream(s):
         graphed.capture(s)
+        pers.persistent_create(s)
         for k in range(4):
             graphed.replay(s)         # each replay reads the next position from the GPU
+            pers.persistent_launch(s)
             s.synchronize()
             assert torch.equal(graphed.codes, seq[k])
+            assert torch.equal(pers.codes, seq[k]), k
             torch.cuda.synchronize()
-    assert torch.equal(eager.x, graphed.x)
+    assert int(pers.err.item()) == 0
+    assert torch.equal(eager.x, graphed.x) and torch.equal(eager.x, pers.x)
     assert torch.equal(eager.state, graphed.state)     # caches included
+    got = _untag_slots(pers, names)
+    for k in names:
+        assert np.array_equal(got[k], ref[k]), k
+    assert torch.equal(eager.logits, pers.logits) and torch.equal(eager.dlogits, pers.dlogits)
+    caches = stages.read_caches(pers)
+    for k in ref_caches:
+        assert np.array_equal(caches[k], ref_caches[k]), k
     graphed.release()
-    with pytest.raises(_lib.M3Error):
-        runtime.FrameState(dm, B, x0).persistent_create()
+    pers.release()
 
 
 def test_attention_frame_past_the_cache_sets_err(attn):
     """A frame whose position reaches max_pos is refused on the GPU: it keeps
-    to the last slot and flags the state's err word."""
+    to the last slot and flags the state's err word (eager and graph frames);
+    a persistent frame raises the err word too, which ends the waits of its
+    launch and every later launch until the frame is recorded again."""
     from autoregressive_audio_lm_amd import _lib
     cfg, dm, om = attn
     B = 1
@@ -494,6 +582,22 @@ def test_attention_frame_past_the_cache_sets_err(attn):
     st.decode()
     torch.cuda.synchronize()
     assert int(st.err.item()) == _lib.M3_ERR_ATTN_FULL
+    st.release()
+    pers = runtime.FrameState(dm, B, x0, frame0=ATTN_MAX_POS - ATTN_POS0 - 1)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        pers.persistent_create(s)
+        pers.persistent_launch(s)
+        s.synchronize()
+        assert int(pers.err.item()) == 0
+        pers.persistent_launch(s)
+        s.synchronize()
+        assert int(pers.err.item()) != 0
+        frame = int(pers.frame.item())
+        pers.persistent_launch(s)                    # computes nothing
+        s.synchronize()
+        assert int(pers.frame.item()) == frame
+    pers.release()
 
 
 # ---- the end token (DiffSynth-Studio MiniMax-Music3 stage 2: the semantic

@@ -154,25 +154,8 @@ def test_full_size_persistent_refuses_unstaged_operands():
         st.persistent_create()
 
 
-def test_full_size_attention_frame_stages():
-    """Frames with decode attention at the full model size near the end of a
-    60 s song (positions 1797 and 1798): every layer's cache holds seeded keys
-    and values at the earlier positions; every stage of two chained
-    graph-replayed frames is compared with the oracle on the GPU's own input
-    of that stage, body layers attending over the cache as it was before the
-    frame plus the slot each side writes (the GPU's written slots compared
-    too), depth steps over the GPU's earlier codebook positions."""
-    cfg = configs.config("frame-full")
-    B, max_pos, pos0 = 1, 2048, 1797
-    md = synth.make_model(cfg, **configs.PRESETS["A"], seed=19, device=DEV)
-    md_np = synth.model_to_numpy(md)
-    dm = runtime.DecodeModel(md, seed=9, free_sources=True, attention=1, max_pos=max_pos,
-                             pos0=pos0)
-    del md
-    torch.cuda.empty_cache()
-    om = O.OracleModel(md_np, attention=1, max_pos=max_pos, pos0=pos0)
-    x0 = synth.activations(B, cfg["H"], 510)
-    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
+def _seed_full_caches(st, cfg, B, max_pos, pos0):
+    """Seeded keys and values at the positions before pos0 of every layer."""
     L, nkv = cfg["n_layers"], cfg["n_kv_heads"]
     n = L * B * nkv * max_pos * 128
     for name, seed in (("kcache", 700), ("vcache", 701)):
@@ -180,21 +163,89 @@ def test_full_size_attention_frame_stages():
         cache = st.state[off:off + 2 * n].view(torch.bfloat16).view(L, B, nkv, max_pos, 128)
         cache[:, :, :, :pos0] = synth.normal_bf16((L, B, nkv, pos0, 128), seed, 1.0, DEV)
     torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def full_attn():
+    cfg = configs.config("frame-full")
+    max_pos, pos0 = 2048, 1797
+    md = synth.make_model(cfg, **configs.PRESETS["A"], seed=19, device=DEV)
+    md_np = synth.model_to_numpy(md)
+    dm = runtime.DecodeModel(md, seed=9, free_sources=True, attention=1, max_pos=max_pos,
+                             pos0=pos0)
+    del md
+    torch.cuda.empty_cache()
+    om = O.OracleModel(md_np, attention=1, max_pos=max_pos, pos0=pos0)
+    yield cfg, dm, om, max_pos, pos0
+    del dm, om
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("path", ["graph", "persistent"])
+def test_full_size_attention_frame_stages(full_attn, path):
+    """Frames with decode attention at the full model size near the end of a
+    60 s song (positions 1797 and 1798): every layer's cache holds seeded keys
+    and values at the earlier positions; every stage of two chained
+    graph-replayed or persistent frames is compared with the oracle on the
+    GPU's own input of that stage, body layers attending over the cache as it
+    was before the frame plus the slot each side writes (the GPU's written
+    slots compared too), depth steps over the GPU's earlier codebook
+    positions."""
+    cfg, dm, om, max_pos, pos0 = full_attn
+    B = 1
+    x0 = synth.activations(B, cfg["H"], 510)
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
+    _seed_full_caches(st, cfg, B, max_pos, pos0)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        st.capture(s)
+        if path == "graph":
+            st.capture(s)
+        else:
+            st.persistent_create(s)
     x = synth.bits(x0)
     for f in (0, 1):
         before = stages.read_caches(st)
         with torch.cuda.stream(s):
-            st.replay(s)
+            if path == "graph":
+                st.replay(s)
+            else:
+                st.persistent_launch(s)
         s.synchronize()
         assert int(st.err.item()) == 0
-        got = stages.read_frame(st, tagged=False)
+        got = stages.read_frame(st, tagged=path == "persistent")
         after = stages.read_caches(st)
         stats = stages.check_frame(om, got, x, seed=9, frame=f,
                                    attn=dict(pos=pos0 + f, before=before, after=after))
-        print(f"attention frame at position {pos0 + f}: {stats.summary()}; codes "
+        print(f"attention {path} frame at position {pos0 + f}: {stats.summary()}; codes "
               f"{got['codes'].tolist()}", flush=True)
         x = got["x"]
     st.release()
+
+
+@pytest.mark.parametrize("B", [1, 2, 6])
+def test_full_size_attention_persistent_equals_graph(full_attn, B):
+    """Persistent and graph-replayed attention frames at the full model size
+    give identical bytes (codes, the fed-back input, the body output, the
+    logits and every KV cache) over three chained frames."""
+    cfg, dm, om, max_pos, pos0 = full_attn
+    x0 = synth.activations(B, cfg["H"], 905, device=DEV)
+    g = runtime.FrameState(dm, B, x0, frame0=0)
+    p = runtime.FrameState(dm, B, x0, frame0=0)
+    for st in (g, p):
+        _seed_full_caches(st, cfg, B, max_pos, pos0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g.capture(s)
+        p.persistent_create(s)
+        for f in range(3):
+            g.replay(s)
+            p.persistent_launch(s)
+            s.synchronize()
+            assert int(p.err.item()) == 0 and int(g.err.item()) == 0
+            assert torch.equal(g.codes, p.codes), f
+            for name in ("x", "h", "logits"):
+                assert torch.equal(getattr(g, name), getattr(p, name)), (f, name)
+    lo, hi = g.layout.kcache, g.layout.attn_ws     # kcache, vcache, dkcache, dvcache
+    assert torch.equal(g.state[lo:hi], p.state[lo:hi])      # every cache, every position
+    g.release()
+    p.release()

@@ -8,7 +8,11 @@ producer comes earlier; (2) no byte is written by two steps of one frame, so
 no newer tag can replace the awaited one while a reader still waits for it;
 (3) what a GEMV reads untagged is written before the launch (only the frame
 end, which runs after every workgroup finished every GEMV, writes it again);
-(4) a frame has fewer steps than the tag period (512)."""
+(4) a frame has fewer steps than the tag period (512); (5) what an attention
+step reads untagged (its KV cache) is written before the launch, by the step
+itself, or by an attention step it depends on through the tags it waits for
+(the depth decoder's cache, filled one position per codebook step; the kernel
+gives those rows' items to the workgroup that wrote them)."""
 import ctypes
 
 import pytest
@@ -73,9 +77,18 @@ def violations(recs):
     n = len(recs)
     if n >= 512:
         bad.append(f"{n} steps: tags repeat within a frame")
-    if recs[-1]["kind"] != _lib.PHASE_FRAME_END or any(r["kind"] != _lib.PHASE_GEMV
-                                                         for r in recs[:-1]):
+    if recs[-1]["kind"] != _lib.PHASE_FRAME_END or any(
+            r["kind"] not in (_lib.PHASE_GEMV, _lib.PHASE_ATTENTION) for r in recs[:-1]):
         bad.append("the frame end is not the last step, or not the only one")
+    # the steps each step depends on through the tags it waits for
+    anc = []
+    for i, r in enumerate(recs):
+        a = set()
+        for g in r["inp"]:
+            p = g["producer"]
+            if g["tagged"] and 0 <= p < i:
+                a |= {p} | anc[p]
+        anc.append(a)
     writes = []                              # (lo, hi, step, tagged)
     for i, r in enumerate(recs):
         for o in r["out"]:
@@ -108,6 +121,12 @@ def violations(recs):
                     if any(w[2] != n - 1 for w in cover):
                         bad.append(f"step {i} reads untagged bytes that step(s) "
                                    f"{sorted({w[2] for w in cover})} write in the frame")
+                elif r["kind"] == _lib.PHASE_ATTENTION:
+                    if any(w[2] != i and not (w[2] in anc[i] and
+                                              recs[w[2]]["kind"] == _lib.PHASE_ATTENTION)
+                           for w in cover):
+                        bad.append(f"attention step {i} reads untagged bytes that step(s) "
+                                   f"{sorted({w[2] for w in cover})} write in the frame")
                 elif any(w[2] >= i for w in cover):
                     bad.append(f"the frame end reads bytes it writes itself")
     return bad
@@ -128,6 +147,60 @@ def test_phase_table_ordering(name, preset, B):
     S = cfg["n_codebooks"] - 1
     assert len(recs) == 4 * cfg["n_layers"] + 2 + S * (4 * cfg["d_layers"] + 1) + 1
     assert violations(recs) == []
+
+
+ATTN_CASES = [("frame-small", "A", 1, 40), ("frame-small", "A", 3, 300),
+              ("frame-small", "C", 2, 64), ("frame-full", "A", 1, 2048),
+              ("frame-full", "B", 6, 2048), ("frame-full", "A", 2, 100)]
+
+
+@pytest.mark.parametrize("name,preset,B,max_pos", ATTN_CASES)
+def test_phase_table_ordering_with_attention(name, preset, B, max_pos):
+    """Frames with decode attention: an attention step per body layer and per
+    depth layer run, between QKV and O."""
+    cfg = configs.config(name)
+    m, keep = fake_model(cfg, preset)
+    m.cfg.attention, m.cfg.max_pos, m.cfg.pos0 = 1, max_pos, 0
+    recs = phase_table(m, B)
+    S = cfg["n_codebooks"] - 1
+    assert len(recs) == 5 * cfg["n_layers"] + 2 + S * (5 * cfg["d_layers"] + 1) + 1
+    kinds = [r["kind"] for r in recs]
+    assert kinds[:5] == [_lib.PHASE_GEMV, _lib.PHASE_ATTENTION] + [_lib.PHASE_GEMV] * 3
+    assert kinds.count(_lib.PHASE_ATTENTION) == cfg["n_layers"] + S * cfg["d_layers"]
+    assert violations(recs) == []
+    # O waits for the attention step's output words
+    o = recs[2]
+    assert any(g["tagged"] and g["producer"] == 1 for g in o["inp"])
+
+
+def test_validator_finds_planted_attention_mistakes():
+    """The attention rules catch a table broken on purpose (on the host)."""
+    import copy
+    cfg = configs.config("frame-small")
+    m, keep = fake_model(cfg, "A")
+    m.cfg.attention, m.cfg.max_pos, m.cfg.pos0 = 1, 300, 0
+    recs = phase_table(m, 2)
+    assert violations(recs) == []
+    att = [i for i, r in enumerate(recs) if r["kind"] == _lib.PHASE_ATTENTION]
+    depth = [i for i in att if i > 5 * cfg["n_layers"]]
+    # a depth attention step that no longer waits for its QKV: what the layer's
+    # earlier steps wrote into the cache is then read without an ordering
+    r1 = copy.deepcopy(recs)
+    j = depth[cfg["d_layers"]]           # the first layer at the second codebook step
+    for g in r1[j]["inp"]:
+        if g["tagged"]:
+            g["tagged"] = False
+    assert violations(r1)
+    # a GEMV reading a KV cache that an attention step writes
+    r2 = copy.deepcopy(recs)
+    cache = copy.deepcopy(next(g for g in recs[att[0]]["out"] if not g["tagged"]))
+    r2[att[0] + 1]["inp"].append(cache)
+    assert violations(r2)
+    # O reading the attention output as if the QKV GEMV had written it
+    r3 = copy.deepcopy(recs)
+    g = next(g for g in r3[att[0] + 1]["inp"] if g["tagged"] and g["producer"] == att[0])
+    g["producer"] = att[0] - 1
+    assert violations(r3)
 
 
 def test_validator_finds_planted_mistakes():
