@@ -123,10 +123,13 @@ __device__ __forceinline__ void attn_reload_kv_at(AttnRegs<G, CH>& R, const uint
 // The chunk's n positions (1 <= n <= CH) against the G heads.  out(h, d, A,
 // M, L) receives, for every head h and dimension d, the chunk's P.V sum A,
 // maximum score M (base 2) and sum of exponentials L.  The 256 threads (tid
-// 0 .. 255) pass three workgroup barriers.
+// 0 .. 255) pass three workgroup barriers.  q: nullptr to take the heads
+// from R.qr (attn_load_q), or their rows in LDS, read where pass 1 needs
+// them (fewer registers; the same products in the same order).
 template <int G, int CH, class Out>
 __device__ __forceinline__ void attn_compute(const AttnRegs<G, CH>& R, int n, float scale2, int tid,
-                                             AttnLds<G, CH>& L, Out&& out) {
+                                             AttnLds<G, CH>& L, Out&& out,
+                                             const uint16_t* q = nullptr) {
   constexpr int PJ = AttnRegs<G, CH>::PJ, PI = AttnRegs<G, CH>::PI, WP = AttnRegs<G, CH>::WP;
   const int lane = tid & 63, wave = tid >> 6, grp = tid >> 2, li = tid & 3;
   // pass 1: scores (base 2, scale folded in); masked positions get -inf
@@ -138,10 +141,12 @@ __device__ __forceinline__ void attn_compute(const AttnRegs<G, CH>& R, int n, fl
       float s = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        s = dot2(R.qr[h][c].x, R.kr[j][c].x, s);
-        s = dot2(R.qr[h][c].y, R.kr[j][c].y, s);
-        s = dot2(R.qr[h][c].z, R.kr[j][c].z, s);
-        s = dot2(R.qr[h][c].w, R.kr[j][c].w, s);
+        const uint4 qv = q ? *reinterpret_cast<const uint4*>(q + (size_t)h * kHD + 8 * (4 * c + li))
+                           : R.qr[h][c];
+        s = dot2(qv.x, R.kr[j][c].x, s);
+        s = dot2(qv.y, R.kr[j][c].y, s);
+        s = dot2(qv.z, R.kr[j][c].z, s);
+        s = dot2(qv.w, R.kr[j][c].w, s);
       }
       s += dpp_f<0xB1>(s);                       // the 4 lanes of the group
       s += dpp_f<0x4E>(s);

@@ -55,37 +55,52 @@ __device__ __forceinline__ float rec_load(const uint64_t* p, uint32_t tag, uint3
 // One (row b, query head qh) merge by 128 threads (d = dimension): chunk c's
 // maximum and sum are held by lane c % 64; the maximum over all chunks, then
 // L = sum l_c e_c and A = sum a_c e_c with e_c = 2^(m_c - M), accumulated in
-// chunk order with the merge kernel's fused multiply-adds.
+// chunk order with the merge kernel's fused multiply-adds.  Each lane first
+// waits for its chunk's maximum; the sums and this thread's values of up to
+// kBatch chunks are then requested at once (by then the records are, as a
+// rule, complete, so they come back in one round trip).
 template <int G>
 __device__ __forceinline__ void attn_merge_one(const AttnArgs& a, int b, int qh, int nc, int d,
-                                               uint32_t ty, uint32_t* err) {
-  const int kvh = qh / G, h = qh % G, lane = threadIdx.x & 63;
+                                               int lane, uint32_t ty, uint32_t* err) {
+  constexpr int kBatch = 32;
+  const int kvh = qh / G, h = qh % G;
   const size_t stride = (size_t)G * (2 + kHD);
   const uint64_t* w = a.rec + (((size_t)b * a.n_kv + kvh) * a.nchunks * G + h) * (2 + kHD);
-  float M = -INFINITY;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, rec_load(w + c * stride, ty, err));
+  auto fix = [&](uint64_t& v, const uint64_t* p) {     // wait for the record's tag
+    long n = 0;
+    while ((uint32_t)(v >> 32) != ty && spin_more(n, err)) v = M3_COH_LOAD(p);
+  };
+  float M = -INFINITY, m0 = -INFINITY;
+  if (lane < nc) m0 = M = rec_load(w + (size_t)lane * stride, ty, err);
+  for (int c = lane + 64; c < nc; c += 64) M = fmaxf(M, rec_load(w + c * stride, ty, err));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float L = 0.f, A = 0.f;
-  constexpr int kBatch = 16;
   for (int c0 = 0; c0 < nc; c0 += 64) {
     const int c = c0 + lane, cn = min(64, nc - c0);
+    const uint64_t* wl = w + (size_t)c * stride + 1;
+    uint64_t lr = c < nc ? M3_COH_LOAD(wl) : 0;
+    uint64_t raw[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      raw[u] = u < cn ? M3_COH_LOAD(w + (size_t)(c0 + u) * stride + 2 + d) : 0;
     float e = 0.f, l = 0.f;
     if (c < nc) {
-      e = exp2f(rec_load(w + c * stride, ty, err) - M);
-      l = rec_load(w + c * stride + 1, ty, err);
+      const float mv = c0 == 0 ? m0 : rec_load(w + c * stride, ty, err);
+      e = exp2f(mv - M);
+      fix(lr, wl);
+      l = __uint_as_float((uint32_t)lr);
     }
     for (int u0 = 0; u0 < cn; u0 += kBatch) {
-      uint64_t raw[kBatch];
+      if (u0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        raw[u] = u0 + u < cn ? M3_COH_LOAD(w + (size_t)(c0 + u0 + u) * stride + 2 + d) : 0;
+        for (int u = 0; u < kBatch; ++u)
+          raw[u] = u0 + u < cn ? M3_COH_LOAD(w + (size_t)(c0 + u0 + u) * stride + 2 + d) : 0;
+      }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (u0 + u >= cn) break;
-        long ns = 0;
-        while ((uint32_t)(raw[u] >> 32) != ty && spin_more(ns, err))
-          raw[u] = M3_COH_LOAD(w + (size_t)(c0 + u0 + u) * stride + 2 + d);
+        fix(raw[u], w + (size_t)(c0 + u0 + u) * stride + 2 + d);
         const float eu = __shfl(e, u0 + u), lu = __shfl(l, u0 + u);
         L = fmaf(lu, eu, L);
         A = fmaf(__uint_as_float((uint32_t)raw[u]), eu, A);
@@ -98,26 +113,27 @@ __device__ __forceinline__ void attn_merge_one(const AttnArgs& a, int b, int qh,
 // The whole attention phase for one workgroup (512 threads).  ebase: the
 // launch's epoch base; phase: this phase's index; staged(): called once the
 // first items' q are staged (the phase clock).
-//
-// Not inlined: the frame kernel's GEMV phases run at the register limit, and
-// a call keeps the attention's registers (saved and restored around it)
-// from pushing theirs into scratch.
 template <int G, int CH, class Staged>
-__device__ __attribute__((noinline)) void attn_phase(const AttnArgs& a, uint8_t* smem, int wg,
-                                                     int nwg, uint32_t ebase, int phase,
-                                                     uint32_t* err, Staged staged) {
+__device__ __forceinline__ void attn_phase(const AttnArgs& a, uint8_t* smem, int wg, int nwg,
+                                           uint32_t ebase, int phase, uint32_t* err,
+                                           Staged staged) {
   const uint32_t tq = tag_of(a.pqkv, ebase), ty = tag_of(phase, ebase);
+  // the thread index through an opaque copy: what the phase derives from it
+  // is computed here, not hoisted out of the frame's phase loop, where it
+  // would hold registers through the GEMV phases (which run at the limit)
+  int tx = threadIdx.x;
+  asm volatile("" : "+v"(tx));
   int pos = a.pos;
   if (a.frame) {
     // a frame past the cache writes the last slot and raises the error
     // word, which ends the launch's waits (the state must be recorded again)
     const long p = (long)a.pos0 + (long)*a.frame;
     pos = p < a.max_pos ? (int)p : a.max_pos - 1;
-    if (p >= a.max_pos && wg == 0 && threadIdx.x == 0) st4<true>(err, 0, M3_ERR_ATTN_FULL);
+    if (p >= a.max_pos && wg == 0 && tx == 0) st4<true>(err, 0, M3_ERR_ATTN_FULL);
   }
   const int T = pos + 1, nc = (T + CH - 1) / CH;
   const int nbk = a.B * a.n_kv, items = nbk * nc;
-  const int half = threadIdx.x >> 8, tid = threadIdx.x & 255, lane = tid & 63, hw = tid >> 6;
+  const int half = tx >> 8, tid = tx & 255, lane = tid & 63, hw = tid >> 6;
   AttnLds<G, CH>& L = reinterpret_cast<AttnLds<G, CH>*>(smem)[half];
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem + 2 * sizeof(AttnLds<G, CH>)) + half * G * kHD;
   // item i (chunk-major: the chunks holding pos, which wait for QKV's K and V
@@ -163,7 +179,6 @@ __device__ __attribute__((noinline)) void attn_phase(const AttnArgs& a, uint8_t*
     __syncthreads();
     if (r0 == 0) staged();
     if (last) attn_reload_kv_at(R, kb, vb, t0, n, tid, pos);
-    attn_load_q(R, qs, tid);
     attn_compute(R, n, a.scale2, tid, L, [&](int h, int d, float A, float Mx, float Ls) {
       if (!live) return;
       if (nc == 1) {
@@ -177,14 +192,14 @@ __device__ __attribute__((noinline)) void attn_phase(const AttnArgs& a, uint8_t*
         }
         rec_store(w + 2 + d, A, ty);
       }
-    });
+    }, qs);
   }
   __syncthreads();            // the last reads of LDS are done before the next phase stages
   if (nc > 1) {
-    const int nm = a.B * a.n_q, qq = threadIdx.x >> 7, d = threadIdx.x & 127;
+    const int nm = a.B * a.n_q, qq = tx >> 7, d = tx & 127;
     for (int m0 = 4 * (nwg - 1 - wg); m0 < nm; m0 += 4 * nwg) {
       const int mi = m0 + qq;
-      if (mi < nm) attn_merge_one<G>(a, mi / a.n_q, mi % a.n_q, nc, d, ty, err);
+      if (mi < nm) attn_merge_one<G>(a, mi / a.n_q, mi % a.n_q, nc, d, tx & 63, ty, err);
     }
   }
 }
