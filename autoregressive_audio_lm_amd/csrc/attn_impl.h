@@ -100,24 +100,24 @@ __device__ __forceinline__ void attn_load_kv(AttnRegs<G, CH>& R, const uint16_t*
   }
 }
 
-// the rows at position tn read again (this workgroup wrote them after
-// attn_load_kv requested them)
+// the key and value rows of position tn taken from krow, vrow (128 bf16
+// each; the rows attn_load_kv requested were written after the request)
 template <int G, int CH>
-__device__ __forceinline__ void attn_reload_kv_at(AttnRegs<G, CH>& R, const uint16_t* kb,
-                                                  const uint16_t* vb, int t0, int n, int tid,
-                                                  int tn) {
+__device__ __forceinline__ void attn_set_kv_at(AttnRegs<G, CH>& R, const uint16_t* krow,
+                                               const uint16_t* vrow, int t0, int n, int tid,
+                                               int tn) {
   const int li = tid & 3, dq = tid & 31;
 #pragma unroll
   for (int j = 0; j < AttnRegs<G, CH>::PJ; ++j) {
     if (attn_kpos<G, CH>(t0, n, tid, j) != tn) continue;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      R.kr[j][c] = *reinterpret_cast<const uint4*>(kb + (size_t)tn * kHD + 8 * (4 * c + li));
+      R.kr[j][c] = *reinterpret_cast<const uint4*>(krow + 8 * (4 * c + li));
   }
 #pragma unroll
   for (int i = 0; i < AttnRegs<G, CH>::PI; ++i)
     if (attn_vpos<G, CH>(t0, n, tid, i) == tn)
-      R.vr[i] = *reinterpret_cast<const uint2*>(vb + (size_t)tn * kHD + 4 * dq);
+      R.vr[i] = *reinterpret_cast<const uint2*>(vrow + 4 * dq);
 }
 
 // The chunk's n positions (1 <= n <= CH) against the G heads.  out(h, d, A,

@@ -12,7 +12,7 @@
 //    words it needs (tagged, like every GEMV operand of the launch), norms and
 //    rotates its G query heads into LDS and, for the chunk holding the
 //    frame's position, writes that position's key and value to the cache and
-//    reads them again; a workgroup runs two items at once, one per 256-thread
+//    uses them from LDS; a workgroup runs two items at once, one per 256-thread
 //    half.  A single chunk writes the output words; otherwise each item
 //    leaves (maximum, sum, P.V) as tagged 64-bit records.
 //  - merge items (row, query head), four per workgroup, on the workgroups
@@ -23,8 +23,8 @@
 // operand, tagged with this phase.
 //
 // Cache visibility.  The chunk holding position pos is worked by the
-// workgroup that writes pos, which reads the row back after a workgroup
-// barrier; every other cached row was written before the launch, except in
+// workgroup that writes pos, which takes that row from LDS; every other
+// cached row was written before the launch, except in
 // the depth decoder, whose step j writes position j - 1 of a per-layer cache
 // that steps j + 1 .. 7 read: item (row, head) goes to the same workgroup at
 // every step, so these rows too are read by the workgroup that wrote them.
@@ -35,10 +35,11 @@ namespace m3 {
 // (AttnArgs, the phase's parameters, is in m3_internal.h: it is stored in the
 // phase table in place of a GEMV's Params.)
 
-// LDS of an attention phase: one AttnLds and G rotated q rows per half
+// LDS of an attention phase, per half: an AttnLds, G rotated q rows and the
+// key and value rows of the frame's position
 template <int G, int CH>
 constexpr size_t attn_phase_smem() {
-  return 2 * sizeof(AttnLds<G, CH>) + 2 * (size_t)G * kHD * 2;
+  return 2 * sizeof(AttnLds<G, CH>) + 2 * (size_t)(G + 2) * kHD * 2;
 }
 
 // a chunk record value: the float's bits with the 16-bit tag above them
@@ -135,7 +136,8 @@ __device__ __forceinline__ void attn_phase(const AttnArgs& a, uint8_t* smem, int
   const int nbk = a.B * a.n_kv, items = nbk * nc;
   const int half = tx >> 8, tid = tx & 255, lane = tid & 63, hw = tid >> 6;
   AttnLds<G, CH>& L = reinterpret_cast<AttnLds<G, CH>*>(smem)[half];
-  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + 2 * sizeof(AttnLds<G, CH>)) + half * G * kHD;
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + 2 * sizeof(AttnLds<G, CH>)) + half * (G + 2) * kHD;
+  uint16_t* kvs = qs + G * kHD;        // this position's key and value rows
   // item i (chunk-major: the chunks holding pos, which wait for QKV's K and V
   // rows, come last) goes to workgroup (i + nwg / 2) % nwg, half (i / nwg) % 2
   const int me = (wg + nwg / 2) % nwg;
@@ -165,20 +167,22 @@ __device__ __forceinline__ void attn_phase(const AttnArgs& a, uint8_t* smem, int
       }
       w0 &= 0xffffu;
       w1 &= 0xffffu;
-      if (k == G + 1) {
-        vb[(size_t)pos * kHD + lane] = (uint16_t)w0;
-        vb[(size_t)pos * kHD + lane + 64] = (uint16_t)w1;
-        continue;
-      }
-      uint32_t y0, y1;
-      head_norm_rope(w0, w1, k < G ? a.q_gamma : a.k_gamma, a.eps, a.rope, pos, lane, y0, y1);
-      uint16_t* dst = k < G ? qs + k * kHD : kb + (size_t)pos * kHD;
+      uint32_t y0 = w0, y1 = w1;
+      if (k <= G)
+        head_norm_rope(w0, w1, k < G ? a.q_gamma : a.k_gamma, a.eps, a.rope, pos, lane, y0, y1);
+      // q to LDS; the key (normed, rotated) and the value to the cache and to LDS
+      uint16_t* dst = k < G ? qs + k * kHD : kvs + (k - G) * kHD;
       dst[lane] = (uint16_t)y0;
       dst[lane + 64] = (uint16_t)y1;
+      if (k >= G) {
+        uint16_t* c = (k == G ? kb : vb) + (size_t)pos * kHD;
+        c[lane] = (uint16_t)y0;
+        c[lane + 64] = (uint16_t)y1;
+      }
     }
     __syncthreads();
     if (r0 == 0) staged();
-    if (last) attn_reload_kv_at(R, kb, vb, t0, n, tid, pos);
+    if (last) attn_set_kv_at(R, kvs, kvs + kHD, t0, n, tid, pos);
     attn_compute(R, n, a.scale2, tid, L, [&](int h, int d, float A, float Mx, float Ls) {
       if (!live) return;
       if (nc == 1) {
