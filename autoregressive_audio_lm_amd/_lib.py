@@ -79,7 +79,7 @@ class PhaseRegion(ctypes.Structure):
 
 
 PHASE_MAX_REGIONS = 4
-PHASE_GEMV, PHASE_FRAME_END, PHASE_ATTENTION = 0, 1, 2
+PHASE_GEMV, PHASE_FRAME_END, PHASE_ATTENTION, PHASE_DRAW = 0, 1, 2, 3
 
 
 class PhaseRecord(ctypes.Structure):

@@ -193,10 +193,12 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // phases of one frame: 4 GEMVs per body layer, lm_head, depth input, per depth
 // step 4 GEMVs per layer and the head, then the frame end; with decode
-// attention one attention phase per body layer and per depth layer run
+// attention one attention phase per body layer and per depth layer run; with
+// the guided draw one draw phase after the lm_head and after each head
 int frame_phases(const m3_config& c) {
   const int per_layer = c.attention ? 5 : 4;
-  return per_layer * c.n_layers + 2 + (c.n_codebooks - 1) * (per_layer * c.d_layers + 1) + 1;
+  const int draws = c.top_k > 0 ? c.n_codebooks : 0;     // guided draws: semantic + depth heads
+  return per_layer * c.n_layers + 2 + (c.n_codebooks - 1) * (per_layer * c.d_layers + 1) + draws + 1;
 }
 
 // the body's decode attention at T = max_pos: positions per chunk and chunks
@@ -408,8 +410,7 @@ struct PlanSink final : FrameSink {
   PersistPlan* pl;
   explicit PlanSink(PersistPlan* p) : pl(p) {}
   hipError_t gemv(const GemvDesc& d) override { return persist_add_gemv(pl, d); }
-  // (the persistent frame carries the per-row draws only)
-  hipError_t cfg_draw(const CfgDesc&) override { return hipErrorInvalidValue; }
+  hipError_t cfg_draw(const CfgDesc& d) override { return persist_add_cfg(pl, d); }
   hipError_t attention(const AttnStep& s, int B) override { return persist_add_attention(pl, attn_args(s, B)); }
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,
@@ -625,7 +626,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
   p_sem = ph;
   M3_TRY(gemv(c.fmt_lm, m->lm_head, d.VL, d.H, h_out, d.H, m->final_norm, 0, 0, logits, d.ldl, 1,
               M3_EPI_NONE, nullptr, 0, lm, guided ? nullptr : &sem));
-  if (guided) M3_TRY(guided_draw(logits, d.VL, d.ldl, 0u, lm_base, end_id, part_sem));
+  if (guided) {
+    p_sem = ph;                     // the draw writes the winner records
+    M3_TRY(guided_draw(logits, d.VL, d.ldl, 0u, lm_base, end_id, part_sem));
+  }
   // ---- depth decoder ----
   Prod pin;
   pin.x = p_h;
@@ -712,7 +716,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
     p_dep = ph;
     M3_TRY(gemv(c.fmt_depth, m->heads[j - 1], d.CV, d.D, hd, d.D, m->d_final_norm, 0, 0, dlogits,
                 d.CV, 1, M3_EPI_NONE, nullptr, 0, hp, guided ? nullptr : &dep));
-    if (guided) M3_TRY(guided_draw(dlogits, d.CV, d.CV, (uint32_t)j, 0, -1, part_dep(j)));
+    if (guided) {
+      p_dep = ph;
+      M3_TRY(guided_draw(dlogits, d.CV, d.CV, (uint32_t)j, 0, -1, part_dep(j)));
+    }
   }
   // ---- last draw, feedback, code ring, frame counter ----
   FeedbackTags ft;
@@ -780,7 +787,16 @@ struct RecordSink final : FrameSink {
     recs.push_back(r);
     return hipSuccess;
   }
-  hipError_t cfg_draw(const CfgDesc&) override { return hipErrorInvalidValue; }
+  hipError_t cfg_draw(const CfgDesc& d) override {
+    // the logits of the step before (it waits for every workgroup's flag of
+    // that step), the one-entry winner record of each row
+    m3_phase_record r{};
+    r.kind = M3_PHASE_DRAW;
+    add(r.in, r.n_in, rows(d.logits, 2 * d.S, d.ldl, 0, d.V, 4, (int)recs.size() - 1, 0));
+    add(r.out, r.n_out, rows(d.part, 2 * d.S, 1, 0, 1, sizeof(Best), -1, 1));
+    recs.push_back(r);
+    return hipSuccess;
+  }
   hipError_t attention(const AttnStep& s, int B) override {
     m3_phase_record r{};
     r.kind = M3_PHASE_ATTENTION;
@@ -1377,7 +1393,7 @@ int m3_frame_persistent_create(const m3_model* model, void* state, int B, int32_
   // one frame kernel per body format: bf16, int8-row or fp8-row body and the
   // same lm_head format, int8-g128 depth
   const m3_config& c = model->cfg;
-  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128 || c.top_k > 0)
+  if (!row_fmt(c.fmt_body) || c.fmt_lm != c.fmt_body || c.fmt_depth != M3_I8G128)
     return M3_ERR_FORMAT;
   // row-block winners carry their column in 16 bits next to the tag
   if (c.n_slice + 1 > 65535 || c.code_vocab > 65535) return M3_ERR_SHAPE;
@@ -1417,7 +1433,6 @@ int m3_frame_phase_table(const m3_model* model, void* state, int B, int32_t* cod
   st = validate_model(model);
   if (st != M3_OK) return st;
   const m3_config& c = model->cfg;
-  if (c.top_k > 0) return M3_ERR_FORMAT;
   RecordSink sink;
   st = build_frame(model, static_cast<uint8_t*>(state), B, codes, sink, true);
   if (st == M3_ERR_HIP) st = M3_ERR_SHAPE;

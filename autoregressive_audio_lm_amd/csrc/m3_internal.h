@@ -244,6 +244,9 @@ hipError_t persist_add_feedback(PersistPlan* pl, const uint16_t* tok_emb_audio,
                                 uint16_t* x_out, int32_t* ring, uint32_t* frame,
                                 const FeedbackTags& ft);
 hipError_t persist_add_attention(PersistPlan* pl, const AttnArgs& a);
+// a guided draw phase (part: the winner records, written tagged; no ids or
+// noise arrays): it waits for every workgroup to finish the step before it
+hipError_t persist_add_cfg(PersistPlan* pl, const CfgDesc& d);
 // phase clock: words of the buffer (3 per phase and workgroup), attach/detach
 size_t persist_clock_words(const PersistLaunch& L);
 void persist_set_clock(PersistLaunch& L, uint64_t* clk);

@@ -55,7 +55,7 @@ struct PersistPlan {
   size_t smem = 0;
   int B = 0;
   int fmt_body = -1;      // the kernel's class-0 format
-  bool attn = false;      // has attention phases (the kernels compiled with them)
+  bool attn = false;      // has attention or guided draw phases (the kernels compiled with them)
 };
 
 size_t persist_phase_bytes() { return sizeof(Phase); }
@@ -116,6 +116,25 @@ hipError_t persist_add_attention(PersistPlan* pl, const AttnArgs& a) {
                                                                             : attn_phase_smem<4, 64>())
                                  : (g == 1 ? attn_phase_smem<1, 128>() : g == 2 ? attn_phase_smem<2, 128>()
                                                                               : attn_phase_smem<4, 128>());
+  if (smem > pl->smem) pl->smem = smem;
+  pl->attn = true;
+  pl->phases.push_back(ph);
+  return hipSuccess;
+}
+
+hipError_t persist_add_cfg(PersistPlan* pl, const CfgDesc& d) {
+  if ((int)pl->phases.size() >= kMaxPhases || pl->phases.empty()) return hipErrorInvalidValue;
+  if (d.V < 1 || d.V > 36 * kCfgPersistThreads || d.S < 1 || d.S > kPersistFlags / 2 ||
+      d.top_k < 1 || !d.part || d.ids || d.noise)
+    return hipErrorInvalidValue;
+  Phase ph{};
+  static_assert(sizeof(CfgDesc) <= sizeof(Params), "draw arguments fit a phase");
+  memcpy(&ph.p, &d, sizeof d);
+  ph.variant = kCfgVariant;
+  ph.signal = 0;
+  // the draw waits (on the flags) for every workgroup to finish the logits
+  pl->phases.back().signal = 1;
+  const size_t smem = sizeof(CfgShared<kCfgPersistThreads>);
   if (smem > pl->smem) pl->smem = smem;
   pl->attn = true;
   pl->phases.push_back(ph);

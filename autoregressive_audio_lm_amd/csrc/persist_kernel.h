@@ -2,6 +2,7 @@
 // persist_kernel.h -- device side of the persistent frame (see persist.hip).
 #include "frame_impl.h"
 #include "persist_attn.h"
+#include "cfg_impl.h"
 
 namespace m3 {
 namespace {
@@ -16,6 +17,12 @@ constexpr int kFeedbackVariant = -1;
 // with ATT (frames with decode attention), so the frames with the identity
 // stub keep their registers.
 constexpr int kAttnVariant = -2;
+// A guided draw phase (the reference's draw: guidance over each song's row
+// pair, top-k, Gumbel-argmax; cfg_impl.h), also carried only by the ATT
+// kernels: it waits for every workgroup's flag of the logits GEMV before it,
+// then workgroup s draws song s.
+constexpr int kCfgVariant = -3;
+constexpr int kCfgPersistThreads = kThreads;
 
 struct Phase {
   Params p;
@@ -126,6 +133,37 @@ __device__ __forceinline__ bool run_attention(int variant, CPhasePtr ph, uint8_t
   }
 }
 
+// a guided draw phase of a kernel compiled with ATT (false: not one); false
+// from wait: the launch gives up (a wait failed)
+template <bool ATT>
+__device__ __forceinline__ bool run_cfg(int variant, CPhasePtr ph, uint8_t* smem, int wg,
+                                        const uint32_t* flags, int nwg, uint32_t ebase, int i,
+                                        uint32_t* err, int* s_ok, uint64_t* at, size_t cstride,
+                                        bool& ok) {
+  if constexpr (ATT) {
+    if (variant != kCfgVariant) return false;
+    ok = wait_flags(flags, nwg, ebase + (uint32_t)i, err, s_ok);
+    if (!ok) return true;
+    clock_mark(at, cstride, 1);
+    const CfgDesc& d = *(const CfgDesc*)&ph->p;
+    if (wg < d.S) {
+      int tx = threadIdx.x;              // (opaque: nothing derived is hoisted out of the loop)
+      asm volatile("" : "+v"(tx));
+      auto& sh = *reinterpret_cast<CfgShared<kCfgPersistThreads>*>(smem);
+      const uint32_t ty = tag_of(i, ebase);
+      if (d.V <= 2 * kCfgPersistThreads)
+        cfg_song<2, kCfgPersistThreads, true>(d, wg, tx, sh, ty);
+      else if (d.V <= 8 * kCfgPersistThreads)
+        cfg_song<8, kCfgPersistThreads, true>(d, wg, tx, sh, ty);
+      else
+        cfg_song<36, kCfgPersistThreads, true>(d, wg, tx, sh, ty);
+    }
+    return true;
+  } else {
+    return false;
+  }
+}
+
 template <int NB, int FB, bool CLK, bool ATT = false>
 __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int nph, uint32_t* flags,
                                                          uint32_t* err, const uint32_t* seq,
@@ -149,6 +187,9 @@ __global__ __launch_bounds__(kThreads) void frame_kernel(const Phase* ph, int np
       clock_mark(at, cstride, 1);
       feedback_run<true>(fb, wg, nwg, c_last, ebase);
     } else if (run_attention<ATT>(variant, (CPhasePtr)(ph + i), smem, wg, nwg, ebase, i, err, at, cstride)) {
+    } else if (bool ok = true; run_cfg<ATT>(variant, (CPhasePtr)(ph + i), smem, wg, flags, nwg, ebase, i,
+                                            err, &s_ok, at, cstride, ok)) {
+      if (!ok) return;
     } else {
       TagWait wait{ebase, i, err, at, cstride};
       const CPhasePtr cp = (CPhasePtr)(ph + i);

@@ -561,7 +561,9 @@ int m3_depth_graph_create(const m3_model* model, void* state, int B, int32_t* co
  * ring and the frame counter are updated exactly as by the other paths, with
  * the same bytes.  Supported: bf16, int8-row or fp8-row body with the same lm_head
  * format and an int8-g128 depth decoder (else M3_ERR_FORMAT), every GEMV
- * operand staged in LDS (at the full model: B <= 6; else M3_ERR_SHAPE), vocab
+ * operand staged in LDS (at the full model: B <= 6; else M3_ERR_SHAPE), the
+ * guided draw (top_k > 0) over at most 18432 columns (its draw phases: the
+ * draw kernel's search with one 512-thread workgroup per song), vocab
  * slice and code vocabulary below 65536.  The frame state must have been
  * initialised with m3_frame_state_init; eager, graph and persistent frames may
  * be interleaved on one state.  The launch fails with M3_ERR_HIP if the device
@@ -589,11 +591,13 @@ int m3_frame_persistent_clock(void* handle, uint64_t* clk, size_t clk_bytes, int
 /* The persistent frame's steps as records of the memory each step reads and
  * writes (host only: nothing is launched and no memory is touched; the state
  * and model pointers only fix addresses).  Record i is step i of the
- * persistent launch (a GEMV, an attention step, or the frame end, which runs
- * after every workgroup has finished every other step); a region is `rows`
+ * persistent launch (a GEMV, an attention step, a guided draw, which waits
+ * for every workgroup to finish the logits step before it, or the frame end,
+ * which runs after every workgroup has finished every other step); a region is `rows`
  * rows of bytes [base + r stride + c0, base + r stride + c1), with the step
  * that produced what is read (-1: written before the launch, or by an
- * earlier step of the frame for the frame end; for an attention step's
+ * earlier step of the frame for the frame end; for a draw, the step before
+ * it; for an attention step's
  * cache reads, by the step itself or by the same layer's attention at the
  * frame's earlier codebook steps) and whether its words carry the producer's
  * tag.  A consumer waits for the tags of its producer, so the ordering this
@@ -603,7 +607,7 @@ int m3_frame_persistent_clock(void* handle, uint64_t* clk, size_t clk_bytes, int
  * that many records; out may be NULL to count; M3_ERR_FORMAT: the frame has
  * no persistent form). */
 #define M3_PHASE_MAX_REGIONS 4
-enum { M3_PHASE_GEMV = 0, M3_PHASE_FRAME_END = 1, M3_PHASE_ATTENTION = 2 };
+enum { M3_PHASE_GEMV = 0, M3_PHASE_FRAME_END = 1, M3_PHASE_ATTENTION = 2, M3_PHASE_DRAW = 3 };
 typedef struct {
   uint64_t base, stride;
   int32_t rows;

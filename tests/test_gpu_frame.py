@@ -354,27 +354,38 @@ def guided():
     return cfg, dm, om
 
 
-@pytest.mark.parametrize("B", [2, 4, 16])
-def test_guided_frame_stages_match_oracle(guided, B):
+@pytest.mark.parametrize("B,path", [(2, "eager"), (4, "eager"), (16, "eager"), (2, "persistent"),
+                                    (6, "persistent")])
+def test_guided_frame_stages_match_oracle(guided, B, path):
     """Three chained frames in the reference's draw mode, every stage against
     the oracle on the GPU's own input of that stage; each draw (guidance over
     the row pair, top-k 50, Gumbel-argmax over the survivors) bit-exact on the
-    GPU's logits, and both rows of a song carry it."""
+    GPU's logits, and both rows of a song carry it (eager frames, and the
+    persistent frame's draw phases)."""
     import stages
     cfg, dm, om = guided
     x0 = synth.activations(B, cfg["H"], 61)
     st = runtime.FrameState(dm, B, x0.to(DEV), frame0=7)
     torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    if path == "persistent":
+        st.persistent_create(s)
     x = synth.bits(x0)
     for f in range(7, 10):
-        st.decode()
-        torch.cuda.synchronize()
-        got = stages.read_frame(st, tagged=False)
+        with torch.cuda.stream(s):
+            if path == "eager":
+                st.decode(s)
+            else:
+                st.persistent_launch(s)
+        s.synchronize()
+        assert int(st.err.item()) == 0
+        got = stages.read_frame(st, tagged=path == "persistent")
         assert np.array_equal(got["codes"][0::2], got["codes"][1::2])
         stats = stages.check_frame(om, got, x, seed=5, frame=f)
-        print(f"guided B={B} frame {f}: {stats.summary()}", flush=True)
+        print(f"guided {path} B={B} frame {f}: {stats.summary()}", flush=True)
         x = got["x"]
     assert int(st.frame.item()) == 10
+    st.release()
 
 
 def test_guided_depth_graph_equals_the_frames_depth_part(guided):
@@ -382,10 +393,12 @@ def test_guided_depth_graph_equals_the_frames_depth_part(guided):
     _depth_graph_equals_frame(dm, cfg, 4, synth.activations(4, cfg["H"], 78).to(DEV), 11)
 
 
-def test_guided_graph_replay_equals_eager_and_persistent_refused(guided):
+@pytest.mark.parametrize("B", [2, 6])
+def test_guided_graph_and_persistent_equal_eager(guided, B):
+    """Graph replays and persistent launches (draw phases) of guided frames
+    give the eager frames' codes frame by frame, and their bytes."""
     from autoregressive_audio_lm_amd import _lib
     cfg, dm, om = guided
-    B = 6
     x0 = synth.activations(B, cfg["H"], 62).to(DEV)
     eager = runtime.FrameState(dm, B, x0, frame0=0)
     seq = []
@@ -395,19 +408,62 @@ def test_guided_graph_replay_equals_eager_and_persistent_refused(guided):
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     graphed = runtime.FrameState(dm, B, x0, frame0=0)
+    pers = runtime.FrameState(dm, B, x0, frame0=0)
     with torch.cuda.stream(s):
         graphed.capture(s)
+        pers.persistent_create(s)
         for k in range(4):
             graphed.replay(s)
+            pers.persistent_launch(s)
             s.synchronize()
             assert torch.equal(graphed.codes, seq[k])
+            assert torch.equal(pers.codes, seq[k]), k
             torch.cuda.synchronize()
-    assert torch.equal(eager.x, graphed.x)
+    assert int(pers.err.item()) == 0
+    assert torch.equal(eager.x, graphed.x) and torch.equal(eager.x, pers.x)
+    for name in ("h", "logits", "dlogits", "ring"):
+        assert torch.equal(getattr(eager, name), getattr(pers, name)), name
     graphed.release()
-    with pytest.raises(_lib.M3Error):
-        runtime.FrameState(dm, B, x0).persistent_create()
+    pers.release()
     with pytest.raises(_lib.M3ValueError):
         runtime.FrameState(dm, 3, x0[:3])
+
+
+@pytest.mark.parametrize("B", [2, 4])
+def test_guided_attention_persistent_equals_eager(attn_long, B):
+    """The frame a song runs: the reference's draw with decode attention over
+    a long cache (several chunks and their merge), persistent launches against
+    eager frames, codes frame by frame and every byte of the caches."""
+    import stages
+    cfg, dm, om = attn_long
+    dm.set_draw(1.5, 50)
+    try:
+        x0 = synth.activations(B, cfg["H"], 66).to(DEV)
+        eager = runtime.FrameState(dm, B, x0, frame0=0)
+        pers = runtime.FrameState(dm, B, x0, frame0=0)
+        _seed_caches(eager, 95 + B)
+        _seed_caches(pers, 95 + B)
+        seq = []
+        for _ in range(3):
+            eager.decode()
+            seq.append(eager.codes.clone())
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            pers.persistent_create(s)
+            for k in range(3):
+                pers.persistent_launch(s)
+                s.synchronize()
+                assert int(pers.err.item()) == 0
+                assert torch.equal(pers.codes, seq[k]), k
+        assert torch.equal(eager.x, pers.x)
+        a, b = stages.read_caches(eager), stages.read_caches(pers)
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
+        eager.release()
+        pers.release()
+    finally:
+        dm.set_draw(1.5, 0)
 
 
 # ---- frames with decode attention over the state's KV caches -----------------
@@ -662,7 +718,8 @@ def test_end_token_frames_match_oracle(path):
     st.release()
 
 
-def test_guided_end_token_frames_match_oracle():
+@pytest.mark.parametrize("path", ["eager", "persistent"])
+def test_guided_end_token_frames_match_oracle(path):
     """The reference's draw with the end token: guidance over the row pair
     makes song 0 (rows 0, 1) draw it; stages against the oracle, both rows of
     a song carry the draw and its stop word."""
@@ -673,11 +730,18 @@ def test_guided_end_token_frames_match_oracle():
     dm, om = _end_model(cfg, "A", x0, [0], [1], top_k=50)
     st = runtime.FrameState(dm, B, x0.to(DEV), frame0=0)
     torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    if path == "persistent":
+        st.persistent_create(s)
     x = synth.bits(x0)
     for f in range(2):
-        st.decode()
-        torch.cuda.synchronize()
-        got = stages.read_frame(st, tagged=False)
+        with torch.cuda.stream(s):
+            if path == "eager":
+                st.decode(s)
+            else:
+                st.persistent_launch(s)
+        s.synchronize()
+        got = stages.read_frame(st, tagged=path == "persistent")
         stages.check_frame(om, got, x, seed=5, frame=f)
         assert np.array_equal(got["codes"][0::2], got["codes"][1::2])
         if f == 0:

@@ -12,7 +12,9 @@ end, which runs after every workgroup finished every GEMV, writes it again);
 step reads untagged (its KV cache) is written before the launch, by the step
 itself, or by an attention step it depends on through the tags it waits for
 (the depth decoder's cache, filled one position per codebook step; the kernel
-gives those rows' items to the workgroup that wrote them)."""
+gives those rows' items to the workgroup that wrote them); (6) what a guided
+draw reads untagged (the logits) is written by the step right before it, for
+whose every workgroup it waits."""
 import ctypes
 
 import pytest
@@ -78,12 +80,15 @@ def violations(recs):
     if n >= 512:
         bad.append(f"{n} steps: tags repeat within a frame")
     if recs[-1]["kind"] != _lib.PHASE_FRAME_END or any(
-            r["kind"] not in (_lib.PHASE_GEMV, _lib.PHASE_ATTENTION) for r in recs[:-1]):
+            r["kind"] not in (_lib.PHASE_GEMV, _lib.PHASE_ATTENTION, _lib.PHASE_DRAW)
+            for r in recs[:-1]):
         bad.append("the frame end is not the last step, or not the only one")
-    # the steps each step depends on through the tags it waits for
+    # the steps each step depends on through the tags it waits for; a draw
+    # (and the frame end) waits for every workgroup to finish the step before
+    # it, and so for every earlier step
     anc = []
     for i, r in enumerate(recs):
-        a = set()
+        a = set(range(i)) if r["kind"] in (_lib.PHASE_DRAW, _lib.PHASE_FRAME_END) else set()
         for g in r["inp"]:
             p = g["producer"]
             if g["tagged"] and 0 <= p < i:
@@ -120,6 +125,10 @@ def violations(recs):
                 elif r["kind"] == _lib.PHASE_GEMV:
                     if any(w[2] != n - 1 for w in cover):
                         bad.append(f"step {i} reads untagged bytes that step(s) "
+                                   f"{sorted({w[2] for w in cover})} write in the frame")
+                elif r["kind"] == _lib.PHASE_DRAW:
+                    if any(w[2] != i - 1 for w in cover) or g["producer"] != i - 1:
+                        bad.append(f"draw step {i} reads untagged bytes that step(s) "
                                    f"{sorted({w[2] for w in cover})} write in the frame")
                 elif r["kind"] == _lib.PHASE_ATTENTION:
                     if any(w[2] != i and not (w[2] in anc[i] and
@@ -231,14 +240,45 @@ def test_validator_finds_planted_mistakes():
     assert violations(r4)
 
 
+GUIDED_CASES = [("frame-small", "A", 2, 0, False), ("frame-small", "B", 6, 40, False),
+                ("frame-small", "A", 4, 300, True), ("frame-full", "A", 2, 2048, True),
+                ("frame-full", "C", 6, 0, True)]
+
+
+@pytest.mark.parametrize("name,preset,B,max_pos,end", GUIDED_CASES)
+def test_phase_table_ordering_with_the_guided_draw(name, preset, B, max_pos, end):
+    """The reference's draw: a draw step after the lm_head and after each
+    head, which the next step's gather and the frame end read (with and
+    without decode attention and the end token)."""
+    cfg = configs.config(name)
+    m, keep = fake_model(cfg, preset)
+    m.cfg.top_k, m.cfg.cfg_scale = 50, 1.5
+    if end:
+        m.cfg.end_id = cfg["end_token"]
+    if max_pos:
+        m.cfg.attention, m.cfg.max_pos, m.cfg.pos0 = 1, max_pos, 0
+    recs = phase_table(m, B)
+    S = cfg["n_codebooks"] - 1
+    per = 5 if max_pos else 4
+    assert len(recs) == per * cfg["n_layers"] + 2 + S * (per * cfg["d_layers"] + 1) + S + 1 + 1
+    kinds = [r["kind"] for r in recs]
+    assert kinds.count(_lib.PHASE_DRAW) == S + 1
+    lm = per * cfg["n_layers"]
+    assert kinds[lm] == _lib.PHASE_GEMV and kinds[lm + 1] == _lib.PHASE_DRAW
+    assert violations(recs) == []
+    # the depth input's gather reads the draw's winner records, tagged by it
+    assert any(g["tagged"] and g["producer"] == lm + 1 for g in recs[lm + 3]["inp"])
+    # a draw that reads logits an earlier step wrote breaks rule (6)
+    import copy
+    r1 = copy.deepcopy(recs)
+    r1[lm + 1]["inp"][0]["producer"] = lm - 1
+    assert violations(r1)
+
+
 def test_phase_table_refuses_what_the_persistent_frame_does_not_carry():
     cfg = configs.config("frame-small")
     m, keep = fake_model(cfg, "A")
-    m.cfg.top_k = 50
     L = _lib.lib()
-    assert L.m3_frame_phase_table(ctypes.byref(m), ctypes.c_void_p(STATE), 2,
-                                  ctypes.c_void_p(CODES), None, 0) == _lib.M3_ERR_FORMAT
-    m.cfg.top_k = 0
     assert L.m3_frame_phase_table(None, ctypes.c_void_p(STATE), 2, ctypes.c_void_p(CODES),
                                   None, 0) == _lib.M3_ERR_NULL
     n = L.m3_frame_phase_table(ctypes.byref(m), ctypes.c_void_p(STATE), 2, ctypes.c_void_p(CODES),
