@@ -19,8 +19,9 @@ codebook steps 2..7 come from the Infinity Cache), the device's streaming-read
 ceiling measured in the same run (m3_stream_read), the single-kernel workloads
 (RMSNorm+GEMV 4096x4096 over 16 rotated weight copies; the depth decoder alone
 at B = 6; the full vs the sliced lm_head + draw at B = 16, ids checked equal),
-context points (other B, presets, the guided draw, attention frames, prefill),
-and the CPU oracle on whole frames at B = 1 and 6.
+context points (other B, presets, the guided draw, attention frames, the frame
+a song runs -- the guided draw with decode attention -- on both frame paths,
+prefill), and the CPU oracle on whole frames at B = 1 and 6.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -872,16 +873,19 @@ def main():
     sweep = []
     guided = []
     attention_frames = []
+    song_frames = []
     if not args.no_sweep:
         for B in (2, 6, 16):
             sweep.append(point(args.preset, B, dm, fbytes))
         # the frame with the reference's draw (guidance 1.5 over each row pair,
         # top-k 50, one draw per song): graph-replayed frames
         dm.set_draw(1.5, 50)
-        for B in (2, 6, 16):
-            st_g, ms_g, _ = time_frames(dm, cfg, B, max(20, args.steps // 4), 3, stream, args.seed)
+        for B, path in ((2, "persistent"), (2, "graph"), (6, "persistent"), (6, "graph"),
+                        (16, "graph")):
+            f = time_frames if path == "graph" else time_frames_persistent
+            st_g, ms_g, _ = f(dm, cfg, B, max(20, args.steps // 4), 3, stream, args.seed)
             st_g.release()
-            guided.append({"preset": args.preset, "B": B, "songs": B // 2, "path": "graph",
+            guided.append({"preset": args.preset, "B": B, "songs": B // 2, "path": path,
                            "ms_per_frame": round(ms_g, 4), "frames_per_s": round(1e3 / ms_g, 2),
                            "GB_s": round(fbytes * 1e3 / ms_g / 1e9, 1)})
             log(f"[bench] guided {guided[-1]}")
@@ -909,6 +913,23 @@ def main():
                                      "kv_bytes_per_frame": kv, "err": err})
             log(f"[bench] attention frame {attention_frames[-1]}")
             torch.cuda.empty_cache()
+        # the frame a song runs: the reference's draw with decode attention
+        dm.set_draw(1.5, 50)
+        for B, path in ((2, "persistent"), (2, "graph"), (6, "persistent"), (6, "graph")):
+            f = time_frames if path == "graph" else time_frames_persistent
+            st_a, ms_a, _ = f(dm, cfg, B, n_att, 3, stream, args.seed)
+            err = int(st_a.err.item())
+            st_a.release()
+            del st_a
+            kv = 36 * B * 8 * 1800 * 128 * 2 * 2
+            song_frames.append({"preset": args.preset, "B": B, "songs": B // 2, "T": 1800,
+                                "path": path, "ms_per_frame": round(ms_a, 4),
+                                "frames_per_s": round(1e3 / ms_a, 2),
+                                "weight_plus_kv_GB_s": round((fbytes + kv) * 1e3 / ms_a / 1e9, 1),
+                                "err": err})
+            log(f"[bench] song frame {song_frames[-1]}")
+            torch.cuda.empty_cache()
+        dm.set_draw(1.5, 0)
         dm.set_attention(0, 0, 0)
         del dm
         torch.cuda.empty_cache()
@@ -975,6 +996,7 @@ def main():
         "guided_frame": guided,
         "prefill": prefill,
         "attention_frame": attention_frames,
+        "song_frame": song_frames,
         "attention": {"kernel": "attn_partial_kernel + attn_merge_kernel (body, 32:8 heads; "
                                 "caches [B, 8, T, 128] bf16, one per layer)", "points": attention},
         "gpu": f"{props.name} {props.gcnArchName} x{props.multi_processor_count} CU",

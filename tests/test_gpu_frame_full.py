@@ -249,3 +249,40 @@ def test_full_size_attention_persistent_equals_graph(full_attn, B):
     assert torch.equal(g.state[lo:hi], p.state[lo:hi])      # every cache, every position
     g.release()
     p.release()
+
+
+@pytest.mark.parametrize("B", [2, 6])
+def test_full_size_song_frame_persistent_equals_graph(full_attn, B):
+    """The frame a song runs at the full model size: the reference's draw
+    (guidance 1.5 over each row pair, top-k 50) with decode attention near
+    the end of a 60 s song; persistent frames (attention and draw phases)
+    byte-identical to graph frames over three chained frames, caches
+    included, and both rows of each song carry its draws."""
+    cfg, dm, om, max_pos, pos0 = full_attn
+    dm.set_draw(1.5, 50)
+    try:
+        x0 = synth.activations(B, cfg["H"], 907, device=DEV)
+        g = runtime.FrameState(dm, B, x0, frame0=0)
+        p = runtime.FrameState(dm, B, x0, frame0=0)
+        for st in (g, p):
+            _seed_full_caches(st, cfg, B, max_pos, pos0)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            g.capture(s)
+            p.persistent_create(s)
+            for f in range(3):
+                g.replay(s)
+                p.persistent_launch(s)
+                s.synchronize()
+                assert int(p.err.item()) == 0 and int(g.err.item()) == 0
+                assert torch.equal(g.codes, p.codes), f
+                assert torch.equal(p.codes[0::2], p.codes[1::2]), f
+                for name in ("x", "h", "logits", "dlogits"):
+                    assert torch.equal(getattr(g, name), getattr(p, name)), (f, name)
+        lo, hi = g.layout.kcache, g.layout.attn_ws
+        assert torch.equal(g.state[lo:hi], p.state[lo:hi])
+        g.release()
+        p.release()
+    finally:
+        dm.set_draw(1.5, 0)
+
