@@ -138,6 +138,79 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnParams p) {
   });
 }
 
+// The frame's attention step in one launch: q/k norm + RoPE, the cache write
+// and the chunk's partial softmax (the arithmetic of qk_norm_rope_kernel and
+// attn_kernel, so the results are theirs).  Workgroup (row, KV head, chunk)
+// first requests its chunk's cached keys and values, then norms and rotates
+// its G query heads from the QKV row into LDS; the chunk holding the position
+// also norms and rotates that position's key and writes key and value to the
+// cache, and takes them from LDS (the other cached rows were written by
+// earlier launches).  One position per row (P = 1).
+struct FusedAttn {
+  AttnParams p;                 // q and ldq unused
+  const uint16_t* qkv;
+  int ldqkv;
+  const float *q_gamma, *k_gamma, *rope;
+  float eps;
+  int pos;                      // without frame_dev
+  uint16_t *k_cache, *v_cache;
+  uint32_t* err;
+};
+
+template <int G, int CH>
+__global__ __launch_bounds__(kAThreads) void attn_fused_kernel(FusedAttn f) {
+  __shared__ AttnLds<G, CH> L;
+  __shared__ __align__(16) uint16_t qs[(G + 2) * kHD];   // q heads, then the position's k, v
+  const AttnParams& p = f.p;
+  const int chunk = blockIdx.x % p.nchunks;
+  const int kvh = (blockIdx.x / p.nchunks) % p.n_kv;
+  const int b = blockIdx.x / (p.nchunks * p.n_kv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pos = p.frame_dev ? frame_pos(p.frame_dev, p.pos0, p.max_pos, blockIdx.x == 0 ? f.err : nullptr)
+                              : f.pos;
+  const int T = pos + 1, nc = (T + CH - 1) / CH;
+  if (chunk >= nc) return;                       // past this row's position
+  const int t0 = chunk * CH;
+  const int n = min(T - t0, CH);
+  const bool last = chunk == nc - 1;
+  const size_t base = ((size_t)b * p.n_kv + kvh) * (size_t)p.max_pos * kHD;
+  uint16_t* kb = f.k_cache + base;
+  uint16_t* vb = f.v_cache + base;
+  AttnRegs<G, CH> R;
+  attn_load_kv(R, kb, vb, t0, n, tid);
+  uint16_t* kvs = qs + G * kHD;
+  for (int k = wave; k < G + (last ? 2 : 0); k += 4) {
+    const int head = k < G ? kvh * G + k : (k == G ? p.n_q + kvh : p.n_q + p.n_kv + kvh);
+    const uint16_t* x = f.qkv + (size_t)b * f.ldqkv + (size_t)head * kHD;
+    uint32_t y0 = x[lane], y1 = x[lane + 64];
+    if (k <= G)
+      head_norm_rope(y0, y1, k < G ? f.q_gamma : f.k_gamma, f.eps, f.rope, pos, lane, y0, y1);
+    uint16_t* dst = k < G ? qs + k * kHD : kvs + (k - G) * kHD;
+    dst[lane] = (uint16_t)y0;
+    dst[lane + 64] = (uint16_t)y1;
+    if (k >= G) {
+      uint16_t* c = (k == G ? kb : vb) + (size_t)pos * kHD;
+      c[lane] = (uint16_t)y0;
+      c[lane + 64] = (uint16_t)y1;
+    }
+  }
+  __syncthreads();
+  if (last) attn_set_kv_at(R, kvs, kvs + kHD, t0, n, tid, pos);
+  float* wrec = p.ws + (((size_t)b * p.n_kv + kvh) * p.nchunks) * (G * (2 + kHD));
+  attn_compute(R, n, p.scale2, tid, L, [&](int h, int d, float A, float M, float Lh) {
+    if (nc == 1) {
+      p.out[(size_t)b * p.ldo + (size_t)(kvh * G + h) * kHD + d] = (uint16_t)f2bf(A / Lh);
+    } else {
+      float* w = wrec + ((size_t)chunk * G + h) * (2 + kHD);
+      if (d == 0) {
+        w[0] = M;
+        w[1] = Lh;
+      }
+      w[2 + d] = A;
+    }
+  }, qs);
+}
+
 // chunks combined in order: one workgroup of 128 threads per (row, query
 // head).  Every load of a batch of up to 32 chunks (their maxima, sums and
 // this thread's P.V dimension) is issued before the first is used, so a
@@ -198,6 +271,17 @@ void launch_attn_g(const AttnParams& p, int CH, int B, hipStream_t s) {
   if (p.nchunks > 1) hipLaunchKernelGGL((attn_merge_kernel<G>), dim3(B * p.n_q), dim3(kHD), 0, s, p);
 }
 
+template <int G>
+void launch_fused_g(const FusedAttn& f, int CH, int B, hipStream_t s) {
+  const dim3 grid(B * f.p.n_kv * f.p.nchunks);
+  if (CH == 64)
+    hipLaunchKernelGGL((attn_fused_kernel<G, 64>), grid, dim3(kAThreads), 0, s, f);
+  else
+    hipLaunchKernelGGL((attn_fused_kernel<G, 128>), grid, dim3(kAThreads), 0, s, f);
+  if (f.p.nchunks > 1)
+    hipLaunchKernelGGL((attn_merge_kernel<G>), dim3(B * f.p.n_q), dim3(kHD), 0, s, f.p);
+}
+
 }  // namespace
 
 // positions per workgroup: 128, or 64 where 128 would leave most CUs idle
@@ -245,6 +329,40 @@ hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, i
     case 2: launch_attn_g<2>(p, ch, B, s); break;
     case 4: launch_attn_g<4>(p, ch, B, s); break;
     default: launch_attn_g<8>(p, ch, B, s); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_fused(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
+                                  const float* q_gamma, const float* k_gamma, float eps,
+                                  const float* rope, int pos, uint16_t* k_cache,
+                                  uint16_t* v_cache, int max_pos, uint16_t* out, int ldo, void* ws,
+                                  hipStream_t s, const uint32_t* frame_dev, int pos0,
+                                  uint32_t* err) {
+  // grid and records as the two-launch path: every position for a
+  // frame-driven call, pos + 1 otherwise
+  const int Tg = frame_dev ? max_pos : pos + 1;
+  const int ch = attn_chunk_size(B, n_kv, Tg);
+  const int nc = (Tg + ch - 1) / ch;
+  FusedAttn f{};
+  f.p = AttnParams{nullptr, 0, k_cache, v_cache, n_q, n_kv, max_pos, Tg, nc,
+                   kLog2e / sqrtf((float)kHD), out, ldo, static_cast<float*>(ws), frame_dev, pos0,
+                   ch, 1, pos + 1};
+  f.qkv = qkv;
+  f.ldqkv = ldqkv;
+  f.q_gamma = q_gamma;
+  f.k_gamma = k_gamma;
+  f.rope = rope;
+  f.eps = eps;
+  f.pos = pos;
+  f.k_cache = k_cache;
+  f.v_cache = v_cache;
+  f.err = err;
+  switch (n_q / n_kv) {
+    case 1: launch_fused_g<1>(f, ch, B, s); break;
+    case 2: launch_fused_g<2>(f, ch, B, s); break;
+    case 4: launch_fused_g<4>(f, ch, B, s); break;
+    default: launch_fused_g<8>(f, ch, B, s); break;
   }
   return hipGetLastError();
 }

@@ -355,13 +355,9 @@ struct LaunchSink final : FrameSink {
   hipError_t gemv(const GemvDesc& d) override { return launch_gemv(d, s); }
   hipError_t cfg_draw(const CfgDesc& d) override { return launch_cfg_draw(d, s); }
   hipError_t attention(const AttnStep& a, int B) override {
-    const int ld = a.n_q * 128;
-    hipError_t e = launch_qk_norm_rope(a.qkv, B, a.ldqkv, a.n_q, a.n_kv, a.q_gamma, a.k_gamma, a.eps,
-                                       a.rope, a.pos, a.q, ld, a.k_cache, a.v_cache, a.max_pos, s,
-                                       a.frame_dev, a.pos0, a.err);
-    if (e != hipSuccess) return e;
-    return launch_decode_attention(a.q, B, ld, a.n_q, a.n_kv, a.k_cache, a.v_cache, a.max_pos,
-                                   a.pos + 1, a.out, ld, a.ws, s, a.frame_dev, a.pos0);
+    return launch_attention_fused(a.qkv, B, a.ldqkv, a.n_q, a.n_kv, a.q_gamma, a.k_gamma, a.eps,
+                                  a.rope, a.pos, a.k_cache, a.v_cache, a.max_pos, a.out,
+                                  a.n_q * 128, a.ws, s, a.frame_dev, a.pos0, a.err);
   }
   hipError_t feedback(const uint16_t* tok, const uint16_t* const* aemb, int32_t* codes,
                       const Best* last_part, int last_nparts, int32_t vocab_base, int n_slice,

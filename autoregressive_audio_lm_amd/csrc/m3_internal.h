@@ -182,6 +182,14 @@ hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, i
                                    const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
                                    int T, uint16_t* out, int ldo, void* ws, hipStream_t s,
                                    const uint32_t* frame_dev = nullptr, int pos0 = 0, int P = 1);
+// the two above in one launch (plus the merge), one position per row: the
+// frame's attention steps (same results)
+hipError_t launch_attention_fused(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
+                                  const float* q_gamma, const float* k_gamma, float eps,
+                                  const float* rope, int pos, uint16_t* k_cache,
+                                  uint16_t* v_cache, int max_pos, uint16_t* out, int ldo, void* ws,
+                                  hipStream_t s, const uint32_t* frame_dev, int pos0,
+                                  uint32_t* err);
 
 // ---- frame helpers -------------------------------------------------------------
 // audio_emb: HOST array of n_cb-1 device pointers (copied into the kernel arguments)

@@ -469,7 +469,7 @@ typedef struct {
                       stream after O (+ residual) of each layer                 */
   /* attention = 1 only (zero-sized otherwise): */
   size_t rope;     /* f32  [max(max_pos, 8), 64, 2] RoPE table                 */
-  size_t aq;       /* bf16 [B, max(nq, d_hidden)] rotated q (scratch)          */
+  size_t aq;       /* bf16 [B, max(nq, d_hidden)] reserved scratch            */
   size_t ao;       /* bf16 [L][B, nq]    each body layer's attention output    */
   size_t dao;      /* bf16 [S][DL][B, d_hidden] each depth layer's attention output */
   size_t kcache, vcache;   /* bf16 [n_layers][B][n_kv][max_pos][128]          */
