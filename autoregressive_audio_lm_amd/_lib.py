@@ -114,6 +114,8 @@ _SIGS = {
                                   ctypes.c_size_t, _P]),
     "m3_decode_attention": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P, ctypes.c_size_t,
                                  _P]),
+    "m3_decode_attention_step": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _I, _P, _P,
+                                      _I, _P, _I, _P, ctypes.c_size_t, _P]),
     "m3_lmhead_sliced": (_I, [_I, _P, _I, _I, _P, _I, _I, _P, ctypes.c_float, _P, _I, _P]),
     "m3_gumbel_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "m3_gumbel_argmax": (_I, [_P, _I, _I, _I, ctypes.POINTER(SampleParams), _P, _P, ctypes.c_size_t, _P]),

@@ -1188,6 +1188,38 @@ int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, in
                                             ldo, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int m3_decode_attention_step(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
+                             int head_dim, const float* q_gamma, const float* k_gamma, float eps,
+                             const float* rope, int pos, uint16_t* k_cache, uint16_t* v_cache,
+                             int max_pos, uint16_t* out, int ldo, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!qkv || !q_gamma || !k_gamma || !rope || !k_cache || !v_cache || !out) return M3_ERR_NULL;
+  if (head_dim != M3_HEAD_DIM || !attn_heads_ok(n_q, n_kv)) return M3_ERR_SHAPE;
+  if (B < 1 || B > M3_MAX_B || max_pos < 1 || max_pos > M3_MAX_POS || pos < 0 || pos >= max_pos)
+    return M3_ERR_SHAPE;
+  if (ldqkv < (n_q + 2 * n_kv) * M3_HEAD_DIM || ldo < n_q * M3_HEAD_DIM) return M3_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return M3_ERR_SHAPE;
+  const size_t need = attn_workspace_bytes(B, n_q, n_kv, pos + 1);
+  if (need && !workspace) return M3_ERR_NULL;
+  if (workspace_bytes < need) return M3_ERR_WORKSPACE;
+  if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(q_gamma, 4) || !aligned(k_gamma, 4) || !aligned(rope, 16) ||
+      (need && !aligned(workspace, 16)) || ldqkv % 8 || ldo % 8)
+    return M3_ERR_ALIGN;
+  const size_t qkv_b = ((size_t)(B - 1) * ldqkv + (n_q + 2 * n_kv) * M3_HEAD_DIM) * 2;
+  const size_t o_b = ((size_t)(B - 1) * ldo + n_q * M3_HEAD_DIM) * 2;
+  const size_t c_b = cache_bytes(B, n_kv, max_pos);
+  if (overlap(qkv, qkv_b, out, o_b) || overlap(qkv, qkv_b, k_cache, c_b) ||
+      overlap(qkv, qkv_b, v_cache, c_b) || overlap(out, o_b, k_cache, c_b) ||
+      overlap(out, o_b, v_cache, c_b) || overlap(k_cache, c_b, v_cache, c_b) ||
+      (need && (overlap(workspace, need, qkv, qkv_b) || overlap(workspace, need, out, o_b) ||
+                overlap(workspace, need, k_cache, c_b) || overlap(workspace, need, v_cache, c_b))))
+    return M3_ERR_ALIAS;
+  return hip_status(launch_attention_fused(qkv, B, ldqkv, n_q, n_kv, q_gamma, k_gamma, eps, rope,
+                                           pos, k_cache, v_cache, max_pos, out, ldo, workspace,
+                                           static_cast<hipStream_t>(stream), nullptr, 0, nullptr));
+}
+
 // ---- the prompt's attention (S sequences of P positions, rows [s][t]) ------------
 int m3_prefill_qk_norm_rope(const uint16_t* qkv, int S, int P, int ldqkv, int n_q, int n_kv,
                             int head_dim, const float* q_gamma, const float* k_gamma, float eps,

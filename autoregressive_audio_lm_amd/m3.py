@@ -270,6 +270,36 @@ def qk_norm_rope(qkv: torch.Tensor, n_q: int, n_kv: int, q_gamma: torch.Tensor,
     return q_out
 
 
+def decode_attention_step(qkv: torch.Tensor, n_q: int, n_kv: int, q_gamma: torch.Tensor,
+                          k_gamma: torch.Tensor, rope: torch.Tensor, pos: int,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor, eps: float = 1e-6,
+                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """m3_decode_attention_step: q/k norm + RoPE at pos (k and v written into
+    the caches) and attention over positions <= pos in one launch; out
+    [B, n_q*128] bf16."""
+    for t, n in ((qkv, "qkv"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"), (rope, "rope"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out"), (workspace, "workspace")):
+        _cuda(t, n)
+    B = qkv.shape[0]
+    for c in (k_cache, v_cache):
+        if c.dim() != 4 or c.shape[0] != B or c.shape[1] != n_kv or c.shape[3] != HEAD_DIM \
+                or not c.is_contiguous():
+            raise ValueError("caches must be contiguous [B, n_kv, max_pos, 128]")
+    if out is None:
+        out = torch.empty(B, n_q * HEAD_DIM, dtype=torch.bfloat16, device=qkv.device)
+    need = attention_workspace_bytes(B, n_q, n_kv, pos + 1)
+    if workspace is None and need:
+        workspace = attention_workspace(B, n_q, n_kv, pos + 1, qkv.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().m3_decode_attention_step(_ptr(qkv), B, qkv.stride(0), int(n_q), int(n_kv), HEAD_DIM,
+                                         _ptr(q_gamma), _ptr(k_gamma), float(eps), _ptr(rope),
+                                         int(pos), _ptr(k_cache), _ptr(v_cache), k_cache.shape[2],
+                                         _ptr(out), out.stride(0), _ptr(workspace), wbytes,
+                                         _stream(stream)))
+    return out
+
+
 def attention_workspace_bytes(B: int, n_q: int, n_kv: int, T: int) -> int:
     return int(lib().m3_attention_workspace_bytes(int(B), int(n_q), int(n_kv), int(T)))
 

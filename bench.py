@@ -405,7 +405,8 @@ def time_prefill(c, stream, M=600, reps=10):
 
 def time_attention(c, stream, B, T=1800, layers=36, reps=5):
     """Decode attention of one frame: for each of the body's layers, the q/k
-    norm + RoPE with the cache write, then attention over T cached positions
+    norm + RoPE with the cache write and attention over T cached positions
+    (m3_decode_attention_step; and m3_decode_attention alone)
     (60 s of frames at 25 per second plus a 300-token prompt), each layer with
     its own cache (so the caches stream from HBM).  Timed as a captured graph
     of all layers, replayed, HIP events on the launch stream."""
@@ -428,9 +429,11 @@ def time_attention(c, stream, B, T=1800, layers=36, reps=5):
 
     def frame(attn_only):
         for kc, vc in caches:
-            if not attn_only:
-                m3.qk_norm_rope(qkv, n_q, n_kv, qg, kg, rope, T - 1, kc, vc, q_out=q, stream=stream)
-            m3.decode_attention(q, n_q, n_kv, kc, vc, T, out=out, workspace=ws, stream=stream)
+            if attn_only:
+                m3.decode_attention(q, n_q, n_kv, kc, vc, T, out=out, workspace=ws, stream=stream)
+            else:      # the whole step in one launch (+ merge): m3_decode_attention_step
+                m3.decode_attention_step(qkv, n_q, n_kv, qg, kg, rope, T - 1, kc, vc, out=out,
+                                         workspace=ws, stream=stream)
 
     res = {}
     with torch.cuda.stream(stream):

@@ -319,6 +319,19 @@ int m3_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv, in
                         const uint16_t* k_cache, const uint16_t* v_cache, int max_pos, int T,
                         uint16_t* out, int ldo, void* workspace, size_t workspace_bytes,
                         void* stream);
+/* One decode step's attention ("MiniMax Music 3, local" and TensorFold PR
+ * #987, kernel list: q/k norm + RoPE, split-key decode attention with a
+ * merge): m3_qk_norm_rope at pos (the caches' slot pos written) followed by
+ * m3_decode_attention over T = pos + 1 positions, in one launch plus the
+ * merge, with the same results and no q buffer.  Arguments as those two
+ * calls (workspace: m3_attention_workspace_bytes(B, n_q, n_kv, pos + 1)
+ * bytes); qkv, out, the caches and the workspace overlap nothing else.
+ * Errors as m3_decode_attention. */
+int m3_decode_attention_step(const uint16_t* qkv, int B, int ldqkv, int n_q, int n_kv,
+                             int head_dim, const float* q_gamma, const float* k_gamma, float eps,
+                             const float* rope, int pos, uint16_t* k_cache, uint16_t* v_cache,
+                             int max_pos, uint16_t* out, int ldo, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---- the prompt's attention ------------------------------------------------- */
 /* The prompt's rows through the same steps as one decode row, all positions at

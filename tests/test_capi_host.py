@@ -226,6 +226,24 @@ def test_attention_refusals(L):
     assert L.m3_decode_attention(*a_arg(ws=P(0x40000000))) == _lib.M3_ERR_ALIAS
     # one chunk: no workspace needed
     assert L.m3_attention_workspace_bytes(2, 16, 16, 64) == 0
+    # the one-launch step: qk norm + rope at pos, attention over pos + 1 positions
+    need_s = L.m3_attention_workspace_bytes(2, 32, 8, 300)
+    s_arg = lambda **k: (k.get("qkv", P(0x10000000)), k.get("B", 2), k.get("ldqkv", 6144),
+                         k.get("nq", 32), k.get("nkv", 8), k.get("hd", 128), P(0x30000000),
+                         P(0x30001000), k.get("eps", 1e-6), tab, k.get("pos", 299),
+                         k.get("kc", P(0x40000000)), k.get("vc", P(0x48000000)), k.get("mp", 512),
+                         k.get("out", P(0x50000000)), k.get("ldo", 4096), k.get("ws", P(0x60000000)),
+                         k.get("wsb", need_s), None)
+    assert L.m3_decode_attention_step(*s_arg(qkv=None)) == _lib.M3_ERR_NULL
+    assert L.m3_decode_attention_step(*s_arg(ws=None)) == _lib.M3_ERR_NULL
+    assert L.m3_decode_attention_step(*s_arg(wsb=need_s - 1)) == _lib.M3_ERR_WORKSPACE
+    assert L.m3_decode_attention_step(*s_arg(pos=512)) == _lib.M3_ERR_SHAPE
+    assert L.m3_decode_attention_step(*s_arg(nq=24)) == _lib.M3_ERR_SHAPE
+    assert L.m3_decode_attention_step(*s_arg(eps=float("nan"))) == _lib.M3_ERR_SHAPE
+    assert L.m3_decode_attention_step(*s_arg(out=P(0x50000002))) == _lib.M3_ERR_ALIGN
+    assert L.m3_decode_attention_step(*s_arg(vc=P(0x40000000 + 4096))) == _lib.M3_ERR_ALIAS
+    assert L.m3_decode_attention_step(*s_arg(out=P(0x10000000 + 4096))) == _lib.M3_ERR_ALIAS
+    assert L.m3_decode_attention_step(*s_arg(ws=P(0x48000000))) == _lib.M3_ERR_ALIAS
 
 
 def test_prompt_attention_refusals(L):

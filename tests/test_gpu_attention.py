@@ -135,6 +135,30 @@ def test_decode_steps_build_the_cache():
                              agree=0.97, rel=1e-2, width=HD)
 
 
+@pytest.mark.parametrize("B,n_q,n_kv", [(2, 32, 8), (1, 16, 16), (5, 8, 4)])
+def test_decode_attention_step_equals_the_two_calls(B, n_q, n_kv):
+    """m3_decode_attention_step (one launch plus the merge) gives the bytes
+    of m3_qk_norm_rope followed by m3_decode_attention: the output and both
+    caches, at positions with one chunk and with several (over seeded
+    earlier positions)."""
+    max_pos = 400
+    ldqkv = (n_q + 2 * n_kv) * HD
+    qg = (1.0 + 0.1 * np.random.default_rng(5).standard_normal(HD)).astype(np.float32)
+    kg = (1.0 + 0.1 * np.random.default_rng(6).standard_normal(HD)).astype(np.float32)
+    qgd, kgd = torch.from_numpy(qg).to(DEV), torch.from_numpy(kg).to(DEV)
+    rope = m3.rope_table(max_pos)
+    kc, vc = fill_cache(B, n_kv, max_pos, max_pos, 40 + B, 1.0)
+    k1, v1, k2, v2 = dev(kc), dev(vc), dev(kc), dev(vc)
+    for pos in (0, 5, 63, 64, 250, 399):
+        qkv = dev(rnd_bf16((B, ldqkv), 600 + pos, 1.5))
+        q = m3.qk_norm_rope(qkv, n_q, n_kv, qgd, kgd, rope, pos, k1, v1)
+        a = m3.decode_attention(q, n_q, n_kv, k1, v1, pos + 1)
+        b = m3.decode_attention_step(qkv, n_q, n_kv, qgd, kgd, rope, pos, k2, v2)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), pos
+        assert torch.equal(k1, k2) and torch.equal(v1, v2), pos
+
+
 # ---- the prompt's attention: S sequences of L positions at once ----------------
 def _prompt_case(S, L, n_q, n_kv, pos_base, max_pos, seed):
     ldqkv = (n_q + 2 * n_kv) * HD
