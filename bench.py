@@ -840,7 +840,7 @@ def main():
     log(f"[bench] cfg draw {cfg_draw}")
     prefill = time_prefill(dm.config, stream)
     log(f"[bench] prefill {prefill}")
-    attention = [time_attention(dm.config, stream, b) for b in (1, 16)]
+    attention = [time_attention(dm.config, stream, b) for b in (1, 6, 16)]
     log(f"[bench] attention {attention}")
     paths_ms = {k: round(v["ms"], 4) for k, v in res.items()}
     for v in res.values():
