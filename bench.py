@@ -1000,8 +1000,10 @@ def main():
         "prefill": prefill,
         "attention_frame": attention_frames,
         "song_frame": song_frames,
-        "attention": {"kernel": "attn_partial_kernel + attn_merge_kernel (body, 32:8 heads; "
-                                "caches [B, 8, T, 128] bf16, one per layer)", "points": attention},
+        "attention": {"kernel": "m3_decode_attention_step: attn_fused_kernel (q/k norm + RoPE, "
+                                "cache write, chunk partials) + attn_merge_kernel (body, 32:8 "
+                                "heads; caches [B, 8, T, 128] bf16, one per layer)",
+                      "points": attention},
         "gpu": f"{props.name} {props.gcnArchName} x{props.multi_processor_count} CU",
     }
     print(json.dumps(out), flush=True)
