@@ -399,7 +399,7 @@ def time_prefill(c, stream, M=600, reps=10):
             "gemms": gemms,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),
-                         "kernel": "prefill_gemm_kernel (the four body GEMMs of a layer)"},
+                         "kernel": "prefill_mfma32_kernel (QKV, gate/up) and prefill_gemm_kernel (O, down): the four body GEMMs of a layer"},
             "prompt_prefill_ms_36_layers": round(36 * layer_us / 1e3, 3)}
 
 

@@ -2,7 +2,9 @@
 rows: "MiniMax Music 3, local"; TensorFold PR #987) against the oracle: the
 row-wise RMSNorm (m3_rmsnorm_rows) and the dense GEMM on the matrix cores
 (m3_prefill_gemm) with its epilogues, at sizes that span several tiles of
-both tile shapes (64 x 128 and 64 x 256) with ragged M, N and K step counts,
+every tile shape (the 16 x 16 x 32 MFMA kernel's 64 x 128, 96 x 128 and 64 x
+256, the 32 x 32 x 16 kernel's 128 x 128 and 128 x 256) with ragged M, N and K
+step counts,
 and at the full body shapes on sampled output columns the oracle computes
 one row block at a time.  Every call goes
 through the C ABI."""
@@ -36,13 +38,16 @@ def gemm(W, a, epi=m3.EPI_NONE, out_f32=False, res=None, flags=0):
     return y.cpu().numpy() if out_f32 else synth.bits(y)
 
 
-# (1000, 4100) and (1024, 4096) reach the 64 x 256 tiles (at least 256 of
-# them); (600, 4096) and (650, 3000) the 96 x 128 tiles (more than 256 tiles
-# of 64 x 128, at most 256 of 96 x 128; 650 rows end in a partial tile); the
-# others 64 x 128
+# At 256 rows or more, 384 tiles of 128 x 256 select the 32 x 32 x 16
+# kernel's 128 x 256 tiles ((1024, 12300): 392, the last 12 columns in a
+# partial tile), else 192 tiles of 128 x 128 its 128 x 128 tiles ((1000,
+# 4100), (1024, 4096) and (300, 8200)); then (600, 4096) and (650, 3000) reach the 96 x 128
+# tiles (more than 256 tiles of 64 x 128, at most 256 of 96 x 128; 650 rows
+# end in a partial tile); the others 64 x 128
 @pytest.mark.parametrize("M,N,K", [(1, 16, 64), (37, 200, 512), (600, 256, 512), (129, 130, 1024),
                                    (300, 520, 256), (37, 300, 8192), (1000, 4100, 128),
-                                   (1024, 4096, 192), (600, 4096, 128), (650, 3000, 192)])
+                                   (1024, 4096, 192), (600, 4096, 128), (650, 3000, 192),
+                                   (1024, 12300, 64), (300, 8200, 192)])
 def test_prefill_gemm_parity(M, N, K):
     W = rand_w(N, K, M + N)
     a = rand_x(M, K, K + 3)
@@ -54,11 +59,13 @@ def test_prefill_gemm_parity(M, N, K):
 @pytest.mark.parametrize("M,K,F,N", [(1, 512, 100, 200), (150, 512, 100, 200), (600, 512, 100, 200),
                                      (70, 8192, 100, 200), (1, 512, 99, 203), (150, 512, 99, 203),
                                      (600, 512, 99, 203), (70, 8192, 99, 203),
-                                     (1000, 64, 2050, 4100), (1024, 64, 2051, 4099)])
+                                     (1000, 64, 2050, 4100), (1024, 64, 2051, 4099),
+                                     (1024, 64, 6150, 12300), (1000, 192, 6151, 12301)])
 def test_prefill_epilogues(M, K, F, N):
     """SwiGLU and residual epilogues; F = 100 / N = 200 give rows of whole
     16-byte chunks, F = 99 / N = 203 ragged tails and unaligned row strides;
-    the last two run on the 64 x 256 tiles (the SwiGLU GEMM has N = 2F)."""
+    the last four run on the 32 x 32 x 16 kernel (the SwiGLU GEMM has N = 2F):
+    128 x 128 tiles for N about 4100, 128 x 256 for N about 12300."""
     Wg, Wu = rand_w(F, K, 11), rand_w(F, K, 12)
     a = rand_x(M, K, 13)
     m = gemm(np.concatenate([Wg, Wu], 0), a, epi=m3.EPI_SWIGLU, flags=m3.PACK_GLU_INTERLEAVE)
