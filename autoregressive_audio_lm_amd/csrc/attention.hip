@@ -282,6 +282,172 @@ void launch_fused_g(const FusedAttn& f, int CH, int B, hipStream_t s) {
     hipLaunchKernelGGL((attn_merge_kernel<G>), dim3(B * f.p.n_q), dim3(kHD), 0, s, f.p);
 }
 
+
+// ---------------------------------------------------------------------------
+// Prompt attention, tiled.  One workgroup per (sequence, KV head, block of RB
+// prompt rows) holds the 64 query vectors of those rows' G heads (vector v =
+// row t0 + v / G, head G kvh + v % G) and walks the keys 0 .. the block's last
+// position in chunks of 64, keeping a running maximum, sum and P.V per vector:
+// no partial records and no merge.  Scores: v_mfma_f32_32x32x16_bf16 (bf16
+// products, fp32 sums; each wave one 32 x 32 block of vectors x keys, q in
+// registers, keys straight from the cache), scaled to base 2 and masked past
+// each row's position; softmax and P.V in fp32 on the VALU as in the decode
+// kernels: p = 2^(s - m), a new maximum rescales the sum and the P.V by
+// 2^(m_old - m_new), out = bf16(P.V / sum).
+constexpr int kPQ = 64;                          // query vectors per workgroup
+constexpr int kPK = 64;                          // keys per chunk
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct PromptAttn {
+  const uint16_t* q;
+  int ldq;
+  const uint16_t* k;
+  const uint16_t* v;
+  int n_kv, max_pos, P, pos_base, nrb;
+  float scale2;                                  // log2(e) / sqrt(head_dim)
+  uint16_t* out;
+  int ldo;
+};
+
+template <int G>
+__global__ __launch_bounds__(kAThreads, 2) void prompt_attn_kernel(PromptAttn a) {
+  constexpr int RB = kPQ / G;
+  __shared__ float Pt[kPK][kPQ + 1];             // scores, then probabilities: [key][vector]
+  __shared__ __align__(16) uint16_t Vs[kPK][kHD];
+  __shared__ float As[kPQ], Ls[kPQ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int w = blockIdx.x;                            // the longest row blocks first
+  const int rb = a.nrb - 1 - w % a.nrb;
+  w /= a.nrb;
+  const int kvh = w % a.n_kv, sq = w / a.n_kv;
+  const int t0 = rb * RB;
+  const int nkeys = a.pos_base + min(t0 + RB, a.P);   // keys 0 .. the block's last position
+  const int nch = (nkeys + kPK - 1) / kPK;
+  const size_t cb = (size_t)(sq * a.n_kv + kvh) * a.max_pos * kHD;
+  const uint16_t* kb = a.k + cb;
+  const uint16_t* vb = a.v + cb;
+  auto vpos = [&](int v) { return a.pos_base + min(t0 + v / G, a.P - 1); };
+
+  // wave (qb, kc): score block of vectors 32 qb .., keys 32 kc .. of a chunk;
+  // A operand: vector 32 qb + l % 32, dims 16 ks + 8 (l / 32) .. +7
+  const int qb = wave >> 1, kc = wave & 1;
+  uint4 qa[8];
+  {
+    const int v = 32 * qb + (lane & 31);
+    const uint16_t* qr = a.q + (size_t)(sq * a.P + min(t0 + v / G, a.P - 1)) * a.ldq +
+                         (size_t)(kvh * G + v % G) * kHD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qa[ks] = *reinterpret_cast<const uint4*>(qr + 16 * ks);
+  }
+  // softmax: 4 threads per vector, 16 keys each; P.V: vectors pv0 .. +3, dims pd0 .. +7
+  const int sv = tid >> 2, sk = tid & 3;
+  const int pv0 = 4 * (tid >> 4), pd0 = 8 * (tid & 15);
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[i][d] = 0.f;
+
+  for (int c = 0; c < nch; ++c) {
+    const int k0 = c * kPK;
+    // the chunk's value rows (past the last key: its row again, weighted 0)
+#pragma unroll
+    for (int e = tid; e < kPK * kHD / 8; e += kAThreads) {
+      const int j = e >> 4, d8 = e & 15;
+      *reinterpret_cast<uint4*>(&Vs[j][8 * d8]) =
+          *reinterpret_cast<const uint4*>(vb + (size_t)min(k0 + j, nkeys - 1) * kHD + 8 * d8);
+    }
+    {
+      const uint16_t* kr = kb + (size_t)min(k0 + 32 * kc + (lane & 31), nkeys - 1) * kHD + 8 * (lane >> 5);
+      uint4 kk[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kk[ks] = *reinterpret_cast<const uint4*>(kr + 16 * ks);
+      f32x16_t sacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[ks]),
+                                                       __builtin_bit_cast(bf16x8_t, kk[ks]), sacc, 0, 0, 0);
+      // lane holds S[32 qb + 8 g + 4 (l / 32) + r][32 kc + l % 32] in sacc[4 g + r]
+      const int j = 32 * kc + (lane & 31), kp = k0 + j;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = 32 * qb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        Pt[j][v] = kp < nkeys && kp <= vpos(v) ? sacc[e] * a.scale2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    {
+      float x[16], mc = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        x[u] = Pt[16 * sk + u][sv];
+        mc = fmaxf(mc, x[u]);
+      }
+      mc = fmaxf(mc, __shfl_xor(mc, 1));
+      mc = fmaxf(mc, __shfl_xor(mc, 2));
+      const float m_new = fmaxf(m_run, mc);      // finite: key 0 is seen by every row
+      const float alpha = exp2f(m_run - m_new);  // 0 at the first chunk
+      float ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float pr = exp2f(x[u] - m_new);
+        Pt[16 * sk + u][sv] = pr;
+        ls += pr;
+      }
+      ls += __shfl_xor(ls, 1);
+      ls += __shfl_xor(ls, 2);
+      l_run = fmaf(l_run, alpha, ls);
+      m_run = m_new;
+      if (sk == 0) As[sv] = alpha;
+    }
+    __syncthreads();
+    {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = As[pv0 + i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[i][d] *= al[i];
+      for (int j = 0; j < kPK; ++j) {
+        const uint4 v4 = *reinterpret_cast<const uint4*>(&Vs[j][pd0]);
+        const float vf[8] = {bf2f(v4.x & 0xffffu), bf2f(v4.x >> 16), bf2f(v4.y & 0xffffu), bf2f(v4.y >> 16),
+                             bf2f(v4.z & 0xffffu), bf2f(v4.z >> 16), bf2f(v4.w & 0xffffu), bf2f(v4.w >> 16)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = Pt[j][pv0 + i];
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[i][d] = fmaf(pr, vf[d], acc[i][d]);
+        }
+      }
+    }
+    __syncthreads();                             // Pt and Vs are rewritten by the next chunk
+  }
+  if (sk == 0) Ls[sv] = l_run;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = pv0 + i, t = t0 + v / G;
+    if (t >= a.P) continue;
+    const float L = Ls[v];
+    uint32_t o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      o[d] = f2bf(acc[i][2 * d] / L) | ((uint32_t)f2bf(acc[i][2 * d + 1] / L) << 16);
+    *reinterpret_cast<uint4*>(a.out + (size_t)(sq * a.P + t) * a.ldo + (size_t)(kvh * G + v % G) * kHD + pd0) =
+        make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <int G>
+void launch_prompt_g(const PromptAttn& a, int S, hipStream_t s) {
+  hipLaunchKernelGGL(prompt_attn_kernel<G>, dim3(S * a.n_kv * a.nrb), dim3(kAThreads), 0, s, a);
+}
+
 }  // namespace
 
 // positions per workgroup: 128, or 64 where 128 would leave most CUs idle
@@ -363,6 +529,21 @@ hipError_t launch_attention_fused(const uint16_t* qkv, int B, int ldqkv, int n_q
     case 2: launch_fused_g<2>(f, ch, B, s); break;
     case 4: launch_fused_g<4>(f, ch, B, s); break;
     default: launch_fused_g<8>(f, ch, B, s); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prompt_attention(const uint16_t* q, int S, int P, int ldq, int n_q, int n_kv,
+                                   const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
+                                   int pos_base, uint16_t* out, int ldo, hipStream_t s) {
+  const int G = n_q / n_kv;
+  PromptAttn a{q, ldq, k_cache, v_cache, n_kv, max_pos, P, pos_base, (P + kPQ / G - 1) / (kPQ / G),
+               kLog2e / sqrtf((float)kHD), out, ldo};
+  switch (G) {
+    case 1: launch_prompt_g<1>(a, S, s); break;
+    case 2: launch_prompt_g<2>(a, S, s); break;
+    case 4: launch_prompt_g<4>(a, S, s); break;
+    default: launch_prompt_g<8>(a, S, s); break;
   }
   return hipGetLastError();
 }

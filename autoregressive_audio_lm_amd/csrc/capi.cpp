@@ -1248,11 +1248,8 @@ int m3_prefill_qk_norm_rope(const uint16_t* qkv, int S, int P, int ldqkv, int n_
                                         static_cast<hipStream_t>(stream), nullptr, 0, nullptr, P));
 }
 
-size_t m3_prefill_attention_workspace_bytes(int S, int P, int n_q, int n_kv, int pos_base) {
-  if (S < 1 || P < 1 || (long)S * P > M3_MAX_M_PREFILL || !attn_heads_ok(n_q, n_kv) ||
-      pos_base < 0 || (long)pos_base + P > M3_MAX_POS)
-    return 0;
-  return attn_workspace_bytes(S * P, n_q, n_kv, pos_base + P);
+size_t m3_prefill_attention_workspace_bytes(int, int, int, int, int) {
+  return 0;                                      // the tiled prompt kernel keeps no partial records
 }
 
 int m3_prefill_attention(const uint16_t* q, int S, int P, int ldq, int n_q, int n_kv, int head_dim,
@@ -1266,23 +1263,19 @@ int m3_prefill_attention(const uint16_t* q, int S, int P, int ldq, int n_q, int 
     return M3_ERR_SHAPE;
   if (ldq < n_q * M3_HEAD_DIM || ldo < n_q * M3_HEAD_DIM) return M3_ERR_SHAPE;
   const int R = S * P;
-  const size_t need = attn_workspace_bytes(R, n_q, n_kv, pos_base + P);
-  if (need && !workspace) return M3_ERR_NULL;
-  if (workspace_bytes < need) return M3_ERR_WORKSPACE;
+  (void)workspace;
+  (void)workspace_bytes;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      (need && !aligned(workspace, 16)) || ldq % 8 || ldo % 8)
+      ldq % 8 || ldo % 8)
     return M3_ERR_ALIGN;
   const size_t q_b = ((size_t)(R - 1) * ldq + n_q * M3_HEAD_DIM) * 2;
   const size_t o_b = ((size_t)(R - 1) * ldo + n_q * M3_HEAD_DIM) * 2;
   const size_t c_b = cache_bytes(S, n_kv, max_pos);
-  if (overlap(out, o_b, q, q_b) || overlap(out, o_b, k_cache, c_b) || overlap(out, o_b, v_cache, c_b) ||
-      (need && (overlap(workspace, need, out, o_b) || overlap(workspace, need, q, q_b) ||
-                overlap(workspace, need, k_cache, c_b) || overlap(workspace, need, v_cache, c_b))))
+  if (overlap(out, o_b, q, q_b) || overlap(out, o_b, k_cache, c_b) || overlap(out, o_b, v_cache, c_b))
     return M3_ERR_ALIAS;
   // row (s, t) attends over positions 0 .. pos_base + t of sequence s
-  return hip_status(launch_decode_attention(q, R, ldq, n_q, n_kv, k_cache, v_cache, max_pos,
-                                            pos_base + 1, out, ldo, workspace,
-                                            static_cast<hipStream_t>(stream), nullptr, 0, P));
+  return hip_status(launch_prompt_attention(q, S, P, ldq, n_q, n_kv, k_cache, v_cache, max_pos,
+                                            pos_base, out, ldo, static_cast<hipStream_t>(stream)));
 }
 
 uint64_t m3_frame_weight_bytes(const m3_config* c) {

@@ -178,6 +178,11 @@ hipError_t launch_qk_norm_rope(const uint16_t* qkv, int B, int ldqkv, int n_q, i
                                uint16_t* k_cache, uint16_t* v_cache, int max_pos, hipStream_t s,
                                const uint32_t* frame_dev = nullptr, int pos0 = 0,
                                uint32_t* err = nullptr, int P = 1);
+// the prompt's causal attention: S sequences of P rows, row (s, t) over
+// positions 0 .. pos_base + t of cache s; no workspace
+hipError_t launch_prompt_attention(const uint16_t* q, int S, int P, int ldq, int n_q, int n_kv,
+                                   const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
+                                   int pos_base, uint16_t* out, int ldo, hipStream_t s);
 hipError_t launch_decode_attention(const uint16_t* q, int B, int ldq, int n_q, int n_kv,
                                    const uint16_t* k_cache, const uint16_t* v_cache, int max_pos,
                                    int T, uint16_t* out, int ldo, void* ws, hipStream_t s,

@@ -343,9 +343,11 @@ int m3_decode_attention_step(const uint16_t* qkv, int B, int ldqkv, int n_q, int
  * [max_pos][128]).  The caches then hold the prompt for decode attention.
  *
  * m3_prefill_attention: causal attention, row (s, t) over positions 0 ..
- * pos_base + t of cache s, with m3_decode_attention's arithmetic and
- * chunking; workspace of m3_prefill_attention_workspace_bytes(S, P, n_q, n_kv,
- * pos_base) bytes (0 when every row fits one chunk).
+ * pos_base + t of cache s: fp32 scores of the bf16 q and keys, scaled to
+ * base 2, a softmax with a running maximum and fp32 P.V over chunks of 64
+ * keys, out = bf16(P.V / sum), one workgroup per block of rows.  No workspace:
+ * m3_prefill_attention_workspace_bytes returns 0 and the workspace arguments
+ * are ignored (they may be NULL, 0).
  *
  * 1 <= S <= M3_MAX_B; S * P <= M3_MAX_M_PREFILL; 0 <= pos_base, pos_base + P
  * <= max_pos <= M3_MAX_POS; the other sizes, alignment and aliasing rules and

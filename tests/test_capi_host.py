@@ -249,8 +249,7 @@ def test_attention_refusals(L):
 def test_prompt_attention_refusals(L):
     P = ctypes.c_void_p
     need = L.m3_prefill_attention_workspace_bytes(2, 300, 32, 8, 0)
-    assert need == 600 * 32 * 3 * 130 * 4                # three chunks of 128 for the last rows
-    assert L.m3_prefill_attention_workspace_bytes(2, 300, 24, 8, 0) == 0   # unsupported heads
+    assert need == 0                                     # the tiled kernel keeps no records
     tab = P(0x1000000)
     cb = 2 * 8 * 512 * 128 * 2
     q_arg = lambda **k: (k.get("qkv", P(0x10000000)), k.get("S", 2), k.get("L", 300),
@@ -263,12 +262,12 @@ def test_prompt_attention_refusals(L):
     assert L.m3_prefill_qk_norm_rope(*q_arg(ld=6000)) == _lib.M3_ERR_SHAPE
     assert L.m3_prefill_qk_norm_rope(*q_arg(qo=P(0x20000004))) == _lib.M3_ERR_ALIGN
     assert L.m3_prefill_qk_norm_rope(*q_arg(qo=P(0x10000000 + 8192))) == _lib.M3_ERR_ALIAS
-    a_arg = lambda **k: (P(0x20000000), k.get("S", 2), k.get("L", 300), 4096, 32, 8, 128,
+    a_arg = lambda **k: (P(0x20000000), k.get("S", 2), k.get("L", 300), 4096, 32, k.get("nkv", 8), 128,
                          P(0x40000000), P(0x40000000 + cb), k.get("mp", 512), k.get("pb", 0),
                          k.get("out", P(0x50000000)), 4096, k.get("ws", P(0x60000000)),
                          k.get("wsb", need), None)
     assert L.m3_prefill_attention(*a_arg(out=None)) == _lib.M3_ERR_NULL
-    assert L.m3_prefill_attention(*a_arg(wsb=need - 4)) == _lib.M3_ERR_WORKSPACE
+    assert L.m3_prefill_attention(*a_arg(nkv=7)) == _lib.M3_ERR_SHAPE        # 32 heads over 7
     assert L.m3_prefill_attention(*a_arg(pb=213)) == _lib.M3_ERR_SHAPE        # 213 + 300 > 512
     assert L.m3_prefill_attention(*a_arg(out=P(0x20000000 + 64))) == _lib.M3_ERR_ALIAS
 
