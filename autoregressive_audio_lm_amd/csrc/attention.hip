@@ -291,8 +291,9 @@ void launch_fused_g(const FusedAttn& f, int CH, int B, hipStream_t s) {
 // no partial records and no merge.  Scores: v_mfma_f32_32x32x16_bf16 (bf16
 // products, fp32 sums; each wave one 32 x 32 block of vectors x keys, q in
 // registers, keys straight from the cache), scaled to base 2 and masked past
-// each row's position; softmax and P.V in fp32 on the VALU as in the decode
-// kernels: p = 2^(s - m), a new maximum rescales the sum and the P.V by
+// each row's position; softmax in fp32 on the VALU and P.V on
+// v_mfma_f32_32x32x2f32 (fp32 products and sums) as in the decode kernels:
+// p = 2^(s - m), a new maximum rescales the sum and the P.V by
 // 2^(m_old - m_new), out = bf16(P.V / sum).
 constexpr int kPQ = 64;                          // query vectors per workgroup
 constexpr int kPK = 64;                          // keys per chunk
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(kAThreads, 2) void prompt_attn_kernel(PromptAttn a)
   const uint16_t* vb = a.v + cb;
   auto vpos = [&](int v) { return a.pos_base + min(t0 + v / G, a.P - 1); };
 
-  // wave (qb, kc): score block of vectors 32 qb .., keys 32 kc .. of a chunk;
+  // scores: wave (qb, kc) = block of vectors 32 qb .., keys 32 kc .. of a chunk;
   // A operand: vector 32 qb + l % 32, dims 16 ks + 8 (l / 32) .. +7
   const int qb = wave >> 1, kc = wave & 1;
   uint4 qa[8];
@@ -340,30 +341,40 @@ __global__ __launch_bounds__(kAThreads, 2) void prompt_attn_kernel(PromptAttn a)
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qa[ks] = *reinterpret_cast<const uint4*>(qr + 16 * ks);
   }
-  // softmax: 4 threads per vector, 16 keys each; P.V: vectors pv0 .. +3, dims pd0 .. +7
+  // the next chunk's keys (this wave's 32) and values (4 x 16 bytes per thread)
+  uint4 kk[8], vv[4];
+  auto load_chunk = [&](int k0) {
+    const uint16_t* kr = kb + (size_t)min(k0 + 32 * kc + (lane & 31), nkeys - 1) * kHD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kk[ks] = *reinterpret_cast<const uint4*>(kr + 16 * ks);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + u * kAThreads, j = e >> 4, d8 = e & 15;
+      vv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)min(k0 + j, nkeys - 1) * kHD + 8 * d8);
+    }
+  };
+  // softmax: 4 threads per vector, 16 keys each
   const int sv = tid >> 2, sk = tid & 3;
-  const int pv0 = 4 * (tid >> 4), pd0 = 8 * (tid & 15);
   float m_run = -INFINITY, l_run = 0.f;
-  float acc[4][8];
+  // P.V on v_mfma_f32_32x32x2_f32: wave (pb, dc) holds vectors 32 pb .., dims
+  // 64 dc .. +63 as two 32 x 32 blocks; A = P[vector l % 32][key 2 s + l / 32],
+  // B = V[key 2 s + l / 32][dim l % 32]
+  const int pb = wave >> 1, dc = wave & 1;
+  f32x16_t acc[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[i][d] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
+  load_chunk(0);
   for (int c = 0; c < nch; ++c) {
     const int k0 = c * kPK;
-    // the chunk's value rows (past the last key: its row again, weighted 0)
 #pragma unroll
-    for (int e = tid; e < kPK * kHD / 8; e += kAThreads) {
-      const int j = e >> 4, d8 = e & 15;
-      *reinterpret_cast<uint4*>(&Vs[j][8 * d8]) =
-          *reinterpret_cast<const uint4*>(vb + (size_t)min(k0 + j, nkeys - 1) * kHD + 8 * d8);
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + u * kAThreads;
+      *reinterpret_cast<uint4*>(&Vs[e >> 4][8 * (e & 15)]) = vv[u];
     }
     {
-      const uint16_t* kr = kb + (size_t)min(k0 + 32 * kc + (lane & 31), nkeys - 1) * kHD + 8 * (lane >> 5);
-      uint4 kk[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kk[ks] = *reinterpret_cast<const uint4*>(kr + 16 * ks);
       f32x16_t sacc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
@@ -379,6 +390,7 @@ __global__ __launch_bounds__(kAThreads, 2) void prompt_attn_kernel(PromptAttn a)
         Pt[j][v] = kp < nkeys && kp <= vpos(v) ? sacc[e] * a.scale2 : -INFINITY;
       }
     }
+    if (c + 1 < nch) load_chunk(k0 + kPK);       // in flight through the softmax and P.V
     __syncthreads();
     {
       float x[16], mc = -INFINITY;
@@ -406,40 +418,36 @@ __global__ __launch_bounds__(kAThreads, 2) void prompt_attn_kernel(PromptAttn a)
     }
     __syncthreads();
     {
-      float al[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = As[pv0 + i];
+      for (int e = 0; e < 16; ++e) {
+        const float al = As[32 * pb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)];
+        acc[0][e] *= al;
+        acc[1][e] *= al;
+      }
+      const int pv = 32 * pb + (lane & 31);
+#pragma unroll 8
+      for (int s2 = 0; s2 < kPK / 2; ++s2) {
+        const int j = 2 * s2 + (lane >> 5);
+        const float pa = Pt[j][pv];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[i][d] *= al[i];
-      for (int j = 0; j < kPK; ++j) {
-        const uint4 v4 = *reinterpret_cast<const uint4*>(&Vs[j][pd0]);
-        const float vf[8] = {bf2f(v4.x & 0xffffu), bf2f(v4.x >> 16), bf2f(v4.y & 0xffffu), bf2f(v4.y >> 16),
-                             bf2f(v4.z & 0xffffu), bf2f(v4.z >> 16), bf2f(v4.w & 0xffffu), bf2f(v4.w >> 16)};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = Pt[j][pv0 + i];
-#pragma unroll
-          for (int d = 0; d < 8; ++d) acc[i][d] = fmaf(pr, vf[d], acc[i][d]);
-        }
+        for (int h = 0; h < 2; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              pa, bf2f(Vs[j][64 * dc + 32 * h + (lane & 31)]), acc[h], 0, 0, 0);
       }
     }
     __syncthreads();                             // Pt and Vs are rewritten by the next chunk
   }
   if (sk == 0) Ls[sv] = l_run;
   __syncthreads();
+  // lane holds O[32 pb + 8 g + 4 (l / 32) + r][64 dc + 32 h + l % 32] in acc[h][4 g + r]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = pv0 + i, t = t0 + v / G;
+  for (int e = 0; e < 16; ++e) {
+    const int v = 32 * pb + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), t = t0 + v / G;
     if (t >= a.P) continue;
     const float L = Ls[v];
-    uint32_t o[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      o[d] = f2bf(acc[i][2 * d] / L) | ((uint32_t)f2bf(acc[i][2 * d + 1] / L) << 16);
-    *reinterpret_cast<uint4*>(a.out + (size_t)(sq * a.P + t) * a.ldo + (size_t)(kvh * G + v % G) * kHD + pd0) =
-        make_uint4(o[0], o[1], o[2], o[3]);
+    uint16_t* orow = a.out + (size_t)(sq * a.P + t) * a.ldo + (size_t)(kvh * G + v % G) * kHD + 64 * dc + (lane & 31);
+    orow[0] = (uint16_t)f2bf(acc[0][e] / L);
+    orow[32] = (uint16_t)f2bf(acc[1][e] / L);
   }
 }
 
