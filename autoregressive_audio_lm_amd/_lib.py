@@ -69,7 +69,7 @@ class FrameLayout(ctypes.Structure):
                                                "flags", "err", "seq", "phases", "th", "tqkv", "tmlp", "tu",
                                                "thd", "tdqkv", "tdmlp", "th2", "thd2", "ho", "hdo", "rope", "aq", "ao", "dao", "kcache",
                                                "vcache", "dkcache", "dvcache", "attn_ws", "tao", "tdao", "trec", "stop",
-                                               "total")]
+                                               "kpart", "kcnt", "total")]
 
 
 class PhaseRegion(ctypes.Structure):

@@ -277,6 +277,11 @@ m3_frame_layout layout_of(const m3_config& c, int B) {
   const int nch = at ? body_attn_chunks(c, B) : 0;
   L.trec = take(at && nch > 1 ? nL * B * c.n_heads * nch * (2 + 128) * 8 : 0);
   L.stop = take((size_t)B * 4);
+  // the eager and graph frames' GEMVs split along K (gemv.hip): the down
+  // projections, whose outputs have max(H, D) rows at most
+  const int kblocks = n_blocks(std::max(d.H, d.D));
+  L.kpart = take(gemv_split_part_bytes(kblocks));
+  L.kcnt = take(gemv_split_counters(kblocks) * 4);
   L.total = off;
   return L;
 }
@@ -496,6 +501,10 @@ int build_frame(const m3_model* m, uint8_t* S, int B, int32_t* codes, FrameSink&
       g.ytag = 1;
       g.rot = sc.rot;
       g.follow = sc.follow;
+    } else {
+      g.kpart = reinterpret_cast<float*>(S + L.kpart);
+      g.kcnt = reinterpret_cast<uint32_t*>(S + L.kcnt);
+      g.kpart_blocks = n_blocks(std::max(d.H, d.D));
     }
     const hipError_t e = sink.gemv(g);
     ++ph;

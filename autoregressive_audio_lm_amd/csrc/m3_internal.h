@@ -83,12 +83,23 @@ struct GemvDesc {
   // count); follow = the block count of the phase before, whose workgroups
   // with one block fewer take this phase's blocks first (0: workgroup 0)
   int rot = 0, follow = 0;
+  // one-launch frames only (no effect on any value): a GEMV without a fused
+  // norm whose B-row operand does not fit LDS may run split along K (see
+  // gemv.hip) with these: fp32 wave partials for kpart_blocks row blocks and
+  // one counter per group of row blocks, zero between launches
+  float* kpart = nullptr;
+  uint32_t* kcnt = nullptr;
+  int kpart_blocks = 0;
 };
 
 // Largest fused-norm activation block held in LDS (elements of B * K_pad).
 constexpr int kMaxNormElems = 65536;
 
 hipError_t launch_gemv(const GemvDesc& d, hipStream_t s);
+// the split-K workspace for GEMVs of up to nblocks row blocks: partial bytes
+// and group counters (GemvDesc::kpart, kcnt)
+size_t gemv_split_part_bytes(int nblocks);
+size_t gemv_split_counters(int nblocks);
 // dynamic LDS bytes launch_gemv uses for (fmt, K, B, fused norm); > 160 KiB = unsupported
 size_t gemv_smem_bytes(int fmt, int K, int B, bool has_gamma);
 // set kernel attributes of every GEMV instantiation (before graph capture)

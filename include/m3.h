@@ -497,6 +497,12 @@ typedef struct {
                       chunk records of each body layer's attention (zero-sized
                       when one chunk covers max_pos)                          */
   size_t stop;     /* int32 [B]: 0, or 1 + the frame that drew the end token    */
+  size_t kpart;    /* f32 wave partial sums of the eager and graph frames' GEMVs
+                      split along K (down projections whose B-row operand does
+                      not fit LDS: B >= 7 in the body at K = 12288); scratch   */
+  size_t kcnt;     /* u32 counters of those GEMVs' row-block groups; zero
+                      between launches (set by m3_frame_state_init, left zero by
+                      every launch)                                            */
   size_t total;
 } m3_frame_layout;
 

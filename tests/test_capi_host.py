@@ -362,9 +362,16 @@ def test_frame_layout_stage_slots(L, name, B):
     for a, b in zip(tagged, tagged[1:]):
         span = getattr(lay, b) - getattr(lay, a)
         assert tneed[a] <= span < tneed[a] + 256, (a, span, tneed[a])
-    # without attention the attention buffers take no room; the rows' stop words come last
+    # without attention the attention buffers take no room; the rows' stop
+    # words come next, then the split-K scratch of the down projections (fp32
+    # partials of 8 waves x 16 rows x 16 outputs per row block of
+    # max(H, D) rows; a counter per group of 4 row blocks)
     assert lay.rope == lay.aq == lay.ao == lay.dao == lay.kcache == lay.trec == lay.stop
-    assert lay.total == lay.stop + (B * 4 + 255) // 256 * 256
+    up = lambda n: (n + 255) // 256 * 256
+    nb = (max(cfg["H"], cfg["D"]) + 15) // 16
+    assert lay.kpart == lay.stop + up(B * 4)
+    assert lay.kcnt == lay.kpart + up(nb * 8 * 16 * 16 * 4)
+    assert lay.total == lay.kcnt + up((nb + 3) // 4 * 4)
     # with the end token the semantic logits have one more column (rows padded to 8)
     ce = make_config(cfg, **configs.PRESETS["A"], end_token=True)
     le = _lib.FrameLayout()

@@ -18,7 +18,7 @@ import torch
 
 import oracle as O
 import stages
-from autoregressive_audio_lm_amd import _lib, configs, runtime, synth
+from autoregressive_audio_lm_amd import _lib, configs, m3, runtime, synth
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -75,6 +75,62 @@ def test_full_size_frame_stages(full, B, path):
     stats = stages.check_frame(om, got, synth.bits(x0), seed=9, frame=7, rows=ROWS[B])
     print(f"preset {preset} {path} B={B}: {stats.summary()}; codes {got['codes'][:2].tolist()}",
           flush=True)
+
+
+@pytest.mark.parametrize("B", [7, 16])
+def test_full_size_split_equals_one_launch(full, B):
+    """From B = 7 on, the down projection's operand (K = 12288) does not fit
+    LDS, and the graph frame runs it split along K (the depth decoder's down
+    too from B = 14): each workgroup stages a quarter of the operand for four
+    row blocks, and the last workgroup of each group of row blocks sums the
+    wave partials in the one-launch kernel's order.  Every layer's output
+    equals, byte for byte, the standalone GEMV call (one launch, operand read
+    from memory) on the frame's own operand and residual, over two replays
+    (the group counters are left at zero for the next launch); O, which is
+    not split, is checked the same way."""
+    preset, cfg, dm, om = full
+    c = dm.config
+    x0 = synth.activations(B, cfg["H"], 700 + B)
+    st = runtime.FrameState(dm, B, x0.to(DEV), frame0=3)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        st.capture(s)
+        st.replay(s)
+        st.replay(s)
+    s.synchronize()
+    assert int(st.frame.item()) == 5
+    mlp, ho, h = st.slots("mlp"), st.slots("ho"), st.slots("h")
+    with torch.cuda.stream(s):
+        for l in range(c.n_layers):
+            y = m3.gemv(dm.fmt_body, dm.packed_layers[l]["down"], c.hidden, c.ffn, mlp[l],
+                        epi=m3.EPI_RESIDUAL, residual=ho[l], stream=s)
+            s.synchronize()
+            assert torch.equal(y.view(torch.int16), h[l].view(torch.int16)), l
+        # O (the attention stub's V heads, 4 query heads per KV head), from
+        # layer 1 on (layer 0's residual, the frame input, is overwritten by
+        # the next input at the frame's end)
+        qkv = st.slots("qkv")
+        nq, nkv = c.n_heads * c.head_dim, c.n_kv_heads * c.head_dim
+        for l in range(1, c.n_layers):
+            y = m3.gemv(dm.fmt_body, dm.packed_layers[l]["o"], c.hidden, nq, qkv[l],
+                        stub_group=c.n_heads // c.n_kv_heads, stub_voff=nq + nkv,
+                        epi=m3.EPI_RESIDUAL, residual=h[l - 1], stream=s)
+            s.synchronize()
+            assert torch.equal(y.view(torch.int16), ho[l].view(torch.int16)), ("o", l)
+        dmlp, hdo, hd, dqkv = st.slots("dmlp"), st.slots("hdo"), st.slots("hd"), st.slots("dqkv")
+        dq = c.d_heads * c.d_head_dim
+        for j in range(c.n_codebooks - 1):
+            for l in range(c.d_layers):
+                y = m3.gemv(dm.fmt_depth, dm.packed_dlayers[l]["down"], c.d_hidden, c.d_ffn,
+                            dmlp[j, l], epi=m3.EPI_RESIDUAL, residual=hdo[j, l], stream=s)
+                y2 = m3.gemv(dm.fmt_depth, dm.packed_dlayers[l]["o"], c.d_hidden, dq, dqkv[j, l],
+                             stub_group=1, stub_voff=2 * dq, epi=m3.EPI_RESIDUAL,
+                             residual=hd[j, l], stream=s)
+                s.synchronize()
+                assert torch.equal(y.view(torch.int16), hd[j, l + 1].view(torch.int16)), (j, l)
+                assert torch.equal(y2.view(torch.int16), hdo[j, l].view(torch.int16)), ("do", j, l)
+    st.release()
+    print(f"preset {preset} B={B}: O and the split down projections equal the one-launch GEMV", flush=True)
 
 
 @pytest.mark.parametrize("preset,B", [("A", 1), ("A", 6), ("B", 2), ("C", 1)])
