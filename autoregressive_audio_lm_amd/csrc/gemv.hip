@@ -329,10 +329,18 @@ hipError_t launch_gemv(const GemvDesc& d, hipStream_t s) {
         return ku == 4 ? launch_split<M3_I8G128, 4>(p, d, s) : launch_split<M3_I8G128, 8>(p, d, s);
     }
   }
-  const size_t smem = smem_bytes_of(d.fmt, d.K, d.B, d.gamma != nullptr);
+  const size_t smem = smem_bytes_of(d.fmt, d.K, d.B, d.gamma != nullptr) +
+                      (lds ? gamma_lds_bytes(d.fmt, d.gamma != nullptr, d.gather != nullptr, p.lds_rows,
+                                             p.lds_stride, d.K, nb_of(d.B))
+                           : 0);
   // resident workgroups per CU from LDS (8 waves each, at most 2 per CU)
   int per_cu = (int)((160 * 1024) / (smem + 1024));
   per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+  // with a fused norm every workgroup normalises the whole B x K operand:
+  // one workgroup per CU does it once per CU.  (Measured on the graph frame,
+  // preset A: B = 6 4.55 -> 4.17 ms, B = 16 5.15 -> 5.04 ms, B = 1 3.72 ->
+  // 3.63 ms, B = 2 3.82 -> 3.74 ms.)
+  if (d.gamma) per_cu = 1;
   int grid = 256 * per_cu;
   if (grid > p.nblocks) grid = p.nblocks;
   switch (d.fmt) {

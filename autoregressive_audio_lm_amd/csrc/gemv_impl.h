@@ -664,14 +664,44 @@ __device__ __forceinline__ void stage_rows_few(const Params& p, uint16_t* act, f
 // the first weight batch would wait for it).  Two groups cover 16 rows of
 // K = 4096.
 constexpr int kPreGroups = 2;
+// One launch per GEMV, more than two rows, a fused norm with K <= 4096: gamma
+// is requested with the first groups too (two float4 per thread) and kept in
+// LDS after the operand rows, so the normalising pass reads no global memory
+// and the second weight batch can be requested before the sum of squares.
+constexpr int kGammaLdsMaxK = 4 * 2 * kThreads;
 struct XGroup {
   uint4 v[kPreGroups][kStageUnroll];
   bool valid;
 };
+struct GPre {
+  float4 g[2];
+  bool valid;
+};
+
+// LDS bytes of the staged gamma in a one-launch GEMV (0: not staged); the
+// host sizes the launch's LDS with it, the kernel decides with it.  Not for
+// int8-g128 (its first groups are not prefetched, see gemv_run, and its
+// 16-row depth kernels keep two workgroups per CU only without it) nor with
+// the gather prologue.
+__host__ __device__ inline size_t gamma_lds_bytes(int fmt, bool has_gamma, bool has_gather, int lds_rows,
+                                                  int lds_stride, int K, int NB) {
+  if (fmt == M3_I8G128 || !has_gamma || has_gather || lds_rows <= 2 || K > kGammaLdsMaxK) return 0;
+  const size_t fixed = (size_t)kWaves * NB * 16 * 4 + (size_t)M3_MAX_B * kWaves * 4 + (size_t)M3_MAX_B * 4;
+  const size_t need = fixed + (size_t)lds_rows * lds_stride * 2 + (size_t)K * 4;
+  return need <= 160 * 1024 ? (size_t)K * 4 : 0;
+}
 
 template <bool COH>
-__device__ __forceinline__ void prefetch_group(const Params& p, XGroup& g, const Tags& tg) {
+__device__ __forceinline__ void prefetch_group(const Params& p, XGroup& g, const Tags& tg, GPre* gp) {
   const int tid = threadIdx.x;
+  if (gp) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = u * kThreads + tid;
+      gp->g[u] = i * 4 < p.K ? *reinterpret_cast<const float4*>(p.gamma + i * 4) : make_float4(0, 0, 0, 0);
+    }
+    gp->valid = true;
+  }
   const int cpr = (p.lds_stride - 8) >> 3;
   const int total = p.lds_rows * cpr;
 #pragma unroll
@@ -688,11 +718,16 @@ __device__ __forceinline__ void prefetch_group(const Params& p, XGroup& g, const
   g.valid = true;
 }
 
-template <bool COH>
+// gl: the LDS gamma of a one-launch GEMV whose gamma was prefetched into
+// gp, else nullptr; after_copy() runs once the copy pass is in LDS (there:
+// the request of the second weight batch, nothing left to read from global
+// memory but the weights)
+template <bool COH, class AfterCopy>
 __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act, float* ss_buf,
                                                   int* code_lds, int wg, const XPre& pre,
                                                   const XGroup& grp,
-                                                  const Tags& tg) {
+                                                  const Tags& tg, float* gl, const GPre* gp,
+                                                  AfterCopy&& after_copy) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int stride = p.lds_stride;
   const int cpr = (stride - 8) >> 3;            // chunks per row: K, padding, zero tile
@@ -745,7 +780,19 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
       }
     }
   }
+  if constexpr (!COH) {
+    if (gl) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = u * kThreads + tid;
+        if (i * 4 < p.K) *reinterpret_cast<float4*>(gl + i * 4) = gp->g[u];
+      }
+    }
+  }
   __syncthreads();
+  if constexpr (!COH) {
+    if (gl) after_copy();
+  }
   if (!p.gamma) return;
   // pass 2: r_b from the sum of squares of row b (float64): lane l sums
   // chunks l + 64 m into accumulator m % 4 (four independent chains whose LDS
@@ -781,8 +828,15 @@ __device__ __forceinline__ void stage_activations(const Params& p, uint16_t* act
   const int kc = p.K >> 3;
   for (int i = tid; i < kc; i += kThreads) {
     const int k = i * 8;
-    const float4 g0 = *reinterpret_cast<const float4*>(p.gamma + k);
-    const float4 g1 = *reinterpret_cast<const float4*>(p.gamma + k + 4);
+    float4 g0, g1;
+    if constexpr (!COH) {
+      const float* gs = gl ? gl : p.gamma;
+      g0 = *reinterpret_cast<const float4*>(gs + k);
+      g1 = *reinterpret_cast<const float4*>(gs + k + 4);
+    } else {      // (the persistent kernel's code as it was)
+      g0 = *reinterpret_cast<const float4*>(p.gamma + k);
+      g1 = *reinterpret_cast<const float4*>(p.gamma + k + 4);
+    }
     const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     // rows in groups of four: the group's LDS reads are issued together
     for (int b0 = 0; b0 < p.lds_rows; b0 += 4) {
@@ -1141,6 +1195,14 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
   pre.valid = false;
   XGroup grp;
   grp.valid = false;
+  // one GEMV per launch: the gamma staged in LDS after the operand rows
+  GPre gpre;
+  gpre.valid = false;
+  float* gl = nullptr;
+  if constexpr (LDS && !COH) {
+    if (gamma_lds_bytes(FMT, p.gamma != nullptr, p.has_gather != 0, p.lds_rows, p.lds_stride, p.K, NB) != 0)
+      gl = reinterpret_cast<float*>(act + (size_t)p.lds_rows * p.lds_stride);
+  }
   const bool ready = wt.probe();
   if (ready) {
     // (persistent launches: only phase 0, whose operand is plain; not worth the registers)
@@ -1152,7 +1214,7 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
         if (p.lds_rows <= 2)
           prefetch_x<COH>(p, pre, tg);
         else if constexpr (FMT != M3_I8G128)
-          prefetch_group<COH>(p, grp, tg);
+          prefetch_group<COH>(p, grp, tg, gl ? &gpre : nullptr);
       }
     }
     load(bufA, scA, 0);
@@ -1162,9 +1224,24 @@ __device__ __forceinline__ void gemv_run(const Params& p, uint8_t* smem, int wg,
     if (!wt.wait()) return;
   }
   if (nitems == 0) return;
-  if (LDS) stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre, grp, tg);
-  wt.staged();
-  if (ready) load(bufB, scB, 1);
+  // with the gamma staged, the second batch is requested once the copy pass
+  // is in LDS (the sum of squares and the normalising pass then overlap two
+  // batches), else after the staging
+  if constexpr (!COH) {
+    bool second = false;
+    if (LDS)
+      stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre, grp, tg, gpre.valid ? gl : nullptr,
+                             &gpre, [&]() {
+                               load(bufB, scB, 1);
+                               second = true;
+                             });
+    wt.staged();
+    if (!second) load(bufB, scB, 1);
+  } else {
+    if (LDS) stage_activations<COH>(p, act, ss_buf, code_lds, wg, pre, grp, tg, nullptr, nullptr, [] {});
+    wt.staged();
+    if (ready) load(bufB, scB, 1);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // the scheduling barriers keep each batch's loads ahead of the next batch's
   // arithmetic (the scheduler would otherwise sink them into it)
