@@ -638,7 +638,7 @@ static void draw_rows(const m3o_model* m, const float* lg, int B, int V,
 
 /* One layer with the identity attention stub, in place on h [B, Hd]: the
    step the frame takes per body layer and per depth layer ([ds] model
-   overview; BASELINE's stubbed attention). */
+   overview; the benchmark workload stubs attention as identity). */
 void m3o_layer_stub(const m3o_layer* L, uint16_t* h, int B, int Hd, int n_heads, int n_kv,
                     int hd, int F, float eps) {
   int nq = n_heads * hd, nkv = n_kv * hd;
